@@ -1,0 +1,348 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle itself.
+
+Each test names what it pins the oracle to: a library routine computing the
+same definition (numpy matmul, torch SDPA, torch's bfloat16 cast), a closed
+form, an invariant the pages state, brute force in plain Python, a value the
+pages print, or bit-for-bit agreement of the incremental decode with the
+full-window recompute that the topos page keeps as its check.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def rng(seed):
+    return np.random.default_rng(seed)
+
+
+# ----------------------------------------------------------------- bf16 rounding
+def test_round_bf16_matches_torch_cast():
+    """Pinned to torch's float32 -> bfloat16 cast (round to nearest even)."""
+    r = rng(1)
+    x = np.concatenate([
+        r.standard_normal(20000).astype(np.float32),
+        (r.standard_normal(2000) * 1e-30).astype(np.float32),
+        (r.standard_normal(2000) * 1e30).astype(np.float32),
+        # exact ties: lower 16 bits = 0x8000, both parities of bit 16
+        (np.arange(1, 4001, dtype=np.uint32) << 16 | 0x8000).astype(np.uint32).view(np.float32)
+        * np.float32(1.0),
+        np.array([0.0, -0.0, 1.0, -1.0], dtype=np.float32),
+    ])
+    x = x[np.isfinite(x)]
+    want = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+    got = oracle.round_bf16(x.astype(np.float64))
+    np.testing.assert_array_equal(got, want)
+
+
+# ------------------------------------------------------------------- O1 populate
+@pytest.mark.parametrize("L,B,T,dm,H,D", [(3, 2, 37, 48, 2, 16), (1, 1, 64, 64, 2, 32)])
+def test_populate_equals_numpy_matmul_per_layer(L, B, T, dm, H, D):
+    """K_l = E . WK_l per layer, head-major: pinned to numpy float64 matmul."""
+    r = rng(2)
+    E = r.standard_normal((B, T, dm))
+    WK = [r.standard_normal((dm, H * D)) * 0.02 for _ in range(L)]
+    WV = [r.standard_normal((dm, H * D)) * 0.02 for _ in range(L)]
+    Kc, Vc = oracle.populate(E, WK, WV, H, D)
+    for l in range(L):
+        for b in range(B):
+            k = (E[b] @ WK[l]).reshape(T, H, D).transpose(1, 0, 2)
+            v = (E[b] @ WV[l]).reshape(T, H, D).transpose(1, 0, 2)
+            np.testing.assert_allclose(Kc[l, b], k, rtol=1e-12, atol=1e-14)
+            np.testing.assert_allclose(Vc[l, b], v, rtol=1e-12, atol=1e-14)
+
+
+def test_populate_each_layer_uses_only_its_own_weights():
+    """[CKE] 'The concept': every layer re-projects E with its own WK/WV.
+    Changing WK_1 changes K slab 1 only; equal weights give equal slabs."""
+    r = rng(3)
+    L, B, T, dm, H, D = 3, 1, 20, 32, 2, 16
+    E = r.standard_normal((B, T, dm))
+    W = r.standard_normal((dm, H * D)) * 0.02
+    WK = [W.copy() for _ in range(L)]
+    WV = [W.copy() for _ in range(L)]
+    Kc, Vc = oracle.populate(E, WK, WV, H, D)
+    for l in range(1, L):
+        np.testing.assert_array_equal(Kc[l], Kc[0])
+    np.testing.assert_array_equal(Kc, Vc)
+    WK2 = [w.copy() for w in WK]
+    WK2[1] = WK2[1] + 0.5
+    Kc2, Vc2 = oracle.populate(E, WK2, WV, H, D)
+    np.testing.assert_array_equal(Kc2[0], Kc[0])
+    np.testing.assert_array_equal(Kc2[2], Kc[2])
+    assert np.abs(Kc2[1] - Kc[1]).min() > 0
+    np.testing.assert_array_equal(Vc2, Vc)
+
+
+def test_layer_offset_matches_page_value():
+    """[CKE] 'View 2': the layer-5 decode call reads A_CROSS_K_CACHE + 15360000
+    for Whisper Base (fp32). Pins the layer-major stride of the cache layout."""
+    g = json.load(open(os.path.join(GOLDEN, "cke_whisper_base_geometry.json")))
+    T, dm = g["encoder_memory_shape"]
+    H, D = g["num_heads"], g["head_dim"]
+    assert H * D == dm and g["key_tokens"] == T
+    off = oracle.layer_offset_bytes(5, 1, H, T, D, g["cache_elem_bytes"])
+    assert off == g["layer5_k_offset_bytes"]
+    # the oracle's own array layout [L][B][H][T][D] has the same stride
+    a = np.zeros((g["n_layers"], 1, H, T, D), dtype=np.float32)
+    assert a[5].ctypes.data - a.ctypes.data == g["layer5_k_offset_bytes"]
+    # and the synthetic Whisper-Base workload has this geometry
+    base = synth.get("base")
+    assert (base.mem_len, base.d_model, base.n_layers, base.n_heads,
+            base.head_dim, base.scale) == (T, dm, g["n_layers"], H, D, g["scale"])
+
+
+def test_populate_bf16_rounds_stored_value():
+    """bf16 storage: the stored value is the exact product sum (numpy float64
+    matmul) rounded once to 8 significant bits, so it is within the unit
+    roundoff 2^-8 of it and is a bf16 value."""
+    r = rng(4)
+    E = synth.bf16_bits_to_f32(synth.to_bf16_bits(r.standard_normal((1, 16, 32)).astype(np.float32)))
+    W = [synth.bf16_bits_to_f32(synth.to_bf16_bits((r.standard_normal((32, 32)) * 0.02).astype(np.float32)))]
+    Kc, _ = oracle.populate(E, W, W, 2, 16, round_bf16=True)
+    exact = (E[0].astype(np.float64) @ W[0].astype(np.float64)).reshape(16, 2, 16).transpose(1, 0, 2)
+    # 8 significant bits: relative rounding error <= 2^-8
+    rel = np.abs(Kc[0, 0] - exact) / np.abs(exact)
+    assert rel.max() <= 2.0 ** -8
+    assert rel.max() > 2.0 ** -12   # and the values really were rounded
+    # and each stored value is representable in bf16
+    np.testing.assert_array_equal(oracle.round_bf16(Kc), Kc)
+
+
+# ----------------------------------------------------------------- O2 attention
+def _sdpa64(q, K, V, scale):
+    """torch SDPA in float64 on the CPU: q [..., nq, D], K, V [..., n, D]."""
+    return torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q), torch.from_numpy(K), torch.from_numpy(V),
+        scale=scale).numpy()
+
+
+@pytest.mark.parametrize("n,D,scale", [(1, 8, 0.5), (7, 16, 0.25), (1500, 64, 0.125),
+                                       (64, 32, 1 / math.sqrt(32))])
+def test_attend_matches_torch_sdpa(n, D, scale):
+    r = rng(5 + n)
+    q = r.standard_normal(D) * 0.45
+    K = r.standard_normal((n, D)) * 0.45
+    V = r.standard_normal((n, D)) * 0.45
+    got = oracle.attend(q, K, V, scale)
+    want = _sdpa64(q[None], K, V, scale)[0]
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-14)
+
+
+def test_attend_brute_force_plain_python():
+    """Explicit score matrix and softmax written with math.exp, no max shift."""
+    r = rng(6)
+    for n in range(1, 9):
+        for D in (1, 3, 8):
+            q = r.standard_normal(D)
+            K = r.standard_normal((n, D))
+            V = r.standard_normal((n, D))
+            sc = 0.3
+            w = [math.exp(sc * sum(q[d] * K[t][d] for d in range(D))) for t in range(n)]
+            Z = sum(w)
+            want = [sum(w[t] * V[t][d] for t in range(n)) / Z for d in range(D)]
+            np.testing.assert_allclose(oracle.attend(q, K, V, sc), want,
+                                       rtol=1e-13, atol=1e-15)
+
+
+def test_attend_closed_forms():
+    r = rng(7)
+    D = 16
+    V = r.standard_normal((10, D))
+    K = r.standard_normal((10, D))
+    # one row: the output is that row
+    np.testing.assert_allclose(oracle.attend(r.standard_normal(D), K[:1], V[:1], 0.7), V[0],
+                               rtol=0, atol=1e-15)
+    # zero query: uniform weights, output is the mean row
+    np.testing.assert_allclose(oracle.attend(np.zeros(D), K, V, 0.7), V.mean(0),
+                               rtol=1e-13, atol=1e-15)
+    # identical keys: uniform weights
+    Kc = np.repeat(K[:1], 10, axis=0)
+    np.testing.assert_allclose(oracle.attend(r.standard_normal(D), Kc, V, 0.7), V.mean(0),
+                               rtol=1e-13, atol=1e-15)
+    # one dominant key: output is that key's value row
+    q = np.zeros(D)
+    q[0] = 1.0
+    Kd = np.zeros((10, D))
+    Kd[6, 0] = 1.0
+    np.testing.assert_allclose(oracle.attend(q, Kd, V, 800.0), V[6], rtol=0, atol=1e-300)
+    # two keys, closed-form logistic weight
+    K2 = np.zeros((2, D))
+    K2[1, 0] = 1.0
+    q2 = np.zeros(D)
+    q2[0] = 2.0
+    w1 = 1.0 / (1.0 + math.exp(-2.0 * 0.5))
+    np.testing.assert_allclose(oracle.attend(q2, K2, V[:2], 0.5),
+                               (1 - w1) * V[0] + w1 * V[1], rtol=1e-14, atol=1e-15)
+
+
+def test_attend_key_bias_shift_invariance():
+    """[WK] section 2: a bias b on every key adds q.b to every score of a
+    query, and softmax ignores a common shift. Even q.b = +-1000 (which would
+    overflow exp without the max shift) leaves the output unchanged."""
+    r = rng(8)
+    n, D = 300, 64
+    q = r.standard_normal(D)
+    K = r.standard_normal((n, D))
+    V = r.standard_normal((n, D))
+    base = oracle.attend(q, K, V, 0.125)
+    for target in (1000.0, -1000.0, 3.0):
+        b = q / np.dot(q, q) * (target / 0.125)
+        got = oracle.attend(q, K + b[None, :], V, 0.125)
+        np.testing.assert_allclose(got, base, rtol=1e-9, atol=1e-12)
+        assert np.all(np.isfinite(got))
+
+
+def test_attend_value_shift_and_key_permutation():
+    r = rng(9)
+    n, D = 50, 32
+    q, K, V = r.standard_normal(D), r.standard_normal((n, D)), r.standard_normal((n, D))
+    base = oracle.attend(q, K, V, 0.2)
+    c = r.standard_normal(D)
+    np.testing.assert_allclose(oracle.attend(q, K, V + c[None], 0.2), base + c,
+                               rtol=1e-12, atol=1e-13)
+    p = r.permutation(n)
+    np.testing.assert_allclose(oracle.attend(q, K[p], V[p], 0.2), base,
+                               rtol=1e-12, atol=1e-14)
+
+
+def test_cross_decode_matches_sdpa_over_heads_and_streams():
+    r = rng(10)
+    B, nq, H, T, D = 3, 5, 4, 41, 16
+    q = r.standard_normal((B, nq, H, D))
+    Kc = r.standard_normal((B, H, T, D))
+    Vc = r.standard_normal((B, H, T, D))
+    got = oracle.cross_decode(q, Kc, Vc, 0.25)
+    want = _sdpa64(q.transpose(0, 2, 1, 3).copy(), Kc, Vc, 0.25).transpose(0, 2, 1, 3)
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-14)
+
+
+# ------------------------------------------------------------ O3 self-attention
+def test_self_append_scatter_equals_masked_blend_and_is_causal():
+    """[TOP]: the new row is written by scatter. [WK] section 4: the ANE writes
+    it with a one-hot masked blend. For finite old rows the two agree bit for
+    bit. Rows past pos never affect the output (NaN there stays out)."""
+    r = rng(11)
+    S, H, P, D = 2, 3, 12, 16
+    old = r.standard_normal((S, H, P, D))
+    for pos in (0, 5, P - 1):
+        q = r.standard_normal((S, H, D))
+        kn = r.standard_normal((S, H, D))
+        vn = r.standard_normal((S, H, D))
+        Ks, Vs = old.copy(), old.copy()
+        out = oracle.self_append_attend(q, kn, vn, Ks, Vs, pos, 0.25)
+        Kb, Vb = old.copy(), old.copy()
+        oracle.kv_blend_update(Kb, kn, pos)
+        oracle.kv_blend_update(Vb, vn, pos)
+        np.testing.assert_array_equal(Ks, Kb)
+        np.testing.assert_array_equal(Vs, Vb)
+        # poison the rows the call must not read
+        Kp, Vp = old.copy(), old.copy()
+        Kp[:, :, pos + 1:] = np.nan
+        Vp[:, :, pos + 1:] = np.nan
+        out_p = oracle.self_append_attend(q, kn, vn, Kp, Vp, pos, 0.25)
+        np.testing.assert_array_equal(out_p, out)
+        # causal SDPA over rows 0..pos (library routine)
+        want = _sdpa64(q[:, :, None, :].copy(), Ks[:, :, :pos + 1].copy(),
+                       Vs[:, :, :pos + 1].copy(), 0.25)[:, :, 0]
+        np.testing.assert_allclose(out, want, rtol=1e-12, atol=1e-14)
+
+
+def test_self_append_bf16_stores_rounded_rows():
+    r = rng(12)
+    S, H, P, D = 1, 2, 6, 8
+    Ks, Vs = np.zeros((S, H, P, D)), np.zeros((S, H, P, D))
+    kn = r.standard_normal((S, H, D)).astype(np.float32).astype(np.float64)
+    vn = r.standard_normal((S, H, D)).astype(np.float32).astype(np.float64)
+    q = r.standard_normal((S, H, D))
+    oracle.self_append_attend(q, kn, vn, Ks, Vs, 3, 0.5, round_bf16=True)
+    want = torch.from_numpy(kn.astype(np.float32)).to(torch.bfloat16).double().numpy()
+    np.testing.assert_array_equal(Ks[:, :, 3], want)
+
+
+# ------------------------------------------- O4/O5 incremental == full window
+def _harness_weights(seed, L, dm, std=0.02):
+    r = rng(seed)
+    return {k: [r.standard_normal((dm, dm)) * std for _ in range(L)]
+            for k in ("WK", "WV", "WQ", "WO", "WQs", "WKs", "WVs", "WOs")}
+
+
+@pytest.mark.parametrize("cfg", [
+    dict(L=1, B=1, nq=1, T=64, H=2, D=32, steps=8, bf16=False),   # Tiny geometry
+    dict(L=2, B=1, nq=3, T=20, H=2, D=8, steps=6, bf16=False),    # shared cache, beams
+    dict(L=2, B=2, nq=1, T=17, H=2, D=8, steps=5, bf16=True),     # streams, bf16 caches
+])
+def test_incremental_decode_equals_full_window_bit_for_bit(cfg):
+    """[TOP] 'What it opened': the whole-window formula and the one-token decode
+    formula must agree bit for bit at toy size. The full-window run re-projects
+    E and recomputes every self K/V row each step, so agreement also shows the
+    projection cache and the appended self cache change no bits."""
+    dm = cfg["H"] * cfg["D"]
+    r = rng(13)
+    E = r.standard_normal((cfg["B"], cfg["T"], dm))
+    if cfg["bf16"]:
+        E = oracle.round_bf16(E)
+    W = _harness_weights(14, cfg["L"], dm)
+    x0 = r.standard_normal((cfg["B"] * cfg["nq"], dm))
+    kw = dict(n_heads=cfg["H"], head_dim=cfg["D"], n_q=cfg["nq"], max_pos=cfg["steps"],
+              n_steps=cfg["steps"], scale=1 / math.sqrt(cfg["D"]), round_bf16=cfg["bf16"])
+    inc = oracle.decoder_run("incremental", E, W, x0, **kw)
+    full = oracle.decoder_run("full", E, W, x0, **kw)
+    for k in inc["rec"]:
+        np.testing.assert_array_equal(inc["rec"][k], full["rec"][k], err_msg=k)
+    for k in ("x", "Kc", "Vc", "Ks", "Vs"):
+        np.testing.assert_array_equal(inc[k], full[k], err_msg=k)
+    # the decode actually moved: inputs differ from step to step
+    assert not np.array_equal(inc["x"][1], inc["x"][2])
+
+
+def test_harness_records_are_consistent_with_call_level_functions():
+    """The decoder's recorded per-call inputs/outputs equal what the exported
+    call-level functions return on those inputs (teacher forcing is sound)."""
+    g = synth.get("tiny")
+    wt = synth.workload_tensors(g, ("E", "WK", "WV", "WQ", "WO", "WQs", "WKs", "WVs", "WOs", "x0"))
+    W = {k: wt[k] for k in ("WK", "WV", "WQ", "WO", "WQs", "WKs", "WVs", "WOs")}
+    kw = dict(n_heads=g.n_heads, head_dim=g.head_dim, n_q=g.n_q, max_pos=g.max_pos,
+              n_steps=g.steps, scale=g.scale)
+    run = oracle.decoder_run("incremental", wt["E"], W, wt["x0"], **kw)
+    Kc, Vc = oracle.populate(wt["E"], wt["WK"], wt["WV"], g.n_heads, g.head_dim)
+    np.testing.assert_array_equal(Kc, run["Kc"])
+    Ks = np.zeros((g.n_layers, g.n_seqs, g.n_heads, g.max_pos, g.head_dim))
+    Vs = np.zeros_like(Ks)
+    rec = run["rec"]
+    shp = (g.n_seqs, g.n_heads, g.head_dim)
+    for t in range(g.steps):
+        for l in range(g.n_layers):
+            so = oracle.self_append_attend(rec["qs"][t, l].reshape(shp), rec["kn"][t, l].reshape(shp),
+                                           rec["vn"][t, l].reshape(shp), Ks[l], Vs[l], t, g.scale)
+            np.testing.assert_array_equal(so.reshape(g.n_seqs, -1), rec["so"][t, l])
+            co = oracle.cross_decode(rec["qc"][t, l].reshape(g.n_streams, g.n_q, g.n_heads, g.head_dim),
+                                     Kc[l], Vc[l], g.scale)
+            np.testing.assert_array_equal(co.reshape(g.n_seqs, -1), rec["co"][t, l])
+
+
+def test_thread_count_does_not_change_bits():
+    r = rng(15)
+    E = r.standard_normal((2, 33, 32))
+    WK = [r.standard_normal((32, 32)) for _ in range(2)]
+    q = r.standard_normal((2, 3, 2, 16))
+    n0 = oracle.get_threads()
+    try:
+        oracle.set_threads(1)
+        K1, V1 = oracle.populate(E, WK, WK, 2, 16)
+        o1 = oracle.cross_decode(q, K1[0], V1[0], 0.25)
+        oracle.set_threads(8)
+        K8, V8 = oracle.populate(E, WK, WK, 2, 16)
+        o8 = oracle.cross_decode(q, K8[0], V8[0], 0.25)
+    finally:
+        oracle.set_threads(n0)
+    np.testing.assert_array_equal(K1, K8)
+    np.testing.assert_array_equal(o1, o8)
