@@ -1,0 +1,347 @@
+#!/usr/bin/env python3
+"""Benchmark: cross-attention projection cache on one MI355X.
+
+One step = one decode window of the workload, i.e. one pass of the whole hot
+path over one batch of synthetic input:
+  populate the projection cache of every decoder layer from E, then
+  for every decode token, for every layer in order:
+      fused self-attention append + attend (cke_selfattn_decode_append)
+      cross-attention over the layer's cache slab (cke_xattn_decode)
+The per-call inputs (queries, new K/V rows) are seeded synthetic tensors,
+resident in device memory before timing starts.
+
+value = decode tokens per second over the timed windows (tokens of all
+sequences, populate included in the time). Kernel durations come from HIP
+events recorded on the launch stream around every call of one instrumented
+window run right after the timed windows, with the same inputs and kernels.
+
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import subprocess
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+
+METRIC = "decode tokens/s (cross+self attn, all layers) + populate TFLOP/s, % roofline"
+HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = {"f32": 157.3, "bf16": 2516.6}
+
+WORKLOAD_TEXT = {
+    "base": "whisper-base cross+self decode: E[1500,512] fp32, 6 layers, 8 heads x 64, "
+            "batch 1, populate + 224 decode steps, self cache capacity 448",
+    "beam": "whisper-base 5-beam decode: shared E[1500,512] fp32 cache, 5 self caches, "
+            "6 layers, 8 heads x 64, populate + 448 decode steps",
+    "large": "large: 16 streams x E[1500,1280] bf16, 32 layers, 20 heads x 64, "
+             "populate + 128 decode steps, bf16 caches, fp32 accumulate",
+    "qformer": "q-former projector cross-attn: 100 blocks x 15 frames, memory width 2048, "
+               "2 layers, 32 heads x 64, 3 queries per block, one pass",
+    "tiny": "tiny: E[64,64] fp32, 1 layer, 2 heads x 32, 8 decode steps",
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--config", default="base", choices=sorted(synth.CONFIGS))
+    ap.add_argument("--mode", default="graph", choices=["graph", "eager"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="approximate CPU time budget of the oracle baseline sample")
+    return ap.parse_args()
+
+
+class Workload:
+    """Device-resident inputs, caches and outputs of one workload."""
+
+    def __init__(self, name, torch, pc):
+        self.torch, self.pc = torch, pc
+        g = self.g = synth.get(name)
+        dev = "cuda:0"
+        self.bf16 = g.dtype == "bf16"
+        wt = synth.workload_tensors(g)
+
+        def dev_f32(a):
+            return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
+
+        def dev_bf16(bits):
+            return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(
+                torch.bfloat16).to(dev)
+
+        if self.bf16:
+            self.E = dev_bf16(wt["E_bits"])
+            self.WK = [dev_bf16(b) for b in wt["WK_bits"]]
+            self.WV = [dev_bf16(b) for b in wt["WV_bits"]]
+        else:
+            self.E = dev_f32(wt["E"])
+            self.WK = [dev_f32(w) for w in wt["WK"]]
+            self.WV = [dev_f32(w) for w in wt["WV"]]
+        del wt
+        cdt = torch.bfloat16 if self.bf16 else torch.float32
+        self.cache = pc.XattnCache(g.n_layers, g.n_streams, g.mem_len, g.d_model, g.n_heads,
+                                   g.head_dim, max_q=g.n_q, dtype=cdt)
+        self.kv = [pc.KVLayer(g.n_seqs, g.n_heads, g.head_dim, g.max_pos, dtype=cdt)
+                   for _ in range(g.n_layers)] if g.n_seqs else []
+        # per-call inputs [steps][L][...]
+        steps, L = g.steps, g.n_layers
+        qc = np.empty((steps, L, g.n_streams, g.n_q, g.n_heads, g.head_dim), np.float32)
+        if g.n_seqs:
+            qs = np.empty((steps, L, g.n_seqs, g.n_heads, g.head_dim), np.float32)
+            kn, vn = np.empty_like(qs), np.empty_like(qs)
+        for t in range(steps):
+            for l in range(L):
+                d = synth.decode_call_inputs(g, t, l)
+                qc[t, l] = d["q_cross"]
+                if g.n_seqs:
+                    qs[t, l], kn[t, l], vn[t, l] = d["q_self"], d["k_new"], d["v_new"]
+        self.qc = dev_f32(qc)
+        self.out_c = torch.empty_like(self.qc)
+        if g.n_seqs:
+            self.qs, self.kn, self.vn = dev_f32(qs), dev_f32(kn), dev_f32(vn)
+            self.out_s = torch.empty_like(self.qs)
+        torch.cuda.synchronize()
+
+    @property
+    def tokens_per_window(self):
+        g = self.g
+        return g.steps * (g.n_seqs if g.n_seqs else g.n_streams * g.n_q)
+
+    def window(self, stream, events=None):
+        """Enqueue one decode window. If events is a dict, record (start, end)
+        event pairs around every call, by kernel family."""
+        g, pc, torch = self.g, self.pc, self.torch
+        ev = events is not None
+
+        def timed(kind, fn):
+            if ev:
+                s = torch.cuda.Event(enable_timing=True)
+                e = torch.cuda.Event(enable_timing=True)
+                s.record(stream)
+                fn()
+                e.record(stream)
+                events.setdefault(kind, []).append((s, e))
+            else:
+                fn()
+
+        timed("populate", lambda: pc.cke_xattn_populate(self.cache, self.E, self.WK, self.WV,
+                                                        stream=stream))
+        for t in range(g.steps):
+            for l in range(g.n_layers):
+                if g.n_seqs:
+                    timed("selfattn", lambda: pc.cke_selfattn_decode_append(
+                        self.qs[t, l], self.kn[t, l], self.vn[t, l], self.kv[l], t, g.scale,
+                        self.out_s[t, l], stream=stream))
+                timed("xattn_decode", lambda: pc.cke_xattn_decode(
+                    self.qc[t, l], self.cache, l, g.scale, self.out_c[t, l], stream=stream))
+
+    # algorithmic work -------------------------------------------------------
+    def elem(self):
+        return 2 if self.bf16 else 4
+
+    def cross_bytes_per_call(self):
+        g = self.g
+        kv = 2 * g.n_streams * g.n_heads * g.mem_len * g.head_dim * self.elem()
+        qo = 2 * g.n_streams * g.n_q * g.n_heads * g.head_dim * 4
+        return kv + qo
+
+    def self_bytes_per_call(self, pos):
+        g = self.g
+        rows = 2 * g.n_seqs * g.n_heads * pos * g.head_dim * self.elem()       # read 0..pos-1
+        new = 2 * g.n_seqs * g.n_heads * g.head_dim * (4 + self.elem())        # k/v in + row out
+        qo = 2 * g.n_seqs * g.n_heads * g.head_dim * 4
+        return rows + new + qo
+
+    def populate_flops(self):
+        g = self.g
+        return 2.0 * g.n_streams * g.mem_len * (2 * g.n_layers * g.d_model) * g.d_model
+
+
+def cpu_baseline(name, budget_s):
+    """The oracle as it stands, on the host's cores, on a bounded sample:
+    populate of the whole cache once, then decode tokens until the budget is
+    used; the window time is populate + steps x the mean token time."""
+    import oracle
+
+    g = synth.get(name)
+    threads = oracle.get_threads()
+    wt = synth.workload_tensors(g)
+    t0 = time.perf_counter()
+    if name == "large":
+        # one stream of the sixteen, scaled x16
+        Kc, Vc = oracle.populate(wt["E"][:1], wt["WK"], wt["WV"], g.n_heads, g.head_dim,
+                                 round_bf16=True)
+        t_pop = (time.perf_counter() - t0) * g.n_streams
+    else:
+        Kc, Vc = oracle.populate(wt["E"], wt["WK"], wt["WV"], g.n_heads, g.head_dim,
+                                 round_bf16=(g.dtype == "bf16"))
+        t_pop = time.perf_counter() - t0
+    del wt
+    S = g.n_seqs if name != "large" else 1
+    Ks = [np.zeros((S, g.n_heads, g.max_pos, g.head_dim)) for _ in range(g.n_layers)] if S else []
+    Vs = [np.zeros_like(k) for k in Ks]
+    t1 = time.perf_counter()
+    n_tok = 0
+    for t in range(g.steps):
+        for l in range(g.n_layers):
+            d = synth.decode_call_inputs(g, t, l)
+            if S:
+                oracle.self_append_attend(d["q_self"][:S], d["k_new"][:S], d["v_new"][:S], Ks[l],
+                                          Vs[l], t, g.scale, round_bf16=(g.dtype == "bf16"))
+            q = d["q_cross"][:1] if name == "large" else d["q_cross"]
+            oracle.cross_decode(q, Kc[l][:1] if name == "large" else Kc[l],
+                                Vc[l][:1] if name == "large" else Vc[l], g.scale)
+        n_tok += 1
+        if time.perf_counter() - t1 > max(1.0, budget_s - t_pop):
+            break
+    t_tok = (time.perf_counter() - t1) / n_tok
+    if name == "large":
+        t_tok *= g.n_streams
+    per_window = t_pop + g.steps * t_tok
+    tokens = g.steps * (g.n_seqs if g.n_seqs else g.n_streams * g.n_q)
+    sample = ("oracle populate of the %s cache%s, then %d of %d decode steps (all layers, "
+              "self + cross); window time = populate + %d x mean step time" %
+              (name, " for 1 of 16 streams x16" if name == "large" else "", n_tok, g.steps,
+               g.steps))
+    return {"value": tokens / per_window, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": sample, "populate_s": t_pop, "step_s": t_tok,
+            "host_cpu": _host_cpu()}
+
+
+def _host_cpu():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _git_sha():
+    try:
+        return subprocess.run(["git", "rev-parse", "--short", "HEAD"], cwd=ROOT,
+                              capture_output=True, text=True, timeout=5).stdout.strip() or None
+    except Exception:
+        return None
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import projection_cache_amd as pc
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    w = Workload(args.config, torch, pc)
+    g = w.g
+
+    stream = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    if args.mode == "graph":
+        with torch.cuda.stream(stream):
+            w.window(stream)           # warm the kernels once outside capture
+        stream.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            w.window(torch.cuda.current_stream())
+        torch.cuda.synchronize()
+
+        def run():
+            with torch.cuda.stream(stream):
+                graph.replay()
+    else:
+        def run():
+            w.window(stream)
+
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        run()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed / args.steps * 1e3
+    tok_s = w.tokens_per_window * args.steps / elapsed
+
+    # instrumented window: HIP events around every call on the launch stream
+    events = {}
+    w.window(stream, events)
+    torch.cuda.synchronize()
+    dur = {k: [s.elapsed_time(e) * 1e-3 for s, e in v] for k, v in events.items()}
+    avg = {k: float(np.mean(v)) for k, v in dur.items()}
+
+    cross_b = w.cross_bytes_per_call()
+    cross_gbs = cross_b / avg["xattn_decode"] / 1e9
+    kernels = {
+        "xattn_decode": {"avg_us": avg["xattn_decode"] * 1e6, "calls_per_step": len(dur["xattn_decode"]),
+                         "bytes_per_call": cross_b, "GB_s": cross_gbs},
+        "populate": {"avg_us": avg["populate"] * 1e6,
+                     "tflops": w.populate_flops() / avg["populate"] / 1e12},
+    }
+    if "selfattn" in dur:
+        sb = [w.self_bytes_per_call(t) for t in range(g.steps) for _ in range(g.n_layers)]
+        kernels["selfattn"] = {"avg_us": avg["selfattn"] * 1e6,
+                               "calls_per_step": len(dur["selfattn"]),
+                               "bytes_per_call_mean": float(np.mean(sb)),
+                               "GB_s": float(np.sum(sb) / np.sum(dur["selfattn"]) / 1e9)}
+    share = {k: float(np.sum(v)) for k, v in dur.items()}
+    dominant = max(share, key=share.get)
+    pop_tflops = kernels["populate"]["tflops"]
+    result = {
+        "metric": METRIC,
+        "value": tok_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.bf16 else "f32",
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD_TEXT[args.config], "name": args.config,
+                   "tokens_per_step": w.tokens_per_window, "decode_steps": g.steps,
+                   "layers": g.n_layers, "mode": args.mode},
+        "roofline": {"bound": "hbm", "kernel": "xattn_decode", "achieved": cross_gbs,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": cross_gbs / HBM_PEAK_GBS,
+                     "traffic": None,
+                     "bytes_per_launch": cross_b, "avg_launch_us": avg["xattn_decode"] * 1e6},
+        "populate": {"tflops": pop_tflops, "peak_tflops": MFMA_PEAK_TFLOPS[g.dtype],
+                     "frac": pop_tflops / MFMA_PEAK_TFLOPS[g.dtype],
+                     "mfma": "v_mfma_f32_32x32x16_bf16" if w.bf16 else "v_mfma_f32_32x32x2_f32"},
+        "kernels": kernels,
+        "time_share": {k: v / sum(share.values()) for k, v in share.items()},
+        "dominant_kernel": dominant,
+        "gpu": torch.cuda.get_device_name(0),
+        "git": _git_sha(),
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(args.config, args.cpu_seconds)
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,170 @@
+/*
+ * cke_xattn.h -- C ABI of libcke_xattn.so: encoder-decoder cross-attention over
+ * a projection cache, and one-token self-attention over an explicit KV cache,
+ * on one AMD Instinct MI355X (gfx950).
+ *
+ * Operations and where the pages define them:
+ *   populate  C-Kernel-Engine, "Whisper: Trace One Encoder Tensor into Every
+ *             Decoder Layer", section "The concept": every decoder layer l
+ *             projects the one encoder memory E with its own weights,
+ *             K_l = E x WK_l and V_l = E x WV_l. Section "View 2" and the
+ *             circuit's projection_cache declaration: the result is kept
+ *             layer-major, head-major, one slab per layer.
+ *   ready     same page, "View 3": installing new encoder memory clears a
+ *             ready flag, and decode refuses with -2 until prefill has
+ *             repopulated the cache.
+ *   decode    same page, "View 2": one query token of layer l attends over
+ *             all key_tokens rows of slab l (not causal) with an explicit
+ *             scale.
+ *   self      "Recurrence as feeds" (topos), "What it opened": the self-
+ *             attention cache is an ordinary input and output; the new row is
+ *             written with scatter, then the token attends.
+ *
+ * Conventions shared by every call
+ *   - All tensors are device memory owned by the caller. The library never
+ *     allocates or frees device memory and keeps no pointer beyond what a
+ *     cache handle records at creation.
+ *   - Row-major, innermost index last. Weights are [d_model][H*D] in the
+ *     y = x . W orientation; head h owns columns [h*D, (h+1)*D).
+ *   - Cache layout (K and V are separate regions of identical shape):
+ *     [L][B][H][T][D], elements of cache_dtype. Layer l's slab starts
+ *     l*B*H*T*D elements into the region (for Whisper Base, fp32, layer 5
+ *     starts 15,360,000 bytes in).
+ *   - Every compute call is asynchronous on the given HIP stream (a
+ *     hipStream_t passed as void*; NULL is the default stream). Status codes
+ *     report host-side validation and launch errors only.
+ *   - Calls that share one cache handle (its workspace) must be ordered on
+ *     one stream; concurrent calls on one handle race.
+ *   - On a non-OK status nothing was launched and no output was written;
+ *     cke_last_error() returns a message (thread-local).
+ */
+#ifndef CKE_XATTN_H
+#define CKE_XATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. CKE_ENOTREADY is the -2 refusal of a stale cache. */
+enum {
+    CKE_OK = 0,
+    CKE_EINVAL = -1,     /* null pointer, bad geometry, unsupported dtype mix */
+    CKE_ENOTREADY = -2,  /* decode on a cache that is not populated */
+    CKE_ERANGE = -3,     /* layer, position or query count out of range */
+    CKE_EDEVICE = -4     /* the HIP runtime reported an error at launch */
+};
+
+/* Element types. */
+enum { CKE_F32 = 0, CKE_BF16 = 1 };
+
+/* Geometry of one projection cache. Fail-closed: mem_len must be positive and
+ * n_heads*head_dim must equal d_model (C-Kernel-Engine page, "View 3": both
+ * are hard errors, not defaults). head_dim must be 32, 64 or 128 and d_model
+ * a multiple of 32. */
+typedef struct cke_xattn_geom {
+    int32_t n_layers;    /* L, >= 1 */
+    int32_t n_streams;   /* B: independent encoder memories, >= 1 */
+    int32_t mem_len;     /* T: encoder memory rows per stream, >= 1 */
+    int32_t d_model;     /* encoder width = n_heads * head_dim */
+    int32_t n_heads;     /* H */
+    int32_t head_dim;    /* D */
+    int32_t max_q;       /* largest n_q a decode call may pass, 1..8 */
+    int32_t cache_dtype; /* CKE_F32 or CKE_BF16 */
+} cke_xattn_geom;
+
+/* Opaque host-side handle: geometry, the caller's K/V/workspace pointers and
+ * the ready flag. Not thread-safe; one handle per cache. */
+typedef struct cke_xattn_cache cke_xattn_cache;
+
+/* Bytes of ONE of the two cache regions (K or V): L*B*H*T*D*elem.
+ * Returns 0 for an invalid geometry. */
+size_t cke_xattn_region_bytes(const cke_xattn_geom* g);
+
+/* Byte offset of layer `layer`'s slab inside a region. Returns (size_t)-1 for
+ * an invalid geometry or layer. */
+size_t cke_xattn_layer_offset_bytes(const cke_xattn_geom* g, int layer);
+
+/* Bytes of device workspace a cache needs for split-key partial results and
+ * merge counters (fp32 partials [B][max_q][H][splits][D+2] plus one 32-bit
+ * counter per (stream, head)). Returns 0 for an invalid geometry. */
+size_t cke_xattn_workspace_bytes(const cke_xattn_geom* g);
+
+/* Number of key splits a decode call of this geometry uses (fixed per
+ * geometry, so results are run-to-run deterministic). 0 if invalid. */
+int cke_xattn_num_splits(const cke_xattn_geom* g);
+
+/* Create a handle over caller-allocated device regions k_dev, v_dev (each
+ * cke_xattn_region_bytes) and ws_dev (cke_xattn_workspace_bytes, 256-byte
+ * aligned). The workspace counters are cleared by every populate call, so
+ * no initialisation is needed. The handle starts NOT ready. */
+int cke_xattn_cache_create(const cke_xattn_geom* g, void* k_dev, void* v_dev,
+                           void* ws_dev, cke_xattn_cache** out);
+
+/* Free the handle (host memory only). NULL is accepted. */
+void cke_xattn_cache_destroy(cke_xattn_cache* c);
+
+/* New encoder memory is about to be installed: clear the ready flag. The
+ * cache contents are left as they are. */
+int cke_xattn_invalidate(cke_xattn_cache* c);
+
+/* 1 if populated and not invalidated since, 0 otherwise (or for NULL). */
+int cke_xattn_is_ready(const cke_xattn_cache* c);
+
+/* Prefill: fill every layer's K and V slab from encoder memory E.
+ *   E   device, [B][T][d_model], e_dtype
+ *   WK  HOST array of L device pointers, each [d_model][H*D], w_dtype
+ *   WV  likewise
+ * Supported (e_dtype, w_dtype, cache_dtype): (F32, F32, F32) -- fp32
+ * products, fp32 accumulation on the matrix cores -- and (BF16, BF16, BF16)
+ * -- bf16 products, fp32 accumulation, result rounded to nearest-even bf16.
+ * Sets the ready flag once the work is enqueued. */
+int cke_xattn_populate(cke_xattn_cache* c, const void* E, int e_dtype,
+                       const void* const* WK, const void* const* WV,
+                       int w_dtype, void* stream);
+
+/* Cross-attention decode at one layer:
+ *   out[b][i][h][:] = sum_t softmax_t(scale * q[b][i][h].K_l[b][h][t]) V_l[b][h][t]
+ * over all T rows (no mask).
+ *   q, out  device fp32 [B][n_q][H][D] (out must not alias q)
+ *   n_q     0..max_q queries per stream (0 is a no-op); queries of one stream
+ *           share every K/V read
+ * Returns CKE_ENOTREADY if the cache is not populated. */
+int cke_xattn_decode(const float* q, int n_q, const cke_xattn_cache* c,
+                     int layer, float scale, float* out, void* stream);
+
+/* One layer's self-attention KV cache, caller-owned: k and v are device
+ * [n_seqs][n_heads][max_pos][head_dim] of dtype (CKE_F32 or CKE_BF16). */
+typedef struct cke_kv_layer {
+    void* k;
+    void* v;
+    int32_t n_seqs;      /* S */
+    int32_t n_heads;     /* H */
+    int32_t head_dim;    /* D: 32, 64 or 128 */
+    int32_t max_pos;     /* capacity in rows */
+    int32_t dtype;       /* CKE_F32 or CKE_BF16 */
+} cke_kv_layer;
+
+/* Fused scatter-append + causal attend for one token per sequence:
+ *   row pos of kv->k, kv->v  <-  k_new, v_new   (rounded to bf16 if dtype is)
+ *   out[s][h][:] = sum_{t<=pos} softmax_t(scale * q[s][h].K[s][h][t]) V[s][h][t]
+ * reading the stored (rounded) values. Rows > pos are never read or written.
+ *   q, k_new, v_new, out  device fp32 [S][H][D]
+ *   pos                   0 <= pos < max_pos, else CKE_ERANGE */
+int cke_selfattn_decode_append(const float* q, const float* k_new,
+                               const float* v_new, const cke_kv_layer* kv,
+                               int pos, float scale, float* out, void* stream);
+
+/* Message for the last non-OK status returned on this thread. */
+const char* cke_last_error(void);
+
+/* Library version string. */
+const char* cke_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CKE_XATTN_H */

@@ -1,0 +1,269 @@
+"""Python binding of libcke_xattn.so (ctypes, argument marshalling only).
+
+Every computation runs in the HIP kernels behind the C ABI declared in
+include/cke_xattn.h; this module turns torch tensors into device pointers,
+picks the current HIP stream and turns non-OK status codes into exceptions.
+PyTorch serves only as the device-memory and stream provider. There is no
+fallback: if the shared library is missing, importing this package fails.
+
+Function names mirror the C entry points:
+  cke_xattn_populate(cache, E, WK, WV)         prefill the projection cache
+  cke_xattn_decode(q, cache, layer, scale, out) cross-attention at one layer
+  cke_selfattn_decode_append(q, k_new, v_new, kv, pos, scale, out)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libcke_xattn.so")
+
+CKE_OK, CKE_EINVAL, CKE_ENOTREADY, CKE_ERANGE, CKE_EDEVICE = 0, -1, -2, -3, -4
+CKE_F32, CKE_BF16 = 0, 1
+_DTYPES = {torch.float32: CKE_F32, torch.bfloat16: CKE_BF16}
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        "libcke_xattn.so is not built (%s); run projection_cache_amd/_build.py "
+        "or __graft_entry__.build() first" % LIB_PATH)
+
+
+class cke_xattn_geom(ctypes.Structure):
+    _fields_ = [("n_layers", ctypes.c_int32), ("n_streams", ctypes.c_int32),
+                ("mem_len", ctypes.c_int32), ("d_model", ctypes.c_int32),
+                ("n_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("max_q", ctypes.c_int32), ("cache_dtype", ctypes.c_int32)]
+
+
+class cke_kv_layer(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("n_seqs", ctypes.c_int32), ("n_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("max_pos", ctypes.c_int32),
+                ("dtype", ctypes.c_int32)]
+
+
+_P, _I, _F, _SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+_lib = ctypes.CDLL(LIB_PATH)
+_lib.cke_last_error.restype = ctypes.c_char_p
+_lib.cke_version.restype = ctypes.c_char_p
+_lib.cke_xattn_region_bytes.restype = _SZ
+_lib.cke_xattn_region_bytes.argtypes = [ctypes.POINTER(cke_xattn_geom)]
+_lib.cke_xattn_layer_offset_bytes.restype = _SZ
+_lib.cke_xattn_layer_offset_bytes.argtypes = [ctypes.POINTER(cke_xattn_geom), _I]
+_lib.cke_xattn_workspace_bytes.restype = _SZ
+_lib.cke_xattn_workspace_bytes.argtypes = [ctypes.POINTER(cke_xattn_geom)]
+_lib.cke_xattn_num_splits.restype = _I
+_lib.cke_xattn_num_splits.argtypes = [ctypes.POINTER(cke_xattn_geom)]
+_lib.cke_xattn_cache_create.restype = _I
+_lib.cke_xattn_cache_create.argtypes = [ctypes.POINTER(cke_xattn_geom), _P, _P, _P,
+                                        ctypes.POINTER(_P)]
+_lib.cke_xattn_cache_destroy.restype = None
+_lib.cke_xattn_cache_destroy.argtypes = [_P]
+_lib.cke_xattn_invalidate.restype = _I
+_lib.cke_xattn_invalidate.argtypes = [_P]
+_lib.cke_xattn_is_ready.restype = _I
+_lib.cke_xattn_is_ready.argtypes = [_P]
+_lib.cke_xattn_populate.restype = _I
+_lib.cke_xattn_populate.argtypes = [_P, _P, _I, ctypes.POINTER(_P), ctypes.POINTER(_P), _I, _P]
+_lib.cke_xattn_decode.restype = _I
+_lib.cke_xattn_decode.argtypes = [_P, _I, _P, _I, _F, _P, _P]
+_lib.cke_selfattn_decode_append.restype = _I
+_lib.cke_selfattn_decode_append.argtypes = [_P, _P, _P, ctypes.POINTER(cke_kv_layer), _I, _F,
+                                            _P, _P]
+
+EXPORTED = ["cke_xattn_region_bytes", "cke_xattn_layer_offset_bytes",
+            "cke_xattn_workspace_bytes", "cke_xattn_num_splits", "cke_xattn_cache_create",
+            "cke_xattn_cache_destroy", "cke_xattn_invalidate", "cke_xattn_is_ready",
+            "cke_xattn_populate", "cke_xattn_decode", "cke_selfattn_decode_append",
+            "cke_last_error", "cke_version"]
+
+
+class CkeError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__("%s (status %d)" % (msg, code))
+        self.code = code
+
+
+def lib():
+    return _lib
+
+
+def cke_last_error() -> str:
+    return _lib.cke_last_error().decode()
+
+
+def cke_version() -> str:
+    return _lib.cke_version().decode()
+
+
+def _check(rc: int) -> None:
+    if rc != CKE_OK:
+        raise CkeError(rc, cke_last_error())
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    if isinstance(x, torch.Tensor):
+        if x.numel() and not x.is_contiguous():
+            raise ValueError("tensor must be contiguous")
+        return x.data_ptr()
+    return int(x)
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def make_geom(n_layers, n_streams, mem_len, d_model, n_heads, head_dim, max_q=1,
+              cache_dtype=CKE_F32) -> cke_xattn_geom:
+    return cke_xattn_geom(n_layers, n_streams, mem_len, d_model, n_heads, head_dim, max_q,
+                          cache_dtype)
+
+
+def cke_xattn_region_bytes(g: cke_xattn_geom) -> int:
+    return int(_lib.cke_xattn_region_bytes(ctypes.byref(g)))
+
+
+def cke_xattn_layer_offset_bytes(g: cke_xattn_geom, layer: int) -> int:
+    r = int(_lib.cke_xattn_layer_offset_bytes(ctypes.byref(g), layer))
+    if r == ctypes.c_size_t(-1).value:
+        raise CkeError(CKE_ERANGE, cke_last_error())
+    return r
+
+
+def cke_xattn_workspace_bytes(g: cke_xattn_geom) -> int:
+    return int(_lib.cke_xattn_workspace_bytes(ctypes.byref(g)))
+
+
+def cke_xattn_num_splits(g: cke_xattn_geom) -> int:
+    return int(_lib.cke_xattn_num_splits(ctypes.byref(g)))
+
+
+def cke_xattn_cache_create(g: cke_xattn_geom, k_dev, v_dev, ws_dev) -> int:
+    h = _P()
+    _check(_lib.cke_xattn_cache_create(ctypes.byref(g), _ptr(k_dev), _ptr(v_dev), _ptr(ws_dev),
+                                       ctypes.byref(h)))
+    return h.value
+
+
+def cke_xattn_cache_destroy(handle) -> None:
+    _lib.cke_xattn_cache_destroy(handle)
+
+
+def cke_xattn_invalidate(handle) -> None:
+    _check(_lib.cke_xattn_invalidate(handle))
+
+
+def cke_xattn_is_ready(handle) -> bool:
+    return bool(_lib.cke_xattn_is_ready(handle))
+
+
+def _handle(cache):
+    return cache.handle if isinstance(cache, XattnCache) else cache
+
+
+def cke_xattn_populate(cache, E, WK, WV, stream=None, e_dtype=None, w_dtype=None) -> None:
+    """Prefill every layer's K/V slab from encoder memory E [B][T][d_model];
+    WK and WV are sequences of L weight tensors [d_model][H*D]."""
+    if e_dtype is None:
+        e_dtype = _DTYPES[E.dtype]
+    if w_dtype is None:
+        w_dtype = _DTYPES[WK[0].dtype]
+    arr = _P * len(WK)
+    wk = arr(*[_ptr(w) for w in WK])
+    wv = arr(*[_ptr(w) for w in WV])
+    _check(_lib.cke_xattn_populate(_handle(cache), _ptr(E), e_dtype, wk, wv, w_dtype,
+                                   _stream(stream)))
+
+
+def cke_xattn_decode(q, cache, layer: int, scale: float, out, n_q=None, stream=None) -> None:
+    """Cross-attention of q [B][n_q][H][D] (fp32) against layer `layer` of the
+    projection cache, into out (same shape)."""
+    if n_q is None:
+        n_q = q.shape[1] if isinstance(q, torch.Tensor) and q.dim() == 4 else 1
+    _check(_lib.cke_xattn_decode(_ptr(q), int(n_q), _handle(cache), int(layer), float(scale),
+                                 _ptr(out), _stream(stream)))
+
+
+def cke_selfattn_decode_append(q, k_new, v_new, kv, pos: int, scale: float, out,
+                               stream=None) -> None:
+    """Scatter k_new/v_new [S][H][D] into row pos of kv and attend over rows
+    0..pos. kv is a KVLayer or a cke_kv_layer."""
+    desc = kv.desc if isinstance(kv, KVLayer) else kv
+    _check(_lib.cke_selfattn_decode_append(_ptr(q), _ptr(k_new), _ptr(v_new), ctypes.byref(desc),
+                                           int(pos), float(scale), _ptr(out), _stream(stream)))
+
+
+class XattnCache:
+    """A projection cache whose K, V and workspace are torch device tensors.
+
+    The tensors are plain device memory handed to the library by pointer; the
+    handle holds the geometry and the ready flag."""
+
+    def __init__(self, n_layers, n_streams, mem_len, d_model, n_heads, head_dim, max_q=1,
+                 dtype=torch.float32, device="cuda"):
+        self.geom = make_geom(n_layers, n_streams, mem_len, d_model, n_heads, head_dim, max_q,
+                              _DTYPES[dtype])
+        nbytes = cke_xattn_region_bytes(self.geom)
+        if nbytes == 0:
+            raise CkeError(CKE_EINVAL, cke_last_error())
+        shape = (n_layers, n_streams, n_heads, mem_len, head_dim)
+        self.k = torch.empty(shape, dtype=dtype, device=device)
+        self.v = torch.empty(shape, dtype=dtype, device=device)
+        ws_bytes = cke_xattn_workspace_bytes(self.geom)
+        self.ws = torch.zeros((ws_bytes + 255) // 256 * 64, dtype=torch.float32, device=device)
+        self.handle = cke_xattn_cache_create(self.geom, self.k, self.v, self.ws)
+        self.n_splits = cke_xattn_num_splits(self.geom)
+
+    def populate(self, E, WK, WV, stream=None):
+        cke_xattn_populate(self, E, WK, WV, stream)
+
+    def decode(self, q, layer, scale, out=None, stream=None):
+        if out is None:
+            out = torch.empty_like(q)
+        cke_xattn_decode(q, self, layer, scale, out, stream=stream)
+        return out
+
+    def invalidate(self):
+        cke_xattn_invalidate(self.handle)
+
+    @property
+    def ready(self) -> bool:
+        return cke_xattn_is_ready(self.handle)
+
+    def close(self):
+        if getattr(self, "handle", None):
+            cke_xattn_cache_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class KVLayer:
+    """One layer's self-attention cache [S][H][max_pos][D] as torch tensors."""
+
+    def __init__(self, n_seqs, n_heads, head_dim, max_pos, dtype=torch.float32, device="cuda",
+                 k=None, v=None):
+        shape = (n_seqs, n_heads, max_pos, head_dim)
+        self.k = torch.zeros(shape, dtype=dtype, device=device) if k is None else k
+        self.v = torch.zeros(shape, dtype=dtype, device=device) if v is None else v
+        self.desc = cke_kv_layer(self.k.data_ptr(), self.v.data_ptr(), n_seqs, n_heads, head_dim,
+                                 max_pos, _DTYPES[dtype])
+
+    def append_attend(self, q, k_new, v_new, pos, scale, out=None, stream=None):
+        if out is None:
+            out = torch.empty_like(q)
+        cke_selfattn_decode_append(q, k_new, v_new, self, pos, scale, out, stream)
+        return out

@@ -1,0 +1,293 @@
+// C ABI of libcke_xattn.so: host-side validation, the cache handle with its
+// ready flag, launch planning and error reporting. Kernels live in
+// populate.hip and attn_decode.hip.
+//
+// The ready flag follows C-Kernel-Engine, "Whisper: Trace One Encoder Tensor
+// into Every Decoder Layer", "View 3": new encoder memory clears it, decode
+// refuses with -2 until prefill has repopulated the cache. Geometry errors are
+// fail-closed (same section): a non-positive encoder memory length or
+// num_heads * head_dim != embed_dim is an error, never a default.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+
+#include "../../include/cke_xattn.h"
+#include "cke_internal.h"
+
+struct cke_xattn_cache {
+    cke_xattn_geom g;
+    void* k;
+    void* v;
+    void* ws;
+    int ready;
+    int nsplit;
+    int chunk;
+};
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+int elem_bytes(int dtype) { return dtype == CKE_BF16 ? 2 : 4; }
+
+bool dtype_ok(int dtype) { return dtype == CKE_F32 || dtype == CKE_BF16; }
+
+bool head_dim_ok(int D) { return D == 32 || D == 64 || D == 128; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Validate a geometry; returns CKE_OK or an error (message set).
+int check_geom(const cke_xattn_geom* g) {
+    if (!g) return fail(CKE_EINVAL, "geometry is NULL");
+    if (g->mem_len <= 0)
+        return fail(CKE_EINVAL, "encoder memory length must be positive (got %d)", g->mem_len);
+    if (g->n_layers < 1 || g->n_layers > cke::kMaxLayers)
+        return fail(CKE_EINVAL, "n_layers must be in [1, %d] (got %d)", cke::kMaxLayers, g->n_layers);
+    if (g->n_streams < 1 || g->n_streams > 65535)
+        return fail(CKE_EINVAL, "n_streams must be in [1, 65535] (got %d)", g->n_streams);
+    if (g->n_heads < 1 || g->n_heads > 65535)
+        return fail(CKE_EINVAL, "n_heads must be in [1, 65535] (got %d)", g->n_heads);
+    if (!head_dim_ok(g->head_dim))
+        return fail(CKE_EINVAL, "head_dim must be 32, 64 or 128 (got %d)", g->head_dim);
+    if ((long long)g->n_heads * g->head_dim != g->d_model)
+        return fail(CKE_EINVAL, "num_heads * head_dim (%d * %d) must equal d_model (%d)",
+                    g->n_heads, g->head_dim, g->d_model);
+    if (g->d_model % 32 != 0)
+        return fail(CKE_EINVAL, "d_model must be a multiple of 32 (got %d)", g->d_model);
+    if (g->max_q < 1 || g->max_q > 8) return fail(CKE_EINVAL, "max_q must be in [1, 8] (got %d)", g->max_q);
+    if (!dtype_ok(g->cache_dtype)) return fail(CKE_EINVAL, "unknown cache dtype %d", g->cache_dtype);
+    const long long rows = (long long)g->n_streams * g->mem_len;
+    if (rows > (1ll << 31) - 1) return fail(CKE_EINVAL, "n_streams * mem_len too large");
+    const long long grid_y = 2ll * g->n_layers * g->d_model / 32;
+    if (grid_y > 65535) return fail(CKE_EINVAL, "2 * n_layers * d_model too large");
+    return CKE_OK;
+}
+
+size_t region_elems(const cke_xattn_geom* g) {
+    return (size_t)g->n_layers * g->n_streams * g->n_heads * (size_t)g->mem_len * g->head_dim;
+}
+
+// Split of the T memory rows of one (stream, head) across workgroups. Fixed
+// per geometry so that decode results are reproducible run to run. Aims for
+// about 1024 workgroups (4 per compute unit) but never fewer rows per
+// workgroup than one pass of its waves.
+void split_plan(const cke_xattn_geom* g, int* nsplit, int* chunk) {
+    const int kpp = cke::cross_keys_per_pass(g->head_dim, elem_bytes(g->cache_dtype));
+    const long long bh = (long long)g->n_streams * g->n_heads;
+    const int max_by_rows = (g->mem_len + kpp - 1) / kpp;
+    long long want = (1024 + bh - 1) / bh;
+    if (want > 64) want = 64;
+    int s = (int)(want < max_by_rows ? want : max_by_rows);
+    if (s < 1) s = 1;
+    int c = (g->mem_len + s - 1) / s;
+    c = ((c + kpp - 1) / kpp) * kpp;
+    *chunk = c;
+    *nsplit = (g->mem_len + c - 1) / c;
+}
+
+constexpr size_t kAlign = 256;
+
+size_t counters_bytes(const cke_xattn_geom* g) {
+    const size_t n = (size_t)g->n_streams * g->n_heads * sizeof(unsigned);
+    return (n + kAlign - 1) / kAlign * kAlign;
+}
+
+size_t partials_bytes(const cke_xattn_geom* g, int nsplit) {
+    return (size_t)g->n_streams * g->max_q * g->n_heads * (size_t)nsplit * (g->head_dim + 2) *
+           sizeof(float);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* cke_last_error(void) { return g_err; }
+
+const char* cke_version(void) { return "cke_xattn 0.1 gfx950"; }
+
+size_t cke_xattn_region_bytes(const cke_xattn_geom* g) {
+    if (check_geom(g) != CKE_OK) return 0;
+    return region_elems(g) * elem_bytes(g->cache_dtype);
+}
+
+size_t cke_xattn_layer_offset_bytes(const cke_xattn_geom* g, int layer) {
+    if (check_geom(g) != CKE_OK) return (size_t)-1;
+    if (layer < 0 || layer >= g->n_layers) {
+        fail(CKE_ERANGE, "layer %d outside [0, %d)", layer, g->n_layers);
+        return (size_t)-1;
+    }
+    return region_elems(g) / g->n_layers * layer * elem_bytes(g->cache_dtype);
+}
+
+int cke_xattn_num_splits(const cke_xattn_geom* g) {
+    if (check_geom(g) != CKE_OK) return 0;
+    int s, c;
+    split_plan(g, &s, &c);
+    return s;
+}
+
+size_t cke_xattn_workspace_bytes(const cke_xattn_geom* g) {
+    if (check_geom(g) != CKE_OK) return 0;
+    int s, c;
+    split_plan(g, &s, &c);
+    return counters_bytes(g) + partials_bytes(g, s);
+}
+
+int cke_xattn_cache_create(const cke_xattn_geom* g, void* k_dev, void* v_dev, void* ws_dev,
+                           cke_xattn_cache** out) {
+    if (!out) return fail(CKE_EINVAL, "out handle pointer is NULL");
+    *out = nullptr;
+    int rc = check_geom(g);
+    if (rc != CKE_OK) return rc;
+    if (!k_dev || !v_dev || !ws_dev) return fail(CKE_EINVAL, "k, v and workspace pointers must be non-NULL");
+    if (!aligned16(k_dev) || !aligned16(v_dev))
+        return fail(CKE_EINVAL, "cache regions must be 16-byte aligned");
+    if ((reinterpret_cast<uintptr_t>(ws_dev) & (kAlign - 1)) != 0)
+        return fail(CKE_EINVAL, "workspace must be 256-byte aligned");
+    cke_xattn_cache* c = new (std::nothrow) cke_xattn_cache;
+    if (!c) return fail(CKE_EINVAL, "out of host memory");
+    c->g = *g;
+    c->k = k_dev;
+    c->v = v_dev;
+    c->ws = ws_dev;
+    c->ready = 0;
+    split_plan(g, &c->nsplit, &c->chunk);
+    *out = c;
+    return CKE_OK;
+}
+
+void cke_xattn_cache_destroy(cke_xattn_cache* c) { delete c; }
+
+int cke_xattn_invalidate(cke_xattn_cache* c) {
+    if (!c) return fail(CKE_EINVAL, "cache handle is NULL");
+    c->ready = 0;
+    return CKE_OK;
+}
+
+int cke_xattn_is_ready(const cke_xattn_cache* c) { return c ? c->ready : 0; }
+
+int cke_xattn_populate(cke_xattn_cache* c, const void* E, int e_dtype, const void* const* WK,
+                       const void* const* WV, int w_dtype, void* stream) {
+    if (!c) return fail(CKE_EINVAL, "cache handle is NULL");
+    if (!E || !WK || !WV) return fail(CKE_EINVAL, "E, WK and WV must be non-NULL");
+    const cke_xattn_geom& g = c->g;
+    const bool f32 = e_dtype == CKE_F32 && w_dtype == CKE_F32 && g.cache_dtype == CKE_F32;
+    const bool bf16 = e_dtype == CKE_BF16 && w_dtype == CKE_BF16 && g.cache_dtype == CKE_BF16;
+    if (!f32 && !bf16)
+        return fail(CKE_EINVAL,
+                    "unsupported dtypes (E %d, W %d, cache %d): need all fp32 or all bf16",
+                    e_dtype, w_dtype, g.cache_dtype);
+    if (!aligned16(E)) return fail(CKE_EINVAL, "E must be 16-byte aligned");
+    cke::PopulateLaunch a;
+    std::memset(&a, 0, sizeof(a));
+    for (int l = 0; l < g.n_layers; ++l) {
+        if (!WK[l] || !WV[l]) return fail(CKE_EINVAL, "weight pointer of layer %d is NULL", l);
+        if (!aligned16(WK[l]) || !aligned16(WV[l]))
+            return fail(CKE_EINVAL, "weights of layer %d must be 16-byte aligned", l);
+        a.wt.w[l] = WK[l];
+        a.wt.w[g.n_layers + l] = WV[l];
+    }
+    a.E = E;
+    a.Kc = c->k;
+    a.Vc = c->v;
+    a.counters = static_cast<unsigned*>(c->ws);
+    a.n_counters = g.n_streams * g.n_heads;
+    a.L = g.n_layers;
+    a.B = g.n_streams;
+    a.T = g.mem_len;
+    a.dm = g.d_model;
+    a.H = g.n_heads;
+    a.D = g.head_dim;
+    a.bf16 = bf16;
+    c->ready = 0;
+    hipError_t e = cke::launch_populate(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(CKE_EDEVICE, "populate launch failed: %s", hipGetErrorString(e));
+    c->ready = 1;
+    return CKE_OK;
+}
+
+int cke_xattn_decode(const float* q, int n_q, const cke_xattn_cache* c, int layer, float scale,
+                     float* out, void* stream) {
+    if (!c) return fail(CKE_EINVAL, "cache handle is NULL");
+    const cke_xattn_geom& g = c->g;
+    if (layer < 0 || layer >= g.n_layers)
+        return fail(CKE_ERANGE, "layer %d outside [0, %d)", layer, g.n_layers);
+    if (n_q < 0 || n_q > g.max_q) return fail(CKE_ERANGE, "n_q %d outside [0, %d]", n_q, g.max_q);
+    if (!c->ready)
+        return fail(CKE_ENOTREADY, "projection cache is not populated for the current encoder memory");
+    if (n_q == 0) return CKE_OK;
+    if (!q || !out) return fail(CKE_EINVAL, "q and out must be non-NULL");
+    if (!aligned16(q) || !aligned16(out)) return fail(CKE_EINVAL, "q and out must be 16-byte aligned");
+    if (!(scale == scale)) return fail(CKE_EINVAL, "scale is NaN");
+    const size_t off = region_elems(&g) / g.n_layers * layer * elem_bytes(g.cache_dtype);
+    cke::XattnLaunch a;
+    a.q = q;
+    a.K = static_cast<const char*>(c->k) + off;
+    a.V = static_cast<const char*>(c->v) + off;
+    a.out = out;
+    a.counters = static_cast<unsigned*>(c->ws);
+    a.part = reinterpret_cast<float*>(static_cast<char*>(c->ws) + counters_bytes(&g));
+    a.B = g.n_streams;
+    a.H = g.n_heads;
+    a.T = g.mem_len;
+    a.D = g.head_dim;
+    a.nq = n_q;
+    a.max_q = g.max_q;
+    a.nsplit = c->nsplit;
+    a.chunk = c->chunk;
+    a.scale = scale;
+    a.bf16 = g.cache_dtype == CKE_BF16;
+    hipError_t e = cke::launch_xattn_decode(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(CKE_EDEVICE, "decode launch failed: %s", hipGetErrorString(e));
+    return CKE_OK;
+}
+
+int cke_selfattn_decode_append(const float* q, const float* k_new, const float* v_new,
+                               const cke_kv_layer* kv, int pos, float scale, float* out,
+                               void* stream) {
+    if (!kv) return fail(CKE_EINVAL, "kv layer descriptor is NULL");
+    if (!q || !k_new || !v_new || !out || !kv->k || !kv->v)
+        return fail(CKE_EINVAL, "q, k_new, v_new, out, kv->k and kv->v must be non-NULL");
+    if (kv->n_seqs < 1 || kv->n_heads < 1 || kv->max_pos < 1)
+        return fail(CKE_EINVAL, "n_seqs, n_heads and max_pos must be >= 1");
+    if (kv->n_heads > 65535 || kv->n_seqs > 65535) return fail(CKE_EINVAL, "n_seqs or n_heads too large");
+    if (!head_dim_ok(kv->head_dim))
+        return fail(CKE_EINVAL, "head_dim must be 32, 64 or 128 (got %d)", kv->head_dim);
+    if (!dtype_ok(kv->dtype)) return fail(CKE_EINVAL, "unknown kv dtype %d", kv->dtype);
+    if (pos < 0 || pos >= kv->max_pos)
+        return fail(CKE_ERANGE, "pos %d outside [0, %d)", pos, kv->max_pos);
+    if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(out) ||
+        !aligned16(kv->k) || !aligned16(kv->v))
+        return fail(CKE_EINVAL, "all tensors must be 16-byte aligned");
+    if (!(scale == scale)) return fail(CKE_EINVAL, "scale is NaN");
+    cke::SelfLaunch a;
+    a.q = q;
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.K = kv->k;
+    a.V = kv->v;
+    a.out = out;
+    a.S = kv->n_seqs;
+    a.H = kv->n_heads;
+    a.D = kv->head_dim;
+    a.max_pos = kv->max_pos;
+    a.pos = pos;
+    a.scale = scale;
+    a.bf16 = kv->dtype == CKE_BF16;
+    hipError_t e = cke::launch_selfattn_append(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(CKE_EDEVICE, "self-attention launch failed: %s", hipGetErrorString(e));
+    return CKE_OK;
+}
+
+}  // extern "C"

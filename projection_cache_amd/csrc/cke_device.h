@@ -1,0 +1,232 @@
+// Device-side building blocks shared by the decode kernels (gfx950, wave64).
+//
+// Attention of one query row against a run of cached K/V rows, computed by a
+// single wavefront with a running max and running sum (the online softmax of
+// Rabe & Staats, which the WhisperKit case study, section 3, lists as the
+// SplitKV attention variant: key chunks keep a running max/sum and are merged).
+// Several wavefronts' partial states are merged through LDS, and several
+// workgroups' partial states through a workspace (the cross-block merge).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace cke {
+
+// exp(x) = 2^(x * log2 e); scores are kept in the base-2 domain so the
+// hardware exp2 (v_exp_f32) applies directly.
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Element storage types: float (fp32) or bf16 held as raw uint16_t bits.
+template <typename TE> struct ElemTraits;
+template <> struct ElemTraits<float> {
+    static constexpr int kVec = 4;  // elements per 16-byte lane load
+};
+template <> struct ElemTraits<uint16_t> {
+    static constexpr int kVec = 8;
+};
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Round to nearest-even bf16 (hardware v_cvt_pk_bf16_f32) and return the bits.
+__device__ __forceinline__ uint16_t to_bf16_bits(float x) {
+    __bf16 h = (__bf16)x;
+    return __builtin_bit_cast(uint16_t, h);
+}
+__device__ __forceinline__ float round_to_bf16(float x) { return (float)(__bf16)x; }
+
+// Load 16 bytes of a cached row as fp32 values.
+__device__ __forceinline__ void load16(const float* __restrict__ p, float (&x)[4]) {
+    const float4 v = *reinterpret_cast<const float4*>(p);
+    x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
+}
+__device__ __forceinline__ void load16(const uint16_t* __restrict__ p, float (&x)[8]) {
+    const uint4 v = *reinterpret_cast<const uint4*>(p);
+    x[0] = bf16_lo(v.x); x[1] = bf16_hi(v.x);
+    x[2] = bf16_lo(v.y); x[3] = bf16_hi(v.y);
+    x[4] = bf16_lo(v.z); x[5] = bf16_hi(v.z);
+    x[6] = bf16_lo(v.w); x[7] = bf16_hi(v.w);
+}
+
+// The same elements from an fp32 source row, rounded to the storage precision
+// (used for the row a self-attention call appends: attention reads the value
+// as stored).
+__device__ __forceinline__ void load16_f32_as(const float* __restrict__ p, float (&x)[4]) {
+    const float4 v = *reinterpret_cast<const float4*>(p);
+    x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
+}
+__device__ __forceinline__ void load16_f32_as(const float* __restrict__ p, float (&x)[8]) {
+    const float4 a = *reinterpret_cast<const float4*>(p);
+    const float4 b = *reinterpret_cast<const float4*>(p + 4);
+    x[0] = round_to_bf16(a.x); x[1] = round_to_bf16(a.y);
+    x[2] = round_to_bf16(a.z); x[3] = round_to_bf16(a.w);
+    x[4] = round_to_bf16(b.x); x[5] = round_to_bf16(b.y);
+    x[6] = round_to_bf16(b.z); x[7] = round_to_bf16(b.w);
+}
+
+// Butterfly reductions over lane groups of a wave64.
+template <int FROM, int TO>
+__device__ __forceinline__ float xor_sum(float v) {
+#pragma unroll
+    for (int m = FROM; m < TO; m <<= 1) v += __shfl_xor(v, m, 64);
+    return v;
+}
+template <int FROM, int TO>
+__device__ __forceinline__ float xor_max(float v) {
+#pragma unroll
+    for (int m = FROM; m < TO; m <<= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
+    return v;
+}
+
+// Geometry of the lane -> (row, dims) mapping for head_dim D and element TE.
+// A row of D elements is read by LPK lanes, 16 bytes each; a wave covers KPW
+// consecutive rows per pass.
+template <int D, typename TE>
+struct RowMap {
+    static constexpr int kVec = ElemTraits<TE>::kVec;
+    static constexpr int kLPK = D / kVec;   // lanes per row
+    static constexpr int kKPW = 64 / kLPK;  // rows per wave pass
+    static_assert(kLPK >= 1 && kLPK <= 64 && (64 % kLPK) == 0, "bad head_dim");
+};
+
+// Running softmax state of one wave for up to NQ queries. m is in the base-2
+// domain (scores pre-multiplied by scale*log2 e); l and acc are partial over
+// this lane's row group until wg_merge() reduces them across groups.
+template <int NQ, int VEC>
+struct WaveState {
+    float m[NQ];
+    float l[NQ];
+    float acc[NQ][VEC];
+    __device__ __forceinline__ void init() {
+#pragma unroll
+        for (int i = 0; i < NQ; ++i) {
+            m[i] = -INFINITY;
+            l[i] = 0.f;
+#pragma unroll
+            for (int j = 0; j < VEC; ++j) acc[i][j] = 0.f;
+        }
+    }
+};
+
+// One wave attends its queries over rows [r0, r1) of K/V (rows D elements
+// apart). Rows are read NP passes at a time, all loads of a tile issued before
+// any arithmetic. If cur_row lies in the range, that row is taken from the
+// fp32 vectors cur_k / cur_v (rounded to the storage precision) instead of
+// memory.
+template <int D, typename TE, int NQ, int NP>
+__device__ __forceinline__ void wave_attend(
+    const TE* __restrict__ K, const TE* __restrict__ V, int r0, int r1,
+    const float (&q)[NQ][RowMap<D, TE>::kVec], int nq, float sl2,
+    int cur_row, const float* __restrict__ cur_k, const float* __restrict__ cur_v,
+    WaveState<NQ, RowMap<D, TE>::kVec>& st)
+{
+    using RM = RowMap<D, TE>;
+    constexpr int VEC = RM::kVec, LPK = RM::kLPK, KPW = RM::kKPW;
+    const int lane = threadIdx.x & 63;
+    const int grp = lane / LPK;
+    const int sub = lane % LPK;
+
+    for (int base = r0; base < r1; base += NP * KPW) {
+        float kf[NP][VEC], vf[NP][VEC];
+        bool valid[NP];
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+            const int row = base + p * KPW + grp;
+            valid[p] = row < r1;
+            if (valid[p] && row != cur_row) {
+                load16(K + (size_t)row * D + sub * VEC, kf[p]);
+                load16(V + (size_t)row * D + sub * VEC, vf[p]);
+            } else if (valid[p]) {
+                load16_f32_as(cur_k + sub * VEC, kf[p]);
+                load16_f32_as(cur_v + sub * VEC, vf[p]);
+            } else {
+#pragma unroll
+                for (int j = 0; j < VEC; ++j) { kf[p][j] = 0.f; vf[p][j] = 0.f; }
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < NQ; ++i) {
+            if (i < nq) {
+                float s[NP];
+                float mt = -INFINITY;
+#pragma unroll
+                for (int p = 0; p < NP; ++p) {
+                    float d = 0.f;
+#pragma unroll
+                    for (int j = 0; j < VEC; ++j) d = fmaf(q[i][j], kf[p][j], d);
+                    d = xor_sum<1, LPK>(d);
+                    s[p] = valid[p] ? d * sl2 : -INFINITY;
+                    mt = fmaxf(mt, s[p]);
+                }
+                mt = xor_max<LPK, 64>(mt);
+                const float mn = fmaxf(st.m[i], mt);
+                if (mn != -INFINITY) {  // wave-uniform
+                    const float alpha = fast_exp2(st.m[i] - mn);
+                    st.l[i] *= alpha;
+#pragma unroll
+                    for (int j = 0; j < VEC; ++j) st.acc[i][j] *= alpha;
+#pragma unroll
+                    for (int p = 0; p < NP; ++p) {
+                        const float e = fast_exp2(s[p] - mn);
+                        st.l[i] += e;
+#pragma unroll
+                        for (int j = 0; j < VEC; ++j) st.acc[i][j] = fmaf(e, vf[p][j], st.acc[i][j]);
+                    }
+                    st.m[i] = mn;
+                }
+            }
+        }
+    }
+}
+
+// Merge the NW waves of a workgroup. Afterwards, for i < nq and d < D,
+// sM[i], sL[i], sA[i*D + d] hold the workgroup's (max, sum, unnormalised
+// output). LDS scratch: wm, wl [NW*NQ], wa [NW*NQ*D]. Ends with a barrier.
+template <int D, typename TE, int NQ, int NW>
+__device__ __forceinline__ void wg_merge(
+    WaveState<NQ, RowMap<D, TE>::kVec>& st, int nq, float* wm, float* wl,
+    float* wa, float* sM, float* sL, float* sA)
+{
+    using RM = RowMap<D, TE>;
+    constexpr int VEC = RM::kVec, LPK = RM::kLPK;
+    const int lane = threadIdx.x & 63;
+    const int w = threadIdx.x >> 6;
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) {
+        if (i < nq) {
+            st.l[i] = xor_sum<LPK, 64>(st.l[i]);
+#pragma unroll
+            for (int j = 0; j < VEC; ++j) st.acc[i][j] = xor_sum<LPK, 64>(st.acc[i][j]);
+            if (lane < LPK) {
+#pragma unroll
+                for (int j = 0; j < VEC; ++j) wa[(w * NQ + i) * D + lane * VEC + j] = st.acc[i][j];
+            }
+            if (lane == 0) {
+                wm[w * NQ + i] = st.m[i];
+                wl[w * NQ + i] = st.l[i];
+            }
+        }
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < nq * D; idx += NW * 64) {
+        const int i = idx / D, d = idx % D;
+        float M = -INFINITY;
+#pragma unroll
+        for (int v = 0; v < NW; ++v) M = fmaxf(M, wm[v * NQ + i]);
+        float L = 0.f, A = 0.f;
+#pragma unroll
+        for (int v = 0; v < NW; ++v) {
+            const float f = fast_exp2(wm[v * NQ + i] - M);
+            L = fmaf(wl[v * NQ + i], f, L);
+            A = fmaf(wa[(v * NQ + i) * D + d], f, A);
+        }
+        sA[i * D + d] = A;
+        if (d == 0) { sM[i] = M; sL[i] = L; }
+    }
+    __syncthreads();
+}
+
+}  // namespace cke

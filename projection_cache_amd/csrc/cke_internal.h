@@ -1,0 +1,61 @@
+// Internal launch descriptors shared by the C-ABI layer and the kernel files.
+// Host-visible only; not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace cke {
+
+constexpr int kMaxLayers = 128;
+
+struct XattnLaunch {
+    const float* q;
+    const void* K;       // layer slab base, [B][H][T][D]
+    const void* V;
+    float* out;
+    float* part;         // workspace partials
+    unsigned* counters;  // workspace counters, one per (b, h)
+    int B, H, T, D, nq, max_q, nsplit, chunk;
+    float scale;
+    bool bf16;
+};
+
+struct SelfLaunch {
+    const float* q;
+    const float* k_new;
+    const float* v_new;
+    void* K;             // [S][H][max_pos][D]
+    void* V;
+    float* out;
+    int S, H, D, max_pos, pos;
+    float scale;
+    bool bf16;
+};
+
+// Pointer table of the 2*L weight matrices: entries [0, L) are WK_0..WK_{L-1},
+// entries [L, 2L) are WV_0..WV_{L-1}. Passed by value as a kernel argument.
+struct WeightTable {
+    const void* w[2 * kMaxLayers];
+};
+
+struct PopulateLaunch {
+    const void* E;       // [B*T][d_model]
+    WeightTable wt;
+    void* Kc;            // [L][B][H][T][D]
+    void* Vc;
+    unsigned* counters;  // cleared by the launch
+    int n_counters;
+    int L, B, T, dm, H, D;
+    bool bf16;
+};
+
+// Rows of K/V one decode workgroup covers per pass of all its waves.
+int cross_keys_per_pass(int D, int elem_bytes);
+
+hipError_t launch_xattn_decode(const XattnLaunch& a, hipStream_t st);
+hipError_t launch_selfattn_append(const SelfLaunch& a, hipStream_t st);
+hipError_t launch_populate(const PopulateLaunch& a, hipStream_t st);
+
+}  // namespace cke

@@ -1,0 +1,155 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, exports
+every entry point the header declares, and validates arguments, geometry and
+the ready flag before it would launch anything."""
+import ctypes
+import json
+import os
+import re
+
+import pytest
+
+import projection_cache_amd as pc
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "cke_xattn.h")
+GOLDEN = os.path.join(ROOT, "tests", "golden")
+
+FAKE = 0x100000  # an aligned non-NULL address; never dereferenced by these calls
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"\b(cke_[a-z0-9_]+)\s*\(", src)
+    return sorted(set(names))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert len(names) >= 13
+    lib = ctypes.CDLL(pc.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(pc.EXPORTED) == names
+
+
+def test_version_string():
+    assert "gfx950" in pc.cke_version()
+
+
+def base_geom(**kw):
+    d = dict(n_layers=6, n_streams=1, mem_len=1500, d_model=512, n_heads=8, head_dim=64,
+             max_q=1, cache_dtype=pc.CKE_F32)
+    d.update(kw)
+    return pc.make_geom(**d)
+
+
+def test_region_and_layer_offset_match_page():
+    """C-Kernel-Engine 'View 2': layer 5's slab of Whisper Base (fp32) starts
+    15,360,000 bytes into the cache region."""
+    g = json.load(open(os.path.join(GOLDEN, "cke_whisper_base_geometry.json")))
+    geom = base_geom()
+    assert pc.cke_xattn_layer_offset_bytes(geom, 5) == g["layer5_k_offset_bytes"]
+    assert pc.cke_xattn_region_bytes(geom) == 6 * 1500 * 512 * 4
+    bf = base_geom(cache_dtype=pc.CKE_BF16)
+    assert pc.cke_xattn_region_bytes(bf) == 6 * 1500 * 512 * 2
+    with pytest.raises(pc.CkeError):
+        pc.cke_xattn_layer_offset_bytes(geom, 6)
+
+
+@pytest.mark.parametrize("bad", [
+    dict(mem_len=0), dict(mem_len=-3), dict(d_model=500), dict(n_heads=7),
+    dict(head_dim=48, d_model=384), dict(max_q=0), dict(max_q=9), dict(n_layers=0),
+    dict(cache_dtype=7), dict(n_streams=0),
+])
+def test_geometry_fails_closed(bad):
+    """C-Kernel-Engine 'View 3': non-positive memory length and
+    num_heads * head_dim != embed_dim are hard errors, not defaults."""
+    g = base_geom(**bad)
+    assert pc.cke_xattn_region_bytes(g) == 0
+    assert pc.cke_xattn_workspace_bytes(g) == 0
+    with pytest.raises(pc.CkeError) as e:
+        pc.cke_xattn_cache_create(g, FAKE, FAKE, FAKE)
+    assert e.value.code == pc.CKE_EINVAL
+    assert pc.cke_last_error()
+
+
+def test_workspace_and_split_plan():
+    for g in (base_geom(), base_geom(max_q=5),
+              base_geom(n_layers=32, n_streams=16, d_model=1280, n_heads=20,
+                        cache_dtype=pc.CKE_BF16),
+              base_geom(n_layers=2, n_streams=100, mem_len=15, d_model=2048, n_heads=32,
+                        max_q=3),
+              base_geom(n_layers=1, mem_len=64, d_model=64, n_heads=2, head_dim=32)):
+        s = pc.cke_xattn_num_splits(g)
+        assert 1 <= s <= 64
+        ws = pc.cke_xattn_workspace_bytes(g)
+        need = g.n_streams * g.max_q * g.n_heads * s * (g.head_dim + 2) * 4
+        assert ws >= need + g.n_streams * g.n_heads * 4
+    # Whisper Base splits its 1500 rows across workgroups, Q-Former does not
+    assert pc.cke_xattn_num_splits(base_geom()) > 1
+    assert pc.cke_xattn_num_splits(base_geom(n_layers=2, n_streams=100, mem_len=15, d_model=2048,
+                                             n_heads=32, max_q=3)) == 1
+
+
+def test_ready_flag_state_machine_without_gpu():
+    """C-Kernel-Engine 'View 3': a cache is not ready until populated; after
+    invalidation decode refuses with -2 before launching anything."""
+    h = pc.cke_xattn_cache_create(base_geom(), FAKE, FAKE, FAKE)
+    try:
+        assert not pc.cke_xattn_is_ready(h)
+        rc = pc.lib().cke_xattn_decode(FAKE, 1, h, 0, 0.125, FAKE, None)
+        assert rc == pc.CKE_ENOTREADY == -2
+        assert "not populated" in pc.cke_last_error()
+        pc.cke_xattn_invalidate(h)
+        assert pc.lib().cke_xattn_decode(FAKE, 1, h, 0, 0.125, FAKE, None) == -2
+        # range checks come first
+        assert pc.lib().cke_xattn_decode(FAKE, 1, h, 6, 0.125, FAKE, None) == pc.CKE_ERANGE
+        assert pc.lib().cke_xattn_decode(FAKE, 2, h, 0, 0.125, FAKE, None) == pc.CKE_ERANGE
+        assert pc.lib().cke_xattn_decode(FAKE, -1, h, 0, 0.125, FAKE, None) == pc.CKE_ERANGE
+    finally:
+        pc.cke_xattn_cache_destroy(h)
+
+
+def test_populate_rejects_bad_arguments_before_launch():
+    h = pc.cke_xattn_cache_create(base_geom(n_layers=2), FAKE, FAKE, FAKE)
+    try:
+        arr = ctypes.c_void_p * 2
+        ok = arr(FAKE, FAKE)
+        nul = arr(FAKE, None)
+        L = pc.lib()
+        assert L.cke_xattn_populate(h, None, 0, ok, ok, 0, None) == pc.CKE_EINVAL
+        assert L.cke_xattn_populate(h, FAKE, 0, nul, ok, 0, None) == pc.CKE_EINVAL
+        # fp32 cache with bf16 inputs: unsupported mix
+        assert L.cke_xattn_populate(h, FAKE, 1, ok, ok, 1, None) == pc.CKE_EINVAL
+        assert L.cke_xattn_populate(h, FAKE + 4, 0, ok, ok, 0, None) == pc.CKE_EINVAL
+        assert not pc.cke_xattn_is_ready(h)
+    finally:
+        pc.cke_xattn_cache_destroy(h)
+
+
+def test_create_rejects_null_and_misaligned():
+    g = base_geom()
+    for k, v, w in ((None, FAKE, FAKE), (FAKE, None, FAKE), (FAKE, FAKE, None),
+                    (FAKE + 8, FAKE, FAKE), (FAKE, FAKE, FAKE + 16)):
+        with pytest.raises(pc.CkeError):
+            pc.cke_xattn_cache_create(g, k, v, w)
+
+
+def test_selfattn_rejects_bad_arguments_before_launch():
+    L = pc.lib()
+
+    def call(pos=0, **kw):
+        d = dict(k=FAKE, v=FAKE, n_seqs=1, n_heads=8, head_dim=64, max_pos=448, dtype=0)
+        d.update(kw)
+        desc = pc.cke_kv_layer(**d)
+        return L.cke_selfattn_decode_append(FAKE, FAKE, FAKE, ctypes.byref(desc), pos, 0.125,
+                                            FAKE, None)
+
+    assert call(pos=448) == pc.CKE_ERANGE
+    assert call(pos=-1) == pc.CKE_ERANGE
+    assert call(head_dim=48) == pc.CKE_EINVAL
+    assert call(dtype=5) == pc.CKE_EINVAL
+    assert call(k=None) == pc.CKE_EINVAL
+    assert call(n_seqs=0) == pc.CKE_EINVAL
+    assert L.cke_selfattn_decode_append(FAKE, FAKE, FAKE, None, 0, 0.125, FAKE, None) == pc.CKE_EINVAL

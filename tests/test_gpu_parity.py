@@ -1,0 +1,367 @@
+"""Parity of the HIP library (through its C ABI) with the CPU oracle.
+
+Inputs are seeded and synthetic (synth/); the oracle computes in float64 from
+the same values. Floating-point outputs must agree within max-abs 1e-4 where
+the cache is fp32 and 2e-2 where it is bf16. Stored cache rows written by the
+self-attention append are compared bit for bit (a copy, or a round-to-nearest
+bf16 conversion of an fp32 value, has exactly one correct result).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    global pc
+    import projection_cache_amd as pc  # noqa: F401  (fails loudly if not built)
+    torch.cuda.set_device(0)
+    yield
+    torch.cuda.synchronize()
+
+
+DEV = "cuda:0"
+
+
+def t32(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(DEV)
+
+
+def tbf16(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits, dtype=np.uint16).view(np.int16)).view(
+        torch.bfloat16).to(DEV)
+
+
+def to_np(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def geometry(name=None, **kw):
+    if name is not None:
+        g = synth.get(name)
+        if not kw:
+            return g
+        d = {f: getattr(g, f) for f in g.__dataclass_fields__}
+    else:
+        d = dict(name="custom", n_streams=1, n_q=1, n_seqs=1, n_layers=1, mem_len=64,
+                 d_model=64, n_heads=2, head_dim=32, scale=1 / math.sqrt(32), dtype="f32",
+                 steps=4, max_pos=8, seed=77)
+    d.update(kw)
+    return synth.Geometry(**d)
+
+
+def make_cache(g, inputs=None):
+    """GPU cache populated from the workload's seeded E/WK/WV."""
+    wt = inputs or synth.workload_tensors(g)
+    dt = torch.bfloat16 if g.dtype == "bf16" else torch.float32
+    cache = pc.XattnCache(g.n_layers, g.n_streams, g.mem_len, g.d_model, g.n_heads, g.head_dim,
+                          max_q=max(g.n_q, 1), dtype=dt)
+    if g.dtype == "bf16":
+        E = tbf16(wt["E_bits"])
+        WK = [tbf16(b) for b in wt["WK_bits"]]
+        WV = [tbf16(b) for b in wt["WV_bits"]]
+    else:
+        E = t32(wt["E"])
+        WK = [t32(w) for w in wt["WK"]]
+        WV = [t32(w) for w in wt["WV"]]
+    cache.populate(E, WK, WV)
+    torch.cuda.synchronize()
+    return cache, wt, (E, WK, WV)
+
+
+_ORACLE_CACHE = {}
+
+
+def oracle_caches(g, wt):
+    """Oracle projection caches of a named workload, computed once per module."""
+    key = (g.name, g.seed, g.n_layers, g.n_streams, g.mem_len, g.d_model, g.dtype)
+    if g.name == "custom" or key not in _ORACLE_CACHE:
+        r = oracle.populate(wt["E"], wt["WK"], wt["WV"], g.n_heads, g.head_dim,
+                            round_bf16=(g.dtype == "bf16"))
+        if g.name == "custom":
+            return r
+        _ORACLE_CACHE[key] = r
+    return _ORACLE_CACHE[key]
+
+
+def max_abs(a, b):
+    return float(np.max(np.abs(np.asarray(a, np.float64) - np.asarray(b, np.float64))))
+
+
+# ------------------------------------------------------------------ populate
+POP_CASES = [
+    ("tiny", {}),
+    ("base", {}),
+    (None, dict(n_layers=2, n_streams=3, mem_len=77, d_model=256, n_heads=4, head_dim=64)),
+    (None, dict(n_layers=2, n_streams=3, mem_len=77, d_model=256, n_heads=4, head_dim=64,
+                dtype="bf16")),
+    (None, dict(n_layers=3, n_streams=2, mem_len=1, d_model=96, n_heads=3, head_dim=32)),
+    (None, dict(n_layers=1, n_streams=1, mem_len=200, d_model=256, n_heads=2, head_dim=128,
+                dtype="bf16")),
+    (None, dict(n_layers=2, n_streams=2, mem_len=130, d_model=384, n_heads=3, head_dim=128)),
+]
+
+
+@pytest.mark.parametrize("name,kw", POP_CASES, ids=lambda x: str(x))
+def test_populate_matches_oracle(name, kw):
+    g = geometry(name, **kw)
+    cache, wt, _ = make_cache(g)
+    Kc, Vc = oracle_caches(g, wt)
+    tol = TOL[g.dtype]
+    assert max_abs(to_np(cache.k), Kc) <= tol
+    assert max_abs(to_np(cache.v), Vc) <= tol
+    assert cache.ready
+
+
+# -------------------------------------------------------------- cross decode
+DEC_CASES = [
+    ("tiny", {}),
+    ("base", {}),
+    ("beam", {}),
+    (None, dict(n_layers=2, n_streams=3, n_q=8, mem_len=77, d_model=256, n_heads=4,
+                head_dim=64)),
+    (None, dict(n_layers=2, n_streams=3, n_q=3, mem_len=77, d_model=256, n_heads=4,
+                head_dim=64, dtype="bf16")),
+    (None, dict(n_layers=3, n_streams=2, mem_len=1, d_model=96, n_heads=3, head_dim=32)),
+    (None, dict(n_layers=1, n_streams=1, n_q=2, mem_len=200, d_model=256, n_heads=2,
+                head_dim=128, dtype="bf16")),
+    (None, dict(n_layers=1, n_streams=1, n_q=5, mem_len=3001, d_model=128, n_heads=2,
+                head_dim=64)),
+]
+
+
+@pytest.mark.parametrize("name,kw", DEC_CASES, ids=lambda x: str(x))
+def test_cross_decode_matches_oracle(name, kw):
+    g = geometry(name, **kw)
+    cache, wt, _ = make_cache(g)
+    Kc, Vc = oracle_caches(g, wt)
+    tol = TOL[g.dtype]
+    for step in (0, 1):
+        for layer in range(g.n_layers):
+            q = synth.decode_call_inputs(g, step, layer)["q_cross"]
+            out = cache.decode(t32(q), layer, g.scale)
+            torch.cuda.synchronize()
+            want = oracle.cross_decode(q, Kc[layer], Vc[layer], g.scale)
+            err = max_abs(to_np(out), want)
+            assert err <= tol, (step, layer, err)
+
+
+def test_cross_decode_peaked_softmax_and_shift_invariance():
+    """A large scale concentrates the softmax (online max tracking across
+    splits matters); adding one constant vector to every key of a head leaves
+    the output unchanged (WhisperKit case study, section 2: a key bias is
+    redundant under softmax)."""
+    g = geometry("base")
+    cache, wt, _ = make_cache(g)
+    Kc, Vc = oracle_caches(g, wt)
+    q = synth.decode_call_inputs(g, 5, 2)["q_cross"]
+    out = cache.decode(t32(q), 2, 4.0)
+    want = oracle.cross_decode(q, Kc[2], Vc[2], 4.0)
+    assert max_abs(to_np(out), want) <= 1e-4
+    base_out = to_np(cache.decode(t32(q), 3, g.scale))
+    # bias per head chosen so that q . b = +40 for this query
+    qv = q[0, 0]
+    bias = qv / np.sum(qv * qv, axis=1, keepdims=True) * (40.0 / g.scale)
+    cache.k[3, 0] += t32(bias)[:, None, :]
+    shifted = to_np(cache.decode(t32(q), 3, g.scale))
+    assert max_abs(shifted, base_out) <= 1e-4
+
+
+def test_cross_decode_is_deterministic_and_nq_zero_is_noop():
+    g = geometry("beam")
+    cache, _, _ = make_cache(g)
+    q = t32(synth.decode_call_inputs(g, 0, 0)["q_cross"])
+    a = cache.decode(q, 1, g.scale).clone()
+    b = cache.decode(q, 1, g.scale).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    out = torch.full_like(q, 7.0)
+    pc.cke_xattn_decode(q, cache, 1, g.scale, out, n_q=0)
+    torch.cuda.synchronize()
+    assert bool(torch.all(out == 7.0))
+
+
+def test_ready_flag_on_gpu():
+    """C-Kernel-Engine 'View 3': new encoder memory invalidates the cache and
+    decode refuses (-2) until populate has run again."""
+    g = geometry("tiny")
+    cache, wt, (E, WK, WV) = make_cache(g)
+    q = t32(synth.decode_call_inputs(g, 0, 0)["q_cross"])
+    cache.decode(q, 0, g.scale)
+    cache.invalidate()
+    with pytest.raises(pc.CkeError) as e:
+        cache.decode(q, 0, g.scale)
+    assert e.value.code == -2
+    # install new encoder memory, repopulate, and decode reads the new projection
+    E2 = E * 2.0
+    cache.populate(E2, WK, WV)
+    out = cache.decode(q, 0, g.scale)
+    Kc, Vc = oracle.populate(2.0 * wt["E"].astype(np.float64), wt["WK"], wt["WV"], g.n_heads,
+                             g.head_dim)
+    want = oracle.cross_decode(to_np(q), Kc[0], Vc[0], g.scale)
+    assert max_abs(to_np(out), want) <= 1e-4
+
+
+# ----------------------------------------------------- self append + attend
+SELF_CASES = [
+    dict(S=1, H=2, D=32, P=8, dtype="f32"),          # Tiny
+    dict(S=1, H=8, D=64, P=448, dtype="f32"),        # Whisper Base, full capacity
+    dict(S=5, H=8, D=64, P=40, dtype="f32"),         # beams
+    dict(S=3, H=4, D=64, P=70, dtype="bf16"),
+    dict(S=2, H=2, D=128, P=33, dtype="f32"),
+    dict(S=2, H=3, D=128, P=33, dtype="bf16"),
+]
+
+
+@pytest.mark.parametrize("c", SELF_CASES, ids=lambda c: "S%d-H%d-D%d-P%d-%s" % tuple(c.values()))
+def test_self_append_attend_matches_oracle(c):
+    S, H, D, P = c["S"], c["H"], c["D"], c["P"]
+    bf = c["dtype"] == "bf16"
+    dt = torch.bfloat16 if bf else torch.float32
+    kv = pc.KVLayer(S, H, D, P, dtype=dt)
+    Ks = np.zeros((S, H, P, D))
+    Vs = np.zeros((S, H, P, D))
+    scale = 1 / math.sqrt(D)
+    std = 0.02 * math.sqrt(H * D)
+    worst = 0.0
+    positions = list(range(P)) if P <= 70 else list(range(P))
+    for pos in positions:
+        key = [31, S, H, D, P, pos]
+        q = synth.normal(key + [0], (S, H, D), std)
+        kn = synth.normal(key + [1], (S, H, D), std)
+        vn = synth.normal(key + [2], (S, H, D), std)
+        out = kv.append_attend(t32(q), t32(kn), t32(vn), pos, scale)
+        want = oracle.self_append_attend(q, kn, vn, Ks, Vs, pos, scale, round_bf16=bf)
+        if pos % 7 == 0 or pos == P - 1:
+            torch.cuda.synchronize()
+            worst = max(worst, max_abs(to_np(out), want))
+    torch.cuda.synchronize()
+    assert worst <= 1e-4
+    # the stored rows are exactly the scattered (rounded) inputs
+    np.testing.assert_array_equal(to_np(kv.k), Ks)
+    np.testing.assert_array_equal(to_np(kv.v), Vs)
+
+
+def test_self_rows_past_pos_are_never_read_or_written():
+    """Poison every row past pos with NaN: the output equals the clean run bit
+    for bit and the poisoned rows are untouched."""
+    S, H, D, P = 2, 8, 64, 64
+    for dt in (torch.float32, torch.bfloat16):
+        clean = pc.KVLayer(S, H, D, P, dtype=dt)
+        dirty = pc.KVLayer(S, H, D, P, dtype=dt)
+        g = torch.Generator().manual_seed(5)
+        for pos in range(0, 40):
+            q, kn, vn = (torch.randn(S, H, D, generator=g).to(DEV) * 0.45 for _ in range(3))
+            dirty.k[:, :, pos + 1:] = float("nan")
+            dirty.v[:, :, pos + 1:] = float("nan")
+            a = clean.append_attend(q, kn, vn, pos, 0.125)
+            b = dirty.append_attend(q, kn, vn, pos, 0.125)
+            torch.cuda.synchronize()
+            assert torch.equal(a, b), pos
+            assert bool(torch.isnan(dirty.k[:, :, pos + 1:]).all())
+            assert torch.equal(clean.k[:, :, :pos + 1], dirty.k[:, :, :pos + 1])
+
+
+# ------------------------------------------------- teacher-forced decode run
+@pytest.mark.parametrize("name", ["tiny", "beam_tiny"])
+def test_teacher_forced_decoder_run_matches_oracle(name):
+    """Whole decode window in the order of the decoder body (self-attention,
+    then cross-attention, per layer, per step): the oracle's harness decoder
+    records every call's inputs and outputs; the GPU replays each call from
+    the recorded inputs (teacher forcing) and must reproduce each output."""
+    if name == "tiny":
+        g = synth.get("tiny")
+    else:
+        g = geometry(None, n_layers=2, n_streams=1, n_q=3, n_seqs=3, mem_len=100, d_model=128,
+                     n_heads=2, head_dim=64, steps=12, max_pos=12, scale=0.125, seed=9)
+    names = ("E", "WK", "WV", "WQ", "WO", "WQs", "WKs", "WVs", "WOs", "x0")
+    wt = synth.workload_tensors(g, names)
+    W = {k: wt[k] for k in names[1:-1]}
+    run = oracle.decoder_run("incremental", wt["E"], W, wt["x0"], n_heads=g.n_heads,
+                             head_dim=g.head_dim, n_q=g.n_q, max_pos=g.max_pos, n_steps=g.steps,
+                             scale=g.scale)
+    cache, _, _ = make_cache(g, wt)
+    kvs = [pc.KVLayer(g.n_seqs, g.n_heads, g.head_dim, g.max_pos) for _ in range(g.n_layers)]
+    rec = run["rec"]
+    shp_s = (g.n_seqs, g.n_heads, g.head_dim)
+    shp_c = (g.n_streams, g.n_q, g.n_heads, g.head_dim)
+    worst = 0.0
+    for t in range(g.steps):
+        for l in range(g.n_layers):
+            so = kvs[l].append_attend(t32(rec["qs"][t, l].reshape(shp_s)),
+                                      t32(rec["kn"][t, l].reshape(shp_s)),
+                                      t32(rec["vn"][t, l].reshape(shp_s)), t, g.scale)
+            co = cache.decode(t32(rec["qc"][t, l].reshape(shp_c)), l, g.scale)
+            torch.cuda.synchronize()
+            worst = max(worst, max_abs(to_np(so).reshape(g.n_seqs, -1), rec["so"][t, l]),
+                        max_abs(to_np(co).reshape(g.n_seqs, -1), rec["co"][t, l]))
+    assert worst <= 1e-4
+    for l in range(g.n_layers):
+        assert max_abs(to_np(kvs[l].k), run["Ks"][l].astype(np.float32)) == 0.0
+
+
+# ---------------------------------------------------- full-size workloads
+def _sampled_slabs(g, wt, picks):
+    """Oracle slabs for the sampled (layer, stream, head) triples."""
+    bf = g.dtype == "bf16"
+    out = {}
+    for (l, b, h) in picks:
+        k = oracle.project_head(wt["E"][b], wt["WK"][l], h * g.head_dim, g.head_dim, bf)
+        v = oracle.project_head(wt["E"][b], wt["WV"][l], h * g.head_dim, g.head_dim, bf)
+        out[(l, b, h)] = (k, v)
+    return out
+
+
+@pytest.mark.parametrize("name", ["large", "qformer"])
+def test_full_size_workload_sampled(name):
+    """The full workload in the launch configuration the benchmark times:
+    populate everything on the GPU, then check sampled slabs and the decode
+    outputs of the sampled (stream, head) pairs against the oracle."""
+    g = synth.get(name)
+    cache, wt, _ = make_cache(g)
+    rng = np.random.default_rng(123)
+    picks = [(0, 0, 0), (g.n_layers - 1, g.n_streams - 1, g.n_heads - 1)]
+    for _ in range(4):
+        picks.append((int(rng.integers(g.n_layers)), int(rng.integers(g.n_streams)),
+                      int(rng.integers(g.n_heads))))
+    ref = _sampled_slabs(g, wt, picks)
+    tol = TOL[g.dtype]
+    for (l, b, h), (k, v) in ref.items():
+        assert max_abs(to_np(cache.k[l, b, h]), k) <= tol, (l, b, h)
+        assert max_abs(to_np(cache.v[l, b, h]), v) <= tol, (l, b, h)
+    for (l, b, h), (k, v) in ref.items():
+        q = synth.decode_call_inputs(g, 3, l)["q_cross"]
+        out = to_np(cache.decode(t32(q), l, g.scale))
+        for i in range(g.n_q):
+            want = oracle.attend(q[b, i, h], k, v, g.scale)
+            assert max_abs(out[b, i, h], want) <= tol, (l, b, h, i)
+
+
+def test_large_self_attention_sampled():
+    """Large workload's self-attention: 16 sequences x 20 heads, bf16 cache of
+    capacity 448, 128 decode positions; outputs at sampled positions."""
+    g = synth.get("large")
+    kv = pc.KVLayer(g.n_seqs, g.n_heads, g.head_dim, g.max_pos, dtype=torch.bfloat16)
+    Ks = np.zeros((g.n_seqs, g.n_heads, g.max_pos, g.head_dim))
+    Vs = np.zeros_like(Ks)
+    worst = 0.0
+    for pos in range(g.steps):
+        d = synth.decode_call_inputs(g, pos, 0)
+        out = kv.append_attend(t32(d["q_self"]), t32(d["k_new"]), t32(d["v_new"]), pos, g.scale)
+        want = oracle.self_append_attend(d["q_self"], d["k_new"], d["v_new"], Ks, Vs, pos,
+                                         g.scale, round_bf16=True)
+        if pos % 16 == 0 or pos == g.steps - 1:
+            worst = max(worst, max_abs(to_np(out), want))
+    assert worst <= 1e-4
+    np.testing.assert_array_equal(to_np(kv.k), Ks)
