@@ -87,9 +87,10 @@ size_t cke_xattn_region_bytes(const cke_xattn_geom* g);
  * an invalid geometry or layer. */
 size_t cke_xattn_layer_offset_bytes(const cke_xattn_geom* g, int layer);
 
-/* Bytes of device workspace a cache needs for split-key partial results and
- * merge counters (fp32 partials [B][max_q][H][splits][D+2] plus one 32-bit
- * counter per (stream, head)). Returns 0 for an invalid geometry. */
+/* Bytes of device workspace a cache needs for split-key partial results:
+ * fp32 [B][max_q][H][splits][D+2] (at least 256). Every decode call writes
+ * the partials it reads, so the workspace needs no initialisation. Returns 0
+ * for an invalid geometry. */
 size_t cke_xattn_workspace_bytes(const cke_xattn_geom* g);
 
 /* Number of key splits a decode call of this geometry uses (fixed per
@@ -98,8 +99,7 @@ int cke_xattn_num_splits(const cke_xattn_geom* g);
 
 /* Create a handle over caller-allocated device regions k_dev, v_dev (each
  * cke_xattn_region_bytes) and ws_dev (cke_xattn_workspace_bytes, 256-byte
- * aligned). The workspace counters are cleared by every populate call, so
- * no initialisation is needed. The handle starts NOT ready. */
+ * aligned). The handle starts NOT ready. */
 int cke_xattn_cache_create(const cke_xattn_geom* g, void* k_dev, void* v_dev,
                            void* ws_dev, cke_xattn_cache** out);
 

@@ -19,7 +19,9 @@ import os
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libcke_xattn.so")
+# CKE_XATTN_LIB selects another build of the same library (e.g. a variant
+# compiled with different launch-shape macros); default: the in-tree build.
+LIB_PATH = os.environ.get("CKE_XATTN_LIB") or os.path.join(_PKG, "libcke_xattn.so")
 
 CKE_OK, CKE_EINVAL, CKE_ENOTREADY, CKE_ERANGE, CKE_EDEVICE = 0, -1, -2, -3, -4
 CKE_F32, CKE_BF16 = 0, 1

@@ -19,21 +19,28 @@ namespace cke {
 // ----------------------------------------------------------------- cross
 // Grid: (nsplit, H, B). Workgroup `split` covers memory rows
 // [split*chunk, min(T, (split+1)*chunk)) of head h of stream b, for all nq
-// queries of that stream. With nsplit > 1 each workgroup writes its partial
-// (max, sum, acc[D]) per query to `part` and the last one to finish (an
-// atomic counter per (b, h)) merges the nsplit partials in ascending split
-// order, writes `out` and resets the counter to zero.
+// queries of that stream, so the queries of one stream share every K/V read.
+// With nsplit == 1 it writes `out` directly; otherwise it writes its partial
+// (max, sum, acc[D]) per query to `part` and xattn_merge_kernel, launched
+// next on the same stream, combines them.
+//
+// Why a second launch: merging inside this kernel needs the partials of
+// other workgroups, which run on other XCDs with their own L2. A
+// release/acquire pair per workgroup is a whole-L2 writeback + invalidate on
+// gfx950, and a fence-free variant (tagged 64-bit partial words with
+// device-scope atomic loads and stores, last arrival by ticket) pays several
+// device-scope round trips on its tail; both measured slower than a second
+// small kernel, whose inputs are coherent at the kernel boundary.
 template <int D, typename TE, int NQ, int NW, int NP>
-__global__ __launch_bounds__(NW * 64) void xattn_decode_kernel(
+__global__ __launch_bounds__(NW * 64) void xattn_partial_kernel(
     const float* __restrict__ q, const TE* __restrict__ Kl, const TE* __restrict__ Vl,
-    float* __restrict__ out, float* __restrict__ part, unsigned* __restrict__ counters,
+    float* __restrict__ out, float* __restrict__ part,
     int nq, int max_q, int H, int T, int nsplit, int chunk, float sl2)
 {
     using RM = RowMap<D, TE>;
     constexpr int VEC = RM::kVec, LPK = RM::kLPK, KPW = RM::kKPW;
     __shared__ float wm[NW * NQ], wl[NW * NQ], wa[NW * NQ * D];
     __shared__ float sM[NQ], sL[NQ], sA[NQ * D];
-    __shared__ int is_last;
 
     const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const size_t bh = (size_t)b * H + h;
@@ -68,41 +75,101 @@ __global__ __launch_bounds__(NW * 64) void xattn_decode_kernel(
         }
         return;
     }
-
     // partial layout [B][max_q][H][nsplit][D+2]: M, L, acc[0..D)
-    auto pslot = [&](int i, int s) -> float* {
+    for (int idx = threadIdx.x; idx < nq * (D + 2); idx += NW * 64) {
+        const int i = idx / (D + 2), k = idx % (D + 2);
+        float* p = part + ((((size_t)b * max_q + i) * H + h) * nsplit + split) * (D + 2);
+        p[k] = k == 0 ? sM[i] : (k == 1 ? sL[i] : sA[i * D + k - 2]);
+    }
+}
+
+// Grid: (H, B), 256 threads. Combines the nsplit partials of each (stream,
+// query, head) of one head:
+//   M = max_s M_s,  L = sum_s L_s 2^(M_s - M),  out = sum_s A_s 2^(M_s - M) / L
+// Thread (o, g) with o = (query, dim) and group g < G = 256 / (nq*D) takes
+// splits s = g, g+G, ... Every load a thread needs (its acc values and, for
+// the first nq*nsplit threads, one (M, L) pair) is issued before any result
+// is used, so the merge costs one memory round trip; groups are then summed
+// in a fixed order (deterministic).
+template <int D>
+__global__ __launch_bounds__(256) void xattn_merge_kernel(
+    const float* __restrict__ part, float* __restrict__ out, int nq, int max_q, int H,
+    int nsplit)
+{
+    constexpr int kBatch = 16;
+    __shared__ float sF[8 * kMaxSplits];   // per (query, split): max, then weight
+    __shared__ float sLs[8 * kMaxSplits];  // per (query, split): sum
+    __shared__ float sSum[8];
+    __shared__ float sAcc[256];
+    const int h = blockIdx.x, b = blockIdx.y;
+    auto slot = [&](int i, int s) -> const float* {
         return part + ((((size_t)b * max_q + i) * H + h) * nsplit + s) * (D + 2);
     };
-    for (int idx = threadIdx.x; idx < nq * D; idx += NW * 64) {
-        const int i = idx / D, d = idx % D;
-        float* p = pslot(i, split);
-        p[2 + d] = sA[i * D + d];
-        if (d == 0) { p[0] = sM[i]; p[1] = sL[i]; }
-    }
-    __threadfence();  // release: partials visible device-wide (all XCD L2s)
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const unsigned prev = atomicAdd(&counters[bh], 1u);
-        is_last = (prev == (unsigned)(nsplit - 1));
-    }
-    __syncthreads();
-    if (!is_last) return;
-    __threadfence();  // acquire: see every other workgroup's partials
+    const int n_out = nq * D;
+    const int G = n_out >= 256 ? 1 : 256 / n_out;
+    const int tid = threadIdx.x;
 
-    for (int idx = threadIdx.x; idx < nq * D; idx += NW * 64) {
-        const int i = idx / D, d = idx % D;
-        float M = -INFINITY;
-        for (int s = 0; s < nsplit; ++s) M = fmaxf(M, pslot(i, s)[0]);
-        float L = 0.f, A = 0.f;
-        for (int s = 0; s < nsplit; ++s) {
-            const float* p = pslot(i, s);
-            const float f = fast_exp2(p[0] - M);
-            L = fmaf(p[1], f, L);
-            A = fmaf(p[2 + d], f, A);
+    // first batch of acc loads for this thread's first output
+    const int o0 = tid % n_out, g0 = tid / n_out;
+    float av[kBatch];
+    if (tid < n_out * G) {
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+            const int s = g0 + j * G;
+            av[j] = s < nsplit ? slot(o0 / D, s)[2 + o0 % D] : 0.f;
         }
-        out[(((size_t)b * nq + i) * H + h) * D + d] = A / L;
     }
-    if (threadIdx.x == 0) atomicExch(&counters[bh], 0u);
+    for (int idx = tid; idx < nq * nsplit; idx += 256) {
+        const int i = idx / nsplit, s = idx % nsplit;
+        const float* p = slot(i, s);
+        sF[i * kMaxSplits + s] = p[0];
+        sLs[i * kMaxSplits + s] = p[1];
+    }
+    __syncthreads();
+    for (int i = tid; i < nq; i += 256) {
+        float M = -INFINITY;
+        for (int s = 0; s < nsplit; ++s) M = fmaxf(M, sF[i * kMaxSplits + s]);
+        float L = 0.f;
+        for (int s = 0; s < nsplit; ++s) {
+            const float f = fast_exp2(sF[i * kMaxSplits + s] - M);
+            sF[i * kMaxSplits + s] = f;
+            L = fmaf(sLs[i * kMaxSplits + s], f, L);
+        }
+        sSum[i] = L;
+    }
+    __syncthreads();
+    for (int idx = tid; idx < n_out * G; idx += 256) {
+        const int o = idx % n_out, g = idx / n_out;
+        const int i = o / D, d = o % D;
+        float A = 0.f;
+        for (int s0 = g; s0 < nsplit; s0 += kBatch * G) {
+            if (!(idx == tid && s0 == g)) {
+#pragma unroll
+                for (int j = 0; j < kBatch; ++j) {
+                    const int s = s0 + j * G;
+                    av[j] = s < nsplit ? slot(i, s)[2 + d] : 0.f;
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j) {
+                const int s = s0 + j * G;
+                if (s < nsplit) A = fmaf(av[j], sF[i * kMaxSplits + s], A);
+            }
+        }
+        if (G == 1)
+            out[(((size_t)b * nq + i) * H + h) * D + d] = A / sSum[i];
+        else
+            sAcc[idx] = A;
+    }
+    if (G > 1) {
+        __syncthreads();
+        for (int o = tid; o < n_out; o += 256) {
+            float A = 0.f;
+            for (int g = 0; g < G; ++g) A += sAcc[g * n_out + o];
+            const int i = o / D, d = o % D;
+            out[(((size_t)b * nq + i) * H + h) * D + d] = A / sSum[i];
+        }
+    }
 }
 
 // ------------------------------------------------------------------ self
@@ -161,18 +228,36 @@ __global__ __launch_bounds__(NW * 64) void selfattn_append_kernel(
 // ------------------------------------------------------------- launchers
 namespace {
 
-constexpr int kCrossWaves = 4;
-constexpr int kSelfWaves = 16;
+#ifndef CKE_CROSS_WAVES
+#define CKE_CROSS_WAVES 4
+#endif
+#ifndef CKE_CROSS_NP
+#define CKE_CROSS_NP 2
+#endif
+#ifndef CKE_SELF_WAVES
+#define CKE_SELF_WAVES 8
+#endif
+#ifndef CKE_SELF_NP
+#define CKE_SELF_NP 4
+#endif
+constexpr int kCrossWaves = CKE_CROSS_WAVES;  // waves per cross-decode workgroup
+constexpr int kCrossNP = CKE_CROSS_NP;        // row passes per load tile
+constexpr int kSelfWaves = CKE_SELF_WAVES;
+constexpr int kSelfNP = CKE_SELF_NP;
 
 template <int D, typename TE, int NQ>
 hipError_t launch_cross_nq(const XattnLaunch& a, hipStream_t st) {
-    constexpr int NP = (sizeof(TE) == 4) ? 4 : 4;
+    // many queries already give each loaded row more work: keep their tiles short
+    constexpr int NP = (NQ > 2 && kCrossNP > 2) ? 2 : kCrossNP;
     dim3 grid(a.nsplit, a.H, a.B);
-    hipLaunchKernelGGL((xattn_decode_kernel<D, TE, NQ, kCrossWaves, NP>), grid,
+    hipLaunchKernelGGL((xattn_partial_kernel<D, TE, NQ, kCrossWaves, NP>), grid,
                        dim3(kCrossWaves * 64), 0, st, a.q,
                        static_cast<const TE*>(a.K), static_cast<const TE*>(a.V), a.out,
-                       a.part, a.counters, a.nq, a.max_q, a.H, a.T, a.nsplit, a.chunk,
-                       a.scale * kLog2e);
+                       a.part, a.nq, a.max_q, a.H, a.T, a.nsplit, a.chunk, a.scale * kLog2e);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || a.nsplit == 1) return e;
+    hipLaunchKernelGGL((xattn_merge_kernel<D>), dim3(a.H, a.B), dim3(256), 0, st, a.part, a.out,
+                       a.nq, a.max_q, a.H, a.nsplit);
     return hipGetLastError();
 }
 
@@ -197,7 +282,7 @@ hipError_t launch_cross_t(const XattnLaunch& a, hipStream_t st) {
 template <int D, typename TE>
 hipError_t launch_self_d(const SelfLaunch& a, hipStream_t st) {
     dim3 grid(a.H, a.S);
-    hipLaunchKernelGGL((selfattn_append_kernel<D, TE, kSelfWaves, 2>), grid,
+    hipLaunchKernelGGL((selfattn_append_kernel<D, TE, kSelfWaves, kSelfNP>), grid,
                        dim3(kSelfWaves * 64), 0, st, a.q, a.k_new, a.v_new,
                        static_cast<TE*>(a.K), static_cast<TE*>(a.V), a.out, a.H,
                        a.max_pos, a.pos, a.scale * kLog2e);

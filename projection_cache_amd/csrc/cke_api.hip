@@ -78,16 +78,24 @@ size_t region_elems(const cke_xattn_geom* g) {
     return (size_t)g->n_layers * g->n_streams * g->n_heads * (size_t)g->mem_len * g->head_dim;
 }
 
+#ifndef CKE_TARGET_WGS
+#define CKE_TARGET_WGS 1024
+#endif
+#ifndef CKE_MAX_SPLITS
+#define CKE_MAX_SPLITS 64
+#endif
+static_assert(CKE_MAX_SPLITS >= 1 && CKE_MAX_SPLITS <= cke::kMaxSplits, "split cap");
+
 // Split of the T memory rows of one (stream, head) across workgroups. Fixed
 // per geometry so that decode results are reproducible run to run. Aims for
-// about 1024 workgroups (4 per compute unit) but never fewer rows per
-// workgroup than one pass of its waves.
+// about CKE_TARGET_WGS workgroups (4 per compute unit) but never fewer rows
+// per workgroup than one pass of its waves.
 void split_plan(const cke_xattn_geom* g, int* nsplit, int* chunk) {
     const int kpp = cke::cross_keys_per_pass(g->head_dim, elem_bytes(g->cache_dtype));
     const long long bh = (long long)g->n_streams * g->n_heads;
     const int max_by_rows = (g->mem_len + kpp - 1) / kpp;
-    long long want = (1024 + bh - 1) / bh;
-    if (want > 64) want = 64;
+    long long want = (CKE_TARGET_WGS + bh - 1) / bh;
+    if (want > CKE_MAX_SPLITS) want = CKE_MAX_SPLITS;
     int s = (int)(want < max_by_rows ? want : max_by_rows);
     if (s < 1) s = 1;
     int c = (g->mem_len + s - 1) / s;
@@ -98,14 +106,9 @@ void split_plan(const cke_xattn_geom* g, int* nsplit, int* chunk) {
 
 constexpr size_t kAlign = 256;
 
-size_t counters_bytes(const cke_xattn_geom* g) {
-    const size_t n = (size_t)g->n_streams * g->n_heads * sizeof(unsigned);
-    return (n + kAlign - 1) / kAlign * kAlign;
-}
-
-size_t partials_bytes(const cke_xattn_geom* g, int nsplit) {
-    return (size_t)g->n_streams * g->max_q * g->n_heads * (size_t)nsplit * (g->head_dim + 2) *
-           sizeof(float);
+// Workspace: fp32 split partials [B][max_q][H][nsplit][D+2].
+size_t partial_words(const cke_xattn_geom* g, int nsplit) {
+    return (size_t)g->n_streams * g->max_q * g->n_heads * (size_t)nsplit * (g->head_dim + 2);
 }
 
 }  // namespace
@@ -141,7 +144,8 @@ size_t cke_xattn_workspace_bytes(const cke_xattn_geom* g) {
     if (check_geom(g) != CKE_OK) return 0;
     int s, c;
     split_plan(g, &s, &c);
-    return counters_bytes(g) + partials_bytes(g, s);
+    const size_t b = partial_words(g, s) * sizeof(float);
+    return b < kAlign ? kAlign : b;
 }
 
 int cke_xattn_cache_create(const cke_xattn_geom* g, void* k_dev, void* v_dev, void* ws_dev,
@@ -201,8 +205,6 @@ int cke_xattn_populate(cke_xattn_cache* c, const void* E, int e_dtype, const voi
     a.E = E;
     a.Kc = c->k;
     a.Vc = c->v;
-    a.counters = static_cast<unsigned*>(c->ws);
-    a.n_counters = g.n_streams * g.n_heads;
     a.L = g.n_layers;
     a.B = g.n_streams;
     a.T = g.mem_len;
@@ -236,8 +238,7 @@ int cke_xattn_decode(const float* q, int n_q, const cke_xattn_cache* c, int laye
     a.K = static_cast<const char*>(c->k) + off;
     a.V = static_cast<const char*>(c->v) + off;
     a.out = out;
-    a.counters = static_cast<unsigned*>(c->ws);
-    a.part = reinterpret_cast<float*>(static_cast<char*>(c->ws) + counters_bytes(&g));
+    a.part = static_cast<float*>(c->ws);
     a.B = g.n_streams;
     a.H = g.n_heads;
     a.T = g.mem_len;

@@ -38,33 +38,37 @@ __device__ __forceinline__ uint16_t to_bf16_bits(float x) {
 }
 __device__ __forceinline__ float round_to_bf16(float x) { return (float)(__bf16)x; }
 
-// Load 16 bytes of a cached row as fp32 values.
-__device__ __forceinline__ void load16(const float* __restrict__ p, float (&x)[4]) {
-    const float4 v = *reinterpret_cast<const float4*>(p);
-    x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
-}
-__device__ __forceinline__ void load16(const uint16_t* __restrict__ p, float (&x)[8]) {
-    const uint4 v = *reinterpret_cast<const uint4*>(p);
-    x[0] = bf16_lo(v.x); x[1] = bf16_hi(v.x);
-    x[2] = bf16_lo(v.y); x[3] = bf16_hi(v.y);
-    x[4] = bf16_lo(v.z); x[5] = bf16_hi(v.z);
-    x[6] = bf16_lo(v.w); x[7] = bf16_hi(v.w);
+// A lane's 16-byte share of a cached row is kept packed in registers (4 fp32
+// or 8 bf16 values) and widened to fp32 only where it is used, so bf16 rows
+// cost half the registers of fp32 ones.
+__device__ __forceinline__ uint4 load16(const void* __restrict__ p) {
+    return *reinterpret_cast<const uint4*>(p);
 }
 
-// The same elements from an fp32 source row, rounded to the storage precision
-// (used for the row a self-attention call appends: attention reads the value
-// as stored).
-__device__ __forceinline__ void load16_f32_as(const float* __restrict__ p, float (&x)[4]) {
-    const float4 v = *reinterpret_cast<const float4*>(p);
-    x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
+template <typename TE> __device__ __forceinline__ float elem(const uint4& r, int j);
+template <> __device__ __forceinline__ float elem<float>(const uint4& r, int j) {
+    const uint32_t w = j == 0 ? r.x : (j == 1 ? r.y : (j == 2 ? r.z : r.w));
+    return __uint_as_float(w);
 }
-__device__ __forceinline__ void load16_f32_as(const float* __restrict__ p, float (&x)[8]) {
+template <> __device__ __forceinline__ float elem<uint16_t>(const uint4& r, int j) {
+    const uint32_t w = (j >> 1) == 0 ? r.x : ((j >> 1) == 1 ? r.y : ((j >> 1) == 2 ? r.z : r.w));
+    return (j & 1) ? bf16_hi(w) : bf16_lo(w);
+}
+
+// The same 16-byte share built from an fp32 source row, rounded to the
+// storage type (the row a self-attention call appends: attention reads the
+// value as stored).
+template <typename TE> __device__ __forceinline__ uint4 pack16_from_f32(const float* __restrict__ p);
+template <> __device__ __forceinline__ uint4 pack16_from_f32<float>(const float* __restrict__ p) {
+    return *reinterpret_cast<const uint4*>(p);
+}
+template <> __device__ __forceinline__ uint4 pack16_from_f32<uint16_t>(const float* __restrict__ p) {
     const float4 a = *reinterpret_cast<const float4*>(p);
     const float4 b = *reinterpret_cast<const float4*>(p + 4);
-    x[0] = round_to_bf16(a.x); x[1] = round_to_bf16(a.y);
-    x[2] = round_to_bf16(a.z); x[3] = round_to_bf16(a.w);
-    x[4] = round_to_bf16(b.x); x[5] = round_to_bf16(b.y);
-    x[6] = round_to_bf16(b.z); x[7] = round_to_bf16(b.w);
+    auto pk = [](float lo, float hi) {
+        return (uint32_t)to_bf16_bits(lo) | ((uint32_t)to_bf16_bits(hi) << 16);
+    };
+    return make_uint4(pk(a.x, a.y), pk(a.z, a.w), pk(b.x, b.y), pk(b.z, b.w));
 }
 
 // Butterfly reductions over lane groups of a wave64.
@@ -112,10 +116,11 @@ struct WaveState {
 };
 
 // One wave attends its queries over rows [r0, r1) of K/V (rows D elements
-// apart). Rows are read NP passes at a time, all loads of a tile issued before
-// any arithmetic. If cur_row lies in the range, that row is taken from the
-// fp32 vectors cur_k / cur_v (rounded to the storage precision) instead of
-// memory.
+// apart). Rows are read in tiles of NP passes; the loads of the next tile are
+// issued before the current tile is computed (register double buffering), so
+// each wave keeps up to 2*NP 16-byte loads per operand in flight. If cur_row
+// lies in the range, that row is taken from the fp32 vectors cur_k / cur_v
+// (rounded to the storage type) instead of memory.
 template <int D, typename TE, int NQ, int NP>
 __device__ __forceinline__ void wave_attend(
     const TE* __restrict__ K, const TE* __restrict__ V, int r0, int r1,
@@ -125,28 +130,28 @@ __device__ __forceinline__ void wave_attend(
 {
     using RM = RowMap<D, TE>;
     constexpr int VEC = RM::kVec, LPK = RM::kLPK, KPW = RM::kKPW;
+    constexpr int TILE = NP * KPW;
     const int lane = threadIdx.x & 63;
     const int grp = lane / LPK;
     const int sub = lane % LPK;
 
-    for (int base = r0; base < r1; base += NP * KPW) {
-        float kf[NP][VEC], vf[NP][VEC];
-        bool valid[NP];
+    auto load_tile = [&](int base, uint4 (&kb)[NP], uint4 (&vb)[NP]) {
 #pragma unroll
         for (int p = 0; p < NP; ++p) {
             const int row = base + p * KPW + grp;
-            valid[p] = row < r1;
-            if (valid[p] && row != cur_row) {
-                load16(K + (size_t)row * D + sub * VEC, kf[p]);
-                load16(V + (size_t)row * D + sub * VEC, vf[p]);
-            } else if (valid[p]) {
-                load16_f32_as(cur_k + sub * VEC, kf[p]);
-                load16_f32_as(cur_v + sub * VEC, vf[p]);
+            if (row < r1 && row != cur_row) {
+                kb[p] = load16(K + (size_t)row * D + sub * VEC);
+                vb[p] = load16(V + (size_t)row * D + sub * VEC);
+            } else if (row < r1) {
+                kb[p] = pack16_from_f32<TE>(cur_k + sub * VEC);
+                vb[p] = pack16_from_f32<TE>(cur_v + sub * VEC);
             } else {
-#pragma unroll
-                for (int j = 0; j < VEC; ++j) { kf[p][j] = 0.f; vf[p][j] = 0.f; }
+                kb[p] = make_uint4(0u, 0u, 0u, 0u);
+                vb[p] = make_uint4(0u, 0u, 0u, 0u);
             }
         }
+    };
+    auto compute_tile = [&](int base, const uint4 (&kb)[NP], const uint4 (&vb)[NP]) {
 #pragma unroll
         for (int i = 0; i < NQ; ++i) {
             if (i < nq) {
@@ -156,9 +161,9 @@ __device__ __forceinline__ void wave_attend(
                 for (int p = 0; p < NP; ++p) {
                     float d = 0.f;
 #pragma unroll
-                    for (int j = 0; j < VEC; ++j) d = fmaf(q[i][j], kf[p][j], d);
+                    for (int j = 0; j < VEC; ++j) d = fmaf(q[i][j], elem<TE>(kb[p], j), d);
                     d = xor_sum<1, LPK>(d);
-                    s[p] = valid[p] ? d * sl2 : -INFINITY;
+                    s[p] = (base + p * KPW + grp < r1) ? d * sl2 : -INFINITY;
                     mt = fmaxf(mt, s[p]);
                 }
                 mt = xor_max<LPK, 64>(mt);
@@ -173,12 +178,26 @@ __device__ __forceinline__ void wave_attend(
                         const float e = fast_exp2(s[p] - mn);
                         st.l[i] += e;
 #pragma unroll
-                        for (int j = 0; j < VEC; ++j) st.acc[i][j] = fmaf(e, vf[p][j], st.acc[i][j]);
+                        for (int j = 0; j < VEC; ++j)
+                            st.acc[i][j] = fmaf(e, elem<TE>(vb[p], j), st.acc[i][j]);
                     }
                     st.m[i] = mn;
                 }
             }
         }
+    };
+
+    if (r0 >= r1) return;
+    uint4 ka[NP], va[NP], kb2[NP], vb2[NP];
+    load_tile(r0, ka, va);
+    for (int base = r0; base < r1; base += 2 * TILE) {
+        const bool more = base + TILE < r1;
+        if (more) load_tile(base + TILE, kb2, vb2);
+        compute_tile(base, ka, va);
+        if (!more) break;
+        const bool more2 = base + 2 * TILE < r1;
+        if (more2) load_tile(base + 2 * TILE, ka, va);
+        compute_tile(base + TILE, kb2, vb2);
     }
 }
 

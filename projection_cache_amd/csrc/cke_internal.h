@@ -15,8 +15,7 @@ struct XattnLaunch {
     const void* K;       // layer slab base, [B][H][T][D]
     const void* V;
     float* out;
-    float* part;         // workspace partials
-    unsigned* counters;  // workspace counters, one per (b, h)
+    float* part;         // workspace: split partials [B][max_q][H][nsplit][D+2]
     int B, H, T, D, nq, max_q, nsplit, chunk;
     float scale;
     bool bf16;
@@ -40,13 +39,14 @@ struct WeightTable {
     const void* w[2 * kMaxLayers];
 };
 
+// Largest number of key splits a decode call may use.
+constexpr int kMaxSplits = 64;
+
 struct PopulateLaunch {
     const void* E;       // [B*T][d_model]
     WeightTable wt;
     void* Kc;            // [L][B][H][T][D]
     void* Vc;
-    unsigned* counters;  // cleared by the launch
-    int n_counters;
     int L, B, T, dm, H, D;
     bool bf16;
 };
@@ -55,6 +55,7 @@ struct PopulateLaunch {
 int cross_keys_per_pass(int D, int elem_bytes);
 
 hipError_t launch_xattn_decode(const XattnLaunch& a, hipStream_t st);
+
 hipError_t launch_selfattn_append(const SelfLaunch& a, hipStream_t st);
 hipError_t launch_populate(const PopulateLaunch& a, hipStream_t st);
 

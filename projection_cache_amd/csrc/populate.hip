@@ -30,8 +30,6 @@ struct GemmArgs {
     WeightTable wt;
     void* Kc;
     void* Vc;
-    unsigned* counters;
-    int n_counters;
     int M, dm, T, L, B, H, D;
 };
 
@@ -77,11 +75,6 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, const f32x16 (&acc)[
         }
 }
 
-__device__ __forceinline__ void clear_counters(const GemmArgs& a) {
-    if (blockIdx.x == 0 && blockIdx.y == 0)
-        for (int i = threadIdx.x; i < a.n_counters; i += blockDim.x) a.counters[i] = 0u;
-}
-
 // fp32 operands on v_mfma_f32_32x32x2_f32. LDS holds both tiles k-major:
 // As[k][m] (transposed on store) and Bs[k][n], so a half-wave reads 32
 // consecutive floats per operand.
@@ -94,7 +87,6 @@ __global__ __launch_bounds__(256) void populate_f32_kernel(GemmArgs a)
     __shared__ float As[BK][BM + 4];
     __shared__ float Bs[BK][BN + 4];
 
-    clear_counters(a);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WGN, wn = wave % WGN;
     const int HD = a.H * a.D;
@@ -162,7 +154,6 @@ __global__ __launch_bounds__(256) void populate_bf16_kernel(GemmArgs a)
     __shared__ __attribute__((aligned(16))) uint16_t As[BM][LDK];
     __shared__ __attribute__((aligned(16))) uint16_t Bs[BN][LDK];
 
-    clear_counters(a);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WGN, wn = wave % WGN;
     const int HD = a.H * a.D;
@@ -241,8 +232,6 @@ hipError_t launch_populate(const PopulateLaunch& a, hipStream_t st) {
     g.wt = a.wt;
     g.Kc = a.Kc;
     g.Vc = a.Vc;
-    g.counters = a.counters;
-    g.n_counters = a.n_counters;
     g.M = a.B * a.T;
     g.dm = a.dm;
     g.T = a.T;

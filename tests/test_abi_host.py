@@ -85,7 +85,7 @@ def test_workspace_and_split_plan():
         assert 1 <= s <= 64
         ws = pc.cke_xattn_workspace_bytes(g)
         need = g.n_streams * g.max_q * g.n_heads * s * (g.head_dim + 2) * 4
-        assert ws >= need + g.n_streams * g.n_heads * 4
+        assert ws >= need
     # Whisper Base splits its 1500 rows across workgroups, Q-Former does not
     assert pc.cke_xattn_num_splits(base_geom()) > 1
     assert pc.cke_xattn_num_splits(base_geom(n_layers=2, n_streams=100, mem_len=15, d_model=2048,
