@@ -11,9 +11,13 @@ The per-call inputs (queries, new K/V rows) are seeded synthetic tensors,
 resident in device memory before timing starts.
 
 value = decode tokens per second over the timed windows (tokens of all
-sequences, populate included in the time). Kernel durations come from HIP
-events recorded on the launch stream around every call of one instrumented
-window run right after the timed windows, with the same inputs and kernels.
+sequences, populate included in the time), each window replayed as one HIP
+graph. Per-call durations come from three more graphs captured from the same
+window, each holding only one kind of call (all populate, all self-attention
+or all cross-attention calls of the window, same inputs, same order, same
+stream), timed with HIP events around their replay: graph-dispatched kernels
+run back to back, so replay time / calls is the kernels' own duration
+(rocprofv3 kernel durations agree to a few percent).
 
 Prints one JSON line.
 """
@@ -119,40 +123,29 @@ class Workload:
         g = self.g
         return g.steps * (g.n_seqs if g.n_seqs else g.n_streams * g.n_q)
 
-    def window(self, stream, events=None, prime=None):
-        """Enqueue one decode window. If events is a dict, record (start, end)
-        event pairs around every call, by kernel family. prime() is called
-        before the populate and before every decode step; it enqueues a spin
-        kernel long enough for the host to queue the step's calls and events
-        before the GPU reaches them, so no event interval contains host time."""
-        g, pc, torch = self.g, self.pc, self.torch
-        ev = events is not None
-
-        def timed(kind, fn):
-            if ev:
-                s = torch.cuda.Event(enable_timing=True)
-                e = torch.cuda.Event(enable_timing=True)
-                s.record(stream)
-                fn()
-                e.record(stream)
-                events.setdefault(kind, []).append((s, e))
-            else:
-                fn()
-
-        if prime:
-            prime()
-        timed("populate", lambda: pc.cke_xattn_populate(self.cache, self.E, self.WK, self.WV,
-                                                        stream=stream))
+    def window(self, stream, kinds=("populate", "selfattn", "xattn_decode")):
+        """Enqueue one decode window on `stream`, or only the calls of the
+        given kinds (in window order)."""
+        g, pc = self.g, self.pc
+        if "populate" in kinds:
+            pc.cke_xattn_populate(self.cache, self.E, self.WK, self.WV, stream=stream)
         for t in range(g.steps):
-            if prime:
-                prime()
             for l in range(g.n_layers):
-                if g.n_seqs:
-                    timed("selfattn", lambda: pc.cke_selfattn_decode_append(
-                        self.qs[t, l], self.kn[t, l], self.vn[t, l], self.kv[l], t, g.scale,
-                        self.out_s[t, l], stream=stream))
-                timed("xattn_decode", lambda: pc.cke_xattn_decode(
-                    self.qc[t, l], self.cache, l, g.scale, self.out_c[t, l], stream=stream))
+                if g.n_seqs and "selfattn" in kinds:
+                    pc.cke_selfattn_decode_append(self.qs[t, l], self.kn[t, l], self.vn[t, l],
+                                                  self.kv[l], t, g.scale, self.out_s[t, l],
+                                                  stream=stream)
+                if "xattn_decode" in kinds:
+                    pc.cke_xattn_decode(self.qc[t, l], self.cache, l, g.scale, self.out_c[t, l],
+                                        stream=stream)
+
+    def calls(self, kind):
+        g = self.g
+        if kind == "populate":
+            return 1
+        if kind == "selfattn":
+            return g.steps * g.n_layers if g.n_seqs else 0
+        return g.steps * g.n_layers
 
     # algorithmic work -------------------------------------------------------
     def elem(self):
@@ -265,14 +258,19 @@ def main():
 
     stream = torch.cuda.Stream()
     torch.cuda.synchronize()
-    if args.mode == "graph":
+
+    def capture(kinds):
         with torch.cuda.stream(stream):
-            w.window(stream)           # warm the kernels once outside capture
+            w.window(stream, kinds)    # warm the kernels once outside capture
         stream.synchronize()
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph, stream=stream):
-            w.window(torch.cuda.current_stream())
+            w.window(torch.cuda.current_stream(), kinds)
         torch.cuda.synchronize()
+        return graph
+
+    if args.mode == "graph":
+        graph = capture(("populate", "selfattn", "xattn_decode"))
 
         def run():
             with torch.cuda.stream(stream):
@@ -292,18 +290,27 @@ def main():
     ms_per_step = elapsed / args.steps * 1e3
     tok_s = w.tokens_per_window * args.steps / elapsed
 
-    # instrumented window: HIP events around every call on the launch stream,
-    # each decode step queued behind a spin kernel (host never starves the GPU)
-    events = {}
-
-    def prime():
-        with torch.cuda.stream(stream):
-            torch.cuda._sleep(int(3.0e6 + 2.5e5 * g.n_layers))
-
-    w.window(stream, events, prime)
-    torch.cuda.synchronize()
-    dur = {k: [s.elapsed_time(e) * 1e-3 for s, e in v] for k, v in events.items()}
-    avg = {k: float(np.mean(v)) for k, v in dur.items()}
+    # per-call durations: one graph per call kind, replayed, timed with events
+    avg, total = {}, {}
+    for kind in ("populate", "selfattn", "xattn_decode"):
+        n = w.calls(kind)
+        if n == 0:
+            continue
+        gk = capture((kind,))
+        best = float("inf")
+        for _ in range(3):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            with torch.cuda.stream(stream):
+                gk.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            best = min(best, e0.elapsed_time(e1) * 1e-3)
+        avg[kind] = best / n
+        total[kind] = best
+        del gk
+    dur = {k: [avg[k]] * w.calls(k) for k in avg}
 
     cross_b = w.cross_bytes_per_call()
     cross_gbs = cross_b / avg["xattn_decode"] / 1e9
@@ -347,6 +354,7 @@ def main():
                      "mfma": "v_mfma_f32_32x32x16_bf16" if w.bf16 else "v_mfma_f32_32x32x2_f32"},
         "kernels": kernels,
         "time_share": {k: v / sum(share.values()) for k, v in share.items()},
+        "kernel_sum_ms_per_step": sum(total.values()) * 1e3,
         "dominant_kernel": dominant,
         "gpu": torch.cuda.get_device_name(0),
         "git": _git_sha(),

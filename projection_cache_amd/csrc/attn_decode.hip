@@ -126,16 +126,15 @@ __global__ __launch_bounds__(256) void xattn_merge_kernel(
         sLs[i * kMaxSplits + s] = p[1];
     }
     __syncthreads();
-    for (int i = tid; i < nq; i += 256) {
-        float M = -INFINITY;
-        for (int s = 0; s < nsplit; ++s) M = fmaxf(M, sF[i * kMaxSplits + s]);
-        float L = 0.f;
-        for (int s = 0; s < nsplit; ++s) {
-            const float f = fast_exp2(sF[i * kMaxSplits + s] - M);
-            sF[i * kMaxSplits + s] = f;
-            L = fmaf(sLs[i * kMaxSplits + s], f, L);
-        }
-        sSum[i] = L;
+    // one wave per query: lane s holds split s (nsplit <= 64)
+    for (int i = tid >> 6; i < nq; i += 4) {
+        const int s = tid & 63;
+        const float m = s < nsplit ? sF[i * kMaxSplits + s] : -INFINITY;
+        const float M = xor_max<1, 64>(m);
+        const float f = s < nsplit ? fast_exp2(m - M) : 0.f;
+        const float L = xor_sum<1, 64>(s < nsplit ? sLs[i * kMaxSplits + s] * f : 0.f);
+        if (s < nsplit) sF[i * kMaxSplits + s] = f;
+        if (s == 0) sSum[i] = L;
     }
     __syncthreads();
     for (int idx = tid; idx < n_out * G; idx += 256) {

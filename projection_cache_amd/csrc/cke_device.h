@@ -71,6 +71,25 @@ template <> __device__ __forceinline__ uint4 pack16_from_f32<uint16_t>(const flo
     return make_uint4(pk(a.x, a.y), pk(a.z, a.w), pk(b.x, b.y), pk(b.z, b.w));
 }
 
+// Sum over aligned groups of N lanes (N = 1..32) using DPP lane permutes for
+// the steps inside a 16-lane row (quad_perm xor 1, xor 2; half-row mirror;
+// row mirror) and a bpermute for the step across rows. After the in-row
+// steps every lane of a group holds the group's sum.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
+    static_assert(N == 1 || N == 2 || N == 4 || N == 8 || N == 16 || N == 32, "group size");
+    if constexpr (N >= 2) v += dpp<0xB1>(v);   // quad_perm [1,0,3,2]
+    if constexpr (N >= 4) v += dpp<0x4E>(v);   // quad_perm [2,3,0,1]
+    if constexpr (N >= 8) v += dpp<0x141>(v);  // row_half_mirror
+    if constexpr (N >= 16) v += dpp<0x140>(v); // row_mirror
+    if constexpr (N >= 32) v += __shfl_xor(v, 16, 64);
+    return v;
+}
+
 // Butterfly reductions over lane groups of a wave64.
 template <int FROM, int TO>
 __device__ __forceinline__ float xor_sum(float v) {
@@ -96,9 +115,10 @@ struct RowMap {
     static_assert(kLPK >= 1 && kLPK <= 64 && (64 % kLPK) == 0, "bad head_dim");
 };
 
-// Running softmax state of one wave for up to NQ queries. m is in the base-2
-// domain (scores pre-multiplied by scale*log2 e); l and acc are partial over
-// this lane's row group until wg_merge() reduces them across groups.
+// Running softmax state of one lane group (the LPK lanes sharing a row slot)
+// for up to NQ queries: m is the group's running max in the base-2 domain
+// (scores pre-multiplied by scale*log2 e), l and acc the sums relative to it.
+// wg_merge() combines the groups of a wave and then the waves.
 template <int NQ, int VEC>
 struct WaveState {
     float m[NQ];
@@ -151,6 +171,9 @@ __device__ __forceinline__ void wave_attend(
             }
         }
     };
+    // Each group of LPK lanes (one row slot) keeps its own running max, so a
+    // tile needs no communication across groups; groups are merged once, in
+    // wg_merge. Lanes of a group hold identical scores and max.
     auto compute_tile = [&](int base, const uint4 (&kb)[NP], const uint4 (&vb)[NP]) {
 #pragma unroll
         for (int i = 0; i < NQ; ++i) {
@@ -162,27 +185,24 @@ __device__ __forceinline__ void wave_attend(
                     float d = 0.f;
 #pragma unroll
                     for (int j = 0; j < VEC; ++j) d = fmaf(q[i][j], elem<TE>(kb[p], j), d);
-                    d = xor_sum<1, LPK>(d);
+                    d = group_sum<LPK>(d);
                     s[p] = (base + p * KPW + grp < r1) ? d * sl2 : -INFINITY;
                     mt = fmaxf(mt, s[p]);
                 }
-                mt = xor_max<LPK, 64>(mt);
                 const float mn = fmaxf(st.m[i], mt);
-                if (mn != -INFINITY) {  // wave-uniform
-                    const float alpha = fast_exp2(st.m[i] - mn);
-                    st.l[i] *= alpha;
+                const float alpha = mn == -INFINITY ? 1.f : fast_exp2(st.m[i] - mn);
+                st.l[i] *= alpha;
 #pragma unroll
-                    for (int j = 0; j < VEC; ++j) st.acc[i][j] *= alpha;
+                for (int j = 0; j < VEC; ++j) st.acc[i][j] *= alpha;
 #pragma unroll
-                    for (int p = 0; p < NP; ++p) {
-                        const float e = fast_exp2(s[p] - mn);
-                        st.l[i] += e;
+                for (int p = 0; p < NP; ++p) {
+                    const float e = s[p] == -INFINITY ? 0.f : fast_exp2(s[p] - mn);
+                    st.l[i] += e;
 #pragma unroll
-                        for (int j = 0; j < VEC; ++j)
-                            st.acc[i][j] = fmaf(e, elem<TE>(vb[p], j), st.acc[i][j]);
-                    }
-                    st.m[i] = mn;
+                    for (int j = 0; j < VEC; ++j)
+                        st.acc[i][j] = fmaf(e, elem<TE>(vb[p], j), st.acc[i][j]);
                 }
+                st.m[i] = mn;
             }
         }
     };
@@ -216,9 +236,13 @@ __device__ __forceinline__ void wg_merge(
 #pragma unroll
     for (int i = 0; i < NQ; ++i) {
         if (i < nq) {
-            st.l[i] = xor_sum<LPK, 64>(st.l[i]);
+            // merge the row groups of this wave: common max, rescale, sum
+            const float M = xor_max<LPK, 64>(st.m[i]);
+            const float f = M == -INFINITY ? 0.f : fast_exp2(st.m[i] - M);
+            st.m[i] = M;
+            st.l[i] = xor_sum<LPK, 64>(st.l[i] * f);
 #pragma unroll
-            for (int j = 0; j < VEC; ++j) st.acc[i][j] = xor_sum<LPK, 64>(st.acc[i][j]);
+            for (int j = 0; j < VEC; ++j) st.acc[i][j] = xor_sum<LPK, 64>(st.acc[i][j] * f);
             if (lane < LPK) {
 #pragma unroll
                 for (int j = 0; j < VEC; ++j) wa[(w * NQ + i) * D + lane * VEC + j] = st.acc[i][j];
