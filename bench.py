@@ -65,6 +65,11 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="approximate CPU time budget of the oracle baseline sample")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain device copy of known size (counter calibration)")
+    ap.add_argument("--counters", action="store_true",
+                    help="only run --steps windows with eager launches and no graph capture "
+                         "(the mode hardware-counter passes use)")
     return ap.parse_args()
 
 
@@ -220,6 +225,35 @@ def cpu_baseline(name, budget_s):
             "host_cpu": _host_cpu()}
 
 
+def measured_traffic(config):
+    """HBM bytes per cross-attention decode call (split + merge kernels) from the
+    committed rocprofv3 counter summary, scaled by its copy calibration; None if
+    the decode kernel sources changed since the counters were taken or the
+    workload was not counted."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    try:
+        t = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    for f in ("attn_decode.hip", "cke_device.h"):
+        src = os.path.join(ROOT, "projection_cache_amd", "csrc", f)
+        if hashlib.sha256(open(src, "rb").read()).hexdigest() != t["sources_sha256"].get(f):
+            return None
+    per = t["per_dispatch_KiB"].get(config)
+    if not per:
+        return None
+    cal = t["calibration"]
+    read = write = 0.0
+    for k, v in per.items():
+        if "xattn_partial_kernel" in k or "xattn_merge_kernel" in k:
+            if "FETCH_SIZE" not in v or "WRITE_SIZE" not in v:
+                return None
+            read += v["FETCH_SIZE"] * 1024 / cal["read_factor"]
+            write += v["WRITE_SIZE"] * 1024 / cal["write_factor"]
+    return {"bytes": read + write, "read": read, "write": write}
+
+
 def _host_cpu():
     try:
         for line in open("/proc/cpuinfo"):
@@ -253,11 +287,31 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     torch.cuda.set_device(0)
+    if args.calibrate_copy:
+        # plain copy kernel of known size: HBM counters per dispatch are read
+        # against its 256 MiB read + 256 MiB write
+        n = 64 << 20
+        src = torch.empty(n, device="cuda").normal_()
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes_read": n * 4, "calibrate_copy_bytes_written": n * 4,
+                          "dispatches": 5}))
+        return
     w = Workload(args.config, torch, pc)
     g = w.g
 
     stream = torch.cuda.Stream()
     torch.cuda.synchronize()
+    if args.counters:
+        for _ in range(args.steps):
+            w.window(stream)
+        torch.cuda.synchronize()
+        print(json.dumps({"counters_windows": args.steps, "config": args.config,
+                          "xattn_bytes_per_call": w.cross_bytes_per_call(),
+                          "xattn_calls_per_window": w.calls("xattn_decode")}))
+        return
 
     def capture(kinds):
         with torch.cuda.stream(stream):
@@ -314,6 +368,7 @@ def main():
 
     cross_b = w.cross_bytes_per_call()
     cross_gbs = cross_b / avg["xattn_decode"] / 1e9
+    traffic = measured_traffic(args.config)
     kernels = {
         "xattn_decode": {"avg_us": avg["xattn_decode"] * 1e6, "calls_per_step": len(dur["xattn_decode"]),
                          "bytes_per_call": cross_b, "GB_s": cross_gbs},
@@ -345,9 +400,12 @@ def main():
         "config": {"workload": WORKLOAD_TEXT[args.config], "name": args.config,
                    "tokens_per_step": w.tokens_per_window, "decode_steps": g.steps,
                    "layers": g.n_layers, "mode": args.mode},
-        "roofline": {"bound": "hbm", "kernel": "xattn_decode", "achieved": cross_gbs,
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": cross_gbs / HBM_PEAK_GBS,
-                     "traffic": None,
+        "roofline": {"bound": "hbm",
+                     "kernel": "cke_xattn_decode (xattn_partial_kernel + xattn_merge_kernel)",
+                     "achieved": cross_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": cross_gbs / HBM_PEAK_GBS,
+                     "traffic": traffic["bytes"] if traffic else None,
+                     "traffic_read_write": [traffic["read"], traffic["write"]] if traffic else None,
                      "bytes_per_launch": cross_b, "avg_launch_us": avg["xattn_decode"] * 1e6},
         "populate": {"tflops": pop_tflops, "peak_tflops": MFMA_PEAK_TFLOPS[g.dtype],
                      "frac": pop_tflops / MFMA_PEAK_TFLOPS[g.dtype],
