@@ -46,7 +46,8 @@ __global__ __launch_bounds__(NW * 64) void xattn_partial_kernel(
     const size_t bh = (size_t)b * H + h;
     const TE* K = Kl + bh * (size_t)T * D;
     const TE* V = Vl + bh * (size_t)T * D;
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
     const int sub = lane % LPK;
 
     float qr[NQ][VEC];
@@ -83,90 +84,112 @@ __global__ __launch_bounds__(NW * 64) void xattn_partial_kernel(
     }
 }
 
-// Grid: (H, B), 256 threads. Combines the nsplit partials of each (stream,
-// query, head) of one head:
+// Grid: (H, B). Combines the nsplit partials of each (stream, query, head)
+// of one head:
 //   M = max_s M_s,  L = sum_s L_s 2^(M_s - M),  out = sum_s A_s 2^(M_s - M) / L
-// Thread (o, g) with o = (query, dim) and group g < G = 256 / (nq*D) takes
-// splits s = g, g+G, ... Every load a thread needs (its acc values and, for
-// the first nq*nsplit threads, one (M, L) pair) is issued before any result
-// is used, so the merge costs one memory round trip; groups are then summed
-// in a fixed order (deterministic).
+// Thread (o, g), o = (query, dim), g < G = ceil(nsplit / kMergeBatch), takes
+// splits s = g, g+G, ... (at most kMergeBatch of them). It loads (M_s, L_s,
+// A_s[d]) of all its splits at once -- clamped, branch-free addresses, so
+// every load is in flight together and the merge costs one memory round
+// trip -- and folds them in ascending s with the running-max update. Groups
+// are then combined through LDS in ascending g (deterministic). Dynamic LDS:
+// 3 floats per (o, g).
+constexpr int kMergeBatch = 16;
+
 template <int D>
-__global__ __launch_bounds__(256) void xattn_merge_kernel(
+__global__ __launch_bounds__(1024) void xattn_merge_kernel(
     const float* __restrict__ part, float* __restrict__ out, int nq, int max_q, int H,
     int nsplit)
 {
-    constexpr int kBatch = 16;
-    __shared__ float sF[8 * kMaxSplits];   // per (query, split): max, then weight
-    __shared__ float sLs[8 * kMaxSplits];  // per (query, split): sum
-    __shared__ float sSum[8];
-    __shared__ float sAcc[256];
+    extern __shared__ float smem[];
     const int h = blockIdx.x, b = blockIdx.y;
-    auto slot = [&](int i, int s) -> const float* {
-        return part + ((((size_t)b * max_q + i) * H + h) * nsplit + s) * (D + 2);
-    };
     const int n_out = nq * D;
-    const int G = n_out >= 256 ? 1 : 256 / n_out;
-    const int tid = threadIdx.x;
-
-    // first batch of acc loads for this thread's first output
-    const int o0 = tid % n_out, g0 = tid / n_out;
-    float av[kBatch];
-    if (tid < n_out * G) {
-#pragma unroll
-        for (int j = 0; j < kBatch; ++j) {
-            const int s = g0 + j * G;
-            av[j] = s < nsplit ? slot(o0 / D, s)[2 + o0 % D] : 0.f;
-        }
-    }
-    for (int idx = tid; idx < nq * nsplit; idx += 256) {
-        const int i = idx / nsplit, s = idx % nsplit;
-        const float* p = slot(i, s);
-        sF[i * kMaxSplits + s] = p[0];
-        sLs[i * kMaxSplits + s] = p[1];
-    }
-    __syncthreads();
-    // one wave per query: lane s holds split s (nsplit <= 64)
-    for (int i = tid >> 6; i < nq; i += 4) {
-        const int s = tid & 63;
-        const float m = s < nsplit ? sF[i * kMaxSplits + s] : -INFINITY;
-        const float M = xor_max<1, 64>(m);
-        const float f = s < nsplit ? fast_exp2(m - M) : 0.f;
-        const float L = xor_sum<1, 64>(s < nsplit ? sLs[i * kMaxSplits + s] * f : 0.f);
-        if (s < nsplit) sF[i * kMaxSplits + s] = f;
-        if (s == 0) sSum[i] = L;
-    }
-    __syncthreads();
-    for (int idx = tid; idx < n_out * G; idx += 256) {
+    const int G = (nsplit + kMergeBatch - 1) / kMergeBatch;
+    float* sm = smem;
+    float* sl = smem + n_out * G;
+    float* sa = smem + 2 * n_out * G;
+    for (int idx = threadIdx.x; idx < n_out * G; idx += blockDim.x) {
         const int o = idx % n_out, g = idx / n_out;
         const int i = o / D, d = o % D;
-        float A = 0.f;
-        for (int s0 = g; s0 < nsplit; s0 += kBatch * G) {
-            if (!(idx == tid && s0 == g)) {
+        const float* p0 = part + (((size_t)b * max_q + i) * H + h) * (size_t)nsplit * (D + 2);
+        float pm[kMergeBatch], pl[kMergeBatch], pa[kMergeBatch];
 #pragma unroll
-                for (int j = 0; j < kBatch; ++j) {
-                    const int s = s0 + j * G;
-                    av[j] = s < nsplit ? slot(i, s)[2 + d] : 0.f;
-                }
-            }
+        for (int j = 0; j < kMergeBatch; ++j) {
+            const int s = min(g + j * G, nsplit - 1);
+            const float* p = p0 + (size_t)s * (D + 2);
+            pm[j] = p[0];
+            pl[j] = p[1];
+            pa[j] = p[2 + d];
+        }
+        float m = -INFINITY, l = 0.f, a = 0.f;
 #pragma unroll
-            for (int j = 0; j < kBatch; ++j) {
-                const int s = s0 + j * G;
-                if (s < nsplit) A = fmaf(av[j], sF[i * kMaxSplits + s], A);
+        for (int j = 0; j < kMergeBatch; ++j) {
+            if (g + j * G < nsplit) {
+                const float mn = fmaxf(m, pm[j]);
+                const float f_old = fast_exp2(m - mn);   // m = -inf on the first split: 0
+                const float f_new = fast_exp2(pm[j] - mn);
+                l = fmaf(l, f_old, pl[j] * f_new);
+                a = fmaf(a, f_old, pa[j] * f_new);
+                m = mn;
             }
         }
-        if (G == 1)
-            out[(((size_t)b * nq + i) * H + h) * D + d] = A / sSum[i];
-        else
-            sAcc[idx] = A;
+        sm[idx] = m;
+        sl[idx] = l;
+        sa[idx] = a;
     }
-    if (G > 1) {
-        __syncthreads();
-        for (int o = tid; o < n_out; o += 256) {
-            float A = 0.f;
-            for (int g = 0; g < G; ++g) A += sAcc[g * n_out + o];
-            const int i = o / D, d = o % D;
-            out[(((size_t)b * nq + i) * H + h) * D + d] = A / sSum[i];
+    __syncthreads();
+    for (int o = threadIdx.x; o < n_out; o += blockDim.x) {
+        float m = -INFINITY, l = 0.f, a = 0.f;
+        for (int g = 0; g < G; ++g) {
+            const float mg = sm[g * n_out + o];
+            const float mn = fmaxf(m, mg);
+            const float f_old = fast_exp2(m - mn);
+            const float f_new = fast_exp2(mg - mn);
+            l = fmaf(l, f_old, sl[g * n_out + o] * f_new);
+            a = fmaf(a, f_old, sa[g * n_out + o] * f_new);
+            m = mn;
+        }
+        const int i = o / D, d = o % D;
+        out[(((size_t)b * nq + i) * H + h) * D + d] = a / l;
+    }
+}
+
+// Short memories (e.g. 15-frame blocks): one wave per (stream, head), NW of
+// them per workgroup, each attending over all T rows on its own, so no
+// cross-wave merge and no split. Grid: ceil(B*H / NW).
+template <int D, typename TE, int NQ, int NW, int NP>
+__global__ __launch_bounds__(NW * 64) void xattn_short_kernel(
+    const float* __restrict__ q, const TE* __restrict__ Kl, const TE* __restrict__ Vl,
+    float* __restrict__ out, int nq, int H, int T, int n_bh, float sl2)
+{
+    using RM = RowMap<D, TE>;
+    constexpr int VEC = RM::kVec, LPK = RM::kLPK;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+    const int bh = blockIdx.x * NW + w;
+    if (bh >= n_bh) return;   // whole wave; this kernel has no barrier
+    const int b = bh / H, h = bh % H;
+    const int lane = threadIdx.x & 63, sub = lane % LPK;
+    const TE* K = Kl + (size_t)bh * T * D;
+    const TE* V = Vl + (size_t)bh * T * D;
+    float qr[NQ][VEC];
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) {
+#pragma unroll
+        for (int j = 0; j < VEC; ++j)
+            qr[i][j] = (i < nq) ? q[(((size_t)b * nq + i) * H + h) * D + sub * VEC + j] : 0.f;
+    }
+    WaveState<NQ, VEC> st;
+    st.init();
+    wave_attend<D, TE, NQ, NP>(K, V, 0, T, qr, nq, sl2, -1, nullptr, nullptr, st);
+    wave_merge_groups<D, TE, NQ>(st, nq);
+    if (lane < LPK) {
+#pragma unroll
+        for (int i = 0; i < NQ; ++i) {
+            if (i < nq) {
+                float* o = out + (((size_t)b * nq + i) * H + h) * D + sub * VEC;
+#pragma unroll
+                for (int j = 0; j < VEC; ++j) o[j] = st.acc[i][j] / st.l[i];
+            }
         }
     }
 }
@@ -194,10 +217,12 @@ __global__ __launch_bounds__(NW * 64) void selfattn_append_kernel(
     TE* V = Vc + bh * (size_t)max_pos * D;
     const float* kn = k_new + bh * D;
     const float* vn = v_new + bh * D;
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
     const int sub = lane % LPK;
 
-    // scatter the new row
+    // scatter the new row; no wave reads it from memory (wave_attend takes it
+    // from k_new / v_new)
     for (int d = threadIdx.x; d < D; d += NW * 64) {
         if constexpr (sizeof(TE) == 2) {
             K[(size_t)pos * D + d] = to_bf16_bits(kn[d]);
@@ -244,8 +269,20 @@ constexpr int kCrossNP = CKE_CROSS_NP;        // row passes per load tile
 constexpr int kSelfWaves = CKE_SELF_WAVES;
 constexpr int kSelfNP = CKE_SELF_NP;
 
+// Memories this short go to xattn_short_kernel.
+constexpr int kShortRows = kShortMemRows;
+
 template <int D, typename TE, int NQ>
 hipError_t launch_cross_nq(const XattnLaunch& a, hipStream_t st) {
+    if (a.T <= kShortRows) {
+        constexpr int NW = 4;
+        const int n_bh = a.B * a.H;
+        hipLaunchKernelGGL((xattn_short_kernel<D, TE, NQ, NW, 2>), dim3((n_bh + NW - 1) / NW),
+                           dim3(NW * 64), 0, st, a.q, static_cast<const TE*>(a.K),
+                           static_cast<const TE*>(a.V), a.out, a.nq, a.H, a.T, n_bh,
+                           a.scale * kLog2e);
+        return hipGetLastError();
+    }
     // many queries already give each loaded row more work: keep their tiles short
     constexpr int NP = (NQ > 2 && kCrossNP > 2) ? 2 : kCrossNP;
     dim3 grid(a.nsplit, a.H, a.B);
@@ -255,16 +292,24 @@ hipError_t launch_cross_nq(const XattnLaunch& a, hipStream_t st) {
                        a.part, a.nq, a.max_q, a.H, a.T, a.nsplit, a.chunk, a.scale * kLog2e);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.nsplit == 1) return e;
-    hipLaunchKernelGGL((xattn_merge_kernel<D>), dim3(a.H, a.B), dim3(256), 0, st, a.part, a.out,
-                       a.nq, a.max_q, a.H, a.nsplit);
+    const int G = (a.nsplit + kMergeBatch - 1) / kMergeBatch;
+    const int pairs = a.nq * D * G;
+    const int threads = pairs >= 1024 ? 1024 : ((pairs + 63) / 64) * 64;
+    const size_t lds = (size_t)3 * pairs * sizeof(float);
+    hipLaunchKernelGGL((xattn_merge_kernel<D>), dim3(a.H, a.B), dim3(threads), lds, st, a.part,
+                       a.out, a.nq, a.max_q, a.H, a.nsplit);
     return hipGetLastError();
 }
 
 template <int D, typename TE>
 hipError_t launch_cross_d(const XattnLaunch& a, hipStream_t st) {
-    if (a.nq <= 1) return launch_cross_nq<D, TE, 1>(a, st);
-    if (a.nq <= 2) return launch_cross_nq<D, TE, 2>(a, st);
-    if (a.nq <= 4) return launch_cross_nq<D, TE, 4>(a, st);
+    switch (a.nq) {
+        case 1: return launch_cross_nq<D, TE, 1>(a, st);
+        case 2: return launch_cross_nq<D, TE, 2>(a, st);
+        case 3: return launch_cross_nq<D, TE, 3>(a, st);
+        case 4: return launch_cross_nq<D, TE, 4>(a, st);
+        case 5: return launch_cross_nq<D, TE, 5>(a, st);
+    }
     return launch_cross_nq<D, TE, 8>(a, st);
 }
 

@@ -91,6 +91,11 @@ static_assert(CKE_MAX_SPLITS >= 1 && CKE_MAX_SPLITS <= cke::kMaxSplits, "split c
 // about CKE_TARGET_WGS workgroups (4 per compute unit) but never fewer rows
 // per workgroup than one pass of its waves.
 void split_plan(const cke_xattn_geom* g, int* nsplit, int* chunk) {
+    if (g->mem_len <= cke::kShortMemRows) {  // one wave per head, no split
+        *nsplit = 1;
+        *chunk = g->mem_len;
+        return;
+    }
     const int kpp = cke::cross_keys_per_pass(g->head_dim, elem_bytes(g->cache_dtype));
     const long long bh = (long long)g->n_streams * g->n_heads;
     const int max_by_rows = (g->mem_len + kpp - 1) / kpp;

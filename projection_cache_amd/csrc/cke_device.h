@@ -135,12 +135,85 @@ struct WaveState {
     }
 };
 
+// Load NP row passes of K and V starting at row `base` into packed
+// registers. Branch-free, so a whole tile is in flight at once: every row
+// index is clamped to r_safe (the last row this wave may read from memory);
+// rows past it are masked or replaced in compute_tile.
+template <int D, typename TE, int NP>
+__device__ __forceinline__ void load_tile(const TE* __restrict__ K, const TE* __restrict__ V,
+                                          int base, int r_safe, int grp, int sub,
+                                          uint4 (&kb)[NP], uint4 (&vb)[NP])
+{
+    using RM = RowMap<D, TE>;
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+        const int row = min(base + p * RM::kKPW + grp, r_safe);
+        const size_t off = (size_t)row * D + sub * RM::kVec;
+        kb[p] = load16(K + off);
+        vb[p] = load16(V + off);
+    }
+}
+
+// Fold one loaded tile into the lane group's running softmax state. Each
+// group of LPK lanes (one row slot) keeps its own running max, so a tile
+// needs no communication across groups; groups are merged once, in
+// wg_merge. Lanes of a group hold identical scores and max. Rows past r1 get
+// score -inf and a zero V share (their loaded bytes may be anything); the
+// row equal to cur_row uses the values ck/cv instead of the loaded ones.
+template <int D, typename TE, int NQ, int NP>
+__device__ __forceinline__ void compute_tile(int base, int r1, int cur_row, bool has_cur,
+                                             const uint4& ck, const uint4& cv, int grp,
+                                             const float (&q)[NQ][RowMap<D, TE>::kVec], int nq,
+                                             float sl2, const uint4 (&kb)[NP],
+                                             const uint4 (&vb)[NP],
+                                             WaveState<NQ, RowMap<D, TE>::kVec>& st)
+{
+    using RM = RowMap<D, TE>;
+    constexpr int VEC = RM::kVec, LPK = RM::kLPK, KPW = RM::kKPW;
+    const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) {
+        if (i < nq) {
+            float s[NP];
+            float mt = -INFINITY;
+#pragma unroll
+            for (int p = 0; p < NP; ++p) {
+                const int row = base + p * KPW + grp;
+                const uint4 kr = (has_cur && row == cur_row) ? ck : kb[p];
+                float d = 0.f;
+#pragma unroll
+                for (int j = 0; j < VEC; ++j) d = fmaf(q[i][j], elem<TE>(kr, j), d);
+                d = group_sum<LPK>(d);
+                s[p] = row < r1 ? d * sl2 : -INFINITY;
+                mt = fmaxf(mt, s[p]);
+            }
+            const float mn = fmaxf(st.m[i], mt);
+            const float alpha = mn == -INFINITY ? 1.f : fast_exp2(st.m[i] - mn);
+            st.l[i] *= alpha;
+#pragma unroll
+            for (int j = 0; j < VEC; ++j) st.acc[i][j] *= alpha;
+#pragma unroll
+            for (int p = 0; p < NP; ++p) {
+                const int row = base + p * KPW + grp;
+                const uint4 vr = row < r1 ? ((has_cur && row == cur_row) ? cv : vb[p]) : zero;
+                const float e = s[p] == -INFINITY ? 0.f : fast_exp2(s[p] - mn);
+                st.l[i] += e;
+#pragma unroll
+                for (int j = 0; j < VEC; ++j) st.acc[i][j] = fmaf(e, elem<TE>(vr, j), st.acc[i][j]);
+            }
+            st.m[i] = mn;
+        }
+    }
+}
+
 // One wave attends its queries over rows [r0, r1) of K/V (rows D elements
-// apart). Rows are read in tiles of NP passes; the loads of the next tile are
-// issued before the current tile is computed (register double buffering), so
-// each wave keeps up to 2*NP 16-byte loads per operand in flight. If cur_row
-// lies in the range, that row is taken from the fp32 vectors cur_k / cur_v
-// (rounded to the storage type) instead of memory.
+// apart; r0, r1 wave-uniform). Rows are read in tiles of NP passes; the
+// loads of the next tile are issued before the current tile is computed
+// (register double buffering), so each wave keeps up to 2*NP 16-byte loads
+// per operand in flight. If cur_row lies in the range it must be its last row
+// (r1 - 1): that row's values are taken from the fp32 vectors cur_k / cur_v
+// (rounded to the storage type) and its memory is never read, so the caller
+// may be writing it concurrently.
 template <int D, typename TE, int NQ, int NP>
 __device__ __forceinline__ void wave_attend(
     const TE* __restrict__ K, const TE* __restrict__ V, int r0, int r1,
@@ -154,70 +227,51 @@ __device__ __forceinline__ void wave_attend(
     const int lane = threadIdx.x & 63;
     const int grp = lane / LPK;
     const int sub = lane % LPK;
-
-    auto load_tile = [&](int base, uint4 (&kb)[NP], uint4 (&vb)[NP]) {
-#pragma unroll
-        for (int p = 0; p < NP; ++p) {
-            const int row = base + p * KPW + grp;
-            if (row < r1 && row != cur_row) {
-                kb[p] = load16(K + (size_t)row * D + sub * VEC);
-                vb[p] = load16(V + (size_t)row * D + sub * VEC);
-            } else if (row < r1) {
-                kb[p] = pack16_from_f32<TE>(cur_k + sub * VEC);
-                vb[p] = pack16_from_f32<TE>(cur_v + sub * VEC);
-            } else {
-                kb[p] = make_uint4(0u, 0u, 0u, 0u);
-                vb[p] = make_uint4(0u, 0u, 0u, 0u);
-            }
-        }
-    };
-    // Each group of LPK lanes (one row slot) keeps its own running max, so a
-    // tile needs no communication across groups; groups are merged once, in
-    // wg_merge. Lanes of a group hold identical scores and max.
-    auto compute_tile = [&](int base, const uint4 (&kb)[NP], const uint4 (&vb)[NP]) {
-#pragma unroll
-        for (int i = 0; i < NQ; ++i) {
-            if (i < nq) {
-                float s[NP];
-                float mt = -INFINITY;
-#pragma unroll
-                for (int p = 0; p < NP; ++p) {
-                    float d = 0.f;
-#pragma unroll
-                    for (int j = 0; j < VEC; ++j) d = fmaf(q[i][j], elem<TE>(kb[p], j), d);
-                    d = group_sum<LPK>(d);
-                    s[p] = (base + p * KPW + grp < r1) ? d * sl2 : -INFINITY;
-                    mt = fmaxf(mt, s[p]);
-                }
-                const float mn = fmaxf(st.m[i], mt);
-                const float alpha = mn == -INFINITY ? 1.f : fast_exp2(st.m[i] - mn);
-                st.l[i] *= alpha;
-#pragma unroll
-                for (int j = 0; j < VEC; ++j) st.acc[i][j] *= alpha;
-#pragma unroll
-                for (int p = 0; p < NP; ++p) {
-                    const float e = s[p] == -INFINITY ? 0.f : fast_exp2(s[p] - mn);
-                    st.l[i] += e;
-#pragma unroll
-                    for (int j = 0; j < VEC; ++j)
-                        st.acc[i][j] = fmaf(e, elem<TE>(vb[p], j), st.acc[i][j]);
-                }
-                st.m[i] = mn;
-            }
-        }
-    };
-
     if (r0 >= r1) return;
+
+    const bool has_cur = cur_row >= r0 && cur_row < r1;
+    uint4 ck = make_uint4(0u, 0u, 0u, 0u), cv = ck;
+    if (has_cur) {
+        ck = pack16_from_f32<TE>(cur_k + sub * VEC);
+        cv = pack16_from_f32<TE>(cur_v + sub * VEC);
+    }
+    // last row that may be read from memory; a wave holding only the current
+    // row reads nothing
+    const int r_safe = has_cur ? r1 - 2 : r1 - 1;
     uint4 ka[NP], va[NP], kb2[NP], vb2[NP];
-    load_tile(r0, ka, va);
+    if (r_safe >= r0) {
+        load_tile<D, TE, NP>(K, V, r0, r_safe, grp, sub, ka, va);
+    } else {
+#pragma unroll
+        for (int p = 0; p < NP; ++p) ka[p] = va[p] = make_uint4(0u, 0u, 0u, 0u);
+    }
     for (int base = r0; base < r1; base += 2 * TILE) {
         const bool more = base + TILE < r1;
-        if (more) load_tile(base + TILE, kb2, vb2);
-        compute_tile(base, ka, va);
+        if (more) load_tile<D, TE, NP>(K, V, base + TILE, r_safe, grp, sub, kb2, vb2);
+        compute_tile<D, TE, NQ, NP>(base, r1, cur_row, has_cur, ck, cv, grp, q, nq, sl2, ka, va, st);
         if (!more) break;
-        const bool more2 = base + 2 * TILE < r1;
-        if (more2) load_tile(base + 2 * TILE, ka, va);
-        compute_tile(base + TILE, kb2, vb2);
+        if (base + 2 * TILE < r1) load_tile<D, TE, NP>(K, V, base + 2 * TILE, r_safe, grp, sub, ka, va);
+        compute_tile<D, TE, NQ, NP>(base + TILE, r1, cur_row, has_cur, ck, cv, grp, q, nq, sl2, kb2, vb2, st);
+    }
+}
+
+// Merge the row groups of one wave: afterwards every lane holds the wave's
+// (max, sum) per query and the wave's unnormalised output for its own dims.
+template <int D, typename TE, int NQ>
+__device__ __forceinline__ void wave_merge_groups(WaveState<NQ, RowMap<D, TE>::kVec>& st, int nq)
+{
+    using RM = RowMap<D, TE>;
+    constexpr int VEC = RM::kVec, LPK = RM::kLPK;
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) {
+        if (i < nq) {
+            const float M = xor_max<LPK, 64>(st.m[i]);
+            const float f = M == -INFINITY ? 0.f : fast_exp2(st.m[i] - M);
+            st.m[i] = M;
+            st.l[i] = xor_sum<LPK, 64>(st.l[i] * f);
+#pragma unroll
+            for (int j = 0; j < VEC; ++j) st.acc[i][j] = xor_sum<LPK, 64>(st.acc[i][j] * f);
+        }
     }
 }
 
@@ -233,16 +287,10 @@ __device__ __forceinline__ void wg_merge(
     constexpr int VEC = RM::kVec, LPK = RM::kLPK;
     const int lane = threadIdx.x & 63;
     const int w = threadIdx.x >> 6;
+    wave_merge_groups<D, TE, NQ>(st, nq);
 #pragma unroll
     for (int i = 0; i < NQ; ++i) {
         if (i < nq) {
-            // merge the row groups of this wave: common max, rescale, sum
-            const float M = xor_max<LPK, 64>(st.m[i]);
-            const float f = M == -INFINITY ? 0.f : fast_exp2(st.m[i] - M);
-            st.m[i] = M;
-            st.l[i] = xor_sum<LPK, 64>(st.l[i] * f);
-#pragma unroll
-            for (int j = 0; j < VEC; ++j) st.acc[i][j] = xor_sum<LPK, 64>(st.acc[i][j] * f);
             if (lane < LPK) {
 #pragma unroll
                 for (int j = 0; j < VEC; ++j) wa[(w * NQ + i) * D + lane * VEC + j] = st.acc[i][j];

@@ -39,6 +39,9 @@ struct WeightTable {
     const void* w[2 * kMaxLayers];
 };
 
+// Memories of at most this many rows are decoded one wave per head, unsplit.
+constexpr int kShortMemRows = 64;
+
 // Largest number of key splits a decode call may use.
 constexpr int kMaxSplits = 64;
 

@@ -138,6 +138,11 @@ DEC_CASES = [
                 head_dim=128, dtype="bf16")),
     (None, dict(n_layers=1, n_streams=1, n_q=5, mem_len=3001, d_model=128, n_heads=2,
                 head_dim=64)),
+    # either side of the short-memory path (one wave per head, no split)
+    (None, dict(n_layers=1, n_streams=2, n_q=3, mem_len=64, d_model=128, n_heads=2, head_dim=64)),
+    (None, dict(n_layers=1, n_streams=2, n_q=3, mem_len=65, d_model=128, n_heads=2, head_dim=64)),
+    (None, dict(n_layers=1, n_streams=5, n_q=2, mem_len=15, d_model=256, n_heads=2, head_dim=128,
+                dtype="bf16")),
 ]
 
 
