@@ -271,13 +271,17 @@ constexpr int kSelfNP = CKE_SELF_NP;
 
 // Memories this short go to xattn_short_kernel.
 constexpr int kShortRows = kShortMemRows;
+#ifndef CKE_SHORT_NP
+#define CKE_SHORT_NP 4
+#endif
+constexpr int kShortNP = CKE_SHORT_NP;  // passes per tile: 16 fp32 rows of 64 in one tile
 
 template <int D, typename TE, int NQ>
 hipError_t launch_cross_nq(const XattnLaunch& a, hipStream_t st) {
     if (a.T <= kShortRows) {
         constexpr int NW = 4;
         const int n_bh = a.B * a.H;
-        hipLaunchKernelGGL((xattn_short_kernel<D, TE, NQ, NW, 2>), dim3((n_bh + NW - 1) / NW),
+        hipLaunchKernelGGL((xattn_short_kernel<D, TE, NQ, NW, kShortNP>), dim3((n_bh + NW - 1) / NW),
                            dim3(NW * 64), 0, st, a.q, static_cast<const TE*>(a.K),
                            static_cast<const TE*>(a.V), a.out, a.nq, a.H, a.T, n_bh,
                            a.scale * kLog2e);

@@ -24,6 +24,8 @@ namespace {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short v4i16_bf __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16_bf lds_v4i16;
 
 struct GemmArgs {
     const void* E;
@@ -221,6 +223,10 @@ __global__ __launch_bounds__(256) void populate_bf16_kernel(GemmArgs a)
 //    8(k) x 8(n) block (eight 16-byte row pieces), transposes it in registers
 //    with v_perm_b32 (two 16-bit halves per output word) and writes eight
 //    16-byte column pieces: Bs[n][k]. Both fragments are then one ds_read_b128.
+//    Adjacent lanes take adjacent k-chunks of the same 8 columns, so the 16
+//    lanes of a write phase cover 16 distinct 16-byte bank slots (rows are
+//    BK+8 elements = an odd number of 16-byte slots apart), and each global
+//    load instruction still reads 8 full 128-byte row segments.
 //  * LDS is double buffered: the next k-tile is loaded into registers while
 //    the current one is multiplied, then stored to the other buffer; one
 //    barrier per k-tile.
@@ -276,9 +282,9 @@ __global__ __launch_bounds__(WGM * WGN * 64) void populate_bf16_big_kernel(GemmA
         }
 #pragma unroll
         for (int i = 0; i < B_PER_T; ++i) {
-            const int blk = tid + i * NT;                 // block: n-chunk fastest
+            const int blk = tid + i * NT;   // block: k-chunk fastest (LDS bank spread)
             if (blk < B_BLOCKS) {
-                const int nb8 = blk % (BN / 8), kb8 = blk / (BN / 8);
+                const int kb8 = blk % (BK / 8), nb8 = blk / (BK / 8);
                 const uint16_t* src = W + (size_t)(k0 + kb8 * 8) * HD + col0 + nb8 * 8;
 #pragma unroll
                 for (int r = 0; r < 8; ++r) rb[i][r] = *reinterpret_cast<const uint4*>(src + (size_t)r * HD);
@@ -296,7 +302,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void populate_bf16_big_kernel(GemmA
         for (int i = 0; i < B_PER_T; ++i) {
             const int blk = tid + i * NT;
             if (blk < B_BLOCKS) {
-                const int nb8 = blk % (BN / 8), kb8 = blk / (BN / 8);
+                const int kb8 = blk % (BK / 8), nb8 = blk / (BK / 8);
                 // rows r = k (8 of them), words c = n pairs; output column n
                 // holds words kp = (k=2kp, k=2kp+1) of that n
 #pragma unroll
@@ -479,6 +485,515 @@ hipError_t launch_f32_big(const GemmArgs& g, hipStream_t st) {
     return hipGetLastError();
 }
 
+constexpr int vmcnt_wait(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
+
+// LDS byte address of a pointer into __shared__ memory.
+__device__ __forceinline__ uint32_t lds_addr(const void* p)
+{
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// global_load_lds_dwordx4: each lane's 16 bytes from src land at LDS address
+// lds_base + lane*16 (lds_base wave-uniform, through M0). Issued from inline
+// assembly so that the compiler neither tracks nor waits on it: the stream
+// kernel orders these loads itself with explicit vmcnt waits and barriers.
+// An SALU write of M0 needs one wait state before a load that writes LDS
+// through it, hence the s_nop. Nothing else in the kernel keeps a value in M0.
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds_base)
+{
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src),
+                 "s"(lds_base)
+                 : "memory");
+}
+
+// One ring slot: A tile then B tile, BK = 32.
+template <int BM, int BN>
+struct StreamSlot {
+    uint16_t a[BM * 32];
+    uint16_t b[32 * BN];
+};
+
+template <int BM, int BN, int WGM, int WGN>
+struct StreamTile {
+    static constexpr int BK = 32;
+    static constexpr int NT = WGM * WGN * 64;
+    static constexpr int WTM = BM / WGM, WTN = BN / WGN, MB = WTM / 32, NB = WTN / 32;
+    static constexpr int A_LD = BM * BK / 8 / NT;   // direct loads per thread per slot
+    static constexpr int B_LD = BK * BN / 8 / NT;
+    static constexpr int BROW = BN / 8;             // 16-byte pieces per B row
+    static_assert((BM * BK / 8) % NT == 0 && (BK * BN / 8) % NT == 0 && MB >= 1 && NB >= 1, "tile");
+    static_assert(BROW >= 16, "B swizzle needs >= 16 pieces per row");
+};
+
+// Issue the direct loads of k-tile kt into one ring slot.
+template <int BM, int BN, int WGM, int WGN>
+__device__ __forceinline__ void stream_issue(StreamSlot<BM, BN>& slot, const uint16_t* __restrict__ E,
+                                             const uint16_t* __restrict__ W, int kt, int m0, int M,
+                                             int dm, int HD, int col0, int wave, int lane)
+{
+    using T = StreamTile<BM, BN, WGM, WGN>;
+    const int k0 = kt * T::BK;
+#pragma unroll
+    for (int i = 0; i < T::A_LD; ++i) {
+        const int s = (wave * T::A_LD + i) * 64 + lane;   // 16-byte slot in the A tile
+        const int row = s >> 2, piece = (s & 3) ^ ((row >> 2) & 3);
+        const int m = min(m0 + row, M - 1);
+        dma16(E + (size_t)m * dm + k0 + piece * 8, lds_addr(slot.a + (wave * T::A_LD + i) * 64 * 8));
+    }
+#pragma unroll
+    for (int i = 0; i < T::B_LD; ++i) {
+        const int s = (wave * T::B_LD + i) * 64 + lane;
+        const int row = s / T::BROW, piece = (s % T::BROW) ^ (4 * (row & 3));
+        dma16(W + (size_t)(k0 + row) * HD + col0 + piece * 8, lds_addr(slot.b + (wave * T::B_LD + i) * 64 * 8));
+    }
+}
+
+// Multiply one ring slot into the accumulators.
+template <int BM, int BN, int WGM, int WGN>
+__device__ __forceinline__ void stream_compute(
+    const StreamSlot<BM, BN>& slot, int wm, int wn, int lane,
+    f32x16 (&acc)[StreamTile<BM, BN, WGM, WGN>::MB][StreamTile<BM, BN, WGM, WGN>::NB])
+{
+    using T = StreamTile<BM, BN, WGM, WGN>;
+#pragma unroll
+    for (int kk = 0; kk < T::BK; kk += 16) {
+        bf16x8 av[T::MB], bv[T::NB];
+#pragma unroll
+        for (int mb = 0; mb < T::MB; ++mb) {
+            const int row = wm * T::WTM + mb * 32 + (lane & 31);
+            const int piece = ((kk >> 3) + (lane >> 5)) ^ ((row >> 2) & 3);
+            av[mb] = *reinterpret_cast<const bf16x8*>(slot.a + row * T::BK + piece * 8);
+        }
+#pragma unroll
+        for (int nb = 0; nb < T::NB; ++nb) {
+            const int g = (lane >> 4) & 3, L = lane & 15;
+            const int ncol = wn * T::WTN + nb * 32 + 16 * (g & 1) + 4 * (L & 3);
+            v4i16_bf h[2];
+#pragma unroll
+            for (int jr = 0; jr < 2; ++jr) {
+                const int krow = kk + 8 * (g >> 1) + 4 * jr + (L >> 2);
+                const int piece = (ncol >> 3) ^ (4 * (krow & 3));
+                h[jr] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_v4i16*)(slot.b + krow * BN + piece * 8 + (ncol & 7)));
+            }
+            bf16x8 b;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                b[j] = __builtin_bit_cast(__bf16, (short)h[0][j]);
+                b[4 + j] = __builtin_bit_cast(__bf16, (short)h[1][j]);
+            }
+            bv[nb] = b;
+        }
+#pragma unroll
+        for (int mb = 0; mb < T::MB; ++mb)
+#pragma unroll
+            for (int nb = 0; nb < T::NB; ++nb)
+                acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[mb], bv[nb], acc[mb][nb], 0, 0, 0);
+    }
+}
+
+// bf16 populate, streaming version for gfx950:
+//  * operand tiles move global -> LDS with global_load_lds_dwordx4 (each lane's
+//    16 bytes land at the instruction's LDS base + lane*16; no staging
+//    registers), into a ring of 4 slots of BK = 32, so three k-tiles are in
+//    flight while one is multiplied; one barrier per k-tile. The loads are
+//    ordered by explicit vmcnt waits: before multiplying k-tile kt a thread
+//    waits until at most the loads of the two later k-tiles are outstanding,
+//    then the barrier makes every thread's loads of kt visible;
+//  * W stays in its [k][n] layout in LDS and the B fragments are read with
+//    ds_read_b64_tr_b16: within each 16-lane group, lane i receives element
+//    i%4 of the 8 bytes addressed by lane 4j + i/4 (j = 0..3), so when four
+//    lanes per row address four consecutive k-rows x 16 columns, lane i gets
+//    four consecutive k of column i. Two such reads give a 32x32x16 B operand;
+//  * the 16-byte pieces of each LDS row are XOR-swizzled by row so that
+//    fragment reads hit distinct banks: A rows (BK = 32 -> 4 pieces)
+//    piece ^ ((row >> 2) & 3); B rows piece ^ 4*(row & 3). The direct loads
+//    pick, per lane, the global piece that belongs in the lane's LDS slot;
+//  * rows of E past M are clamped to row M-1 for loading; their products
+//    only reach output rows that are never stored.
+template <int BM, int BN, int WGM, int WGN>
+__global__ __launch_bounds__(WGM * WGN * 64) void populate_bf16_stream_kernel(GemmArgs a, int num_m, int num_n)
+{
+    using T = StreamTile<BM, BN, WGM, WGN>;
+    constexpr int LD_PER_SLOT = T::A_LD + T::B_LD;
+    constexpr int GROUP_M = 8;
+    __shared__ __attribute__((aligned(1024))) StreamSlot<BM, BN> ring0;
+    __shared__ __attribute__((aligned(1024))) StreamSlot<BM, BN> ring1;
+    __shared__ __attribute__((aligned(1024))) StreamSlot<BM, BN> ring2;
+    __shared__ __attribute__((aligned(1024))) StreamSlot<BM, BN> ring3;
+
+    const int ntiles = num_m * num_n;
+    const int per_xcd = (ntiles + 7) / 8;
+    const int tile = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+    if (tile >= ntiles) return;
+    const int group = tile / (GROUP_M * num_n);
+    const int first_m = group * GROUP_M;
+    const int gsize = min(num_m - first_m, GROUP_M);
+    const int pid_m = first_m + (tile % (GROUP_M * num_n)) % gsize;
+    const int pid_n = (tile % (GROUP_M * num_n)) / gsize;
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wave / WGN, wn = wave % WGN;
+    const int HD = a.H * a.D;
+    const int m0 = pid_m * BM;
+    const int n0 = pid_n * BN;
+    const int p = n0 / HD;
+    const int col0 = n0 - p * HD;
+    const uint16_t* __restrict__ E = static_cast<const uint16_t*>(a.E);
+    const uint16_t* __restrict__ W = static_cast<const uint16_t*>(a.wt.w[p]);
+
+    f32x16 acc[T::MB][T::NB];
+#pragma unroll
+    for (int i = 0; i < T::MB; ++i)
+#pragma unroll
+        for (int j = 0; j < T::NB; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+    const int nk = a.dm / T::BK;
+    auto issue = [&](StreamSlot<BM, BN>& slot, int kt) {
+        if (kt < nk) stream_issue<BM, BN, WGM, WGN>(slot, E, W, kt, m0, a.M, a.dm, HD, col0, wave, lane);
+    };
+    // Wait until this thread's loads of k-tile kt have landed (the loads of up
+    // to two later k-tiles may stay outstanding), then barrier so that every
+    // thread's have; no fence, so outstanding loads into other slots continue.
+    auto sync_tile = [&](int kt) {
+        const int later = min(2, nk - 1 - kt);
+        // s_waitcnt immediate (gfx9 encoding): vmcnt in bits 3:0 and 15:14,
+        // expcnt 6:4 and lgkmcnt 11:8 left at their maxima (no wait).
+        if (later >= 2)
+            __builtin_amdgcn_s_waitcnt(vmcnt_wait(2 * LD_PER_SLOT));
+        else if (later == 1)
+            __builtin_amdgcn_s_waitcnt(vmcnt_wait(LD_PER_SLOT));
+        else
+            __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));
+        __builtin_amdgcn_s_barrier();
+    };
+
+    // The host launches this kernel only when nk is a multiple of the ring
+    // depth, so every pass of the loop below runs all four slots.
+    stream_issue<BM, BN, WGM, WGN>(ring0, E, W, 0, m0, a.M, a.dm, HD, col0, wave, lane);
+    stream_issue<BM, BN, WGM, WGN>(ring1, E, W, 1, m0, a.M, a.dm, HD, col0, wave, lane);
+    stream_issue<BM, BN, WGM, WGN>(ring2, E, W, 2, m0, a.M, a.dm, HD, col0, wave, lane);
+    for (int kt = 0; kt < nk; kt += 4) {
+        sync_tile(kt);
+        issue(ring3, kt + 3);
+        stream_compute<BM, BN, WGM, WGN>(ring0, wm, wn, lane, acc);
+        sync_tile(kt + 1);
+        issue(ring0, kt + 4);
+        stream_compute<BM, BN, WGM, WGN>(ring1, wm, wn, lane, acc);
+        sync_tile(kt + 2);
+        issue(ring1, kt + 5);
+        stream_compute<BM, BN, WGM, WGN>(ring2, wm, wn, lane, acc);
+        sync_tile(kt + 3);
+        issue(ring2, kt + 6);
+        stream_compute<BM, BN, WGM, WGN>(ring3, wm, wn, lane, acc);
+    }
+    epilogue<BM, BN, WGM, WGN, uint16_t>(a, acc, m0, p, col0);
+}
+
+// Read the fragments of one 16-deep k step of a ring slot for the transposed
+// product C^T = W^T E^T: the W side (MFMA A operand, rows = output columns n)
+// through ds_read_b64_tr_b16, the E side (MFMA B operand, columns = output
+// rows m) as 16-byte row pieces.
+template <int BM, int BN, int WGM, int WGN>
+struct FragsT {
+    bf16x8 w[StreamTile<BM, BN, WGM, WGN>::NB];
+    bf16x8 e[StreamTile<BM, BN, WGM, WGN>::MB];
+};
+
+template <int BM, int BN, int WGM, int WGN>
+__device__ __forceinline__ void read_frags_t(const StreamSlot<BM, BN>& slot, int kk, int wm, int wn, int lane,
+                                             FragsT<BM, BN, WGM, WGN>& f)
+{
+    using T = StreamTile<BM, BN, WGM, WGN>;
+#pragma unroll
+    for (int mb = 0; mb < T::MB; ++mb) {
+        const int row = wm * T::WTM + mb * 32 + (lane & 31);
+        const int piece = ((kk >> 3) + (lane >> 5)) ^ ((row >> 2) & 3);
+        f.e[mb] = *reinterpret_cast<const bf16x8*>(slot.a + row * T::BK + piece * 8);
+    }
+#pragma unroll
+    for (int nb = 0; nb < T::NB; ++nb) {
+        const int g = (lane >> 4) & 3, L = lane & 15;
+        const int ncol = wn * T::WTN + nb * 32 + 16 * (g & 1) + 4 * (L & 3);
+        v4i16_bf h[2];
+#pragma unroll
+        for (int jr = 0; jr < 2; ++jr) {
+            const int krow = kk + 8 * (g >> 1) + 4 * jr + (L >> 2);
+            const int piece = (ncol >> 3) ^ (4 * (krow & 3));
+            h[jr] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_v4i16*)(slot.b + krow * BN + piece * 8 + (ncol & 7)));
+        }
+        bf16x8 b;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            b[j] = __builtin_bit_cast(__bf16, (short)h[0][j]);
+            b[4 + j] = __builtin_bit_cast(__bf16, (short)h[1][j]);
+        }
+        f.w[nb] = b;
+    }
+}
+
+template <int BM, int BN, int WGM, int WGN>
+__device__ __forceinline__ void mfma_frags_t(
+    const FragsT<BM, BN, WGM, WGN>& f,
+    f32x16 (&acc)[StreamTile<BM, BN, WGM, WGN>::NB][StreamTile<BM, BN, WGM, WGN>::MB])
+{
+    using T = StreamTile<BM, BN, WGM, WGN>;
+#pragma unroll
+    for (int nb = 0; nb < T::NB; ++nb)
+#pragma unroll
+        for (int mb = 0; mb < T::MB; ++mb)
+            acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.w[nb], f.e[mb], acc[nb][mb], 0, 0, 0);
+}
+
+// Store a transposed accumulator tile (acc[nb][mb] holds C^T: register r of
+// lane L is output column n = 8*(r/4) + 4*(L/32) + r%4 and output row
+// m = L%32 of its 32x32 block). Each lane packs four consecutive columns of
+// one row, which lie in one head since D is a multiple of 4, into one 8-byte
+// bf16 store at Kc/Vc[l][b][h][t][d..d+3]. (b, t) is worked out once per row.
+template <int BM, int BN, int WGM, int WGN>
+__device__ __forceinline__ void epilogue_t_bf16(
+    const GemmArgs& a,
+    const f32x16 (&acc)[StreamTile<BM, BN, WGM, WGN>::NB][StreamTile<BM, BN, WGM, WGN>::MB], int m0, int p,
+    int col0, int wm, int wn, int lane)
+{
+    using T = StreamTile<BM, BN, WGM, WGN>;
+    const int l = p < a.L ? p : p - a.L;
+    uint16_t* C = static_cast<uint16_t*>(p < a.L ? a.Kc : a.Vc);
+    const size_t TD = (size_t)a.T * a.D;
+    size_t row_off[T::MB];
+    bool ok[T::MB];
+#pragma unroll
+    for (int mb = 0; mb < T::MB; ++mb) {
+        const int m = m0 + wm * T::WTM + mb * 32 + (lane & 31);
+        ok[mb] = m < a.M;
+        const int b = m / a.T, t = m - b * a.T;
+        row_off[mb] = (size_t)(l * a.B + b) * a.H * TD + (size_t)t * a.D;
+    }
+#pragma unroll
+    for (int nb = 0; nb < T::NB; ++nb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const int n = col0 + wn * T::WTN + nb * 32 + 8 * g + 4 * (lane >> 5);
+            const int h = n / a.D, d = n - h * a.D;
+            const size_t col_off = (size_t)h * TD + d;
+#pragma unroll
+            for (int mb = 0; mb < T::MB; ++mb) {
+                const f32x16& v = acc[nb][mb];
+                uint2 w;
+                w.x = (uint32_t)to_bf16_bits(v[4 * g]) | ((uint32_t)to_bf16_bits(v[4 * g + 1]) << 16);
+                w.y = (uint32_t)to_bf16_bits(v[4 * g + 2]) | ((uint32_t)to_bf16_bits(v[4 * g + 3]) << 16);
+                if (ok[mb]) *reinterpret_cast<uint2*>(C + row_off[mb] + col_off) = w;
+            }
+        }
+}
+
+// Store a transposed accumulator tile (as epilogue_t_bf16 holds it) through
+// LDS so that global writes are whole rows: for a fixed head the tile's rows
+// t .. t+BM-1 of one stream are contiguous in Kc/Vc[l][b][h][t][d], so each
+// wave writes 64 x 16 consecutive bytes per store. `stage` is at least
+// BM*BN*2 bytes of LDS no wave reads any more; the caller has passed a barrier
+// after its last read. Staging layout: [head j][row m][D] bf16, 16-byte pieces
+// of a row XOR-swizzled by (m % (D/8)) and the two 8-byte halves of a piece
+// swapped when bit 3 of m is set, so that the 8-byte writes of 32 consecutive
+// rows and the 16-byte reads of consecutive pieces spread over the banks.
+template <int BM, int BN, int WGM, int WGN>
+__device__ __forceinline__ void epilogue_t_lds(
+    const GemmArgs& a,
+    const f32x16 (&acc)[StreamTile<BM, BN, WGM, WGN>::NB][StreamTile<BM, BN, WGM, WGN>::MB], int m0, int p,
+    int col0, int wm, int wn, int lane, uint16_t* stage)
+{
+    using T = StreamTile<BM, BN, WGM, WGN>;
+    constexpr int NT = T::NT;
+    const int lgD = __builtin_ctz(a.D);
+    const int lgP = lgD - 3;              // log2 of 16-byte pieces per row
+    const int PD = 1 << lgP;
+#pragma unroll
+    for (int nb = 0; nb < T::NB; ++nb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const int n = wn * T::WTN + nb * 32 + 8 * g + 4 * (lane >> 5);
+            const int j = n >> lgD, d = n & (a.D - 1);
+            const int q = d >> 3, half = (d >> 2) & 1;
+#pragma unroll
+            for (int mb = 0; mb < T::MB; ++mb) {
+                const int m = wm * T::WTM + mb * 32 + (lane & 31);
+                const f32x16& v = acc[nb][mb];
+                uint2 w;
+                w.x = (uint32_t)to_bf16_bits(v[4 * g]) | ((uint32_t)to_bf16_bits(v[4 * g + 1]) << 16);
+                w.y = (uint32_t)to_bf16_bits(v[4 * g + 2]) | ((uint32_t)to_bf16_bits(v[4 * g + 3]) << 16);
+                const int off = ((j * BM + m) << lgD) + ((q ^ (m & (PD - 1))) << 3) +
+                                ((half ^ ((m >> 3) & 1)) << 2);
+                *reinterpret_cast<uint2*>(stage + off) = w;
+            }
+        }
+    __syncthreads();
+    const int l = p < a.L ? p : p - a.L;
+    uint16_t* C = static_cast<uint16_t*>(p < a.L ? a.Kc : a.Vc);
+    const size_t TD = (size_t)a.T * a.D;
+    const int h0 = col0 >> lgD;
+    const int b0 = m0 / a.T, t0 = m0 - b0 * a.T;
+    const int tid = threadIdx.x;
+    constexpr int PIECES = BM * BN / 8;
+#pragma unroll 4
+    for (int id = tid; id < PIECES; id += NT) {
+        const int q = id & (PD - 1);
+        const int m = (id >> lgP) & (BM - 1);
+        const int j = id >> (lgP + 8);    // BM == 256 rows per head block
+        if (m0 + m < a.M) {
+            int t = t0 + m, b = b0;
+            if (t >= a.T) {
+                if (a.T >= BM) { t -= a.T; b += 1; }
+                else { b += t / a.T; t -= (t / a.T) * a.T; }
+            }
+            const int off = ((j * BM + m) << lgD) + ((q ^ (m & (PD - 1))) << 3);
+            uint4 v = *reinterpret_cast<const uint4*>(stage + off);
+            if ((m >> 3) & 1) { const uint32_t x = v.x, y = v.y; v.x = v.z; v.y = v.w; v.z = x; v.w = y; }
+            const size_t idx = ((size_t)(l * a.B + b) * a.H + h0 + j) * TD + (size_t)t * a.D + q * 8;
+            *reinterpret_cast<uint4*>(C + idx) = v;
+        }
+    }
+}
+
+// bf16 populate with four waves (one per SIMD), each owning a 128x128 block
+// of a 256x256 output tile, which halves LDS read traffic per MFMA against
+// 128x64 wave blocks. The product is formed transposed (W^T as the MFMA A
+// operand, E^T as B) so that each lane ends up with four consecutive output
+// columns of one row and stores 8 bytes at a time.
+// Operand tiles stream into a ring of NSLOT slots of BK = 32 by direct
+// global->LDS loads (see populate_bf16_stream_kernel for the load, swizzle and
+// transposed-read scheme). Within k-tile s the fragment reads of its second
+// k step are issued before the MFMAs of its first; the barrier that publishes
+// k-tile s+1 sits between the two MFMA groups, and the first reads of k-tile
+// s+1 are issued right after it, so LDS reads overlap MFMAs across k-tiles.
+// At the barrier for k-tile s+1 every wave has finished its reads of k-tile
+// s-1 (they fed MFMAs issued before it), so that slot is refilled with k-tile
+// s-1+NSLOT: NSLOT-2 k-tiles are in flight while one is multiplied.
+template <int BM, int BN, int NSLOT>
+__global__ __launch_bounds__(256) void populate_bf16_w4_kernel(GemmArgs a, int num_m, int num_n)
+{
+    static_assert(BM == 256, "the LDS epilogue indexes 256 rows per head block");
+    constexpr int WGM = 2, WGN = 2;
+    using T = StreamTile<BM, BN, WGM, WGN>;
+    using F = FragsT<BM, BN, WGM, WGN>;
+    constexpr int LD_PER_SLOT = T::A_LD + T::B_LD;
+    static_assert(NSLOT >= 3 && (NSLOT - 2) * LD_PER_SLOT <= 63, "ring depth");
+    constexpr int GROUP_M = 8;
+    __shared__ __attribute__((aligned(1024))) StreamSlot<BM, BN> ring[NSLOT];
+
+    const int ntiles = num_m * num_n;
+    const int per_xcd = (ntiles + 7) / 8;
+    const int tile = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+    if (tile >= ntiles) return;
+    const int group = tile / (GROUP_M * num_n);
+    const int first_m = group * GROUP_M;
+    const int gsize = min(num_m - first_m, GROUP_M);
+    const int pid_m = first_m + (tile % (GROUP_M * num_n)) % gsize;
+    const int pid_n = (tile % (GROUP_M * num_n)) / gsize;
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wave / WGN, wn = wave % WGN;
+    const int HD = a.H * a.D;
+    const int m0 = pid_m * BM;
+    const int n0 = pid_n * BN;
+    const int p = n0 / HD;
+    const int col0 = n0 - p * HD;
+    const uint16_t* __restrict__ E = static_cast<const uint16_t*>(a.E);
+    const uint16_t* __restrict__ W = static_cast<const uint16_t*>(a.wt.w[p]);
+
+    f32x16 acc[T::NB][T::MB];
+#pragma unroll
+    for (int i = 0; i < T::NB; ++i)
+#pragma unroll
+        for (int j = 0; j < T::MB; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+    const int nk = a.dm / T::BK;
+    // Before the wait for k-tile j, k-tiles 0..min(j + NSLOT - 3, nk - 1) have
+    // been issued (0..NSLOT-2 for j = 0); wait until only the later ones are
+    // outstanding, then barrier so that every thread's loads of j are visible.
+    auto sync_tile = [&](int j) {
+        const int issued = min(j == 0 ? NSLOT - 2 : j + NSLOT - 3, nk - 1);
+        const int later = issued - j;
+        if (later >= 3)
+            __builtin_amdgcn_s_waitcnt(vmcnt_wait(3 * LD_PER_SLOT));
+        else if (later == 2)
+            __builtin_amdgcn_s_waitcnt(vmcnt_wait(2 * LD_PER_SLOT));
+        else if (later == 1)
+            __builtin_amdgcn_s_waitcnt(vmcnt_wait(LD_PER_SLOT));
+        else
+            __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));
+        __builtin_amdgcn_s_barrier();
+    };
+    static_assert(NSLOT - 2 <= 3, "sync_tile handles up to three k-tiles in flight");
+
+    for (int t = 0; t < NSLOT - 1 && t < nk; ++t)
+        stream_issue<BM, BN, WGM, WGN>(ring[t], E, W, t, m0, a.M, a.dm, HD, col0, wave, lane);
+    sync_tile(0);
+    F cur, nxt;
+    read_frags_t<BM, BN, WGM, WGN>(ring[0], 0, wm, wn, lane, cur);
+    // The last k-tile is peeled off so that the loop body has no join between
+    // the reads for k-tile s+1 and the MFMAs that follow them (a join would
+    // make the compiler wait for those reads there).
+    int slot = 0;
+    for (int s = 0; s + 1 < nk; ++s) {
+        read_frags_t<BM, BN, WGM, WGN>(ring[slot], 16, wm, wn, lane, nxt);
+        mfma_frags_t<BM, BN, WGM, WGN>(cur, acc);
+        const int next_slot = slot + 1 == NSLOT ? 0 : slot + 1;
+        sync_tile(s + 1);
+        const int t = s - 1 + NSLOT;
+        if (t < nk) {
+            const int fill = slot == 0 ? NSLOT - 1 : slot - 1;
+            stream_issue<BM, BN, WGM, WGN>(ring[fill], E, W, t, m0, a.M, a.dm, HD, col0, wave, lane);
+        }
+        read_frags_t<BM, BN, WGM, WGN>(ring[next_slot], 0, wm, wn, lane, cur);
+        mfma_frags_t<BM, BN, WGM, WGN>(nxt, acc);
+        slot = next_slot;
+    }
+    read_frags_t<BM, BN, WGM, WGN>(ring[slot], 16, wm, wn, lane, nxt);
+    mfma_frags_t<BM, BN, WGM, WGN>(cur, acc);
+    mfma_frags_t<BM, BN, WGM, WGN>(nxt, acc);
+#ifndef CKE_POP_LDS_EPILOGUE
+#define CKE_POP_LDS_EPILOGUE 1
+#endif
+    if (CKE_POP_LDS_EPILOGUE && NSLOT * (int)sizeof(StreamSlot<BM, BN>) >= BM * BN * 2) {
+        __syncthreads();
+        epilogue_t_lds<BM, BN, WGM, WGN>(a, acc, m0, p, col0, wm, wn, lane,
+                                         reinterpret_cast<uint16_t*>(&ring[0]));
+    } else {
+        epilogue_t_bf16<BM, BN, WGM, WGN>(a, acc, m0, p, col0, wm, wn, lane);
+    }
+}
+
+template <int BM, int BN, int NSLOT>
+hipError_t launch_bf16_w4(const GemmArgs& g, hipStream_t st) {
+    const int HD = g.H * g.D;
+    const int num_m = (g.M + BM - 1) / BM;
+    const int num_n = 2 * g.L * HD / BN;
+    const int ntiles = num_m * num_n;
+    const int grid = ((ntiles + 7) / 8) * 8;
+    hipLaunchKernelGGL((populate_bf16_w4_kernel<BM, BN, NSLOT>), dim3(grid), dim3(256), 0, st, g, num_m,
+                       num_n);
+    return hipGetLastError();
+}
+
+template <int BM, int BN, int WGM, int WGN>
+hipError_t launch_bf16_stream(const GemmArgs& g, hipStream_t st) {
+    const int HD = g.H * g.D;
+    const int num_m = (g.M + BM - 1) / BM;
+    const int num_n = 2 * g.L * HD / BN;
+    const int ntiles = num_m * num_n;
+    const int grid = ((ntiles + 7) / 8) * 8;
+    hipLaunchKernelGGL((populate_bf16_stream_kernel<BM, BN, WGM, WGN>), dim3(grid),
+                       dim3(WGM * WGN * 64), 0, st, g, num_m, num_n);
+    return hipGetLastError();
+}
+
 template <int BM, int BN, int BK, int WGM, int WGN>
 hipError_t launch_bf16_big(const GemmArgs& g, hipStream_t st) {
     const int HD = g.H * g.D;
@@ -533,6 +1048,16 @@ hipError_t launch_populate(const PopulateLaunch& a, hipStream_t st) {
 #ifndef CKE_POP_BF16_WGN
 #define CKE_POP_BF16_WGN 2
 #endif
+#ifndef CKE_POP_BF16_KERNEL
+#define CKE_POP_BF16_KERNEL 2
+#endif
+#ifndef CKE_POP_W4_SLOTS
+#define CKE_POP_W4_SLOTS 4
+#endif
+    if (CKE_POP_BF16_KERNEL == 2 && a.bf16 && HD % 256 == 0 && a.dm % 32 == 0)
+        return launch_bf16_w4<256, 256, CKE_POP_W4_SLOTS>(g, st);
+    if (CKE_POP_BF16_KERNEL == 1 && a.bf16 && HD % 256 == 0 && a.dm % 128 == 0)
+        return launch_bf16_stream<256, 256, 2, 4>(g, st);
     if (a.bf16 && HD % CKE_POP_BF16_BN == 0 && a.dm % CKE_POP_BF16_BK == 0)
         return launch_bf16_big<CKE_POP_BF16_BM, CKE_POP_BF16_BN, CKE_POP_BF16_BK, CKE_POP_BF16_WGM,
                                CKE_POP_BF16_WGN>(g, st);
