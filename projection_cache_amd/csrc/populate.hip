@@ -548,151 +548,6 @@ __device__ __forceinline__ void stream_issue(StreamSlot<BM, BN>& slot, const uin
     }
 }
 
-// Multiply one ring slot into the accumulators.
-template <int BM, int BN, int WGM, int WGN>
-__device__ __forceinline__ void stream_compute(
-    const StreamSlot<BM, BN>& slot, int wm, int wn, int lane,
-    f32x16 (&acc)[StreamTile<BM, BN, WGM, WGN>::MB][StreamTile<BM, BN, WGM, WGN>::NB])
-{
-    using T = StreamTile<BM, BN, WGM, WGN>;
-#pragma unroll
-    for (int kk = 0; kk < T::BK; kk += 16) {
-        bf16x8 av[T::MB], bv[T::NB];
-#pragma unroll
-        for (int mb = 0; mb < T::MB; ++mb) {
-            const int row = wm * T::WTM + mb * 32 + (lane & 31);
-            const int piece = ((kk >> 3) + (lane >> 5)) ^ ((row >> 2) & 3);
-            av[mb] = *reinterpret_cast<const bf16x8*>(slot.a + row * T::BK + piece * 8);
-        }
-#pragma unroll
-        for (int nb = 0; nb < T::NB; ++nb) {
-            const int g = (lane >> 4) & 3, L = lane & 15;
-            const int ncol = wn * T::WTN + nb * 32 + 16 * (g & 1) + 4 * (L & 3);
-            v4i16_bf h[2];
-#pragma unroll
-            for (int jr = 0; jr < 2; ++jr) {
-                const int krow = kk + 8 * (g >> 1) + 4 * jr + (L >> 2);
-                const int piece = (ncol >> 3) ^ (4 * (krow & 3));
-                h[jr] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_v4i16*)(slot.b + krow * BN + piece * 8 + (ncol & 7)));
-            }
-            bf16x8 b;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                b[j] = __builtin_bit_cast(__bf16, (short)h[0][j]);
-                b[4 + j] = __builtin_bit_cast(__bf16, (short)h[1][j]);
-            }
-            bv[nb] = b;
-        }
-#pragma unroll
-        for (int mb = 0; mb < T::MB; ++mb)
-#pragma unroll
-            for (int nb = 0; nb < T::NB; ++nb)
-                acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[mb], bv[nb], acc[mb][nb], 0, 0, 0);
-    }
-}
-
-// bf16 populate, streaming version for gfx950:
-//  * operand tiles move global -> LDS with global_load_lds_dwordx4 (each lane's
-//    16 bytes land at the instruction's LDS base + lane*16; no staging
-//    registers), into a ring of 4 slots of BK = 32, so three k-tiles are in
-//    flight while one is multiplied; one barrier per k-tile. The loads are
-//    ordered by explicit vmcnt waits: before multiplying k-tile kt a thread
-//    waits until at most the loads of the two later k-tiles are outstanding,
-//    then the barrier makes every thread's loads of kt visible;
-//  * W stays in its [k][n] layout in LDS and the B fragments are read with
-//    ds_read_b64_tr_b16: within each 16-lane group, lane i receives element
-//    i%4 of the 8 bytes addressed by lane 4j + i/4 (j = 0..3), so when four
-//    lanes per row address four consecutive k-rows x 16 columns, lane i gets
-//    four consecutive k of column i. Two such reads give a 32x32x16 B operand;
-//  * the 16-byte pieces of each LDS row are XOR-swizzled by row so that
-//    fragment reads hit distinct banks: A rows (BK = 32 -> 4 pieces)
-//    piece ^ ((row >> 2) & 3); B rows piece ^ 4*(row & 3). The direct loads
-//    pick, per lane, the global piece that belongs in the lane's LDS slot;
-//  * rows of E past M are clamped to row M-1 for loading; their products
-//    only reach output rows that are never stored.
-template <int BM, int BN, int WGM, int WGN>
-__global__ __launch_bounds__(WGM * WGN * 64) void populate_bf16_stream_kernel(GemmArgs a, int num_m, int num_n)
-{
-    using T = StreamTile<BM, BN, WGM, WGN>;
-    constexpr int LD_PER_SLOT = T::A_LD + T::B_LD;
-    constexpr int GROUP_M = 8;
-    __shared__ __attribute__((aligned(1024))) StreamSlot<BM, BN> ring0;
-    __shared__ __attribute__((aligned(1024))) StreamSlot<BM, BN> ring1;
-    __shared__ __attribute__((aligned(1024))) StreamSlot<BM, BN> ring2;
-    __shared__ __attribute__((aligned(1024))) StreamSlot<BM, BN> ring3;
-
-    const int ntiles = num_m * num_n;
-    const int per_xcd = (ntiles + 7) / 8;
-    const int tile = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
-    if (tile >= ntiles) return;
-    const int group = tile / (GROUP_M * num_n);
-    const int first_m = group * GROUP_M;
-    const int gsize = min(num_m - first_m, GROUP_M);
-    const int pid_m = first_m + (tile % (GROUP_M * num_n)) % gsize;
-    const int pid_n = (tile % (GROUP_M * num_n)) / gsize;
-
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int wm = wave / WGN, wn = wave % WGN;
-    const int HD = a.H * a.D;
-    const int m0 = pid_m * BM;
-    const int n0 = pid_n * BN;
-    const int p = n0 / HD;
-    const int col0 = n0 - p * HD;
-    const uint16_t* __restrict__ E = static_cast<const uint16_t*>(a.E);
-    const uint16_t* __restrict__ W = static_cast<const uint16_t*>(a.wt.w[p]);
-
-    f32x16 acc[T::MB][T::NB];
-#pragma unroll
-    for (int i = 0; i < T::MB; ++i)
-#pragma unroll
-        for (int j = 0; j < T::NB; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-
-    const int nk = a.dm / T::BK;
-    auto issue = [&](StreamSlot<BM, BN>& slot, int kt) {
-        if (kt < nk) stream_issue<BM, BN, WGM, WGN>(slot, E, W, kt, m0, a.M, a.dm, HD, col0, wave, lane);
-    };
-    // Wait until this thread's loads of k-tile kt have landed (the loads of up
-    // to two later k-tiles may stay outstanding), then barrier so that every
-    // thread's have; no fence, so outstanding loads into other slots continue.
-    auto sync_tile = [&](int kt) {
-        const int later = min(2, nk - 1 - kt);
-        // s_waitcnt immediate (gfx9 encoding): vmcnt in bits 3:0 and 15:14,
-        // expcnt 6:4 and lgkmcnt 11:8 left at their maxima (no wait).
-        if (later >= 2)
-            __builtin_amdgcn_s_waitcnt(vmcnt_wait(2 * LD_PER_SLOT));
-        else if (later == 1)
-            __builtin_amdgcn_s_waitcnt(vmcnt_wait(LD_PER_SLOT));
-        else
-            __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));
-        __builtin_amdgcn_s_barrier();
-    };
-
-    // The host launches this kernel only when nk is a multiple of the ring
-    // depth, so every pass of the loop below runs all four slots.
-    stream_issue<BM, BN, WGM, WGN>(ring0, E, W, 0, m0, a.M, a.dm, HD, col0, wave, lane);
-    stream_issue<BM, BN, WGM, WGN>(ring1, E, W, 1, m0, a.M, a.dm, HD, col0, wave, lane);
-    stream_issue<BM, BN, WGM, WGN>(ring2, E, W, 2, m0, a.M, a.dm, HD, col0, wave, lane);
-    for (int kt = 0; kt < nk; kt += 4) {
-        sync_tile(kt);
-        issue(ring3, kt + 3);
-        stream_compute<BM, BN, WGM, WGN>(ring0, wm, wn, lane, acc);
-        sync_tile(kt + 1);
-        issue(ring0, kt + 4);
-        stream_compute<BM, BN, WGM, WGN>(ring1, wm, wn, lane, acc);
-        sync_tile(kt + 2);
-        issue(ring1, kt + 5);
-        stream_compute<BM, BN, WGM, WGN>(ring2, wm, wn, lane, acc);
-        sync_tile(kt + 3);
-        issue(ring2, kt + 6);
-        stream_compute<BM, BN, WGM, WGN>(ring3, wm, wn, lane, acc);
-    }
-    epilogue<BM, BN, WGM, WGN, uint16_t>(a, acc, m0, p, col0);
-}
-
 // Read the fragments of one 16-deep k step of a ring slot for the transposed
 // product C^T = W^T E^T: the W side (MFMA A operand, rows = output columns n)
 // through ds_read_b64_tr_b16, the E side (MFMA B operand, columns = output
@@ -751,48 +606,8 @@ __device__ __forceinline__ void mfma_frags_t(
 
 // Store a transposed accumulator tile (acc[nb][mb] holds C^T: register r of
 // lane L is output column n = 8*(r/4) + 4*(L/32) + r%4 and output row
-// m = L%32 of its 32x32 block). Each lane packs four consecutive columns of
-// one row, which lie in one head since D is a multiple of 4, into one 8-byte
-// bf16 store at Kc/Vc[l][b][h][t][d..d+3]. (b, t) is worked out once per row.
-template <int BM, int BN, int WGM, int WGN>
-__device__ __forceinline__ void epilogue_t_bf16(
-    const GemmArgs& a,
-    const f32x16 (&acc)[StreamTile<BM, BN, WGM, WGN>::NB][StreamTile<BM, BN, WGM, WGN>::MB], int m0, int p,
-    int col0, int wm, int wn, int lane)
-{
-    using T = StreamTile<BM, BN, WGM, WGN>;
-    const int l = p < a.L ? p : p - a.L;
-    uint16_t* C = static_cast<uint16_t*>(p < a.L ? a.Kc : a.Vc);
-    const size_t TD = (size_t)a.T * a.D;
-    size_t row_off[T::MB];
-    bool ok[T::MB];
-#pragma unroll
-    for (int mb = 0; mb < T::MB; ++mb) {
-        const int m = m0 + wm * T::WTM + mb * 32 + (lane & 31);
-        ok[mb] = m < a.M;
-        const int b = m / a.T, t = m - b * a.T;
-        row_off[mb] = (size_t)(l * a.B + b) * a.H * TD + (size_t)t * a.D;
-    }
-#pragma unroll
-    for (int nb = 0; nb < T::NB; ++nb)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const int n = col0 + wn * T::WTN + nb * 32 + 8 * g + 4 * (lane >> 5);
-            const int h = n / a.D, d = n - h * a.D;
-            const size_t col_off = (size_t)h * TD + d;
-#pragma unroll
-            for (int mb = 0; mb < T::MB; ++mb) {
-                const f32x16& v = acc[nb][mb];
-                uint2 w;
-                w.x = (uint32_t)to_bf16_bits(v[4 * g]) | ((uint32_t)to_bf16_bits(v[4 * g + 1]) << 16);
-                w.y = (uint32_t)to_bf16_bits(v[4 * g + 2]) | ((uint32_t)to_bf16_bits(v[4 * g + 3]) << 16);
-                if (ok[mb]) *reinterpret_cast<uint2*>(C + row_off[mb] + col_off) = w;
-            }
-        }
-}
-
-// Store a transposed accumulator tile (as epilogue_t_bf16 holds it) through
-// LDS so that global writes are whole rows: for a fixed head the tile's rows
+// m = L%32 of its 32x32 block; four consecutive columns of one row lie in one
+// head since D is a multiple of 4) through LDS so that global writes are whole rows: for a fixed head the tile's rows
 // t .. t+BM-1 of one stream are contiguous in Kc/Vc[l][b][h][t][d], so each
 // wave writes 64 x 16 consecutive bytes per store. `stage` is at least
 // BM*BN*2 bytes of LDS no wave reads any more; the caller has passed a barrier
@@ -858,20 +673,35 @@ __device__ __forceinline__ void epilogue_t_lds(
     }
 }
 
-// bf16 populate with four waves (one per SIMD), each owning a 128x128 block
-// of a 256x256 output tile, which halves LDS read traffic per MFMA against
-// 128x64 wave blocks. The product is formed transposed (W^T as the MFMA A
-// operand, E^T as B) so that each lane ends up with four consecutive output
-// columns of one row and stores 8 bytes at a time.
-// Operand tiles stream into a ring of NSLOT slots of BK = 32 by direct
-// global->LDS loads (see populate_bf16_stream_kernel for the load, swizzle and
-// transposed-read scheme). Within k-tile s the fragment reads of its second
-// k step are issued before the MFMAs of its first; the barrier that publishes
-// k-tile s+1 sits between the two MFMA groups, and the first reads of k-tile
-// s+1 are issued right after it, so LDS reads overlap MFMAs across k-tiles.
-// At the barrier for k-tile s+1 every wave has finished its reads of k-tile
-// s-1 (they fed MFMAs issued before it), so that slot is refilled with k-tile
-// s-1+NSLOT: NSLOT-2 k-tiles are in flight while one is multiplied.
+// bf16 populate for gfx950. Four waves (one per SIMD) each own a 128x128
+// block of a 256x256 output tile. The product is formed transposed (W^T as
+// the MFMA A operand, E^T as B) so that each lane ends up with four
+// consecutive output columns of one row.
+//  * operand tiles move global -> LDS with global_load_lds_dwordx4 (each lane's
+//    16 bytes land at the instruction's LDS base + lane*16; no staging
+//    registers) into a ring of NSLOT slots of BK = 32;
+//  * W stays in its [k][n] layout in LDS and its fragments are read with
+//    ds_read_b64_tr_b16: within each 16-lane group, lane i receives element
+//    i%4 of the 8 bytes addressed by lane 4j + i/4 (j = 0..3), so when four
+//    lanes per row address four consecutive k-rows x 16 columns, lane i gets
+//    four consecutive k of column i. Two such reads give a 32x32x16 operand;
+//  * the 16-byte pieces of each LDS row are XOR-swizzled by row so that
+//    fragment reads hit distinct banks: E rows (BK = 32 -> 4 pieces)
+//    piece ^ ((row >> 2) & 3); W rows piece ^ 4*(row & 3). The direct loads
+//    pick, per lane, the global piece that belongs in the lane's LDS slot;
+//  * rows of E past M are clamped to row M-1 for loading; their products
+//    only reach output rows that are never stored;
+//  * within k-tile s the fragment reads of its second k step are issued
+//    before the MFMAs of its first; the barrier that publishes k-tile s+1
+//    sits between the two MFMA groups and the first reads of k-tile s+1 are
+//    issued right after it, so LDS reads overlap MFMAs across k-tiles;
+//  * at the barrier for k-tile s+1 every wave has finished its reads of
+//    k-tile s-1 (they fed MFMAs issued before it), so that slot is refilled
+//    with k-tile s-1+NSLOT: NSLOT-2 k-tiles are in flight while one is
+//    multiplied. A thread waits for its own loads with an explicit vmcnt,
+//    the barrier then makes every thread's loads visible;
+//  * the finished tile is staged through the ring (epilogue_t_lds) and
+//    written as whole rows.
 template <int BM, int BN, int NSLOT>
 __global__ __launch_bounds__(256) void populate_bf16_w4_kernel(GemmArgs a, int num_m, int num_n)
 {
@@ -947,10 +777,9 @@ __global__ __launch_bounds__(256) void populate_bf16_w4_kernel(GemmArgs a, int n
         const int next_slot = slot + 1 == NSLOT ? 0 : slot + 1;
         sync_tile(s + 1);
         const int t = s - 1 + NSLOT;
-        if (t < nk) {
-            const int fill = slot == 0 ? NSLOT - 1 : slot - 1;
+        const int fill = slot == 0 ? NSLOT - 1 : slot - 1;
+        if (t < nk)
             stream_issue<BM, BN, WGM, WGN>(ring[fill], E, W, t, m0, a.M, a.dm, HD, col0, wave, lane);
-        }
         read_frags_t<BM, BN, WGM, WGN>(ring[next_slot], 0, wm, wn, lane, cur);
         mfma_frags_t<BM, BN, WGM, WGN>(nxt, acc);
         slot = next_slot;
@@ -958,16 +787,9 @@ __global__ __launch_bounds__(256) void populate_bf16_w4_kernel(GemmArgs a, int n
     read_frags_t<BM, BN, WGM, WGN>(ring[slot], 16, wm, wn, lane, nxt);
     mfma_frags_t<BM, BN, WGM, WGN>(cur, acc);
     mfma_frags_t<BM, BN, WGM, WGN>(nxt, acc);
-#ifndef CKE_POP_LDS_EPILOGUE
-#define CKE_POP_LDS_EPILOGUE 1
-#endif
-    if (CKE_POP_LDS_EPILOGUE && NSLOT * (int)sizeof(StreamSlot<BM, BN>) >= BM * BN * 2) {
-        __syncthreads();
-        epilogue_t_lds<BM, BN, WGM, WGN>(a, acc, m0, p, col0, wm, wn, lane,
-                                         reinterpret_cast<uint16_t*>(&ring[0]));
-    } else {
-        epilogue_t_bf16<BM, BN, WGM, WGN>(a, acc, m0, p, col0, wm, wn, lane);
-    }
+    static_assert(NSLOT * sizeof(StreamSlot<BM, BN>) >= BM * BN * 2, "ring too small to stage the tile");
+    __syncthreads();
+    epilogue_t_lds<BM, BN, WGM, WGN>(a, acc, m0, p, col0, wm, wn, lane, reinterpret_cast<uint16_t*>(&ring[0]));
 }
 
 template <int BM, int BN, int NSLOT>
@@ -979,18 +801,6 @@ hipError_t launch_bf16_w4(const GemmArgs& g, hipStream_t st) {
     const int grid = ((ntiles + 7) / 8) * 8;
     hipLaunchKernelGGL((populate_bf16_w4_kernel<BM, BN, NSLOT>), dim3(grid), dim3(256), 0, st, g, num_m,
                        num_n);
-    return hipGetLastError();
-}
-
-template <int BM, int BN, int WGM, int WGN>
-hipError_t launch_bf16_stream(const GemmArgs& g, hipStream_t st) {
-    const int HD = g.H * g.D;
-    const int num_m = (g.M + BM - 1) / BM;
-    const int num_n = 2 * g.L * HD / BN;
-    const int ntiles = num_m * num_n;
-    const int grid = ((ntiles + 7) / 8) * 8;
-    hipLaunchKernelGGL((populate_bf16_stream_kernel<BM, BN, WGM, WGN>), dim3(grid),
-                       dim3(WGM * WGN * 64), 0, st, g, num_m, num_n);
     return hipGetLastError();
 }
 
@@ -1033,34 +843,10 @@ hipError_t launch_populate(const PopulateLaunch& a, hipStream_t st) {
     g.H = a.H;
     g.D = a.D;
     const int HD = a.H * a.D;
-#ifndef CKE_POP_BF16_BM
-#define CKE_POP_BF16_BM 256
-#endif
-#ifndef CKE_POP_BF16_BN
-#define CKE_POP_BF16_BN 256
-#endif
-#ifndef CKE_POP_BF16_BK
-#define CKE_POP_BF16_BK 64
-#endif
-#ifndef CKE_POP_BF16_WGM
-#define CKE_POP_BF16_WGM 4
-#endif
-#ifndef CKE_POP_BF16_WGN
-#define CKE_POP_BF16_WGN 2
-#endif
-#ifndef CKE_POP_BF16_KERNEL
-#define CKE_POP_BF16_KERNEL 2
-#endif
 #ifndef CKE_POP_W4_SLOTS
 #define CKE_POP_W4_SLOTS 4
 #endif
-    if (CKE_POP_BF16_KERNEL == 2 && a.bf16 && HD % 256 == 0 && a.dm % 32 == 0)
-        return launch_bf16_w4<256, 256, CKE_POP_W4_SLOTS>(g, st);
-    if (CKE_POP_BF16_KERNEL == 1 && a.bf16 && HD % 256 == 0 && a.dm % 128 == 0)
-        return launch_bf16_stream<256, 256, 2, 4>(g, st);
-    if (a.bf16 && HD % CKE_POP_BF16_BN == 0 && a.dm % CKE_POP_BF16_BK == 0)
-        return launch_bf16_big<CKE_POP_BF16_BM, CKE_POP_BF16_BN, CKE_POP_BF16_BK, CKE_POP_BF16_WGM,
-                               CKE_POP_BF16_WGN>(g, st);
+    if (a.bf16 && HD % 256 == 0 && a.dm % 32 == 0) return launch_bf16_w4<256, 256, CKE_POP_W4_SLOTS>(g, st);
     if (a.bf16 && HD % 128 == 0 && a.dm % 64 == 0) return launch_bf16_big<128, 128, 64, 2, 2>(g, st);
 #ifndef CKE_POP_F32_BM
 #define CKE_POP_F32_BM 64

@@ -110,6 +110,17 @@ POP_CASES = [
     (None, dict(n_layers=1, n_streams=1, mem_len=200, d_model=256, n_heads=2, head_dim=128,
                 dtype="bf16")),
     (None, dict(n_layers=2, n_streams=2, mem_len=130, d_model=384, n_heads=3, head_dim=128)),
+    # bf16, 256-wide column tiles: memories shorter than a row tile (several
+    # streams per tile) and longer than one (a tile straddling two streams)
+    (None, dict(n_layers=2, n_streams=3, mem_len=100, d_model=256, n_heads=8, head_dim=32,
+                dtype="bf16")),
+    (None, dict(n_layers=1, n_streams=2, mem_len=300, d_model=512, n_heads=8, head_dim=64,
+                dtype="bf16")),
+    # bf16 widths that are not a multiple of 256 (128-wide tiles) or of 128
+    (None, dict(n_layers=2, n_streams=2, mem_len=130, d_model=384, n_heads=3, head_dim=128,
+                dtype="bf16")),
+    (None, dict(n_layers=3, n_streams=2, mem_len=33, d_model=96, n_heads=3, head_dim=32,
+                dtype="bf16")),
 ]
 
 
