@@ -70,6 +70,9 @@ def parse():
     ap.add_argument("--counters", action="store_true",
                     help="only run --steps windows with eager launches and no graph capture "
                          "(the mode hardware-counter passes use)")
+    ap.add_argument("--counter-tokens", type=int, default=None,
+                    help="with --counters: stop each window after this many decode steps "
+                         "(every call of a kind moves the same bytes, so a few suffice)")
     return ap.parse_args()
 
 
@@ -128,13 +131,14 @@ class Workload:
         g = self.g
         return g.steps * (g.n_seqs if g.n_seqs else g.n_streams * g.n_q)
 
-    def window(self, stream, kinds=("populate", "selfattn", "xattn_decode")):
+    def window(self, stream, kinds=("populate", "selfattn", "xattn_decode"), tokens=None):
         """Enqueue one decode window on `stream`, or only the calls of the
-        given kinds (in window order)."""
+        given kinds (in window order); `tokens` cuts it after that many decode
+        steps (counter runs only)."""
         g, pc = self.g, self.pc
         if "populate" in kinds:
             pc.cke_xattn_populate(self.cache, self.E, self.WK, self.WV, stream=stream)
-        for t in range(g.steps):
+        for t in range(g.steps if tokens is None else min(tokens, g.steps)):
             for l in range(g.n_layers):
                 if g.n_seqs and "selfattn" in kinds:
                     pc.cke_selfattn_decode_append(self.qs[t, l], self.kn[t, l], self.vn[t, l],
@@ -306,7 +310,7 @@ def main():
     torch.cuda.synchronize()
     if args.counters:
         for _ in range(args.steps):
-            w.window(stream)
+            w.window(stream, tokens=args.counter_tokens)
         torch.cuda.synchronize()
         print(json.dumps({"counters_windows": args.steps, "config": args.config,
                           "xattn_bytes_per_call": w.cross_bytes_per_call(),

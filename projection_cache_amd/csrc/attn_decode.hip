@@ -256,7 +256,7 @@ namespace {
 #define CKE_CROSS_WAVES 4
 #endif
 #ifndef CKE_CROSS_NP
-#define CKE_CROSS_NP 2
+#define CKE_CROSS_NP 4
 #endif
 #ifndef CKE_SELF_WAVES
 #define CKE_SELF_WAVES 8

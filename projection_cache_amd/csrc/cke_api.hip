@@ -79,7 +79,7 @@ size_t region_elems(const cke_xattn_geom* g) {
 }
 
 #ifndef CKE_TARGET_WGS
-#define CKE_TARGET_WGS 1024
+#define CKE_TARGET_WGS 256
 #endif
 #ifndef CKE_MAX_SPLITS
 #define CKE_MAX_SPLITS 64
@@ -88,7 +88,7 @@ static_assert(CKE_MAX_SPLITS >= 1 && CKE_MAX_SPLITS <= cke::kMaxSplits, "split c
 
 // Split of the T memory rows of one (stream, head) across workgroups. Fixed
 // per geometry so that decode results are reproducible run to run. Aims for
-// about CKE_TARGET_WGS workgroups (4 per compute unit) but never fewer rows
+// about CKE_TARGET_WGS workgroups (one per compute unit) but never fewer rows
 // per workgroup than one pass of its waves.
 void split_plan(const cke_xattn_geom* g, int* nsplit, int* chunk) {
     if (g->mem_len <= cke::kShortMemRows) {  // one wave per head, no split
