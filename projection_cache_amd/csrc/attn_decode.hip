@@ -245,8 +245,17 @@ __global__ __launch_bounds__(NW * 64) void selfattn_append_kernel(
     WaveState<1, VEC> st;
     st.init();
     wave_attend<D, TE, 1, NP>(K, V, r0, r1, qr, 1, sl2, pos, kn, vn, st);
-    wg_merge<D, TE, 1, NW>(st, 1, wm, wl, wa, sM, sL, sA);
-    for (int d = threadIdx.x; d < D; d += NW * 64) out[bh * D + d] = sA[d] / sL[0];
+    if constexpr (NW == 1) {
+        // one wave holds every row: no cross-wave merge, no barrier
+        wave_merge_groups<D, TE, 1>(st, 1);
+        if (lane < LPK) {
+#pragma unroll
+            for (int j = 0; j < VEC; ++j) out[bh * D + sub * VEC + j] = st.acc[0][j] / st.l[0];
+        }
+    } else {
+        wg_merge<D, TE, 1, NW>(st, 1, wm, wl, wa, sM, sL, sA);
+        for (int d = threadIdx.x; d < D; d += NW * 64) out[bh * D + d] = sA[d] / sL[0];
+    }
 }
 
 // ------------------------------------------------------------- launchers
@@ -327,14 +336,25 @@ hipError_t launch_cross_t(const XattnLaunch& a, hipStream_t st) {
     return hipErrorInvalidValue;
 }
 
+template <int D, typename TE, int NW>
+hipError_t launch_self_nw(const SelfLaunch& a, hipStream_t st) {
+    dim3 grid(a.H, a.S);
+    hipLaunchKernelGGL((selfattn_append_kernel<D, TE, NW, kSelfNP>), grid, dim3(NW * 64), 0, st,
+                       a.q, a.k_new, a.v_new, static_cast<TE*>(a.K), static_cast<TE*>(a.V), a.out,
+                       a.H, a.max_pos, a.pos, a.scale * kLog2e);
+    return hipGetLastError();
+}
+
+// Waves per workgroup grow with the rows attended (pos + 1): each wave gets
+// at least one full load tile, so short caches skip the cross-wave merge.
 template <int D, typename TE>
 hipError_t launch_self_d(const SelfLaunch& a, hipStream_t st) {
-    dim3 grid(a.H, a.S);
-    hipLaunchKernelGGL((selfattn_append_kernel<D, TE, kSelfWaves, kSelfNP>), grid,
-                       dim3(kSelfWaves * 64), 0, st, a.q, a.k_new, a.v_new,
-                       static_cast<TE*>(a.K), static_cast<TE*>(a.V), a.out, a.H,
-                       a.max_pos, a.pos, a.scale * kLog2e);
-    return hipGetLastError();
+    constexpr int rows_per_tile = RowMap<D, TE>::kKPW * kSelfNP;
+    const int tiles = (a.pos + 1 + rows_per_tile - 1) / rows_per_tile;
+    if (tiles <= 1 || kSelfWaves == 1) return launch_self_nw<D, TE, 1>(a, st);
+    if (tiles <= 2 || kSelfWaves == 2) return launch_self_nw<D, TE, 2>(a, st);
+    if (tiles <= 4 || kSelfWaves == 4) return launch_self_nw<D, TE, 4>(a, st);
+    return launch_self_nw<D, TE, kSelfWaves>(a, st);
 }
 
 template <typename TE>

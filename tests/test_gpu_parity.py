@@ -237,6 +237,7 @@ SELF_CASES = [
     dict(S=3, H=4, D=64, P=70, dtype="bf16"),
     dict(S=2, H=2, D=128, P=33, dtype="f32"),
     dict(S=2, H=3, D=128, P=33, dtype="bf16"),
+    dict(S=2, H=2, D=64, P=200, dtype="bf16"),       # bf16 rows past 4 load tiles
 ]
 
 
