@@ -792,6 +792,188 @@ __global__ __launch_bounds__(256) void populate_bf16_w4_kernel(GemmArgs a, int n
     epilogue_t_lds<BM, BN, WGM, WGN>(a, acc, m0, p, col0, wm, wn, lane, reinterpret_cast<uint16_t*>(&ring[0]));
 }
 
+// fp32 populate for gfx950 on v_mfma_f32_32x32x2_f32: 64x64 output tiles,
+// four waves (2x2) of 32x32. Same scheme as the bf16 kernel, at fp32 widths:
+//  * the product is formed transposed, C^T = W^T E^T: lane l's A operand is
+//    W[k][n] (n = l%32, k = kk + l/32) and its B operand E[m][k] (m = l%32),
+//    so both tiles stay in LDS as loaded and each lane finally holds four
+//    consecutive output columns of one row;
+//  * operands move global -> LDS with global_load_lds_dwordx4 into a ring of
+//    NSLOT slots of BK = 16 or 32 (a 64xBK E tile and a BKx64 W tile,
+//    BK/16 16-byte pieces of each per thread), so NSLOT-1 k-tiles are in
+//    flight; a thread
+//    waits for its own loads with vmcnt, then one barrier per k-tile makes
+//    every thread's loads visible. After that barrier every wave has finished
+//    k-tile s-1, whose slot is refilled with k-tile s-1+NSLOT;
+//  * E rows (BK/4 16-byte pieces) hold global piece p at position
+//    p ^ ((m >> 1) & 3) (BK 16) or p ^ (m & 7) (BK 32), W rows
+//    (sixteen pieces) at p ^ 8*(k & 1), so the
+//    fragment reads of 32 rows / two k-rows spread over the banks;
+//  * rows of E past M are clamped to M-1 for loading and never stored;
+//  * the finished tile is staged through the ring as [head][row][D] and
+//    written as whole rows (a head's 64 rows of one stream are contiguous).
+// Requires D <= 64 with 64 % D == 0 (a tile holds whole heads).
+template <int NSLOT, int BK>
+__global__ __launch_bounds__(256) void populate_f32_dma_kernel(GemmArgs a, int num_m, int num_n)
+{
+    constexpr int BM = 64, BN = 64, NT = 256, GROUP_M = 8;
+    static_assert(BK == 16 || BK == 32, "k-tile");
+    constexpr int APR = BK / 4;                // 16-byte pieces per E row
+    constexpr int SLOT = BM * BK + BK * BN;   // floats
+    constexpr int A_LD = BM * APR / NT, B_LD = BK * (BN / 4) / NT;
+    constexpr int LD_PER_SLOT = A_LD + B_LD;   // loads per thread per k-tile
+    static_assert(NSLOT >= 2 && (NSLOT - 1) * LD_PER_SLOT <= 63, "ring depth");
+    static_assert(NSLOT * SLOT >= BM * BN, "ring too small to stage the tile");
+    __shared__ __attribute__((aligned(1024))) float ring[NSLOT * SLOT];
+
+    const int ntiles = num_m * num_n;
+    const int per_xcd = (ntiles + 7) / 8;
+    const int tile = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+    if (tile >= ntiles) return;
+    const int group = tile / (GROUP_M * num_n);
+    const int first_m = group * GROUP_M;
+    const int gsize = min(num_m - first_m, GROUP_M);
+    const int pid_m = first_m + (tile % (GROUP_M * num_n)) % gsize;
+    const int pid_n = (tile % (GROUP_M * num_n)) / gsize;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    const int HD = a.H * a.D;
+    const int m0 = pid_m * BM;
+    const int n0 = pid_n * BN;
+    const int p = n0 / HD;
+    const int col0 = n0 - p * HD;
+    const float* __restrict__ E = static_cast<const float*>(a.E);
+    const float* __restrict__ W = static_cast<const float*>(a.wt.w[p]);
+    // E row m holds global piece p at LDS position p ^ e_swz(m): the 16-byte
+    // reads of eight consecutive rows then hit eight distinct groups of four
+    // banks (rows are 64 or 128 bytes, the LDS has 32 banks of 4 bytes)
+    auto e_swz = [](int m) { return APR == 4 ? (m >> 1) & 3 : m & 7; };
+
+    // this thread's pieces: E piece tid + i*NT (row x / APR, LDS position
+    // x % APR), W piece tid + i*NT (row x / 16)
+    const float* a_src[A_LD];
+    const float* b_src[B_LD];
+#pragma unroll
+    for (int i = 0; i < A_LD; ++i) {
+        const int x = tid + i * NT, row = x / APR, pos = x % APR;
+        a_src[i] = E + (size_t)min(m0 + row, a.M - 1) * a.dm + ((pos ^ e_swz(row)) << 2);
+    }
+#pragma unroll
+    for (int i = 0; i < B_LD; ++i) {
+        const int x = tid + i * NT, row = x >> 4, pos = x & 15;
+        b_src[i] = W + (size_t)row * HD + col0 + ((pos ^ (8 * (row & 1))) << 2);
+    }
+    auto issue = [&](int slot, int kt) {
+        float* A = ring + slot * SLOT;
+        float* B = A + BM * BK;
+#pragma unroll
+        for (int i = 0; i < A_LD; ++i) dma16(a_src[i] + kt * BK, lds_addr(A + (i * NT + wave * 64) * 4));
+#pragma unroll
+        for (int i = 0; i < B_LD; ++i)
+            dma16(b_src[i] + (size_t)kt * BK * HD, lds_addr(B + (i * NT + wave * 64) * 4));
+    };
+    const int nk = a.dm / BK;
+    auto sync_tile = [&](int j) {
+        const int issued = min(j == 0 ? NSLOT - 1 : j + NSLOT - 2, nk - 1);
+        const int later = issued - j;
+        if (later >= 3)
+            __builtin_amdgcn_s_waitcnt(vmcnt_wait(3 * LD_PER_SLOT));
+        else if (later == 2)
+            __builtin_amdgcn_s_waitcnt(vmcnt_wait(2 * LD_PER_SLOT));
+        else if (later == 1)
+            __builtin_amdgcn_s_waitcnt(vmcnt_wait(LD_PER_SLOT));
+        else
+            __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));
+        __builtin_amdgcn_s_barrier();
+    };
+    static_assert(NSLOT - 1 <= 3, "sync_tile handles up to three k-tiles in flight");
+
+    // k order inside a k-tile: the two half-waves of an MFMA step take k from
+    // separate halves of the tile (step s: k = s for lanes 0-31 and
+    // k = BK/2 + s for lanes 32-63; any order is exact as long as both
+    // operands follow it). A lane's E values for the whole tile are then BK/2
+    // consecutive k of its row: BK/8 16-byte reads instead of BK/2 4-byte ones.
+    const int n_l = wn * 32 + (lane & 31);
+    const int m_l = wm * 32 + (lane & 31);
+    const int kh = lane >> 5;
+    f32x16 acc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+
+    for (int t = 0; t < NSLOT && t < nk; ++t) issue(t, t);
+    int slot = 0;
+    for (int s = 0; s < nk; ++s) {
+        sync_tile(s);
+        if (s >= 1 && s - 1 + NSLOT < nk) issue(slot == 0 ? NSLOT - 1 : slot - 1, s - 1 + NSLOT);
+        const float* A = ring + slot * SLOT;
+        const float* B = A + BM * BK;
+        float4 ep[BK / 8];
+#pragma unroll
+        for (int c = 0; c < BK / 8; ++c)
+            ep[c] = *reinterpret_cast<const float4*>(A + m_l * BK + (((kh * (BK / 8) + c) ^ e_swz(m_l)) << 2));
+#pragma unroll
+        for (int st = 0; st < BK / 2; ++st) {
+            const int k = kh * (BK / 2) + st;
+            const float wv = B[k * BN + (((n_l >> 2) ^ (8 * (k & 1))) << 2) + (n_l & 3)];
+            const float4& e4 = ep[st >> 2];
+            const float ev = (st & 3) == 0 ? e4.x : (st & 3) == 1 ? e4.y : (st & 3) == 2 ? e4.z : e4.w;
+            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(wv, ev, acc, 0, 0, 0);
+        }
+        slot = slot + 1 == NSLOT ? 0 : slot + 1;
+    }
+
+    // epilogue: stage [head j][row m][D] with 16-byte pieces XOR-swizzled by row
+    __syncthreads();
+    float* stage = ring;
+    const int lgD = __builtin_ctz(a.D);
+    const int lgP = lgD - 2;                 // log2 of 16-byte pieces per row
+    const int PD = 1 << lgP;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        const int n = wn * 32 + 8 * g + 4 * (lane >> 5);
+        const int j = n >> lgD, d = n & (a.D - 1);
+        const int off = ((j * BM + m_l) << lgD) + (((d >> 2) ^ (m_l & (PD - 1))) << 2);
+        *reinterpret_cast<float4*>(stage + off) = make_float4(acc[4 * g], acc[4 * g + 1], acc[4 * g + 2],
+                                                              acc[4 * g + 3]);
+    }
+    __syncthreads();
+    const int l = p < a.L ? p : p - a.L;
+    float* C = static_cast<float*>(p < a.L ? a.Kc : a.Vc);
+    const size_t TD = (size_t)a.T * a.D;
+    const int h0 = col0 >> lgD;
+    const int b0 = m0 / a.T, t0 = m0 - b0 * a.T;
+#pragma unroll 4
+    for (int id = tid; id < BM * BN / 4; id += NT) {
+        const int q = id & (PD - 1);
+        const int m = (id >> lgP) & (BM - 1);
+        const int j = id >> (lgP + 6);       // BM == 64 rows per head block
+        if (m0 + m < a.M) {
+            int t = t0 + m, b = b0;
+            if (t >= a.T) {
+                if (a.T >= BM) { t -= a.T; b += 1; }
+                else { b += t / a.T; t -= (t / a.T) * a.T; }
+            }
+            const float4 v = *reinterpret_cast<const float4*>(stage + ((j * BM + m) << lgD) +
+                                                              ((q ^ (m & (PD - 1))) << 2));
+            const size_t idx = ((size_t)(l * a.B + b) * a.H + h0 + j) * TD + (size_t)t * a.D + q * 4;
+            *reinterpret_cast<float4*>(C + idx) = v;
+        }
+    }
+}
+
+template <int NSLOT, int BK>
+hipError_t launch_f32_dma(const GemmArgs& g, hipStream_t st) {
+    const int HD = g.H * g.D;
+    const int num_m = (g.M + 63) / 64;
+    const int num_n = 2 * g.L * HD / 64;
+    const int ntiles = num_m * num_n;
+    const int grid = ((ntiles + 7) / 8) * 8;
+    hipLaunchKernelGGL((populate_f32_dma_kernel<NSLOT, BK>), dim3(grid), dim3(256), 0, st, g, num_m, num_n);
+    return hipGetLastError();
+}
+
 template <int BM, int BN, int NSLOT>
 hipError_t launch_bf16_w4(const GemmArgs& g, hipStream_t st) {
     const int HD = g.H * g.D;
@@ -848,6 +1030,14 @@ hipError_t launch_populate(const PopulateLaunch& a, hipStream_t st) {
 #endif
     if (a.bf16 && HD % 256 == 0 && a.dm % 32 == 0) return launch_bf16_w4<256, 256, CKE_POP_W4_SLOTS>(g, st);
     if (a.bf16 && HD % 128 == 0 && a.dm % 64 == 0) return launch_bf16_big<128, 128, 64, 2, 2>(g, st);
+#ifndef CKE_POP_F32_DMA
+#define CKE_POP_F32_DMA 3
+#endif
+#ifndef CKE_POP_F32_DMA_BK
+#define CKE_POP_F32_DMA_BK 32
+#endif
+    if (!a.bf16 && HD % 64 == 0 && a.D <= 64 && 64 % a.D == 0 && a.dm % CKE_POP_F32_DMA_BK == 0)
+        return launch_f32_dma<CKE_POP_F32_DMA, CKE_POP_F32_DMA_BK>(g, st);
 #ifndef CKE_POP_F32_BM
 #define CKE_POP_F32_BM 64
 #endif
