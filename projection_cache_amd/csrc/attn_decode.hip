@@ -31,7 +31,7 @@ namespace cke {
 // device-scope atomic loads and stores, last arrival by ticket) pays several
 // device-scope round trips on its tail; both measured slower than a second
 // small kernel, whose inputs are coherent at the kernel boundary.
-template <int D, typename TE, int NQ, int NW, int NP>
+template <int D, typename TE, int NQ, int NW, int NP, bool STREAM>
 __global__ __launch_bounds__(NW * 64) void xattn_partial_kernel(
     const float* __restrict__ q, const TE* __restrict__ Kl, const TE* __restrict__ Vl,
     float* __restrict__ out, float* __restrict__ part,
@@ -66,7 +66,7 @@ __global__ __launch_bounds__(NW * 64) void xattn_partial_kernel(
 
     WaveState<NQ, VEC> st;
     st.init();
-    wave_attend<D, TE, NQ, NP>(K, V, r0, r1, qr, nq, sl2, -1, nullptr, nullptr, st);
+    wave_attend<D, TE, NQ, NP, STREAM>(K, V, r0, r1, qr, nq, sl2, -1, nullptr, nullptr, st);
     wg_merge<D, TE, NQ, NW>(st, nq, wm, wl, wa, sM, sL, sA);
 
     if (nsplit == 1) {
@@ -299,10 +299,16 @@ hipError_t launch_cross_nq(const XattnLaunch& a, hipStream_t st) {
     // many queries already give each loaded row more work: keep their tiles short
     constexpr int NP = (NQ > 2 && kCrossNP > 2) ? 2 : kCrossNP;
     dim3 grid(a.nsplit, a.H, a.B);
-    hipLaunchKernelGGL((xattn_partial_kernel<D, TE, NQ, kCrossWaves, NP>), grid,
-                       dim3(kCrossWaves * 64), 0, st, a.q,
-                       static_cast<const TE*>(a.K), static_cast<const TE*>(a.V), a.out,
-                       a.part, a.nq, a.max_q, a.H, a.T, a.nsplit, a.chunk, a.scale * kLog2e);
+    if (a.stream_rows)
+        hipLaunchKernelGGL((xattn_partial_kernel<D, TE, NQ, kCrossWaves, NP, true>), grid,
+                           dim3(kCrossWaves * 64), 0, st, a.q,
+                           static_cast<const TE*>(a.K), static_cast<const TE*>(a.V), a.out,
+                           a.part, a.nq, a.max_q, a.H, a.T, a.nsplit, a.chunk, a.scale * kLog2e);
+    else
+        hipLaunchKernelGGL((xattn_partial_kernel<D, TE, NQ, kCrossWaves, NP, false>), grid,
+                           dim3(kCrossWaves * 64), 0, st, a.q,
+                           static_cast<const TE*>(a.K), static_cast<const TE*>(a.V), a.out,
+                           a.part, a.nq, a.max_q, a.H, a.T, a.nsplit, a.chunk, a.scale * kLog2e);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.nsplit == 1) return e;
     const int G = (a.nsplit + kMergeBatch - 1) / kMergeBatch;

@@ -74,6 +74,11 @@ int check_geom(const cke_xattn_geom* g) {
     return CKE_OK;
 }
 
+// Whole cross caches (K + V, all layers) above this size are streamed past
+// the caches by decode (twice the MALL; Whisper Base's 37 MB and Q-Former's
+// 49 MB stay resident between calls, Large's 3.9 GB cannot).
+constexpr size_t kStreamCacheBytes = size_t(512) << 20;
+
 size_t region_elems(const cke_xattn_geom* g) {
     return (size_t)g->n_layers * g->n_streams * g->n_heads * (size_t)g->mem_len * g->head_dim;
 }
@@ -254,6 +259,9 @@ int cke_xattn_decode(const float* q, int n_q, const cke_xattn_cache* c, int laye
     a.chunk = c->chunk;
     a.scale = scale;
     a.bf16 = g.cache_dtype == CKE_BF16;
+    // K and V of every layer together: a cache this much larger than the
+    // 256 MB MALL is never re-read from it, so its rows are streamed
+    a.stream_rows = 2 * region_elems(&g) * elem_bytes(g.cache_dtype) > kStreamCacheBytes;
     hipError_t e = cke::launch_xattn_decode(a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(CKE_EDEVICE, "decode launch failed: %s", hipGetErrorString(e));
     return CKE_OK;

@@ -19,6 +19,7 @@ struct XattnLaunch {
     int B, H, T, D, nq, max_q, nsplit, chunk;
     float scale;
     bool bf16;
+    bool stream_rows;    // whole cross cache far larger than the MALL: non-temporal row loads
 };
 
 struct SelfLaunch {
