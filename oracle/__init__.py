@@ -62,6 +62,7 @@ def lib():
         L.orc_cross_decode.argtypes = [_I] * 5 + [_D, _P, _P, _P, _P]
         L.orc_self_append_attend.argtypes = [_I] * 5 + [_D, _I] + [_P] * 6
         L.orc_kv_blend_update.argtypes = [_I] * 5 + [_P, _P]
+        L.orc_self_prefill_append.argtypes = [_I] * 7 + [_D, _I] + [_P] * 6
         L.orc_matvec.argtypes = [_I, _I, _P, _P, _P]
         L.orc_rms_feedback.argtypes = [_I, _P, _P]
         L.orc_decoder_run.restype = _I
@@ -158,6 +159,25 @@ def self_append_attend(q, k_new, v_new, Ks, Vs, pos: int, scale: float,
     lib().orc_self_append_attend(S, H, D, max_pos, int(pos), float(scale),
                                  int(round_bf16), _ptr(q), _ptr(k_new),
                                  _ptr(v_new), _ptr(Ks), _ptr(Vs), _ptr(out))
+    return out
+
+
+def self_prefill_append(q, k_new, v_new, Ks, Vs, pos: int, scale: float,
+                        round_bf16: bool = False) -> np.ndarray:
+    """Write rows pos .. pos+n-1 of Ks, Vs [S][Hkv][max_pos][D] (float64,
+    updated in place) and attend causally. q [S][n][Hq][D], k_new and v_new
+    [S][n][Hkv][D]; Hq a multiple of Hkv (grouped heads). Returns [S][n][Hq][D]."""
+    q, k_new, v_new = _f64(q), _f64(k_new), _f64(v_new)
+    assert Ks.dtype == np.float64 and Ks.flags.c_contiguous
+    assert Vs.dtype == np.float64 and Vs.flags.c_contiguous
+    S, Hkv, max_pos, D = Ks.shape
+    n, Hq = q.shape[1], q.shape[2]
+    assert q.shape == (S, n, Hq, D) and k_new.shape == (S, n, Hkv, D) == v_new.shape
+    assert Hq % Hkv == 0 and 0 <= pos and pos + n <= max_pos
+    out = np.empty_like(q)
+    lib().orc_self_prefill_append(S, n, Hq, Hkv, D, max_pos, int(pos), float(scale),
+                                  int(round_bf16), _ptr(q), _ptr(k_new), _ptr(v_new),
+                                  _ptr(Ks), _ptr(Vs), _ptr(out))
     return out
 
 

@@ -225,6 +225,43 @@ void orc_self_append_attend(int S, int H, int D, int max_pos, int pos,
         }
 }
 
+/* Several new rows at once, with grouped key/value heads ([WK] section 3
+ * lists the MHA/GQA/MQA head sharing; the ContextPrefill of [WK] section 4
+ * starts the decoder from several prefix positions at once). Shapes:
+ *   q, out [S][n][Hq][D];  kn, vn [S][n][Hkv][D];  Ks, Vs [S][Hkv][max_pos][D].
+ * First rows pos .. pos+n-1 of every (sequence, kv head) are written (rounded
+ * to bf16 when asked); then query i of head h attends, causally, rows
+ * 0 .. pos+i of kv head h / (Hq / Hkv), the last n of them being the rows
+ * just written. */
+void orc_self_prefill_append(int S, int n, int Hq, int Hkv, int D, int max_pos, int pos,
+                             double scale, int round_bf16, const double* q,
+                             const double* kn, const double* vn, double* Ks,
+                             double* Vs, double* out)
+{
+    for (int s = 0; s < S; ++s)
+        for (int i = 0; i < n; ++i)
+            for (int hk = 0; hk < Hkv; ++hk) {
+                size_t row = (((size_t)s * Hkv + hk) * max_pos + pos + i) * D;
+                size_t io = (((size_t)s * n + i) * Hkv + hk) * D;
+                for (int d = 0; d < D; ++d) {
+                    double k = kn[io + d], v = vn[io + d];
+                    Ks[row + d] = round_bf16 ? orc_round_bf16(k) : k;
+                    Vs[row + d] = round_bf16 ? orc_round_bf16(v) : v;
+                }
+            }
+    const int G = Hq / Hkv;
+#pragma omp parallel for collapse(3) schedule(static)
+    for (int s = 0; s < S; ++s)
+        for (int i = 0; i < n; ++i)
+            for (int h = 0; h < Hq; ++h) {
+                size_t base = ((size_t)s * Hkv + h / G) * (size_t)max_pos * D;
+                size_t qi = (((size_t)s * n + i) * Hq + h) * D;
+                double* sc = (double*)malloc(sizeof(double) * (size_t)(pos + i + 1));
+                attend_one(pos + i + 1, D, scale, q + qi, Ks + base, Vs + base, out + qi, sc);
+                free(sc);
+            }
+}
+
 /* [WK] section 4: the ANE decoder updates its fixed-length cache with a
  * one-hot mask m (1 at the current position): cache*(1-m) + cur*m, applied to
  * every row. Exported so the scatter above can be checked against it. */

@@ -268,6 +268,69 @@ def test_self_append_bf16_stores_rounded_rows():
     np.testing.assert_array_equal(Ks[:, :, 3], want)
 
 
+# ------------------------------------- several new rows at once, grouped heads
+def _prefill_case(r, S, n, Hq, Hkv, P, D):
+    return (r.standard_normal((S, n, Hq, D)), r.standard_normal((S, n, Hkv, D)),
+            r.standard_normal((S, n, Hkv, D)), r.standard_normal((S, Hkv, P, D)))
+
+
+@pytest.mark.parametrize("S,n,Hq,Hkv,P,D,pos", [
+    (2, 3, 4, 4, 10, 8, 0),     # ContextPrefill-like: 3 prefix rows from an empty cache
+    (1, 5, 6, 2, 16, 8, 4),     # grouped heads, 3 queries per kv head
+    (2, 4, 4, 1, 9, 16, 5),     # one kv head (MQA), last row of the capacity
+])
+def test_prefill_equals_successive_single_row_calls(S, n, Hq, Hkv, P, D, pos):
+    """n rows written at once give, query by query, exactly what n single-row
+    appends give, with every query head reading its group's kv head (repeat_kv,
+    the MHA/GQA/MQA sharing of [WK] section 3). Bit for bit: both reduce to the
+    same attention over the same stored rows."""
+    r = rng(40)
+    q, kn, vn, old = _prefill_case(r, S, n, Hq, Hkv, P, D)
+    Ks, Vs = old.copy(), old.copy()
+    out = oracle.self_prefill_append(q, kn, vn, Ks, Vs, pos, 0.3)
+    G = Hq // Hkv
+    Kr = np.ascontiguousarray(np.repeat(old, G, axis=1))   # [S][Hq][P][D]
+    Vr = Kr.copy()
+    for i in range(n):
+        kr = np.ascontiguousarray(np.repeat(kn[:, i], G, axis=1))
+        vr = np.ascontiguousarray(np.repeat(vn[:, i], G, axis=1))
+        got = oracle.self_append_attend(q[:, i], kr, vr, Kr, Vr, pos + i, 0.3)
+        np.testing.assert_array_equal(out[:, i], got)
+    np.testing.assert_array_equal(Ks, Kr[:, ::G])
+    np.testing.assert_array_equal(Vs, Vr[:, ::G])
+
+
+def test_prefill_matches_causal_sdpa_and_never_reads_past_the_new_rows():
+    """Library routine: torch SDPA in float64 with a causal mask offset by pos
+    and the kv heads repeated per group. Rows past pos+n-1 are poisoned with
+    NaN and must neither change the output nor be written."""
+    r = rng(41)
+    S, n, Hq, Hkv, P, D, pos = 2, 6, 6, 3, 20, 16, 7
+    q, kn, vn, old = _prefill_case(r, S, n, Hq, Hkv, P, D)
+    old[:, :, pos + n:] = np.nan
+    Ks, Vs = old.copy(), old.copy()
+    out = oracle.self_prefill_append(q, kn, vn, Ks, Vs, pos, 0.125)
+    assert np.isnan(Ks[:, :, pos + n:]).all() and np.isnan(Vs[:, :, pos + n:]).all()
+    G = Hq // Hkv
+    K = torch.from_numpy(np.repeat(Ks[:, :, :pos + n], G, axis=1))   # [S][Hq][pos+n][D]
+    V = torch.from_numpy(np.repeat(Vs[:, :, :pos + n], G, axis=1))
+    Q = torch.from_numpy(q.transpose(0, 2, 1, 3).copy())               # [S][Hq][n][D]
+    mask = torch.arange(pos + n)[None, :] <= (pos + torch.arange(n))[:, None]
+    want = torch.nn.functional.scaled_dot_product_attention(Q, K, V, attn_mask=mask, scale=0.125)
+    np.testing.assert_allclose(out, want.numpy().transpose(0, 2, 1, 3), rtol=1e-12, atol=1e-14)
+
+
+def test_prefill_bf16_stores_rounded_rows():
+    r = rng(42)
+    S, n, Hq, Hkv, P, D = 1, 3, 2, 1, 8, 8
+    q, kn, vn, _ = _prefill_case(r, S, n, Hq, Hkv, P, D)
+    kn = kn.astype(np.float32).astype(np.float64)
+    Ks, Vs = np.zeros((S, Hkv, P, D)), np.zeros((S, Hkv, P, D))
+    oracle.self_prefill_append(q, kn, vn, Ks, Vs, 2, 0.5, round_bf16=True)
+    want = torch.from_numpy(kn.astype(np.float32)).to(torch.bfloat16).double().numpy()
+    np.testing.assert_array_equal(Ks[:, :, 2:5], want.transpose(0, 2, 1, 3))
+
+
 # ------------------------------------------- O4/O5 incremental == full window
 def _harness_weights(seed, L, dm, std=0.02):
     r = rng(seed)
