@@ -258,6 +258,56 @@ def measured_traffic(config):
     return {"bytes": read + write, "read": read, "write": write}
 
 
+def measure_prefill(torch, pc, g, stream):
+    """Time cke_selfattn_prefill_append at the workload's self-attention shape:
+    3 rows from an empty cache (a ContextPrefill start) and a 64-row chunk at
+    position 64. Each is one HIP graph of 16 identical calls (each call rewrites
+    the same rows), replayed and timed with events. Bytes per call are the
+    rows read once (0 .. pos+n-1 of K and V), the rows written and the fp32
+    q, k_new, v_new and out."""
+    if not g.n_seqs:
+        return None
+    dt = torch.bfloat16 if g.dtype == "bf16" else torch.float32
+    elem = 2 if g.dtype == "bf16" else 4
+    S, H, D = g.n_seqs, g.n_heads, g.head_dim
+    kv = pc.KVLayer(S, H, D, g.max_pos, dtype=dt)
+    kv.k.normal_(0, 0.45)
+    kv.v.normal_(0, 0.45)
+    res = []
+    for n, pos in ((3, 0), (64, 64)):
+        q = torch.randn(S, n, H, D, device="cuda") * 0.45
+        kn = torch.randn(S, n, H, D, device="cuda") * 0.45
+        vn = torch.randn(S, n, H, D, device="cuda") * 0.45
+        out = torch.empty_like(q)
+
+        def calls():
+            for _ in range(16):
+                pc.cke_selfattn_prefill_append(q, kn, vn, kv, pos, n, H, g.scale, out,
+                                               stream=torch.cuda.current_stream())
+        with torch.cuda.stream(stream):
+            calls()
+        stream.synchronize()
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr, stream=stream):
+            calls()
+        torch.cuda.synchronize()
+        best = float("inf")
+        for _ in range(3):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            with torch.cuda.stream(stream):
+                gr.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            best = min(best, e0.elapsed_time(e1) * 1e-3 / 16)
+        nbytes = S * H * D * (2 * (pos + n) * elem + 2 * n * elem + 4 * n * 4)
+        res.append({"n_new": n, "pos": pos, "seqs": S, "heads": H, "kv_heads": H,
+                    "avg_us": best * 1e6, "bytes_per_call": nbytes, "GB_s": nbytes / best / 1e9})
+        del gr
+    return res
+
+
 def _host_cpu():
     try:
         for line in open("/proc/cpuinfo"):
@@ -421,6 +471,9 @@ def main():
         "gpu": torch.cuda.get_device_name(0),
         "git": _git_sha(),
     }
+    prefill = measure_prefill(torch, pc, g, stream)
+    if prefill:
+        result["selfattn_prefill"] = prefill
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args.config, args.cpu_seconds)
     print(json.dumps(result))

@@ -157,6 +157,26 @@ int cke_selfattn_decode_append(const float* q, const float* k_new,
                                const float* v_new, const cke_kv_layer* kv,
                                int pos, float scale, float* out, void* stream);
 
+/* Several new tokens per sequence at once, with grouped key/value heads:
+ * rows pos .. pos+n_new-1 of every (sequence, kv head) are written from
+ * k_new, v_new (rounded to bf16 if dtype is), then query i of head h attends
+ * causally over rows 0 .. pos+i of kv head h / (n_q_heads / kv->n_heads):
+ *   out[s][i][h][:] = sum_{t<=pos+i} softmax_t(scale * q[s][i][h].K[s][g][t]) V[s][g][t]
+ * reading the stored (rounded) values. Rows >= pos+n_new are never read or
+ * written. With n_new = 1 and n_q_heads = kv->n_heads this is
+ * cke_selfattn_decode_append with [S][1][H][D] tensors.
+ *   WhisperKit case study, section 4: the decoder's ContextPrefill starts at a
+ *   cache already holding several prefix positions (several rows written at
+ *   once); section 3: heads may share key/value heads (MHA, GQA, MQA).
+ *   q, out        device fp32 [S][n_new][n_q_heads][D] (out must not alias q)
+ *   k_new, v_new  device fp32 [S][n_new][kv->n_heads][D]
+ *   n_q_heads     a positive multiple of kv->n_heads, at most 65535
+ *   n_new >= 1, pos >= 0 and pos + n_new <= max_pos, else CKE_ERANGE */
+int cke_selfattn_prefill_append(const float* q, const float* k_new,
+                                const float* v_new, const cke_kv_layer* kv,
+                                int pos, int n_new, int n_q_heads, float scale,
+                                float* out, void* stream);
+
 /* Message for the last non-OK status returned on this thread. */
 const char* cke_last_error(void);
 

@@ -75,12 +75,15 @@ _lib.cke_xattn_decode.argtypes = [_P, _I, _P, _I, _F, _P, _P]
 _lib.cke_selfattn_decode_append.restype = _I
 _lib.cke_selfattn_decode_append.argtypes = [_P, _P, _P, ctypes.POINTER(cke_kv_layer), _I, _F,
                                             _P, _P]
+_lib.cke_selfattn_prefill_append.restype = _I
+_lib.cke_selfattn_prefill_append.argtypes = [_P, _P, _P, ctypes.POINTER(cke_kv_layer), _I, _I, _I,
+                                             _F, _P, _P]
 
 EXPORTED = ["cke_xattn_region_bytes", "cke_xattn_layer_offset_bytes",
             "cke_xattn_workspace_bytes", "cke_xattn_num_splits", "cke_xattn_cache_create",
             "cke_xattn_cache_destroy", "cke_xattn_invalidate", "cke_xattn_is_ready",
             "cke_xattn_populate", "cke_xattn_decode", "cke_selfattn_decode_append",
-            "cke_last_error", "cke_version"]
+            "cke_selfattn_prefill_append", "cke_last_error", "cke_version"]
 
 
 class CkeError(RuntimeError):
@@ -195,6 +198,16 @@ def cke_xattn_decode(q, cache, layer: int, scale: float, out, n_q=None, stream=N
                                  _ptr(out), _stream(stream)))
 
 
+def cke_selfattn_prefill_append(q, k_new, v_new, kv, pos: int, n_new: int, n_q_heads: int,
+                                scale: float, out, stream=None) -> None:
+    """Write rows pos..pos+n_new-1 of kv from k_new/v_new [S][n_new][Hkv][D] and
+    attend causally for q [S][n_new][n_q_heads][D] (grouped kv heads)."""
+    desc = kv.desc if isinstance(kv, KVLayer) else kv
+    _check(_lib.cke_selfattn_prefill_append(_ptr(q), _ptr(k_new), _ptr(v_new), ctypes.byref(desc),
+                                            int(pos), int(n_new), int(n_q_heads), float(scale),
+                                            _ptr(out), _stream(stream)))
+
+
 def cke_selfattn_decode_append(q, k_new, v_new, kv, pos: int, scale: float, out,
                                stream=None) -> None:
     """Scatter k_new/v_new [S][H][D] into row pos of kv and attend over rows
@@ -268,4 +281,12 @@ class KVLayer:
         if out is None:
             out = torch.empty_like(q)
         cke_selfattn_decode_append(q, k_new, v_new, self, pos, scale, out, stream)
+        return out
+
+    def prefill_attend(self, q, k_new, v_new, pos, scale, out=None, stream=None):
+        """q [S][n][Hq][D], k_new/v_new [S][n][H][D]; Hq a multiple of H."""
+        if out is None:
+            out = torch.empty_like(q)
+        cke_selfattn_prefill_append(q, k_new, v_new, self, pos, q.shape[1], q.shape[2], scale, out,
+                                    stream)
         return out

@@ -258,6 +258,78 @@ __global__ __launch_bounds__(NW * 64) void selfattn_append_kernel(
     }
 }
 
+// --------------------------------------------------------- self prefill
+// Grid: (Hkv, S). One workgroup per (sequence, kv head) writes that kv head's
+// rows pos .. pos+n_new-1 (rounded to the storage type), passes a workgroup
+// barrier -- whose workgroup-scope release/acquire makes those stores visible
+// to its own waves -- and then its waves take groups of up to QB consecutive
+// tokens of one query head of the kv head's group (group j: head
+// h = kv*G + j % G, tokens QB*(j / G) ..), reading rows 0 .. pos+i once per
+// group with each token i masked to its own causal limit pos+i+1. Rows past
+// pos+n_new-1 are neither read nor written, and no workgroup touches another
+// one's rows.
+template <int D, typename TE, int NW, int NP, int QB>
+__global__ __launch_bounds__(NW * 64) void selfattn_prefill_kernel(
+    const float* __restrict__ q, const float* __restrict__ k_new,
+    const float* __restrict__ v_new, TE* __restrict__ Kc, TE* __restrict__ Vc,
+    float* __restrict__ out, int Hkv, int Hq, int max_pos, int pos, int n_new, float sl2)
+{
+    using RM = RowMap<D, TE>;
+    constexpr int VEC = RM::kVec, LPK = RM::kLPK;
+    const int hk = blockIdx.x, s = blockIdx.y;
+    const size_t skv = (size_t)s * Hkv + hk;
+    TE* K = Kc + skv * (size_t)max_pos * D;
+    TE* V = Vc + skv * (size_t)max_pos * D;
+    const int G = Hq / Hkv;
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+    const int sub = lane % LPK;
+
+    for (int x = threadIdx.x; x < n_new * D; x += NW * 64) {
+        const int i = x / D, d = x % D;
+        const size_t src = (((size_t)s * n_new + i) * Hkv + hk) * D + d;
+        const size_t dst = (size_t)(pos + i) * D + d;
+        if constexpr (sizeof(TE) == 2) {
+            K[dst] = to_bf16_bits(k_new[src]);
+            V[dst] = to_bf16_bits(v_new[src]);
+        } else {
+            K[dst] = k_new[src];
+            V[dst] = v_new[src];
+        }
+    }
+    __syncthreads();
+
+    const int blocks = (n_new + QB - 1) / QB;
+    for (int j = w; j < blocks * G; j += NW) {
+        const int h = hk * G + j % G, i0 = QB * (j / G);
+        const int nq = min(QB, n_new - i0);
+        float qr[QB][VEC];
+        int lim[QB];
+#pragma unroll
+        for (int k = 0; k < QB; ++k) {
+            const int i = min(i0 + k, n_new - 1);
+            lim[k] = pos + i + 1;
+            const size_t qo = (((size_t)s * n_new + i) * Hq + h) * D;
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) qr[k][e] = q[qo + sub * VEC + e];
+        }
+        WaveState<QB, VEC> st;
+        st.init();
+        wave_attend_causal<D, TE, QB, NP>(K, V, lim, qr, nq, sl2, st);
+        wave_merge_groups<D, TE, QB>(st, nq);
+        if (lane < LPK) {
+#pragma unroll
+            for (int k = 0; k < QB; ++k) {
+                if (k < nq) {
+                    const size_t qo = (((size_t)s * n_new + i0 + k) * Hq + h) * D;
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e) out[qo + sub * VEC + e] = st.acc[k][e] / st.l[k];
+                }
+            }
+        }
+    }
+}
+
 // ------------------------------------------------------------- launchers
 namespace {
 
@@ -373,6 +445,49 @@ hipError_t launch_self_t(const SelfLaunch& a, hipStream_t st) {
     return hipErrorInvalidValue;
 }
 
+constexpr int kPrefillQB = 8;   // tokens of one head sharing a wave's row reads
+constexpr int kPrefillNP = 2;
+
+template <int D, typename TE, int NW, int QB>
+hipError_t launch_prefill_nw(const PrefillLaunch& a, hipStream_t st) {
+    hipLaunchKernelGGL((selfattn_prefill_kernel<D, TE, NW, QB == 1 ? kSelfNP : kPrefillNP, QB>),
+                       dim3(a.Hkv, a.S), dim3(NW * 64), 0,
+                       st, a.q, a.k_new, a.v_new, static_cast<TE*>(a.K), static_cast<TE*>(a.V), a.out,
+                       a.Hkv, a.Hq, a.max_pos, a.pos, a.n_new, a.scale * kLog2e);
+    return hipGetLastError();
+}
+
+// A kv head with at most 8 queries gives each query a wave of its own
+// (short, latency-bound calls such as a few prefix rows); with more, each
+// wave takes kPrefillQB tokens of one head and reads their rows once. Up to
+// 8 waves per workgroup.
+template <int D, typename TE>
+hipError_t launch_prefill_d(const PrefillLaunch& a, hipStream_t st) {
+    const long long G = a.Hq / a.Hkv;
+    if ((long long)a.n_new * G <= 8) {
+        const long long queries = (long long)a.n_new * G;
+        if (queries <= 1) return launch_prefill_nw<D, TE, 1, 1>(a, st);
+        if (queries <= 2) return launch_prefill_nw<D, TE, 2, 1>(a, st);
+        if (queries <= 4) return launch_prefill_nw<D, TE, 4, 1>(a, st);
+        return launch_prefill_nw<D, TE, 8, 1>(a, st);
+    }
+    const long long groups = (long long)((a.n_new + kPrefillQB - 1) / kPrefillQB) * G;
+    if (groups <= 1) return launch_prefill_nw<D, TE, 1, kPrefillQB>(a, st);
+    if (groups <= 2) return launch_prefill_nw<D, TE, 2, kPrefillQB>(a, st);
+    if (groups <= 4) return launch_prefill_nw<D, TE, 4, kPrefillQB>(a, st);
+    return launch_prefill_nw<D, TE, 8, kPrefillQB>(a, st);
+}
+
+template <typename TE>
+hipError_t launch_prefill_t(const PrefillLaunch& a, hipStream_t st) {
+    switch (a.D) {
+        case 32: return launch_prefill_d<32, TE>(a, st);
+        case 64: return launch_prefill_d<64, TE>(a, st);
+        case 128: return launch_prefill_d<128, TE>(a, st);
+    }
+    return hipErrorInvalidValue;
+}
+
 }  // namespace
 
 int cross_keys_per_pass(int D, int elem_bytes) {
@@ -386,6 +501,10 @@ hipError_t launch_xattn_decode(const XattnLaunch& a, hipStream_t st) {
 
 hipError_t launch_selfattn_append(const SelfLaunch& a, hipStream_t st) {
     return a.bf16 ? launch_self_t<uint16_t>(a, st) : launch_self_t<float>(a, st);
+}
+
+hipError_t launch_selfattn_prefill(const PrefillLaunch& a, hipStream_t st) {
+    return a.bf16 ? launch_prefill_t<uint16_t>(a, st) : launch_prefill_t<float>(a, st);
 }
 
 }  // namespace cke

@@ -267,9 +267,13 @@ int cke_xattn_decode(const float* q, int n_q, const cke_xattn_cache* c, int laye
     return CKE_OK;
 }
 
-int cke_selfattn_decode_append(const float* q, const float* k_new, const float* v_new,
-                               const cke_kv_layer* kv, int pos, float scale, float* out,
-                               void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Checks shared by the self-attention calls, in the order they report.
+int check_self_args(const float* q, const float* k_new, const float* v_new,
+                    const cke_kv_layer* kv, const float* out, float scale) {
     if (!kv) return fail(CKE_EINVAL, "kv layer descriptor is NULL");
     if (!q || !k_new || !v_new || !out || !kv->k || !kv->v)
         return fail(CKE_EINVAL, "q, k_new, v_new, out, kv->k and kv->v must be non-NULL");
@@ -279,12 +283,24 @@ int cke_selfattn_decode_append(const float* q, const float* k_new, const float* 
     if (!head_dim_ok(kv->head_dim))
         return fail(CKE_EINVAL, "head_dim must be 32, 64 or 128 (got %d)", kv->head_dim);
     if (!dtype_ok(kv->dtype)) return fail(CKE_EINVAL, "unknown kv dtype %d", kv->dtype);
-    if (pos < 0 || pos >= kv->max_pos)
-        return fail(CKE_ERANGE, "pos %d outside [0, %d)", pos, kv->max_pos);
     if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(out) ||
         !aligned16(kv->k) || !aligned16(kv->v))
         return fail(CKE_EINVAL, "all tensors must be 16-byte aligned");
     if (!(scale == scale)) return fail(CKE_EINVAL, "scale is NaN");
+    return CKE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int cke_selfattn_decode_append(const float* q, const float* k_new, const float* v_new,
+                               const cke_kv_layer* kv, int pos, float scale, float* out,
+                               void* stream) {
+    const int rc = check_self_args(q, k_new, v_new, kv, out, scale);
+    if (rc != CKE_OK) return rc;
+    if (pos < 0 || pos >= kv->max_pos)
+        return fail(CKE_ERANGE, "pos %d outside [0, %d)", pos, kv->max_pos);
     cke::SelfLaunch a;
     a.q = q;
     a.k_new = k_new;
@@ -301,6 +317,38 @@ int cke_selfattn_decode_append(const float* q, const float* k_new, const float* 
     a.bf16 = kv->dtype == CKE_BF16;
     hipError_t e = cke::launch_selfattn_append(a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(CKE_EDEVICE, "self-attention launch failed: %s", hipGetErrorString(e));
+    return CKE_OK;
+}
+
+int cke_selfattn_prefill_append(const float* q, const float* k_new, const float* v_new,
+                                const cke_kv_layer* kv, int pos, int n_new, int n_q_heads,
+                                float scale, float* out, void* stream) {
+    const int rc = check_self_args(q, k_new, v_new, kv, out, scale);
+    if (rc != CKE_OK) return rc;
+    if (n_q_heads < 1 || n_q_heads > 65535 || n_q_heads % kv->n_heads != 0)
+        return fail(CKE_EINVAL, "n_q_heads %d must be a positive multiple of kv->n_heads %d (at most 65535)",
+                    n_q_heads, kv->n_heads);
+    if (n_new < 1 || pos < 0 || (long long)pos + n_new > kv->max_pos)
+        return fail(CKE_ERANGE, "rows [%d, %lld) outside [0, %d) or n_new < 1", pos,
+                    (long long)pos + n_new, kv->max_pos);
+    cke::PrefillLaunch a;
+    a.q = q;
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.K = kv->k;
+    a.V = kv->v;
+    a.out = out;
+    a.S = kv->n_seqs;
+    a.Hkv = kv->n_heads;
+    a.Hq = n_q_heads;
+    a.D = kv->head_dim;
+    a.max_pos = kv->max_pos;
+    a.pos = pos;
+    a.n_new = n_new;
+    a.scale = scale;
+    a.bf16 = kv->dtype == CKE_BF16;
+    hipError_t e = cke::launch_selfattn_prefill(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(CKE_EDEVICE, "self-attention prefill launch failed: %s", hipGetErrorString(e));
     return CKE_OK;
 }
 

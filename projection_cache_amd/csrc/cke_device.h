@@ -265,6 +265,85 @@ __device__ __forceinline__ void wave_attend(
     }
 }
 
+// compute_tile for causal groups of queries: query i only sees rows below
+// lim[i] (its own causal limit); rows at or past it score -inf for that
+// query. Every row of the tile was loaded from [0, max lim) (the caller
+// clamps loads there), so a masked row's V share is finite and its weight 0.
+template <int D, typename TE, int NQ, int NP>
+__device__ __forceinline__ void compute_tile_causal(int base, const int (&lim)[NQ], int grp,
+                                                    const float (&q)[NQ][RowMap<D, TE>::kVec],
+                                                    int nq, float sl2, const uint4 (&kb)[NP],
+                                                    const uint4 (&vb)[NP],
+                                                    WaveState<NQ, RowMap<D, TE>::kVec>& st)
+{
+    using RM = RowMap<D, TE>;
+    constexpr int VEC = RM::kVec, LPK = RM::kLPK, KPW = RM::kKPW;
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) {
+        if (i < nq) {
+            float s[NP];
+            float mt = -INFINITY;
+#pragma unroll
+            for (int p = 0; p < NP; ++p) {
+                const int row = base + p * KPW + grp;
+                float d = 0.f;
+#pragma unroll
+                for (int j = 0; j < VEC; ++j) d = fmaf(q[i][j], elem<TE>(kb[p], j), d);
+                d = group_sum<LPK>(d);
+                s[p] = row < lim[i] ? d * sl2 : -INFINITY;
+                mt = fmaxf(mt, s[p]);
+            }
+            const float mn = fmaxf(st.m[i], mt);
+            const float alpha = mn == -INFINITY ? 1.f : fast_exp2(st.m[i] - mn);
+            st.l[i] *= alpha;
+#pragma unroll
+            for (int j = 0; j < VEC; ++j) st.acc[i][j] *= alpha;
+#pragma unroll
+            for (int p = 0; p < NP; ++p) {
+                const float e = s[p] == -INFINITY ? 0.f : fast_exp2(s[p] - mn);
+                st.l[i] += e;
+#pragma unroll
+                for (int j = 0; j < VEC; ++j) st.acc[i][j] = fmaf(e, elem<TE>(vb[p], j), st.acc[i][j]);
+            }
+            st.m[i] = mn;
+        }
+    }
+}
+
+// One wave attends a causal group of queries over rows [0, max lim): the rows
+// are read once for the whole group (register double buffering as in
+// wave_attend); query i sees rows below lim[i]. lim is non-decreasing and
+// lim[nq-1] is the largest.
+template <int D, typename TE, int NQ, int NP>
+__device__ __forceinline__ void wave_attend_causal(
+    const TE* __restrict__ K, const TE* __restrict__ V, const int (&lim)[NQ],
+    const float (&q)[NQ][RowMap<D, TE>::kVec], int nq, float sl2,
+    WaveState<NQ, RowMap<D, TE>::kVec>& st)
+{
+    using RM = RowMap<D, TE>;
+    constexpr int LPK = RM::kLPK, KPW = RM::kKPW;
+    constexpr int TILE = NP * KPW;
+    const int lane = threadIdx.x & 63;
+    const int grp = lane / LPK;
+    const int sub = lane % LPK;
+    int r1 = lim[0];
+#pragma unroll
+    for (int i = 1; i < NQ; ++i)
+        if (i < nq) r1 = max(r1, lim[i]);
+    if (r1 <= 0) return;
+    const int r_safe = r1 - 1;
+    uint4 ka[NP], va[NP], kb2[NP], vb2[NP];
+    load_tile<D, TE, NP>(K, V, 0, r_safe, grp, sub, ka, va);
+    for (int base = 0; base < r1; base += 2 * TILE) {
+        const bool more = base + TILE < r1;
+        if (more) load_tile<D, TE, NP>(K, V, base + TILE, r_safe, grp, sub, kb2, vb2);
+        compute_tile_causal<D, TE, NQ, NP>(base, lim, grp, q, nq, sl2, ka, va, st);
+        if (!more) break;
+        if (base + 2 * TILE < r1) load_tile<D, TE, NP>(K, V, base + 2 * TILE, r_safe, grp, sub, ka, va);
+        compute_tile_causal<D, TE, NQ, NP>(base + TILE, lim, grp, q, nq, sl2, kb2, vb2, st);
+    }
+}
+
 // Merge the row groups of one wave: afterwards every lane holds the wave's
 // (max, sum) per query and the wave's unnormalised output for its own dims.
 template <int D, typename TE, int NQ>

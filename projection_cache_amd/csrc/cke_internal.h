@@ -34,6 +34,18 @@ struct SelfLaunch {
     bool bf16;
 };
 
+struct PrefillLaunch {
+    const float* q;      // [S][n_new][Hq][D]
+    const float* k_new;  // [S][n_new][Hkv][D]
+    const float* v_new;
+    void* K;             // [S][Hkv][max_pos][D]
+    void* V;
+    float* out;          // [S][n_new][Hq][D]
+    int S, Hkv, Hq, D, max_pos, pos, n_new;
+    float scale;
+    bool bf16;
+};
+
 // Pointer table of the 2*L weight matrices: entries [0, L) are WK_0..WK_{L-1},
 // entries [L, 2L) are WV_0..WV_{L-1}. Passed by value as a kernel argument.
 struct WeightTable {
@@ -61,6 +73,7 @@ int cross_keys_per_pass(int D, int elem_bytes);
 hipError_t launch_xattn_decode(const XattnLaunch& a, hipStream_t st);
 
 hipError_t launch_selfattn_append(const SelfLaunch& a, hipStream_t st);
+hipError_t launch_selfattn_prefill(const PrefillLaunch& a, hipStream_t st);
 hipError_t launch_populate(const PopulateLaunch& a, hipStream_t st);
 
 }  // namespace cke

@@ -26,7 +26,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) >= 13
+    assert len(names) >= 14
     lib = ctypes.CDLL(pc.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -153,3 +153,24 @@ def test_selfattn_rejects_bad_arguments_before_launch():
     assert call(k=None) == pc.CKE_EINVAL
     assert call(n_seqs=0) == pc.CKE_EINVAL
     assert L.cke_selfattn_decode_append(FAKE, FAKE, FAKE, None, 0, 0.125, FAKE, None) == pc.CKE_EINVAL
+
+
+def test_prefill_rejects_bad_arguments_before_launch():
+    L = pc.lib()
+
+    def call(pos=0, n_new=3, n_q_heads=8, **kw):
+        d = dict(k=FAKE, v=FAKE, n_seqs=1, n_heads=8, head_dim=64, max_pos=448, dtype=0)
+        d.update(kw)
+        desc = pc.cke_kv_layer(**d)
+        return L.cke_selfattn_prefill_append(FAKE, FAKE, FAKE, ctypes.byref(desc), pos, n_new,
+                                             n_q_heads, 0.125, FAKE, None)
+
+    assert call(pos=446) == pc.CKE_ERANGE            # rows 446..448 run past max_pos
+    assert call(pos=-1) == pc.CKE_ERANGE
+    assert call(n_new=0) == pc.CKE_ERANGE
+    assert call(n_q_heads=12) == pc.CKE_EINVAL       # not a multiple of the 8 kv heads
+    assert call(n_q_heads=0) == pc.CKE_EINVAL
+    assert call(head_dim=48) == pc.CKE_EINVAL
+    assert call(k=None) == pc.CKE_EINVAL
+    assert "n_q_heads" in (call(n_q_heads=4) and pc.cke_last_error())
+    assert L.cke_selfattn_prefill_append(FAKE, FAKE, FAKE, None, 0, 1, 8, 0.125, FAKE, None) == pc.CKE_EINVAL

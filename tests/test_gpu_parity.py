@@ -270,6 +270,50 @@ def test_self_append_attend_matches_oracle(c):
     np.testing.assert_array_equal(to_np(kv.v), Vs)
 
 
+PREFILL_CASES = [
+    dict(S=1, n=3, Hq=8, Hkv=8, D=64, P=448, pos=0, dtype="f32"),     # Whisper Base ContextPrefill
+    dict(S=2, n=5, Hq=6, Hkv=2, D=64, P=40, pos=7, dtype="bf16"),     # grouped kv heads
+    dict(S=3, n=16, Hq=4, Hkv=1, D=128, P=64, pos=20, dtype="f32"),   # one kv head, D 128
+    dict(S=2, n=1, Hq=8, Hkv=2, D=32, P=16, pos=15, dtype="f32"),     # one row, last position
+    dict(S=4, n=33, Hq=20, Hkv=20, D=64, P=448, pos=100, dtype="bf16"),  # Large heads, 33-row chunk
+    dict(S=1, n=448, Hq=8, Hkv=8, D=64, P=448, pos=0, dtype="f32"),   # the whole capacity at once
+    dict(S=2, n=2, Hq=8, Hkv=2, D=128, P=24, pos=9, dtype="bf16"),    # 8 queries per kv head
+    dict(S=1, n=12, Hq=2, Hkv=1, D=32, P=30, pos=3, dtype="bf16"),    # ragged last token group
+]
+
+
+@pytest.mark.parametrize("c", PREFILL_CASES,
+                         ids=lambda c: "S%d-n%d-Hq%d-Hkv%d-D%d-P%d-pos%d-%s" % tuple(c.values()))
+def test_prefill_matches_oracle(c):
+    """Several rows per sequence at once, grouped kv heads: output within the
+    cache dtype's tolerance of the oracle, stored rows bit-exact, and the rows
+    past the new ones (poisoned with NaN) neither read nor written."""
+    S, n, Hq, Hkv, D, P, pos = (c[k] for k in ("S", "n", "Hq", "Hkv", "D", "P", "pos"))
+    bf = c["dtype"] == "bf16"
+    dt = torch.bfloat16 if bf else torch.float32
+    r = np.random.default_rng([43, S, n, Hq, Hkv, D, P, pos])
+    q = (r.standard_normal((S, n, Hq, D)) * 0.45).astype(np.float32)
+    kn = (r.standard_normal((S, n, Hkv, D)) * 0.45).astype(np.float32)
+    vn = (r.standard_normal((S, n, Hkv, D)) * 0.45).astype(np.float32)
+    old = (r.standard_normal((S, Hkv, P, D)) * 0.45).astype(np.float32)
+    old[:, :, pos + n:] = np.nan
+    kv = pc.KVLayer(S, Hkv, D, P, dtype=dt)
+    kv.k.copy_(torch.from_numpy(old).to(dt))
+    kv.v.copy_(torch.from_numpy(-old).to(dt))
+    Ks = kv.k.double().cpu().numpy().copy()
+    Vs = kv.v.double().cpu().numpy().copy()
+    scale = 1.0 / math.sqrt(D)
+    out = kv.prefill_attend(t32(q), t32(kn), t32(vn), pos, scale)
+    torch.cuda.synchronize()
+    want = oracle.self_prefill_append(q, kn, vn, Ks, Vs, pos, scale, round_bf16=bf)
+    assert max_abs(to_np(out), want) <= TOL[c["dtype"]]
+    got_k = kv.k.double().cpu().numpy()
+    got_v = kv.v.double().cpu().numpy()
+    np.testing.assert_array_equal(got_k[:, :, :pos + n], Ks[:, :, :pos + n])
+    np.testing.assert_array_equal(got_v[:, :, :pos + n], Vs[:, :, :pos + n])
+    assert np.isnan(got_k[:, :, pos + n:]).all() and np.isnan(got_v[:, :, pos + n:]).all()
+
+
 def test_self_rows_past_pos_are_never_read_or_written():
     """Poison every row past pos with NaN: the output equals the clean run bit
     for bit and the poisoned rows are untouched."""
