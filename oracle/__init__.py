@@ -63,6 +63,7 @@ def lib():
         L.orc_self_append_attend.argtypes = [_I] * 5 + [_D, _I] + [_P] * 6
         L.orc_kv_blend_update.argtypes = [_I] * 5 + [_P, _P]
         L.orc_self_prefill_append.argtypes = [_I] * 7 + [_D, _I] + [_P] * 6
+        L.orc_cross_decode_weights.argtypes = [_I] * 5 + [_D, _P, _P, _P, _P, _I, _P, _P]
         L.orc_matvec.argtypes = [_I, _I, _P, _P, _P]
         L.orc_rms_feedback.argtypes = [_I, _P, _P]
         L.orc_decoder_run.restype = _I
@@ -145,6 +146,22 @@ def cross_decode(q, Kc_l, Vc_l, scale: float) -> np.ndarray:
     lib().orc_cross_decode(B, nq, H, T, D, float(scale), _ptr(q), _ptr(Kc_l),
                            _ptr(Vc_l), _ptr(out))
     return out
+
+
+def cross_decode_weights(q, Kc_l, Vc_l, scale: float, heads):
+    """cross_decode plus the softmax weights of the heads listed in ``heads``,
+    averaged over them: returns (out [B][nq][H][D], weights [B][nq][T])."""
+    q, Kc_l, Vc_l = _f64(q), _f64(Kc_l), _f64(Vc_l)
+    B, nq, H, D = q.shape
+    T = Kc_l.shape[2]
+    hs = np.ascontiguousarray(np.asarray(heads, dtype=np.int32))
+    assert hs.ndim == 1 and len(hs) >= 1 and (hs >= 0).all() and (hs < H).all()
+    out = np.empty_like(q)
+    w = np.empty((B, nq, T), dtype=np.float64)
+    lib().orc_cross_decode_weights(B, nq, H, T, D, float(scale), _ptr(q), _ptr(Kc_l),
+                                   _ptr(Vc_l), hs.ctypes.data_as(ctypes.c_void_p), len(hs),
+                                   _ptr(out), _ptr(w))
+    return out, w
 
 
 def self_append_attend(q, k_new, v_new, Ks, Vs, pos: int, scale: float,

@@ -194,6 +194,48 @@ void orc_cross_decode(int B, int nq, int H, int T, int D, double scale,
             }
 }
 
+/* Cross-attention weights of selected heads, averaged over them ([WK]
+ * section 8: the decoder's alignment heads expose their attention weights,
+ * which are averaged over those heads for word timing). For every stream b
+ * and query i:
+ *   p[h][t] = exp(scale q.K_t - max) / sum_u exp(scale q.K_u - max)   (head h)
+ *   weights[b][i][t] = (1 / n_sel) * sum_k p[heads[k]][t]
+ * in ascending k. Also returns the attention output of every head, as
+ * orc_cross_decode does. */
+void orc_cross_decode_weights(int B, int nq, int H, int T, int D, double scale,
+                              const double* q, const double* Kc, const double* Vc,
+                              const int* heads, int n_sel, double* out, double* weights)
+{
+    orc_cross_decode(B, nq, H, T, D, scale, q, Kc, Vc, out);
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int b = 0; b < B; ++b)
+        for (int i = 0; i < nq; ++i) {
+            double* w = weights + ((size_t)b * nq + i) * T;
+            double* s = (double*)malloc(sizeof(double) * (size_t)T);
+            for (int t = 0; t < T; ++t) w[t] = 0.0;
+            for (int k = 0; k < n_sel; ++k) {
+                const int h = heads[k];
+                const double* qv = q + (((size_t)b * nq + i) * H + h) * D;
+                const double* K = Kc + (((size_t)b * H + h) * T) * D;
+                double m = -INFINITY;
+                for (int t = 0; t < T; ++t) {
+                    double dot = 0.0;
+                    for (int d = 0; d < D; ++d) dot += qv[d] * K[(size_t)t * D + d];
+                    s[t] = dot * scale;
+                    if (s[t] > m) m = s[t];
+                }
+                double Z = 0.0;
+                for (int t = 0; t < T; ++t) {
+                    s[t] = exp(s[t] - m);
+                    Z += s[t];
+                }
+                for (int t = 0; t < T; ++t) w[t] += s[t] / Z;
+            }
+            for (int t = 0; t < T; ++t) w[t] /= n_sel;
+            free(s);
+        }
+}
+
 /* ---------------------------------------------- O3: self-attention decode
  * [TOP] "What it opened": the cache is an ordinary input and output; the new
  * row is written with scatter, then the token attends over the cache.

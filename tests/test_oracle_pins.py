@@ -268,6 +268,56 @@ def test_self_append_bf16_stores_rounded_rows():
     np.testing.assert_array_equal(Ks[:, :, 3], want)
 
 
+# --------------------------------------- attention weights of selected heads
+def _weights_case(r, B=2, nq=3, H=4, T=37, D=8):
+    return (r.standard_normal((B, nq, H, D)), r.standard_normal((B, H, T, D)),
+            r.standard_normal((B, H, T, D)))
+
+
+def test_weights_match_torch_softmax_and_are_consistent_with_the_output():
+    """Library routine: torch softmax of scale*q.K^T in float64, averaged over
+    the selected heads. Consistency: for one selected head the weights applied
+    to V give that head's attention output from cross_decode. Each weight row
+    sums to 1."""
+    r = rng(50)
+    q, K, V = _weights_case(r)
+    heads = [3, 0, 2]
+    out, w = oracle.cross_decode_weights(q, K, V, 0.35, heads)
+    np.testing.assert_array_equal(out, oracle.cross_decode(q, K, V, 0.35))
+    sc = torch.einsum("bihd,bhtd->biht", torch.from_numpy(q), torch.from_numpy(K)) * 0.35
+    p = torch.softmax(sc, dim=-1)[:, :, heads].mean(dim=2).numpy()
+    np.testing.assert_allclose(w, p, rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(w.sum(axis=-1), 1.0, rtol=1e-12)
+    _, w1 = oracle.cross_decode_weights(q, K, V, 0.35, [2])
+    np.testing.assert_allclose(np.einsum("bit,btd->bid", w1, V[:, 2]), out[:, :, 2],
+                               rtol=1e-12, atol=1e-14)
+
+
+def test_weights_closed_forms_and_invariances():
+    """Identical keys give uniform weights 1/T; one key far ahead of the rest
+    takes all the weight; adding one vector to every key of a head (a key bias,
+    [WK] section 2) leaves the weights unchanged; a selection is the mean of
+    its single-head selections."""
+    r = rng(51)
+    q, K, V = _weights_case(r, B=1, nq=2, H=3, T=11, D=4)
+    Ku = np.repeat(K[:, :, :1], 11, axis=2)
+    _, wu = oracle.cross_decode_weights(q, Ku, V, 1.0, [0, 1, 2])
+    np.testing.assert_allclose(wu, 1.0 / 11, rtol=1e-14)
+    Kd = K.copy()
+    Kd[:, 1, 7] = q[0, 0, 1] * 1e3          # q.k_7 huge for query 0 of head 1
+    _, wd = oracle.cross_decode_weights(q, Kd, V, 1.0, [1])
+    assert abs(wd[0, 0, 7] - 1.0) < 1e-12
+    bias = r.standard_normal(4)
+    Kb = K + bias
+    _, w0 = oracle.cross_decode_weights(q, K, V, 0.5, [0, 2])
+    _, wb = oracle.cross_decode_weights(q, Kb, V, 0.5, [0, 2])
+    # a key bias shifts every score of a query by the same q.b
+    np.testing.assert_allclose(wb, w0, rtol=1e-10, atol=1e-14)
+    _, wa = oracle.cross_decode_weights(q, K, V, 0.5, [0])
+    _, wc = oracle.cross_decode_weights(q, K, V, 0.5, [2])
+    np.testing.assert_allclose(w0, (wa + wc) / 2, rtol=1e-13, atol=1e-16)
+
+
 # ------------------------------------- several new rows at once, grouped heads
 def _prefill_case(r, S, n, Hq, Hkv, P, D):
     return (r.standard_normal((S, n, Hq, D)), r.standard_normal((S, n, Hkv, D)),
