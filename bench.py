@@ -308,6 +308,45 @@ def measure_prefill(torch, pc, g, stream):
     return res
 
 
+def measure_weights(torch, pc, w, stream):
+    """Time cke_xattn_decode_weights against cke_xattn_decode on the workload's
+    cache: one HIP graph per call kind holding one call per layer (the same
+    queries), with every other head selected."""
+    g = w.g
+    heads = list(range(0, g.n_heads, 2))[:32]
+    q = w.qc[0, 0]
+    out = torch.empty_like(q)
+    wts = torch.empty(g.n_streams, g.n_q, g.mem_len, device="cuda")
+
+    def timed(fn):
+        with torch.cuda.stream(stream):
+            fn()
+        stream.synchronize()
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr, stream=stream):
+            fn()
+        torch.cuda.synchronize()
+        best = float("inf")
+        for _ in range(3):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            with torch.cuda.stream(stream):
+                gr.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            best = min(best, e0.elapsed_time(e1) * 1e-3 / g.n_layers)
+        return best
+
+    cs = torch.cuda.current_stream
+    t_w = timed(lambda: [pc.cke_xattn_decode_weights(q, w.cache, l, g.scale, heads, out, wts,
+                                                     stream=cs()) for l in range(g.n_layers)])
+    t_d = timed(lambda: [pc.cke_xattn_decode(q, w.cache, l, g.scale, out, stream=cs())
+                         for l in range(g.n_layers)])
+    return {"heads": len(heads), "avg_us": t_w * 1e6, "decode_only_us": t_d * 1e6,
+            "extra_us": (t_w - t_d) * 1e6}
+
+
 def _host_cpu():
     try:
         for line in open("/proc/cpuinfo"):
@@ -471,6 +510,7 @@ def main():
         "gpu": torch.cuda.get_device_name(0),
         "git": _git_sha(),
     }
+    result["xattn_decode_weights"] = measure_weights(torch, pc, w, stream)
     prefill = measure_prefill(torch, pc, g, stream)
     if prefill:
         result["selfattn_prefill"] = prefill

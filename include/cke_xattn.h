@@ -87,10 +87,11 @@ size_t cke_xattn_region_bytes(const cke_xattn_geom* g);
  * an invalid geometry or layer. */
 size_t cke_xattn_layer_offset_bytes(const cke_xattn_geom* g, int layer);
 
-/* Bytes of device workspace a cache needs for split-key partial results:
- * fp32 [B][max_q][H][splits][D+2] (at least 256). Every decode call writes
- * the partials it reads, so the workspace needs no initialisation. Returns 0
- * for an invalid geometry. */
+/* Bytes of device workspace a cache needs: split-key partial results, fp32
+ * [B][max_q][H][splits][D+2], then (256-byte aligned) per-head softmax
+ * statistics, fp32 [B][max_q][H][2], that only cke_xattn_decode_weights
+ * writes (at least 256 bytes in all). Every call writes what it reads, so the
+ * workspace needs no initialisation. Returns 0 for an invalid geometry. */
 size_t cke_xattn_workspace_bytes(const cke_xattn_geom* g);
 
 /* Number of key splits a decode call of this geometry uses (fixed per
@@ -134,6 +135,24 @@ int cke_xattn_populate(cke_xattn_cache* c, const void* E, int e_dtype,
  * Returns CKE_ENOTREADY if the cache is not populated. */
 int cke_xattn_decode(const float* q, int n_q, const cke_xattn_cache* c,
                      int layer, float scale, float* out, void* stream);
+
+/* cke_xattn_decode plus the attention weights of selected heads, averaged
+ * over them:
+ *   weights[b][i][t] = (1 / n_heads_sel) * sum_k p_k[t],
+ *   p_k[t] = softmax_t(scale * q[b][i][heads[k]].K_l[b][heads[k]][t])
+ * normalised with the same (max, sum) the decode itself formed.
+ *   WhisperKit case study, section 8: the decoder exposes the attention
+ *   weights of its alignment heads, averaged over those heads, for word-level
+ *   timing.
+ *   heads        HOST array of n_heads_sel head indices in [0, H) (repeats
+ *                allowed); 1 <= n_heads_sel <= 32
+ *   weights      device fp32 [B][n_q][T], 16-byte aligned
+ * Errors as cke_xattn_decode, plus CKE_EINVAL / CKE_ERANGE for the head
+ * list. Uses the statistics part of the cache's workspace. */
+int cke_xattn_decode_weights(const float* q, int n_q, const cke_xattn_cache* c,
+                             int layer, float scale, const int32_t* heads,
+                             int n_heads_sel, float* out, float* weights,
+                             void* stream);
 
 /* One layer's self-attention KV cache, caller-owned: k and v are device
  * [n_seqs][n_heads][max_pos][head_dim] of dtype (CKE_F32 or CKE_BF16). */

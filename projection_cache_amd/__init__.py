@@ -75,6 +75,9 @@ _lib.cke_xattn_decode.argtypes = [_P, _I, _P, _I, _F, _P, _P]
 _lib.cke_selfattn_decode_append.restype = _I
 _lib.cke_selfattn_decode_append.argtypes = [_P, _P, _P, ctypes.POINTER(cke_kv_layer), _I, _F,
                                             _P, _P]
+_lib.cke_xattn_decode_weights.restype = _I
+_lib.cke_xattn_decode_weights.argtypes = [_P, _I, _P, _I, _F, ctypes.POINTER(ctypes.c_int32), _I,
+                                          _P, _P, _P]
 _lib.cke_selfattn_prefill_append.restype = _I
 _lib.cke_selfattn_prefill_append.argtypes = [_P, _P, _P, ctypes.POINTER(cke_kv_layer), _I, _I, _I,
                                              _F, _P, _P]
@@ -83,7 +86,8 @@ EXPORTED = ["cke_xattn_region_bytes", "cke_xattn_layer_offset_bytes",
             "cke_xattn_workspace_bytes", "cke_xattn_num_splits", "cke_xattn_cache_create",
             "cke_xattn_cache_destroy", "cke_xattn_invalidate", "cke_xattn_is_ready",
             "cke_xattn_populate", "cke_xattn_decode", "cke_selfattn_decode_append",
-            "cke_selfattn_prefill_append", "cke_last_error", "cke_version"]
+            "cke_selfattn_prefill_append", "cke_xattn_decode_weights", "cke_last_error",
+            "cke_version"]
 
 
 class CkeError(RuntimeError):
@@ -198,6 +202,16 @@ def cke_xattn_decode(q, cache, layer: int, scale: float, out, n_q=None, stream=N
                                  _ptr(out), _stream(stream)))
 
 
+def cke_xattn_decode_weights(q, cache, layer: int, scale: float, heads, out, weights,
+                             stream=None) -> None:
+    """Cross decode plus the softmax weights of the listed heads averaged over
+    them: weights [B][n_q][T] fp32. cache is an XattnCache."""
+    n_q = q.shape[1]
+    hs = (ctypes.c_int32 * len(heads))(*[int(h) for h in heads])
+    _check(_lib.cke_xattn_decode_weights(_ptr(q), n_q, cache.handle, int(layer), float(scale), hs,
+                                         len(heads), _ptr(out), _ptr(weights), _stream(stream)))
+
+
 def cke_selfattn_prefill_append(q, k_new, v_new, kv, pos: int, n_new: int, n_q_heads: int,
                                 scale: float, out, stream=None) -> None:
     """Write rows pos..pos+n_new-1 of kv from k_new/v_new [S][n_new][Hkv][D] and
@@ -246,6 +260,17 @@ class XattnCache:
             out = torch.empty_like(q)
         cke_xattn_decode(q, self, layer, scale, out, stream=stream)
         return out
+
+    def decode_weights(self, q, layer, scale, heads, out=None, weights=None, stream=None):
+        """(out, weights): decode output and the listed heads' mean attention
+        weights [B][n_q][T]."""
+        if out is None:
+            out = torch.empty_like(q)
+        if weights is None:
+            weights = torch.empty(q.shape[0], q.shape[1], self.geom.mem_len, dtype=torch.float32,
+                                  device=q.device)
+        cke_xattn_decode_weights(q, self, layer, scale, heads, out, weights, stream)
+        return out, weights
 
     def invalidate(self):
         cke_xattn_invalidate(self.handle)

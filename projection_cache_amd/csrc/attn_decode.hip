@@ -34,7 +34,7 @@ namespace cke {
 template <int D, typename TE, int NQ, int NW, int NP, bool STREAM>
 __global__ __launch_bounds__(NW * 64) void xattn_partial_kernel(
     const float* __restrict__ q, const TE* __restrict__ Kl, const TE* __restrict__ Vl,
-    float* __restrict__ out, float* __restrict__ part,
+    float* __restrict__ out, float* __restrict__ part, float* __restrict__ stats,
     int nq, int max_q, int H, int T, int nsplit, int chunk, float sl2)
 {
     using RM = RowMap<D, TE>;
@@ -74,6 +74,11 @@ __global__ __launch_bounds__(NW * 64) void xattn_partial_kernel(
             const int i = idx / D, d = idx % D;
             out[(((size_t)b * nq + i) * H + h) * D + d] = sA[i * D + d] / sL[i];
         }
+        if (stats && threadIdx.x < nq) {
+            float* st2 = stats + (((size_t)b * max_q + threadIdx.x) * H + h) * 2;
+            st2[0] = sM[threadIdx.x];
+            st2[1] = sL[threadIdx.x];
+        }
         return;
     }
     // partial layout [B][max_q][H][nsplit][D+2]: M, L, acc[0..D)
@@ -98,8 +103,8 @@ constexpr int kMergeBatch = 16;
 
 template <int D>
 __global__ __launch_bounds__(1024) void xattn_merge_kernel(
-    const float* __restrict__ part, float* __restrict__ out, int nq, int max_q, int H,
-    int nsplit)
+    const float* __restrict__ part, float* __restrict__ out, float* __restrict__ stats, int nq,
+    int max_q, int H, int nsplit)
 {
     extern __shared__ float smem[];
     const int h = blockIdx.x, b = blockIdx.y;
@@ -151,6 +156,11 @@ __global__ __launch_bounds__(1024) void xattn_merge_kernel(
         }
         const int i = o / D, d = o % D;
         out[(((size_t)b * nq + i) * H + h) * D + d] = a / l;
+        if (stats && d == 0) {
+            float* st2 = stats + (((size_t)b * max_q + i) * H + h) * 2;
+            st2[0] = m;
+            st2[1] = l;
+        }
     }
 }
 
@@ -160,7 +170,8 @@ __global__ __launch_bounds__(1024) void xattn_merge_kernel(
 template <int D, typename TE, int NQ, int NW, int NP>
 __global__ __launch_bounds__(NW * 64) void xattn_short_kernel(
     const float* __restrict__ q, const TE* __restrict__ Kl, const TE* __restrict__ Vl,
-    float* __restrict__ out, int nq, int H, int T, int n_bh, float sl2)
+    float* __restrict__ out, float* __restrict__ stats, int nq, int max_q, int H, int T, int n_bh,
+    float sl2)
 {
     using RM = RowMap<D, TE>;
     constexpr int VEC = RM::kVec, LPK = RM::kLPK;
@@ -189,6 +200,11 @@ __global__ __launch_bounds__(NW * 64) void xattn_short_kernel(
                 float* o = out + (((size_t)b * nq + i) * H + h) * D + sub * VEC;
 #pragma unroll
                 for (int j = 0; j < VEC; ++j) o[j] = st.acc[i][j] / st.l[i];
+                if (stats && lane == 0) {
+                    float* st2 = stats + (((size_t)b * max_q + i) * H + h) * 2;
+                    st2[0] = st.m[i];
+                    st2[1] = st.l[i];
+                }
             }
         }
     }
@@ -255,6 +271,46 @@ __global__ __launch_bounds__(NW * 64) void selfattn_append_kernel(
     } else {
         wg_merge<D, TE, 1, NW>(st, 1, wm, wl, wa, sM, sL, sA);
         for (int d = threadIdx.x; d < D; d += NW * 64) out[bh * D + d] = sA[d] / sL[0];
+    }
+}
+
+// ----------------------------------------------------- attention weights
+// Grid: (ceil(T / (4 * KPW)), B), 4 waves. Rows map to lanes as in the decode
+// kernels: a group of LPK lanes reads one row, 16 bytes per lane, so a wave
+// covers KPW consecutive rows with coalesced loads. For every query i the
+// group re-forms the row's score under each selected head,
+// s = scale log2(e) q.K[b][h][t] (dot reduced across the group with DPP),
+// weights it with that head's final (max, sum) in the base-2 domain left in
+// `stats` by the decode of the same call, p = 2^(s - max) / sum, and the
+// group's first lane writes the mean over the selected heads, summed in list
+// order (deterministic).
+template <int D, typename TE>
+__global__ __launch_bounds__(256) void xattn_weights_kernel(
+    const float* __restrict__ q, const TE* __restrict__ Kl, const float* __restrict__ stats,
+    float* __restrict__ weights, HeadList heads, int H, int T, int nq, int max_q, float sl2)
+{
+    using RM = RowMap<D, TE>;
+    constexpr int VEC = RM::kVec, LPK = RM::kLPK, KPW = RM::kKPW;
+    const int b = blockIdx.y;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int grp = lane / LPK, sub = lane % LPK;
+    const int t = (blockIdx.x * 4 + w) * KPW + grp;
+    const int tr = min(t, T - 1);   // rows past T load row T-1 and write nothing
+    const int n_sel = heads.n;
+    for (int i = 0; i < nq; ++i) {
+        float acc = 0.f;
+        for (int k = 0; k < n_sel; ++k) {
+            const int h = heads.h[k];
+            const uint4 r = load16(Kl + (((size_t)b * H + h) * T + tr) * D + sub * VEC);
+            const float* qv = q + (((size_t)b * nq + i) * H + h) * D + sub * VEC;
+            float dot = 0.f;
+#pragma unroll
+            for (int j = 0; j < VEC; ++j) dot = fmaf(qv[j], elem<TE>(r, j), dot);
+            dot = group_sum<LPK>(dot);
+            const float* st2 = stats + (((size_t)b * max_q + i) * H + h) * 2;
+            acc += fast_exp2(dot * sl2 - st2[0]) / st2[1];
+        }
+        if (sub == 0 && t < T) weights[((size_t)b * nq + i) * T + t] = acc / n_sel;
     }
 }
 
@@ -364,8 +420,8 @@ hipError_t launch_cross_nq(const XattnLaunch& a, hipStream_t st) {
         const int n_bh = a.B * a.H;
         hipLaunchKernelGGL((xattn_short_kernel<D, TE, NQ, NW, kShortNP>), dim3((n_bh + NW - 1) / NW),
                            dim3(NW * 64), 0, st, a.q, static_cast<const TE*>(a.K),
-                           static_cast<const TE*>(a.V), a.out, a.nq, a.H, a.T, n_bh,
-                           a.scale * kLog2e);
+                           static_cast<const TE*>(a.V), a.out, a.stats, a.nq, a.max_q, a.H, a.T,
+                           n_bh, a.scale * kLog2e);
         return hipGetLastError();
     }
     // many queries already give each loaded row more work: keep their tiles short
@@ -375,12 +431,14 @@ hipError_t launch_cross_nq(const XattnLaunch& a, hipStream_t st) {
         hipLaunchKernelGGL((xattn_partial_kernel<D, TE, NQ, kCrossWaves, NP, true>), grid,
                            dim3(kCrossWaves * 64), 0, st, a.q,
                            static_cast<const TE*>(a.K), static_cast<const TE*>(a.V), a.out,
-                           a.part, a.nq, a.max_q, a.H, a.T, a.nsplit, a.chunk, a.scale * kLog2e);
+                           a.part, a.stats, a.nq, a.max_q, a.H, a.T, a.nsplit, a.chunk,
+                           a.scale * kLog2e);
     else
         hipLaunchKernelGGL((xattn_partial_kernel<D, TE, NQ, kCrossWaves, NP, false>), grid,
                            dim3(kCrossWaves * 64), 0, st, a.q,
                            static_cast<const TE*>(a.K), static_cast<const TE*>(a.V), a.out,
-                           a.part, a.nq, a.max_q, a.H, a.T, a.nsplit, a.chunk, a.scale * kLog2e);
+                           a.part, a.stats, a.nq, a.max_q, a.H, a.T, a.nsplit, a.chunk,
+                           a.scale * kLog2e);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.nsplit == 1) return e;
     const int G = (a.nsplit + kMergeBatch - 1) / kMergeBatch;
@@ -388,7 +446,7 @@ hipError_t launch_cross_nq(const XattnLaunch& a, hipStream_t st) {
     const int threads = pairs >= 1024 ? 1024 : ((pairs + 63) / 64) * 64;
     const size_t lds = (size_t)3 * pairs * sizeof(float);
     hipLaunchKernelGGL((xattn_merge_kernel<D>), dim3(a.H, a.B), dim3(threads), lds, st, a.part,
-                       a.out, a.nq, a.max_q, a.H, a.nsplit);
+                       a.out, a.stats, a.nq, a.max_q, a.H, a.nsplit);
     return hipGetLastError();
 }
 
@@ -501,6 +559,30 @@ hipError_t launch_xattn_decode(const XattnLaunch& a, hipStream_t st) {
 
 hipError_t launch_selfattn_append(const SelfLaunch& a, hipStream_t st) {
     return a.bf16 ? launch_self_t<uint16_t>(a, st) : launch_self_t<float>(a, st);
+}
+
+hipError_t launch_xattn_weights(const WeightsLaunch& a, hipStream_t st) {
+    switch (a.D) {
+#define CKE_WEIGHTS_CASE(DD)                                                                            \
+        case DD:                                                                                          \
+            if (a.bf16) {                                                                                 \
+                constexpr int rows = 4 * RowMap<DD, uint16_t>::kKPW;                                      \
+                hipLaunchKernelGGL((xattn_weights_kernel<DD, uint16_t>), dim3((a.T + rows - 1) / rows, a.B), \
+                                   dim3(256), 0, st, a.q, static_cast<const uint16_t*>(a.K), a.stats,      \
+                                   a.weights, a.heads, a.H, a.T, a.nq, a.max_q, a.scale * kLog2e);        \
+            } else {                                                                                      \
+                constexpr int rows = 4 * RowMap<DD, float>::kKPW;                                         \
+                hipLaunchKernelGGL((xattn_weights_kernel<DD, float>), dim3((a.T + rows - 1) / rows, a.B), \
+                                   dim3(256), 0, st, a.q, static_cast<const float*>(a.K), a.stats,        \
+                                   a.weights, a.heads, a.H, a.T, a.nq, a.max_q, a.scale * kLog2e);        \
+            }                                                                                             \
+            return hipGetLastError();
+        CKE_WEIGHTS_CASE(32)
+        CKE_WEIGHTS_CASE(64)
+        CKE_WEIGHTS_CASE(128)
+#undef CKE_WEIGHTS_CASE
+    }
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_selfattn_prefill(const PrefillLaunch& a, hipStream_t st) {

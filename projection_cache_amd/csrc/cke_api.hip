@@ -116,9 +116,17 @@ void split_plan(const cke_xattn_geom* g, int* nsplit, int* chunk) {
 
 constexpr size_t kAlign = 256;
 
-// Workspace: fp32 split partials [B][max_q][H][nsplit][D+2].
+// Workspace: fp32 split partials [B][max_q][H][nsplit][D+2], then (256-byte
+// aligned) fp32 per-head statistics [B][max_q][H][2] that a decode call
+// writes only when attention weights are requested.
 size_t partial_words(const cke_xattn_geom* g, int nsplit) {
     return (size_t)g->n_streams * g->max_q * g->n_heads * (size_t)nsplit * (g->head_dim + 2);
+}
+size_t stats_offset_bytes(const cke_xattn_geom* g, int nsplit) {
+    return (partial_words(g, nsplit) * sizeof(float) + kAlign - 1) / kAlign * kAlign;
+}
+size_t stats_bytes(const cke_xattn_geom* g) {
+    return (size_t)g->n_streams * g->max_q * g->n_heads * 2 * sizeof(float);
 }
 
 }  // namespace
@@ -154,7 +162,7 @@ size_t cke_xattn_workspace_bytes(const cke_xattn_geom* g) {
     if (check_geom(g) != CKE_OK) return 0;
     int s, c;
     split_plan(g, &s, &c);
-    const size_t b = partial_words(g, s) * sizeof(float);
+    const size_t b = stats_offset_bytes(g, s) + stats_bytes(g);
     return b < kAlign ? kAlign : b;
 }
 
@@ -229,8 +237,65 @@ int cke_xattn_populate(cke_xattn_cache* c, const void* E, int e_dtype, const voi
     return CKE_OK;
 }
 
+}  // extern "C"
+
+namespace {
+
+// Checks and launch shared by the two cross-decode calls; `stats` is null
+// unless attention weights follow.
+int cross_decode(const float* q, int n_q, const cke_xattn_cache* c, int layer, float scale,
+                 float* out, float* stats, void* stream);
+
+}  // namespace
+
+extern "C" {
+
 int cke_xattn_decode(const float* q, int n_q, const cke_xattn_cache* c, int layer, float scale,
                      float* out, void* stream) {
+    return cross_decode(q, n_q, c, layer, scale, out, nullptr, stream);
+}
+
+int cke_xattn_decode_weights(const float* q, int n_q, const cke_xattn_cache* c, int layer,
+                             float scale, const int32_t* heads, int n_heads_sel, float* out,
+                             float* weights, void* stream) {
+    if (!c) return fail(CKE_EINVAL, "cache handle is NULL");
+    const cke_xattn_geom& g = c->g;
+    if (!heads || n_heads_sel < 1 || n_heads_sel > cke::kMaxWeightHeads)
+        return fail(CKE_EINVAL, "heads must list 1..%d heads", cke::kMaxWeightHeads);
+    for (int k = 0; k < n_heads_sel; ++k)
+        if (heads[k] < 0 || heads[k] >= g.n_heads)
+            return fail(CKE_ERANGE, "heads[%d] = %d outside [0, %d)", k, heads[k], g.n_heads);
+    if (n_q > 0 && (!weights || !aligned16(weights)))
+        return fail(CKE_EINVAL, "weights must be non-NULL and 16-byte aligned");
+    float* stats = reinterpret_cast<float*>(static_cast<char*>(c->ws) + stats_offset_bytes(&g, c->nsplit));
+    int rc = cross_decode(q, n_q, c, layer, scale, out, stats, stream);
+    if (rc != CKE_OK || n_q == 0) return rc;
+    cke::WeightsLaunch a;
+    a.q = q;
+    a.K = static_cast<const char*>(c->k) + region_elems(&g) / g.n_layers * layer * elem_bytes(g.cache_dtype);
+    a.stats = stats;
+    a.weights = weights;
+    a.heads.n = n_heads_sel;
+    for (int k = 0; k < cke::kMaxWeightHeads; ++k) a.heads.h[k] = k < n_heads_sel ? heads[k] : 0;
+    a.B = g.n_streams;
+    a.H = g.n_heads;
+    a.T = g.mem_len;
+    a.D = g.head_dim;
+    a.nq = n_q;
+    a.max_q = g.max_q;
+    a.scale = scale;
+    a.bf16 = g.cache_dtype == CKE_BF16;
+    hipError_t e = cke::launch_xattn_weights(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(CKE_EDEVICE, "attention-weight launch failed: %s", hipGetErrorString(e));
+    return CKE_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+int cross_decode(const float* q, int n_q, const cke_xattn_cache* c, int layer, float scale,
+                 float* out, float* stats, void* stream) {
     if (!c) return fail(CKE_EINVAL, "cache handle is NULL");
     const cke_xattn_geom& g = c->g;
     if (layer < 0 || layer >= g.n_layers)
@@ -262,14 +327,12 @@ int cke_xattn_decode(const float* q, int n_q, const cke_xattn_cache* c, int laye
     // K and V of every layer together: a cache this much larger than the
     // 256 MB MALL is never re-read from it, so its rows are streamed
     a.stream_rows = 2 * region_elems(&g) * elem_bytes(g.cache_dtype) > kStreamCacheBytes;
+    a.stats = stats;
     hipError_t e = cke::launch_xattn_decode(a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(CKE_EDEVICE, "decode launch failed: %s", hipGetErrorString(e));
     return CKE_OK;
 }
 
-}  // extern "C"
-
-namespace {
 
 // Checks shared by the self-attention calls, in the order they report.
 int check_self_args(const float* q, const float* k_new, const float* v_new,

@@ -20,6 +20,7 @@ struct XattnLaunch {
     float scale;
     bool bf16;
     bool stream_rows;    // whole cross cache far larger than the MALL: non-temporal row loads
+    float* stats;        // nullptr, or fp32 [B][max_q][H][2]: each head's final (max, sum), base 2
 };
 
 struct SelfLaunch {
@@ -30,6 +31,24 @@ struct SelfLaunch {
     void* V;
     float* out;
     int S, H, D, max_pos, pos;
+    float scale;
+    bool bf16;
+};
+
+// Selected heads for attention-weight output (at most kMaxWeightHeads).
+constexpr int kMaxWeightHeads = 32;
+struct HeadList {
+    int n;
+    int h[kMaxWeightHeads];
+};
+
+struct WeightsLaunch {
+    const float* q;      // [B][nq][H][D]
+    const void* K;       // layer slab base, [B][H][T][D]
+    const float* stats;  // [B][max_q][H][2] from the decode of the same call
+    float* weights;      // [B][nq][T]
+    HeadList heads;
+    int B, H, T, D, nq, max_q;
     float scale;
     bool bf16;
 };
@@ -74,6 +93,7 @@ hipError_t launch_xattn_decode(const XattnLaunch& a, hipStream_t st);
 
 hipError_t launch_selfattn_append(const SelfLaunch& a, hipStream_t st);
 hipError_t launch_selfattn_prefill(const PrefillLaunch& a, hipStream_t st);
+hipError_t launch_xattn_weights(const WeightsLaunch& a, hipStream_t st);
 hipError_t launch_populate(const PopulateLaunch& a, hipStream_t st);
 
 }  // namespace cke

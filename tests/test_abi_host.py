@@ -26,7 +26,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) >= 14
+    assert len(names) >= 15
     lib = ctypes.CDLL(pc.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -85,7 +85,8 @@ def test_workspace_and_split_plan():
         assert 1 <= s <= 64
         ws = pc.cke_xattn_workspace_bytes(g)
         need = g.n_streams * g.max_q * g.n_heads * s * (g.head_dim + 2) * 4
-        assert ws >= need
+        stats = g.n_streams * g.max_q * g.n_heads * 2 * 4
+        assert ws >= (need + 255) // 256 * 256 + stats
     # Whisper Base splits its 1500 rows across workgroups, Q-Former does not
     assert pc.cke_xattn_num_splits(base_geom()) > 1
     assert pc.cke_xattn_num_splits(base_geom(n_layers=2, n_streams=100, mem_len=15, d_model=2048,
@@ -174,3 +175,24 @@ def test_prefill_rejects_bad_arguments_before_launch():
     assert call(k=None) == pc.CKE_EINVAL
     assert "n_q_heads" in (call(n_q_heads=4) and pc.cke_last_error())
     assert L.cke_selfattn_prefill_append(FAKE, FAKE, FAKE, None, 0, 1, 8, 0.125, FAKE, None) == pc.CKE_EINVAL
+
+
+def test_decode_weights_rejects_bad_head_lists_before_launch():
+    h = pc.cke_xattn_cache_create(base_geom(), FAKE, FAKE, FAKE)
+    try:
+        L = pc.lib()
+
+        def call(heads, n=None):
+            arr = (ctypes.c_int32 * max(1, len(heads)))(*heads)
+            return L.cke_xattn_decode_weights(FAKE, 1, h, 0, 0.125, arr, len(heads) if n is None else n,
+                                              FAKE, FAKE, None)
+
+        assert call([0, 8]) == pc.CKE_ERANGE          # head 8 of 8
+        assert call([-1]) == pc.CKE_ERANGE
+        assert call([], 0) == pc.CKE_EINVAL
+        assert call(list(range(8)) * 5) == pc.CKE_EINVAL   # more than 32 heads
+        assert L.cke_xattn_decode_weights(FAKE, 1, h, 0, 0.125, None, 1, FAKE, FAKE, None) == pc.CKE_EINVAL
+        # a valid list on an unpopulated cache: refused with -2 before any launch
+        assert call([1, 3]) == pc.CKE_ENOTREADY
+    finally:
+        pc.cke_xattn_cache_destroy(h)

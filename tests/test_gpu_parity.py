@@ -173,6 +173,39 @@ def test_cross_decode_matches_oracle(name, kw):
             assert err <= tol, (step, layer, err)
 
 
+WEIGHT_CASES = [
+    ("base", {}, [0, 3, 5]),                                   # split over workgroups + merge
+    (None, dict(n_layers=1, n_streams=16, mem_len=100, d_model=1280, n_heads=20, head_dim=64,
+                dtype="bf16"), [2, 19, 7, 2]),                 # unsplit (one workgroup per head)
+    (None, dict(n_layers=2, n_streams=5, n_q=3, mem_len=15, d_model=256, n_heads=4,
+                head_dim=64), [1, 2]),                         # short memory, several queries
+    (None, dict(n_layers=1, n_streams=2, n_q=2, mem_len=300, d_model=256, n_heads=2,
+                head_dim=128, dtype="bf16"), [1]),
+    (None, dict(n_layers=1, n_streams=3, mem_len=77, d_model=96, n_heads=3, head_dim=32), [0, 1, 2]),
+]
+
+
+@pytest.mark.parametrize("name,kw,heads", WEIGHT_CASES, ids=lambda x: str(x))
+def test_cross_decode_weights_match_oracle(name, kw, heads):
+    """Mean attention weights of the selected heads within the cache dtype's
+    tolerance of the oracle, rows summing to 1, and the decode output of the
+    same call unchanged."""
+    g = geometry(name, **kw)
+    cache, wt, _ = make_cache(g)
+    Kc, Vc = oracle_caches(g, wt)
+    tol = TOL[g.dtype]
+    layer = g.n_layers - 1
+    q = synth.decode_call_inputs(g, 1, layer)["q_cross"]
+    out, w = cache.decode_weights(t32(q), layer, g.scale, heads)
+    plain = cache.decode(t32(q), layer, g.scale)
+    torch.cuda.synchronize()
+    want_out, want_w = oracle.cross_decode_weights(q, Kc[layer], Vc[layer], g.scale, heads)
+    assert max_abs(to_np(out), want_out) <= tol
+    assert max_abs(to_np(w), want_w) <= tol
+    np.testing.assert_allclose(to_np(w).sum(axis=-1), 1.0, atol=1e-4)
+    np.testing.assert_array_equal(to_np(out), to_np(plain))
+
+
 def test_cross_decode_peaked_softmax_and_shift_invariance():
     """A large scale concentrates the softmax (online max tracking across
     splits matters); adding one constant vector to every key of a head leaves
