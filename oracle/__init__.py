@@ -54,6 +54,9 @@ def lib():
         L.orc_round_bf16.restype = _D
         L.orc_round_bf16.argtypes = [_D]
         L.orc_round_bf16_array.argtypes = [_P, _P, _SZ]
+        L.orc_round_fp8.restype = _D
+        L.orc_round_fp8.argtypes = [_D]
+        L.orc_round_fp8_array.argtypes = [_P, _P, _SZ]
         L.orc_project_head.argtypes = [_I, _I, _I, _P, _P, _I, _I, _I, _P]
         L.orc_populate.argtypes = [_I] * 6 + [_P, _P, _P, _I, _P, _P]
         L.orc_layer_offset_bytes.restype = _SZ
@@ -99,19 +102,35 @@ def round_bf16(x) -> np.ndarray:
     return y
 
 
-def project_head(E_b, W, col0: int, D: int, round_bf16: bool = False) -> np.ndarray:
+def round_fp8(x) -> np.ndarray:
+    """Clamp to [-448, 448], then round to the nearest fp8 e4m3 value (ties
+    to even)."""
+    a = _f64(x)
+    y = np.empty_like(a)
+    lib().orc_round_fp8_array(_ptr(a), _ptr(y), a.size)
+    return y
+
+
+def _round_mode(round_bf16: bool, round_fp8: bool) -> int:
+    assert not (round_bf16 and round_fp8)
+    return 1 if round_bf16 else (2 if round_fp8 else 0)
+
+
+def project_head(E_b, W, col0: int, D: int, round_bf16: bool = False,
+                 round_fp8: bool = False) -> np.ndarray:
     """One head's projection slab [T][D] of E_b [T][dm] by W [dm][ldw]."""
     E_b, W = _f64(E_b), _f64(W)
     T, dm = E_b.shape
     out = np.empty((T, D), dtype=np.float64)
     lib().orc_project_head(T, dm, D, _ptr(E_b), _ptr(W), W.shape[1], col0,
-                           int(round_bf16), _ptr(out))
+                           _round_mode(round_bf16, round_fp8), _ptr(out))
     return out
 
 
-def populate(E, WK, WV, H: int, D: int, round_bf16: bool = False):
+def populate(E, WK, WV, H: int, D: int, round_bf16: bool = False, round_fp8: bool = False):
     """Projection caches (Kc, Vc), each [L][B][H][T][D], from E [B][T][dm]
-    and per-layer weights WK, WV (sequences of [dm][H*D])."""
+    and per-layer weights WK, WV (sequences of [dm][H*D]); stored values
+    rounded to bfloat16 or to fp8 e4m3 when asked."""
     E = _f64(E)
     WK = _f64(np.stack(list(WK)))
     WV = _f64(np.stack(list(WV)))
@@ -120,7 +139,7 @@ def populate(E, WK, WV, H: int, D: int, round_bf16: bool = False):
     Kc = np.empty((L, B, H, T, D), dtype=np.float64)
     Vc = np.empty_like(Kc)
     lib().orc_populate(L, B, T, dm, H, D, _ptr(E), _ptr(WK), _ptr(WV),
-                       int(round_bf16), _ptr(Kc), _ptr(Vc))
+                       _round_mode(round_bf16, round_fp8), _ptr(Kc), _ptr(Vc))
     return Kc, Vc
 
 

@@ -77,6 +77,40 @@ void orc_round_bf16_array(const double* x, double* y, size_t n)
     for (size_t i = 0; i < n; ++i) y[i] = orc_round_bf16(x[i]);
 }
 
+/* ----------------------------------------------------- fp8 (e4m3) rounding
+ * The compressed projection cache stores 8-bit floats with 4 exponent bits
+ * (bias 7) and 3 mantissa bits, no infinities: largest finite 448, smallest
+ * normal 2^-6, subnormal spacing 2^-9 (the OCP "E4M3" format). A value is
+ * first clamped to [-448, 448] (the cache saturates rather than storing a
+ * non-finite code) and then rounded to the nearest representable value, ties
+ * to even.
+ */
+double orc_round_fp8(double x)
+{
+    if (x != x) return x;
+    if (x > 448.0) x = 448.0;
+    if (x < -448.0) x = -448.0;
+    if (x == 0.0) return x;
+    const double min_normal = ldexp(1.0, -6);
+    if (fabs(x) < min_normal) return ldexp(nearbyint(ldexp(x, 9)), -9);
+    int e;
+    double f = frexp(x, &e);            /* x = f * 2^e, 0.5 <= |f| < 1 */
+    double r = nearbyint(ldexp(f, 4));  /* 4 significant bits, ties-to-even */
+    return ldexp(r, e - 4);
+}
+
+void orc_round_fp8_array(const double* x, double* y, size_t n)
+{
+    for (size_t i = 0; i < n; ++i) y[i] = orc_round_fp8(x[i]);
+}
+
+/* Storage rounding of a cache element: 0 none (fp32 stores the fp64 value
+ * here), 1 bfloat16, 2 fp8 e4m3. */
+static double round_store(double x, int mode)
+{
+    return mode == 1 ? orc_round_bf16(x) : (mode == 2 ? orc_round_fp8(x) : x);
+}
+
 /* ---------------------------------------------------------------- O1: project
  * [CKE] "The concept": every decoder layer l applies its own WK_l / WV_l to the
  * one encoder memory E (K_l = E x WK_l, V_l = E x WV_l); the encoder's internal
@@ -86,10 +120,11 @@ void orc_round_bf16_array(const double* x, double* y, size_t n)
  * orc_project_head writes one head's slab:
  *   out[t][d] = sum_{c ascending} E[t][c] * W[c][col0 + d],  t < T, d < D
  * E is token-major [T][dm]; W is [dm][ldw] row-major (y = x . W orientation).
- * If round_bf16 != 0 the stored value is rounded to bfloat16.
+ * round_mode: 0 stores the value as is, 1 rounds it to bfloat16, 2 to fp8
+ * e4m3 (round_store).
  */
 void orc_project_head(int T, int dm, int D, const double* E, const double* W,
-                      int ldw, int col0, int round_bf16, double* out)
+                      int ldw, int col0, int round_mode, double* out)
 {
     for (int t = 0; t < T; ++t) {
         const double* e = E + (size_t)t * dm;
@@ -97,7 +132,7 @@ void orc_project_head(int T, int dm, int D, const double* E, const double* W,
             double acc = 0.0;
             for (int c = 0; c < dm; ++c)
                 acc += e[c] * W[(size_t)c * ldw + col0 + d];
-            out[(size_t)t * D + d] = round_bf16 ? orc_round_bf16(acc) : acc;
+            out[(size_t)t * D + d] = round_store(acc, round_mode);
         }
     }
 }
@@ -105,7 +140,7 @@ void orc_project_head(int T, int dm, int D, const double* E, const double* W,
 /* Whole projection cache: Kc, Vc are [L][B][H][T][D]; E is [B][T][dm];
  * WK, WV are [L][dm][H*D]. */
 void orc_populate(int L, int B, int T, int dm, int H, int D, const double* E,
-                  const double* WK, const double* WV, int round_bf16,
+                  const double* WK, const double* WV, int round_mode,
                   double* Kc, double* Vc)
 {
     const int HD = H * D;
@@ -116,9 +151,9 @@ void orc_populate(int L, int B, int T, int dm, int H, int D, const double* E,
                 size_t slab = ((((size_t)l * B + b) * H + h) * T) * D;
                 const double* Eb = E + (size_t)b * T * dm;
                 orc_project_head(T, dm, D, Eb, WK + (size_t)l * dm * HD, HD,
-                                 h * D, round_bf16, Kc + slab);
+                                 h * D, round_mode, Kc + slab);
                 orc_project_head(T, dm, D, Eb, WV + (size_t)l * dm * HD, HD,
-                                 h * D, round_bf16, Vc + slab);
+                                 h * D, round_mode, Vc + slab);
             }
 }
 

@@ -24,6 +24,38 @@ def rng(seed):
     return np.random.default_rng(seed)
 
 
+# ----------------------------------------------------------------- fp8 rounding
+def test_round_fp8_matches_torch_e4m3fn_cast_of_clamped_values():
+    """Pinned to torch's float32 -> float8_e4m3fn cast (nearest, ties to even)
+    of the value clamped to [-448, 448]: every finite code, every midpoint
+    between neighbouring codes (exact ties), subnormals and values far out of
+    range; all results are finite e4m3 values."""
+    codes = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).float().numpy()
+    fin = np.unique(codes[np.isfinite(codes)])
+    mids = (fin[1:] + fin[:-1]) / 2
+    r = rng(60)
+    x = np.concatenate([fin, mids, r.standard_normal(20000) * 3, r.standard_normal(5000) * 0.01,
+                        r.standard_normal(3000) * 1000,
+                        np.array([448, 449, 463.99, 464, 465, 1e30, -1e30, 2.0 ** -9, 2.0 ** -10,
+                                  3 * 2.0 ** -11, 0.0, -0.0])]).astype(np.float32)
+    got = oracle.round_fp8(x)
+    want = torch.from_numpy(np.clip(x, -448, 448)).to(torch.float8_e4m3fn).float().numpy()
+    np.testing.assert_array_equal(got, want)
+    assert np.isin(got, fin).all()
+
+
+def test_populate_fp8_stores_rounded_projection():
+    """The fp8 cache holds round_fp8 of the exact projection."""
+    r = rng(61)
+    E = r.standard_normal((2, 9, 16))
+    WK = [r.standard_normal((16, 8)) * 0.3 for _ in range(2)]
+    WV = [r.standard_normal((16, 8)) * 0.3 for _ in range(2)]
+    K0, V0 = oracle.populate(E, WK, WV, 2, 4)
+    K8, V8 = oracle.populate(E, WK, WV, 2, 4, round_fp8=True)
+    np.testing.assert_array_equal(K8, oracle.round_fp8(K0))
+    np.testing.assert_array_equal(V8, oracle.round_fp8(V0))
+
+
 # ----------------------------------------------------------------- bf16 rounding
 def test_round_bf16_matches_torch_cast():
     """Pinned to torch's float32 -> bfloat16 cast (round to nearest even)."""
