@@ -49,6 +49,9 @@ WORKLOAD_TEXT = {
             "6 layers, 8 heads x 64, populate + 448 decode steps",
     "large": "large: 16 streams x E[1500,1280] bf16, 32 layers, 20 heads x 64, "
              "populate + 128 decode steps, bf16 caches, fp32 accumulate",
+    "large_fp8": "large over an fp8 cache: 16 streams x E[1500,1280] bf16, 32 layers, "
+                 "20 heads x 64, populate + 128 decode steps, fp8 E4M3 projection cache, "
+                 "bf16 self caches, fp32 accumulate",
     "qformer": "q-former projector cross-attn: 100 blocks x 15 frames, memory width 2048, "
                "2 layers, 32 heads x 64, 3 queries per block, one pass",
     "tiny": "tiny: E[64,64] fp32, 1 layer, 2 heads x 32, 8 decode steps",
@@ -83,7 +86,8 @@ class Workload:
         self.torch, self.pc = torch, pc
         g = self.g = synth.get(name)
         dev = "cuda:0"
-        self.bf16 = g.dtype == "bf16"
+        self.bf16 = g.dtype in ("bf16", "fp8")      # bf16 E, W and self caches
+        self.cache_elem = {"f32": 4, "bf16": 2, "fp8": 1}[g.dtype]
         wt = synth.workload_tensors(g)
 
         def dev_f32(a):
@@ -102,10 +106,12 @@ class Workload:
             self.WK = [dev_f32(w) for w in wt["WK"]]
             self.WV = [dev_f32(w) for w in wt["WV"]]
         del wt
-        cdt = torch.bfloat16 if self.bf16 else torch.float32
+        cdt = {"f32": torch.float32, "bf16": torch.bfloat16,
+               "fp8": torch.float8_e4m3fn}[g.dtype]
+        sdt = torch.bfloat16 if self.bf16 else torch.float32
         self.cache = pc.XattnCache(g.n_layers, g.n_streams, g.mem_len, g.d_model, g.n_heads,
                                    g.head_dim, max_q=g.n_q, dtype=cdt)
-        self.kv = [pc.KVLayer(g.n_seqs, g.n_heads, g.head_dim, g.max_pos, dtype=cdt)
+        self.kv = [pc.KVLayer(g.n_seqs, g.n_heads, g.head_dim, g.max_pos, dtype=sdt)
                    for _ in range(g.n_layers)] if g.n_seqs else []
         # per-call inputs [steps][L][...]
         steps, L = g.steps, g.n_layers
@@ -158,11 +164,12 @@ class Workload:
 
     # algorithmic work -------------------------------------------------------
     def elem(self):
+        """Bytes per self-attention cache element."""
         return 2 if self.bf16 else 4
 
     def cross_bytes_per_call(self):
         g = self.g
-        kv = 2 * g.n_streams * g.n_heads * g.mem_len * g.head_dim * self.elem()
+        kv = 2 * g.n_streams * g.n_heads * g.mem_len * g.head_dim * self.cache_elem
         qo = 2 * g.n_streams * g.n_q * g.n_heads * g.head_dim * 4
         return kv + qo
 
@@ -188,17 +195,18 @@ def cpu_baseline(name, budget_s):
     threads = oracle.get_threads()
     wt = synth.workload_tensors(g)
     t0 = time.perf_counter()
-    if name == "large":
-        # one stream of the sixteen, scaled x16
+    one = name in ("large", "large_fp8")   # one stream of the sixteen, scaled x16
+    if one:
         Kc, Vc = oracle.populate(wt["E"][:1], wt["WK"], wt["WV"], g.n_heads, g.head_dim,
-                                 round_bf16=True)
+                                 round_bf16=(g.dtype == "bf16"), round_fp8=(g.dtype == "fp8"))
         t_pop = (time.perf_counter() - t0) * g.n_streams
     else:
         Kc, Vc = oracle.populate(wt["E"], wt["WK"], wt["WV"], g.n_heads, g.head_dim,
                                  round_bf16=(g.dtype == "bf16"))
         t_pop = time.perf_counter() - t0
     del wt
-    S = g.n_seqs if name != "large" else 1
+    S = g.n_seqs if not one else 1
+    self_bf16 = g.dtype in ("bf16", "fp8")
     Ks = [np.zeros((S, g.n_heads, g.max_pos, g.head_dim)) for _ in range(g.n_layers)] if S else []
     Vs = [np.zeros_like(k) for k in Ks]
     t1 = time.perf_counter()
@@ -208,21 +216,21 @@ def cpu_baseline(name, budget_s):
             d = synth.decode_call_inputs(g, t, l)
             if S:
                 oracle.self_append_attend(d["q_self"][:S], d["k_new"][:S], d["v_new"][:S], Ks[l],
-                                          Vs[l], t, g.scale, round_bf16=(g.dtype == "bf16"))
-            q = d["q_cross"][:1] if name == "large" else d["q_cross"]
-            oracle.cross_decode(q, Kc[l][:1] if name == "large" else Kc[l],
-                                Vc[l][:1] if name == "large" else Vc[l], g.scale)
+                                          Vs[l], t, g.scale, round_bf16=self_bf16)
+            q = d["q_cross"][:1] if one else d["q_cross"]
+            oracle.cross_decode(q, Kc[l][:1] if one else Kc[l], Vc[l][:1] if one else Vc[l],
+                                g.scale)
         n_tok += 1
         if time.perf_counter() - t1 > max(1.0, budget_s - t_pop):
             break
     t_tok = (time.perf_counter() - t1) / n_tok
-    if name == "large":
+    if one:
         t_tok *= g.n_streams
     per_window = t_pop + g.steps * t_tok
     tokens = g.steps * (g.n_seqs if g.n_seqs else g.n_streams * g.n_q)
     sample = ("oracle populate of the %s cache%s, then %d of %d decode steps (all layers, "
               "self + cross); window time = populate + %d x mean step time" %
-              (name, " for 1 of 16 streams x16" if name == "large" else "", n_tok, g.steps,
+              (name, " for 1 of 16 streams x16" if one else "", n_tok, g.steps,
                g.steps))
     return {"value": tokens / per_window, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": sample, "populate_s": t_pop, "step_s": t_tok,
@@ -267,8 +275,9 @@ def measure_prefill(torch, pc, g, stream):
     q, k_new, v_new and out."""
     if not g.n_seqs:
         return None
-    dt = torch.bfloat16 if g.dtype == "bf16" else torch.float32
-    elem = 2 if g.dtype == "bf16" else 4
+    self_bf16 = g.dtype in ("bf16", "fp8")   # self caches of fp8 workloads are bf16
+    dt = torch.bfloat16 if self_bf16 else torch.float32
+    elem = 2 if self_bf16 else 4
     S, H, D = g.n_seqs, g.n_heads, g.head_dim
     kv = pc.KVLayer(S, H, D, g.max_pos, dtype=dt)
     kv.k.normal_(0, 0.45)
@@ -477,6 +486,7 @@ def main():
     share = {k: float(np.sum(v)) for k, v in dur.items()}
     dominant = max(share, key=share.get)
     pop_tflops = kernels["populate"]["tflops"]
+    pop_dt = "bf16" if w.bf16 else "f32"        # the MFMA input type
     result = {
         "metric": METRIC,
         "value": tok_s,
@@ -488,7 +498,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if w.bf16 else "f32",
+        "dtype": {"f32": "f32", "bf16": "bf16", "fp8": "fp8"}[g.dtype],
         "data": "synthetic",
         "config": {"workload": WORKLOAD_TEXT[args.config], "name": args.config,
                    "tokens_per_step": w.tokens_per_window, "decode_steps": g.steps,
@@ -500,8 +510,8 @@ def main():
                      "traffic": traffic["bytes"] if traffic else None,
                      "traffic_read_write": [traffic["read"], traffic["write"]] if traffic else None,
                      "bytes_per_launch": cross_b, "avg_launch_us": avg["xattn_decode"] * 1e6},
-        "populate": {"tflops": pop_tflops, "peak_tflops": MFMA_PEAK_TFLOPS[g.dtype],
-                     "frac": pop_tflops / MFMA_PEAK_TFLOPS[g.dtype],
+        "populate": {"tflops": pop_tflops, "peak_tflops": MFMA_PEAK_TFLOPS[pop_dt],
+                     "frac": pop_tflops / MFMA_PEAK_TFLOPS[pop_dt],
                      "mfma": "v_mfma_f32_32x32x16_bf16" if w.bf16 else "v_mfma_f32_32x32x2_f32"},
         "kernels": kernels,
         "time_share": {k: v / sum(share.values()) for k, v in share.items()},

@@ -57,8 +57,11 @@ enum {
     CKE_EDEVICE = -4     /* the HIP runtime reported an error at launch */
 };
 
-/* Element types. */
-enum { CKE_F32 = 0, CKE_BF16 = 1 };
+/* Element types. CKE_FP8 is the 8-bit float with 4 exponent and 3 mantissa
+ * bits (OCP E4M3: largest finite 448, no infinities), for projection caches
+ * only (the compressed cache: decode is bandwidth-bound and reads half the
+ * bytes of bf16). */
+enum { CKE_F32 = 0, CKE_BF16 = 1, CKE_FP8 = 2 };
 
 /* Geometry of one projection cache. Fail-closed: mem_len must be positive and
  * n_heads*head_dim must equal d_model (C-Kernel-Engine page, "View 3": both
@@ -72,7 +75,7 @@ typedef struct cke_xattn_geom {
     int32_t n_heads;     /* H */
     int32_t head_dim;    /* D */
     int32_t max_q;       /* largest n_q a decode call may pass, 1..8 */
-    int32_t cache_dtype; /* CKE_F32 or CKE_BF16 */
+    int32_t cache_dtype; /* CKE_F32, CKE_BF16 or CKE_FP8 */
 } cke_xattn_geom;
 
 /* Opaque host-side handle: geometry, the caller's K/V/workspace pointers and
@@ -119,8 +122,11 @@ int cke_xattn_is_ready(const cke_xattn_cache* c);
  *   WK  HOST array of L device pointers, each [d_model][H*D], w_dtype
  *   WV  likewise
  * Supported (e_dtype, w_dtype, cache_dtype): (F32, F32, F32) -- fp32
- * products, fp32 accumulation on the matrix cores -- and (BF16, BF16, BF16)
- * -- bf16 products, fp32 accumulation, result rounded to nearest-even bf16.
+ * products, fp32 accumulation on the matrix cores --, (BF16, BF16, BF16)
+ * -- bf16 products, fp32 accumulation, result rounded to nearest-even bf16
+ * -- and (BF16, BF16, FP8) -- the same products, result clamped to
+ * [-448, 448] and rounded to nearest-even E4M3; this one needs
+ * n_heads*head_dim to be a multiple of 256 (CKE_EINVAL otherwise).
  * Sets the ready flag once the work is enqueued. */
 int cke_xattn_populate(cke_xattn_cache* c, const void* E, int e_dtype,
                        const void* const* WK, const void* const* WV,

@@ -24,8 +24,10 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("CKE_XATTN_LIB") or os.path.join(_PKG, "libcke_xattn.so")
 
 CKE_OK, CKE_EINVAL, CKE_ENOTREADY, CKE_ERANGE, CKE_EDEVICE = 0, -1, -2, -3, -4
-CKE_F32, CKE_BF16 = 0, 1
-_DTYPES = {torch.float32: CKE_F32, torch.bfloat16: CKE_BF16}
+CKE_F32, CKE_BF16, CKE_FP8 = 0, 1, 2
+# fp8 (E4M3, OCP "fn" variant: no infinities, largest finite 448) is a
+# projection-cache type only, populated from bf16 E and weights
+_DTYPES = {torch.float32: CKE_F32, torch.bfloat16: CKE_BF16, torch.float8_e4m3fn: CKE_FP8}
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(

@@ -11,6 +11,7 @@
 // Both are HBM-bound streaming kernels (0.5-2.5 FLOP per byte). Each lane
 // reads 16 contiguous bytes of a K row and of a V row, a wave reads whole
 // rows, and every load of a tile is issued before the arithmetic that uses it.
+#include "../../include/cke_xattn.h"
 #include "cke_device.h"
 #include "cke_internal.h"
 
@@ -546,6 +547,26 @@ hipError_t launch_prefill_t(const PrefillLaunch& a, hipStream_t st) {
     return hipErrorInvalidValue;
 }
 
+// One workgroup of 4 waves per 4*KPW memory rows of one stream.
+template <int D, typename TE>
+hipError_t launch_weights_d(const WeightsLaunch& a, hipStream_t st) {
+    constexpr int rows = 4 * RowMap<D, TE>::kKPW;
+    hipLaunchKernelGGL((xattn_weights_kernel<D, TE>), dim3((a.T + rows - 1) / rows, a.B), dim3(256),
+                       0, st, a.q, static_cast<const TE*>(a.K), a.stats, a.weights, a.heads, a.H,
+                       a.T, a.nq, a.max_q, a.scale * kLog2e);
+    return hipGetLastError();
+}
+
+template <typename TE>
+hipError_t launch_weights_t(const WeightsLaunch& a, hipStream_t st) {
+    switch (a.D) {
+        case 32: return launch_weights_d<32, TE>(a, st);
+        case 64: return launch_weights_d<64, TE>(a, st);
+        case 128: return launch_weights_d<128, TE>(a, st);
+    }
+    return hipErrorInvalidValue;
+}
+
 }  // namespace
 
 int cross_keys_per_pass(int D, int elem_bytes) {
@@ -554,7 +575,12 @@ int cross_keys_per_pass(int D, int elem_bytes) {
 }
 
 hipError_t launch_xattn_decode(const XattnLaunch& a, hipStream_t st) {
-    return a.bf16 ? launch_cross_t<uint16_t>(a, st) : launch_cross_t<float>(a, st);
+    switch (a.dtype) {
+        case CKE_F32: return launch_cross_t<float>(a, st);
+        case CKE_BF16: return launch_cross_t<uint16_t>(a, st);
+        case CKE_FP8: return launch_cross_t<uint8_t>(a, st);
+    }
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_selfattn_append(const SelfLaunch& a, hipStream_t st) {
@@ -562,25 +588,10 @@ hipError_t launch_selfattn_append(const SelfLaunch& a, hipStream_t st) {
 }
 
 hipError_t launch_xattn_weights(const WeightsLaunch& a, hipStream_t st) {
-    switch (a.D) {
-#define CKE_WEIGHTS_CASE(DD)                                                                            \
-        case DD:                                                                                          \
-            if (a.bf16) {                                                                                 \
-                constexpr int rows = 4 * RowMap<DD, uint16_t>::kKPW;                                      \
-                hipLaunchKernelGGL((xattn_weights_kernel<DD, uint16_t>), dim3((a.T + rows - 1) / rows, a.B), \
-                                   dim3(256), 0, st, a.q, static_cast<const uint16_t*>(a.K), a.stats,      \
-                                   a.weights, a.heads, a.H, a.T, a.nq, a.max_q, a.scale * kLog2e);        \
-            } else {                                                                                      \
-                constexpr int rows = 4 * RowMap<DD, float>::kKPW;                                         \
-                hipLaunchKernelGGL((xattn_weights_kernel<DD, float>), dim3((a.T + rows - 1) / rows, a.B), \
-                                   dim3(256), 0, st, a.q, static_cast<const float*>(a.K), a.stats,        \
-                                   a.weights, a.heads, a.H, a.T, a.nq, a.max_q, a.scale * kLog2e);        \
-            }                                                                                             \
-            return hipGetLastError();
-        CKE_WEIGHTS_CASE(32)
-        CKE_WEIGHTS_CASE(64)
-        CKE_WEIGHTS_CASE(128)
-#undef CKE_WEIGHTS_CASE
+    switch (a.dtype) {
+        case CKE_F32: return launch_weights_t<float>(a, st);
+        case CKE_BF16: return launch_weights_t<uint16_t>(a, st);
+        case CKE_FP8: return launch_weights_t<uint8_t>(a, st);
     }
     return hipErrorInvalidValue;
 }

@@ -39,9 +39,10 @@ int fail(int code, const char* fmt, ...) {
     return code;
 }
 
-int elem_bytes(int dtype) { return dtype == CKE_BF16 ? 2 : 4; }
+int elem_bytes(int dtype) { return dtype == CKE_FP8 ? 1 : (dtype == CKE_BF16 ? 2 : 4); }
 
 bool dtype_ok(int dtype) { return dtype == CKE_F32 || dtype == CKE_BF16; }
+bool cache_dtype_ok(int dtype) { return dtype_ok(dtype) || dtype == CKE_FP8; }
 
 bool head_dim_ok(int D) { return D == 32 || D == 64 || D == 128; }
 
@@ -66,7 +67,7 @@ int check_geom(const cke_xattn_geom* g) {
     if (g->d_model % 32 != 0)
         return fail(CKE_EINVAL, "d_model must be a multiple of 32 (got %d)", g->d_model);
     if (g->max_q < 1 || g->max_q > 8) return fail(CKE_EINVAL, "max_q must be in [1, 8] (got %d)", g->max_q);
-    if (!dtype_ok(g->cache_dtype)) return fail(CKE_EINVAL, "unknown cache dtype %d", g->cache_dtype);
+    if (!cache_dtype_ok(g->cache_dtype)) return fail(CKE_EINVAL, "unknown cache dtype %d", g->cache_dtype);
     const long long rows = (long long)g->n_streams * g->mem_len;
     if (rows > (1ll << 31) - 1) return fail(CKE_EINVAL, "n_streams * mem_len too large");
     const long long grid_y = 2ll * g->n_layers * g->d_model / 32;
@@ -206,10 +207,13 @@ int cke_xattn_populate(cke_xattn_cache* c, const void* E, int e_dtype, const voi
     const cke_xattn_geom& g = c->g;
     const bool f32 = e_dtype == CKE_F32 && w_dtype == CKE_F32 && g.cache_dtype == CKE_F32;
     const bool bf16 = e_dtype == CKE_BF16 && w_dtype == CKE_BF16 && g.cache_dtype == CKE_BF16;
-    if (!f32 && !bf16)
+    const bool fp8 = e_dtype == CKE_BF16 && w_dtype == CKE_BF16 && g.cache_dtype == CKE_FP8;
+    if (!f32 && !bf16 && !fp8)
         return fail(CKE_EINVAL,
-                    "unsupported dtypes (E %d, W %d, cache %d): need all fp32 or all bf16",
-                    e_dtype, w_dtype, g.cache_dtype);
+                    "unsupported dtypes (E %d, W %d, cache %d): need all fp32, all bf16, or bf16 "
+                    "inputs with an fp8 cache", e_dtype, w_dtype, g.cache_dtype);
+    if (fp8 && (g.n_heads * g.head_dim) % 256 != 0)
+        return fail(CKE_EINVAL, "an fp8 cache needs n_heads * head_dim to be a multiple of 256");
     if (!aligned16(E)) return fail(CKE_EINVAL, "E must be 16-byte aligned");
     cke::PopulateLaunch a;
     std::memset(&a, 0, sizeof(a));
@@ -229,7 +233,8 @@ int cke_xattn_populate(cke_xattn_cache* c, const void* E, int e_dtype, const voi
     a.dm = g.d_model;
     a.H = g.n_heads;
     a.D = g.head_dim;
-    a.bf16 = bf16;
+    a.bf16 = bf16 || fp8;
+    a.fp8 = fp8;
     c->ready = 0;
     hipError_t e = cke::launch_populate(a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(CKE_EDEVICE, "populate launch failed: %s", hipGetErrorString(e));
@@ -284,7 +289,7 @@ int cke_xattn_decode_weights(const float* q, int n_q, const cke_xattn_cache* c, 
     a.nq = n_q;
     a.max_q = g.max_q;
     a.scale = scale;
-    a.bf16 = g.cache_dtype == CKE_BF16;
+    a.dtype = g.cache_dtype;
     hipError_t e = cke::launch_xattn_weights(a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(CKE_EDEVICE, "attention-weight launch failed: %s", hipGetErrorString(e));
     return CKE_OK;
@@ -323,7 +328,7 @@ int cross_decode(const float* q, int n_q, const cke_xattn_cache* c, int layer, f
     a.nsplit = c->nsplit;
     a.chunk = c->chunk;
     a.scale = scale;
-    a.bf16 = g.cache_dtype == CKE_BF16;
+    a.dtype = g.cache_dtype;
     // K and V of every layer together: a cache this much larger than the
     // 256 MB MALL is never re-read from it, so its rows are streamed
     a.stream_rows = 2 * region_elems(&g) * elem_bytes(g.cache_dtype) > kStreamCacheBytes;

@@ -19,13 +19,17 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Element storage types: float (fp32) or bf16 held as raw uint16_t bits.
+// Element storage types: float (fp32), bf16 held as raw uint16_t bits, or
+// fp8 E4M3 held as raw uint8_t bits (projection caches only).
 template <typename TE> struct ElemTraits;
 template <> struct ElemTraits<float> {
     static constexpr int kVec = 4;  // elements per 16-byte lane load
 };
 template <> struct ElemTraits<uint16_t> {
     static constexpr int kVec = 8;
+};
+template <> struct ElemTraits<uint8_t> {
+    static constexpr int kVec = 16;
 };
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -38,8 +42,8 @@ __device__ __forceinline__ uint16_t to_bf16_bits(float x) {
 }
 __device__ __forceinline__ float round_to_bf16(float x) { return (float)(__bf16)x; }
 
-// A lane's 16-byte share of a cached row is kept packed in registers (4 fp32
-// or 8 bf16 values) and widened to fp32 only where it is used, so bf16 rows
+// A lane's 16-byte share of a cached row is kept packed in registers (4 fp32,
+// 8 bf16 or 16 fp8 values) and widened to fp32 only where it is used, so bf16 rows
 // cost half the registers of fp32 ones. With STREAM the load is marked
 // non-temporal: right for a cache far larger than the 256 MB MALL, whose rows
 // can never be reused from it (8% faster on the Large 123 MB slab), wrong for
@@ -64,6 +68,31 @@ template <> __device__ __forceinline__ float elem<uint16_t>(const uint4& r, int 
     const uint32_t w = (j >> 1) == 0 ? r.x : ((j >> 1) == 1 ? r.y : ((j >> 1) == 2 ? r.z : r.w));
     return (j & 1) ? bf16_hi(w) : bf16_lo(w);
 }
+// fp8: the hardware converts the two values of one 16-bit half of a word at
+// once (v_cvt_pk_f32_fp8, OCP E4M3 on gfx950); j is a constant after
+// unrolling, so the half select is an immediate and the converted pair is
+// shared by j and j ^ 1.
+template <> __device__ __forceinline__ float elem<uint8_t>(const uint4& r, int j) {
+    const int wi = j >> 2;
+    const int w = (int)(wi == 0 ? r.x : (wi == 1 ? r.y : (wi == 2 ? r.z : r.w)));
+    const auto pr = (j & 2) ? __builtin_amdgcn_cvt_pk_f32_fp8(w, true)
+                            : __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
+    return (j & 1) ? pr[1] : pr[0];
+}
+
+// fp32 -> fp8 E4M3, nearest-even, after clamping to the largest finite value
+// (the hardware conversion turns out-of-range values into NaN). Two values go
+// into the low (HI = false) or high 16 bits of `old`.
+constexpr float kFp8Max = 448.f;
+template <bool HI>
+__device__ __forceinline__ int pack2_fp8(float a, float b, int old) {
+    a = fminf(fmaxf(a, -kFp8Max), kFp8Max);
+    b = fminf(fmaxf(b, -kFp8Max), kFp8Max);
+    return __builtin_amdgcn_cvt_pk_fp8_f32(a, b, old, HI);
+}
+__device__ __forceinline__ uint32_t pack4_fp8(float a, float b, float c, float d) {
+    return (uint32_t)pack2_fp8<true>(c, d, pack2_fp8<false>(a, b, 0));
+}
 
 // The same 16-byte share built from an fp32 source row, rounded to the
 // storage type (the row a self-attention call appends: attention reads the
@@ -79,6 +108,15 @@ template <> __device__ __forceinline__ uint4 pack16_from_f32<uint16_t>(const flo
         return (uint32_t)to_bf16_bits(lo) | ((uint32_t)to_bf16_bits(hi) << 16);
     };
     return make_uint4(pk(a.x, a.y), pk(a.z, a.w), pk(b.x, b.y), pk(b.z, b.w));
+}
+template <> __device__ __forceinline__ uint4 pack16_from_f32<uint8_t>(const float* __restrict__ p) {
+    uint32_t w[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const float4 a = *reinterpret_cast<const float4*>(p + 4 * k);
+        w[k] = pack4_fp8(a.x, a.y, a.z, a.w);
+    }
+    return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
 // Sum over aligned groups of N lanes (N = 1..32) using DPP lane permutes for

@@ -18,7 +18,7 @@ struct XattnLaunch {
     float* part;         // workspace: split partials [B][max_q][H][nsplit][D+2]
     int B, H, T, D, nq, max_q, nsplit, chunk;
     float scale;
-    bool bf16;
+    int dtype;           // CKE_F32, CKE_BF16 or CKE_FP8
     bool stream_rows;    // whole cross cache far larger than the MALL: non-temporal row loads
     float* stats;        // nullptr, or fp32 [B][max_q][H][2]: each head's final (max, sum), base 2
 };
@@ -50,7 +50,7 @@ struct WeightsLaunch {
     HeadList heads;
     int B, H, T, D, nq, max_q;
     float scale;
-    bool bf16;
+    int dtype;           // CKE_F32, CKE_BF16 or CKE_FP8
 };
 
 struct PrefillLaunch {
@@ -83,7 +83,8 @@ struct PopulateLaunch {
     void* Kc;            // [L][B][H][T][D]
     void* Vc;
     int L, B, T, dm, H, D;
-    bool bf16;
+    bool bf16;           // bf16 E and W (else fp32)
+    bool fp8;            // bf16 inputs, fp8 E4M3 cache
 };
 
 // Rows of K/V one decode workgroup covers per pass of all its waves.

@@ -673,6 +673,71 @@ __device__ __forceinline__ void epilogue_t_lds(
     }
 }
 
+// epilogue_t_lds for an fp8 E4M3 cache: each lane's four consecutive columns
+// become one 4-byte word (clamped to +-448, nearest-even), staged as
+// [head j][row m][D] bytes and written to global memory in 16-byte pieces
+// (16 dims of one row). In the staging, the pieces of row m are XOR-swizzled
+// by m % (D/16) and the four words of a piece rotated by XOR with
+// (m >> 2) % 4, so that the 4-byte writes of 32 consecutive rows spread over
+// the banks. `stage` is at least BM*BN bytes, free as for epilogue_t_lds.
+template <int BM, int BN, int WGM, int WGN>
+__device__ __forceinline__ void epilogue_t_lds_fp8(
+    const GemmArgs& a,
+    const f32x16 (&acc)[StreamTile<BM, BN, WGM, WGN>::NB][StreamTile<BM, BN, WGM, WGN>::MB], int m0, int p,
+    int col0, int wm, int wn, int lane, uint8_t* stage)
+{
+    using T = StreamTile<BM, BN, WGM, WGN>;
+    constexpr int NT = T::NT;
+    const int lgD = __builtin_ctz(a.D);
+    const int lgP = lgD - 4;              // log2 of 16-byte pieces per row
+    const int PD = 1 << lgP;
+#pragma unroll
+    for (int nb = 0; nb < T::NB; ++nb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const int n = wn * T::WTN + nb * 32 + 8 * g + 4 * (lane >> 5);
+            const int j = n >> lgD, d = n & (a.D - 1);
+            const int q = d >> 4, wd = (d >> 2) & 3;
+#pragma unroll
+            for (int mb = 0; mb < T::MB; ++mb) {
+                const int m = wm * T::WTM + mb * 32 + (lane & 31);
+                const f32x16& v = acc[nb][mb];
+                const uint32_t w = pack4_fp8(v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]);
+                const int off = ((j * BM + m) << lgD) + ((q ^ (m & (PD - 1))) << 4) +
+                                ((wd ^ ((m >> 2) & 3)) << 2);
+                *reinterpret_cast<uint32_t*>(stage + off) = w;
+            }
+        }
+    __syncthreads();
+    const int l = p < a.L ? p : p - a.L;
+    uint8_t* C = static_cast<uint8_t*>(p < a.L ? a.Kc : a.Vc);
+    const size_t TD = (size_t)a.T * a.D;
+    const int h0 = col0 >> lgD;
+    const int b0 = m0 / a.T, t0 = m0 - b0 * a.T;
+    const int tid = threadIdx.x;
+    constexpr int PIECES = BM * BN / 16;
+#pragma unroll 4
+    for (int id = tid; id < PIECES; id += NT) {
+        const int q = id & (PD - 1);
+        const int m = (id >> lgP) & (BM - 1);
+        const int j = id >> (lgP + 8);    // BM == 256 rows per head block
+        if (m0 + m < a.M) {
+            int t = t0 + m, b = b0;
+            if (t >= a.T) {
+                if (a.T >= BM) { t -= a.T; b += 1; }
+                else { b += t / a.T; t -= (t / a.T) * a.T; }
+            }
+            const int off = ((j * BM + m) << lgD) + ((q ^ (m & (PD - 1))) << 4);
+            uint4 v = *reinterpret_cast<const uint4*>(stage + off);
+            const int r = (m >> 2) & 3;   // word k of the piece sits at k ^ r
+            if (r & 1) { uint32_t x = v.x; v.x = v.y; v.y = x; x = v.z; v.z = v.w; v.w = x; }
+            if (r & 2) { uint32_t x = v.x; v.x = v.z; v.z = x; x = v.y; v.y = v.w; v.w = x; }
+            const size_t idx = ((size_t)(l * a.B + b) * a.H + h0 + j) * TD + (size_t)t * a.D + q * 16;
+            *reinterpret_cast<uint4*>(C + idx) = v;
+        }
+    }
+}
+
 // bf16 populate for gfx950. Four waves (one per SIMD) each own a 128x128
 // block of a 256x256 output tile. The product is formed transposed (W^T as
 // the MFMA A operand, E^T as B) so that each lane ends up with four
@@ -700,9 +765,9 @@ __device__ __forceinline__ void epilogue_t_lds(
 //    with k-tile s-1+NSLOT: NSLOT-2 k-tiles are in flight while one is
 //    multiplied. A thread waits for its own loads with an explicit vmcnt,
 //    the barrier then makes every thread's loads visible;
-//  * the finished tile is staged through the ring (epilogue_t_lds) and
-//    written as whole rows.
-template <int BM, int BN, int NSLOT>
+//  * the finished tile is staged through the ring (epilogue_t_lds, or
+//    epilogue_t_lds_fp8 for an fp8 cache) and written as whole rows.
+template <int BM, int BN, int NSLOT, bool FP8>
 __global__ __launch_bounds__(256) void populate_bf16_w4_kernel(GemmArgs a, int num_m, int num_n)
 {
     static_assert(BM == 256, "the LDS epilogue indexes 256 rows per head block");
@@ -789,7 +854,12 @@ __global__ __launch_bounds__(256) void populate_bf16_w4_kernel(GemmArgs a, int n
     mfma_frags_t<BM, BN, WGM, WGN>(nxt, acc);
     static_assert(NSLOT * sizeof(StreamSlot<BM, BN>) >= BM * BN * 2, "ring too small to stage the tile");
     __syncthreads();
-    epilogue_t_lds<BM, BN, WGM, WGN>(a, acc, m0, p, col0, wm, wn, lane, reinterpret_cast<uint16_t*>(&ring[0]));
+    if constexpr (FP8)
+        epilogue_t_lds_fp8<BM, BN, WGM, WGN>(a, acc, m0, p, col0, wm, wn, lane,
+                                             reinterpret_cast<uint8_t*>(&ring[0]));
+    else
+        epilogue_t_lds<BM, BN, WGM, WGN>(a, acc, m0, p, col0, wm, wn, lane,
+                                         reinterpret_cast<uint16_t*>(&ring[0]));
 }
 
 // fp32 populate for gfx950 on v_mfma_f32_32x32x2_f32: 64x64 output tiles,
@@ -974,15 +1044,15 @@ hipError_t launch_f32_dma(const GemmArgs& g, hipStream_t st) {
     return hipGetLastError();
 }
 
-template <int BM, int BN, int NSLOT>
+template <int BM, int BN, int NSLOT, bool FP8>
 hipError_t launch_bf16_w4(const GemmArgs& g, hipStream_t st) {
     const int HD = g.H * g.D;
     const int num_m = (g.M + BM - 1) / BM;
     const int num_n = 2 * g.L * HD / BN;
     const int ntiles = num_m * num_n;
     const int grid = ((ntiles + 7) / 8) * 8;
-    hipLaunchKernelGGL((populate_bf16_w4_kernel<BM, BN, NSLOT>), dim3(grid), dim3(256), 0, st, g, num_m,
-                       num_n);
+    hipLaunchKernelGGL((populate_bf16_w4_kernel<BM, BN, NSLOT, FP8>), dim3(grid), dim3(256), 0, st, g,
+                       num_m, num_n);
     return hipGetLastError();
 }
 
@@ -1028,7 +1098,11 @@ hipError_t launch_populate(const PopulateLaunch& a, hipStream_t st) {
 #ifndef CKE_POP_W4_SLOTS
 #define CKE_POP_W4_SLOTS 4
 #endif
-    if (a.bf16 && HD % 256 == 0 && a.dm % 32 == 0) return launch_bf16_w4<256, 256, CKE_POP_W4_SLOTS>(g, st);
+    if (a.fp8) {   // only the 256x256 kernel has an fp8 epilogue
+        if (HD % 256 == 0 && a.dm % 32 == 0) return launch_bf16_w4<256, 256, CKE_POP_W4_SLOTS, true>(g, st);
+        return hipErrorInvalidValue;
+    }
+    if (a.bf16 && HD % 256 == 0 && a.dm % 32 == 0) return launch_bf16_w4<256, 256, CKE_POP_W4_SLOTS, false>(g, st);
     if (a.bf16 && HD % 128 == 0 && a.dm % 64 == 0) return launch_bf16_big<128, 128, 64, 2, 2>(g, st);
 #ifndef CKE_POP_F32_DMA
 #define CKE_POP_F32_DMA 3

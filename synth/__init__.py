@@ -47,7 +47,8 @@ class Geometry:
     n_heads: int        # H
     head_dim: int       # D
     scale: float
-    dtype: str          # "f32" or "bf16": cache (and E/W) storage type
+    dtype: str          # cache storage type: "f32", "bf16" or "fp8" (E/W are bf16 for
+                        # both of the latter, fp32 for "f32")
     steps: int          # decode steps in one window
     max_pos: int        # self-attention cache capacity
     seed: int
@@ -70,6 +71,9 @@ CONFIGS = {
                       "bf16", 128, 448, 3),
     "qformer": Geometry("qformer", 100, 3, 0, 2, 15, 2048, 32, 64, 0.125,
                         "f32", 1, 0, 4),
+    # the Large workload over an 8-bit (E4M3) projection cache, same inputs
+    "large_fp8": Geometry("large_fp8", 16, 1, 16, 32, 1500, 1280, 20, 64, 0.125,
+                          "fp8", 128, 448, 3),
 }
 
 # Fixed enumeration of tensor kinds; part of every seed key.
@@ -120,10 +124,11 @@ def q_std(g: Geometry) -> float:
 def workload_tensors(g: Geometry, which=("E", "WK", "WV")) -> dict:
     """Encoder memory and per-layer weights of a workload.
 
-    Returns float32 arrays (exact values) and, for bf16 workloads, the bf16
-    bit patterns under the key ``name + "_bits"``. E is [B][T][d_model];
-    each weight is a list of L arrays [d_model][H*D] (y = x . W orientation).
-    For bf16 workloads the float32 arrays hold the bf16-rounded values.
+    Returns float32 arrays (exact values) and, for bf16 and fp8 workloads
+    (bf16 inputs), the bf16 bit patterns under the key ``name + "_bits"``. E
+    is [B][T][d_model]; each weight is a list of L arrays [d_model][H*D]
+    (y = x . W orientation). For those workloads the float32 arrays hold the
+    bf16-rounded values.
     """
     out = {}
     seed = g.seed
@@ -139,7 +144,7 @@ def workload_tensors(g: Geometry, which=("E", "WK", "WV")) -> dict:
         else:
             out[name] = [normal([seed, tid, l], (g.d_model, g.hd), g.w_std)
                          for l in range(g.n_layers)]
-        if g.dtype == "bf16":
+        if g.dtype in ("bf16", "fp8"):
             if name == "E":
                 bits = to_bf16_bits(out[name])
                 out[name + "_bits"] = bits

@@ -129,6 +129,35 @@ def test_populate_rejects_bad_arguments_before_launch():
         pc.cke_xattn_cache_destroy(h)
 
 
+def test_fp8_cache_geometry_and_populate_checks():
+    """fp8 E4M3 projection caches: one byte per element, populated only from
+    bf16 E and weights, and only at widths n_heads*head_dim that are a
+    multiple of 256; self-attention caches do not take fp8."""
+    g = base_geom(cache_dtype=pc.CKE_FP8)
+    assert pc.cke_xattn_region_bytes(g) == 6 * 1500 * 512
+    assert pc.cke_xattn_layer_offset_bytes(g, 5) == 5 * 1500 * 512
+    L = pc.lib()
+    arr = ctypes.c_void_p * 6
+    ok = arr(*([FAKE] * 6))
+    h = pc.cke_xattn_cache_create(g, FAKE, FAKE, FAKE)
+    try:
+        assert L.cke_xattn_populate(h, FAKE, pc.CKE_F32, ok, ok, pc.CKE_F32, None) == pc.CKE_EINVAL
+        assert L.cke_xattn_populate(h, FAKE, pc.CKE_FP8, ok, ok, pc.CKE_FP8, None) == pc.CKE_EINVAL
+        assert not pc.cke_xattn_is_ready(h)
+    finally:
+        pc.cke_xattn_cache_destroy(h)
+    narrow = base_geom(n_layers=1, d_model=96, n_heads=3, head_dim=32, cache_dtype=pc.CKE_FP8)
+    h = pc.cke_xattn_cache_create(narrow, FAKE, FAKE, FAKE)
+    try:
+        rc = L.cke_xattn_populate(h, FAKE, pc.CKE_BF16, ok, ok, pc.CKE_BF16, None)
+        assert rc == pc.CKE_EINVAL and "256" in pc.cke_last_error()
+    finally:
+        pc.cke_xattn_cache_destroy(h)
+    kv = pc.cke_kv_layer(FAKE, FAKE, 1, 2, 64, 8, pc.CKE_FP8)
+    rc = L.cke_selfattn_decode_append(FAKE, FAKE, FAKE, ctypes.byref(kv), 0, 0.125, FAKE, None)
+    assert rc == pc.CKE_EINVAL
+
+
 def test_create_rejects_null_and_misaligned():
     g = base_geom()
     for k, v, w in ((None, FAKE, FAKE), (FAKE, None, FAKE), (FAKE, FAKE, None),

@@ -5,6 +5,12 @@ the same values. Floating-point outputs must agree within max-abs 1e-4 where
 the cache is fp32 and 2e-2 where it is bf16. Stored cache rows written by the
 self-attention append are compared bit for bit (a copy, or a round-to-nearest
 bf16 conversion of an fp32 value, has exactly one correct result).
+
+fp8 (E4M3) projection caches: a stored value is a rounding decision, taken
+from the kernel's fp32 accumulation, so each stored element must lie between
+the fp8 roundings of (exact - e) and (exact + e), e the fp32 accumulation
+error bound; attention over an fp8 cache is checked on the oracle's own fp8
+cache, uploaded in place of the kernel's, to the fp32 bar of 1e-4.
 """
 import math
 
@@ -44,7 +50,17 @@ def tbf16(bits):
 
 
 def to_np(t):
-    return t.detach().float().cpu().numpy().astype(np.float64)
+    return t.detach().cpu().float().numpy().astype(np.float64)
+
+
+def tfp8(a):
+    """float64 values that are exact fp8 E4M3 numbers -> device fp8 tensor
+    (the conversion of a representable value is exact)."""
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(
+        torch.float8_e4m3fn).to(DEV)
+
+
+CACHE_DT = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.float8_e4m3fn}
 
 
 def geometry(name=None, **kw):
@@ -64,10 +80,9 @@ def geometry(name=None, **kw):
 def make_cache(g, inputs=None):
     """GPU cache populated from the workload's seeded E/WK/WV."""
     wt = inputs or synth.workload_tensors(g)
-    dt = torch.bfloat16 if g.dtype == "bf16" else torch.float32
     cache = pc.XattnCache(g.n_layers, g.n_streams, g.mem_len, g.d_model, g.n_heads, g.head_dim,
-                          max_q=max(g.n_q, 1), dtype=dt)
-    if g.dtype == "bf16":
+                          max_q=max(g.n_q, 1), dtype=CACHE_DT[g.dtype])
+    if g.dtype in ("bf16", "fp8"):
         E = tbf16(wt["E_bits"])
         WK = [tbf16(b) for b in wt["WK_bits"]]
         WV = [tbf16(b) for b in wt["WV_bits"]]
@@ -405,6 +420,106 @@ def test_teacher_forced_decoder_run_matches_oracle(name):
         assert max_abs(to_np(kvs[l].k), run["Ks"][l].astype(np.float32)) == 0.0
 
 
+# ------------------------------------------------------------ fp8 caches
+def fp8_bracket(exact, absdot, dm):
+    """Lowest and highest fp8 values a correct populate may store for the
+    exact products `exact`. The kernel sums dm products of bf16 values, each
+    exact in fp32, in fp32: in any order the sum errs by at most
+    dm * 2^-24 * sum|e w| to first order (doubled here to cover the second);
+    rounding is monotone, so the stored value lies between the roundings of
+    the two ends of that interval."""
+    bound = 2.0 * dm * 2.0 ** -24 * absdot
+    return oracle.round_fp8(exact - bound), oracle.round_fp8(exact + bound)
+
+
+def _abs_products(E, W, H, D):
+    """sum_k |E[b,t,k]| |W[k,n]| as [B][H][T][D]."""
+    B, T, _ = E.shape
+    a = np.abs(np.asarray(E, np.float64)) @ np.abs(np.asarray(W, np.float64))
+    return a.reshape(B, T, H, D).transpose(0, 2, 1, 3)
+
+
+FP8_POP_CASES = [
+    dict(n_layers=2, n_streams=3, mem_len=100, d_model=256, n_heads=8, head_dim=32),
+    dict(n_layers=1, n_streams=2, mem_len=300, d_model=512, n_heads=8, head_dim=64),
+    dict(n_layers=1, n_streams=1, mem_len=257, d_model=256, n_heads=2, head_dim=128),
+    # values past the largest finite fp8 (448) are clamped to it
+    dict(n_layers=1, n_streams=1, mem_len=64, d_model=256, n_heads=4, head_dim=64, e_std=1000.0),
+    # values in the subnormal range (below 2^-6)
+    dict(n_layers=1, n_streams=2, mem_len=40, d_model=256, n_heads=4, head_dim=64, e_std=0.02),
+]
+
+
+@pytest.mark.parametrize("kw", FP8_POP_CASES, ids=lambda x: str(x))
+def test_fp8_populate_rounds_the_exact_products(kw):
+    g = geometry(None, dtype="fp8", **kw)
+    cache, wt, _ = make_cache(g)
+    Kx, Vx = oracle.populate(wt["E"], wt["WK"], wt["WV"], g.n_heads, g.head_dim)
+    flips = 0
+    for l in range(g.n_layers):
+        for got, exact, W in ((cache.k[l], Kx[l], wt["WK"][l]), (cache.v[l], Vx[l], wt["WV"][l])):
+            lo, hi = fp8_bracket(exact, _abs_products(wt["E"], W, g.n_heads, g.head_dim), g.d_model)
+            got = to_np(got)
+            assert np.all(got >= lo) and np.all(got <= hi)
+            flips += int(np.count_nonzero(got != oracle.round_fp8(exact)))
+    # a stored value other than the rounding of the exact product needs the
+    # exact value within the accumulation error of a rounding boundary: rare
+    assert flips <= max(2, 1e-3 * 2 * Kx.size)
+    if kw.get("e_std", 1.0) > 100:
+        assert float(to_np(cache.k).max()) == 448.0 and float(to_np(cache.k).min()) == -448.0
+    assert cache.ready
+
+
+FP8_DEC_CASES = [
+    dict(n_layers=2, n_streams=3, mem_len=1500, d_model=512, n_heads=8, head_dim=64),
+    dict(n_layers=2, n_streams=3, n_q=3, mem_len=77, d_model=256, n_heads=4, head_dim=64),
+    dict(n_layers=1, n_streams=5, n_q=2, mem_len=15, d_model=256, n_heads=2, head_dim=128),
+    dict(n_layers=1, n_streams=2, n_q=8, mem_len=300, d_model=256, n_heads=8, head_dim=32),
+    dict(n_layers=1, n_streams=1, n_q=5, mem_len=3001, d_model=256, n_heads=2, head_dim=128),
+]
+
+
+def _fp8_cache_with_oracle_values(g):
+    """A populated (ready) GPU fp8 cache whose contents are then replaced by
+    the oracle's fp8 cache, so that kernel and oracle attend over identical
+    values."""
+    cache, wt, _ = make_cache(g)
+    Kc, Vc = oracle.populate(wt["E"], wt["WK"], wt["WV"], g.n_heads, g.head_dim, round_fp8=True)
+    cache.k.copy_(tfp8(Kc))
+    cache.v.copy_(tfp8(Vc))
+    torch.cuda.synchronize()
+    return cache, Kc, Vc
+
+
+@pytest.mark.parametrize("kw", FP8_DEC_CASES, ids=lambda x: str(x))
+def test_fp8_cross_decode_matches_oracle(kw):
+    g = geometry(None, dtype="fp8", **kw)
+    cache, Kc, Vc = _fp8_cache_with_oracle_values(g)
+    assert cache.ready
+    for layer in range(g.n_layers):
+        q = synth.decode_call_inputs(g, 1, layer)["q_cross"]
+        out = cache.decode(t32(q), layer, g.scale)
+        torch.cuda.synchronize()
+        want = oracle.cross_decode(q, Kc[layer], Vc[layer], g.scale)
+        assert max_abs(to_np(out), want) <= TOL["f32"], layer
+
+
+@pytest.mark.parametrize("kw,heads", [
+    (dict(n_layers=1, n_streams=2, mem_len=1500, d_model=512, n_heads=8, head_dim=64), [0, 5, 7]),
+    (dict(n_layers=1, n_streams=5, n_q=3, mem_len=15, d_model=256, n_heads=4, head_dim=64), [3]),
+    (dict(n_layers=1, n_streams=2, n_q=2, mem_len=300, d_model=256, n_heads=8, head_dim=32), [1, 1, 6]),
+], ids=lambda x: str(x))
+def test_fp8_cross_decode_weights_match_oracle(kw, heads):
+    g = geometry(None, dtype="fp8", **kw)
+    cache, Kc, Vc = _fp8_cache_with_oracle_values(g)
+    q = synth.decode_call_inputs(g, 2, 0)["q_cross"]
+    out, w = cache.decode_weights(t32(q), 0, g.scale, heads)
+    torch.cuda.synchronize()
+    want_out, want_w = oracle.cross_decode_weights(q, Kc[0], Vc[0], g.scale, heads)
+    assert max_abs(to_np(out), want_out) <= TOL["f32"]
+    assert max_abs(to_np(w), want_w) <= TOL["f32"]
+
+
 # ---------------------------------------------------- full-size workloads
 def _sampled_slabs(g, wt, picks):
     """Oracle slabs for the sampled (layer, stream, head) triples."""
@@ -415,6 +530,37 @@ def _sampled_slabs(g, wt, picks):
         v = oracle.project_head(wt["E"][b], wt["WV"][l], h * g.head_dim, g.head_dim, bf)
         out[(l, b, h)] = (k, v)
     return out
+
+
+def test_full_size_fp8_workload_sampled():
+    """The Large workload over an fp8 cache, as the benchmark times it:
+    populate everything on the GPU; sampled slabs lie in the fp8 bracket of
+    the exact products; decode of the sampled heads, after their slabs are
+    replaced by the oracle's fp8 slabs, matches the oracle to 1e-4."""
+    g = synth.get("large_fp8")
+    cache, wt, _ = make_cache(g)
+    rng = np.random.default_rng(321)
+    picks = [(0, 0, 0), (g.n_layers - 1, g.n_streams - 1, g.n_heads - 1)]
+    for _ in range(3):
+        picks.append((int(rng.integers(g.n_layers)), int(rng.integers(g.n_streams)),
+                      int(rng.integers(g.n_heads))))
+    D = g.head_dim
+    for (l, b, h) in picks:
+        for got, W in ((cache.k[l, b, h], wt["WK"][l]), (cache.v[l, b, h], wt["WV"][l])):
+            Wh = W[:, h * D:(h + 1) * D]
+            exact = oracle.project_head(wt["E"][b], W, h * D, D)
+            absdot = np.abs(wt["E"][b].astype(np.float64)) @ np.abs(Wh.astype(np.float64))
+            lo, hi = fp8_bracket(exact, absdot, g.d_model)
+            got = to_np(got)
+            assert np.all(got >= lo) and np.all(got <= hi), (l, b, h)
+        k = oracle.project_head(wt["E"][b], wt["WK"][l], h * D, D, round_fp8=True)
+        v = oracle.project_head(wt["E"][b], wt["WV"][l], h * D, D, round_fp8=True)
+        cache.k[l, b, h].copy_(tfp8(k))
+        cache.v[l, b, h].copy_(tfp8(v))
+        q = synth.decode_call_inputs(g, 3, l)["q_cross"]
+        out = to_np(cache.decode(t32(q), l, g.scale))
+        want = oracle.attend(q[b, 0, h], k, v, g.scale)
+        assert max_abs(out[b, 0, h], want) <= TOL["f32"], (l, b, h)
 
 
 @pytest.mark.parametrize("name", ["large", "qformer"])
