@@ -59,8 +59,9 @@ enum {
 
 /* Element types. CKE_FP8 is the 8-bit float with 4 exponent and 3 mantissa
  * bits (OCP E4M3: largest finite 448, no infinities), for projection caches
- * only (the compressed cache: decode is bandwidth-bound and reads half the
- * bytes of bf16). */
+ * only: the compressed cache. WhisperKit case study, section 9: compress
+ * where bandwidth is the limit, as it is for decode, which then reads half
+ * the bytes of a bf16 cache. */
 enum { CKE_F32 = 0, CKE_BF16 = 1, CKE_FP8 = 2 };
 
 /* Geometry of one projection cache. Fail-closed: mem_len must be positive and

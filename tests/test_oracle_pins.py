@@ -56,6 +56,47 @@ def test_populate_fp8_stores_rounded_projection():
     np.testing.assert_array_equal(V8, oracle.round_fp8(V0))
 
 
+def _storage_error_bound(q, K, V, K2, V2, scale):
+    """Bound (exact, not first order) on |attend(q, K2, V2) - attend(q, K, V)| per
+    output dim: with every score changed by at most delta = scale *
+    max_t sum_j |q_j| |K2_tj - K_tj|, each weight changes by a factor within
+    [e^-2delta, e^2delta], so the weighted sum moves by at most
+    (e^(2 delta) - 1) * range_t(V2_d) / 2, and replacing V by V2 adds at most
+    max_t |V2_td - V_td|."""
+    delta = scale * np.max(np.abs(K2 - K) @ np.abs(q))
+    spread = (V2.max(axis=0) - V2.min(axis=0)) / 2
+    return (math.exp(2 * delta) - 1) * spread + np.abs(V2 - V).max(axis=0)
+
+
+@pytest.mark.parametrize("dm", [512, 1280])
+def test_fp8_cache_decode_error_within_its_bound(dm):
+    """Tolerance of the compressed cache at the workloads' value spreads (one
+    head, 1500 memory rows, unit-RMS encoder rows, weight std 0.02, bf16
+    inputs): decode over the fp8-rounded (and over the bf16-rounded) cache
+    stays within the bound above of decode over the exact cache, for queries
+    at the projected-row spread and at 4x it (sharper softmax)."""
+    T, D, scale = 1500, 64, 0.125
+    E = synth.bf16_bits_to_f32(synth.to_bf16_bits(synth.normal([900, 0, dm], (1, T, dm))))
+    W = [synth.bf16_bits_to_f32(synth.to_bf16_bits(synth.normal([900, k, dm], (dm, D), 0.02)))
+         for k in (1, 2)]
+    K, V = (oracle.project_head(E[0], w, 0, D) for w in W)
+    K8, V8 = oracle.round_fp8(K), oracle.round_fp8(V)
+    Kb, Vb = oracle.round_bf16(K), oracle.round_bf16(V)
+    worst = {}
+    for spread in (1.0, 4.0):
+        for i in range(4):
+            q = synth.normal([901, i, dm], (D,), 0.02 * math.sqrt(dm) * spread).astype(np.float64)
+            exact = oracle.attend(q, K, V, scale)
+            for name, (K2, V2) in (("fp8", (K8, V8)), ("bf16", (Kb, Vb))):
+                err = np.abs(oracle.attend(q, K2, V2, scale) - exact)
+                assert np.all(err <= _storage_error_bound(q, K, V, K2, V2, scale)), (name, spread, i)
+                worst[(name, spread)] = max(worst.get((name, spread), 0.0), float(err.max()))
+    # the 8-bit cache costs accuracy: its error is well above the bf16 cache's
+    assert worst[("fp8", 1.0)] > 4 * worst[("bf16", 1.0)]
+    print("decode max-abs error vs exact cache, d_model %d:" % dm,
+          {"%s@%gx" % k: "%.2e" % v for k, v in worst.items()})
+
+
 # ----------------------------------------------------------------- bf16 rounding
 def test_round_bf16_matches_torch_cast():
     """Pinned to torch's float32 -> bfloat16 cast (round to nearest even)."""
