@@ -69,6 +69,8 @@ def lib():
         L.orc_cross_decode_weights.argtypes = [_I] * 5 + [_D, _P, _P, _P, _P, _I, _P, _P]
         L.orc_matvec.argtypes = [_I, _I, _P, _P, _P]
         L.orc_rms_feedback.argtypes = [_I, _P, _P]
+        L.orc_decoder_layer_step.restype = _I
+        L.orc_decoder_layer_step.argtypes = [_I] * 8 + [_D, _I] + [_P] * 17
         L.orc_decoder_run.restype = _I
         L.orc_decoder_run.argtypes = ([_I] * 10 + [_D, _I] + [_P] * 10 +
                                       [_P] * 7 + [_P] * 4)
@@ -230,6 +232,34 @@ def matvec(x, W) -> np.ndarray:
     y = np.empty(W.shape[1], dtype=np.float64)
     lib().orc_matvec(W.shape[0], W.shape[1], _ptr(x), _ptr(W), _ptr(y))
     return y
+
+
+def decoder_layer_step(x, W: dict, Kc, Vc, Ks, Vs, pos: int, *, n_q: int, scale: float,
+                       round_bf16: bool = False, records: bool = False):
+    """One harness-decoder layer for one token of each of S sequences.
+
+    x [S][dm] (returned updated, the input is not modified); W holds this
+    layer's [dm][dm] weights under WQs, WKs, WVs, WOs, WQ, WO; Kc, Vc are the
+    layer's projection-cache slab [B][H][T][D] (sequence s reads stream
+    s // n_q); Ks, Vs [S][H][max_pos][D] are this layer's self caches,
+    updated in place (row pos written, rounded to bf16 if asked). With
+    records, also returns the per-call values (qs, kn, vn, so, qc, co).
+    """
+    x = _f64(x).copy()
+    S, dm = x.shape
+    Kc, Vc = _f64(Kc), _f64(Vc)
+    B, H, T, D = Kc.shape
+    assert Ks.dtype == np.float64 and Ks.flags.c_contiguous and Vs.flags.c_contiguous
+    max_pos = Ks.shape[2]
+    Ws = [_f64(W[k]) for k in ("WQs", "WKs", "WVs", "WOs", "WQ", "WO")]
+    rec = {k: np.zeros((S, dm)) for k in ("qs", "kn", "vn", "so", "qc", "co")}
+    rc = lib().orc_decoder_layer_step(S, n_q, T, dm, H, D, max_pos, int(pos), float(scale),
+                                      int(round_bf16), _ptr(x), *[_ptr(w) for w in Ws],
+                                      _ptr(Kc), _ptr(Vc), _ptr(Ks), _ptr(Vs),
+                                      *[_ptr(rec[k]) for k in ("qs", "kn", "vn", "so", "qc", "co")])
+    if rc != 0:
+        raise ValueError("orc_decoder_layer_step rejected its geometry")
+    return (x, rec) if records else x
 
 
 def decoder_run(mode: str, E, W: dict, x0, *, n_heads: int, head_dim: int,

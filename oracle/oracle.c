@@ -408,6 +408,68 @@ void orc_rms_feedback(int dm, const double* x, double* y)
 }
 
 /*
+ * One decoder layer for one token of each of S = B*nq sequences, the body of
+ * the harness decoder above: x ([S][dm]) is updated in place, the self-
+ * attention row pos of every (sequence, head) is written into Ks, Vs
+ * ([S][H][max_pos][D], rounded to bf16 when round_bf16), and sequence s
+ * reads stream s / nq of the layer's projection-cache slab Kc, Vc
+ * ([B][H][T][D]). Weights are [dm][dm] (y = x.W). rec_* ([S][dm], nullable)
+ * receive the self query, new key, new value, self-attention output, cross
+ * query and cross-attention output. Returns -1 for a bad geometry.
+ */
+int orc_decoder_layer_step(int S, int nq, int T, int dm, int H, int D,
+                           int max_pos, int pos, double scale, int round_bf16,
+                           double* x, const double* WQs, const double* WKs,
+                           const double* WVs, const double* WOs,
+                           const double* WQ, const double* WO,
+                           const double* Kc, const double* Vc, double* Ks,
+                           double* Vs, double* rec_qs, double* rec_kn,
+                           double* rec_vn, double* rec_so, double* rec_qc,
+                           double* rec_co)
+{
+    if (H * D != dm || T <= 0 || nq <= 0 || S % nq != 0 || pos < 0 || pos >= max_pos)
+        return -1;
+    double* qs = (double*)malloc(sizeof(double) * (size_t)dm);
+    double* ks = (double*)malloc(sizeof(double) * (size_t)dm);
+    double* vs = (double*)malloc(sizeof(double) * (size_t)dm);
+    double* so = (double*)malloc(sizeof(double) * (size_t)dm);
+    double* qc = (double*)malloc(sizeof(double) * (size_t)dm);
+    double* co = (double*)malloc(sizeof(double) * (size_t)dm);
+    double* sc = (double*)malloc(sizeof(double) * (size_t)(T > max_pos ? T : max_pos));
+    for (int s = 0; s < S; ++s) {
+        const int b = s / nq;
+        double* xr = x + (size_t)s * dm;
+        matvec(dm, dm, xr, WQs, qs);
+        matvec(dm, dm, xr, WKs, ks);
+        matvec(dm, dm, xr, WVs, vs);
+        for (int h = 0; h < H; ++h) {
+            double* kh = Ks + (((size_t)s * H + h) * max_pos) * D;
+            double* vh = Vs + (((size_t)s * H + h) * max_pos) * D;
+            for (int d = 0; d < D; ++d) {
+                kh[(size_t)pos * D + d] = round_bf16 ? orc_round_bf16(ks[h * D + d]) : ks[h * D + d];
+                vh[(size_t)pos * D + d] = round_bf16 ? orc_round_bf16(vs[h * D + d]) : vs[h * D + d];
+            }
+            attend_one(pos + 1, D, scale, qs + h * D, kh, vh, so + h * D, sc);
+        }
+        add_matvec(dm, so, WOs, xr);
+        matvec(dm, dm, xr, WQ, qc);
+        for (int h = 0; h < H; ++h) {
+            const size_t slab = (((size_t)b * H + h) * T) * D;
+            attend_one(T, D, scale, qc + h * D, Kc + slab, Vc + slab, co + h * D, sc);
+        }
+        add_matvec(dm, co, WO, xr);
+        if (rec_qs) memcpy(rec_qs + (size_t)s * dm, qs, sizeof(double) * dm);
+        if (rec_kn) memcpy(rec_kn + (size_t)s * dm, ks, sizeof(double) * dm);
+        if (rec_vn) memcpy(rec_vn + (size_t)s * dm, vs, sizeof(double) * dm);
+        if (rec_so) memcpy(rec_so + (size_t)s * dm, so, sizeof(double) * dm);
+        if (rec_qc) memcpy(rec_qc + (size_t)s * dm, qc, sizeof(double) * dm);
+        if (rec_co) memcpy(rec_co + (size_t)s * dm, co, sizeof(double) * dm);
+    }
+    free(qs); free(ks); free(vs); free(so); free(qc); free(co); free(sc);
+    return 0;
+}
+
+/*
  * Record layout (each nullable): rec_* are [n_steps][L][S][dm] holding, per
  * step and layer, the self query, new key, new value, self-attention output,
  * cross query and cross-attention output. x_seq is [n_steps+1][S][dm].
@@ -439,10 +501,7 @@ int orc_decoder_run(int mode, int L, int B, int nq, int T, int dm, int H,
     const size_t cross_n = (size_t)L * B * H * T * D;
     const size_t self_n = (size_t)L * S * H * max_pos * D;
     double* xs = (double*)calloc((size_t)(n_steps + 1) * S * dm, sizeof(double));
-    double* xc = (double*)malloc(sizeof(double) * (size_t)dm);
     double* qs = (double*)malloc(sizeof(double) * (size_t)dm);
-    double* ks = (double*)malloc(sizeof(double) * (size_t)dm);
-    double* vs = (double*)malloc(sizeof(double) * (size_t)dm);
     double* so = (double*)malloc(sizeof(double) * (size_t)dm);
     double* qc = (double*)malloc(sizeof(double) * (size_t)dm);
     double* co = (double*)malloc(sizeof(double) * (size_t)dm);
@@ -469,41 +528,27 @@ int orc_decoder_run(int mode, int L, int B, int nq, int T, int dm, int H,
                                      WV + l * ws, dm, h * D, round_bf16,
                                      vc + XC(l, b, h));
                 }
+        /* every step runs the layers in order, each as one layer step over
+         * all sequences; the sequences' hidden states live in xt */
+        double* xt = (double*)malloc(sizeof(double) * (size_t)S * dm);
         for (int t = 0; t < n_steps; ++t) {
-            for (int s = 0; s < S; ++s) {
-                const int b = s / nq;
-                memcpy(xc, xs + ((size_t)t * S + s) * dm, sizeof(double) * dm);
-                for (int l = 0; l < L; ++l) {
-                    matvec(dm, dm, xc, WQs + l * ws, qs);
-                    matvec(dm, dm, xc, WKs + l * ws, ks);
-                    matvec(dm, dm, xc, WVs + l * ws, vs);
-                    for (int h = 0; h < H; ++h) {
-                        double* krow = kself + XS(l, s, h) + (size_t)t * D;
-                        double* vrow = vself + XS(l, s, h) + (size_t)t * D;
-                        for (int d = 0; d < D; ++d) {
-                            krow[d] = round_bf16 ? orc_round_bf16(ks[h * D + d]) : ks[h * D + d];
-                            vrow[d] = round_bf16 ? orc_round_bf16(vs[h * D + d]) : vs[h * D + d];
-                        }
-                        attend_one(t + 1, D, scale, qs + h * D,
-                                   kself + XS(l, s, h), vself + XS(l, s, h),
-                                   so + h * D, sc);
-                    }
-                    if (rec_qs) memcpy(REC(rec_qs, t, l, s), qs, sizeof(double) * dm);
-                    if (rec_kn) memcpy(REC(rec_kn, t, l, s), ks, sizeof(double) * dm);
-                    if (rec_vn) memcpy(REC(rec_vn, t, l, s), vs, sizeof(double) * dm);
-                    if (rec_so) memcpy(REC(rec_so, t, l, s), so, sizeof(double) * dm);
-                    add_matvec(dm, so, WOs + l * ws, xc);
-                    matvec(dm, dm, xc, WQ + l * ws, qc);
-                    for (int h = 0; h < H; ++h)
-                        attend_one(T, D, scale, qc + h * D, kc + XC(l, b, h),
-                                   vc + XC(l, b, h), co + h * D, sc);
-                    if (rec_qc) memcpy(REC(rec_qc, t, l, s), qc, sizeof(double) * dm);
-                    if (rec_co) memcpy(REC(rec_co, t, l, s), co, sizeof(double) * dm);
-                    add_matvec(dm, co, WO + l * ws, xc);
-                }
-                rms_feedback(dm, xc, xs + ((size_t)(t + 1) * S + s) * dm);
-            }
+            memcpy(xt, xs + (size_t)t * S * dm, sizeof(double) * (size_t)S * dm);
+            for (int l = 0; l < L; ++l)
+                orc_decoder_layer_step(S, nq, T, dm, H, D, max_pos, t, scale, round_bf16, xt,
+                                       WQs + l * ws, WKs + l * ws, WVs + l * ws, WOs + l * ws,
+                                       WQ + l * ws, WO + l * ws, kc + XC(l, 0, 0),
+                                       vc + XC(l, 0, 0), kself + XS(l, 0, 0),
+                                       vself + XS(l, 0, 0),
+                                       rec_qs ? REC(rec_qs, t, l, 0) : NULL,
+                                       rec_kn ? REC(rec_kn, t, l, 0) : NULL,
+                                       rec_vn ? REC(rec_vn, t, l, 0) : NULL,
+                                       rec_so ? REC(rec_so, t, l, 0) : NULL,
+                                       rec_qc ? REC(rec_qc, t, l, 0) : NULL,
+                                       rec_co ? REC(rec_co, t, l, 0) : NULL);
+            for (int s = 0; s < S; ++s)
+                rms_feedback(dm, xt + (size_t)s * dm, xs + ((size_t)(t + 1) * S + s) * dm);
         }
+        free(xt);
     } else {
         /* Full-window recompute, no cache carried between steps. */
         double* hid = (double*)malloc(sizeof(double) * (size_t)max_pos * dm);
@@ -596,7 +641,7 @@ int orc_decoder_run(int mode, int L, int B, int nq, int T, int dm, int H,
 #undef REC
 #undef XC
 #undef XS
-    free(xs); free(xc); free(qs); free(ks); free(vs); free(so); free(qc);
+    free(xs); free(qs); free(so); free(qc);
     free(co); free(sc); free(kc); free(vc); free(kself); free(vself);
     return 0;
 }

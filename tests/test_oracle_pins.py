@@ -515,6 +515,90 @@ def test_harness_records_are_consistent_with_call_level_functions():
             np.testing.assert_array_equal(co.reshape(g.n_seqs, -1), rec["co"][t, l])
 
 
+def _torch_layer_step(x, W, Kc, Vc, Ks, Vs, pos, nq, scale, round_bf16):
+    """The harness decoder layer written with torch float64 matmuls and SDPA:
+    causal self-attention over rows 0..pos of the self cache (row pos from
+    this token), then cross-attention over stream s // nq of the slab."""
+    F = torch.nn.functional
+    S, dm = x.shape
+    B, H, T, D = Kc.shape
+    t = lambda a: torch.from_numpy(np.asarray(a, np.float64))
+    xt = t(x)
+    heads = lambda a: a.reshape(S, H, 1, D)
+    q, k, v = (xt @ t(W[n]) for n in ("WQs", "WKs", "WVs"))
+    rd = (lambda a: t(oracle.round_bf16(a.numpy()))) if round_bf16 else (lambda a: a)
+    Kself = t(Ks).clone()
+    Vself = t(Vs).clone()
+    Kself[:, :, pos] = rd(k).reshape(S, H, D)
+    Vself[:, :, pos] = rd(v).reshape(S, H, D)
+    so = F.scaled_dot_product_attention(heads(q), Kself[:, :, :pos + 1], Vself[:, :, :pos + 1],
+                                        scale=scale)
+    x1 = xt + so.reshape(S, dm) @ t(W["WOs"])
+    qc = x1 @ t(W["WQ"])
+    b = torch.arange(S) // nq
+    co = F.scaled_dot_product_attention(heads(qc), t(Kc)[b], t(Vc)[b], scale=scale)
+    return (x1 + co.reshape(S, dm) @ t(W["WO"])).numpy(), Kself.numpy(), Vself.numpy()
+
+
+@pytest.mark.parametrize("cfg", [
+    dict(B=1, nq=1, T=40, H=2, D=16, pos=0, bf16=False),
+    dict(B=1, nq=3, T=25, H=4, D=8, pos=5, bf16=False),
+    dict(B=2, nq=2, T=17, H=2, D=16, pos=9, bf16=True),
+])
+def test_decoder_layer_step_matches_torch_composition(cfg):
+    """One decoder layer (self-attention residual, then cross-attention
+    residual: [CKE] 'The concept' decoder-body order) against torch float64
+    matmul + SDPA; the self row pos is written, other rows untouched. At
+    pos = 0 the self output is the new value row itself."""
+    r = rng(70 + cfg["pos"])
+    H, D, B, nq, T, pos = cfg["H"], cfg["D"], cfg["B"], cfg["nq"], cfg["T"], cfg["pos"]
+    dm, S, max_pos = H * D, B * nq, 12
+    W = {k: r.standard_normal((dm, dm)) * 0.2 for k in ("WQs", "WKs", "WVs", "WOs", "WQ", "WO")}
+    Kc, Vc = r.standard_normal((2, B, H, T, D))
+    Ks = r.standard_normal((S, H, max_pos, D))
+    Vs = r.standard_normal((S, H, max_pos, D))
+    if cfg["bf16"]:
+        Ks, Vs = oracle.round_bf16(Ks), oracle.round_bf16(Vs)
+    x = r.standard_normal((S, dm))
+    want_x, want_K, want_V = _torch_layer_step(x, W, Kc, Vc, Ks, Vs, pos, nq, 0.3, cfg["bf16"])
+    K0, V0 = Ks.copy(), Vs.copy()
+    got, rec = oracle.decoder_layer_step(x, W, Kc, Vc, Ks, Vs, pos, n_q=nq, scale=0.3,
+                                         round_bf16=cfg["bf16"], records=True)
+    np.testing.assert_allclose(got, want_x, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(Ks, want_K, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(Vs, want_V, rtol=0, atol=1e-13)
+    others = np.arange(max_pos) != pos
+    np.testing.assert_array_equal(Ks[:, :, others], K0[:, :, others])
+    if pos == 0:
+        np.testing.assert_allclose(rec["so"], rec["vn"], rtol=0, atol=1e-15)
+
+
+def test_decoder_layer_steps_reproduce_the_decoder_run():
+    """Running the layer step layer by layer, token by token, with the rms
+    feedback between tokens (here in numpy, so agreement is to rounding),
+    gives the harness decoder's run."""
+    g = synth.get("tiny")
+    L, dm, H, D = 2, 64, 2, 32
+    r = rng(71)
+    E = r.standard_normal((1, 30, dm))
+    W = _harness_weights(72, L, dm)
+    x0 = r.standard_normal((1, dm))
+    kw = dict(n_heads=H, head_dim=D, n_q=1, max_pos=6, n_steps=6, scale=g.scale)
+    run = oracle.decoder_run("incremental", E, W, x0, **kw)
+    Kc, Vc = oracle.populate(E, W["WK"], W["WV"], H, D)
+    Ks = np.zeros((L, 1, H, 6, D))
+    Vs = np.zeros_like(Ks)
+    x = x0.copy()
+    for t in range(6):
+        for l in range(L):
+            Wl = {k: W[k][l] for k in ("WQs", "WKs", "WVs", "WOs", "WQ", "WO")}
+            x = oracle.decoder_layer_step(x, Wl, Kc[l], Vc[l], Ks[l], Vs[l], t, n_q=1,
+                                          scale=g.scale)
+        x = x / np.sqrt(np.mean(x * x, axis=1, keepdims=True))
+        np.testing.assert_allclose(x, run["x"][t + 1], rtol=0, atol=1e-14)
+    np.testing.assert_allclose(Ks, run["Ks"], rtol=0, atol=1e-14)
+
+
 def test_thread_count_does_not_change_bits():
     r = rng(15)
     E = r.standard_normal((2, 33, 32))
