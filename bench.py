@@ -356,6 +356,86 @@ def measure_weights(torch, pc, w, stream):
             "extra_us": (t_w - t_d) * 1e6}
 
 
+def measure_decoder_step(torch, pc, w, stream, tokens=4):
+    """Time cke_decoder_layer_step at the workload's shape: a HIP graph of
+    `tokens` decode tokens x all layers (one call per layer, positions
+    0..tokens-1) over the workload's populated cache, with random weights of
+    the layer shape (fp32 or bf16 as the workload's inputs). For fp32 weights
+    the same layer is also timed as the composition of separate calls (torch
+    matmuls for the six products, the library's self and cross calls, torch
+    residual adds), for comparison."""
+    g = w.g
+    S = g.n_streams * g.n_q
+    if not g.n_seqs or g.n_seqs != S:
+        return None
+    L, dm = g.n_layers, g.d_model
+    wdt = torch.bfloat16 if w.bf16 else torch.float32
+    gen = torch.Generator(device="cuda").manual_seed(11)
+    Wd = [[(torch.randn(dm, dm, device="cuda", generator=gen) * 0.02).to(wdt) for _ in range(6)]
+          for _ in range(L)]
+    descs = [pc.decoder_layer_desc(*Wl) for Wl in Wd]
+    kvs = [pc.KVLayer(S, g.n_heads, g.head_dim, g.max_pos, dtype=wdt) for _ in range(L)]
+    ws = torch.empty(pc.cke_decoder_step_workspace_bytes(w.cache.geom, S) // 4, device="cuda")
+    x = torch.randn(S, dm, device="cuda", generator=gen)
+
+    def graph_time(fn):
+        with torch.cuda.stream(stream):
+            fn()
+        stream.synchronize()
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr, stream=stream):
+            fn()
+        torch.cuda.synchronize()
+        best = float("inf")
+        for _ in range(3):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            with torch.cuda.stream(stream):
+                gr.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            best = min(best, e0.elapsed_time(e1) * 1e-3)
+        return best
+
+    cs = torch.cuda.current_stream
+
+    def fused():
+        for t in range(tokens):
+            for l in range(L):
+                pc.cke_decoder_layer_step(x, descs[l], kvs[l], t, w.cache, l, g.scale, ws,
+                                          stream=cs())
+    t_f = graph_time(fused) / (tokens * L)
+    welem = 2 if w.bf16 else 4
+    slab = 2 * g.n_streams * g.n_heads * g.mem_len * g.head_dim * w.cache_elem
+    self_rows = 2 * S * g.n_heads * ((tokens + 1) / 2) * g.head_dim * welem
+    by = 6 * dm * dm * welem + slab + self_rows + 12 * S * dm * 4
+    res = {"seqs": S, "layers": L, "tokens": tokens, "avg_us_per_layer": t_f * 1e6,
+           "tokens_per_s": S / (t_f * L), "bytes_per_layer": by, "GB_s": by / t_f / 1e9,
+           "launches_per_layer": 6 if w.cache.n_splits == 1 else 7}
+    if not w.bf16:
+        H, D = g.n_heads, g.head_dim
+        q, k, v, so, x1, qc, co = (torch.empty(S, dm, device="cuda") for _ in range(7))
+
+        def composed():
+            for t in range(tokens):
+                for l in range(L):
+                    WQs, WKs, WVs, WOs, WQ, WO = Wd[l]
+                    torch.mm(x, WQs, out=q)
+                    torch.mm(x, WKs, out=k)
+                    torch.mm(x, WVs, out=v)
+                    pc.cke_selfattn_decode_append(q, k, v, kvs[l], t, g.scale, so, stream=cs())
+                    torch.addmm(x, so, WOs, out=x1)
+                    torch.mm(x1, WQ, out=qc)
+                    pc.cke_xattn_decode(qc.view(g.n_streams, g.n_q, H, D), w.cache, l, g.scale,
+                                        co, stream=cs())
+                    torch.addmm(x1, co, WO, out=x)
+        t_c = graph_time(composed) / (tokens * L)
+        res["composed_us_per_layer"] = t_c * 1e6
+        res["speedup_vs_composed"] = t_c / t_f
+    return res
+
+
 def _host_cpu():
     try:
         for line in open("/proc/cpuinfo"):
@@ -521,6 +601,9 @@ def main():
         "git": _git_sha(),
     }
     result["xattn_decode_weights"] = measure_weights(torch, pc, w, stream)
+    step = measure_decoder_step(torch, pc, w, stream)
+    if step:
+        result["decoder_layer_step"] = step
     prefill = measure_prefill(torch, pc, g, stream)
     if prefill:
         result["selfattn_prefill"] = prefill

@@ -203,6 +203,45 @@ int cke_selfattn_prefill_append(const float* q, const float* k_new,
                                 int pos, int n_new, int n_q_heads, float scale,
                                 float* out, void* stream);
 
+/* One decoder layer's projection weights, each [d_model][d_model] in the
+ * y = x . W orientation, device memory of w dtype (CKE_F32 or CKE_BF16),
+ * 16-byte aligned. */
+typedef struct cke_decoder_layer {
+    const void* wq_self;   /* self-attention query, key, value, output */
+    const void* wk_self;
+    const void* wv_self;
+    const void* wo_self;
+    const void* wq_cross;  /* cross-attention query and output */
+    const void* wo_cross;
+    int32_t dtype;
+} cke_decoder_layer;
+
+/* Bytes of device workspace cke_decoder_layer_step needs for n_seqs
+ * sequences: seven fp32 [n_seqs][d_model] buffers. 0 if invalid. */
+size_t cke_decoder_step_workspace_bytes(const cke_xattn_geom* g, int n_seqs);
+
+/* One decoder layer for one token of each of S = kv->n_seqs sequences, in the
+ * decoder-body order of the C-Kernel-Engine page, "The concept" (self-
+ * attention, then cross-attention whose queries come from the decoder and
+ * whose keys and values come from the projection cache of this layer; the
+ * MLP and norms have no weights in these workloads and are not part of it):
+ *   x += SelfAttn(x.WQs, x.WKs, x.WVs; kv, pos) . WOs
+ *   x += CrossAttn(x.WQ; slab `layer` of c) . WO
+ * SelfAttn is cke_selfattn_decode_append (row pos of kv written, rows 0..pos
+ * attended); CrossAttn is cke_xattn_decode with n_q = S / n_streams, sequence
+ * s being query s % n_q of stream s / n_q. Products accumulate in fp32 from
+ * fp32 or bf16 weights.
+ *   x      device fp32 [S][d_model], updated in place
+ *   kv     this layer's self cache: n_heads and head_dim equal the cache's
+ *   ws     device, cke_decoder_step_workspace_bytes(geometry of c, S) bytes,
+ *          256-byte aligned; needs no initialisation
+ * Uses c's workspace too, so calls on one cache must be ordered on one
+ * stream. Errors: CKE_ENOTREADY if c is not populated; CKE_ERANGE for layer,
+ * pos, or S not n_streams x n_q with n_q <= max_q; CKE_EINVAL otherwise. */
+int cke_decoder_layer_step(float* x, const cke_decoder_layer* w, const cke_kv_layer* kv,
+                           int pos, const cke_xattn_cache* c, int layer, float scale,
+                           void* ws, void* stream);
+
 /* Message for the last non-OK status returned on this thread. */
 const char* cke_last_error(void);
 

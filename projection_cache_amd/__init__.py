@@ -49,6 +49,13 @@ class cke_kv_layer(ctypes.Structure):
                 ("dtype", ctypes.c_int32)]
 
 
+class cke_decoder_layer(ctypes.Structure):
+    _fields_ = [("wq_self", ctypes.c_void_p), ("wk_self", ctypes.c_void_p),
+                ("wv_self", ctypes.c_void_p), ("wo_self", ctypes.c_void_p),
+                ("wq_cross", ctypes.c_void_p), ("wo_cross", ctypes.c_void_p),
+                ("dtype", ctypes.c_int32)]
+
+
 _P, _I, _F, _SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
 _lib = ctypes.CDLL(LIB_PATH)
 _lib.cke_last_error.restype = ctypes.c_char_p
@@ -83,12 +90,18 @@ _lib.cke_xattn_decode_weights.argtypes = [_P, _I, _P, _I, _F, ctypes.POINTER(cty
 _lib.cke_selfattn_prefill_append.restype = _I
 _lib.cke_selfattn_prefill_append.argtypes = [_P, _P, _P, ctypes.POINTER(cke_kv_layer), _I, _I, _I,
                                              _F, _P, _P]
+_lib.cke_decoder_step_workspace_bytes.restype = _SZ
+_lib.cke_decoder_step_workspace_bytes.argtypes = [ctypes.POINTER(cke_xattn_geom), _I]
+_lib.cke_decoder_layer_step.restype = _I
+_lib.cke_decoder_layer_step.argtypes = [_P, ctypes.POINTER(cke_decoder_layer),
+                                        ctypes.POINTER(cke_kv_layer), _I, _P, _I, _F, _P, _P]
 
 EXPORTED = ["cke_xattn_region_bytes", "cke_xattn_layer_offset_bytes",
             "cke_xattn_workspace_bytes", "cke_xattn_num_splits", "cke_xattn_cache_create",
             "cke_xattn_cache_destroy", "cke_xattn_invalidate", "cke_xattn_is_ready",
             "cke_xattn_populate", "cke_xattn_decode", "cke_selfattn_decode_append",
-            "cke_selfattn_prefill_append", "cke_xattn_decode_weights", "cke_last_error",
+            "cke_selfattn_prefill_append", "cke_xattn_decode_weights",
+            "cke_decoder_step_workspace_bytes", "cke_decoder_layer_step", "cke_last_error",
             "cke_version"]
 
 
@@ -231,6 +244,31 @@ def cke_selfattn_decode_append(q, k_new, v_new, kv, pos: int, scale: float, out,
     desc = kv.desc if isinstance(kv, KVLayer) else kv
     _check(_lib.cke_selfattn_decode_append(_ptr(q), _ptr(k_new), _ptr(v_new), ctypes.byref(desc),
                                            int(pos), float(scale), _ptr(out), _stream(stream)))
+
+
+def cke_decoder_step_workspace_bytes(g: cke_xattn_geom, n_seqs: int) -> int:
+    return int(_lib.cke_decoder_step_workspace_bytes(ctypes.byref(g), int(n_seqs)))
+
+
+def decoder_layer_desc(WQs, WKs, WVs, WOs, WQ, WO) -> cke_decoder_layer:
+    """Descriptor of one layer's six [d_model][d_model] device weights (one
+    dtype, fp32 or bf16). The tensors must outlive every call that uses it."""
+    ws = (WQs, WKs, WVs, WOs, WQ, WO)
+    dt = {w.dtype for w in ws}
+    if len(dt) != 1:
+        raise ValueError("decoder weights must share one dtype")
+    return cke_decoder_layer(*[_ptr(w) for w in ws], _DTYPES[dt.pop()])
+
+
+def cke_decoder_layer_step(x, w, kv, pos: int, cache, layer: int, scale: float, ws,
+                           stream=None) -> None:
+    """One decoder layer for one token per sequence: x [S][d_model] fp32 is
+    updated in place (self-attention residual, then cross-attention residual
+    over `cache` slab `layer`); w is a cke_decoder_layer, kv a KVLayer."""
+    desc = kv.desc if isinstance(kv, KVLayer) else kv
+    _check(_lib.cke_decoder_layer_step(_ptr(x), ctypes.byref(w), ctypes.byref(desc), int(pos),
+                                       _handle(cache), int(layer), float(scale), _ptr(ws),
+                                       _stream(stream)))
 
 
 class XattnCache:

@@ -421,3 +421,138 @@ int cke_selfattn_prefill_append(const float* q, const float* k_new, const float*
 }
 
 }  // extern "C"
+
+namespace {
+
+// Decoder-step workspace: seven fp32 [S][d_model] buffers, each 256-byte
+// aligned: self q, k, v, self output, hidden state after the self residual,
+// cross q, cross output.
+constexpr int kStepBuffers = 7;
+
+size_t step_buffer_bytes(const cke_xattn_geom* g, int n_seqs) {
+    const size_t b = (size_t)n_seqs * g->d_model * sizeof(float);
+    return (b + kAlign - 1) / kAlign * kAlign;
+}
+
+hipError_t gemv(const float* X, int n_out, const void* const* W, float* const* Y,
+                const float* const* R, int S, int dm, bool bf16, hipStream_t st) {
+    cke::GemvLaunch a;
+    std::memset(&a, 0, sizeof(a));
+    a.X = X;
+    a.n_out = n_out;
+    for (int i = 0; i < n_out; ++i) a.o[i] = cke::GemvOut{W[i], Y[i], R ? R[i] : nullptr};
+    for (int i = n_out; i < 3; ++i) a.o[i] = a.o[0];
+    a.S = S;
+    a.K = dm;
+    a.N = dm;
+    a.bf16 = bf16;
+    return cke::launch_gemv(a, st);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t cke_decoder_step_workspace_bytes(const cke_xattn_geom* g, int n_seqs) {
+    if (check_geom(g) != CKE_OK) return 0;
+    if (n_seqs < 1 || n_seqs > 65535) {
+        fail(CKE_EINVAL, "n_seqs must be in [1, 65535] (got %d)", n_seqs);
+        return 0;
+    }
+    return kStepBuffers * step_buffer_bytes(g, n_seqs);
+}
+
+int cke_decoder_layer_step(float* x, const cke_decoder_layer* w, const cke_kv_layer* kv, int pos,
+                           const cke_xattn_cache* c, int layer, float scale, void* ws,
+                           void* stream) {
+    if (!c) return fail(CKE_EINVAL, "cache handle is NULL");
+    const cke_xattn_geom& g = c->g;
+    if (layer < 0 || layer >= g.n_layers)
+        return fail(CKE_ERANGE, "layer %d outside [0, %d)", layer, g.n_layers);
+    if (!c->ready)
+        return fail(CKE_ENOTREADY, "projection cache is not populated for the current encoder memory");
+    if (!w || !kv) return fail(CKE_EINVAL, "weights and kv layer descriptors must be non-NULL");
+    const void* W[6] = {w->wq_self, w->wk_self, w->wv_self, w->wo_self, w->wq_cross, w->wo_cross};
+    for (int i = 0; i < 6; ++i)
+        if (!W[i] || !aligned16(W[i])) return fail(CKE_EINVAL, "weight %d is NULL or not 16-byte aligned", i);
+    if (!dtype_ok(w->dtype)) return fail(CKE_EINVAL, "unknown weight dtype %d", w->dtype);
+    if (!kv->k || !kv->v || !aligned16(kv->k) || !aligned16(kv->v))
+        return fail(CKE_EINVAL, "kv->k and kv->v must be non-NULL and 16-byte aligned");
+    if (!dtype_ok(kv->dtype)) return fail(CKE_EINVAL, "unknown kv dtype %d", kv->dtype);
+    if (kv->n_heads != g.n_heads || kv->head_dim != g.head_dim)
+        return fail(CKE_EINVAL, "kv heads x head_dim (%d x %d) must match the cache's (%d x %d)",
+                    kv->n_heads, kv->head_dim, g.n_heads, g.head_dim);
+    if (kv->n_seqs < 1 || kv->n_seqs > 65535 || kv->max_pos < 1)
+        return fail(CKE_EINVAL, "n_seqs must be in [1, 65535] and max_pos >= 1");
+    const int S = kv->n_seqs;
+    if (S % g.n_streams != 0 || S / g.n_streams > g.max_q)
+        return fail(CKE_ERANGE, "n_seqs %d must be n_streams (%d) x n_q with n_q <= max_q (%d)", S,
+                    g.n_streams, g.max_q);
+    if (pos < 0 || pos >= kv->max_pos) return fail(CKE_ERANGE, "pos %d outside [0, %d)", pos, kv->max_pos);
+    if (!x || !aligned16(x)) return fail(CKE_EINVAL, "x must be non-NULL and 16-byte aligned");
+    if (!ws || (reinterpret_cast<uintptr_t>(ws) & (kAlign - 1)) != 0)
+        return fail(CKE_EINVAL, "workspace must be non-NULL and 256-byte aligned");
+    if (!(scale == scale)) return fail(CKE_EINVAL, "scale is NaN");
+    const int dm = g.d_model;
+    const bool wbf16 = w->dtype == CKE_BF16;
+    if (cke::gemv_rows_per_pass(S, dm, wbf16) < 1)
+        return fail(CKE_EINVAL, "d_model %d too large for the decoder-step products", dm);
+
+    const size_t stride = step_buffer_bytes(&g, S);
+    float* buf[kStepBuffers];
+    for (int i = 0; i < kStepBuffers; ++i)
+        buf[i] = reinterpret_cast<float*>(static_cast<char*>(ws) + i * stride);
+    float *qs = buf[0], *ks = buf[1], *vs = buf[2], *so = buf[3], *x1 = buf[4], *qc = buf[5],
+          *co = buf[6];
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    // 1. self-attention projections, one launch for the three weights
+    {
+        float* Y[3] = {qs, ks, vs};
+        e = gemv(x, 3, W, Y, nullptr, S, dm, wbf16, st);
+        if (e != hipSuccess) return fail(CKE_EDEVICE, "decoder-step projection launch failed: %s", hipGetErrorString(e));
+    }
+    // 2. append row pos to the self cache and attend
+    cke::SelfLaunch sa;
+    sa.q = qs;
+    sa.k_new = ks;
+    sa.v_new = vs;
+    sa.K = kv->k;
+    sa.V = kv->v;
+    sa.out = so;
+    sa.S = S;
+    sa.H = kv->n_heads;
+    sa.D = kv->head_dim;
+    sa.max_pos = kv->max_pos;
+    sa.pos = pos;
+    sa.scale = scale;
+    sa.bf16 = kv->dtype == CKE_BF16;
+    e = cke::launch_selfattn_append(sa, st);
+    if (e != hipSuccess) return fail(CKE_EDEVICE, "self-attention launch failed: %s", hipGetErrorString(e));
+    // 3. x1 = x + so . WOs   4. qc = x1 . WQ
+    {
+        const void* Wo[1] = {W[3]};
+        float* Y[1] = {x1};
+        const float* R[1] = {x};
+        e = gemv(so, 1, Wo, Y, R, S, dm, wbf16, st);
+        if (e != hipSuccess) return fail(CKE_EDEVICE, "decoder-step projection launch failed: %s", hipGetErrorString(e));
+        const void* Wq[1] = {W[4]};
+        float* Yq[1] = {qc};
+        e = gemv(x1, 1, Wq, Yq, nullptr, S, dm, wbf16, st);
+        if (e != hipSuccess) return fail(CKE_EDEVICE, "decoder-step projection launch failed: %s", hipGetErrorString(e));
+    }
+    // 5. cross-attention: sequence s is query s % n_q of stream s / n_q
+    int rc = cross_decode(qc, S / g.n_streams, c, layer, scale, co, nullptr, stream);
+    if (rc != CKE_OK) return rc;
+    // 6. x = x1 + co . WO
+    {
+        const void* Wo[1] = {W[5]};
+        float* Y[1] = {x};
+        const float* R[1] = {x1};
+        e = gemv(co, 1, Wo, Y, R, S, dm, wbf16, st);
+        if (e != hipSuccess) return fail(CKE_EDEVICE, "decoder-step projection launch failed: %s", hipGetErrorString(e));
+    }
+    return CKE_OK;
+}
+
+}  // extern "C"

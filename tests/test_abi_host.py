@@ -158,6 +158,30 @@ def test_fp8_cache_geometry_and_populate_checks():
     assert rc == pc.CKE_EINVAL
 
 
+def test_decoder_step_workspace_and_argument_checks():
+    """cke_decoder_layer_step validates before launching: NULL handle and
+    descriptors, the layer range, then the ready flag (the checks behind the
+    flag run in the GPU tests, which can populate)."""
+    g = base_geom(n_layers=2, max_q=5)
+    ws = pc.cke_decoder_step_workspace_bytes(g, 5)
+    assert ws == 7 * ((5 * 512 * 4 + 255) // 256 * 256)
+    assert pc.cke_decoder_step_workspace_bytes(g, 0) == 0
+    L = pc.lib()
+    w = pc.cke_decoder_layer(*([FAKE] * 6), pc.CKE_F32)
+    kv = pc.cke_kv_layer(FAKE, FAKE, 5, 8, 64, 16, pc.CKE_F32)
+    h = pc.cke_xattn_cache_create(g, FAKE, FAKE, FAKE)
+    try:
+        def step(w=w, kv=kv, pos=3, layer=1, x=FAKE, wsp=FAKE):
+            return L.cke_decoder_layer_step(x, ctypes.byref(w), ctypes.byref(kv), pos, h, layer,
+                                            0.125, wsp, None)
+        assert step() == pc.CKE_ENOTREADY
+        assert step(layer=2) == pc.CKE_ERANGE
+        assert L.cke_decoder_layer_step(FAKE, None, ctypes.byref(kv), 0, None, 0, 0.1, FAKE,
+                                        None) == pc.CKE_EINVAL
+    finally:
+        pc.cke_xattn_cache_destroy(h)
+
+
 def test_create_rejects_null_and_misaligned():
     g = base_geom()
     for k, v, w in ((None, FAKE, FAKE), (FAKE, None, FAKE), (FAKE, FAKE, None),

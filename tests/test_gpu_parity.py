@@ -12,6 +12,7 @@ the fp8 roundings of (exact - e) and (exact + e), e the fp32 accumulation
 error bound; attention over an fp8 cache is checked on the oracle's own fp8
 cache, uploaded in place of the kernel's, to the fp32 bar of 1e-4.
 """
+import dataclasses
 import math
 
 import numpy as np
@@ -418,6 +419,94 @@ def test_teacher_forced_decoder_run_matches_oracle(name):
     assert worst <= 1e-4
     for l in range(g.n_layers):
         assert max_abs(to_np(kvs[l].k), run["Ks"][l].astype(np.float32)) == 0.0
+
+
+# --------------------------------------------------------- decoder step
+STEP_NAMES = ("WQs", "WKs", "WVs", "WOs", "WQ", "WO")
+
+
+def _step_setup(g):
+    """Populated GPU cache, the layer weights on the GPU and as float64, GPU
+    self caches, the oracle's projection cache and empty oracle self caches."""
+    wt = synth.workload_tensors(g, ("E", "WK", "WV") + STEP_NAMES + ("x0",))
+    cache, _, _ = make_cache(g, wt)
+    bf = g.dtype in ("bf16", "fp8")
+    dev_w = {k: ([tbf16(b) for b in wt[k + "_bits"]] if bf else [t32(w) for w in wt[k]])
+             for k in STEP_NAMES}
+    descs = [pc.decoder_layer_desc(*[dev_w[k][l] for k in STEP_NAMES]) for l in range(g.n_layers)]
+    S = g.n_streams * g.n_q
+    sdt = torch.bfloat16 if bf else torch.float32
+    kvs = [pc.KVLayer(S, g.n_heads, g.head_dim, g.max_pos, dtype=sdt) for _ in range(g.n_layers)]
+    ws = torch.empty(pc.cke_decoder_step_workspace_bytes(cache.geom, S) // 4, device=DEV)
+    Kc, Vc = oracle_caches(g, wt)
+    Ks = np.zeros((g.n_layers, S, g.n_heads, g.max_pos, g.head_dim))
+    Vs = np.zeros_like(Ks)
+    return dict(wt=wt, cache=cache, dev_w=dev_w, descs=descs, kvs=kvs, ws=ws, Kc=Kc, Vc=Vc,
+                Ks=Ks, Vs=Vs, S=S, bf=bf)
+
+
+STEP_CASES = [
+    ("tiny", {}),
+    (None, dict(n_layers=2, n_streams=1, n_q=1, mem_len=1500, d_model=512, n_heads=8,
+                head_dim=64, max_pos=16)),
+    (None, dict(n_layers=2, n_streams=1, n_q=5, mem_len=300, d_model=512, n_heads=8,
+                head_dim=64, max_pos=16)),                     # 5 beams over one cache
+    (None, dict(n_layers=2, n_streams=2, n_q=2, mem_len=77, d_model=256, n_heads=8,
+                head_dim=32, max_pos=16)),                     # 2 streams x 2 queries
+    (None, dict(n_layers=2, n_streams=3, n_q=1, mem_len=200, d_model=640, n_heads=5,
+                head_dim=128, max_pos=16, dtype="bf16")),      # bf16 weights and caches
+    (None, dict(n_layers=1, n_streams=2, n_q=8, mem_len=100, d_model=384, n_heads=6,
+                head_dim=64, max_pos=16, dtype="bf16")),       # 16 sequences, two passes
+]
+
+
+@pytest.mark.parametrize("name,kw", STEP_CASES, ids=lambda x: str(x))
+def test_decoder_layer_step_matches_oracle(name, kw):
+    """Teacher-forced: every call gets the oracle's input hidden state; its
+    output and the self-cache row it wrote are compared with the oracle's
+    layer step, for several tokens and every layer."""
+    g = geometry(name, **kw)
+    g = dataclasses.replace(g, n_seqs=g.n_streams * g.n_q)
+    st = _step_setup(g)
+    tol = TOL["bf16" if st["bf"] else "f32"]
+    W = [{k: st["wt"][k][l] for k in STEP_NAMES} for l in range(g.n_layers)]
+    x = st["wt"]["x0"][:st["S"]].astype(np.float64)
+    xd = torch.empty(st["S"], g.d_model, device=DEV)
+    for t in range(3):
+        for l in range(g.n_layers):
+            xd.copy_(t32(x))
+            pc.cke_decoder_layer_step(xd, st["descs"][l], st["kvs"][l], t, st["cache"], l, g.scale,
+                                      st["ws"])
+            x = oracle.decoder_layer_step(x, W[l], st["Kc"][l], st["Vc"][l], st["Ks"][l],
+                                          st["Vs"][l], t, n_q=g.n_q, scale=g.scale,
+                                          round_bf16=st["bf"])
+            torch.cuda.synchronize()
+            assert max_abs(to_np(xd), x) <= tol, (t, l, max_abs(to_np(xd), x))
+            assert max_abs(to_np(st["kvs"][l].k[:, :, t]), st["Ks"][l][:, :, t]) <= tol
+            assert max_abs(to_np(st["kvs"][l].v[:, :, t]), st["Vs"][l][:, :, t]) <= tol
+        x = x / np.sqrt(np.mean(x * x, axis=1, keepdims=True))
+    # rows past the last position were never written
+    assert float(np.abs(to_np(st["kvs"][0].k[:, :, 3:])).max(initial=0.0)) == 0.0
+
+
+def test_decoder_layer_step_rejects_bad_pairings_on_a_ready_cache():
+    g = geometry(None, n_layers=1, n_streams=2, n_q=2, n_seqs=4, mem_len=40, d_model=256,
+                 n_heads=8, head_dim=32, max_pos=8)
+    st = _step_setup(g)
+    x = torch.zeros(st["S"], g.d_model, device=DEV)
+    kv3 = pc.KVLayer(3, g.n_heads, g.head_dim, g.max_pos)      # 3 sequences over 2 streams
+    kv6 = pc.KVLayer(6, g.n_heads, g.head_dim, g.max_pos)      # n_q = 3 > max_q = 2
+    kvh = pc.KVLayer(4, 4, 64, g.max_pos)                      # other head split
+    for kv, code in ((kv3, pc.CKE_ERANGE), (kv6, pc.CKE_ERANGE), (kvh, pc.CKE_EINVAL)):
+        with pytest.raises(pc.CkeError) as e:
+            pc.cke_decoder_layer_step(x, st["descs"][0], kv, 0, st["cache"], 0, g.scale, st["ws"])
+        assert e.value.code == code
+    with pytest.raises(pc.CkeError) as e:
+        pc.cke_decoder_layer_step(x, st["descs"][0], st["kvs"][0], 8, st["cache"], 0, g.scale,
+                                  st["ws"])
+    assert e.value.code == pc.CKE_ERANGE
+    torch.cuda.synchronize()
+    assert float(x.abs().max()) == 0.0     # nothing was launched
 
 
 # ------------------------------------------------------------ fp8 caches
