@@ -104,7 +104,7 @@ def oracle_caches(g, wt):
     key = (g.name, g.seed, g.n_layers, g.n_streams, g.mem_len, g.d_model, g.dtype)
     if g.name == "custom" or key not in _ORACLE_CACHE:
         r = oracle.populate(wt["E"], wt["WK"], wt["WV"], g.n_heads, g.head_dim,
-                            round_bf16=(g.dtype == "bf16"))
+                            round_bf16=(g.dtype == "bf16"), round_fp8=(g.dtype == "fp8"))
         if g.name == "custom":
             return r
         _ORACLE_CACHE[key] = r
@@ -170,6 +170,12 @@ DEC_CASES = [
     (None, dict(n_layers=1, n_streams=2, n_q=3, mem_len=65, d_model=128, n_heads=2, head_dim=64)),
     (None, dict(n_layers=1, n_streams=5, n_q=2, mem_len=15, d_model=256, n_heads=2, head_dim=128,
                 dtype="bf16")),
+    # a long memory: the split count reaches its cap (64) and the merge runs 4 batches
+    (None, dict(n_layers=1, n_streams=1, n_q=2, mem_len=20000, d_model=128, n_heads=2,
+                head_dim=64)),
+    # Whisper Base geometry with the largest query count (8) on the split path
+    (None, dict(n_layers=1, n_streams=1, n_q=8, mem_len=1500, d_model=512, n_heads=8,
+                head_dim=64)),
 ]
 
 
@@ -456,7 +462,11 @@ STEP_CASES = [
     (None, dict(n_layers=2, n_streams=3, n_q=1, mem_len=200, d_model=640, n_heads=5,
                 head_dim=128, max_pos=16, dtype="bf16")),      # bf16 weights and caches
     (None, dict(n_layers=1, n_streams=2, n_q=8, mem_len=100, d_model=384, n_heads=6,
-                head_dim=64, max_pos=16, dtype="bf16")),       # 16 sequences, two passes
+                head_dim=64, max_pos=16, dtype="bf16")),       # 16 sequences, one pass
+    (None, dict(n_layers=1, n_streams=2, n_q=1, mem_len=1, d_model=256, n_heads=8,
+                head_dim=32, max_pos=16)),                     # one memory row
+    (None, dict(n_layers=1, n_streams=1, n_q=1, mem_len=300, d_model=512, n_heads=8,
+                head_dim=64, max_pos=16, dtype="fp8")),        # over an fp8 cache
 ]
 
 
@@ -565,6 +575,7 @@ FP8_DEC_CASES = [
     dict(n_layers=1, n_streams=5, n_q=2, mem_len=15, d_model=256, n_heads=2, head_dim=128),
     dict(n_layers=1, n_streams=2, n_q=8, mem_len=300, d_model=256, n_heads=8, head_dim=32),
     dict(n_layers=1, n_streams=1, n_q=5, mem_len=3001, d_model=256, n_heads=2, head_dim=128),
+    dict(n_layers=2, n_streams=3, n_q=2, mem_len=1, d_model=256, n_heads=4, head_dim=64),
 ]
 
 
