@@ -363,7 +363,8 @@ def measure_decoder_step(torch, pc, w, stream, tokens=4):
     the layer shape (fp32 or bf16 as the workload's inputs). For fp32 weights
     the same layer is also timed as the composition of separate calls (torch
     matmuls for the six products, the library's self and cross calls, torch
-    residual adds), for comparison."""
+    residual adds), for comparison. Weights are output-major, as the step
+    takes them."""
     g = w.g
     S = g.n_streams * g.n_q
     if not g.n_seqs or g.n_seqs != S:
@@ -420,16 +421,16 @@ def measure_decoder_step(torch, pc, w, stream, tokens=4):
         def composed():
             for t in range(tokens):
                 for l in range(L):
-                    WQs, WKs, WVs, WOs, WQ, WO = Wd[l]
-                    torch.mm(x, WQs, out=q)
-                    torch.mm(x, WKs, out=k)
-                    torch.mm(x, WVs, out=v)
+                    WQs, WKs, WVs, WOs, WQ, WO = Wd[l]   # output-major, as nn.Linear
+                    torch.mm(x, WQs.t(), out=q)
+                    torch.mm(x, WKs.t(), out=k)
+                    torch.mm(x, WVs.t(), out=v)
                     pc.cke_selfattn_decode_append(q, k, v, kvs[l], t, g.scale, so, stream=cs())
-                    torch.addmm(x, so, WOs, out=x1)
-                    torch.mm(x1, WQ, out=qc)
+                    torch.addmm(x, so, WOs.t(), out=x1)
+                    torch.mm(x1, WQ.t(), out=qc)
                     pc.cke_xattn_decode(qc.view(g.n_streams, g.n_q, H, D), w.cache, l, g.scale,
                                         co, stream=cs())
-                    torch.addmm(x1, co, WO, out=x)
+                    torch.addmm(x1, co, WO.t(), out=x)
         t_c = graph_time(composed) / (tokens * L)
         res["composed_us_per_layer"] = t_c * 1e6
         res["speedup_vs_composed"] = t_c / t_f

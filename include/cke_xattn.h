@@ -203,9 +203,10 @@ int cke_selfattn_prefill_append(const float* q, const float* k_new,
                                 int pos, int n_new, int n_q_heads, float scale,
                                 float* out, void* stream);
 
-/* One decoder layer's projection weights, each [d_model][d_model] in the
- * y = x . W orientation, device memory of w dtype (CKE_F32 or CKE_BF16),
- * 16-byte aligned. */
+/* One decoder layer's projection weights, each [d_model][d_model] stored
+ * output-major: row j holds output feature j's d_model input weights
+ * (y[j] = sum_c x[c] W[j][c], the nn.Linear layout). Device memory of w dtype
+ * (CKE_F32 or CKE_BF16), 16-byte aligned. */
 typedef struct cke_decoder_layer {
     const void* wq_self;   /* self-attention query, key, value, output */
     const void* wk_self;
@@ -225,12 +226,13 @@ size_t cke_decoder_step_workspace_bytes(const cke_xattn_geom* g, int n_seqs);
  * attention, then cross-attention whose queries come from the decoder and
  * whose keys and values come from the projection cache of this layer; the
  * MLP and norms have no weights in these workloads and are not part of it):
- *   x += SelfAttn(x.WQs, x.WKs, x.WVs; kv, pos) . WOs
- *   x += CrossAttn(x.WQ; slab `layer` of c) . WO
+ *   x += SelfAttn(x.WQs^T, x.WKs^T, x.WVs^T; kv, pos) . WOs^T
+ *   x += CrossAttn(x.WQ^T; slab `layer` of c) . WO^T
  * SelfAttn is cke_selfattn_decode_append (row pos of kv written, rows 0..pos
  * attended); CrossAttn is cke_xattn_decode with n_q = S / n_streams, sequence
- * s being query s % n_q of stream s / n_q. Products accumulate in fp32 from
- * fp32 or bf16 weights.
+ * s being query s % n_q of stream s / n_q. Products run on the matrix cores
+ * with fp32 accumulation: fp32 weights exactly, bf16 weights against x split
+ * into two bf16 terms (about 16 significant bits of x).
  *   x      device fp32 [S][d_model], updated in place
  *   kv     this layer's self cache: n_heads and head_dim equal the cache's
  *   ws     device, cke_decoder_step_workspace_bytes(geometry of c, S) bytes,

@@ -251,8 +251,9 @@ def cke_decoder_step_workspace_bytes(g: cke_xattn_geom, n_seqs: int) -> int:
 
 
 def decoder_layer_desc(WQs, WKs, WVs, WOs, WQ, WO) -> cke_decoder_layer:
-    """Descriptor of one layer's six [d_model][d_model] device weights (one
-    dtype, fp32 or bf16). The tensors must outlive every call that uses it."""
+    """Descriptor of one layer's six [d_model][d_model] device weights, stored
+    output-major (row j = output j's input weights, as nn.Linear.weight), one
+    dtype, fp32 or bf16. The tensors must outlive every call that uses it."""
     ws = (WQs, WKs, WVs, WOs, WQ, WO)
     dt = {w.dtype for w in ws}
     if len(dt) != 1:

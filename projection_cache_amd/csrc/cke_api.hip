@@ -495,8 +495,8 @@ int cke_decoder_layer_step(float* x, const cke_decoder_layer* w, const cke_kv_la
     if (!(scale == scale)) return fail(CKE_EINVAL, "scale is NaN");
     const int dm = g.d_model;
     const bool wbf16 = w->dtype == CKE_BF16;
-    if (cke::gemv_rows_per_pass(S, dm, wbf16) < 1)
-        return fail(CKE_EINVAL, "d_model %d too large for the decoder-step products", dm);
+    if (!cke::gemv_shape_ok(dm, dm))
+        return fail(CKE_EINVAL, "d_model %d must be a multiple of 32 for the decoder-step products", dm);
 
     const size_t stride = step_buffer_bytes(&g, S);
     float* buf[kStepBuffers];

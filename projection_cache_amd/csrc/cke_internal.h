@@ -88,10 +88,10 @@ struct PopulateLaunch {
 };
 
 // Rows of K/V one decode workgroup covers per pass of all its waves.
-// Decoder-step products Y = R + X.W (decoder_step.hip): up to three weights
-// sharing X, each with its own output and optional residual.
+// Decoder-step products Y = R + X.W^T (decoder_step.hip): up to three
+// weights sharing X, each with its own output and optional residual.
 struct GemvOut {
-    const void* W;       // [K][N], fp32 or bf16
+    const void* W;       // [N][K] (output-major), fp32 or bf16
     float* Y;            // [S][N]
     const float* R;      // nullptr or [S][N]
 };
@@ -101,10 +101,7 @@ struct GemvLaunch {
     int n_out, S, K, N;
     bool bf16;
 };
-constexpr size_t kGemvMaxLds = 128 * 1024;   // gfx950: 160 KB of LDS per CU
-int gemv_cols_per_block(bool bf16);
-size_t gemv_lds_bytes(int sb, int K, bool bf16);
-int gemv_rows_per_pass(int S, int K, bool bf16);
+bool gemv_shape_ok(int K, int N);   // K a multiple of 32, N of 16
 hipError_t launch_gemv(const GemvLaunch& a, hipStream_t st);
 
 int cross_keys_per_pass(int D, int elem_bytes);

@@ -1,226 +1,143 @@
 // Skinny products of the decoder-layer step on gfx950:
-//   Y[s][n] = R[s][n] + sum_k X[s][k] W[k][n]      (R optional)
+//   Y[s][n] = R[s][n] + sum_k X[s][k] W[n][k]      (R optional)
 // for the few rows s of one decode token (one per sequence), with fp32 X, Y, R
-// and fp32 or bf16 weights W [K][N] in the y = x.W orientation. One launch
-// takes up to three weights that share X (the self-attention Q, K and V
-// projections of C-Kernel-Engine's decoder body, "The concept").
+// and fp32 or bf16 weights W [N][K] stored output-major (row n holds output
+// n's K input weights, the nn.Linear layout). One launch takes up to three
+// weights that share X (the self-attention Q, K and V projections of
+// C-Kernel-Engine's decoder body, "The concept").
 //
-// These products read every weight element once for a handful of rows
-// (0.5-16 FLOP per weight byte), so they are bound by the weight stream, not
-// by arithmetic: plain fp32 FMAs on the vector units, no matrix cores.
+// The products are done on the matrix cores with the sequences as the 16 rows
+// of one MFMA tile: v_mfma_f32_16x16x32_bf16 for bf16 weights, with X split
+// into two bf16 terms (x = hi + lo, |x - hi - lo| <= 2^-17 |x|, so the sum
+// keeps about 16 significant bits of X against bf16's 8), and
+// v_mfma_f32_16x16x4_f32 for fp32 weights (exact fp32 products). On the vector
+// units the 16 rows x K x N multiply-adds of the largest workload kept each
+// workgroup busy for microseconds; here they are a few dozen MFMAs.
 //
-// Work split: a workgroup (8 waves) owns NB = G x 4 columns (G lanes of 4
-// columns: 16 bytes of fp32 or 8 bytes of bf16 per lane) of every weight
-// row, and all K rows. Its 512/G row groups stride over the rows, each lane
-// holding up to 16 rows (12 of fp32) in registers; the first rows are
-// requested before X is staged, so
-// the two latencies overlap. X (a chunk of SB sequences) is staged in LDS as
-// it lies in memory, [s][k], with 16-byte stores; the 4 lanes of a row group
-// read it as broadcasts. Row-group partial sums are reduced inside each 16-lane row
-// with DPP rotations and across rows and waves through LDS (reusing the X
-// space), in a fixed order (deterministic). Column blocks are assigned
-// XCD by XCD, so the two 64-byte halves of a 128-byte weight line are read by
-// workgroups of one XCD and share its L2.
-#include <type_traits>
-
+// Work split: a workgroup (8 waves) owns 16 output columns (one MFMA tile
+// wide) and all K; its waves split K. Because row n of W is contiguous in k,
+// lane l of an MFMA (column l % 16, k-group l / 16) loads 16 contiguous bytes
+// of W (8 bf16 or 4 fp32 k values) and the matching 8 or 4 contiguous values
+// of its X row straight from memory, with no LDS staging; the k values a
+// lane group holds are the same for both operands, which is all the product
+// needs. Every load of a wave is issued before its first MFMA. The 8 waves'
+// 16 x 16 partial tiles are summed through LDS in wave order (deterministic)
+// and the first 16 x 16 threads add the residual and store. (Measured: two or
+// four tiles per workgroup, sharing the X loads, were slower, and 4 or 16
+// waves no better than 8.)
 #include "cke_device.h"
 #include "cke_internal.h"
 
 namespace cke {
 namespace {
 
-#ifndef CKE_GEMV_G
-#define CKE_GEMV_G 4
+#ifndef CKE_GEMV_WAVES
+#define CKE_GEMV_WAVES 8
 #endif
-constexpr int kGemvG = CKE_GEMV_G;   // lanes across one weight row's column block
-constexpr int kGemvThreads = 512;
-// weight rows held in registers per lane (fp32 pieces take twice the registers)
-template <typename TW> constexpr int gemv_rows() { return sizeof(TW) == 4 ? 12 : 16; }
+constexpr int kGemvWaves = CKE_GEMV_WAVES;   // waves per workgroup, splitting K
+constexpr int kGemvCols = 16;   // output columns per workgroup (one MFMA tile)
+constexpr int kGemvRowsMax = 16;
+constexpr int kGemvBatch = 8;   // 16-byte W pieces in flight per lane
 
-template <typename TW, int SB>
-__global__ __launch_bounds__(kGemvThreads) void gemv_kernel(const float* __restrict__ X,
-                                                            GemvOut o0, GemvOut o1, GemvOut o2,
-                                                            int S, int K, int N, int nblk)
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+template <typename TW>
+__global__ __launch_bounds__(kGemvWaves * 64) void gemv_kernel(const float* __restrict__ X,
+                                                               GemvOut o0, GemvOut o1,
+                                                               GemvOut o2, int S, int K, int N)
 {
-    constexpr int CV = 4;                     // columns per lane (16 B fp32, 8 B bf16)
-    constexpr int G = kGemvG;
-    constexpr int NB = G * CV;                // columns per workgroup
-    constexpr int NT = kGemvThreads;
-    constexpr int RG = NT / G;                // row groups per workgroup
-    constexpr int NW = NT / 64;
-    extern __shared__ float smem[];           // xs [SB][K], later red [4*NW][SB][NB]
-    static_assert(G == 1 || G == 2 || G == 4, "row groups are reduced inside 16-lane rows");
+    constexpr int CKV = 16 / sizeof(TW);   // k values per lane per 16-byte piece
+    constexpr int CK = 4 * CKV;            // k values per chunk (4 lane groups)
+    __shared__ float red[kGemvWaves][kGemvRowsMax * kGemvCols];
 
-    const int per_xcd = (nblk + 7) / 8;
-    const int blk = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
-    if (blk >= nblk) return;                  // whole workgroup, before any barrier
     const GemvOut o = blockIdx.y == 0 ? o0 : (blockIdx.y == 1 ? o1 : o2);
-    const TW* __restrict__ Wc = static_cast<const TW*>(o.W) + (size_t)blk * NB +
-                                (threadIdx.x % G) * CV;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int g = threadIdx.x % G, rg = threadIdx.x / G;
-    float* xs = smem;
-    float* red = smem;
+    const int n0 = blockIdx.x * kGemvCols;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int i = lane & 15, g = lane >> 4;
+    const int nch = K / CK;
+    const int cpw = (nch + kGemvWaves - 1) / kGemvWaves;
+    const int c0 = wave * cpw, c1 = min(nch, c0 + cpw);
+    const TW* __restrict__ Wr = static_cast<const TW*>(o.W) + (size_t)(n0 + i) * K + g * CKV;
 
-    // a lane's 4 columns of one weight row: 16 bytes of fp32 or 8 of bf16
-    using Piece = typename std::conditional<sizeof(TW) == 4, uint4, uint2>::type;
-    constexpr int ROWS = gemv_rows<TW>();
-    Piece w[ROWS];
-    auto load_rows = [&](int kb) {
+    for (int s0 = 0; s0 < S; s0 += kGemvRowsMax) {
+        const bool row_ok = s0 + i < S;
+        const float* __restrict__ Xr = X + (size_t)(s0 + i) * K + g * CKV;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int cb = c0; cb < c1; cb += kGemvBatch) {
+            uint4 w[kGemvBatch];
+            float4 x[kGemvBatch][CKV / 4];
 #pragma unroll
-        for (int u = 0; u < ROWS; ++u) {
-            const int k = kb + rg + u * RG;
-            if (k < K) w[u] = *reinterpret_cast<const Piece*>(Wc + (size_t)k * N);
-        }
-    };
-
-    for (int s0 = 0; s0 < S; s0 += SB) {
-        const int sn = min(SB, S - s0);
-        // the first rows of weights do not depend on X: in flight while X is staged
-        load_rows(0);
-        __syncthreads();   // readers of the previous chunk's LDS are done
-        {
-            // rows s0.. of X are contiguous: 16-byte loads and stores, up to
-            // 16 in flight per thread (K is a multiple of 4); rows past S are
-            // zero
-            const float4* X4 = reinterpret_cast<const float4*>(X + (size_t)s0 * K);
-            float4* xs4 = reinterpret_cast<float4*>(xs);
-            const int n4 = sn * K / 4, tot4 = SB * K / 4;
-            for (int i0 = threadIdx.x; i0 < tot4; i0 += NT * 16) {
-                float4 v[16];
+            for (int u = 0; u < kGemvBatch; ++u) {
+                const int c = cb + u;
+                if (c < c1) {
+                    w[u] = load16(Wr + (size_t)c * CK);
 #pragma unroll
-                for (int u = 0; u < 16; ++u) {
-                    const int i = i0 + u * NT;
-                    v[u] = i < n4 ? X4[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+                    for (int h = 0; h < CKV / 4; ++h)
+                        x[u][h] = row_ok ? *reinterpret_cast<const float4*>(Xr + (size_t)c * CK + 4 * h)
+                                         : make_float4(0.f, 0.f, 0.f, 0.f);
                 }
-#pragma unroll
-                for (int u = 0; u < 16; ++u)
-                    if (i0 + u * NT < tot4) xs4[i0 + u * NT] = v[u];
             }
-        }
-        __syncthreads();
-        float acc[SB][CV];
 #pragma unroll
-        for (int s = 0; s < SB; ++s)
+            for (int u = 0; u < kGemvBatch; ++u) {
+                if (cb + u < c1) {
+                    if constexpr (sizeof(TW) == 2) {
+                        const float xv[8] = {x[u][0].x, x[u][0].y, x[u][0].z, x[u][0].w,
+                                             x[u][1].x, x[u][1].y, x[u][1].z, x[u][1].w};
+                        bf16x8 hi, lo;
 #pragma unroll
-            for (int c = 0; c < CV; ++c) acc[s][c] = 0.f;
-        for (int kb = 0; kb < K; kb += RG * ROWS) {
-            if (kb > 0) load_rows(kb);
-#pragma unroll
-            for (int u = 0; u < ROWS; ++u) {
-                const int k = kb + rg + u * RG;
-                if (k < K) {
-                    float xv[SB];   // broadcast reads: the 4 lanes of a row group share k
-#pragma unroll
-                    for (int j = 0; j < SB; ++j) xv[j] = xs[j * K + k];
-#pragma unroll
-                    for (int c = 0; c < CV; ++c) {
-                        float wv;
-                        if constexpr (sizeof(TW) == 4) {
-                            wv = elem<float>(w[u], c);
-                        } else {
-                            const uint32_t h = c < 2 ? w[u].x : w[u].y;
-                            wv = (c & 1) ? bf16_hi(h) : bf16_lo(h);
+                        for (int e = 0; e < 8; ++e) {
+                            const __bf16 h = (__bf16)xv[e];
+                            hi[e] = h;
+                            lo[e] = (__bf16)(xv[e] - (float)h);
                         }
+                        const bf16x8 b = __builtin_bit_cast(bf16x8, w[u]);
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, b, acc, 0, 0, 0);
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, b, acc, 0, 0, 0);
+                    } else {
+                        const float xv[4] = {x[u][0].x, x[u][0].y, x[u][0].z, x[u][0].w};
+                        const float wv[4] = {__uint_as_float(w[u].x), __uint_as_float(w[u].y),
+                                             __uint_as_float(w[u].z), __uint_as_float(w[u].w)};
 #pragma unroll
-                        for (int s = 0; s < SB; ++s) acc[s][c] = fmaf(xv[s], wv, acc[s][c]);
+                        for (int j = 0; j < 4; ++j)
+                            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xv[j], wv[j], acc, 0, 0, 0);
                     }
                 }
             }
         }
-        __syncthreads();   // every read of xs is done before red reuses the space
-        // The 16/G row groups inside each 16-lane row are summed with DPP row
-        // rotations by G, 2G, .. 8 lanes, which keep a lane's column group;
-        // the 4*NW row sums of the workgroup then go through LDS.
+        // lane l holds tile rows 4*(l/16) + r, column l % 16
+        __syncthreads();   // the previous pass's readers of red are done
 #pragma unroll
-        for (int s = 0; s < SB; ++s)
-#pragma unroll
-            for (int c = 0; c < CV; ++c) {
-                float v = acc[s][c];
-                if constexpr (G <= 1) v += dpp<0x121>(v);   // row_ror:1
-                if constexpr (G <= 2) v += dpp<0x122>(v);   // row_ror:2
-                v += dpp<0x124>(v);                         // row_ror:4
-                v += dpp<0x128>(v);                         // row_ror:8
-                acc[s][c] = v;
-            }
-        if ((lane & 15) < G) {
-            const int row = wave * 4 + (lane >> 4);
-#pragma unroll
-            for (int s = 0; s < SB; ++s)
-#pragma unroll
-                for (int c = 0; c < CV; ++c) red[(row * SB + s) * NB + g * CV + c] = acc[s][c];
-        }
+        for (int r = 0; r < 4; ++r) red[wave][(4 * g + r) * kGemvCols + i] = acc[r];
         __syncthreads();
-        for (int i = threadIdx.x; i < sn * NB; i += NT) {
-            const int s = i / NB, col = i - s * NB;
-            float v = red[s * NB + col];
+        for (int e = threadIdx.x; e < kGemvRowsMax * kGemvCols; e += kGemvWaves * 64) {   // one pass
+            const int s = e / kGemvCols, col = e % kGemvCols;
+            if (s0 + s < S) {
+                float v = red[0][e];
 #pragma unroll
-            for (int r = 1; r < 4 * NW; ++r) v += red[(r * SB + s) * NB + col];
-            const size_t idx = (size_t)(s0 + s) * N + (size_t)blk * NB + col;
-            if (o.R) v += o.R[idx];
-            o.Y[idx] = v;
+                for (int wv = 1; wv < kGemvWaves; ++wv) v += red[wv][e];
+                const size_t idx = (size_t)(s0 + s) * N + n0 + col;
+                if (o.R) v += o.R[idx];
+                o.Y[idx] = v;
+            }
         }
     }
-}
-
-template <typename TW, int SB>
-hipError_t launch_gemv_sb(const GemvLaunch& a, hipStream_t st) {
-    const int nblk = a.N / gemv_cols_per_block(a.bf16);
-    const int grid = ((nblk + 7) / 8) * 8;
-    const size_t lds = gemv_lds_bytes(SB, a.K, a.bf16);
-    hipLaunchKernelGGL((gemv_kernel<TW, SB>), dim3(grid, a.n_out), dim3(kGemvThreads), lds, st, a.X, a.o[0],
-                       a.o[1], a.o[2], a.S, a.K, a.N, nblk);
-    return hipGetLastError();
 }
 
 template <typename TW>
 hipError_t launch_gemv_t(const GemvLaunch& a, hipStream_t st) {
-    switch (gemv_rows_per_pass(a.S, a.K, a.bf16)) {
-        case 1: return launch_gemv_sb<TW, 1>(a, st);
-        case 2: return launch_gemv_sb<TW, 2>(a, st);
-        case 4: return launch_gemv_sb<TW, 4>(a, st);
-        case 8: return launch_gemv_sb<TW, 8>(a, st);
-        case 16: return launch_gemv_sb<TW, 16>(a, st);
-    }
-    return hipErrorInvalidValue;
+    hipLaunchKernelGGL((gemv_kernel<TW>), dim3(a.N / kGemvCols, a.n_out), dim3(kGemvWaves * 64), 0,
+                       st, a.X, a.o[0], a.o[1], a.o[2], a.S, a.K, a.N);
+    return hipGetLastError();
 }
 
 }  // namespace
 
-int gemv_cols_per_block(bool) { return kGemvG * 4; }
-
-size_t gemv_lds_bytes(int sb, int K, bool bf16) {
-    const size_t xs = (size_t)K * sb;
-    const size_t red = (size_t)4 * (kGemvThreads / 64) * sb * gemv_cols_per_block(bf16);
-    return (xs > red ? xs : red) * sizeof(float);
-}
-
-// LDS a workgroup may take on the current device (the smaller of
-// kGemvMaxLds and what the runtime reports).
-static size_t gemv_lds_limit() {
-    int dev = 0, v = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess ||
-        v <= 0)
-        return 64 * 1024;
-    return (size_t)v < kGemvMaxLds ? (size_t)v : kGemvMaxLds;
-}
-
-// Sequences per pass over the weights: the smallest power of two covering S,
-// at most 16, and small enough for the staged X chunk and the reduction
-// buffer to fit the LDS limit; 0 if not even one row fits.
-int gemv_rows_per_pass(int S, int K, bool bf16) {
-    const size_t lim = gemv_lds_limit();
-    int sb = 1;
-    while (sb < S && sb < 16) sb *= 2;
-    while (sb >= 1 && gemv_lds_bytes(sb, K, bf16) > lim) sb /= 2;
-    return sb;
-}
+bool gemv_shape_ok(int K, int N) { return K > 0 && N > 0 && K % 32 == 0 && N % kGemvCols == 0; }
 
 hipError_t launch_gemv(const GemvLaunch& a, hipStream_t st) {
-    if (a.n_out < 1 || a.n_out > 3 || a.N % gemv_cols_per_block(a.bf16) != 0 ||
-        gemv_rows_per_pass(a.S, a.K, a.bf16) < 1)
-        return hipErrorInvalidValue;
+    if (a.n_out < 1 || a.n_out > 3 || a.S < 1 || !gemv_shape_ok(a.K, a.N)) return hipErrorInvalidValue;
     return a.bf16 ? launch_gemv_t<uint16_t>(a, st) : launch_gemv_t<float>(a, st);
 }
 

@@ -437,7 +437,8 @@ def _step_setup(g):
     wt = synth.workload_tensors(g, ("E", "WK", "WV") + STEP_NAMES + ("x0",))
     cache, _, _ = make_cache(g, wt)
     bf = g.dtype in ("bf16", "fp8")
-    dev_w = {k: ([tbf16(b) for b in wt[k + "_bits"]] if bf else [t32(w) for w in wt[k]])
+    # the step takes output-major weights: the transpose of the oracle's y = x.W matrices
+    dev_w = {k: ([tbf16(b.T) for b in wt[k + "_bits"]] if bf else [t32(w.T) for w in wt[k]])
              for k in STEP_NAMES}
     descs = [pc.decoder_layer_desc(*[dev_w[k][l] for k in STEP_NAMES]) for l in range(g.n_layers)]
     S = g.n_streams * g.n_q
