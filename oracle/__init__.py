@@ -69,6 +69,9 @@ def lib():
         L.orc_cross_decode_weights.argtypes = [_I] * 5 + [_D, _P, _P, _P, _P, _I, _P, _P]
         L.orc_matvec.argtypes = [_I, _I, _P, _P, _P]
         L.orc_rms_feedback.argtypes = [_I, _P, _P]
+        L.orc_lift_gelu.argtypes = [_I, _I, _I, _P, _P, _P, _I, _P]
+        L.orc_gelu.restype = _D
+        L.orc_gelu.argtypes = [_D]
         L.orc_decoder_layer_step.restype = _I
         L.orc_decoder_layer_step.argtypes = [_I] * 8 + [_D, _I] + [_P] * 17
         L.orc_decoder_run.restype = _I
@@ -232,6 +235,26 @@ def matvec(x, W) -> np.ndarray:
     y = np.empty(W.shape[1], dtype=np.float64)
     lib().orc_matvec(W.shape[0], W.shape[1], _ptr(x), _ptr(W), _ptr(y))
     return y
+
+
+def lift_gelu(x, W, pos=None) -> np.ndarray:
+    """Projector memory: gelu(x . W) (exact erf GELU) plus the window positions
+    pos [pos_rows][n] broadcast over blocks of pos_rows rows; x [rows][k_in],
+    W [k_in][n]."""
+    x, W = _f64(x), _f64(W)
+    rows, k_in = x.shape
+    n = W.shape[1]
+    out = np.empty((rows, n), dtype=np.float64)
+    if pos is None:
+        lib().orc_lift_gelu(rows, k_in, n, _ptr(x), _ptr(W), None, 1, _ptr(out))
+    else:
+        pos = _f64(pos)
+        lib().orc_lift_gelu(rows, k_in, n, _ptr(x), _ptr(W), _ptr(pos), pos.shape[0], _ptr(out))
+    return out
+
+
+def gelu(v: float) -> float:
+    return float(lib().orc_gelu(float(v)))
 
 
 def decoder_layer_step(x, W: dict, Kc, Vc, Ks, Vs, pos: int, *, n_q: int, scale: float,

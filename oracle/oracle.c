@@ -17,7 +17,9 @@
  *          (C-Kernel-Engine) -- "The concept", "View 2", "View 3",
  *          "Deliberate failure".
  *   [TOP]  "Recurrence as feeds" (topos) -- "What it opened".
- *   [WK]   "Caso de estudio: WhisperKit" (ANE knowledge base) -- sections 2, 3, 4.
+ *   [WK]   "Caso de estudio: WhisperKit" (ANE knowledge base) -- sections 2, 3, 4, 8.
+ *   [GRN]  "Forward map - granite_nar" (transcribe.cpp) -- "Projector (NLE
+ *          simplified Q-Former)".
  *
  * Parity pins live in tests/test_oracle_pins.py; every function below is
  * pinned there by something other than itself (library routines, closed forms,
@@ -356,6 +358,37 @@ void orc_kv_blend_update(int S, int H, int D, int max_pos, int pos,
                         cache[row + d] * (1.0 - m) + cur[io + d] * m;
             }
 }
+
+/* --------------------------------------------------- projector memory lift
+ * [GRN] "Forward map - granite_nar", "Projector (NLE simplified Q-Former)":
+ * the projector's key/value memory is the GELU (the exact, erf-based one) of
+ * a linear lift of the normalised 4-way encoder concat, plus the window
+ * position embedding broadcast over the blocks of pos_rows frames:
+ *   out[r][j] = gelu(sum_c x[r][c] W[c][j]) + pos[r % pos_rows][j]
+ * x is [rows][k_in], W [k_in][n], pos [pos_rows][n] (NULL: no positions),
+ * out [rows][n]. No bias (the page's linear names only a weight).
+ */
+static double gelu_exact(double v) { return 0.5 * v * (1.0 + erf(v / sqrt(2.0))); }
+
+void orc_lift_gelu(int rows, int k_in, int n, const double* x, const double* W,
+                   const double* pos, int pos_rows, double* out)
+{
+#pragma omp parallel for schedule(static)
+    for (int r = 0; r < rows; ++r) {
+        double* o = out + (size_t)r * n;
+        for (int j = 0; j < n; ++j) o[j] = 0.0;
+        /* every o[j] still sums its k_in products in ascending c order */
+        for (int c = 0; c < k_in; ++c) {
+            const double xv = x[(size_t)r * k_in + c];
+            const double* w = W + (size_t)c * n;
+            for (int j = 0; j < n; ++j) o[j] += xv * w[j];
+        }
+        for (int j = 0; j < n; ++j)
+            o[j] = gelu_exact(o[j]) + (pos ? pos[(size_t)(r % pos_rows) * n + j] : 0.0);
+    }
+}
+
+double orc_gelu(double v) { return gelu_exact(v); }
 
 /* ------------------------------------------------- harness decoder (O4/O5)
  * The workloads give projection weights but no norm, MLP or vocabulary, so the

@@ -97,6 +97,32 @@ def test_fp8_cache_decode_error_within_its_bound(dm):
           {"%s@%gx" % k: "%.2e" % v for k, v in worst.items()})
 
 
+# ------------------------------------------------------ projector memory lift
+def test_lift_gelu_matches_torch_exact_gelu_with_broadcast_positions():
+    """[GRN] 'Projector': gelu(x.W) + window positions broadcast over blocks of
+    15 frames, against torch float64 matmul + exact (erf) GELU."""
+    r = rng(80)
+    x = r.standard_normal((45, 64))
+    W = r.standard_normal((64, 32)) * 0.3
+    pos = r.standard_normal((15, 32)) * 0.02
+    got = oracle.lift_gelu(x, W, pos)
+    pre = torch.from_numpy(x) @ torch.from_numpy(W)
+    want = torch.nn.functional.gelu(pre, approximate="none") + torch.from_numpy(np.tile(pos, (3, 1)))
+    np.testing.assert_allclose(got, want.numpy(), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(oracle.lift_gelu(x, W), got - np.tile(pos, (3, 1)), rtol=0, atol=1e-15)
+
+
+def test_gelu_closed_forms():
+    """gelu(0) = 0, gelu(v) - gelu(-v) = v (Phi(v) + Phi(-v) = 1), gelu(v) -> v
+    for large v and -> 0 for large negative v, gelu(1) = Phi(1)."""
+    assert oracle.gelu(0.0) == 0.0
+    for v in (0.3, 1.7, 4.0, 11.0):
+        assert abs(oracle.gelu(v) - oracle.gelu(-v) - v) <= 1e-15 * max(1.0, v)
+    assert abs(oracle.gelu(12.0) - 12.0) < 1e-15 * 12
+    assert abs(oracle.gelu(-12.0)) < 1e-30
+    assert abs(oracle.gelu(1.0) - 0.5 * (1 + math.erf(1 / math.sqrt(2)))) < 1e-16
+
+
 # ----------------------------------------------------------------- bf16 rounding
 def test_round_bf16_matches_torch_cast():
     """Pinned to torch's float32 -> bfloat16 cast (round to nearest even)."""
