@@ -52,8 +52,9 @@ WORKLOAD_TEXT = {
     "large_fp8": "large over an fp8 cache: 16 streams x E[1500,1280] bf16, 32 layers, "
                  "20 heads x 64, populate + 128 decode steps, fp8 E4M3 projection cache, "
                  "bf16 self caches, fp32 accumulate",
-    "qformer": "q-former projector cross-attn: 100 blocks x 15 frames, memory width 2048, "
-               "2 layers, 32 heads x 64, 3 queries per block, one pass",
+    "qformer": "q-former projector cross-attn: 1500 x 4096 encoder concat lifted to 2048 "
+               "(exact GELU, window positions), 100 blocks x 15 frames, 2 layers, 32 heads x 64, "
+               "3 queries per block, one pass",
     "tiny": "tiny: E[64,64] fp32, 1 layer, 2 heads x 32, 8 decode steps",
 }
 
@@ -106,6 +107,13 @@ class Workload:
             self.WK = [dev_f32(w) for w in wt["WK"]]
             self.WV = [dev_f32(w) for w in wt["WV"]]
         del wt
+        # a projector memory (Q-Former): E is produced in the window by the
+        # lift gelu(X_lift . W_lift) + window positions, then populated
+        self.lift = None
+        if g.lift_in:
+            lt = synth.workload_tensors(g, ("X_lift", "W_lift", "pos"))
+            self.lift = {k: dev_f32(v) for k, v in lt.items()}
+            del lt
         cdt = {"f32": torch.float32, "bf16": torch.bfloat16,
                "fp8": torch.float8_e4m3fn}[g.dtype]
         sdt = torch.bfloat16 if self.bf16 else torch.float32
@@ -143,6 +151,10 @@ class Workload:
         steps (counter runs only)."""
         g, pc = self.g, self.pc
         if "populate" in kinds:
+            if self.lift is not None:
+                pc.cke_memory_lift_gelu(self.lift["X_lift"], self.lift["W_lift"],
+                                        self.E.view(-1, g.d_model), self.lift["pos"],
+                                        stream=stream)
             pc.cke_xattn_populate(self.cache, self.E, self.WK, self.WV, stream=stream)
         for t in range(g.steps if tokens is None else min(tokens, g.steps)):
             for l in range(g.n_layers):
@@ -181,8 +193,12 @@ class Workload:
         return rows + new + qo
 
     def populate_flops(self):
+        """K/V projections of every layer, plus the memory lift when there is one."""
         g = self.g
-        return 2.0 * g.n_streams * g.mem_len * (2 * g.n_layers * g.d_model) * g.d_model
+        f = 2.0 * g.n_streams * g.mem_len * (2 * g.n_layers * g.d_model) * g.d_model
+        if g.lift_in:
+            f += 2.0 * g.n_streams * g.mem_len * g.lift_in * g.d_model
+        return f
 
 
 def cpu_baseline(name, budget_s):
@@ -201,7 +217,12 @@ def cpu_baseline(name, budget_s):
                                  round_bf16=(g.dtype == "bf16"), round_fp8=(g.dtype == "fp8"))
         t_pop = (time.perf_counter() - t0) * g.n_streams
     else:
-        Kc, Vc = oracle.populate(wt["E"], wt["WK"], wt["WV"], g.n_heads, g.head_dim,
+        E = wt["E"]
+        if g.lift_in:   # the projector memory is lifted first, as on the GPU
+            lt = synth.workload_tensors(g, ("X_lift", "W_lift", "pos"))
+            E = oracle.lift_gelu(lt["X_lift"], lt["W_lift"], lt["pos"]).reshape(
+                g.n_streams, g.mem_len, -1)
+        Kc, Vc = oracle.populate(E, wt["WK"], wt["WV"], g.n_heads, g.head_dim,
                                  round_bf16=(g.dtype == "bf16"))
         t_pop = time.perf_counter() - t0
     del wt

@@ -244,6 +244,23 @@ int cke_decoder_layer_step(float* x, const cke_decoder_layer* w, const cke_kv_la
                            int pos, const cke_xattn_cache* c, int layer, float scale,
                            void* ws, void* stream);
 
+/* Projector memory lift, the prologue that produces a Q-Former-style encoder
+ * memory before it is populated:
+ *   out[r][j] = gelu(sum_c x[r][c] w[c][j]) + pos[r % pos_rows][j]
+ * with the exact (erf) GELU, fp32 throughout, products on the matrix cores.
+ *   transcribe.cpp "Forward map - granite_nar", "Projector (NLE simplified
+ *   Q-Former)": the normalised 4-way encoder concat is lifted 4096 -> 2048
+ *   with a GELU, and the window position embedding is added to every block of
+ *   15 frames before the blocks serve as key/value memory.
+ *   x    device fp32 [rows][k_in], k_in a multiple of 32
+ *   w    device fp32 [k_in][n] (y = x . w), n a multiple of 64
+ *   pos  device fp32 [pos_rows][n], or NULL for no positions
+ *   out  device fp32 [rows][n], token-major (usable as E of cke_xattn_populate
+ *        with n_streams = rows / mem_len); must not alias x, w or pos
+ * CKE_EINVAL for NULL or misaligned pointers and unsupported sizes. */
+int cke_memory_lift_gelu(const float* x, int rows, int k_in, const float* w, int n,
+                         const float* pos, int pos_rows, float* out, void* stream);
+
 /* Message for the last non-OK status returned on this thread. */
 const char* cke_last_error(void);
 

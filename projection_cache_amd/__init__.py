@@ -95,14 +95,16 @@ _lib.cke_decoder_step_workspace_bytes.argtypes = [ctypes.POINTER(cke_xattn_geom)
 _lib.cke_decoder_layer_step.restype = _I
 _lib.cke_decoder_layer_step.argtypes = [_P, ctypes.POINTER(cke_decoder_layer),
                                         ctypes.POINTER(cke_kv_layer), _I, _P, _I, _F, _P, _P]
+_lib.cke_memory_lift_gelu.restype = _I
+_lib.cke_memory_lift_gelu.argtypes = [_P, _I, _I, _P, _I, _P, _I, _P, _P]
 
 EXPORTED = ["cke_xattn_region_bytes", "cke_xattn_layer_offset_bytes",
             "cke_xattn_workspace_bytes", "cke_xattn_num_splits", "cke_xattn_cache_create",
             "cke_xattn_cache_destroy", "cke_xattn_invalidate", "cke_xattn_is_ready",
             "cke_xattn_populate", "cke_xattn_decode", "cke_selfattn_decode_append",
             "cke_selfattn_prefill_append", "cke_xattn_decode_weights",
-            "cke_decoder_step_workspace_bytes", "cke_decoder_layer_step", "cke_last_error",
-            "cke_version"]
+            "cke_decoder_step_workspace_bytes", "cke_decoder_layer_step", "cke_memory_lift_gelu",
+            "cke_last_error", "cke_version"]
 
 
 class CkeError(RuntimeError):
@@ -270,6 +272,16 @@ def cke_decoder_layer_step(x, w, kv, pos: int, cache, layer: int, scale: float, 
     _check(_lib.cke_decoder_layer_step(_ptr(x), ctypes.byref(w), ctypes.byref(desc), int(pos),
                                        _handle(cache), int(layer), float(scale), _ptr(ws),
                                        _stream(stream)))
+
+
+def cke_memory_lift_gelu(x, w, out, pos=None, stream=None) -> None:
+    """out [rows][n] = gelu(x [rows][k_in] . w [k_in][n]) + pos[r % pos_rows]
+    (exact GELU; pos [pos_rows][n] or None), all fp32 device tensors."""
+    rows, k_in = x.shape[0], x.shape[-1]
+    n = w.shape[1]
+    _check(_lib.cke_memory_lift_gelu(_ptr(x), int(rows), int(k_in), _ptr(w), int(n), _ptr(pos),
+                                     int(pos.shape[0]) if pos is not None else 0, _ptr(out),
+                                     _stream(stream)))
 
 
 class XattnCache:

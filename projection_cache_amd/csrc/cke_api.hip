@@ -556,3 +556,33 @@ int cke_decoder_layer_step(float* x, const cke_decoder_layer* w, const cke_kv_la
 }
 
 }  // extern "C"
+
+extern "C" {
+
+int cke_memory_lift_gelu(const float* x, int rows, int k_in, const float* w, int n,
+                         const float* pos, int pos_rows, float* out, void* stream) {
+    if (!x || !w || !out) return fail(CKE_EINVAL, "x, w and out must be non-NULL");
+    if (!aligned16(x) || !aligned16(w) || !aligned16(out) || (pos && !aligned16(pos)))
+        return fail(CKE_EINVAL, "x, w, pos and out must be 16-byte aligned");
+    if (rows < 1 || k_in < 1 || n < 1)
+        return fail(CKE_EINVAL, "rows, k_in and n must be positive (got %d, %d, %d)", rows, k_in, n);
+    if (k_in % 32 != 0 || n % 64 != 0)
+        return fail(CKE_EINVAL, "k_in must be a multiple of 32 and n of 64 (got %d, %d)", k_in, n);
+    if ((long long)rows * k_in > (1ll << 31) - 1 || (long long)rows * n > (1ll << 31) - 1)
+        return fail(CKE_EINVAL, "rows x k_in or rows x n too large");
+    if (pos && pos_rows < 1) return fail(CKE_EINVAL, "pos_rows must be >= 1 when pos is given");
+    cke::LiftLaunch a;
+    a.x = x;
+    a.w = w;
+    a.pos = pos;
+    a.out = out;
+    a.rows = rows;
+    a.k_in = k_in;
+    a.n = n;
+    a.pos_rows = pos ? pos_rows : 1;
+    hipError_t e = cke::launch_lift(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(CKE_EDEVICE, "memory lift launch failed: %s", hipGetErrorString(e));
+    return CKE_OK;
+}
+
+}  // extern "C"

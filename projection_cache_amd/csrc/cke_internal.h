@@ -113,4 +113,14 @@ hipError_t launch_selfattn_prefill(const PrefillLaunch& a, hipStream_t st);
 hipError_t launch_xattn_weights(const WeightsLaunch& a, hipStream_t st);
 hipError_t launch_populate(const PopulateLaunch& a, hipStream_t st);
 
+// Projector memory lift: out[r][j] = gelu(sum_c x[r][c] w[c][j]) + pos[r % pos_rows][j].
+struct LiftLaunch {
+    const float* x;      // [rows][k_in]
+    const float* w;      // [k_in][n]
+    const float* pos;    // nullptr or [pos_rows][n]
+    float* out;          // [rows][n]
+    int rows, k_in, n, pos_rows;
+};
+hipError_t launch_lift(const LiftLaunch& a, hipStream_t st);
+
 }  // namespace cke

@@ -19,6 +19,8 @@
 #include "cke_device.h"
 #include "cke_internal.h"
 
+#include <cstring>
+
 namespace cke {
 namespace {
 
@@ -33,6 +35,8 @@ struct GemmArgs {
     void* Kc;
     void* Vc;
     int M, dm, T, L, B, H, D;
+    const float* pos;    // memory lift only: [pos_rows][H*D] or nullptr
+    int pos_rows;
 };
 
 // Row of a 32x32 MFMA accumulator block held in register r of `lane`
@@ -883,7 +887,7 @@ __global__ __launch_bounds__(256) void populate_bf16_w4_kernel(GemmArgs a, int n
 //  * the finished tile is staged through the ring as [head][row][D] and
 //    written as whole rows (a head's 64 rows of one stream are contiguous).
 // Requires D <= 64 with 64 % D == 0 (a tile holds whole heads).
-template <int NSLOT, int BK>
+template <int NSLOT, int BK, bool LIFT = false>
 __global__ __launch_bounds__(256) void populate_f32_dma_kernel(GemmArgs a, int num_m, int num_n)
 {
     constexpr int BM = 64, BN = 64, NT = 256, GROUP_M = 8;
@@ -994,6 +998,42 @@ __global__ __launch_bounds__(256) void populate_f32_dma_kernel(GemmArgs a, int n
         slot = slot + 1 == NSLOT ? 0 : slot + 1;
     }
 
+    if constexpr (LIFT) {
+        // memory lift: C is token-major [M][HD]; stage the 64 x 64 tile as
+        // rows of 16 pieces XOR-swizzled by row, then write whole rows with
+        // the GELU and the window positions applied
+        __syncthreads();
+        float* stage = ring;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const int q = (wn * 32 + 8 * g + 4 * (lane >> 5)) >> 2;
+            *reinterpret_cast<float4*>(stage + m_l * BN + ((q ^ (m_l & 15)) << 2)) =
+                make_float4(acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]);
+        }
+        __syncthreads();
+        float* C = static_cast<float*>(a.Kc);
+        auto gelu = [](float v) { return 0.5f * v * (1.f + erff(v * 0.70710678118654752f)); };
+#pragma unroll 4
+        for (int id = tid; id < BM * BN / 4; id += NT) {
+            const int m = id >> 4, q = id & 15;
+            if (m0 + m < a.M) {
+                float4 v = *reinterpret_cast<const float4*>(stage + m * BN + ((q ^ (m & 15)) << 2));
+                v = make_float4(gelu(v.x), gelu(v.y), gelu(v.z), gelu(v.w));
+                const int col = n0 + 4 * q;
+                if (a.pos) {
+                    const float4 pv = *reinterpret_cast<const float4*>(
+                        a.pos + (size_t)((m0 + m) % a.pos_rows) * HD + col);
+                    v.x += pv.x;
+                    v.y += pv.y;
+                    v.z += pv.z;
+                    v.w += pv.w;
+                }
+                *reinterpret_cast<float4*>(C + (size_t)(m0 + m) * HD + col) = v;
+            }
+        }
+        return;
+    }
+
     // epilogue: stage [head j][row m][D] with 16-byte pieces XOR-swizzled by row
     __syncthreads();
     float* stage = ring;
@@ -1081,8 +1121,37 @@ hipError_t launch_cfg(const GemmArgs& g, bool bf16, hipStream_t st) {
 
 }  // namespace
 
+// Projector memory lift: out = gelu(x . W) (+ positions), fp32, on the fp32
+// DMA populate kernel with a token-major epilogue. One weight, N = n columns.
+hipError_t launch_lift(const LiftLaunch& a, hipStream_t st) {
+    if (a.rows < 1 || a.k_in % 32 != 0 || a.n % 64 != 0 || (a.pos && a.pos_rows < 1))
+        return hipErrorInvalidValue;
+    GemmArgs g;
+    std::memset(&g, 0, sizeof(g));
+    g.E = a.x;
+    g.wt.w[0] = a.w;
+    g.Kc = a.out;
+    g.M = a.rows;
+    g.dm = a.k_in;
+    g.T = a.rows;
+    g.L = 1;
+    g.B = 1;
+    g.H = a.n / 64;
+    g.D = 64;
+    g.pos = a.pos;
+    g.pos_rows = a.pos_rows;
+    const int num_m = (a.rows + 63) / 64, num_n = a.n / 64;
+    const int ntiles = num_m * num_n;
+    const int grid = ((ntiles + 7) / 8) * 8;
+    hipLaunchKernelGGL((populate_f32_dma_kernel<3, 32, true>), dim3(grid), dim3(256), 0, st, g, num_m,
+                       num_n);
+    return hipGetLastError();
+}
+
 hipError_t launch_populate(const PopulateLaunch& a, hipStream_t st) {
     GemmArgs g;
+    g.pos = nullptr;
+    g.pos_rows = 0;
     g.E = a.E;
     g.wt = a.wt;
     g.Kc = a.Kc;

@@ -20,7 +20,8 @@ Geometry follows the pages:
   * same page, "View 2": 8 heads, head_dim 64, 1500 key tokens, scale 0.125.
   * WhisperKit case study, section 4: self-attention cache capacity 448.
   * transcribe.cpp granite_nar forward map, "Projector": 2 layers, 32 heads x 64,
-    blocks of 15 frames, 3 queries per block.
+    blocks of 15 frames, 3 queries per block; the memory comes from a 4096 -> 2048
+    lift of the encoder concat (X_lift, W_lift) plus window positions (pos).
 """
 from __future__ import annotations
 
@@ -54,6 +55,7 @@ class Geometry:
     seed: int
     e_std: float = 1.0
     w_std: float = 0.02
+    lift_in: int = 0    # projector memory lift input width (0: E is drawn directly)
 
     @property
     def hd(self) -> int:
@@ -70,7 +72,7 @@ CONFIGS = {
     "large": Geometry("large", 16, 1, 16, 32, 1500, 1280, 20, 64, 0.125,
                       "bf16", 128, 448, 3),
     "qformer": Geometry("qformer", 100, 3, 0, 2, 15, 2048, 32, 64, 0.125,
-                        "f32", 1, 0, 4),
+                        "f32", 1, 0, 4, lift_in=4096),
     # the Large workload over an 8-bit (E4M3) projection cache, same inputs
     "large_fp8": Geometry("large_fp8", 16, 1, 16, 32, 1500, 1280, 20, 64, 0.125,
                           "fp8", 128, 448, 3),
@@ -81,6 +83,7 @@ TENSOR_IDS = {
     "E": 0, "WK": 1, "WV": 2, "WQ": 3, "WO": 4,
     "WQs": 5, "WKs": 6, "WVs": 7, "WOs": 8, "x0": 9,
     "q_cross": 10, "q_self": 11, "k_new": 12, "v_new": 13,
+    "X_lift": 14, "W_lift": 15, "pos": 16,
     "custom": 99,
 }
 
@@ -140,6 +143,15 @@ def workload_tensors(g: Geometry, which=("E", "WK", "WV")) -> dict:
         elif name == "x0":
             n = max(g.n_seqs, 1)
             out[name] = normal([seed, tid], (n, g.d_model), 1.0)
+            continue
+        elif name == "X_lift":   # stands in for the normalised 4-way encoder concat
+            out[name] = normal([seed, tid], (g.n_streams * g.mem_len, g.lift_in), 1.0)
+            continue
+        elif name == "W_lift":
+            out[name] = normal([seed, tid], (g.lift_in, g.d_model), g.w_std)
+            continue
+        elif name == "pos":      # window position embedding, one row per frame of a block
+            out[name] = normal([seed, tid], (g.mem_len, g.d_model), 0.02)
             continue
         else:
             out[name] = [normal([seed, tid, l], (g.d_model, g.hd), g.w_std)

@@ -182,6 +182,19 @@ def test_decoder_step_workspace_and_argument_checks():
         pc.cke_xattn_cache_destroy(h)
 
 
+def test_memory_lift_rejects_bad_arguments_before_launch():
+    L = pc.lib()
+    ok = dict(x=FAKE, rows=30, k_in=64, w=FAKE, n=128, pos=FAKE, pos_rows=15, out=FAKE)
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return L.cke_memory_lift_gelu(a["x"], a["rows"], a["k_in"], a["w"], a["n"], a["pos"],
+                                      a["pos_rows"], a["out"], None)
+    for bad in (dict(x=None), dict(out=None), dict(w=FAKE + 4), dict(rows=0), dict(k_in=48),
+                dict(n=96), dict(pos_rows=0), dict(pos=FAKE + 8)):
+        assert call(**bad) == pc.CKE_EINVAL, bad
+
+
 def test_create_rejects_null_and_misaligned():
     g = base_geom()
     for k, v, w in ((None, FAKE, FAKE), (FAKE, None, FAKE), (FAKE, FAKE, None),

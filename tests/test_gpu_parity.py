@@ -520,7 +520,41 @@ def test_decoder_layer_step_rejects_bad_pairings_on_a_ready_cache():
     assert float(x.abs().max()) == 0.0     # nothing was launched
 
 
-# ------------------------------------------------------------ fp8 caches
+# ------------------------------------------------------ projector memory lift
+LIFT_CASES = [
+    dict(rows=45, k_in=64, n=128, pos_rows=15),     # ragged row tile, three blocks of positions
+    dict(rows=200, k_in=256, n=192, pos_rows=0),    # no positions
+    dict(rows=64, k_in=4096, n=64, pos_rows=15),    # the Q-Former's input width
+]
+
+
+@pytest.mark.parametrize("c", LIFT_CASES, ids=lambda c: "r%d-k%d-n%d-p%d" % tuple(c.values()))
+def test_memory_lift_matches_oracle(c):
+    x = synth.normal([90, 0, c["rows"]], (c["rows"], c["k_in"]))
+    W = synth.normal([90, 1, c["rows"]], (c["k_in"], c["n"]), 0.02)
+    pos = synth.normal([90, 2, c["rows"]], (c["pos_rows"], c["n"]), 0.02) if c["pos_rows"] else None
+    out = torch.full((c["rows"], c["n"]), float("nan"), device=DEV)
+    pc.cke_memory_lift_gelu(t32(x), t32(W), out, None if pos is None else t32(pos))
+    torch.cuda.synchronize()
+    want = oracle.lift_gelu(x, W, pos)
+    assert max_abs(to_np(out), want) <= TOL["f32"]
+
+
+def test_qformer_memory_lift_full_size_sampled():
+    """The Q-Former workload's lift at its full size (1500 x 4096 -> 2048, 15
+    position rows), sampled rows against the oracle."""
+    g = synth.get("qformer")
+    wt = synth.workload_tensors(g, ("X_lift", "W_lift", "pos"))
+    rows = g.n_streams * g.mem_len
+    out = torch.empty(rows, g.d_model, device=DEV)
+    pc.cke_memory_lift_gelu(t32(wt["X_lift"]), t32(wt["W_lift"]), out, t32(wt["pos"]))
+    torch.cuda.synchronize()
+    pick = np.array([0, 1, 14, 15, 733, rows - 1])
+    want = oracle.lift_gelu(wt["X_lift"][pick], wt["W_lift"]) + wt["pos"][pick % g.mem_len]
+    assert max_abs(to_np(out)[pick], want) <= TOL["f32"]
+
+
+
 def fp8_bracket(exact, absdot, dm):
     """Lowest and highest fp8 values a correct populate may store for the
     exact products `exact`. The kernel sums dm products of bf16 values, each
