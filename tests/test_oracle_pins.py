@@ -74,7 +74,8 @@ def test_fp8_cache_decode_error_within_its_bound(dm):
     head, 1500 memory rows, unit-RMS encoder rows, weight std 0.02, bf16
     inputs): decode over the fp8-rounded (and over the bf16-rounded) cache
     stays within the bound above of decode over the exact cache, for queries
-    at the projected-row spread and at 4x it (sharper softmax)."""
+    at the projected-row spread and at 4x it (sharper softmax); the PSNR of
+    the fp8 cache's outputs against the exact ones is at least 35 dB."""
     T, D, scale = 1500, 64, 0.125
     E = synth.bf16_bits_to_f32(synth.to_bf16_bits(synth.normal([900, 0, dm], (1, T, dm))))
     W = [synth.bf16_bits_to_f32(synth.to_bf16_bits(synth.normal([900, k, dm], (dm, D), 0.02)))
@@ -82,19 +83,31 @@ def test_fp8_cache_decode_error_within_its_bound(dm):
     K, V = (oracle.project_head(E[0], w, 0, D) for w in W)
     K8, V8 = oracle.round_fp8(K), oracle.round_fp8(V)
     Kb, Vb = oracle.round_bf16(K), oracle.round_bf16(V)
-    worst = {}
+    worst, psnr = {}, {}
     for spread in (1.0, 4.0):
-        for i in range(4):
+        outs = {"exact": [], "fp8": [], "bf16": []}
+        for i in range(8):
             q = synth.normal([901, i, dm], (D,), 0.02 * math.sqrt(dm) * spread).astype(np.float64)
             exact = oracle.attend(q, K, V, scale)
+            outs["exact"].append(exact)
             for name, (K2, V2) in (("fp8", (K8, V8)), ("bf16", (Kb, Vb))):
-                err = np.abs(oracle.attend(q, K2, V2, scale) - exact)
+                got = oracle.attend(q, K2, V2, scale)
+                outs[name].append(got)
+                err = np.abs(got - exact)
                 assert np.all(err <= _storage_error_bound(q, K, V, K2, V2, scale)), (name, spread, i)
                 worst[(name, spread)] = max(worst.get((name, spread), 0.0), float(err.max()))
-    # the 8-bit cache costs accuracy: its error is well above the bf16 cache's
+        ref = np.array(outs["exact"])
+        for name in ("fp8", "bf16"):
+            rmse = math.sqrt(float(np.mean((np.array(outs[name]) - ref) ** 2)))
+            psnr[(name, spread)] = 20 * math.log10(float(np.abs(ref).max()) / rmse)
+    # the 8-bit cache costs accuracy: its error is well above the bf16 cache's,
+    # yet it passes the 35 dB PSNR gate WhisperKit's CI applies to its
+    # converted models (case study, section 8)
     assert worst[("fp8", 1.0)] > 4 * worst[("bf16", 1.0)]
-    print("decode max-abs error vs exact cache, d_model %d:" % dm,
-          {"%s@%gx" % k: "%.2e" % v for k, v in worst.items()})
+    assert min(v for (n, _), v in psnr.items() if n == "fp8") >= 35.0
+    print("decode vs exact cache, d_model %d: max-abs" % dm,
+          {"%s@%gx" % k: "%.2e" % v for k, v in worst.items()},
+          "PSNR dB", {"%s@%gx" % k: round(v, 1) for k, v in psnr.items()})
 
 
 # ------------------------------------------------------ projector memory lift
