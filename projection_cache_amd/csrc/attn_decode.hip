@@ -1,16 +1,23 @@
 // Decode-time attention kernels for gfx950:
 //   * cross-attention of one query token (per stream, up to NQ of them)
 //     against one layer slab of the projection cache, split over the memory
-//     rows and merged by the last workgroup to finish (C-Kernel-Engine,
-//     "Whisper: Trace One Encoder Tensor into Every Decoder Layer", "View 2":
-//     query_tokens = 1 against all key_tokens rows, head-major K/V);
-//   * fused scatter-append + causal attention over a self-attention KV cache
-//     ("Recurrence as feeds", "What it opened": the cache is an explicit input
-//     and output and the new row is written with scatter).
+//     rows (xattn_partial_kernel) and merged by a second, small kernel
+//     (xattn_merge_kernel), or one wave per head for short memories
+//     (xattn_short_kernel) (C-Kernel-Engine, "Whisper: Trace One Encoder
+//     Tensor into Every Decoder Layer", "View 2": query_tokens = 1 against all
+//     key_tokens rows, head-major K/V);
+//   * the softmax weights of selected heads from the decode's own statistics
+//     (xattn_weights_kernel; WhisperKit case study, section 8);
+//   * fused scatter-append + causal attention over a self-attention KV cache,
+//     one row (selfattn_append_kernel) or several rows with grouped kv heads
+//     (selfattn_prefill_kernel) ("Recurrence as feeds", "What it opened": the
+//     cache is an explicit input and output and the new rows are written with
+//     scatter; WhisperKit case study, sections 3 and 4).
 //
-// Both are HBM-bound streaming kernels (0.5-2.5 FLOP per byte). Each lane
-// reads 16 contiguous bytes of a K row and of a V row, a wave reads whole
-// rows, and every load of a tile is issued before the arithmetic that uses it.
+// All are HBM-bound streaming kernels (0.5-2.5 FLOP per byte). Each lane
+// reads 16 contiguous bytes of a K row and of a V row (4 fp32, 8 bf16 or 16
+// fp8 values), a wave reads whole rows, and every load of a tile is issued
+// before the arithmetic that uses it.
 #include "../../include/cke_xattn.h"
 #include "cke_device.h"
 #include "cke_internal.h"
