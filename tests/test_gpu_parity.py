@@ -468,6 +468,8 @@ STEP_CASES = [
                 head_dim=32, max_pos=16)),                     # one memory row
     (None, dict(n_layers=1, n_streams=1, n_q=1, mem_len=300, d_model=512, n_heads=8,
                 head_dim=64, max_pos=16, dtype="fp8")),        # over an fp8 cache
+    (None, dict(n_layers=2, n_streams=1, n_q=1, mem_len=500, d_model=256, n_heads=8,
+                head_dim=32, max_pos=16)),                     # split cross merged by the product
 ]
 
 
