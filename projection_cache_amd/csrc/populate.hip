@@ -368,6 +368,167 @@ __global__ __launch_bounds__(WGM * WGN * 64) void populate_bf16_big_kernel(GemmA
 }
 
 // fp32 operands on v_mfma_f32_32x32x2_f32 with the same pipeline as the
+// fp32 populate as three bf16 products ("bf16x3"): each fp32 operand x is
+// split while it is staged into x = hi + lo with hi = bf16(x) and
+// lo = bf16(x - hi) (both nearest-even; |x - hi - lo| <= 2^-17 |x|), and the
+// tile product is hi.hi + hi.lo + lo.hi on v_mfma_f32_32x32x16_bf16 with fp32
+// accumulation (the dropped lo.lo term is below 2^-16 of each product). Three
+// bf16 MFMAs do the work of 48 fp32 ones (v_mfma_f32_32x32x2_f32), so this
+// beats the native fp32 path by several times for products of fp32 size.
+// Structure as populate_bf16_big_kernel (register-staged, W transposed while
+// staged, double-buffered LDS), with separate hi and lo tiles for both operands:
+//  * E: each thread loads 16-byte pieces (4 fp32 of one row) and writes their
+//    hi and lo halves (8 bytes each) to Ah[m][k], Al[m][k];
+//  * W: each thread loads an 8(k) x 2(n) block (eight 8-byte row pieces) and
+//    writes, per column, its 8 k values as one 16-byte hi and one 16-byte lo
+//    piece of Bh[n][k], Bl[n][k].
+template <int BM, int BN, int BK, int WGM, int WGN>
+__global__ __launch_bounds__(WGM * WGN * 64) void populate_f32x3_kernel(GemmArgs a, int num_m, int num_n)
+{
+    constexpr int NT = WGM * WGN * 64;
+    constexpr int LDK = BK + 8;
+    constexpr int WTM = BM / WGM, WTN = BN / WGN, MB = WTM / 32, NB = WTN / 32;
+    constexpr int A_VEC = BM * BK / 4 / NT;        // 16-byte E pieces per thread
+    constexpr int B_BLOCKS = (BK / 8) * (BN / 2);   // 8x2 blocks of the W tile
+    constexpr int B_PER = B_BLOCKS >= NT ? B_BLOCKS / NT : 1;
+    constexpr int GROUP_M = 8;
+    static_assert(MB >= 1 && NB >= 1 && A_VEC >= 1 && (BM * BK / 4) % NT == 0, "tile");
+    static_assert(B_BLOCKS % NT == 0 || B_BLOCKS < NT, "W blocks per thread");
+    __shared__ __attribute__((aligned(16))) uint16_t Ah[2][BM * LDK];
+    __shared__ __attribute__((aligned(16))) uint16_t Al[2][BM * LDK];
+    __shared__ __attribute__((aligned(16))) uint16_t Bh[2][BN * LDK];
+    __shared__ __attribute__((aligned(16))) uint16_t Bl[2][BN * LDK];
+
+    const int ntiles = num_m * num_n;
+    const int per_xcd = (ntiles + 7) / 8;
+    const int tile = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+    if (tile >= ntiles) return;
+    const int group = tile / (GROUP_M * num_n);
+    const int first_m = group * GROUP_M;
+    const int gsize = min(num_m - first_m, GROUP_M);
+    const int pid_m = first_m + (tile % (GROUP_M * num_n)) % gsize;
+    const int pid_n = (tile % (GROUP_M * num_n)) / gsize;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / WGN, wn = wave % WGN;
+    const int HD = a.H * a.D;
+    const int m0 = pid_m * BM;
+    const int n0 = pid_n * BN;
+    const int p = n0 / HD;
+    const int col0 = n0 - p * HD;
+    const float* __restrict__ E = static_cast<const float*>(a.E);
+    const float* __restrict__ W = static_cast<const float*>(a.wt.w[p]);
+
+    // split two floats into packed bf16 (hi, lo) words
+    auto split2 = [](float x0, float x1, uint32_t& hi, uint32_t& lo) {
+        const __bf16 h0 = (__bf16)x0, h1 = (__bf16)x1;
+        const __bf16 l0 = (__bf16)(x0 - (float)h0), l1 = (__bf16)(x1 - (float)h1);
+        hi = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+        lo = (uint32_t)__builtin_bit_cast(uint16_t, l0) | ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
+    };
+
+    float4 ra[A_VEC];
+    float2 rb[B_PER][8];
+    auto load_tiles = [&](int k0) {
+#pragma unroll
+        for (int i = 0; i < A_VEC; ++i) {
+            const int idx = tid + i * NT;
+            const int r = idx / (BK / 4), c4 = (idx % (BK / 4)) * 4;
+            const int m = m0 + r;
+            ra[i] = m < a.M ? *reinterpret_cast<const float4*>(E + (size_t)m * a.dm + k0 + c4)
+                            : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+#pragma unroll
+        for (int i = 0; i < B_PER; ++i) {
+            const int blk = tid + i * NT;   // block: k-chunk fastest
+            if (blk < B_BLOCKS) {
+                const int kb8 = blk % (BK / 8), nb2 = blk / (BK / 8);
+                const float* src = W + (size_t)(k0 + kb8 * 8) * HD + col0 + nb2 * 2;
+#pragma unroll
+                for (int r = 0; r < 8; ++r) rb[i][r] = *reinterpret_cast<const float2*>(src + (size_t)r * HD);
+            }
+        }
+    };
+    auto store_tiles = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < A_VEC; ++i) {
+            const int idx = tid + i * NT;
+            const int r = idx / (BK / 4), c4 = (idx % (BK / 4)) * 4;
+            uint32_t h01, l01, h23, l23;
+            split2(ra[i].x, ra[i].y, h01, l01);
+            split2(ra[i].z, ra[i].w, h23, l23);
+            *reinterpret_cast<uint2*>(&Ah[buf][r * LDK + c4]) = make_uint2(h01, h23);
+            *reinterpret_cast<uint2*>(&Al[buf][r * LDK + c4]) = make_uint2(l01, l23);
+        }
+#pragma unroll
+        for (int i = 0; i < B_PER; ++i) {
+            const int blk = tid + i * NT;
+            if (blk < B_BLOCKS) {
+                const int kb8 = blk % (BK / 8), nb2 = blk / (BK / 8);
+                // column n = nb2*2 + j takes k values rb[i][0..7].{x,y}[j]
+                uint32_t h[2][4], l[2][4];
+#pragma unroll
+                for (int kp = 0; kp < 4; ++kp) {
+                    split2(rb[i][2 * kp].x, rb[i][2 * kp + 1].x, h[0][kp], l[0][kp]);
+                    split2(rb[i][2 * kp].y, rb[i][2 * kp + 1].y, h[1][kp], l[1][kp]);
+                }
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const int n = nb2 * 2 + j;
+                    *reinterpret_cast<uint4*>(&Bh[buf][n * LDK + kb8 * 8]) =
+                        make_uint4(h[j][0], h[j][1], h[j][2], h[j][3]);
+                    *reinterpret_cast<uint4*>(&Bl[buf][n * LDK + kb8 * 8]) =
+                        make_uint4(l[j][0], l[j][1], l[j][2], l[j][3]);
+                }
+            }
+        }
+    };
+
+    f32x16 acc[MB][NB];
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+    load_tiles(0);
+    store_tiles(0);
+    __syncthreads();
+    const int nk = a.dm / BK;
+    for (int kt = 0; kt < nk; ++kt) {
+        const int buf = kt & 1;
+        if (kt + 1 < nk) load_tiles((kt + 1) * BK);
+#pragma unroll
+        for (int kk = 0; kk < BK; kk += 16) {
+            bf16x8 ah[MB], al[MB], bh[NB], bl[NB];
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) {
+                const int off = (wm * WTM + mb * 32 + (lane & 31)) * LDK + kk + 8 * (lane >> 5);
+                ah[mb] = *reinterpret_cast<const bf16x8*>(&Ah[buf][off]);
+                al[mb] = *reinterpret_cast<const bf16x8*>(&Al[buf][off]);
+            }
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                const int off = (wn * WTN + nb * 32 + (lane & 31)) * LDK + kk + 8 * (lane >> 5);
+                bh[nb] = *reinterpret_cast<const bf16x8*>(&Bh[buf][off]);
+                bl[nb] = *reinterpret_cast<const bf16x8*>(&Bl[buf][off]);
+            }
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) {
+                    acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[mb], bh[nb], acc[mb][nb], 0, 0, 0);
+                    acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[mb], bl[nb], acc[mb][nb], 0, 0, 0);
+                    acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[mb], bh[nb], acc[mb][nb], 0, 0, 0);
+                }
+        }
+        if (kt + 1 < nk) store_tiles(buf ^ 1);
+        __syncthreads();
+    }
+    epilogue<BM, BN, WGM, WGN, float>(a, acc, m0, p, col0);
+}
+
 // bf16 kernel: both tiles staged k-major in LDS (As[k][m] transposed while
 // storing, Bs[k][n] as loaded) so a half-wave reads 32 consecutive floats per
 // operand; the next k-tile is prefetched into registers during the MFMA loop
@@ -1108,6 +1269,18 @@ hipError_t launch_bf16_big(const GemmArgs& g, hipStream_t st) {
     return hipGetLastError();
 }
 
+template <int BM, int BN, int BK, int WGM, int WGN>
+hipError_t launch_f32x3(const GemmArgs& g, hipStream_t st) {
+    const int HD = g.H * g.D;
+    const int num_m = (g.M + BM - 1) / BM;
+    const int num_n = 2 * g.L * HD / BN;
+    const int ntiles = num_m * num_n;
+    const int grid = ((ntiles + 7) / 8) * 8;
+    hipLaunchKernelGGL((populate_f32x3_kernel<BM, BN, BK, WGM, WGN>), dim3(grid), dim3(WGM * WGN * 64), 0,
+                       st, g, num_m, num_n);
+    return hipGetLastError();
+}
+
 template <int BM, int BN, int WGM, int WGN>
 hipError_t launch_cfg(const GemmArgs& g, bool bf16, hipStream_t st) {
     const int HD = g.H * g.D;
@@ -1123,6 +1296,8 @@ hipError_t launch_cfg(const GemmArgs& g, bool bf16, hipStream_t st) {
 
 // Projector memory lift: out = gelu(x . W) (+ positions), fp32, on the fp32
 // DMA populate kernel with a token-major epilogue. One weight, N = n columns.
+// (The three-bf16-product kernel's 128 x 128 tiles give the Q-Former lift's
+// 1500 x 2048 output only 192 tiles for 256 compute units; it measured slower.)
 hipError_t launch_lift(const LiftLaunch& a, hipStream_t st) {
     if (a.rows < 1 || a.k_in % 32 != 0 || a.n % 64 != 0 || (a.pos && a.pos_rows < 1))
         return hipErrorInvalidValue;
@@ -1173,6 +1348,17 @@ hipError_t launch_populate(const PopulateLaunch& a, hipStream_t st) {
     }
     if (a.bf16 && HD % 256 == 0 && a.dm % 32 == 0) return launch_bf16_w4<256, 256, CKE_POP_W4_SLOTS, false>(g, st);
     if (a.bf16 && HD % 128 == 0 && a.dm % 64 == 0) return launch_bf16_big<128, 128, 64, 2, 2>(g, st);
+#ifndef CKE_POP_F32X3
+#define CKE_POP_F32X3 1
+#endif
+#ifndef CKE_POP_X3_BM
+#define CKE_POP_X3_BM 128
+#endif
+#ifndef CKE_POP_X3_BK
+#define CKE_POP_X3_BK 32
+#endif
+    if (CKE_POP_F32X3 && !a.bf16 && HD % CKE_POP_X3_BM == 0 && a.dm % CKE_POP_X3_BK == 0)
+        return launch_f32x3<CKE_POP_X3_BM, CKE_POP_X3_BM, CKE_POP_X3_BK, 2, 2>(g, st);
 #ifndef CKE_POP_F32_DMA
 #define CKE_POP_F32_DMA 3
 #endif
