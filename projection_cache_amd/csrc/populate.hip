@@ -529,127 +529,6 @@ __global__ __launch_bounds__(WGM * WGN * 64) void populate_f32x3_kernel(GemmArgs
     epilogue<BM, BN, WGM, WGN, float>(a, acc, m0, p, col0);
 }
 
-// bf16 kernel: both tiles staged k-major in LDS (As[k][m] transposed while
-// storing, Bs[k][n] as loaded) so a half-wave reads 32 consecutive floats per
-// operand; the next k-tile is prefetched into registers during the MFMA loop
-// into a second LDS buffer (one barrier per k-tile); same tile order.
-template <int BM, int BN, int BK, int WGM, int WGN>
-__global__ __launch_bounds__(WGM * WGN * 64) void populate_f32_big_kernel(GemmArgs a, int num_m, int num_n)
-{
-    constexpr int NT = WGM * WGN * 64;
-    constexpr int WTM = BM / WGM, WTN = BN / WGN, MB = WTM / 32, NB = WTN / 32;
-    constexpr int A_VEC = BM * BK / 4 / NT;   // float4 pieces per thread
-    constexpr int B_VEC = BK * BN / 4 / NT;
-    constexpr int LDM = BM + 4, LDN = BN + 4;
-    constexpr int GROUP_M = 8;
-    static_assert(MB >= 1 && NB >= 1 && A_VEC >= 1 && B_VEC >= 1, "tile");
-    static_assert((BM * BK / 4) % NT == 0 && (BK * BN / 4) % NT == 0, "tile");
-    __shared__ __attribute__((aligned(16))) float As[2][BK * LDM];
-    __shared__ __attribute__((aligned(16))) float Bs[2][BK * LDN];
-
-    const int ntiles = num_m * num_n;
-    const int per_xcd = (ntiles + 7) / 8;
-    const int tile = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
-    if (tile >= ntiles) return;
-    const int group = tile / (GROUP_M * num_n);
-    const int first_m = group * GROUP_M;
-    const int gsize = min(num_m - first_m, GROUP_M);
-    const int pid_m = first_m + (tile % (GROUP_M * num_n)) % gsize;
-    const int pid_n = (tile % (GROUP_M * num_n)) / gsize;
-
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave / WGN, wn = wave % WGN;
-    const int HD = a.H * a.D;
-    const int m0 = pid_m * BM;
-    const int n0 = pid_n * BN;
-    const int p = n0 / HD;
-    const int col0 = n0 - p * HD;
-    const float* __restrict__ E = static_cast<const float*>(a.E);
-    const float* __restrict__ W = static_cast<const float*>(a.wt.w[p]);
-
-    float4 ra[A_VEC], rb[B_VEC];
-    auto load_tiles = [&](int k0) {
-#pragma unroll
-        for (int i = 0; i < A_VEC; ++i) {
-            const int idx = tid + i * NT;
-            const int r = idx / (BK / 4), c4 = (idx % (BK / 4)) * 4;
-            const int m = m0 + r;
-            ra[i] = m < a.M ? *reinterpret_cast<const float4*>(E + (size_t)m * a.dm + k0 + c4)
-                            : make_float4(0.f, 0.f, 0.f, 0.f);
-        }
-#pragma unroll
-        for (int i = 0; i < B_VEC; ++i) {
-            const int idx = tid + i * NT;
-            const int r = idx / (BN / 4), c4 = (idx % (BN / 4)) * 4;
-            rb[i] = *reinterpret_cast<const float4*>(W + (size_t)(k0 + r) * HD + col0 + c4);
-        }
-    };
-    auto store_tiles = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < A_VEC; ++i) {
-            const int idx = tid + i * NT;
-            const int r = idx / (BK / 4), c4 = (idx % (BK / 4)) * 4;
-            As[buf][(c4 + 0) * LDM + r] = ra[i].x;
-            As[buf][(c4 + 1) * LDM + r] = ra[i].y;
-            As[buf][(c4 + 2) * LDM + r] = ra[i].z;
-            As[buf][(c4 + 3) * LDM + r] = ra[i].w;
-        }
-#pragma unroll
-        for (int i = 0; i < B_VEC; ++i) {
-            const int idx = tid + i * NT;
-            const int r = idx / (BN / 4), c4 = (idx % (BN / 4)) * 4;
-            *reinterpret_cast<float4*>(&Bs[buf][r * LDN + c4]) = rb[i];
-        }
-    };
-
-    f32x16 acc[MB][NB];
-#pragma unroll
-    for (int i = 0; i < MB; ++i)
-#pragma unroll
-        for (int j = 0; j < NB; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-
-    load_tiles(0);
-    store_tiles(0);
-    __syncthreads();
-    const int nk = a.dm / BK;
-    for (int kt = 0; kt < nk; ++kt) {
-        const int buf = kt & 1;
-        if (kt + 1 < nk) load_tiles((kt + 1) * BK);
-#pragma unroll
-        for (int kk = 0; kk < BK; kk += 2) {
-            float av[MB], bv[NB];
-#pragma unroll
-            for (int mb = 0; mb < MB; ++mb)
-                av[mb] = As[buf][(kk + (lane >> 5)) * LDM + wm * WTM + mb * 32 + (lane & 31)];
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb)
-                bv[nb] = Bs[buf][(kk + (lane >> 5)) * LDN + wn * WTN + nb * 32 + (lane & 31)];
-#pragma unroll
-            for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-                for (int nb = 0; nb < NB; ++nb)
-                    acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[mb], bv[nb], acc[mb][nb], 0, 0, 0);
-        }
-        if (kt + 1 < nk) store_tiles(buf ^ 1);
-        __syncthreads();
-    }
-    epilogue<BM, BN, WGM, WGN, float>(a, acc, m0, p, col0);
-}
-
-template <int BM, int BN, int BK, int WGM, int WGN>
-hipError_t launch_f32_big(const GemmArgs& g, hipStream_t st) {
-    const int HD = g.H * g.D;
-    const int num_m = (g.M + BM - 1) / BM;
-    const int num_n = 2 * g.L * HD / BN;
-    const int ntiles = num_m * num_n;
-    const int grid = ((ntiles + 7) / 8) * 8;
-    hipLaunchKernelGGL((populate_f32_big_kernel<BM, BN, BK, WGM, WGN>), dim3(grid),
-                       dim3(WGM * WGN * 64), 0, st, g, num_m, num_n);
-    return hipGetLastError();
-}
-
 constexpr int vmcnt_wait(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
 
 // LDS byte address of a pointer into __shared__ memory.
@@ -1367,24 +1246,6 @@ hipError_t launch_populate(const PopulateLaunch& a, hipStream_t st) {
 #endif
     if (!a.bf16 && HD % 64 == 0 && a.D <= 64 && 64 % a.D == 0 && a.dm % CKE_POP_F32_DMA_BK == 0)
         return launch_f32_dma<CKE_POP_F32_DMA, CKE_POP_F32_DMA_BK>(g, st);
-#ifndef CKE_POP_F32_BM
-#define CKE_POP_F32_BM 64
-#endif
-#ifndef CKE_POP_F32_BN
-#define CKE_POP_F32_BN 64
-#endif
-#ifndef CKE_POP_F32_BK
-#define CKE_POP_F32_BK 16
-#endif
-#ifndef CKE_POP_F32_WGM
-#define CKE_POP_F32_WGM 2
-#endif
-#ifndef CKE_POP_F32_WGN
-#define CKE_POP_F32_WGN 2
-#endif
-    if (!a.bf16 && HD % CKE_POP_F32_BN == 0 && a.dm % CKE_POP_F32_BK == 0)
-        return launch_f32_big<CKE_POP_F32_BM, CKE_POP_F32_BN, CKE_POP_F32_BK, CKE_POP_F32_WGM,
-                              CKE_POP_F32_WGN>(g, st);
     if (HD % 128 == 0) return launch_cfg<128, 128, 2, 2>(g, a.bf16, st);
     if (HD % 64 == 0) return launch_cfg<64, 64, 2, 2>(g, a.bf16, st);
     return launch_cfg<128, 32, 4, 1>(g, a.bf16, st);
