@@ -648,6 +648,15 @@ __device__ __forceinline__ void mfma_frags_t(
             acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.w[nb], f.e[mb], acc[nb][mb], 0, 0, 0);
 }
 
+// Two floats to packed bf16 (nearest-even), the first in the low half: one
+// v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const f32x2 f = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
+}
+
 // Store a transposed accumulator tile (acc[nb][mb] holds C^T: register r of
 // lane L is output column n = 8*(r/4) + 4*(L/32) + r%4 and output row
 // m = L%32 of its 32x32 block; four consecutive columns of one row lie in one
@@ -682,8 +691,8 @@ __device__ __forceinline__ void epilogue_t_lds(
                 const int m = wm * T::WTM + mb * 32 + (lane & 31);
                 const f32x16& v = acc[nb][mb];
                 uint2 w;
-                w.x = (uint32_t)to_bf16_bits(v[4 * g]) | ((uint32_t)to_bf16_bits(v[4 * g + 1]) << 16);
-                w.y = (uint32_t)to_bf16_bits(v[4 * g + 2]) | ((uint32_t)to_bf16_bits(v[4 * g + 3]) << 16);
+                w.x = pack_bf16x2(v[4 * g], v[4 * g + 1]);
+                w.y = pack_bf16x2(v[4 * g + 2], v[4 * g + 3]);
                 const int off = ((j * BM + m) << lgD) + ((q ^ (m & (PD - 1))) << 3) +
                                 ((half ^ ((m >> 3) & 1)) << 2);
                 *reinterpret_cast<uint2*>(stage + off) = w;
@@ -696,23 +705,27 @@ __device__ __forceinline__ void epilogue_t_lds(
     const int h0 = col0 >> lgD;
     const int b0 = m0 / a.T, t0 = m0 - b0 * a.T;
     const int tid = threadIdx.x;
-    constexpr int PIECES = BM * BN / 8;
-#pragma unroll 4
-    for (int id = tid; id < PIECES; id += NT) {
-        const int q = id & (PD - 1);
-        const int m = (id >> lgP) & (BM - 1);
-        const int j = id >> (lgP + 8);    // BM == 256 rows per head block
-        if (m0 + m < a.M) {
-            int t = t0 + m, b = b0;
-            if (t >= a.T) {
-                if (a.T >= BM) { t -= a.T; b += 1; }
-                else { b += t / a.T; t -= (t / a.T) * a.T; }
-            }
-            const int off = ((j * BM + m) << lgD) + ((q ^ (m & (PD - 1))) << 3);
-            uint4 v = *reinterpret_cast<const uint4*>(stage + off);
-            if ((m >> 3) & 1) { const uint32_t x = v.x, y = v.y; v.x = v.z; v.y = v.w; v.z = x; v.w = y; }
-            const size_t idx = ((size_t)(l * a.B + b) * a.H + h0 + j) * TD + (size_t)t * a.D + q * 8;
-            *reinterpret_cast<uint4*>(C + idx) = v;
+    // Thread tid always stores 16-byte piece q of its rows m = tid / PD + r * (NT / PD),
+    // r < PD, in each of the tile's BN / D heads: one row address per r, then one
+    // add per head.
+    const int q = tid & (PD - 1);
+    const int mstep = NT >> lgP;
+    const int heads = BN >> lgD;
+    for (int r = 0; r < PD; ++r) {
+        const int m = (tid >> lgP) + r * mstep;
+        if (m0 + m >= a.M) break;   // m grows with r
+        int t = t0 + m, b = b0;
+        if (t >= a.T) {
+            if (a.T >= BM) { t -= a.T; b += 1; }
+            else { b += t / a.T; t -= (t / a.T) * a.T; }
+        }
+        const int soff = (m << lgD) + ((q ^ (m & (PD - 1))) << 3);
+        const bool swap = (m >> 3) & 1;
+        uint16_t* dst = C + ((size_t)(l * a.B + b) * a.H + h0) * TD + (size_t)t * a.D + q * 8;
+        for (int j = 0; j < heads; ++j) {
+            uint4 v = *reinterpret_cast<const uint4*>(stage + soff + ((j * BM) << lgD));
+            if (swap) { const uint32_t x = v.x, y = v.y; v.x = v.z; v.y = v.w; v.z = x; v.w = y; }
+            *reinterpret_cast<uint4*>(dst + j * TD) = v;
         }
     }
 }
@@ -759,25 +772,26 @@ __device__ __forceinline__ void epilogue_t_lds_fp8(
     const int h0 = col0 >> lgD;
     const int b0 = m0 / a.T, t0 = m0 - b0 * a.T;
     const int tid = threadIdx.x;
-    constexpr int PIECES = BM * BN / 16;
-#pragma unroll 4
-    for (int id = tid; id < PIECES; id += NT) {
-        const int q = id & (PD - 1);
-        const int m = (id >> lgP) & (BM - 1);
-        const int j = id >> (lgP + 8);    // BM == 256 rows per head block
-        if (m0 + m < a.M) {
-            int t = t0 + m, b = b0;
-            if (t >= a.T) {
-                if (a.T >= BM) { t -= a.T; b += 1; }
-                else { b += t / a.T; t -= (t / a.T) * a.T; }
-            }
-            const int off = ((j * BM + m) << lgD) + ((q ^ (m & (PD - 1))) << 4);
-            uint4 v = *reinterpret_cast<const uint4*>(stage + off);
-            const int r = (m >> 2) & 3;   // word k of the piece sits at k ^ r
-            if (r & 1) { uint32_t x = v.x; v.x = v.y; v.y = x; x = v.z; v.z = v.w; v.w = x; }
-            if (r & 2) { uint32_t x = v.x; v.x = v.z; v.z = x; x = v.y; v.y = v.w; v.w = x; }
-            const size_t idx = ((size_t)(l * a.B + b) * a.H + h0 + j) * TD + (size_t)t * a.D + q * 16;
-            *reinterpret_cast<uint4*>(C + idx) = v;
+    // as in epilogue_t_lds: piece q of rows m = tid / PD + r * (NT / PD) in every head
+    const int q = tid & (PD - 1);
+    const int mstep = NT >> lgP;
+    const int heads = BN >> lgD;
+    for (int r = 0; r < PD; ++r) {
+        const int m = (tid >> lgP) + r * mstep;
+        if (m0 + m >= a.M) break;   // m grows with r
+        int t = t0 + m, b = b0;
+        if (t >= a.T) {
+            if (a.T >= BM) { t -= a.T; b += 1; }
+            else { b += t / a.T; t -= (t / a.T) * a.T; }
+        }
+        const int soff = (m << lgD) + ((q ^ (m & (PD - 1))) << 4);
+        const int rot = (m >> 2) & 3;   // word k of the piece sits at k ^ rot
+        uint8_t* dst = C + ((size_t)(l * a.B + b) * a.H + h0) * TD + (size_t)t * a.D + q * 16;
+        for (int j = 0; j < heads; ++j) {
+            uint4 v = *reinterpret_cast<const uint4*>(stage + soff + ((j * BM) << lgD));
+            if (rot & 1) { uint32_t x = v.x; v.x = v.y; v.y = x; x = v.z; v.z = v.w; v.w = x; }
+            if (rot & 2) { uint32_t x = v.x; v.x = v.z; v.z = x; x = v.y; v.y = v.w; v.w = x; }
+            *reinterpret_cast<uint4*>(dst + j * TD) = v;
         }
     }
 }
