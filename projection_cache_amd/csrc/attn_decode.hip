@@ -74,7 +74,7 @@ __global__ __launch_bounds__(NW * 64) void xattn_partial_kernel(
 
     WaveState<NQ, VEC> st;
     st.init();
-    wave_attend<D, TE, NQ, NP, STREAM>(K, V, r0, r1, qr, nq, sl2, -1, nullptr, nullptr, st);
+    wave_attend<D, TE, NQ, NP, STREAM>(K, V, r0, r1, qr, nq, sl2, st);
     wg_merge<D, TE, NQ, NW>(st, nq, wm, wl, wa, sM, sL, sA);
 
     if (nsplit == 1) {
@@ -199,7 +199,7 @@ __global__ __launch_bounds__(NW * 64) void xattn_short_kernel(
     }
     WaveState<NQ, VEC> st;
     st.init();
-    wave_attend<D, TE, NQ, NP>(K, V, 0, T, qr, nq, sl2, -1, nullptr, nullptr, st);
+    wave_attend<D, TE, NQ, NP>(K, V, 0, T, qr, nq, sl2, st);
     wave_merge_groups<D, TE, NQ>(st, nq);
     if (lane < LPK) {
 #pragma unroll
@@ -245,30 +245,32 @@ __global__ __launch_bounds__(NW * 64) void selfattn_append_kernel(
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
     const int sub = lane % LPK;
 
-    // scatter the new row; no wave reads it from memory (wave_attend takes it
-    // from k_new / v_new)
-    for (int d = threadIdx.x; d < D; d += NW * 64) {
-        if constexpr (sizeof(TE) == 2) {
-            K[(size_t)pos * D + d] = to_bf16_bits(kn[d]);
-            V[(size_t)pos * D + d] = to_bf16_bits(vn[d]);
-        } else {
-            K[(size_t)pos * D + d] = kn[d];
-            V[(size_t)pos * D + d] = vn[d];
-        }
-    }
-
-    float qr[1][VEC];
-#pragma unroll
-    for (int j = 0; j < VEC; ++j) qr[0][j] = q[bh * D + sub * VEC + j];
-
     const int n = pos + 1;
     const int per_wave = ((n + NW * KPW - 1) / (NW * KPW)) * KPW;
     const int r0 = min(n, w * per_wave);
     const int r1 = min(n, r0 + per_wave);
+    const bool has_cur = r0 <= pos && pos < r1;   // this wave's range ends with row pos
+
+    // Loads first: the new row's fp32 source (only the wave that owns row pos),
+    // the query, then the cache rows 0..pos-1 inside wave_attend; the new row
+    // is rounded and folded in after them, so no load waits for another.
+    CurRow<TE> ckr{}, cvr{};
+    if (has_cur) {
+        ckr = load_cur<TE>(kn + sub * VEC);
+        cvr = load_cur<TE>(vn + sub * VEC);
+    }
+    float qr[1][VEC];
+#pragma unroll
+    for (int j = 0; j < VEC; ++j) qr[0][j] = q[bh * D + sub * VEC + j];
 
     WaveState<1, VEC> st;
     st.init();
-    wave_attend<D, TE, 1, NP>(K, V, r0, r1, qr, 1, sl2, pos, kn, vn, st);
+    wave_attend<D, TE, 1, NP>(K, V, r0, min(r1, pos), qr, 1, sl2, st);
+    if (has_cur) {
+        keep_below(ckr);
+        keep_below(cvr);
+        fold_row<D, TE, 1>(pos, pack_cur<TE>(ckr), pack_cur<TE>(cvr), lane / LPK, qr, 1, sl2, st);
+    }
     if constexpr (NW == 1) {
         // one wave holds every row: no cross-wave merge, no barrier
         wave_merge_groups<D, TE, 1>(st, 1);
@@ -279,6 +281,18 @@ __global__ __launch_bounds__(NW * 64) void selfattn_append_kernel(
     } else {
         wg_merge<D, TE, 1, NW>(st, 1, wm, wl, wa, sM, sL, sA);
         for (int d = threadIdx.x; d < D; d += NW * 64) out[bh * D + d] = sA[d] / sL[0];
+    }
+    // Scatter the new row last. No wave reads it from memory (its owner folds
+    // it in from k_new / v_new), and stored earlier its loads and stores would
+    // come before, and delay, the cache-row loads.
+    for (int d = threadIdx.x; d < D; d += NW * 64) {
+        if constexpr (sizeof(TE) == 2) {
+            K[(size_t)pos * D + d] = to_bf16_bits(kn[d]);
+            V[(size_t)pos * D + d] = to_bf16_bits(vn[d]);
+        } else {
+            K[(size_t)pos * D + d] = kn[d];
+            V[(size_t)pos * D + d] = vn[d];
+        }
     }
 }
 

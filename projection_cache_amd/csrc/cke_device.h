@@ -94,28 +94,45 @@ __device__ __forceinline__ uint32_t pack4_fp8(float a, float b, float c, float d
     return (uint32_t)pack2_fp8<true>(c, d, pack2_fp8<false>(a, b, 0));
 }
 
-// The same 16-byte share built from an fp32 source row, rounded to the
-// storage type (the row a self-attention call appends: attention reads the
-// value as stored).
-template <typename TE> __device__ __forceinline__ uint4 pack16_from_f32(const float* __restrict__ p);
-template <> __device__ __forceinline__ uint4 pack16_from_f32<float>(const float* __restrict__ p) {
-    return *reinterpret_cast<const uint4*>(p);
+// The same 16-byte share of the row a self-attention call appends, from its
+// fp32 source: load_cur reads the source (16 / sizeof(TE) floats) and
+// pack_cur rounds it to the storage type, since attention reads the value as
+// stored. Separate steps, so that a kernel can issue the source loads first
+// and round the values only after its cache-row loads.
+template <typename TE> struct CurRow { float4 f[16 / sizeof(TE) / 4]; };
+template <typename TE>
+__device__ __forceinline__ CurRow<TE> load_cur(const float* __restrict__ p) {
+    CurRow<TE> r;
+#pragma unroll
+    for (int k = 0; k < (int)(16 / sizeof(TE) / 4); ++k) r.f[k] = reinterpret_cast<const float4*>(p)[k];
+    return r;
 }
-template <> __device__ __forceinline__ uint4 pack16_from_f32<uint16_t>(const float* __restrict__ p) {
-    const float4 a = *reinterpret_cast<const float4*>(p);
-    const float4 b = *reinterpret_cast<const float4*>(p + 4);
+// An empty statement that takes r's registers as in/out operands and clobbers
+// memory. Placed after a kernel's cache-row loads it keeps the rounding of r
+// below them: the compiler would otherwise hoist that pure arithmetic up to
+// the source loads and wait for them there, before any cache-row load.
+template <typename TE>
+__device__ __forceinline__ void keep_below(CurRow<TE>& r) {
+#pragma unroll
+    for (int k = 0; k < (int)(16 / sizeof(TE) / 4); ++k)
+        asm volatile("" : "+v"(r.f[k].x), "+v"(r.f[k].y), "+v"(r.f[k].z), "+v"(r.f[k].w) : : "memory");
+}
+template <typename TE> __device__ __forceinline__ uint4 pack_cur(const CurRow<TE>& r);
+template <> __device__ __forceinline__ uint4 pack_cur<float>(const CurRow<float>& r) {
+    const float4 a = r.f[0];
+    return make_uint4(__float_as_uint(a.x), __float_as_uint(a.y), __float_as_uint(a.z), __float_as_uint(a.w));
+}
+template <> __device__ __forceinline__ uint4 pack_cur<uint16_t>(const CurRow<uint16_t>& r) {
+    const float4 a = r.f[0], b = r.f[1];
     auto pk = [](float lo, float hi) {
         return (uint32_t)to_bf16_bits(lo) | ((uint32_t)to_bf16_bits(hi) << 16);
     };
     return make_uint4(pk(a.x, a.y), pk(a.z, a.w), pk(b.x, b.y), pk(b.z, b.w));
 }
-template <> __device__ __forceinline__ uint4 pack16_from_f32<uint8_t>(const float* __restrict__ p) {
+template <> __device__ __forceinline__ uint4 pack_cur<uint8_t>(const CurRow<uint8_t>& r) {
     uint32_t w[4];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const float4 a = *reinterpret_cast<const float4*>(p + 4 * k);
-        w[k] = pack4_fp8(a.x, a.y, a.z, a.w);
-    }
+    for (int k = 0; k < 4; ++k) w[k] = pack4_fp8(r.f[k].x, r.f[k].y, r.f[k].z, r.f[k].w);
     return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
@@ -258,49 +275,45 @@ __device__ __forceinline__ void compute_tile(int base, int r1, int cur_row, bool
 // apart; r0, r1 wave-uniform). Rows are read in tiles of NP passes; the
 // loads of the next tile are issued before the current tile is computed
 // (register double buffering), so each wave keeps up to 2*NP 16-byte loads
-// per operand in flight. If cur_row lies in the range it must be its last row
-// (r1 - 1): that row's values are taken from the fp32 vectors cur_k / cur_v
-// (rounded to the storage type) and its memory is never read, so the caller
-// may be writing it concurrently.
+// per operand in flight.
 template <int D, typename TE, int NQ, int NP, bool STREAM = false>
 __device__ __forceinline__ void wave_attend(
     const TE* __restrict__ K, const TE* __restrict__ V, int r0, int r1,
     const float (&q)[NQ][RowMap<D, TE>::kVec], int nq, float sl2,
-    int cur_row, const float* __restrict__ cur_k, const float* __restrict__ cur_v,
     WaveState<NQ, RowMap<D, TE>::kVec>& st)
 {
     using RM = RowMap<D, TE>;
-    constexpr int VEC = RM::kVec, LPK = RM::kLPK, KPW = RM::kKPW;
+    constexpr int LPK = RM::kLPK, KPW = RM::kKPW;
     constexpr int TILE = NP * KPW;
     const int lane = threadIdx.x & 63;
     const int grp = lane / LPK;
     const int sub = lane % LPK;
     if (r0 >= r1) return;
 
-    const bool has_cur = cur_row >= r0 && cur_row < r1;
-    uint4 ck = make_uint4(0u, 0u, 0u, 0u), cv = ck;
-    if (has_cur) {
-        ck = pack16_from_f32<TE>(cur_k + sub * VEC);
-        cv = pack16_from_f32<TE>(cur_v + sub * VEC);
-    }
-    // last row that may be read from memory; a wave holding only the current
-    // row reads nothing
-    const int r_safe = has_cur ? r1 - 2 : r1 - 1;
+    const uint4 none = make_uint4(0u, 0u, 0u, 0u);
+    const int r_safe = r1 - 1;   // last row that may be read
     uint4 ka[NP], va[NP], kb2[NP], vb2[NP];
-    if (r_safe >= r0) {
-        load_tile<D, TE, NP, STREAM>(K, V, r0, r_safe, grp, sub, ka, va);
-    } else {
-#pragma unroll
-        for (int p = 0; p < NP; ++p) ka[p] = va[p] = make_uint4(0u, 0u, 0u, 0u);
-    }
+    load_tile<D, TE, NP, STREAM>(K, V, r0, r_safe, grp, sub, ka, va);
     for (int base = r0; base < r1; base += 2 * TILE) {
         const bool more = base + TILE < r1;
         if (more) load_tile<D, TE, NP, STREAM>(K, V, base + TILE, r_safe, grp, sub, kb2, vb2);
-        compute_tile<D, TE, NQ, NP>(base, r1, cur_row, has_cur, ck, cv, grp, q, nq, sl2, ka, va, st);
+        compute_tile<D, TE, NQ, NP>(base, r1, -1, false, none, none, grp, q, nq, sl2, ka, va, st);
         if (!more) break;
         if (base + 2 * TILE < r1) load_tile<D, TE, NP, STREAM>(K, V, base + 2 * TILE, r_safe, grp, sub, ka, va);
-        compute_tile<D, TE, NQ, NP>(base + TILE, r1, cur_row, has_cur, ck, cv, grp, q, nq, sl2, kb2, vb2, st);
+        compute_tile<D, TE, NQ, NP>(base + TILE, r1, -1, false, none, none, grp, q, nq, sl2, kb2, vb2, st);
     }
+}
+
+// Fold one row held in registers (ck, cv: this lane's 16-byte shares) into
+// the running state, as the row `row` of a one-pass tile whose other rows
+// are masked: lane group 0 takes it, every other group sees only masked rows.
+template <int D, typename TE, int NQ>
+__device__ __forceinline__ void fold_row(int row, const uint4& ck, const uint4& cv, int grp,
+                                         const float (&q)[NQ][RowMap<D, TE>::kVec], int nq, float sl2,
+                                         WaveState<NQ, RowMap<D, TE>::kVec>& st)
+{
+    const uint4 zero[1] = {make_uint4(0u, 0u, 0u, 0u)};
+    compute_tile<D, TE, NQ, 1>(row, row + 1, row, true, ck, cv, grp, q, nq, sl2, zero, zero, st);
 }
 
 // compute_tile for causal groups of queries: query i only sees rows below
