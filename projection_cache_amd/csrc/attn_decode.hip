@@ -446,8 +446,11 @@ hipError_t launch_cross_nq(const XattnLaunch& a, hipStream_t st) {
                            n_bh, a.scale * kLog2e);
         return hipGetLastError();
     }
-    // many queries already give each loaded row more work: keep their tiles short
-    constexpr int NP = (NQ > 2 && kCrossNP > 2) ? 2 : kCrossNP;
+    // With more than two queries, bf16 and fp8 rows (8 or 16 values per lane)
+    // keep their tiles short: long ones cost registers (fp8 spills from four
+    // queries on). fp32 rows (4 values per lane) keep full tiles at any query
+    // count, 167 registers at most (Beam's 5 queries: 11.3 against 11.75 us).
+    constexpr int NP = (NQ > 2 && sizeof(TE) < 4 && kCrossNP > 2) ? 2 : kCrossNP;
     dim3 grid(a.nsplit, a.H, a.B);
     if (a.stream_rows)
         hipLaunchKernelGGL((xattn_partial_kernel<D, TE, NQ, kCrossWaves, NP, true>), grid,

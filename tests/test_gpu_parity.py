@@ -307,17 +307,17 @@ def test_self_append_attend_matches_oracle(c):
     scale = 1 / math.sqrt(D)
     std = 0.02 * math.sqrt(H * D)
     worst = 0.0
-    positions = list(range(P)) if P <= 70 else list(range(P))
-    for pos in positions:
+    # every position: the wave that owns row pos changes with pos, and so do
+    # the waves per workgroup the launcher picks
+    for pos in range(P):
         key = [31, S, H, D, P, pos]
         q = synth.normal(key + [0], (S, H, D), std)
         kn = synth.normal(key + [1], (S, H, D), std)
         vn = synth.normal(key + [2], (S, H, D), std)
         out = kv.append_attend(t32(q), t32(kn), t32(vn), pos, scale)
         want = oracle.self_append_attend(q, kn, vn, Ks, Vs, pos, scale, round_bf16=bf)
-        if pos % 7 == 0 or pos == P - 1:
-            torch.cuda.synchronize()
-            worst = max(worst, max_abs(to_np(out), want))
+        torch.cuda.synchronize()
+        worst = max(worst, max_abs(to_np(out), want))
     torch.cuda.synchronize()
     assert worst <= 1e-4
     # the stored rows are exactly the scattered (rounded) inputs
