@@ -293,6 +293,8 @@ SELF_CASES = [
     dict(S=2, H=2, D=128, P=33, dtype="f32"),
     dict(S=2, H=3, D=128, P=33, dtype="bf16"),
     dict(S=2, H=2, D=64, P=200, dtype="bf16"),       # bf16 rows past 4 load tiles
+    dict(S=2, H=2, D=32, P=1, dtype="f32"),          # capacity 1: only the new row, never a cache row
+    dict(S=7, H=3, D=64, P=17, dtype="bf16"),        # odd sequence and head counts
 ]
 
 
