@@ -264,6 +264,20 @@ def cpu_baseline(name, budget_s, threads=None):
             "host_cpu": _host_cpu()}
 
 
+# HBM bandwidth x loaded latency (8 TB/s x ~2 us): a call that moves fewer bytes
+# than this cannot keep enough requests in flight to approach the peak, so its
+# time is set by latency and launch cost, not by bandwidth.
+LATENCY_BOUND_BYTES = 16e6
+
+
+def roofline_regime(bytes_per_call):
+    """Which limit a decode call of this size runs into (reported beside frac)."""
+    if bytes_per_call < LATENCY_BOUND_BYTES:
+        return ("latency: %.1f MB per call is below the ~16 MB HBM bandwidth x latency product"
+                % (bytes_per_call / 1e6))
+    return "bandwidth"
+
+
 def measured_traffic(config):
     """HBM bytes per cross-attention decode call (split + merge kernels) from the
     committed rocprofv3 counter summary, scaled by its copy calibration; None if
@@ -694,7 +708,8 @@ def main():
                      "frac": cross_gbs / HBM_PEAK_GBS,
                      "traffic": traffic["bytes"] if traffic else None,
                      "traffic_read_write": [traffic["read"], traffic["write"]] if traffic else None,
-                     "bytes_per_launch": cross_b, "avg_launch_us": avg["xattn_decode"] * 1e6},
+                     "bytes_per_launch": cross_b, "avg_launch_us": avg["xattn_decode"] * 1e6,
+                     "regime": roofline_regime(cross_b)},
         "populate": populate_report(w, pop_tflops, pop_dt),
         "kernels": kernels,
         "time_share": {k: v / sum(share.values()) for k, v in share.items()},
