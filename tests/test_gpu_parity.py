@@ -151,6 +151,45 @@ def test_populate_matches_oracle(name, kw):
     assert cache.ready
 
 
+def _random_geometries(n, seed=2026):
+    """Seeded random shapes for populate + decode: every head_dim, fp32 and
+    bf16, ragged memory lengths, 1-3 layers and streams, 1-8 queries; every
+    other bf16 shape has H*D a multiple of 256 (the 256-wide tile kernel)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        D = int(rng.choice([32, 64, 128]))
+        dtype = ("f32", "bf16")[i % 2]
+        if i % 4 == 1:
+            H = 256 * int(rng.integers(1, 4)) // D
+        else:
+            H = int(rng.integers(1, 9))
+        out.append(dict(n_layers=int(rng.integers(1, 4)), n_streams=int(rng.integers(1, 4)),
+                        n_q=int(rng.integers(1, 9)), mem_len=int(rng.integers(1, 601)),
+                        d_model=H * D, n_heads=H, head_dim=D, dtype=dtype,
+                        scale=1 / math.sqrt(D), seed=1000 + i))
+    return out
+
+
+@pytest.mark.parametrize("kw", _random_geometries(16),
+                         ids=lambda k: "L%d-B%d-q%d-T%d-H%dx%d-%s" % (
+                             k["n_layers"], k["n_streams"], k["n_q"], k["mem_len"], k["n_heads"],
+                             k["head_dim"], k["dtype"]))
+def test_random_geometry_populate_then_decode(kw):
+    g = geometry(None, **kw)
+    cache, wt, _ = make_cache(g)
+    Kc, Vc = oracle_caches(g, wt)
+    tol = TOL[g.dtype]
+    assert max_abs(to_np(cache.k), Kc) <= tol
+    assert max_abs(to_np(cache.v), Vc) <= tol
+    for layer in range(g.n_layers):
+        q = synth.decode_call_inputs(g, 0, layer)["q_cross"]
+        out = cache.decode(t32(q), layer, g.scale)
+        torch.cuda.synchronize()
+        err = max_abs(to_np(out), oracle.cross_decode(q, Kc[layer], Vc[layer], g.scale))
+        assert err <= tol, (layer, err)
+
+
 # -------------------------------------------------------------- cross decode
 DEC_CASES = [
     ("tiny", {}),
