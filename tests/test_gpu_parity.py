@@ -378,6 +378,25 @@ PREFILL_CASES = [
 ]
 
 
+def _random_prefill_cases(n, seed=2027):
+    """Seeded random prefill shapes: 1-4 sequences and kv heads, 1-8 query
+    heads per kv head, every head_dim, capacities up to 200, chunks up to 64
+    rows anywhere in the cache."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        P = int(rng.integers(1, 201))
+        rows = int(rng.integers(1, min(P, 64) + 1))
+        Hkv = int(rng.integers(1, 5))
+        out.append(dict(S=int(rng.integers(1, 5)), n=rows, Hq=Hkv * int(rng.choice([1, 2, 3, 4, 8])),
+                        Hkv=Hkv, D=int(rng.choice([32, 64, 128])), P=P,
+                        pos=int(rng.integers(0, P - rows + 1)), dtype=("f32", "bf16")[i % 2]))
+    return out
+
+
+PREFILL_CASES += _random_prefill_cases(12)
+
+
 @pytest.mark.parametrize("c", PREFILL_CASES,
                          ids=lambda c: "S%d-n%d-Hq%d-Hkv%d-D%d-P%d-pos%d-%s" % tuple(c.values()))
 def test_prefill_matches_oracle(c):
