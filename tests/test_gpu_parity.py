@@ -635,6 +635,23 @@ def _abs_products(E, W, H, D):
     return a.reshape(B, T, H, D).transpose(0, 2, 1, 3)
 
 
+def _random_fp8_geometries(n, seed=2028):
+    """Seeded random fp8-cache shapes (H*D a multiple of 256, as its populate
+    requires): every head_dim, 1-2 layers, 1-3 streams, 1-8 queries, ragged
+    memories."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        D = int(rng.choice([32, 64, 128]))
+        H = 256 * int(rng.integers(1, 4)) // D
+        out.append(dict(n_layers=int(rng.integers(1, 3)), n_streams=int(rng.integers(1, 4)),
+                        n_q=int(rng.integers(1, 9)), mem_len=int(rng.integers(1, 700)),
+                        d_model=H * D, n_heads=H, head_dim=D, scale=1 / math.sqrt(D),
+                        seed=3000 + i))
+    return out
+
+
+
 FP8_POP_CASES = [
     dict(n_layers=2, n_streams=3, mem_len=100, d_model=256, n_heads=8, head_dim=32),
     dict(n_layers=1, n_streams=2, mem_len=300, d_model=512, n_heads=8, head_dim=64),
@@ -644,6 +661,7 @@ FP8_POP_CASES = [
     # values in the subnormal range (below 2^-6)
     dict(n_layers=1, n_streams=2, mem_len=40, d_model=256, n_heads=4, head_dim=64, e_std=0.02),
 ]
+FP8_POP_CASES += _random_fp8_geometries(6, seed=2029)
 
 
 @pytest.mark.parametrize("kw", FP8_POP_CASES, ids=lambda x: str(x))
@@ -674,6 +692,8 @@ FP8_DEC_CASES = [
     dict(n_layers=1, n_streams=1, n_q=5, mem_len=3001, d_model=256, n_heads=2, head_dim=128),
     dict(n_layers=2, n_streams=3, n_q=2, mem_len=1, d_model=256, n_heads=4, head_dim=64),
 ]
+
+FP8_DEC_CASES += _random_fp8_geometries(6)
 
 
 def _fp8_cache_with_oracle_values(g):
