@@ -533,6 +533,25 @@ STEP_CASES = [
 ]
 
 
+def _random_step_cases(n, seed=2030):
+    """Seeded random decoder-layer steps: fp32, bf16 and fp8 caches in turn,
+    every head_dim, 1-3 streams x 1-8 queries, ragged memories."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        dtype = ("f32", "bf16", "fp8")[i % 3]
+        D = int(rng.choice([32, 64, 128]))
+        H = 256 * int(rng.integers(1, 3)) // D if dtype == "fp8" else int(rng.integers(1, 9))
+        out.append((None, dict(n_layers=int(rng.integers(1, 3)), n_streams=int(rng.integers(1, 4)),
+                               n_q=int(rng.integers(1, 9)), mem_len=int(rng.integers(1, 400)),
+                               d_model=H * D, n_heads=H, head_dim=D, scale=1 / math.sqrt(D),
+                               max_pos=8, dtype=dtype, seed=4000 + i)))
+    return out
+
+
+STEP_CASES += _random_step_cases(6)
+
+
 @pytest.mark.parametrize("name,kw", STEP_CASES, ids=lambda x: str(x))
 def test_decoder_layer_step_matches_oracle(name, kw):
     """Teacher-forced: every call gets the oracle's input hidden state; its
