@@ -841,3 +841,66 @@ def test_large_self_attention_sampled():
             worst = max(worst, max_abs(to_np(out), want))
     assert worst <= 1e-4
     np.testing.assert_array_equal(to_np(kv.k), Ks)
+
+
+# ------------------------------------------------------------ graph replay
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_graph_replays_match_the_eager_window(dtype):
+    """The call sequence bench.py times, captured once into a HIP graph:
+    populate, then for four positions and both layers one self-attention append
+    and one cross decode. Replayed three times, with eager resets and
+    synchronisations in between, every replay must reproduce the eager run's
+    outputs and self caches bit for bit (all kernels are deterministic)."""
+    g = geometry(None, n_layers=2, n_streams=2, n_q=1, mem_len=300, d_model=256, n_heads=4,
+                 head_dim=64, dtype=dtype, scale=0.125, max_pos=8)
+    cache, wt, (E, WK, WV) = make_cache(g)
+    S, H, D, P, L, steps = g.n_streams, g.n_heads, g.head_dim, g.max_pos, g.n_layers, 4
+    kdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    kvs = [pc.KVLayer(S, H, D, P, dtype=kdt) for _ in range(L)]
+    r = np.random.default_rng(55)
+    qs, kn, vn, qc = ([[t32(r.standard_normal((S, H, D)) * 0.45) for _ in range(L)] for _ in range(steps)]
+                      for _ in range(4))
+    qc = [[q.view(S, 1, H, D) for q in row] for row in qc]
+    so = [[torch.empty(S, H, D, device=DEV) for _ in range(L)] for _ in range(steps)]
+    co = [[torch.empty(S, 1, H, D, device=DEV) for _ in range(L)] for _ in range(steps)]
+
+    def window():
+        cache.populate(E, WK, WV)
+        for t in range(steps):
+            for l in range(L):
+                kvs[l].append_attend(qs[t][l], kn[t][l], vn[t][l], t, g.scale, out=so[t][l])
+                pc.cke_xattn_decode(qc[t][l], cache, l, g.scale, co[t][l])
+
+    def reset():
+        for kv in kvs:
+            kv.k.zero_()
+            kv.v.zero_()
+        for row in so + co:
+            for o in row:
+                o.fill_(float("nan"))
+        cache.k.fill_(float("nan"))
+        cache.v.fill_(float("nan"))
+        torch.cuda.synchronize()
+
+    def snapshot():
+        torch.cuda.synchronize()
+        return ([o.clone() for row in so + co for o in row]
+                + [x.clone() for kv in kvs for x in (kv.k, kv.v)] + [cache.k.clone(), cache.v.clone()])
+
+    reset()
+    window()
+    want = snapshot()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    reset()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s):
+        window()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        reset()
+        graph.replay()
+        got = snapshot()
+        for a, b in zip(got, want):
+            assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), rep
+        torch.cuda.synchronize()
