@@ -904,3 +904,48 @@ def test_graph_replays_match_the_eager_window(dtype):
         for a, b in zip(got, want):
             assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), rep
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_graph_replays_of_decoder_layer_steps_match_eager(dtype):
+    """Three positions of decoder-layer steps over both layers (seven launches
+    each, workspace reused), captured once and replayed three times: the hidden
+    state and the self caches match the eager run bit for bit."""
+    g = geometry(None, n_layers=2, n_streams=2, n_q=2, n_seqs=4, mem_len=500, d_model=256,
+                 n_heads=8, head_dim=32, dtype=dtype, scale=1 / math.sqrt(32), max_pos=8)
+    st = _step_setup(g)
+    x0 = t32(st["wt"]["x0"][:st["S"]])
+    x = torch.empty_like(x0)
+
+    def steps():
+        for t in range(3):
+            for l in range(g.n_layers):
+                pc.cke_decoder_layer_step(x, st["descs"][l], st["kvs"][l], t, st["cache"], l,
+                                          g.scale, st["ws"])
+
+    def reset():
+        x.copy_(x0)
+        for kv in st["kvs"]:
+            kv.k.zero_()
+            kv.v.zero_()
+        torch.cuda.synchronize()
+
+    def snapshot():
+        torch.cuda.synchronize()
+        return [x.clone()] + [y.clone() for kv in st["kvs"] for y in (kv.k, kv.v)]
+
+    reset()
+    steps()
+    want = snapshot()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    reset()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s):
+        steps()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        reset()
+        graph.replay()
+        for a, b in zip(snapshot(), want):
+            assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), rep
