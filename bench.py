@@ -547,7 +547,9 @@ def populate_report(w, tflops, pop_dt):
     else:
         r["mfma"] = "v_mfma_f32_32x32x2_f32"
     if g.lift_in:
-        r["includes"] = "memory lift (v_mfma_f32_32x32x2_f32) + K/V projections"
+        # the library runs the lift as three bf16 products when its input is at least 1024 wide
+        lift_mfma = "three bf16 products" if g.lift_in >= 1024 else "v_mfma_f32_32x32x2_f32"
+        r["includes"] = "memory lift (%s) + K/V projections" % lift_mfma
     return r
 
 

@@ -81,6 +81,37 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, const f32x16 (&acc)[
         }
 }
 
+// Memory-lift epilogue for accumulators laid out as in epilogue (lane l holds
+// column l % 32 of each 32x32 block, register r its row acc_row(l, r)):
+// C[m][n] = gelu(acc) (+ pos[m % pos_rows][n]), C token-major [M][H*D]. Each
+// store covers 32 consecutive columns of one row per half-wave.
+template <int BM, int BN, int WGM, int WGN>
+__device__ __forceinline__ void epilogue_lift(const GemmArgs& a, const f32x16 (&acc)[BM / WGM / 32][BN / WGN / 32],
+                                              int m0, int n0)
+{
+    constexpr int WTM = BM / WGM, WTN = BN / WGN, MB = WTM / 32, NB = WTN / 32;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = wave / WGN, wn = wave % WGN;
+    const int N = a.H * a.D;
+    float* C = static_cast<float*>(a.Kc);
+    auto gelu = [](float v) { return 0.5f * v * (1.f + erff(v * 0.70710678118654752f)); };
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            const int col = n0 + wn * WTN + nb * 32 + (lane & 31);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = m0 + wm * WTM + mb * 32 + acc_row(lane, r);
+                if (row < a.M) {
+                    float v = gelu(acc[mb][nb][r]);
+                    if (a.pos) v += a.pos[(size_t)(row % a.pos_rows) * N + col];
+                    C[(size_t)row * N + col] = v;
+                }
+            }
+        }
+}
+
 // fp32 operands on v_mfma_f32_32x32x2_f32. LDS holds both tiles k-major:
 // As[k][m] (transposed on store) and Bs[k][n], so a half-wave reads 32
 // consecutive floats per operand.
@@ -382,7 +413,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void populate_bf16_big_kernel(GemmA
 //  * W: each thread loads an 8(k) x 2(n) block (eight 8-byte row pieces) and
 //    writes, per column, its 8 k values as one 16-byte hi and one 16-byte lo
 //    piece of Bh[n][k], Bl[n][k].
-template <int BM, int BN, int BK, int WGM, int WGN>
+template <int BM, int BN, int BK, int WGM, int WGN, bool LIFT = false>
 __global__ __launch_bounds__(WGM * WGN * 64) void populate_f32x3_kernel(GemmArgs a, int num_m, int num_n)
 {
     constexpr int NT = WGM * WGN * 64;
@@ -526,7 +557,10 @@ __global__ __launch_bounds__(WGM * WGN * 64) void populate_f32x3_kernel(GemmArgs
         if (kt + 1 < nk) store_tiles(buf ^ 1);
         __syncthreads();
     }
-    epilogue<BM, BN, WGM, WGN, float>(a, acc, m0, p, col0);
+    if constexpr (LIFT)
+        epilogue_lift<BM, BN, WGM, WGN>(a, acc, m0, n0);
+    else
+        epilogue<BM, BN, WGM, WGN, float>(a, acc, m0, p, col0);
 }
 
 constexpr int vmcnt_wait(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
@@ -1187,10 +1221,23 @@ hipError_t launch_cfg(const GemmArgs& g, bool bf16, hipStream_t st) {
 
 }  // namespace
 
-// Projector memory lift: out = gelu(x . W) (+ positions), fp32, on the fp32
-// DMA populate kernel with a token-major epilogue. One weight, N = n columns.
-// (The three-bf16-product kernel's 128 x 128 tiles give the Q-Former lift's
-// 1500 x 2048 output only 192 tiles for 256 compute units; it measured slower.)
+// Projector memory lift: out = gelu(x . W) (+ positions), fp32, one weight,
+// N = n columns, with a token-major epilogue. Inputs at least 1024 wide run as
+// three bf16 products on 128 x 64 tiles (the Q-Former's 1500 x 4096 x 2048:
+// 204 us, max error 3e-5, against 248 us on the fp32 kernel; 128 x 128 tiles,
+// only 192 of them for 256 compute units, took 257 us). Narrower inputs stay on
+// the fp32 DMA kernel, where splitting the operands costs more than it saves.
+namespace {
+template <int BM, int BN>
+hipError_t launch_lift_x3(const GemmArgs& g, int n, hipStream_t st) {
+    const int num_m = (g.M + BM - 1) / BM, num_n = n / BN;
+    const int grid = ((num_m * num_n + 7) / 8) * 8;
+    hipLaunchKernelGGL((populate_f32x3_kernel<BM, BN, 32, 2, 2, true>), dim3(grid), dim3(256), 0, st, g,
+                       num_m, num_n);
+    return hipGetLastError();
+}
+}  // namespace
+
 hipError_t launch_lift(const LiftLaunch& a, hipStream_t st) {
     if (a.rows < 1 || a.k_in % 32 != 0 || a.n % 64 != 0 || (a.pos && a.pos_rows < 1))
         return hipErrorInvalidValue;
@@ -1208,6 +1255,7 @@ hipError_t launch_lift(const LiftLaunch& a, hipStream_t st) {
     g.D = 64;
     g.pos = a.pos;
     g.pos_rows = a.pos_rows;
+    if (a.k_in >= 1024) return launch_lift_x3<128, 64>(g, a.n, st);   // n % 64 == 0 checked above
     const int num_m = (a.rows + 63) / 64, num_n = a.n / 64;
     const int ntiles = num_m * num_n;
     const int grid = ((ntiles + 7) / 8) * 8;
