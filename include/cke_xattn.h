@@ -247,7 +247,10 @@ int cke_decoder_layer_step(float* x, const cke_decoder_layer* w, const cke_kv_la
 /* Projector memory lift, the prologue that produces a Q-Former-style encoder
  * memory before it is populated:
  *   out[r][j] = gelu(sum_c x[r][c] w[c][j]) + pos[r % pos_rows][j]
- * with the exact (erf) GELU, fp32 throughout, products on the matrix cores.
+ * with the exact (erf) GELU, fp32 inputs, accumulation and output, products
+ * on the matrix cores: for k_in >= 1024 as three bf16 products of operands
+ * split into two bf16 terms each (each product within 2^-16 of its fp32
+ * value), otherwise as fp32 products.
  *   transcribe.cpp "Forward map - granite_nar", "Projector (NLE simplified
  *   Q-Former)": the normalised 4-way encoder concat is lifted 4096 -> 2048
  *   with a GELU, and the window position embedding is added to every block of
