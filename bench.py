@@ -67,6 +67,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--config", default="base", choices=sorted(synth.CONFIGS))
     ap.add_argument("--mode", default="graph", choices=["graph", "eager"])
+    ap.add_argument("--also", default="large",
+                    help="comma-separated workloads measured after the headline one and "
+                         "reported under 'also' (their windows and rooflines, no extras); "
+                         "'none' for none")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="approximate CPU time budget of the oracle baseline sample")
@@ -204,9 +208,11 @@ class Workload:
 
 def cpu_baseline(name, budget_s, threads=None):
     """The oracle as it stands, on the host's cores (or `threads` of them), on
-    a bounded sample: populate of the whole cache once, then decode tokens
-    until the budget is used; the window time is populate + steps x the mean
-    token time."""
+    a bounded sample: populate, then decode tokens until the budget is used;
+    the window time is populate + steps x the mean token time. For the Large
+    workloads (16 streams x 32 layers) the sample is one stream's first
+    `LARGE_POP_ROWS` memory rows for populate (scaled to all 16 x 1500 rows)
+    and one stream of the sixteen for decode (scaled x16): extrapolated."""
     import oracle
 
     g = synth.get(name)
@@ -215,12 +221,19 @@ def cpu_baseline(name, budget_s, threads=None):
         oracle.set_threads(threads)
     threads = oracle.get_threads()
     wt = synth.workload_tensors(g)
+    one = name in ("large", "large_fp8")   # one stream of the sixteen
     t0 = time.perf_counter()
-    one = name in ("large", "large_fp8")   # one stream of the sixteen, scaled x16
     if one:
-        Kc, Vc = oracle.populate(wt["E"][:1], wt["WK"], wt["WV"], g.n_heads, g.head_dim,
-                                 round_bf16=(g.dtype == "bf16"), round_fp8=(g.dtype == "fp8"))
-        t_pop = (time.perf_counter() - t0) * g.n_streams
+        rows = LARGE_POP_ROWS
+        oracle.populate(wt["E"][:1, :rows], wt["WK"], wt["WV"], g.n_heads, g.head_dim,
+                        round_bf16=(g.dtype == "bf16"), round_fp8=(g.dtype == "fp8"))
+        t_pop = (time.perf_counter() - t0) * (g.n_streams * g.mem_len / rows)
+        # decode reads the projection of the whole memory: the oracle's own
+        # projection of one stream is too slow to run here, and attention
+        # time does not depend on the values, so the rows are drawn
+        shp = (g.n_layers, 1, g.n_heads, g.mem_len, g.head_dim)
+        Kc = synth.normal([g.seed, 97, 0], shp, synth.q_std(g))
+        Vc = synth.normal([g.seed, 97, 1], shp, synth.q_std(g))
     else:
         E = wt["E"]
         if g.lift_in:   # the projector memory is lifted first, as on the GPU
@@ -244,24 +257,33 @@ def cpu_baseline(name, budget_s, threads=None):
                 oracle.self_append_attend(d["q_self"][:S], d["k_new"][:S], d["v_new"][:S], Ks[l],
                                           Vs[l], t, g.scale, round_bf16=self_bf16)
             q = d["q_cross"][:1] if one else d["q_cross"]
-            oracle.cross_decode(q, Kc[l][:1] if one else Kc[l], Vc[l][:1] if one else Vc[l],
-                                g.scale)
+            oracle.cross_decode(q, Kc[l], Vc[l], g.scale)
         n_tok += 1
-        if time.perf_counter() - t1 > max(1.0, budget_s - t_pop):
+        if time.perf_counter() - t1 > max(1.0, budget_s - (time.perf_counter() - t0)):
             break
     t_tok = (time.perf_counter() - t1) / n_tok
     if one:
         t_tok *= g.n_streams
     per_window = t_pop + g.steps * t_tok
     tokens = g.steps * (g.n_seqs if g.n_seqs else g.n_streams * g.n_q)
-    sample = ("oracle populate of the %s cache%s, then %d of %d decode steps (all layers, "
-              "self + cross); window time = populate + %d x mean step time" %
-              (name, " for 1 of 16 streams x16" if one else "", n_tok, g.steps,
-               g.steps))
+    if one:
+        sample = ("extrapolated: oracle populate of %d of 1500 memory rows of 1 of 16 streams "
+                  "(x%d), then %d of %d decode steps of 1 of 16 streams (x16, all layers, self + "
+                  "cross); window time = populate + %d x mean step time"
+                  % (LARGE_POP_ROWS, g.n_streams * g.mem_len // LARGE_POP_ROWS, n_tok, g.steps,
+                     g.steps))
+    else:
+        sample = ("oracle populate of the %s cache, then %d of %d decode steps (all layers, "
+                  "self + cross); window time = populate + %d x mean step time"
+                  % (name, n_tok, g.steps, g.steps))
     oracle.set_threads(saved)
     return {"value": tokens / per_window, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": sample, "populate_s": t_pop, "step_s": t_tok,
             "host_cpu": _host_cpu()}
+
+
+# memory rows of one stream the Large oracle baseline populates (of 1500)
+LARGE_POP_ROWS = 64
 
 
 # HBM bandwidth x loaded latency (8 TB/s x ~2 us): a call that moves fewer bytes
@@ -466,11 +488,13 @@ def measure_decoder_step(torch, pc, w, stream, tokens=4):
                     torch.mm(x, WQs.t(), out=q)
                     torch.mm(x, WKs.t(), out=k)
                     torch.mm(x, WVs.t(), out=v)
-                    pc.cke_selfattn_decode_append(q, k, v, kvs[l], t, g.scale, so, stream=cs())
+                    pc.cke_selfattn_decode_append(q.view(S, H, D), k.view(S, H, D),
+                                                  v.view(S, H, D), kvs[l], t, g.scale,
+                                                  so.view(S, H, D), stream=cs())
                     torch.addmm(x, so, WOs.t(), out=x1)
                     torch.mm(x1, WQ.t(), out=qc)
                     pc.cke_xattn_decode(qc.view(g.n_streams, g.n_q, H, D), w.cache, l, g.scale,
-                                        co, stream=cs())
+                                        co.view(g.n_streams, g.n_q, H, D), stream=cs())
                     torch.addmm(x1, co, WO.t(), out=x)
         t_c = graph_time(composed) / (tokens * L)
         res["composed_us_per_layer"] = t_c * 1e6
@@ -529,28 +553,58 @@ def measure_cold_decode(torch, pc, w, stream, calls=24):
 
 
 def populate_report(w, tflops, pop_dt):
-    """Populate TFLOP/s against the MFMA peaks. fp32 products of a width that
-    is a multiple of 128 run as three bf16 MFMA products (operands split into
-    two bf16 terms): their algorithmic rate is reported against the fp32 peak
-    and the issued rate (3x) against the bf16 peak the instruction runs at."""
+    """Populate TFLOP/s against the MFMA peak of the instruction it issues.
+    fp32 products of a width that is a multiple of 128 run as three bf16 MFMA
+    products (operands split into two bf16 terms): `frac` is their issued
+    rate (3x the algorithmic FLOP) against the bf16 peak; the algorithmic
+    rate against the fp32 peak is reported beside it."""
     g = w.g
-    x3 = not w.bf16 and g.d_model % 128 == 0 and g.d_model % 32 == 0
-    r = {"tflops": tflops, "peak_tflops": MFMA_PEAK_TFLOPS[pop_dt],
-         "frac": tflops / MFMA_PEAK_TFLOPS[pop_dt]}
+    x3 = not w.bf16 and g.d_model % 128 == 0
+    r = {"tflops": tflops}
     if w.bf16:
-        r["mfma"] = "v_mfma_f32_32x32x16_bf16"
+        r.update(mfma="v_mfma_f32_32x32x16_bf16", peak_tflops=MFMA_PEAK_TFLOPS["bf16"],
+                 frac=tflops / MFMA_PEAK_TFLOPS["bf16"])
     elif x3:
-        r["mfma"] = "v_mfma_f32_32x32x16_bf16, three products of bf16-split fp32 operands"
-        r["issued_tflops"] = 3 * tflops
-        r["issued_peak_tflops"] = MFMA_PEAK_TFLOPS["bf16"]
-        r["issued_frac"] = 3 * tflops / MFMA_PEAK_TFLOPS["bf16"]
+        r.update(mfma="v_mfma_f32_32x32x16_bf16, three products of bf16-split fp32 operands",
+                 issued_tflops=3 * tflops, peak_tflops=MFMA_PEAK_TFLOPS["bf16"],
+                 frac=3 * tflops / MFMA_PEAK_TFLOPS["bf16"],
+                 algorithmic_frac_vs_f32_peak=tflops / MFMA_PEAK_TFLOPS["f32"])
     else:
-        r["mfma"] = "v_mfma_f32_32x32x2_f32"
+        r.update(mfma="v_mfma_f32_32x32x2_f32", peak_tflops=MFMA_PEAK_TFLOPS["f32"],
+                 frac=tflops / MFMA_PEAK_TFLOPS["f32"])
     if g.lift_in:
         # the library runs the lift as three bf16 products when its input is at least 1024 wide
         lift_mfma = "three bf16 products" if g.lift_in >= 1024 else "v_mfma_f32_32x32x2_f32"
         r["includes"] = "memory lift (%s) + K/V projections" % lift_mfma
+    r["target_frac"] = 0.5
+    r["target_met"] = r["frac"] >= 0.5
     return r
+
+
+def library_info(pc):
+    """Which build of the library this process loaded: its path, whether the
+    path came from the override variable, the SHA-256 of the file and of the
+    sources it is built from (csrc/ and the public header)."""
+    import hashlib
+
+    def sha(paths):
+        h = hashlib.sha256()
+        for path in paths:
+            h.update(os.path.relpath(path, ROOT).encode())
+            h.update(open(path, "rb").read())
+        return h.hexdigest()
+
+    csrc = os.path.join(ROOT, "projection_cache_amd", "csrc")
+    srcs = sorted(os.path.join(csrc, f) for f in os.listdir(csrc))
+    srcs.append(os.path.join(ROOT, "include", "cke_xattn.h"))
+    return {"path": pc.LIB_PATH, "override": bool(os.environ.get("CKE_XATTN_LIB")),
+            "sha256": sha([pc.LIB_PATH]), "sources_sha256": sha(srcs)}
+
+
+def _progress(msg):
+    """One line per finished phase on stderr (stdout carries only the JSON
+    line), so that a long default run is never silent for minutes."""
+    print("bench: " + msg, file=sys.stderr, flush=True)
 
 
 def _host_cpu():
@@ -571,12 +625,29 @@ def _git_sha():
         return None
 
 
+# Environment variables rocprofv3 exports to the profiled process when it
+# collects hardware counters (--pmc or a counter input file).
+COUNTER_ENV = ("ROCPROF_COUNTER_COLLECTION", "ROCPROF_COUNTERS")
+
+
+def counter_collection_active(environ=None) -> bool:
+    environ = os.environ if environ is None else environ
+    return any(environ.get(k) not in (None, "", "0") for k in COUNTER_ENV)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
         sys.exit(2)
+    if counter_collection_active() and not (args.counters or args.calibrate_copy):
+        # a process that captures HIP graphs while rocprofv3 collects
+        # counters has crashed inside the profiler: refuse before any GPU work
+        print("bench.py: hardware-counter collection is active; the default run captures HIP "
+              "graphs, which is not supported under counter collection. Run the eager counter "
+              "mode instead: bench.py --counters [--counter-tokens N]", file=sys.stderr)
+        sys.exit(3)
 
     import torch
 
@@ -598,12 +669,10 @@ def main():
         print(json.dumps({"calibrate_copy_bytes_read": n * 4, "calibrate_copy_bytes_written": n * 4,
                           "dispatches": 5}))
         return
-    w = Workload(args.config, torch, pc)
-    g = w.g
-
     stream = torch.cuda.Stream()
-    torch.cuda.synchronize()
     if args.counters:
+        w = Workload(args.config, torch, pc)
+        torch.cuda.synchronize()
         for _ in range(args.steps):
             w.window(stream, tokens=args.counter_tokens)
         torch.cuda.synchronize()
@@ -611,6 +680,57 @@ def main():
                           "xattn_bytes_per_call": w.cross_bytes_per_call(),
                           "xattn_calls_per_window": w.calls("xattn_decode")}))
         return
+
+    head = measure(args.config, args, torch, pc, stream, extras=True)
+    _progress("%s measured" % args.config)
+    result = {
+        "metric": METRIC,
+        "value": head.pop("value"),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head.pop("ms_per_step"),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": head.pop("dtype"),
+        "data": "synthetic",
+        "config": head.pop("config"),
+        "roofline": head.pop("roofline"),
+    }
+    result.update(head)
+    result["gpu"] = torch.cuda.get_device_name(0)
+    result["git"] = _git_sha()
+    result["library"] = library_info(pc)
+    also = [c for c in args.also.split(",") if c and c != "none" and c != args.config]
+    if also:
+        result["also"] = {}
+        for name in also:
+            blk = measure(name, args, torch, pc, stream, extras=False)
+            _progress("%s measured" % name)
+            if not args.no_cpu_baseline:
+                blk["cpu_baseline"] = cpu_baseline(name, args.cpu_seconds)
+                _progress("%s oracle baseline timed" % name)
+            result["also"][name] = blk
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(args.config, args.cpu_seconds)
+        _progress("%s oracle baseline timed" % args.config)
+        if args.config in ("tiny", "base", "beam"):
+            result["cpu_baseline_1thread"] = cpu_baseline(args.config, args.cpu_seconds,
+                                                          threads=1)
+    print(json.dumps(result))
+
+
+def measure(name, args, torch, pc, stream, extras):
+    """Time one workload: `args.steps` whole windows replayed as one HIP graph
+    each (value, ms_per_step), then the per-call durations from one graph per
+    call kind, the roofline of the cross-attention call and of the window, and
+    (extras) the other entry points at the workload's shape. Frees the
+    workload's device memory before returning."""
+    w = Workload(name, torch, pc)
+    g = w.g
+    torch.cuda.synchronize()
 
     def capture(kinds, reps=1):
         with torch.cuda.stream(stream):
@@ -643,6 +763,9 @@ def main():
     elapsed = time.perf_counter() - t0
     ms_per_step = elapsed / args.steps * 1e3
     tok_s = w.tokens_per_window * args.steps / elapsed
+    if args.mode == "graph":
+        del graph
+    _progress("%s: %d windows timed, %.2f ms each" % (name, args.steps, ms_per_step))
 
     # per-call durations: one graph per call kind, replayed, timed with events
     avg, total = {}, {}
@@ -671,71 +794,72 @@ def main():
 
     cross_b = w.cross_bytes_per_call()
     cross_gbs = cross_b / avg["xattn_decode"] / 1e9
-    traffic = measured_traffic(args.config)
+    traffic = measured_traffic(name)
     kernels = {
         "xattn_decode": {"avg_us": avg["xattn_decode"] * 1e6, "calls_per_step": len(dur["xattn_decode"]),
                          "bytes_per_call": cross_b, "GB_s": cross_gbs},
         "populate": {"avg_us": avg["populate"] * 1e6,
                      "tflops": w.populate_flops() / avg["populate"] / 1e12},
     }
+    self_bytes = 0.0
     if "selfattn" in dur:
         sb = [w.self_bytes_per_call(t) for t in range(g.steps) for _ in range(g.n_layers)]
+        self_bytes = float(np.sum(sb))
         kernels["selfattn"] = {"avg_us": avg["selfattn"] * 1e6,
                                "calls_per_step": len(dur["selfattn"]),
                                "bytes_per_call_mean": float(np.mean(sb)),
-                               "GB_s": float(np.sum(sb) / np.sum(dur["selfattn"]) / 1e9)}
+                               "GB_s": float(self_bytes / np.sum(dur["selfattn"]) / 1e9)}
     share = {k: float(np.sum(v)) for k, v in dur.items()}
     dominant = max(share, key=share.get)
-    pop_tflops = kernels["populate"]["tflops"]
     pop_dt = "bf16" if w.bf16 else "f32"        # the MFMA input type
-    result = {
-        "metric": METRIC,
+    # the whole window against HBM: the decode calls' algorithmic bytes (K/V
+    # rows read, new rows, queries and outputs) over the measured window time
+    decode_bytes = cross_b * w.calls("xattn_decode") + self_bytes
+    window_gbs = decode_bytes / (ms_per_step * 1e-3) / 1e9
+    tok_at_peak = w.tokens_per_window / (decode_bytes / (HBM_PEAK_GBS * 1e9))
+    blk = {
         "value": tok_s,
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
         "ms_per_step": ms_per_step,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
         "dtype": {"f32": "f32", "bf16": "bf16", "fp8": "fp8"}[g.dtype],
-        "data": "synthetic",
-        "config": {"workload": WORKLOAD_TEXT[args.config], "name": args.config,
+        "config": {"workload": WORKLOAD_TEXT[name], "name": name,
                    "tokens_per_step": w.tokens_per_window, "decode_steps": g.steps,
                    "layers": g.n_layers, "mode": args.mode},
         "roofline": {"bound": "hbm",
-                     "kernel": "cke_xattn_decode (xattn_partial_kernel + xattn_merge_kernel)",
+                     "kernel": "cke_xattn_decode (xattn_partial_kernel%s)"
+                               % (" + xattn_merge_kernel" if w.cache.n_splits > 1 else ""),
                      "achieved": cross_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": cross_gbs / HBM_PEAK_GBS,
                      "traffic": traffic["bytes"] if traffic else None,
                      "traffic_read_write": [traffic["read"], traffic["write"]] if traffic else None,
                      "bytes_per_launch": cross_b, "avg_launch_us": avg["xattn_decode"] * 1e6,
                      "regime": roofline_regime(cross_b)},
-        "populate": populate_report(w, pop_tflops, pop_dt),
+        "window_roofline": {"bound": "hbm", "decode_bytes_per_step": decode_bytes,
+                            "achieved": window_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                            "frac": window_gbs / HBM_PEAK_GBS,
+                            "tokens_per_s_at_peak": tok_at_peak,
+                            "target_tokens_per_s": 0.6 * tok_at_peak,
+                            "target_met": tok_s >= 0.6 * tok_at_peak},
+        "populate": populate_report(w, kernels["populate"]["tflops"], pop_dt),
         "kernels": kernels,
         "time_share": {k: v / sum(share.values()) for k, v in share.items()},
         "kernel_sum_ms_per_step": sum(total.values()) * 1e3,
         "dominant_kernel": dominant,
-        "gpu": torch.cuda.get_device_name(0),
-        "git": _git_sha(),
     }
-    result["xattn_decode_weights"] = measure_weights(torch, pc, w, stream)
-    step = measure_decoder_step(torch, pc, w, stream)
-    if step:
-        result["decoder_layer_step"] = step
-    prefill = measure_prefill(torch, pc, g, stream)
-    if prefill:
-        result["selfattn_prefill"] = prefill
-    cold = measure_cold_decode(torch, pc, w, stream)
-    if cold:
-        result["xattn_decode_mall_cold"] = cold
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(args.config, args.cpu_seconds)
-        if args.config in ("tiny", "base", "beam"):
-            result["cpu_baseline_1thread"] = cpu_baseline(args.config, args.cpu_seconds,
-                                                          threads=1)
-    print(json.dumps(result))
+    if extras:
+        blk["xattn_decode_weights"] = measure_weights(torch, pc, w, stream)
+        step = measure_decoder_step(torch, pc, w, stream)
+        if step:
+            blk["decoder_layer_step"] = step
+        prefill = measure_prefill(torch, pc, g, stream)
+        if prefill:
+            blk["selfattn_prefill"] = prefill
+        cold = measure_cold_decode(torch, pc, w, stream)
+        if cold:
+            blk["xattn_decode_mall_cold"] = cold
+    del w
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return blk
 
 
 if __name__ == "__main__":

@@ -148,7 +148,7 @@ int cke_xattn_decode(const float* q, int n_q, const cke_xattn_cache* c,
  *   weights[b][i][t] = (1 / n_heads_sel) * sum_k p_k[t],
  *   p_k[t] = softmax_t(scale * q[b][i][heads[k]].K_l[b][heads[k]][t])
  * normalised with the same (max, sum) the decode itself formed.
- *   WhisperKit case study, section 8: the decoder exposes the attention
+ *   WhisperKit case study, section 6: the decoder exposes the attention
  *   weights of its alignment heads, averaged over those heads, for word-level
  *   timing.
  *   heads        HOST array of n_heads_sel head indices in [0, H) (repeats
@@ -191,7 +191,7 @@ int cke_selfattn_decode_append(const float* q, const float* k_new,
  * reading the stored (rounded) values. Rows >= pos+n_new are never read or
  * written. With n_new = 1 and n_q_heads = kv->n_heads this is
  * cke_selfattn_decode_append with [S][1][H][D] tensors.
- *   WhisperKit case study, section 4: the decoder's ContextPrefill starts at a
+ *   WhisperKit case study, section 5: the decoder's ContextPrefill starts at a
  *   cache already holding several prefix positions (several rows written at
  *   once); section 3: heads may share key/value heads (MHA, GQA, MQA).
  *   q, out        device fp32 [S][n_new][n_q_heads][D] (out must not alias q)

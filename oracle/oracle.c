@@ -232,7 +232,7 @@ void orc_cross_decode(int B, int nq, int H, int T, int D, double scale,
 }
 
 /* Cross-attention weights of selected heads, averaged over them ([WK]
- * section 8: the decoder's alignment heads expose their attention weights,
+ * section 6: the decoder's alignment heads expose their attention weights,
  * which are averaged over those heads for word timing). For every stream b
  * and query i:
  *   p[h][t] = exp(scale q.K_t - max) / sum_u exp(scale q.K_u - max)   (head h)
@@ -305,7 +305,7 @@ void orc_self_append_attend(int S, int H, int D, int max_pos, int pos,
 }
 
 /* Several new rows at once, with grouped key/value heads ([WK] section 3
- * lists the MHA/GQA/MQA head sharing; the ContextPrefill of [WK] section 4
+ * lists the MHA/GQA/MQA head sharing; the ContextPrefill of [WK] section 5
  * starts the decoder from several prefix positions at once). Shapes:
  *   q, out [S][n][Hq][D];  kn, vn [S][n][Hkv][D];  Ks, Vs [S][Hkv][max_pos][D].
  * First rows pos .. pos+n-1 of every (sequence, kv head) are written (rounded

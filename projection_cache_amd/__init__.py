@@ -140,6 +140,39 @@ def _ptr(x):
     return int(x)
 
 
+def _meta(name, t, shape=None, dtypes=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch tensor (got %s)" % (name, type(t).__name__))
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s (got %s)" % (name, tuple(shape), tuple(t.shape)))
+    if dtypes is not None and t.dtype not in dtypes:
+        raise ValueError("%s must be of dtype %s (got %s)"
+                         % (name, " or ".join(str(d) for d in dtypes), t.dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def _devs(*specs):
+    """Check (name, tensor, shape, dtypes) specs: every shape, dtype and
+    contiguity first, then that each tensor lives on the GPU, before the
+    addresses are handed to a kernel (a host address or a short buffer would
+    be read or written out of bounds on the GPU). Returns the addresses."""
+    for spec in specs:
+        _meta(*spec)
+    for spec in specs:
+        if spec[1].device.type != "cuda":
+            raise ValueError("%s must be a device tensor (got device %s)" % (spec[0], spec[1].device))
+    return [spec[1].data_ptr() for spec in specs]
+
+
+def _dev(name, t, shape=None, dtypes=None):
+    return _devs((name, t, shape, dtypes))[0]
+
+
+_F32 = (torch.float32,)
+_IN_DTYPES = {CKE_F32: torch.float32, CKE_BF16: torch.bfloat16, CKE_FP8: torch.float8_e4m3fn}
+
+
 def _stream(stream):
     if stream is None:
         return torch.cuda.current_stream().cuda_stream
@@ -196,56 +229,106 @@ def _handle(cache):
     return cache.handle if isinstance(cache, XattnCache) else cache
 
 
+def _geom(cache) -> cke_xattn_geom:
+    """Geometry of an XattnCache; the tensor-level wrappers need it to check
+    the shapes they hand to the library (raw handles go through lib())."""
+    if not isinstance(cache, XattnCache):
+        raise TypeError("cache must be an XattnCache (raw handles: call lib() directly)")
+    if not cache.handle:
+        raise ValueError("cache has been closed")
+    return cache.geom
+
+
 def cke_xattn_populate(cache, E, WK, WV, stream=None, e_dtype=None, w_dtype=None) -> None:
     """Prefill every layer's K/V slab from encoder memory E [B][T][d_model];
-    WK and WV are sequences of L weight tensors [d_model][H*D]."""
+    WK and WV are sequences of L weight tensors [d_model][H*D], one per layer
+    of the cache (an XattnCache)."""
+    g = _geom(cache)
+    if len(WK) != g.n_layers or len(WV) != g.n_layers:
+        raise ValueError("WK and WV must hold one weight per layer: %d each (got %d and %d)"
+                         % (g.n_layers, len(WK), len(WV)))
     if e_dtype is None:
         e_dtype = _DTYPES[E.dtype]
     if w_dtype is None:
         w_dtype = _DTYPES[WK[0].dtype]
-    arr = _P * len(WK)
-    wk = arr(*[_ptr(w) for w in WK])
-    wv = arr(*[_ptr(w) for w in WV])
-    _check(_lib.cke_xattn_populate(_handle(cache), _ptr(E), e_dtype, wk, wv, w_dtype,
+    wshape, wdt = (g.d_model, g.n_heads * g.head_dim), (_IN_DTYPES[w_dtype],)
+    ptrs = _devs(("E", E, (g.n_streams, g.mem_len, g.d_model), (_IN_DTYPES[e_dtype],)),
+                 *[("WK[%d]" % i, w, wshape, wdt) for i, w in enumerate(WK)],
+                 *[("WV[%d]" % i, w, wshape, wdt) for i, w in enumerate(WV)])
+    e_ptr = ptrs[0]
+    arr = _P * g.n_layers
+    wk = arr(*ptrs[1:1 + g.n_layers])
+    wv = arr(*ptrs[1 + g.n_layers:])
+    _check(_lib.cke_xattn_populate(_handle(cache), e_ptr, e_dtype, wk, wv, w_dtype,
                                    _stream(stream)))
+
+
+def _qshape(g, q):
+    """(B, n_q, H, D) of a query tensor for the cache geometry g."""
+    if not isinstance(q, torch.Tensor) or q.dim() != 4:
+        raise ValueError("q must be a 4-d tensor [B][n_q][H][D]")
+    return (g.n_streams, q.shape[1], g.n_heads, g.head_dim)
 
 
 def cke_xattn_decode(q, cache, layer: int, scale: float, out, n_q=None, stream=None) -> None:
     """Cross-attention of q [B][n_q][H][D] (fp32) against layer `layer` of the
-    projection cache, into out (same shape)."""
+    projection cache (an XattnCache), into out (same shape)."""
+    g = _geom(cache)
+    shape = _qshape(g, q)
     if n_q is None:
-        n_q = q.shape[1] if isinstance(q, torch.Tensor) and q.dim() == 4 else 1
-    _check(_lib.cke_xattn_decode(_ptr(q), int(n_q), _handle(cache), int(layer), float(scale),
-                                 _ptr(out), _stream(stream)))
+        n_q = shape[1]
+    elif int(n_q) > shape[1]:
+        raise ValueError("n_q %d exceeds the %d queries q holds" % (n_q, shape[1]))
+    q_ptr, out_ptr = _devs(("q", q, shape, _F32), ("out", out, shape, _F32))
+    _check(_lib.cke_xattn_decode(q_ptr, int(n_q), _handle(cache), int(layer), float(scale),
+                                 out_ptr, _stream(stream)))
 
 
 def cke_xattn_decode_weights(q, cache, layer: int, scale: float, heads, out, weights,
                              stream=None) -> None:
     """Cross decode plus the softmax weights of the listed heads averaged over
     them: weights [B][n_q][T] fp32. cache is an XattnCache."""
-    n_q = q.shape[1]
+    g = _geom(cache)
+    shape = _qshape(g, q)
+    q_ptr, out_ptr, w_ptr = _devs(("q", q, shape, _F32), ("out", out, shape, _F32),
+                                  ("weights", weights, (g.n_streams, shape[1], g.mem_len), _F32))
     hs = (ctypes.c_int32 * len(heads))(*[int(h) for h in heads])
-    _check(_lib.cke_xattn_decode_weights(_ptr(q), n_q, cache.handle, int(layer), float(scale), hs,
-                                         len(heads), _ptr(out), _ptr(weights), _stream(stream)))
+    _check(_lib.cke_xattn_decode_weights(q_ptr, shape[1], cache.handle, int(layer), float(scale),
+                                         hs, len(heads), out_ptr, w_ptr, _stream(stream)))
+
+
+def _kv(kv):
+    if not isinstance(kv, KVLayer):
+        raise TypeError("kv must be a KVLayer")
+    return kv
 
 
 def cke_selfattn_prefill_append(q, k_new, v_new, kv, pos: int, n_new: int, n_q_heads: int,
                                 scale: float, out, stream=None) -> None:
     """Write rows pos..pos+n_new-1 of kv from k_new/v_new [S][n_new][Hkv][D] and
     attend causally for q [S][n_new][n_q_heads][D] (grouped kv heads)."""
-    desc = kv.desc if isinstance(kv, KVLayer) else kv
-    _check(_lib.cke_selfattn_prefill_append(_ptr(q), _ptr(k_new), _ptr(v_new), ctypes.byref(desc),
-                                            int(pos), int(n_new), int(n_q_heads), float(scale),
-                                            _ptr(out), _stream(stream)))
+    kv = _kv(kv)
+    d = kv.desc
+    qshape = (d.n_seqs, int(n_new), int(n_q_heads), d.head_dim)
+    kshape = (d.n_seqs, int(n_new), d.n_heads, d.head_dim)
+    *ptrs, out_ptr = _devs(("q", q, qshape, _F32), ("k_new", k_new, kshape, _F32),
+                           ("v_new", v_new, kshape, _F32), ("out", out, qshape, _F32))
+    _check(_lib.cke_selfattn_prefill_append(*ptrs, ctypes.byref(d), int(pos), int(n_new),
+                                            int(n_q_heads), float(scale), out_ptr,
+                                            _stream(stream)))
 
 
 def cke_selfattn_decode_append(q, k_new, v_new, kv, pos: int, scale: float, out,
                                stream=None) -> None:
-    """Scatter k_new/v_new [S][H][D] into row pos of kv and attend over rows
-    0..pos. kv is a KVLayer or a cke_kv_layer."""
-    desc = kv.desc if isinstance(kv, KVLayer) else kv
-    _check(_lib.cke_selfattn_decode_append(_ptr(q), _ptr(k_new), _ptr(v_new), ctypes.byref(desc),
-                                           int(pos), float(scale), _ptr(out), _stream(stream)))
+    """Scatter k_new/v_new [S][H][D] into row pos of kv (a KVLayer) and attend
+    over rows 0..pos."""
+    kv = _kv(kv)
+    d = kv.desc
+    shape = (d.n_seqs, d.n_heads, d.head_dim)
+    *ptrs, out_ptr = _devs(*[(n, t, shape, _F32) for n, t in (("q", q), ("k_new", k_new),
+                                                               ("v_new", v_new), ("out", out))])
+    _check(_lib.cke_selfattn_decode_append(*ptrs, ctypes.byref(d), int(pos), float(scale),
+                                           out_ptr, _stream(stream)))
 
 
 def cke_decoder_step_workspace_bytes(g: cke_xattn_geom, n_seqs: int) -> int:
@@ -260,28 +343,61 @@ def decoder_layer_desc(WQs, WKs, WVs, WOs, WQ, WO) -> cke_decoder_layer:
     dt = {w.dtype for w in ws}
     if len(dt) != 1:
         raise ValueError("decoder weights must share one dtype")
-    return cke_decoder_layer(*[_ptr(w) for w in ws], _DTYPES[dt.pop()])
+    dt = dt.pop()
+    if dt not in (torch.float32, torch.bfloat16):
+        raise ValueError("decoder weights must be fp32 or bf16 (got %s)" % dt)
+    dm = WQs.shape[0] if WQs.dim() == 2 else -1
+    names = ("WQs", "WKs", "WVs", "WOs", "WQ", "WO")
+    desc = cke_decoder_layer(*_devs(*[(n, w, (dm, dm)) for n, w in zip(names, ws)]), _DTYPES[dt])
+    desc.d_model = dm
+    return desc
 
 
 def cke_decoder_layer_step(x, w, kv, pos: int, cache, layer: int, scale: float, ws,
                            stream=None) -> None:
     """One decoder layer for one token per sequence: x [S][d_model] fp32 is
     updated in place (self-attention residual, then cross-attention residual
-    over `cache` slab `layer`); w is a cke_decoder_layer, kv a KVLayer."""
-    desc = kv.desc if isinstance(kv, KVLayer) else kv
-    _check(_lib.cke_decoder_layer_step(_ptr(x), ctypes.byref(w), ctypes.byref(desc), int(pos),
-                                       _handle(cache), int(layer), float(scale), _ptr(ws),
+    over `cache` slab `layer`); w is a cke_decoder_layer from
+    decoder_layer_desc, kv a KVLayer, ws a workspace of
+    cke_decoder_step_workspace_bytes bytes."""
+    g = _geom(cache)
+    d = _kv(kv).desc
+    if getattr(w, "d_model", None) != g.d_model:
+        raise ValueError("decoder weights must come from decoder_layer_desc with d_model %d"
+                         % g.d_model)
+    need = cke_decoder_step_workspace_bytes(g, d.n_seqs)
+    if isinstance(ws, torch.Tensor) and ws.numel() * ws.element_size() < need:
+        raise ValueError("ws holds %d bytes; the step needs %d"
+                         % (ws.numel() * ws.element_size(), need))
+    x_ptr, ws_ptr = _devs(("x", x, (d.n_seqs, g.d_model), _F32), ("ws", ws, None, None))
+    _check(_lib.cke_decoder_layer_step(x_ptr, ctypes.byref(w), ctypes.byref(d), int(pos),
+                                       _handle(cache), int(layer), float(scale), ws_ptr,
                                        _stream(stream)))
 
 
 def cke_memory_lift_gelu(x, w, out, pos=None, stream=None) -> None:
     """out [rows][n] = gelu(x [rows][k_in] . w [k_in][n]) + pos[r % pos_rows]
-    (exact GELU; pos [pos_rows][n] or None), all fp32 device tensors."""
-    rows, k_in = x.shape[0], x.shape[-1]
+    (exact GELU; pos [pos_rows][n] or None), all fp32 device tensors (out may
+    be any contiguous view of rows x n elements, such as an encoder memory
+    [B][T][n])."""
+    if not isinstance(x, torch.Tensor) or x.dim() != 2 or w.dim() != 2:
+        raise ValueError("x and w must be 2-d tensors [rows][k_in] and [k_in][n]")
+    rows, k_in = x.shape
     n = w.shape[1]
-    _check(_lib.cke_memory_lift_gelu(_ptr(x), int(rows), int(k_in), _ptr(w), int(n), _ptr(pos),
-                                     int(pos.shape[0]) if pos is not None else 0, _ptr(out),
-                                     _stream(stream)))
+    if out.numel() != rows * n:
+        raise ValueError("out must hold rows x n = %d elements (got %d)" % (rows * n, out.numel()))
+    specs = [("x", x, (rows, k_in), _F32), ("w", w, (k_in, n), _F32), ("out", out, None, _F32)]
+    pos_rows = 0
+    if pos is not None:
+        if pos.dim() != 2:
+            raise ValueError("pos must be a 2-d tensor [pos_rows][n]")
+        pos_rows = pos.shape[0]
+        specs.append(("pos", pos, (pos_rows, n), _F32))
+    ptrs = _devs(*specs)
+    x_ptr, w_ptr, out_ptr = ptrs[:3]
+    pos_ptr = ptrs[3] if pos is not None else None
+    _check(_lib.cke_memory_lift_gelu(x_ptr, int(rows), int(k_in), w_ptr, int(n), pos_ptr,
+                                     int(pos_rows), out_ptr, _stream(stream)))
 
 
 class XattnCache:
@@ -345,15 +461,36 @@ class XattnCache:
 
 
 class KVLayer:
-    """One layer's self-attention cache [S][H][max_pos][D] as torch tensors."""
+    """One layer's self-attention cache [S][H][max_pos][D] as torch tensors.
 
-    def __init__(self, n_seqs, n_heads, head_dim, max_pos, dtype=torch.float32, device="cuda",
-                 k=None, v=None):
-        shape = (n_seqs, n_heads, max_pos, head_dim)
-        self.k = torch.zeros(shape, dtype=dtype, device=device) if k is None else k
-        self.v = torch.zeros(shape, dtype=dtype, device=device) if v is None else v
+    With k and v given, their shape and dtype describe the cache (they must
+    agree with each other and with any explicit arguments)."""
+
+    def __init__(self, n_seqs=None, n_heads=None, head_dim=None, max_pos=None, dtype=None,
+                 device="cuda", k=None, v=None):
+        if (k is None) != (v is None):
+            raise ValueError("give both k and v, or neither")
+        if k is None:
+            dtype = torch.float32 if dtype is None else dtype
+            shape = (n_seqs, n_heads, max_pos, head_dim)
+            self.k = torch.zeros(shape, dtype=dtype, device=device)
+            self.v = torch.zeros(shape, dtype=dtype, device=device)
+        else:
+            if k.dim() != 4 or k.shape != v.shape or k.dtype != v.dtype:
+                raise ValueError("k and v must be 4-d tensors [S][H][max_pos][D] of one shape "
+                                 "and dtype")
+            want = (n_seqs, n_heads, max_pos, head_dim)
+            for name, a, b in zip(("n_seqs", "n_heads", "max_pos", "head_dim"), want, k.shape):
+                if a is not None and a != b:
+                    raise ValueError("%s %d disagrees with k's shape %s" % (name, a, tuple(k.shape)))
+            if dtype is not None and dtype != k.dtype:
+                raise ValueError("dtype %s disagrees with k's dtype %s" % (dtype, k.dtype))
+            _devs(("k", k, None, (torch.float32, torch.bfloat16)),
+                  ("v", v, None, (torch.float32, torch.bfloat16)))
+            self.k, self.v = k, v
+        n_seqs, n_heads, max_pos, head_dim = self.k.shape
         self.desc = cke_kv_layer(self.k.data_ptr(), self.v.data_ptr(), n_seqs, n_heads, head_dim,
-                                 max_pos, _DTYPES[dtype])
+                                 max_pos, _DTYPES[self.k.dtype])
 
     def append_attend(self, q, k_new, v_new, pos, scale, out=None, stream=None):
         if out is None:

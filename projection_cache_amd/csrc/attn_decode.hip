@@ -7,7 +7,7 @@
 //     Tensor into Every Decoder Layer", "View 2": query_tokens = 1 against all
 //     key_tokens rows, head-major K/V);
 //   * the softmax weights of selected heads from the decode's own statistics
-//     (xattn_weights_kernel; WhisperKit case study, section 8);
+//     (xattn_weights_kernel; WhisperKit case study, section 6);
 //   * fused scatter-append + causal attention over a self-attention KV cache,
 //     one row (selfattn_append_kernel) or several rows with grouped kv heads
 //     (selfattn_prefill_kernel) ("Recurrence as feeds", "What it opened": the

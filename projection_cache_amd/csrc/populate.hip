@@ -1308,7 +1308,6 @@ hipError_t launch_populate(const PopulateLaunch& a, hipStream_t st) {
 #endif
     if (!a.bf16 && HD % 64 == 0 && a.D <= 64 && 64 % a.D == 0 && a.dm % CKE_POP_F32_DMA_BK == 0)
         return launch_f32_dma<CKE_POP_F32_DMA, CKE_POP_F32_DMA_BK>(g, st);
-    if (HD % 128 == 0) return launch_cfg<128, 128, 2, 2>(g, a.bf16, st);
     if (HD % 64 == 0) return launch_cfg<64, 64, 2, 2>(g, a.bf16, st);
     return launch_cfg<128, 32, 4, 1>(g, a.bf16, st);
 }

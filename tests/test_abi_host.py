@@ -262,3 +262,92 @@ def test_decode_weights_rejects_bad_head_lists_before_launch():
         assert call([1, 3]) == pc.CKE_ENOTREADY
     finally:
         pc.cke_xattn_cache_destroy(h)
+
+
+# ----------------------------------------------- Python binding argument checks
+def _host_cache(geom):
+    """An XattnCache over fake device addresses: enough for the binding's
+    checks, which all run before anything reaches a device."""
+    c = pc.XattnCache.__new__(pc.XattnCache)
+    c.geom = geom
+    c.handle = pc.cke_xattn_cache_create(geom, FAKE, FAKE, FAKE)
+    return c
+
+
+def test_binding_populate_checks_weight_count_and_shapes():
+    import torch
+    g = base_geom(n_layers=2, mem_len=10, d_model=64, n_heads=2, head_dim=32)
+    c = _host_cache(g)
+    try:
+        E = torch.zeros(1, 10, 64)
+        W = [torch.zeros(64, 64) for _ in range(2)]
+        with pytest.raises(ValueError, match="one weight per layer"):
+            pc.cke_xattn_populate(c, E, W[:1], W)              # short WK list
+        with pytest.raises(ValueError, match="one weight per layer"):
+            pc.cke_xattn_populate(c, E, W, W + W)              # uneven lists
+        with pytest.raises(ValueError, match="E must have shape"):
+            pc.cke_xattn_populate(c, torch.zeros(1, 11, 64), W, W)
+        with pytest.raises(ValueError, match=r"WV\[1\] must have shape"):
+            pc.cke_xattn_populate(c, E, W, [W[0], torch.zeros(64, 32)])
+        with pytest.raises(ValueError, match="dtype"):
+            pc.cke_xattn_populate(c, E, W, [W[0], W[1].bfloat16()])
+        with pytest.raises(ValueError, match="device tensor"):
+            pc.cke_xattn_populate(c, E, W, W)                 # host tensors
+        with pytest.raises(TypeError):
+            pc.cke_xattn_populate(c.handle, E, W, W)          # raw handle: no geometry
+        assert not pc.cke_xattn_is_ready(c.handle)
+    finally:
+        c.close()
+
+
+def test_binding_decode_and_self_calls_check_shapes_before_launch():
+    import torch
+    g = base_geom(n_layers=1, n_streams=2, mem_len=10, d_model=64, n_heads=2, head_dim=32,
+                  max_q=3)
+    c = _host_cache(g)
+    try:
+        q = torch.zeros(2, 3, 2, 32)
+        with pytest.raises(ValueError, match="q must have shape"):
+            pc.cke_xattn_decode(torch.zeros(1, 3, 2, 32), c, 0, 0.125, q)
+        with pytest.raises(ValueError, match="out must have shape"):
+            pc.cke_xattn_decode(q, c, 0, 0.125, torch.zeros(2, 2, 2, 32))
+        with pytest.raises(ValueError, match="exceeds"):
+            pc.cke_xattn_decode(q, c, 0, 0.125, q.clone(), n_q=4)
+        with pytest.raises(ValueError, match="dtype"):
+            pc.cke_xattn_decode(q.double(), c, 0, 0.125, q)
+        with pytest.raises(ValueError, match="device tensor"):
+            pc.cke_xattn_decode(q, c, 0, 0.125, q.clone())
+        with pytest.raises(ValueError, match="weights must have shape"):
+            pc.cke_xattn_decode_weights(q, c, 0, 0.125, [0], q.clone(), torch.zeros(2, 3, 9))
+    finally:
+        c.close()
+
+
+def test_binding_kv_layer_takes_shape_and_dtype_from_its_tensors():
+    import torch
+    k = torch.zeros(2, 4, 16, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="disagrees"):
+        pc.KVLayer(2, 4, 64, 16, dtype=torch.float32, k=k, v=k.clone())   # bf16 described as fp32
+    with pytest.raises(ValueError, match="disagrees"):
+        pc.KVLayer(2, 4, 64, 32, k=k, v=k.clone())                        # wrong capacity
+    with pytest.raises(ValueError, match="one shape"):
+        pc.KVLayer(k=k, v=torch.zeros(2, 4, 16, 64))
+    with pytest.raises(ValueError, match="both k and v"):
+        pc.KVLayer(k=k)
+    with pytest.raises(ValueError, match="device tensor"):
+        pc.KVLayer(k=k, v=k.clone())
+    with pytest.raises(TypeError, match="KVLayer"):
+        pc.cke_selfattn_decode_append(None, None, None, pc.cke_kv_layer(), 0, 0.125, None)
+
+
+def test_binding_lift_checks_shapes():
+    import torch
+    x, w = torch.zeros(30, 64), torch.zeros(64, 128)
+    with pytest.raises(ValueError, match="w must have shape"):
+        pc.cke_memory_lift_gelu(x, torch.zeros(32, 128), torch.zeros(30, 128))
+    with pytest.raises(ValueError, match="out must hold"):
+        pc.cke_memory_lift_gelu(x, w, torch.zeros(29, 128))
+    with pytest.raises(ValueError, match="pos must have shape"):
+        pc.cke_memory_lift_gelu(x, w, torch.zeros(30, 128), torch.zeros(15, 64))
+    with pytest.raises(ValueError, match="device tensor"):
+        pc.cke_memory_lift_gelu(x, w, torch.zeros(30, 128))

@@ -24,3 +24,17 @@ def test_roofline_regime_separates_latency_and_bandwidth_bound_calls():
     # Large: one bf16 layer slab over 16 streams is 122,880,000 bytes (+ q/out)
     assert bench.roofline_regime(123043840) == "bandwidth"
     assert bench.roofline_regime(bench.LATENCY_BOUND_BYTES) == "bandwidth"
+
+
+def test_graph_modes_refuse_to_run_under_counter_collection():
+    """Counter passes must use the eager --counters mode: with rocprofv3's
+    counter-collection variables set, the default (graph-capturing) run exits
+    with a message before touching the GPU."""
+    env = dict(os.environ, ROCPROF_COUNTER_COLLECTION="1")
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--config", "tiny"],
+                       capture_output=True, text=True, timeout=300, env=env)
+    assert r.returncode == 3
+    assert "--counters" in r.stderr and r.stdout == ""
+    assert bench.counter_collection_active({"ROCPROF_COUNTERS": "pmc: FETCH_SIZE"})
+    assert not bench.counter_collection_active({"ROCPROF_COUNTER_COLLECTION": "0"})
+    assert not bench.counter_collection_active({})

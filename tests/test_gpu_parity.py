@@ -589,10 +589,13 @@ def test_decoder_layer_step_rejects_bad_pairings_on_a_ready_cache():
     kv3 = pc.KVLayer(3, g.n_heads, g.head_dim, g.max_pos)      # 3 sequences over 2 streams
     kv6 = pc.KVLayer(6, g.n_heads, g.head_dim, g.max_pos)      # n_q = 3 > max_q = 2
     kvh = pc.KVLayer(4, 4, 64, g.max_pos)                      # other head split
+    wsb = torch.zeros(pc.cke_decoder_step_workspace_bytes(st["cache"].geom, 6) // 4, device=DEV)
     for kv, code in ((kv3, pc.CKE_ERANGE), (kv6, pc.CKE_ERANGE), (kvh, pc.CKE_EINVAL)):
+        xs = torch.zeros(kv.desc.n_seqs, g.d_model, device=DEV)
         with pytest.raises(pc.CkeError) as e:
-            pc.cke_decoder_layer_step(x, st["descs"][0], kv, 0, st["cache"], 0, g.scale, st["ws"])
+            pc.cke_decoder_layer_step(xs, st["descs"][0], kv, 0, st["cache"], 0, g.scale, wsb)
         assert e.value.code == code
+        assert float(xs.abs().max()) == 0.0
     with pytest.raises(pc.CkeError) as e:
         pc.cke_decoder_layer_step(x, st["descs"][0], st["kvs"][0], 8, st["cache"], 0, g.scale,
                                   st["ws"])
@@ -619,21 +622,6 @@ def test_memory_lift_matches_oracle(c):
     torch.cuda.synchronize()
     want = oracle.lift_gelu(x, W, pos)
     assert max_abs(to_np(out), want) <= TOL["f32"]
-
-
-def test_qformer_memory_lift_full_size_sampled():
-    """The Q-Former workload's lift at its full size (1500 x 4096 -> 2048, 15
-    position rows), sampled rows against the oracle."""
-    g = synth.get("qformer")
-    wt = synth.workload_tensors(g, ("X_lift", "W_lift", "pos"))
-    rows = g.n_streams * g.mem_len
-    out = torch.empty(rows, g.d_model, device=DEV)
-    pc.cke_memory_lift_gelu(t32(wt["X_lift"]), t32(wt["W_lift"]), out, t32(wt["pos"]))
-    torch.cuda.synchronize()
-    pick = np.array([0, 1, 14, 15, 733, rows - 1])
-    want = oracle.lift_gelu(wt["X_lift"][pick], wt["W_lift"]) + wt["pos"][pick % g.mem_len]
-    assert max_abs(to_np(out)[pick], want) <= TOL["f32"]
-
 
 
 def fp8_bracket(exact, absdot, dm):
@@ -757,76 +745,143 @@ def test_fp8_cross_decode_weights_match_oracle(kw, heads):
 
 
 # ---------------------------------------------------- full-size workloads
-def _sampled_slabs(g, wt, picks):
-    """Oracle slabs for the sampled (layer, stream, head) triples."""
-    bf = g.dtype == "bf16"
-    out = {}
-    for (l, b, h) in picks:
-        k = oracle.project_head(wt["E"][b], wt["WK"][l], h * g.head_dim, g.head_dim, bf)
-        v = oracle.project_head(wt["E"][b], wt["WV"][l], h * g.head_dim, g.head_dim, bf)
-        out[(l, b, h)] = (k, v)
-    return out
+# The workloads at their full sizes, in the launch configuration the benchmark
+# times. What the oracle can compute one element at a time is compared
+# element by element; the rest is covered by properties that hold at any size:
+#   - every output element is written (outputs and caches start as NaN);
+#   - populate: every 256 x 256 output tile of the grouped product (rows of
+#     the B*T memory rows, all columns of every layer) is compared on its
+#     first, last and one random row, against the oracle's projection of
+#     just those rows; and every (layer, stream, head) slab satisfies a
+#     random-sign projection identity, K.r = E.(W_h r), within the rounding
+#     bound of the cache type (Freivalds' check: a wrong row, column block or
+#     tile anywhere breaks it);
+#   - decode: every (stream, query, head) output at the first and the last
+#     layer, over seeded slabs written into the cache, against the oracle on
+#     the same slabs.
+def _nan_fill(t):
+    if t.dtype == torch.float8_e4m3fn:
+        t.view(torch.uint8).fill_(0x7F)      # E4M3 NaN
+    else:
+        t.fill_(float("nan"))
 
 
-def test_full_size_fp8_workload_sampled():
-    """The Large workload over an fp8 cache, as the benchmark times it:
-    populate everything on the GPU; sampled slabs lie in the fp8 bracket of
-    the exact products; decode of the sampled heads, after their slabs are
-    replaced by the oracle's fp8 slabs, matches the oracle to 1e-4."""
-    g = synth.get("large_fp8")
-    cache, wt, _ = make_cache(g)
-    rng = np.random.default_rng(321)
-    picks = [(0, 0, 0), (g.n_layers - 1, g.n_streams - 1, g.n_heads - 1)]
-    for _ in range(3):
-        picks.append((int(rng.integers(g.n_layers)), int(rng.integers(g.n_streams)),
-                      int(rng.integers(g.n_heads))))
-    D = g.head_dim
-    for (l, b, h) in picks:
-        for got, W in ((cache.k[l, b, h], wt["WK"][l]), (cache.v[l, b, h], wt["WV"][l])):
-            Wh = W[:, h * D:(h + 1) * D]
-            exact = oracle.project_head(wt["E"][b], W, h * D, D)
-            absdot = np.abs(wt["E"][b].astype(np.float64)) @ np.abs(Wh.astype(np.float64))
-            lo, hi = fp8_bracket(exact, absdot, g.d_model)
-            got = to_np(got)
-            assert np.all(got >= lo) and np.all(got <= hi), (l, b, h)
-        k = oracle.project_head(wt["E"][b], wt["WK"][l], h * D, D, round_fp8=True)
-        v = oracle.project_head(wt["E"][b], wt["WV"][l], h * D, D, round_fp8=True)
-        cache.k[l, b, h].copy_(tfp8(k))
-        cache.v[l, b, h].copy_(tfp8(v))
-        q = synth.decode_call_inputs(g, 3, l)["q_cross"]
-        out = to_np(cache.decode(t32(q), l, g.scale))
-        want = oracle.attend(q[b, 0, h], k, v, g.scale)
-        assert max_abs(out[b, 0, h], want) <= TOL["f32"], (l, b, h)
+def _finite_per_layer(t):
+    return all(bool(torch.isfinite(t[l].float()).all()) for l in range(t.shape[0]))
 
 
-@pytest.mark.parametrize("name", ["large", "qformer"])
-def test_full_size_workload_sampled(name):
-    """The full workload in the launch configuration the benchmark times:
-    populate everything on the GPU, then check sampled slabs and the decode
-    outputs of the sampled (stream, head) pairs against the oracle."""
+def _tile_rows(M, tile, rng):
+    """First, last and one random row of every `tile`-row block of M rows."""
+    rows = set()
+    for r0 in range(0, M, tile):
+        r1 = min(M, r0 + tile) - 1
+        rows.update((r0, r1, int(rng.integers(r0, r1 + 1))))
+    return np.array(sorted(rows))
+
+
+def _round_bracket(exact, absdot, dm, dtype):
+    """Lowest and highest values a correct populate may store: the roundings
+    (bf16 or fp8, both monotone) of exact -/+ the fp32 accumulation bound
+    (products of bf16 values are exact in fp32; a dm-term fp32 sum errs by at
+    most dm * 2^-24 * sum|e w| to first order, doubled for the second)."""
+    bound = 2.0 * dm * 2.0 ** -24 * absdot
+    rnd = oracle.round_fp8 if dtype == "fp8" else oracle.round_bf16
+    return rnd(exact - bound), rnd(exact + bound)
+
+
+# per stored element: largest rounding error relative to the value (half an
+# ulp: 2^-9 for bf16, 2^-4 for E4M3, with a factor 2-4 of margin for the fp32
+# accumulation) and the absolute floor (E4M3 subnormal spacing 2^-9)
+_FREIVALDS = {"bf16": (2.0 ** -7, 1e-3), "fp8": (2.0 ** -3, 64 * 2.0 ** -10 + 1e-3)}
+
+
+@pytest.mark.parametrize("name", ["large", "large_fp8"])
+def test_full_size_populate_every_tile(name):
     g = synth.get(name)
-    cache, wt, _ = make_cache(g)
-    rng = np.random.default_rng(123)
-    picks = [(0, 0, 0), (g.n_layers - 1, g.n_streams - 1, g.n_heads - 1)]
-    for _ in range(4):
-        picks.append((int(rng.integers(g.n_layers)), int(rng.integers(g.n_streams)),
-                      int(rng.integers(g.n_heads))))
-    ref = _sampled_slabs(g, wt, picks)
-    tol = TOL[g.dtype]
-    for (l, b, h), (k, v) in ref.items():
-        assert max_abs(to_np(cache.k[l, b, h]), k) <= tol, (l, b, h)
-        assert max_abs(to_np(cache.v[l, b, h]), v) <= tol, (l, b, h)
-    for (l, b, h), (k, v) in ref.items():
-        q = synth.decode_call_inputs(g, 3, l)["q_cross"]
-        out = to_np(cache.decode(t32(q), l, g.scale))
-        for i in range(g.n_q):
-            want = oracle.attend(q[b, i, h], k, v, g.scale)
-            assert max_abs(out[b, i, h], want) <= tol, (l, b, h, i)
+    wt = synth.workload_tensors(g)
+    cache = pc.XattnCache(g.n_layers, g.n_streams, g.mem_len, g.d_model, g.n_heads, g.head_dim,
+                          max_q=g.n_q, dtype=CACHE_DT[g.dtype])
+    _nan_fill(cache.k)
+    _nan_fill(cache.v)
+    E = tbf16(wt["E_bits"])
+    WK = [tbf16(b) for b in wt["WK_bits"]]
+    WV = [tbf16(b) for b in wt["WV_bits"]]
+    cache.populate(E, WK, WV)
+    torch.cuda.synchronize()
+    assert cache.ready
+    assert _finite_per_layer(cache.k) and _finite_per_layer(cache.v)
+    B, T, H, D, L, dm = g.n_streams, g.mem_len, g.n_heads, g.head_dim, g.n_layers, g.d_model
+    # every 256 x 256 tile: its first, last and one random row, all columns
+    rows = _tile_rows(B * T, 256, np.random.default_rng(77))
+    worst = 0.0
+    for b in range(B):
+        rb = rows[(rows // T) == b] % T
+        if len(rb) == 0:
+            continue
+        Kx, Vx = oracle.populate(wt["E"][b:b + 1, rb], wt["WK"], wt["WV"], H, D)
+        idx = torch.from_numpy(rb).to(DEV)
+        absE = np.abs(wt["E"][b, rb].astype(np.float64))
+        for got_all, exact_all, Ws in ((cache.k, Kx, wt["WK"]), (cache.v, Vx, wt["WV"])):
+            got = to_np(got_all[:, b].index_select(2, idx))          # [L][H][n][D]
+            for l in range(L):
+                absdot = (absE @ np.abs(Ws[l].astype(np.float64))).reshape(len(rb), H, D)
+                lo, hi = _round_bracket(exact_all[l, 0], absdot.transpose(1, 0, 2), dm, g.dtype)
+                assert np.all(got[l] >= lo) and np.all(got[l] <= hi), (b, l)
+                if g.dtype == "bf16":
+                    worst = max(worst, max_abs(got[l], oracle.round_bf16(exact_all[l, 0])))
+    assert worst <= TOL["bf16"]
+    # Freivalds: K_l[b][h] . r == E_b . (W_l[:, h] r) for every slab, all rows
+    rel, floor = _FREIVALDS[g.dtype]
+    r = np.random.default_rng(78).choice([-1.0, 1.0], size=D)
+    r_dev = torch.from_numpy(r).float().to(DEV)
+    E64 = wt["E"].astype(np.float64)
+    for got_all, Ws in ((cache.k, wt["WK"]), (cache.v, wt["WV"])):
+        for l in range(L):
+            slab = got_all[l].float()                                   # [B][H][T][D]
+            y = to_np(slab @ r_dev)                                     # [B][H][T]
+            mag = to_np(slab.abs().sum(-1))
+            wr = Ws[l].astype(np.float64).reshape(dm, H, D) @ r         # [dm][H]
+            want = (E64 @ wr).transpose(0, 2, 1)                        # [B][H][T]
+            assert np.all(np.abs(y - want) <= rel * mag + floor), l
 
 
-def test_large_self_attention_sampled():
+@pytest.mark.parametrize("name", ["large", "large_fp8"])
+def test_full_size_decode_every_head(name):
+    """Every (stream, head) output of the full-size decode, at the first and
+    the last layer, with the cache holding seeded slabs of the projected
+    spread (stored exactly in the cache type), against the oracle on the same
+    slabs. A cache this large (K and V of 32 layers, far above the 256 MB
+    MALL) is read with streaming loads: this is that path's parity case."""
+    g = synth.get(name)
+    cache = pc.XattnCache(g.n_layers, g.n_streams, g.mem_len, g.d_model, g.n_heads, g.head_dim,
+                          max_q=g.n_q, dtype=CACHE_DT[g.dtype])
+    zeros_e = torch.zeros(g.n_streams, g.mem_len, g.d_model, dtype=torch.bfloat16, device=DEV)
+    zeros_w = [torch.zeros(g.d_model, g.hd, dtype=torch.bfloat16, device=DEV)] * g.n_layers
+    cache.populate(zeros_e, zeros_w, zeros_w)            # sets the ready flag
+    del zeros_e
+    shape = (g.n_streams, g.n_heads, g.mem_len, g.head_dim)
+    for l in (0, g.n_layers - 1):
+        kv = []
+        for which, dst in ((0, cache.k[l]), (1, cache.v[l])):
+            x = torch.from_numpy(synth.normal([g.seed, 90, l, which], shape, synth.q_std(g)))
+            x = x.to(CACHE_DT[g.dtype])                  # the slab as stored (rounded)
+            dst.copy_(x.to(DEV))
+            kv.append(x.double().numpy())
+        for step in (0, 5):
+            q = synth.decode_call_inputs(g, step, l)["q_cross"]
+            out = torch.full(q.shape, float("nan"), device=DEV)
+            pc.cke_xattn_decode(t32(q), cache, l, g.scale, out)
+            torch.cuda.synchronize()
+            got = to_np(out)
+            assert np.isfinite(got).all()
+            want = oracle.cross_decode(q, kv[0], kv[1], g.scale)
+            assert max_abs(got, want) <= TOL["f32"], (l, step)
+
+
+def test_large_self_attention_every_position():
     """Large workload's self-attention: 16 sequences x 20 heads, bf16 cache of
-    capacity 448, 128 decode positions; outputs at sampled positions."""
+    capacity 448, all 128 decode positions; every output compared, stored rows
+    bit-exact."""
     g = synth.get("large")
     kv = pc.KVLayer(g.n_seqs, g.n_heads, g.head_dim, g.max_pos, dtype=torch.bfloat16)
     Ks = np.zeros((g.n_seqs, g.n_heads, g.max_pos, g.head_dim))
@@ -837,10 +892,152 @@ def test_large_self_attention_sampled():
         out = kv.append_attend(t32(d["q_self"]), t32(d["k_new"]), t32(d["v_new"]), pos, g.scale)
         want = oracle.self_append_attend(d["q_self"], d["k_new"], d["v_new"], Ks, Vs, pos,
                                          g.scale, round_bf16=True)
-        if pos % 16 == 0 or pos == g.steps - 1:
-            worst = max(worst, max_abs(to_np(out), want))
+        worst = max(worst, max_abs(to_np(out), want))
     assert worst <= 1e-4
     np.testing.assert_array_equal(to_np(kv.k), Ks)
+    np.testing.assert_array_equal(to_np(kv.v), Vs)
+
+
+def test_qformer_memory_lift_full_size():
+    """The Q-Former workload's lift at full size (1500 x 4096 -> 2048, 15
+    position rows): every element against the oracle."""
+    g = synth.get("qformer")
+    wt = synth.workload_tensors(g, ("X_lift", "W_lift", "pos"))
+    rows = g.n_streams * g.mem_len
+    out = torch.full((rows, g.d_model), float("nan"), device=DEV)
+    pc.cke_memory_lift_gelu(t32(wt["X_lift"]), t32(wt["W_lift"]), out, t32(wt["pos"]))
+    torch.cuda.synchronize()
+    want = oracle.lift_gelu(wt["X_lift"], wt["W_lift"], wt["pos"])
+    assert max_abs(to_np(out), want) <= TOL["f32"]
+
+
+def test_qformer_populate_and_decode_full_size():
+    """The Q-Former workload's projections and block-local decode at full
+    size: populate from the lifted memory (the oracle's lift, rounded to fp32)
+    compared on every element of both layers; decode of every block, query and
+    head over the oracle's cache written into the library's cache."""
+    g = synth.get("qformer")
+    lt = synth.workload_tensors(g, ("X_lift", "W_lift", "pos"))
+    E = oracle.lift_gelu(lt["X_lift"], lt["W_lift"], lt["pos"]).astype(np.float32)
+    E = E.reshape(g.n_streams, g.mem_len, g.d_model)
+    wt = synth.workload_tensors(g)
+    cache = pc.XattnCache(g.n_layers, g.n_streams, g.mem_len, g.d_model, g.n_heads, g.head_dim,
+                          max_q=g.n_q)
+    _nan_fill(cache.k)
+    _nan_fill(cache.v)
+    cache.populate(t32(E), [t32(w) for w in wt["WK"]], [t32(w) for w in wt["WV"]])
+    torch.cuda.synchronize()
+    Kc, Vc = oracle.populate(E, wt["WK"], wt["WV"], g.n_heads, g.head_dim)
+    assert max_abs(to_np(cache.k), Kc) <= TOL["f32"]
+    assert max_abs(to_np(cache.v), Vc) <= TOL["f32"]
+    K32, V32 = Kc.astype(np.float32), Vc.astype(np.float32)
+    cache.k.copy_(t32(K32))
+    cache.v.copy_(t32(V32))
+    for l in range(g.n_layers):
+        q = synth.decode_call_inputs(g, 0, l)["q_cross"]
+        out = torch.full(q.shape, float("nan"), device=DEV)
+        pc.cke_xattn_decode(t32(q), cache, l, g.scale, out)
+        torch.cuda.synchronize()
+        want = oracle.cross_decode(q, K32[l], V32[l], g.scale)
+        assert max_abs(to_np(out), want) <= TOL["f32"], l
+
+
+# ------------------------------------------- split count and resume from state
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "fp8"])
+def test_split_count_does_not_change_the_result(dtype):
+    """The same head's keys and values, decoded in geometries whose key splits
+    differ (32, 8 and 1 workgroups per head, the last with no merge), give the
+    same output to within fp32 summation-order effects, and each matches the
+    oracle."""
+    T, H, D = 1500, 8, 64
+    dm = H * D
+    std = 0.02 * math.sqrt(dm)
+    r = np.random.default_rng(404)
+    kx = torch.from_numpy(r.standard_normal((H, T, D)) * std).float().to(CACHE_DT[dtype])
+    vx = torch.from_numpy(r.standard_normal((H, T, D)) * std).float().to(CACHE_DT[dtype])
+    q = (r.standard_normal((1, 2, H, D)) * std).astype(np.float32)
+    want = oracle.cross_decode(q, kx.double().numpy()[None], vx.double().numpy()[None], 0.125)
+    in_dt = torch.float32 if dtype == "f32" else torch.bfloat16
+    outs, splits = [], []
+    for B in (1, 4, 32):
+        cache = pc.XattnCache(1, B, T, dm, H, D, max_q=2, dtype=CACHE_DT[dtype])
+        cache.populate(torch.zeros(B, T, dm, dtype=in_dt, device=DEV),
+                       [torch.zeros(dm, dm, dtype=in_dt, device=DEV)],
+                       [torch.zeros(dm, dm, dtype=in_dt, device=DEV)])
+        cache.k[0].copy_(kx.to(DEV).expand(B, H, T, D))
+        cache.v[0].copy_(vx.to(DEV).expand(B, H, T, D))
+        out = cache.decode(t32(q).expand(B, 2, H, D).contiguous(), 0, 0.125)
+        torch.cuda.synchronize()
+        o = to_np(out)
+        for b in range(1, B):   # identical streams are computed identically
+            np.testing.assert_array_equal(o[b], o[0])
+        outs.append(o[0])
+        splits.append(cache.n_splits)
+        assert max_abs(o[0:1], want) <= TOL["f32"], B
+    assert splits[0] > splits[1] > splits[2] == 1, splits
+    for o in outs[1:]:
+        assert max_abs(o, outs[0]) <= 2e-6
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_decode_resumes_bit_identically_from_host_copies_of_its_state(dtype):
+    """The caches are ordinary inputs and outputs ('Recurrence as feeds',
+    'What it opened'): stop a decode window at step k, copy the projection
+    cache, every layer's self cache and pos to host memory, drop every device
+    buffer and handle, restore into fresh ones and continue. Every output of
+    the resumed run equals the uninterrupted run's bit for bit."""
+    if dtype == "f32":
+        g = dataclasses.replace(synth.get("base"), steps=16)
+    else:
+        g = geometry(None, n_layers=2, n_streams=2, n_q=1, n_seqs=2, mem_len=700, d_model=512,
+                     n_heads=8, head_dim=64, dtype="bf16", scale=0.125, steps=16, max_pos=32)
+    k_stop = 7
+    wt = synth.workload_tensors(g)
+    sdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    calls = [[synth.decode_call_inputs(g, t, l) for l in range(g.n_layers)]
+             for t in range(g.steps)]
+
+    def fresh():
+        cache, _, _ = make_cache(g, wt)
+        kvs = [pc.KVLayer(g.n_seqs, g.n_heads, g.head_dim, g.max_pos, dtype=sdt)
+               for _ in range(g.n_layers)]
+        return cache, kvs
+
+    def run(cache, kvs, t0, t1):
+        outs = []
+        for t in range(t0, t1):
+            for l in range(g.n_layers):
+                d = calls[t][l]
+                so = kvs[l].append_attend(t32(d["q_self"]), t32(d["k_new"]), t32(d["v_new"]), t,
+                                          g.scale)
+                co = cache.decode(t32(d["q_cross"]), l, g.scale)
+                outs += [so, co]
+        torch.cuda.synchronize()
+        return [o.cpu() for o in outs]
+
+    cache, kvs = fresh()
+    want = run(cache, kvs, 0, g.steps)
+    del cache, kvs
+
+    cache, kvs = fresh()
+    got = run(cache, kvs, 0, k_stop)
+    saved = {"pos": k_stop, "k": cache.k.cpu(), "v": cache.v.cpu(),
+             "self": [(kv.k.cpu(), kv.v.cpu()) for kv in kvs]}
+    cache.close()
+    del cache, kvs
+    torch.cuda.synchronize()
+
+    cache, kvs = fresh()                 # new tensors and handles, populated afresh
+    assert torch.equal(cache.k.cpu().view(torch.uint8), saved["k"].view(torch.uint8))
+    cache.k.copy_(saved["k"].to(DEV))
+    cache.v.copy_(saved["v"].to(DEV))
+    for kv, (k, v) in zip(kvs, saved["self"]):
+        kv.k.copy_(k.to(DEV))
+        kv.v.copy_(v.to(DEV))
+    got += run(cache, kvs, saved["pos"], g.steps)
+    assert len(got) == len(want)
+    for i, (a, b) in enumerate(zip(got, want)):
+        assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), i
 
 
 # ------------------------------------------------------------ graph replay
