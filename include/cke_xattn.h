@@ -244,6 +244,30 @@ int cke_decoder_layer_step(float* x, const cke_decoder_layer* w, const cke_kv_la
                            int pos, const cke_xattn_cache* c, int layer, float scale,
                            void* ws, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * decoder-layer step as cke_decoder_layer_step, with its seven step buffers
+ * in a fixed array inside the library instead of a caller workspace. The
+ * library holds one such array per GPU it runs on, of
+ * cke_decoder_step_scratch_bytes() bytes (2 MiB), until the process ends;
+ * the call itself allocates nothing (no hipMalloc, hipFree or allocating
+ * library routine). The array's device address is looked up once per GPU,
+ * on the first call with that GPU current.
+ *   Same arguments and results as cke_decoder_layer_step, minus ws; the
+ *   projection cache's own workspace (given at cache creation) is still used.
+ *   CKE_EINVAL if the seven buffers (each n_seqs x d_model fp32, 256-byte
+ *   aligned) do not fit the array; CKE_EDEVICE if the array's address cannot
+ *   be found.
+ * Every call on one GPU shares that GPU's array, which keeps the last call's
+ * contents (every buffer is written before it is read, so nothing needs
+ * clearing); calls that overlap on one GPU (other streams, other threads)
+ * race and must be ordered by the caller. */
+size_t cke_decoder_step_scratch_bytes(void);
+int cke_decoder_layer_step_noalloc(float* x, const cke_decoder_layer* w,
+                                   const cke_kv_layer* kv, int pos,
+                                   const cke_xattn_cache* c, int layer,
+                                   float scale, void* stream);
+
 /* Projector memory lift, the prologue that produces a Q-Former-style encoder
  * memory before it is populated:
  *   out[r][j] = gelu(sum_c x[r][c] w[c][j]) + pos[r % pos_rows][j]

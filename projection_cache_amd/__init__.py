@@ -95,6 +95,11 @@ _lib.cke_decoder_step_workspace_bytes.argtypes = [ctypes.POINTER(cke_xattn_geom)
 _lib.cke_decoder_layer_step.restype = _I
 _lib.cke_decoder_layer_step.argtypes = [_P, ctypes.POINTER(cke_decoder_layer),
                                         ctypes.POINTER(cke_kv_layer), _I, _P, _I, _F, _P, _P]
+_lib.cke_decoder_step_scratch_bytes.restype = _SZ
+_lib.cke_decoder_step_scratch_bytes.argtypes = []
+_lib.cke_decoder_layer_step_noalloc.restype = _I
+_lib.cke_decoder_layer_step_noalloc.argtypes = [_P, ctypes.POINTER(cke_decoder_layer),
+                                                ctypes.POINTER(cke_kv_layer), _I, _P, _I, _F, _P]
 _lib.cke_memory_lift_gelu.restype = _I
 _lib.cke_memory_lift_gelu.argtypes = [_P, _I, _I, _P, _I, _P, _I, _P, _P]
 
@@ -103,7 +108,9 @@ EXPORTED = ["cke_xattn_region_bytes", "cke_xattn_layer_offset_bytes",
             "cke_xattn_cache_destroy", "cke_xattn_invalidate", "cke_xattn_is_ready",
             "cke_xattn_populate", "cke_xattn_decode", "cke_selfattn_decode_append",
             "cke_selfattn_prefill_append", "cke_xattn_decode_weights",
-            "cke_decoder_step_workspace_bytes", "cke_decoder_layer_step", "cke_memory_lift_gelu",
+            "cke_decoder_step_workspace_bytes", "cke_decoder_layer_step",
+            "cke_decoder_step_scratch_bytes", "cke_decoder_layer_step_noalloc",
+            "cke_memory_lift_gelu",
             "cke_last_error", "cke_version"]
 
 
@@ -373,6 +380,25 @@ def cke_decoder_layer_step(x, w, kv, pos: int, cache, layer: int, scale: float, 
     _check(_lib.cke_decoder_layer_step(x_ptr, ctypes.byref(w), ctypes.byref(d), int(pos),
                                        _handle(cache), int(layer), float(scale), ws_ptr,
                                        _stream(stream)))
+
+
+def cke_decoder_step_scratch_bytes() -> int:
+    return int(_lib.cke_decoder_step_scratch_bytes())
+
+
+def cke_decoder_layer_step_noalloc(x, w, kv, pos: int, cache, layer: int, scale: float,
+                                   stream=None) -> None:
+    """cke_decoder_layer_step with the step buffers in the library's own
+    per-GPU scratch array: no workspace argument, nothing allocated."""
+    g = _geom(cache)
+    d = _kv(kv).desc
+    if getattr(w, "d_model", None) != g.d_model:
+        raise ValueError("decoder weights must come from decoder_layer_desc with d_model %d"
+                         % g.d_model)
+    x_ptr = _dev("x", x, (d.n_seqs, g.d_model), _F32)
+    _check(_lib.cke_decoder_layer_step_noalloc(x_ptr, ctypes.byref(w), ctypes.byref(d), int(pos),
+                                               _handle(cache), int(layer), float(scale),
+                                               _stream(stream)))
 
 
 def cke_memory_lift_gelu(x, w, out, pos=None, stream=None) -> None:

@@ -9,9 +9,11 @@
 // num_heads * head_dim != embed_dim is an error, never a default.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 
 #include "../../include/cke_xattn.h"
@@ -462,9 +464,16 @@ size_t cke_decoder_step_workspace_bytes(const cke_xattn_geom* g, int n_seqs) {
     return kStepBuffers * step_buffer_bytes(g, n_seqs);
 }
 
-int cke_decoder_layer_step(float* x, const cke_decoder_layer* w, const cke_kv_layer* kv, int pos,
-                           const cke_xattn_cache* c, int layer, float scale, void* ws,
-                           void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Checks and launches shared by the two decoder-step entry points. `ws` is
+// the seven-buffer workspace (caller memory or the library's scratch array);
+// `ws_cap` its capacity in bytes, or 0 when the caller vouches for the size.
+int decoder_layer_step(float* x, const cke_decoder_layer* w, const cke_kv_layer* kv, int pos,
+                       const cke_xattn_cache* c, int layer, float scale, void* ws, size_t ws_cap,
+                       void* stream) {
     if (!c) return fail(CKE_EINVAL, "cache handle is NULL");
     const cke_xattn_geom& g = c->g;
     if (layer < 0 || layer >= g.n_layers)
@@ -492,6 +501,11 @@ int cke_decoder_layer_step(float* x, const cke_decoder_layer* w, const cke_kv_la
     if (!x || !aligned16(x)) return fail(CKE_EINVAL, "x must be non-NULL and 16-byte aligned");
     if (!ws || (reinterpret_cast<uintptr_t>(ws) & (kAlign - 1)) != 0)
         return fail(CKE_EINVAL, "workspace must be non-NULL and 256-byte aligned");
+    if (ws_cap && kStepBuffers * step_buffer_bytes(&g, S) > ws_cap)
+        return fail(CKE_EINVAL,
+                    "n_seqs x d_model (%d x %d) needs %zu bytes of step buffers; the library's "
+                    "scratch holds %zu", S, g.d_model, kStepBuffers * step_buffer_bytes(&g, S),
+                    ws_cap);
     if (!(scale == scale)) return fail(CKE_EINVAL, "scale is NaN");
     const int dm = g.d_model;
     const bool wbf16 = w->dtype == CKE_BF16;
@@ -553,6 +567,59 @@ int cke_decoder_layer_step(float* x, const cke_decoder_layer* w, const cke_kv_la
         if (e != hipSuccess) return fail(CKE_EDEVICE, "decoder-step projection launch failed: %s", hipGetErrorString(e));
     }
     return CKE_OK;
+}
+
+// The allocation-free decoder step's buffers: one file-scope device array per
+// GPU, alive until the process ends. In host code `scratch` names only a
+// host-side stand-in; the device address of each GPU's copy comes from
+// hipGetSymbolAddress with that GPU current and is kept per device.
+constexpr size_t kStepScratchBytes = size_t(2) << 20;
+static __device__ __align__(256) unsigned char scratch[kStepScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of the current GPU's scratch array (looked up once per
+// device); nullptr with the message set on failure.
+void* step_scratch() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        fail(CKE_EDEVICE, "no current HIP device (or device index >= %d)", kMaxDevices);
+        return nullptr;
+    }
+    void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (p) return p;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (p) return p;
+    hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+        fail(CKE_EDEVICE, "scratch address lookup failed on device %d: %s", dev, hipGetErrorString(e));
+        return nullptr;
+    }
+    g_scratch_ptr[dev].store(p, std::memory_order_release);
+    return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+int cke_decoder_layer_step(float* x, const cke_decoder_layer* w, const cke_kv_layer* kv, int pos,
+                           const cke_xattn_cache* c, int layer, float scale, void* ws,
+                           void* stream) {
+    return decoder_layer_step(x, w, kv, pos, c, layer, scale, ws, 0, stream);
+}
+
+size_t cke_decoder_step_scratch_bytes(void) { return kStepScratchBytes; }
+
+int cke_decoder_layer_step_noalloc(float* x, const cke_decoder_layer* w, const cke_kv_layer* kv,
+                                   int pos, const cke_xattn_cache* c, int layer, float scale,
+                                   void* stream) {
+    void* ws = step_scratch();
+    if (!ws) return CKE_EDEVICE;
+    return decoder_layer_step(x, w, kv, pos, c, layer, scale, ws, kStepScratchBytes, stream);
 }
 
 }  // extern "C"
