@@ -300,6 +300,12 @@ def roofline_regime(bytes_per_call):
     return "bandwidth"
 
 
+# the sources of the decode kernels: counters taken before any of them
+# changed no longer describe the kernel that runs
+DECODE_SOURCES = ("attn_kernels.h", "attn_decode.hip", "attn_f32.hip", "attn_bf16.hip",
+                  "attn_fp8.hip", "cke_device.h")
+
+
 def measured_traffic(config):
     """HBM bytes per cross-attention decode call (split + merge kernels) from the
     committed rocprofv3 counter summary, scaled by its copy calibration; None if
@@ -311,7 +317,7 @@ def measured_traffic(config):
         t = json.load(open(path))
     except (OSError, ValueError):
         return None
-    for f in ("attn_decode.hip", "cke_device.h"):
+    for f in DECODE_SOURCES:
         src = os.path.join(ROOT, "projection_cache_amd", "csrc", f)
         if hashlib.sha256(open(src, "rb").read()).hexdigest() != t["sources_sha256"].get(f):
             return None

@@ -9,7 +9,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libcke_xattn.so")
-SOURCES = ["cke_api.hip", "attn_decode.hip", "populate.hip", "decoder_step.hip"]
+SOURCES = ["cke_api.hip", "attn_decode.hip", "attn_f32.hip", "attn_bf16.hip", "attn_fp8.hip",
+           "populate.hip", "decoder_step.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17",

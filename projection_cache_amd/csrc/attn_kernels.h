@@ -1,0 +1,617 @@
+#pragma once
+// Decode-time attention kernels and their launch templates, included by the
+// per-element-type translation units attn_f32.hip, attn_bf16.hip and
+// attn_fp8.hip (each instantiates its own type, so the three build in
+// parallel) and by attn_decode.hip (the type dispatch). Everything here has
+// internal linkage: each translation unit owns its instantiations.
+//
+// Decode-time attention kernels for gfx950:
+//   * cross-attention of one query token (per stream, up to NQ of them)
+//     against one layer slab of the projection cache, split over the memory
+//     rows (xattn_partial_kernel) and merged by a second, small kernel
+//     (xattn_merge_kernel), or one wave per head for short memories
+//     (xattn_short_kernel) (C-Kernel-Engine, "Whisper: Trace One Encoder
+//     Tensor into Every Decoder Layer", "View 2": query_tokens = 1 against all
+//     key_tokens rows, head-major K/V);
+//   * the softmax weights of selected heads from the decode's own statistics
+//     (xattn_weights_kernel; WhisperKit case study, section 6);
+//   * fused scatter-append + causal attention over a self-attention KV cache,
+//     one row (selfattn_append_kernel) or several rows with grouped kv heads
+//     (selfattn_prefill_kernel) ("Recurrence as feeds", "What it opened": the
+//     cache is an explicit input and output and the new rows are written with
+//     scatter; WhisperKit case study, sections 3 and 4).
+//
+// All are HBM-bound streaming kernels (0.5-2.5 FLOP per byte). Each lane
+// reads 16 contiguous bytes of a K row and of a V row (4 fp32, 8 bf16 or 16
+// fp8 values), a wave reads whole rows, and every load of a tile is issued
+// before the arithmetic that uses it.
+#include "../../include/cke_xattn.h"
+#include "cke_device.h"
+#include "cke_internal.h"
+
+namespace cke {
+namespace {
+
+// ----------------------------------------------------------------- cross
+// Grid: (nsplit, H, B). Workgroup `split` covers memory rows
+// [split*chunk, min(T, (split+1)*chunk)) of head h of stream b, for all nq
+// queries of that stream, so the queries of one stream share every K/V read.
+// With nsplit == 1 it writes `out` directly; otherwise it writes its partial
+// (max, sum, acc[D]) per query to `part` and xattn_merge_kernel, launched
+// next on the same stream, combines them.
+//
+// Why a second launch: merging inside this kernel needs the partials of
+// other workgroups, which run on other XCDs with their own L2. A
+// release/acquire pair per workgroup is a whole-L2 writeback + invalidate on
+// gfx950, and a fence-free variant (tagged 64-bit partial words with
+// device-scope atomic loads and stores, last arrival by ticket) pays several
+// device-scope round trips on its tail; both measured slower than a second
+// small kernel, whose inputs are coherent at the kernel boundary.
+template <int D, typename TE, int NQ, int NW, int NP, bool STREAM>
+__global__ __launch_bounds__(NW * 64) void xattn_partial_kernel(
+    const float* __restrict__ q, const TE* __restrict__ Kl, const TE* __restrict__ Vl,
+    float* __restrict__ out, float* __restrict__ part, float* __restrict__ stats,
+    int nq, int max_q, int H, int T, int nsplit, int chunk, float sl2)
+{
+    using RM = RowMap<D, TE>;
+    constexpr int VEC = RM::kVec, LPK = RM::kLPK, KPW = RM::kKPW;
+    __shared__ float wm[NW * NQ], wl[NW * NQ], wa[NW * NQ * D];
+    __shared__ float sM[NQ], sL[NQ], sA[NQ * D];
+
+    const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const size_t bh = (size_t)b * H + h;
+    const TE* K = Kl + bh * (size_t)T * D;
+    const TE* V = Vl + bh * (size_t)T * D;
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+    const int sub = lane % LPK;
+
+    float qr[NQ][VEC];
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) {
+#pragma unroll
+        for (int j = 0; j < VEC; ++j)
+            qr[i][j] = (i < nq) ? q[(((size_t)b * nq + i) * H + h) * D + sub * VEC + j] : 0.f;
+    }
+
+    const int c0 = split * chunk;
+    const int c1 = min(T, c0 + chunk);
+    const int per_wave = ((c1 - c0 + NW * KPW - 1) / (NW * KPW)) * KPW;
+    const int r0 = min(c1, c0 + w * per_wave);
+    const int r1 = min(c1, r0 + per_wave);
+
+    WaveState<NQ, VEC> st;
+    st.init();
+    wave_attend<D, TE, NQ, NP, STREAM>(K, V, r0, r1, qr, nq, sl2, st);
+    wg_merge<D, TE, NQ, NW>(st, nq, wm, wl, wa, sM, sL, sA);
+
+    if (nsplit == 1) {
+        for (int idx = threadIdx.x; idx < nq * D; idx += NW * 64) {
+            const int i = idx / D, d = idx % D;
+            out[(((size_t)b * nq + i) * H + h) * D + d] = sA[i * D + d] / sL[i];
+        }
+        if (stats && threadIdx.x < nq) {
+            float* st2 = stats + (((size_t)b * max_q + threadIdx.x) * H + h) * 2;
+            st2[0] = sM[threadIdx.x];
+            st2[1] = sL[threadIdx.x];
+        }
+        return;
+    }
+    // partial layout [B][max_q][H][nsplit][D+2]: M, L, acc[0..D)
+    for (int idx = threadIdx.x; idx < nq * (D + 2); idx += NW * 64) {
+        const int i = idx / (D + 2), k = idx % (D + 2);
+        float* p = part + ((((size_t)b * max_q + i) * H + h) * nsplit + split) * (D + 2);
+        p[k] = k == 0 ? sM[i] : (k == 1 ? sL[i] : sA[i * D + k - 2]);
+    }
+}
+
+// Grid: (H, B). Combines the nsplit partials of each (stream, query, head)
+// of one head:
+//   M = max_s M_s,  L = sum_s L_s 2^(M_s - M),  out = sum_s A_s 2^(M_s - M) / L
+// Thread (o, g), o = (query, dim), g < G = ceil(nsplit / kMergeBatch), takes
+// splits s = g, g+G, ... (at most kMergeBatch of them). It loads (M_s, L_s,
+// A_s[d]) of all its splits at once -- clamped, branch-free addresses, so
+// every load is in flight together and the merge costs one memory round
+// trip -- and folds them in ascending s with the running-max update. Groups
+// are then combined through LDS in ascending g (deterministic). Dynamic LDS:
+// 3 floats per (o, g).
+constexpr int kMergeBatch = 16;
+
+template <int D>
+__global__ __launch_bounds__(1024) void xattn_merge_kernel(
+    const float* __restrict__ part, float* __restrict__ out, float* __restrict__ stats, int nq,
+    int max_q, int H, int nsplit)
+{
+    extern __shared__ float smem[];
+    const int h = blockIdx.x, b = blockIdx.y;
+    const int n_out = nq * D;
+    const int G = (nsplit + kMergeBatch - 1) / kMergeBatch;
+    float* sm = smem;
+    float* sl = smem + n_out * G;
+    float* sa = smem + 2 * n_out * G;
+    for (int idx = threadIdx.x; idx < n_out * G; idx += blockDim.x) {
+        const int o = idx % n_out, g = idx / n_out;
+        const int i = o / D, d = o % D;
+        const float* p0 = part + (((size_t)b * max_q + i) * H + h) * (size_t)nsplit * (D + 2);
+        float pm[kMergeBatch], pl[kMergeBatch], pa[kMergeBatch];
+#pragma unroll
+        for (int j = 0; j < kMergeBatch; ++j) {
+            const int s = min(g + j * G, nsplit - 1);
+            const float* p = p0 + (size_t)s * (D + 2);
+            pm[j] = p[0];
+            pl[j] = p[1];
+            pa[j] = p[2 + d];
+        }
+        float m = -INFINITY, l = 0.f, a = 0.f;
+#pragma unroll
+        for (int j = 0; j < kMergeBatch; ++j) {
+            if (g + j * G < nsplit) {
+                const float mn = fmaxf(m, pm[j]);
+                const float f_old = fast_exp2(m - mn);   // m = -inf on the first split: 0
+                const float f_new = fast_exp2(pm[j] - mn);
+                l = fmaf(l, f_old, pl[j] * f_new);
+                a = fmaf(a, f_old, pa[j] * f_new);
+                m = mn;
+            }
+        }
+        sm[idx] = m;
+        sl[idx] = l;
+        sa[idx] = a;
+    }
+    __syncthreads();
+    for (int o = threadIdx.x; o < n_out; o += blockDim.x) {
+        float m = -INFINITY, l = 0.f, a = 0.f;
+        for (int g = 0; g < G; ++g) {
+            const float mg = sm[g * n_out + o];
+            const float mn = fmaxf(m, mg);
+            const float f_old = fast_exp2(m - mn);
+            const float f_new = fast_exp2(mg - mn);
+            l = fmaf(l, f_old, sl[g * n_out + o] * f_new);
+            a = fmaf(a, f_old, sa[g * n_out + o] * f_new);
+            m = mn;
+        }
+        const int i = o / D, d = o % D;
+        out[(((size_t)b * nq + i) * H + h) * D + d] = a / l;
+        if (stats && d == 0) {
+            float* st2 = stats + (((size_t)b * max_q + i) * H + h) * 2;
+            st2[0] = m;
+            st2[1] = l;
+        }
+    }
+}
+
+// Short memories (e.g. 15-frame blocks): one wave per (stream, head), NW of
+// them per workgroup, each attending over all T rows on its own, so no
+// cross-wave merge and no split. Grid: ceil(B*H / NW).
+template <int D, typename TE, int NQ, int NW, int NP>
+__global__ __launch_bounds__(NW * 64) void xattn_short_kernel(
+    const float* __restrict__ q, const TE* __restrict__ Kl, const TE* __restrict__ Vl,
+    float* __restrict__ out, float* __restrict__ stats, int nq, int max_q, int H, int T, int n_bh,
+    float sl2)
+{
+    using RM = RowMap<D, TE>;
+    constexpr int VEC = RM::kVec, LPK = RM::kLPK;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+    const int bh = blockIdx.x * NW + w;
+    if (bh >= n_bh) return;   // whole wave; this kernel has no barrier
+    const int b = bh / H, h = bh % H;
+    const int lane = threadIdx.x & 63, sub = lane % LPK;
+    const TE* K = Kl + (size_t)bh * T * D;
+    const TE* V = Vl + (size_t)bh * T * D;
+    float qr[NQ][VEC];
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) {
+#pragma unroll
+        for (int j = 0; j < VEC; ++j)
+            qr[i][j] = (i < nq) ? q[(((size_t)b * nq + i) * H + h) * D + sub * VEC + j] : 0.f;
+    }
+    WaveState<NQ, VEC> st;
+    st.init();
+    wave_attend<D, TE, NQ, NP>(K, V, 0, T, qr, nq, sl2, st);
+    wave_merge_groups<D, TE, NQ>(st, nq);
+    if (lane < LPK) {
+#pragma unroll
+        for (int i = 0; i < NQ; ++i) {
+            if (i < nq) {
+                float* o = out + (((size_t)b * nq + i) * H + h) * D + sub * VEC;
+#pragma unroll
+                for (int j = 0; j < VEC; ++j) o[j] = st.acc[i][j] / st.l[i];
+                if (stats && lane == 0) {
+                    float* st2 = stats + (((size_t)b * max_q + i) * H + h) * 2;
+                    st2[0] = st.m[i];
+                    st2[1] = st.l[i];
+                }
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------------ self
+// Grid: (H, S). One workgroup per (sequence, head) owns rows 0..pos of that
+// head's cache: it writes row pos from k_new / v_new (rounded to the storage
+// type) and attends over rows 0..pos, taking row pos from the fp32 inputs
+// rounded the same way rather than re-reading it, so no workgroup ever reads a
+// row another one writes. Rows > pos are neither read nor written.
+template <int D, typename TE, int NW, int NP>
+__global__ __launch_bounds__(NW * 64) void selfattn_append_kernel(
+    const float* __restrict__ q, const float* __restrict__ k_new,
+    const float* __restrict__ v_new, TE* __restrict__ Kc, TE* __restrict__ Vc,
+    float* __restrict__ out, int H, int max_pos, int pos, float sl2)
+{
+    using RM = RowMap<D, TE>;
+    constexpr int VEC = RM::kVec, LPK = RM::kLPK, KPW = RM::kKPW;
+    __shared__ float wm[NW], wl[NW], wa[NW * D];
+    __shared__ float sM[1], sL[1], sA[D];
+
+    const int h = blockIdx.x, s = blockIdx.y;
+    const size_t bh = (size_t)s * H + h;
+    TE* K = Kc + bh * (size_t)max_pos * D;
+    TE* V = Vc + bh * (size_t)max_pos * D;
+    const float* kn = k_new + bh * D;
+    const float* vn = v_new + bh * D;
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+    const int sub = lane % LPK;
+
+    const int n = pos + 1;
+    const int per_wave = ((n + NW * KPW - 1) / (NW * KPW)) * KPW;
+    const int r0 = min(n, w * per_wave);
+    const int r1 = min(n, r0 + per_wave);
+    const bool has_cur = r0 <= pos && pos < r1;   // this wave's range ends with row pos
+
+    // Loads first: the new row's fp32 source (only the wave that owns row pos),
+    // the query, then the cache rows 0..pos-1 inside wave_attend; the new row
+    // is rounded and folded in after them, so no load waits for another.
+    CurRow<TE> ckr{}, cvr{};
+    if (has_cur) {
+        ckr = load_cur<TE>(kn + sub * VEC);
+        cvr = load_cur<TE>(vn + sub * VEC);
+    }
+    float qr[1][VEC];
+#pragma unroll
+    for (int j = 0; j < VEC; ++j) qr[0][j] = q[bh * D + sub * VEC + j];
+
+    WaveState<1, VEC> st;
+    st.init();
+    wave_attend<D, TE, 1, NP>(K, V, r0, min(r1, pos), qr, 1, sl2, st);
+    if (has_cur) {
+        keep_below(ckr);
+        keep_below(cvr);
+        fold_row<D, TE, 1>(pos, pack_cur<TE>(ckr), pack_cur<TE>(cvr), lane / LPK, qr, 1, sl2, st);
+    }
+    if constexpr (NW == 1) {
+        // one wave holds every row: no cross-wave merge, no barrier
+        wave_merge_groups<D, TE, 1>(st, 1);
+        if (lane < LPK) {
+#pragma unroll
+            for (int j = 0; j < VEC; ++j) out[bh * D + sub * VEC + j] = st.acc[0][j] / st.l[0];
+        }
+    } else {
+        wg_merge<D, TE, 1, NW>(st, 1, wm, wl, wa, sM, sL, sA);
+        for (int d = threadIdx.x; d < D; d += NW * 64) out[bh * D + d] = sA[d] / sL[0];
+    }
+    // Scatter the new row last. No wave reads it from memory (its owner folds
+    // it in from k_new / v_new), and stored earlier its loads and stores would
+    // come before, and delay, the cache-row loads.
+    for (int d = threadIdx.x; d < D; d += NW * 64) {
+        if constexpr (sizeof(TE) == 2) {
+            K[(size_t)pos * D + d] = to_bf16_bits(kn[d]);
+            V[(size_t)pos * D + d] = to_bf16_bits(vn[d]);
+        } else {
+            K[(size_t)pos * D + d] = kn[d];
+            V[(size_t)pos * D + d] = vn[d];
+        }
+    }
+}
+
+// ----------------------------------------------------- attention weights
+// Grid: (ceil(T / (4 * KPW)), B), 4 waves. Rows map to lanes as in the decode
+// kernels: a group of LPK lanes reads one row, 16 bytes per lane, so a wave
+// covers KPW consecutive rows with coalesced loads. For every query i the
+// group re-forms the row's score under each selected head,
+// s = scale log2(e) q.K[b][h][t] (dot reduced across the group with DPP),
+// weights it with that head's final (max, sum) in the base-2 domain left in
+// `stats` by the decode of the same call, p = 2^(s - max) / sum, and the
+// group's first lane writes the mean over the selected heads, summed in list
+// order (deterministic).
+template <int D, typename TE>
+__global__ __launch_bounds__(256) void xattn_weights_kernel(
+    const float* __restrict__ q, const TE* __restrict__ Kl, const float* __restrict__ stats,
+    float* __restrict__ weights, HeadList heads, int H, int T, int nq, int max_q, float sl2)
+{
+    using RM = RowMap<D, TE>;
+    constexpr int VEC = RM::kVec, LPK = RM::kLPK, KPW = RM::kKPW;
+    const int b = blockIdx.y;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int grp = lane / LPK, sub = lane % LPK;
+    const int t = (blockIdx.x * 4 + w) * KPW + grp;
+    const int tr = min(t, T - 1);   // rows past T load row T-1 and write nothing
+    const int n_sel = heads.n;
+    for (int i = 0; i < nq; ++i) {
+        float acc = 0.f;
+        for (int k = 0; k < n_sel; ++k) {
+            const int h = heads.h[k];
+            const uint4 r = load16(Kl + (((size_t)b * H + h) * T + tr) * D + sub * VEC);
+            const float* qv = q + (((size_t)b * nq + i) * H + h) * D + sub * VEC;
+            float dot = 0.f;
+#pragma unroll
+            for (int j = 0; j < VEC; ++j) dot = fmaf(qv[j], elem<TE>(r, j), dot);
+            dot = group_sum<LPK>(dot);
+            const float* st2 = stats + (((size_t)b * max_q + i) * H + h) * 2;
+            acc += fast_exp2(dot * sl2 - st2[0]) / st2[1];
+        }
+        if (sub == 0 && t < T) weights[((size_t)b * nq + i) * T + t] = acc / n_sel;
+    }
+}
+
+// --------------------------------------------------------- self prefill
+// Grid: (Hkv, S). One workgroup per (sequence, kv head) writes that kv head's
+// rows pos .. pos+n_new-1 (rounded to the storage type), passes a workgroup
+// barrier -- whose workgroup-scope release/acquire makes those stores visible
+// to its own waves -- and then its waves take groups of up to QB consecutive
+// tokens of one query head of the kv head's group (group j: head
+// h = kv*G + j % G, tokens QB*(j / G) ..), reading rows 0 .. pos+i once per
+// group with each token i masked to its own causal limit pos+i+1. Rows past
+// pos+n_new-1 are neither read nor written, and no workgroup touches another
+// one's rows.
+template <int D, typename TE, int NW, int NP, int QB>
+__global__ __launch_bounds__(NW * 64) void selfattn_prefill_kernel(
+    const float* __restrict__ q, const float* __restrict__ k_new,
+    const float* __restrict__ v_new, TE* __restrict__ Kc, TE* __restrict__ Vc,
+    float* __restrict__ out, int Hkv, int Hq, int max_pos, int pos, int n_new, float sl2)
+{
+    using RM = RowMap<D, TE>;
+    constexpr int VEC = RM::kVec, LPK = RM::kLPK;
+    const int hk = blockIdx.x, s = blockIdx.y;
+    const size_t skv = (size_t)s * Hkv + hk;
+    TE* K = Kc + skv * (size_t)max_pos * D;
+    TE* V = Vc + skv * (size_t)max_pos * D;
+    const int G = Hq / Hkv;
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+    const int sub = lane % LPK;
+
+    for (int x = threadIdx.x; x < n_new * D; x += NW * 64) {
+        const int i = x / D, d = x % D;
+        const size_t src = (((size_t)s * n_new + i) * Hkv + hk) * D + d;
+        const size_t dst = (size_t)(pos + i) * D + d;
+        if constexpr (sizeof(TE) == 2) {
+            K[dst] = to_bf16_bits(k_new[src]);
+            V[dst] = to_bf16_bits(v_new[src]);
+        } else {
+            K[dst] = k_new[src];
+            V[dst] = v_new[src];
+        }
+    }
+    __syncthreads();
+
+    const int blocks = (n_new + QB - 1) / QB;
+    for (int j = w; j < blocks * G; j += NW) {
+        const int h = hk * G + j % G, i0 = QB * (j / G);
+        const int nq = min(QB, n_new - i0);
+        float qr[QB][VEC];
+        int lim[QB];
+#pragma unroll
+        for (int k = 0; k < QB; ++k) {
+            const int i = min(i0 + k, n_new - 1);
+            lim[k] = pos + i + 1;
+            const size_t qo = (((size_t)s * n_new + i) * Hq + h) * D;
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) qr[k][e] = q[qo + sub * VEC + e];
+        }
+        WaveState<QB, VEC> st;
+        st.init();
+        wave_attend_causal<D, TE, QB, NP>(K, V, lim, qr, nq, sl2, st);
+        wave_merge_groups<D, TE, QB>(st, nq);
+        if (lane < LPK) {
+#pragma unroll
+            for (int k = 0; k < QB; ++k) {
+                if (k < nq) {
+                    const size_t qo = (((size_t)s * n_new + i0 + k) * Hq + h) * D;
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e) out[qo + sub * VEC + e] = st.acc[k][e] / st.l[k];
+                }
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------- launchers
+
+#ifndef CKE_CROSS_WAVES
+#define CKE_CROSS_WAVES 4
+#endif
+#ifndef CKE_CROSS_NP
+#define CKE_CROSS_NP 4
+#endif
+#ifndef CKE_SELF_WAVES
+#define CKE_SELF_WAVES 8
+#endif
+#ifndef CKE_SELF_NP
+#define CKE_SELF_NP 4
+#endif
+constexpr int kCrossWaves = CKE_CROSS_WAVES;  // waves per cross-decode workgroup
+constexpr int kCrossNP = CKE_CROSS_NP;        // row passes per load tile
+constexpr int kSelfWaves = CKE_SELF_WAVES;
+constexpr int kSelfNP = CKE_SELF_NP;
+
+// Memories this short go to xattn_short_kernel.
+constexpr int kShortRows = kShortMemRows;
+#ifndef CKE_SHORT_NP
+#define CKE_SHORT_NP 4
+#endif
+constexpr int kShortNP = CKE_SHORT_NP;  // passes per tile: 16 fp32 rows of 64 in one tile
+
+template <int D, typename TE, int NQ>
+hipError_t launch_cross_nq(const XattnLaunch& a, hipStream_t st) {
+    if (a.T <= kShortRows) {
+        constexpr int NW = 4;
+        const int n_bh = a.B * a.H;
+        hipLaunchKernelGGL((xattn_short_kernel<D, TE, NQ, NW, kShortNP>), dim3((n_bh + NW - 1) / NW),
+                           dim3(NW * 64), 0, st, a.q, static_cast<const TE*>(a.K),
+                           static_cast<const TE*>(a.V), a.out, a.stats, a.nq, a.max_q, a.H, a.T,
+                           n_bh, a.scale * kLog2e);
+        return hipGetLastError();
+    }
+    // With more than two queries, bf16 and fp8 rows (8 or 16 values per lane)
+    // keep their tiles short: long ones cost registers (fp8 spills from four
+    // queries on). fp32 rows (4 values per lane) keep full tiles at any query
+    // count, 167 registers at most (Beam's 5 queries: 11.3 against 11.75 us).
+    constexpr int NP = (NQ > 2 && sizeof(TE) < 4 && kCrossNP > 2) ? 2 : kCrossNP;
+    dim3 grid(a.nsplit, a.H, a.B);
+    // streaming loads only for 16- and 8-bit caches: an fp32 cache of over
+    // 512 MB takes normal loads (one kernel variant fewer to build)
+    if (sizeof(TE) < 4 && a.stream_rows)
+        hipLaunchKernelGGL((xattn_partial_kernel<D, TE, NQ, kCrossWaves, NP, (sizeof(TE) < 4)>), grid,
+                           dim3(kCrossWaves * 64), 0, st, a.q,
+                           static_cast<const TE*>(a.K), static_cast<const TE*>(a.V), a.out,
+                           a.part, a.stats, a.nq, a.max_q, a.H, a.T, a.nsplit, a.chunk,
+                           a.scale * kLog2e);
+    else
+        hipLaunchKernelGGL((xattn_partial_kernel<D, TE, NQ, kCrossWaves, NP, false>), grid,
+                           dim3(kCrossWaves * 64), 0, st, a.q,
+                           static_cast<const TE*>(a.K), static_cast<const TE*>(a.V), a.out,
+                           a.part, a.stats, a.nq, a.max_q, a.H, a.T, a.nsplit, a.chunk,
+                           a.scale * kLog2e);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || a.nsplit == 1) return e;
+    const int G = (a.nsplit + kMergeBatch - 1) / kMergeBatch;
+    const int pairs = a.nq * D * G;
+    const int threads = pairs >= 1024 ? 1024 : ((pairs + 63) / 64) * 64;
+    const size_t lds = (size_t)3 * pairs * sizeof(float);
+    hipLaunchKernelGGL((xattn_merge_kernel<D>), dim3(a.H, a.B), dim3(threads), lds, st, a.part,
+                       a.out, a.stats, a.nq, a.max_q, a.H, a.nsplit);
+    return hipGetLastError();
+}
+
+template <int D, typename TE>
+hipError_t launch_cross_d(const XattnLaunch& a, hipStream_t st) {
+    switch (a.nq) {
+        case 1: return launch_cross_nq<D, TE, 1>(a, st);
+        case 2: return launch_cross_nq<D, TE, 2>(a, st);
+        case 3: return launch_cross_nq<D, TE, 3>(a, st);
+        case 4: return launch_cross_nq<D, TE, 4>(a, st);
+        case 5: return launch_cross_nq<D, TE, 5>(a, st);
+    }
+    return launch_cross_nq<D, TE, 8>(a, st);
+}
+
+template <typename TE>
+hipError_t launch_cross_t(const XattnLaunch& a, hipStream_t st) {
+    switch (a.D) {
+        case 32: return launch_cross_d<32, TE>(a, st);
+        case 64: return launch_cross_d<64, TE>(a, st);
+        case 128: return launch_cross_d<128, TE>(a, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <int D, typename TE, int NW>
+hipError_t launch_self_nw(const SelfLaunch& a, hipStream_t st) {
+    dim3 grid(a.H, a.S);
+    hipLaunchKernelGGL((selfattn_append_kernel<D, TE, NW, kSelfNP>), grid, dim3(NW * 64), 0, st,
+                       a.q, a.k_new, a.v_new, static_cast<TE*>(a.K), static_cast<TE*>(a.V), a.out,
+                       a.H, a.max_pos, a.pos, a.scale * kLog2e);
+    return hipGetLastError();
+}
+
+// Waves per workgroup grow with the rows attended (pos + 1): each wave gets
+// at least one full load tile, so short caches skip the cross-wave merge.
+template <int D, typename TE>
+hipError_t launch_self_d(const SelfLaunch& a, hipStream_t st) {
+    constexpr int rows_per_tile = RowMap<D, TE>::kKPW * kSelfNP;
+    const int tiles = (a.pos + 1 + rows_per_tile - 1) / rows_per_tile;
+    if (tiles <= 1 || kSelfWaves == 1) return launch_self_nw<D, TE, 1>(a, st);
+    if (tiles <= 2 || kSelfWaves == 2) return launch_self_nw<D, TE, 2>(a, st);
+    if (tiles <= 4 || kSelfWaves == 4) return launch_self_nw<D, TE, 4>(a, st);
+    return launch_self_nw<D, TE, kSelfWaves>(a, st);
+}
+
+template <typename TE>
+hipError_t launch_self_t(const SelfLaunch& a, hipStream_t st) {
+    switch (a.D) {
+        case 32: return launch_self_d<32, TE>(a, st);
+        case 64: return launch_self_d<64, TE>(a, st);
+        case 128: return launch_self_d<128, TE>(a, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+constexpr int kPrefillQB = 8;   // tokens of one head sharing a wave's row reads
+constexpr int kPrefillNP = 2;
+
+template <int D, typename TE, int NW, int QB>
+hipError_t launch_prefill_nw(const PrefillLaunch& a, hipStream_t st) {
+    hipLaunchKernelGGL((selfattn_prefill_kernel<D, TE, NW, QB == 1 ? kSelfNP : kPrefillNP, QB>),
+                       dim3(a.Hkv, a.S), dim3(NW * 64), 0,
+                       st, a.q, a.k_new, a.v_new, static_cast<TE*>(a.K), static_cast<TE*>(a.V), a.out,
+                       a.Hkv, a.Hq, a.max_pos, a.pos, a.n_new, a.scale * kLog2e);
+    return hipGetLastError();
+}
+
+// A kv head with at most 8 queries gives each query a wave of its own
+// (short, latency-bound calls such as a few prefix rows); with more, each
+// wave takes kPrefillQB tokens of one head and reads their rows once. Up to
+// 8 waves per workgroup.
+template <int D, typename TE>
+hipError_t launch_prefill_d(const PrefillLaunch& a, hipStream_t st) {
+    const long long G = a.Hq / a.Hkv;
+    if ((long long)a.n_new * G <= 8) {
+        const long long queries = (long long)a.n_new * G;
+        if (queries <= 1) return launch_prefill_nw<D, TE, 1, 1>(a, st);
+        if (queries <= 2) return launch_prefill_nw<D, TE, 2, 1>(a, st);
+        if (queries <= 4) return launch_prefill_nw<D, TE, 4, 1>(a, st);
+        return launch_prefill_nw<D, TE, 8, 1>(a, st);
+    }
+    const long long groups = (long long)((a.n_new + kPrefillQB - 1) / kPrefillQB) * G;
+    if (groups <= 1) return launch_prefill_nw<D, TE, 1, kPrefillQB>(a, st);
+    if (groups <= 2) return launch_prefill_nw<D, TE, 2, kPrefillQB>(a, st);
+    if (groups <= 4) return launch_prefill_nw<D, TE, 4, kPrefillQB>(a, st);
+    return launch_prefill_nw<D, TE, 8, kPrefillQB>(a, st);
+}
+
+template <typename TE>
+hipError_t launch_prefill_t(const PrefillLaunch& a, hipStream_t st) {
+    switch (a.D) {
+        case 32: return launch_prefill_d<32, TE>(a, st);
+        case 64: return launch_prefill_d<64, TE>(a, st);
+        case 128: return launch_prefill_d<128, TE>(a, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+// One workgroup of 4 waves per 4*KPW memory rows of one stream.
+template <int D, typename TE>
+hipError_t launch_weights_d(const WeightsLaunch& a, hipStream_t st) {
+    constexpr int rows = 4 * RowMap<D, TE>::kKPW;
+    hipLaunchKernelGGL((xattn_weights_kernel<D, TE>), dim3((a.T + rows - 1) / rows, a.B), dim3(256),
+                       0, st, a.q, static_cast<const TE*>(a.K), a.stats, a.weights, a.heads, a.H,
+                       a.T, a.nq, a.max_q, a.scale * kLog2e);
+    return hipGetLastError();
+}
+
+template <typename TE>
+hipError_t launch_weights_t(const WeightsLaunch& a, hipStream_t st) {
+    switch (a.D) {
+        case 32: return launch_weights_d<32, TE>(a, st);
+        case 64: return launch_weights_d<64, TE>(a, st);
+        case 128: return launch_weights_d<128, TE>(a, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+// Per-type entry points, defined in attn_f32.hip, attn_bf16.hip, attn_fp8.hip.
+hipError_t launch_cross_f32(const XattnLaunch& a, hipStream_t st);
+hipError_t launch_weights_f32(const WeightsLaunch& a, hipStream_t st);
+hipError_t launch_cross_bf16(const XattnLaunch& a, hipStream_t st);
+hipError_t launch_weights_bf16(const WeightsLaunch& a, hipStream_t st);
+hipError_t launch_cross_fp8(const XattnLaunch& a, hipStream_t st);
+hipError_t launch_weights_fp8(const WeightsLaunch& a, hipStream_t st);
+hipError_t launch_self_f32(const SelfLaunch& a, hipStream_t st);
+hipError_t launch_prefill_f32(const PrefillLaunch& a, hipStream_t st);
+hipError_t launch_self_bf16(const SelfLaunch& a, hipStream_t st);
+hipError_t launch_prefill_bf16(const PrefillLaunch& a, hipStream_t st);
+
+}  // namespace cke
