@@ -133,6 +133,31 @@ int cke_xattn_populate(cke_xattn_cache* c, const void* E, int e_dtype,
                        const void* const* WK, const void* const* WV,
                        int w_dtype, void* stream);
 
+/* cke_xattn_populate with caller workspace for the fp32 path: E and every
+ * weight are split once into bf16 planes hi = bf16(x), lo = bf16(x - hi)
+ * (nearest-even; hi + lo is within 2^-17 |x| of x) in ws, E as is and each
+ * weight transposed, and the projections run as three bf16 products
+ * lo.hi + hi.lo + hi.hi per k step with fp32 accumulation (each product
+ * within 2^-16 of its fp32 value), reading the planes instead of splitting
+ * every tile as it is loaded. The result is the same projection as
+ * cke_xattn_populate (same page and section: K_l = E x WK_l, V_l = E x WV_l,
+ * stored layer-major, head-major).
+ *   ws, ws_bytes  device, 256-byte aligned, at least
+ *                 cke_xattn_populate_workspace_bytes(g, e_dtype, w_dtype)
+ *                 bytes; contents need no initialisation and are dead after
+ *                 the call (the caller may reuse them once it is ordered
+ *                 after the call on its stream)
+ * The workspace applies to fp32 inputs and cache with n_heads*head_dim a
+ * multiple of 128 and d_model a multiple of 64; for any other combination
+ * cke_xattn_populate_workspace_bytes returns 0 and this call is
+ * cke_xattn_populate (ws may then be NULL). Errors as cke_xattn_populate,
+ * plus CKE_EINVAL for a NULL, misaligned or too small workspace. */
+size_t cke_xattn_populate_workspace_bytes(const cke_xattn_geom* g, int e_dtype,
+                                          int w_dtype);
+int cke_xattn_populate_ws(cke_xattn_cache* c, const void* E, int e_dtype,
+                          const void* const* WK, const void* const* WV,
+                          int w_dtype, void* ws, size_t ws_bytes, void* stream);
+
 /* Cross-attention decode at one layer:
  *   out[b][i][h][:] = sum_t softmax_t(scale * q[b][i][h].K_l[b][h][t]) V_l[b][h][t]
  * over all T rows (no mask).
@@ -287,6 +312,21 @@ int cke_decoder_layer_step_noalloc(float* x, const cke_decoder_layer* w,
  * CKE_EINVAL for NULL or misaligned pointers and unsupported sizes. */
 int cke_memory_lift_gelu(const float* x, int rows, int k_in, const float* w, int n,
                          const float* pos, int pos_rows, float* out, void* stream);
+
+/* cke_memory_lift_gelu with caller workspace: x and w are split once into
+ * bf16 hi/lo planes in ws (w transposed) and the product runs as three bf16
+ * products over them, as cke_xattn_populate_ws does (same page and section
+ * as cke_memory_lift_gelu; same result within the same bound).
+ *   ws, ws_bytes  device, 256-byte aligned, at least
+ *                 cke_memory_lift_workspace_bytes(rows, k_in, n) bytes
+ * Applies when k_in is a multiple of 64 and n of 128; otherwise the
+ * workspace size is 0 and this call is cke_memory_lift_gelu (ws may be
+ * NULL). Errors as cke_memory_lift_gelu, plus CKE_EINVAL for a NULL,
+ * misaligned or too small workspace. */
+size_t cke_memory_lift_workspace_bytes(int rows, int k_in, int n);
+int cke_memory_lift_gelu_ws(const float* x, int rows, int k_in, const float* w, int n,
+                            const float* pos, int pos_rows, float* out, void* ws,
+                            size_t ws_bytes, void* stream);
 
 /* Message for the last non-OK status returned on this thread. */
 const char* cke_last_error(void);

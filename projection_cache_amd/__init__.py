@@ -79,6 +79,15 @@ _lib.cke_xattn_is_ready.restype = _I
 _lib.cke_xattn_is_ready.argtypes = [_P]
 _lib.cke_xattn_populate.restype = _I
 _lib.cke_xattn_populate.argtypes = [_P, _P, _I, ctypes.POINTER(_P), ctypes.POINTER(_P), _I, _P]
+_lib.cke_xattn_populate_workspace_bytes.restype = _SZ
+_lib.cke_xattn_populate_workspace_bytes.argtypes = [ctypes.POINTER(cke_xattn_geom), _I, _I]
+_lib.cke_xattn_populate_ws.restype = _I
+_lib.cke_xattn_populate_ws.argtypes = [_P, _P, _I, ctypes.POINTER(_P), ctypes.POINTER(_P), _I, _P,
+                                       _SZ, _P]
+_lib.cke_memory_lift_workspace_bytes.restype = _SZ
+_lib.cke_memory_lift_workspace_bytes.argtypes = [_I, _I, _I]
+_lib.cke_memory_lift_gelu_ws.restype = _I
+_lib.cke_memory_lift_gelu_ws.argtypes = [_P, _I, _I, _P, _I, _P, _I, _P, _P, _SZ, _P]
 _lib.cke_xattn_decode.restype = _I
 _lib.cke_xattn_decode.argtypes = [_P, _I, _P, _I, _F, _P, _P]
 _lib.cke_selfattn_decode_append.restype = _I
@@ -106,7 +115,9 @@ _lib.cke_memory_lift_gelu.argtypes = [_P, _I, _I, _P, _I, _P, _I, _P, _P]
 EXPORTED = ["cke_xattn_region_bytes", "cke_xattn_layer_offset_bytes",
             "cke_xattn_workspace_bytes", "cke_xattn_num_splits", "cke_xattn_cache_create",
             "cke_xattn_cache_destroy", "cke_xattn_invalidate", "cke_xattn_is_ready",
-            "cke_xattn_populate", "cke_xattn_decode", "cke_selfattn_decode_append",
+            "cke_xattn_populate", "cke_xattn_populate_workspace_bytes", "cke_xattn_populate_ws",
+            "cke_memory_lift_workspace_bytes", "cke_memory_lift_gelu_ws",
+            "cke_xattn_decode", "cke_selfattn_decode_append",
             "cke_selfattn_prefill_append", "cke_xattn_decode_weights",
             "cke_decoder_step_workspace_bytes", "cke_decoder_layer_step",
             "cke_decoder_step_scratch_bytes", "cke_decoder_layer_step_noalloc",
@@ -246,10 +257,27 @@ def _geom(cache) -> cke_xattn_geom:
     return cache.geom
 
 
-def cke_xattn_populate(cache, E, WK, WV, stream=None, e_dtype=None, w_dtype=None) -> None:
+def cke_xattn_populate_workspace_bytes(g: cke_xattn_geom, e_dtype=CKE_F32, w_dtype=CKE_F32) -> int:
+    return int(_lib.cke_xattn_populate_workspace_bytes(ctypes.byref(g), int(e_dtype), int(w_dtype)))
+
+
+def cke_memory_lift_workspace_bytes(rows: int, k_in: int, n: int) -> int:
+    return int(_lib.cke_memory_lift_workspace_bytes(int(rows), int(k_in), int(n)))
+
+
+def _ws(ws):
+    """(address, bytes) of an optional workspace tensor."""
+    if ws is None:
+        return None, 0
+    return _dev("ws", ws), ws.numel() * ws.element_size()
+
+
+def cke_xattn_populate(cache, E, WK, WV, stream=None, e_dtype=None, w_dtype=None, ws=None) -> None:
     """Prefill every layer's K/V slab from encoder memory E [B][T][d_model];
     WK and WV are sequences of L weight tensors [d_model][H*D], one per layer
-    of the cache (an XattnCache)."""
+    of the cache (an XattnCache). With `ws` (a device tensor of at least
+    cke_xattn_populate_workspace_bytes bytes) the fp32 path splits its
+    operands once into bf16 planes there (cke_xattn_populate_ws)."""
     g = _geom(cache)
     if len(WK) != g.n_layers or len(WV) != g.n_layers:
         raise ValueError("WK and WV must hold one weight per layer: %d each (got %d and %d)"
@@ -266,8 +294,13 @@ def cke_xattn_populate(cache, E, WK, WV, stream=None, e_dtype=None, w_dtype=None
     arr = _P * g.n_layers
     wk = arr(*ptrs[1:1 + g.n_layers])
     wv = arr(*ptrs[1 + g.n_layers:])
-    _check(_lib.cke_xattn_populate(_handle(cache), e_ptr, e_dtype, wk, wv, w_dtype,
-                                   _stream(stream)))
+    if ws is None:
+        _check(_lib.cke_xattn_populate(_handle(cache), e_ptr, e_dtype, wk, wv, w_dtype,
+                                       _stream(stream)))
+    else:
+        ws_ptr, ws_bytes = _ws(ws)
+        _check(_lib.cke_xattn_populate_ws(_handle(cache), e_ptr, e_dtype, wk, wv, w_dtype, ws_ptr,
+                                          ws_bytes, _stream(stream)))
 
 
 def _qshape(g, q):
@@ -401,11 +434,13 @@ def cke_decoder_layer_step_noalloc(x, w, kv, pos: int, cache, layer: int, scale:
                                                _stream(stream)))
 
 
-def cke_memory_lift_gelu(x, w, out, pos=None, stream=None) -> None:
+def cke_memory_lift_gelu(x, w, out, pos=None, stream=None, ws=None) -> None:
     """out [rows][n] = gelu(x [rows][k_in] . w [k_in][n]) + pos[r % pos_rows]
     (exact GELU; pos [pos_rows][n] or None), all fp32 device tensors (out may
     be any contiguous view of rows x n elements, such as an encoder memory
-    [B][T][n])."""
+    [B][T][n]). With `ws` (at least cke_memory_lift_workspace_bytes bytes)
+    the operands are split once into bf16 planes there
+    (cke_memory_lift_gelu_ws)."""
     if not isinstance(x, torch.Tensor) or x.dim() != 2 or w.dim() != 2:
         raise ValueError("x and w must be 2-d tensors [rows][k_in] and [k_in][n]")
     rows, k_in = x.shape
@@ -422,8 +457,14 @@ def cke_memory_lift_gelu(x, w, out, pos=None, stream=None) -> None:
     ptrs = _devs(*specs)
     x_ptr, w_ptr, out_ptr = ptrs[:3]
     pos_ptr = ptrs[3] if pos is not None else None
-    _check(_lib.cke_memory_lift_gelu(x_ptr, int(rows), int(k_in), w_ptr, int(n), pos_ptr,
-                                     int(pos_rows), out_ptr, _stream(stream)))
+    if ws is None:
+        _check(_lib.cke_memory_lift_gelu(x_ptr, int(rows), int(k_in), w_ptr, int(n), pos_ptr,
+                                         int(pos_rows), out_ptr, _stream(stream)))
+    else:
+        ws_ptr, ws_bytes = _ws(ws)
+        _check(_lib.cke_memory_lift_gelu_ws(x_ptr, int(rows), int(k_in), w_ptr, int(n), pos_ptr,
+                                            int(pos_rows), out_ptr, ws_ptr, ws_bytes,
+                                            _stream(stream)))
 
 
 class XattnCache:
@@ -447,8 +488,14 @@ class XattnCache:
         self.handle = cke_xattn_cache_create(self.geom, self.k, self.v, self.ws)
         self.n_splits = cke_xattn_num_splits(self.geom)
 
-    def populate(self, E, WK, WV, stream=None):
-        cke_xattn_populate(self, E, WK, WV, stream)
+    def populate(self, E, WK, WV, stream=None, ws=None):
+        cke_xattn_populate(self, E, WK, WV, stream, ws=ws)
+
+    def populate_workspace(self, device="cuda"):
+        """A device workspace for populate(..., ws=) of fp32 inputs, or None
+        when the geometry takes none."""
+        n = cke_xattn_populate_workspace_bytes(self.geom)
+        return torch.empty((n + 3) // 4, dtype=torch.float32, device=device) if n else None
 
     def decode(self, q, layer, scale, out=None, stream=None):
         if out is None:

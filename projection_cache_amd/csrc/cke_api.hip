@@ -202,8 +202,13 @@ int cke_xattn_invalidate(cke_xattn_cache* c) {
 
 int cke_xattn_is_ready(const cke_xattn_cache* c) { return c ? c->ready : 0; }
 
-int cke_xattn_populate(cke_xattn_cache* c, const void* E, int e_dtype, const void* const* WK,
-                       const void* const* WV, int w_dtype, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Checks shared by the populate calls; fills the launch descriptor.
+int populate_args(const cke_xattn_cache* c, const void* E, int e_dtype, const void* const* WK,
+                  const void* const* WV, int w_dtype, cke::PopulateLaunch* a) {
     if (!c) return fail(CKE_EINVAL, "cache handle is NULL");
     if (!E || !WK || !WV) return fail(CKE_EINVAL, "E, WK and WV must be non-NULL");
     const cke_xattn_geom& g = c->g;
@@ -217,31 +222,76 @@ int cke_xattn_populate(cke_xattn_cache* c, const void* E, int e_dtype, const voi
     if (fp8 && (g.n_heads * g.head_dim) % 256 != 0)
         return fail(CKE_EINVAL, "an fp8 cache needs n_heads * head_dim to be a multiple of 256");
     if (!aligned16(E)) return fail(CKE_EINVAL, "E must be 16-byte aligned");
-    cke::PopulateLaunch a;
-    std::memset(&a, 0, sizeof(a));
+    std::memset(a, 0, sizeof(*a));
     for (int l = 0; l < g.n_layers; ++l) {
         if (!WK[l] || !WV[l]) return fail(CKE_EINVAL, "weight pointer of layer %d is NULL", l);
         if (!aligned16(WK[l]) || !aligned16(WV[l]))
             return fail(CKE_EINVAL, "weights of layer %d must be 16-byte aligned", l);
-        a.wt.w[l] = WK[l];
-        a.wt.w[g.n_layers + l] = WV[l];
+        a->wt.w[l] = WK[l];
+        a->wt.w[g.n_layers + l] = WV[l];
     }
-    a.E = E;
-    a.Kc = c->k;
-    a.Vc = c->v;
-    a.L = g.n_layers;
-    a.B = g.n_streams;
-    a.T = g.mem_len;
-    a.dm = g.d_model;
-    a.H = g.n_heads;
-    a.D = g.head_dim;
-    a.bf16 = bf16 || fp8;
-    a.fp8 = fp8;
+    a->E = E;
+    a->Kc = c->k;
+    a->Vc = c->v;
+    a->L = g.n_layers;
+    a->B = g.n_streams;
+    a->T = g.mem_len;
+    a->dm = g.d_model;
+    a->H = g.n_heads;
+    a->D = g.head_dim;
+    a->bf16 = bf16 || fp8;
+    a->fp8 = fp8;
+    return CKE_OK;
+}
+
+int populate_impl(cke_xattn_cache* c, const void* E, int e_dtype, const void* const* WK,
+                  const void* const* WV, int w_dtype, void* ws, size_t ws_bytes, bool with_ws,
+                  void* stream) {
+    cke::PopulateLaunch a;
+    const int rc = populate_args(c, E, e_dtype, WK, WV, w_dtype, &a);
+    if (rc != CKE_OK) return rc;
+    const size_t need = with_ws ? cke::populate_planes_bytes(a) : 0;
+    if (need) {
+        if (!ws || (reinterpret_cast<uintptr_t>(ws) & (kAlign - 1)) != 0)
+            return fail(CKE_EINVAL, "workspace must be non-NULL and 256-byte aligned");
+        if (ws_bytes < need)
+            return fail(CKE_EINVAL, "workspace holds %zu bytes; populate needs %zu", ws_bytes, need);
+    }
     c->ready = 0;
-    hipError_t e = cke::launch_populate(a, static_cast<hipStream_t>(stream));
+    hipError_t e = need ? cke::launch_populate_planes(a, ws, static_cast<hipStream_t>(stream))
+                        : cke::launch_populate(a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(CKE_EDEVICE, "populate launch failed: %s", hipGetErrorString(e));
     c->ready = 1;
     return CKE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int cke_xattn_populate(cke_xattn_cache* c, const void* E, int e_dtype, const void* const* WK,
+                       const void* const* WV, int w_dtype, void* stream) {
+    return populate_impl(c, E, e_dtype, WK, WV, w_dtype, nullptr, 0, false, stream);
+}
+
+size_t cke_xattn_populate_workspace_bytes(const cke_xattn_geom* g, int e_dtype, int w_dtype) {
+    if (check_geom(g) != CKE_OK) return 0;
+    if (e_dtype != CKE_F32 || w_dtype != CKE_F32 || g->cache_dtype != CKE_F32) return 0;
+    cke::PopulateLaunch a;
+    std::memset(&a, 0, sizeof(a));
+    a.L = g->n_layers;
+    a.B = g->n_streams;
+    a.T = g->mem_len;
+    a.dm = g->d_model;
+    a.H = g->n_heads;
+    a.D = g->head_dim;
+    return cke::populate_planes_bytes(a);
+}
+
+int cke_xattn_populate_ws(cke_xattn_cache* c, const void* E, int e_dtype, const void* const* WK,
+                          const void* const* WV, int w_dtype, void* ws, size_t ws_bytes,
+                          void* stream) {
+    return populate_impl(c, E, e_dtype, WK, WV, w_dtype, ws, ws_bytes, true, stream);
 }
 
 }  // extern "C"
@@ -626,8 +676,12 @@ int cke_decoder_layer_step_noalloc(float* x, const cke_decoder_layer* w, const c
 
 extern "C" {
 
-int cke_memory_lift_gelu(const float* x, int rows, int k_in, const float* w, int n,
-                         const float* pos, int pos_rows, float* out, void* stream) {
+}  // extern "C"
+
+namespace {
+
+int lift_args(const float* x, int rows, int k_in, const float* w, int n, const float* pos,
+              int pos_rows, float* out, cke::LiftLaunch* a) {
     if (!x || !w || !out) return fail(CKE_EINVAL, "x, w and out must be non-NULL");
     if (!aligned16(x) || !aligned16(w) || !aligned16(out) || (pos && !aligned16(pos)))
         return fail(CKE_EINVAL, "x, w, pos and out must be 16-byte aligned");
@@ -638,16 +692,57 @@ int cke_memory_lift_gelu(const float* x, int rows, int k_in, const float* w, int
     if ((long long)rows * k_in > (1ll << 31) - 1 || (long long)rows * n > (1ll << 31) - 1)
         return fail(CKE_EINVAL, "rows x k_in or rows x n too large");
     if (pos && pos_rows < 1) return fail(CKE_EINVAL, "pos_rows must be >= 1 when pos is given");
+    a->x = x;
+    a->w = w;
+    a->pos = pos;
+    a->out = out;
+    a->rows = rows;
+    a->k_in = k_in;
+    a->n = n;
+    a->pos_rows = pos ? pos_rows : 1;
+    return CKE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int cke_memory_lift_gelu(const float* x, int rows, int k_in, const float* w, int n,
+                         const float* pos, int pos_rows, float* out, void* stream) {
     cke::LiftLaunch a;
-    a.x = x;
-    a.w = w;
-    a.pos = pos;
-    a.out = out;
+    const int rc = lift_args(x, rows, k_in, w, n, pos, pos_rows, out, &a);
+    if (rc != CKE_OK) return rc;
+    hipError_t e = cke::launch_lift(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(CKE_EDEVICE, "memory lift launch failed: %s", hipGetErrorString(e));
+    return CKE_OK;
+}
+
+size_t cke_memory_lift_workspace_bytes(int rows, int k_in, int n) {
+    if (rows < 1 || k_in < 1 || n < 1 || k_in % 32 != 0 || n % 64 != 0) return 0;
+    if ((long long)rows * k_in > (1ll << 31) - 1 || (long long)rows * n > (1ll << 31) - 1) return 0;
+    cke::LiftLaunch a;
+    std::memset(&a, 0, sizeof(a));
     a.rows = rows;
     a.k_in = k_in;
     a.n = n;
-    a.pos_rows = pos ? pos_rows : 1;
-    hipError_t e = cke::launch_lift(a, static_cast<hipStream_t>(stream));
+    return cke::lift_planes_bytes(a);
+}
+
+int cke_memory_lift_gelu_ws(const float* x, int rows, int k_in, const float* w, int n,
+                            const float* pos, int pos_rows, float* out, void* ws, size_t ws_bytes,
+                            void* stream) {
+    cke::LiftLaunch a;
+    const int rc = lift_args(x, rows, k_in, w, n, pos, pos_rows, out, &a);
+    if (rc != CKE_OK) return rc;
+    const size_t need = cke::lift_planes_bytes(a);
+    if (need) {
+        if (!ws || (reinterpret_cast<uintptr_t>(ws) & (kAlign - 1)) != 0)
+            return fail(CKE_EINVAL, "workspace must be non-NULL and 256-byte aligned");
+        if (ws_bytes < need)
+            return fail(CKE_EINVAL, "workspace holds %zu bytes; the lift needs %zu", ws_bytes, need);
+    }
+    hipError_t e = need ? cke::launch_lift_planes(a, ws, static_cast<hipStream_t>(stream))
+                        : cke::launch_lift(a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(CKE_EDEVICE, "memory lift launch failed: %s", hipGetErrorString(e));
     return CKE_OK;
 }

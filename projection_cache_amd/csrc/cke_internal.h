@@ -123,4 +123,13 @@ struct LiftLaunch {
 };
 hipError_t launch_lift(const LiftLaunch& a, hipStream_t st);
 
+// fp32 products as three bf16 products over operands split once into bf16
+// hi/lo planes in caller workspace (a prologue), for widths the planes kernel
+// takes (K a multiple of 64, output columns per weight of 128); 0 bytes means
+// the shape does not use planes.
+size_t populate_planes_bytes(const PopulateLaunch& a);
+size_t lift_planes_bytes(const LiftLaunch& a);
+hipError_t launch_populate_planes(const PopulateLaunch& a, void* ws, hipStream_t st);
+hipError_t launch_lift_planes(const LiftLaunch& a, void* ws, hipStream_t st);
+
 }  // namespace cke

@@ -545,14 +545,23 @@ __global__ __launch_bounds__(WGM * WGN * 64) void populate_f32x3_kernel(GemmArgs
                 bh[nb] = *reinterpret_cast<const bf16x8*>(&Bh[buf][off]);
                 bl[nb] = *reinterpret_cast<const bf16x8*>(&Bl[buf][off]);
             }
+            // one pass over the blocks per product term: consecutive MFMAs
+            // write different accumulators (see populate_planes_x3_kernel)
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-                for (int nb = 0; nb < NB; ++nb) {
+                for (int nb = 0; nb < NB; ++nb)
                     acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[mb], bh[nb], acc[mb][nb], 0, 0, 0);
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
                     acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[mb], bl[nb], acc[mb][nb], 0, 0, 0);
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
                     acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[mb], bh[nb], acc[mb][nb], 0, 0, 0);
-                }
         }
         if (kt + 1 < nk) store_tiles(buf ^ 1);
         __syncthreads();
@@ -868,7 +877,10 @@ __global__ __launch_bounds__(256) void populate_bf16_w4_kernel(GemmArgs a, int n
     using F = FragsT<BM, BN, WGM, WGN>;
     constexpr int LD_PER_SLOT = T::A_LD + T::B_LD;
     static_assert(NSLOT >= 3 && (NSLOT - 2) * LD_PER_SLOT <= 63, "ring depth");
-    constexpr int GROUP_M = 8;
+#ifndef CKE_POP_GROUP_M
+#define CKE_POP_GROUP_M 8
+#endif
+    constexpr int GROUP_M = CKE_POP_GROUP_M;
     __shared__ __attribute__((aligned(1024))) StreamSlot<BM, BN> ring[NSLOT];
 
     const int ntiles = num_m * num_n;
@@ -952,6 +964,307 @@ __global__ __launch_bounds__(256) void populate_bf16_w4_kernel(GemmArgs a, int n
     else
         epilogue_t_lds<BM, BN, WGM, WGN>(a, acc, m0, p, col0, wm, wn, lane,
                                          reinterpret_cast<uint16_t*>(&ring[0]));
+}
+
+// ------------------------------------------------- fp32 from split planes
+// fp32 products as three bf16 products, with every operand split ONCE into
+// bf16 planes hi = bf16(x), lo = bf16(x - hi) (both nearest-even) by a
+// prologue into caller workspace, instead of once per tile load: Whisper
+// Base's E is read by 24 column tiles and each weight by 12 row tiles, and
+// the per-tile split made the fp32 kernel bound by its vector work.
+//
+// Planes: E (or a lift input x) keeps its layout, [M][K] in both planes;
+// each weight W [K][N] is split and transposed to [N][K], so that both
+// operands of the product are rows with k contiguous and one loader serves
+// both.
+
+// hi/lo planes of n8 groups of 8 consecutive floats (layout kept).
+__global__ __launch_bounds__(256) void split_rows_kernel(const float* __restrict__ x, size_t n8,
+                                                         uint16_t* __restrict__ hi,
+                                                         uint16_t* __restrict__ lo)
+{
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n8; i += (size_t)gridDim.x * 256) {
+        const float4 a = reinterpret_cast<const float4*>(x)[2 * i];
+        const float4 b = reinterpret_cast<const float4*>(x)[2 * i + 1];
+        const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+        uint32_t h[4], l[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const __bf16 h0 = (__bf16)v[2 * j], h1 = (__bf16)v[2 * j + 1];
+            const __bf16 l0 = (__bf16)(v[2 * j] - (float)h0), l1 = (__bf16)(v[2 * j + 1] - (float)h1);
+            h[j] = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+            l[j] = (uint32_t)__builtin_bit_cast(uint16_t, l0) | ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
+        }
+        reinterpret_cast<uint4*>(hi)[i] = make_uint4(h[0], h[1], h[2], h[3]);
+        reinterpret_cast<uint4*>(lo)[i] = make_uint4(l[0], l[1], l[2], l[3]);
+    }
+}
+
+// Weight j of the table, W [K][N] fp32, to planes [N][K]: hi at
+// planes + j*2*N*K, lo N*K elements after it. Grid (N/64, K/64, matrices);
+// a 64 x 64 block goes through LDS as packed (hi | lo << 16) words, padded
+// rows (65 words) so both the transposed writes and the row reads spread
+// over the banks. (A k-blocked layout, a k-tile of consecutive rows in one
+// contiguous run, made the product 3x slower: all tiles then read the same
+// narrow address window at once.)
+__global__ __launch_bounds__(256) void split_transpose_kernel(WeightTable wt, int K, int N,
+                                                              uint16_t* __restrict__ planes)
+{
+    __shared__ uint32_t sh[64 * 65];
+    const float* __restrict__ W = static_cast<const float*>(wt.w[blockIdx.z]);
+    uint16_t* __restrict__ Wh = planes + (size_t)blockIdx.z * 2 * N * K;
+    uint16_t* __restrict__ Wl = Wh + (size_t)N * K;
+    const int n0 = blockIdx.x * 64, k0 = blockIdx.y * 64;
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int idx = tid + i * 256;
+        const int k = idx >> 4, c4 = (idx & 15) * 4;
+        const float4 v = *reinterpret_cast<const float4*>(W + (size_t)(k0 + k) * N + n0 + c4);
+        const float f[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const __bf16 h = (__bf16)f[j];
+            const __bf16 l = (__bf16)(f[j] - (float)h);
+            sh[(c4 + j) * 65 + k] = (uint32_t)__builtin_bit_cast(uint16_t, h) |
+                                    ((uint32_t)__builtin_bit_cast(uint16_t, l) << 16);
+        }
+    }
+    __syncthreads();
+    const int n = tid >> 2, kc = (tid & 3) * 16;
+    uint32_t h[8], l[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const uint32_t w0 = sh[n * 65 + kc + 2 * j], w1 = sh[n * 65 + kc + 2 * j + 1];
+        h[j] = (w0 & 0xffffu) | (w1 << 16);
+        l[j] = (w0 >> 16) | (w1 & 0xffff0000u);
+    }
+    uint4* dh = reinterpret_cast<uint4*>(Wh + (size_t)(n0 + n) * K + k0 + kc);
+    uint4* dl = reinterpret_cast<uint4*>(Wl + (size_t)(n0 + n) * K + k0 + kc);
+    dh[0] = make_uint4(h[0], h[1], h[2], h[3]);
+    dh[1] = make_uint4(h[4], h[5], h[6], h[7]);
+    dl[0] = make_uint4(l[0], l[1], l[2], l[3]);
+    dl[1] = make_uint4(l[4], l[5], l[6], l[7]);
+}
+
+// One ring slot of the planes product: the hi and lo planes of the E tile
+// (BM rows) and of the transposed W tile (BN rows), each row BK k values.
+// BK = 32: four 16-byte pieces per row, piece p of row r stored at position
+// p ^ ((r >> 2) & 3) so that a fragment read of 32 rows spreads over the
+// banks. BK = 16: two pieces per row, swapped in rows with bit 3 set (rows r
+// and r + 8 of a fragment read would otherwise hit the same banks: counters
+// showed four conflict cycles per read).
+template <int BM, int BN, int BK>
+struct PlaneSlot {
+    uint16_t ah[BM * BK];
+    uint16_t al[BM * BK];
+    uint16_t bh[BN * BK];
+    uint16_t bl[BN * BK];
+};
+
+template <int BK>
+__device__ __forceinline__ int plane_pos(int row, int piece) {
+    if constexpr (BK == 32) return piece ^ ((row >> 2) & 3);
+    else return piece ^ ((row >> 3) & 1);
+}
+
+// Grid: one workgroup of 4 waves (2 x 2) per BM x BN output tile, tiles in
+// the grouped, XCD-ordered sequence of the other populate kernels. Operands
+// move global -> LDS with global_load_lds_dwordx4 into a ring of NSLOT slots
+// (NSLOT-2 k-tiles in flight while one is multiplied; one barrier per
+// k-tile), as in populate_bf16_w4_kernel. Each 16-deep k step multiplies
+// lo.hi + hi.lo + hi.hi into fp32 accumulators (small terms first); the
+// accumulators are in the layout of epilogue (head-major fp32 stores) and
+// epilogue_lift (token-major GELU + positions).
+//   Ep: E planes, hi then lo, each [M][K]; Wp: per column block j = n / HD
+//   (n / N for the lift), hi and lo planes [HD][K] at Wp + j*2*HD*K.
+// 128 x 128 tiles (64 x 64 per wave) suit outputs with few columns; 192 x
+// 256 tiles (96 x 128 per wave) stream 40% fewer operand bytes per product
+// and cover 1500 memory rows with eight row tiles.
+template <int BM, int BN, int BK, int NSLOT, bool LIFT>
+__global__ __launch_bounds__(256) void populate_planes_x3_kernel(GemmArgs a, const uint16_t* __restrict__ Ep,
+                                                                 const uint16_t* __restrict__ Wp, int K,
+                                                                 int num_m, int num_n)
+{
+    constexpr int WGM = 2, WGN = 2;
+    constexpr int WTM = BM / WGM, WTN = BN / WGN, MB = WTM / 32, NB = WTN / 32;
+    constexpr int PPR = BK / 8;                                  // 16-byte pieces per row
+    constexpr int A_BLK = BM * PPR / 64, B_BLK = BN * PPR / 64;   // 64-piece blocks per plane
+    constexpr int LPT = (2 * A_BLK + 2 * B_BLK) / 4;              // loads per thread per slot
+    constexpr int LD_PER_SLOT = LPT;
+    static_assert((BM * PPR) % 64 == 0 && (BN * PPR) % 64 == 0 && (2 * A_BLK + 2 * B_BLK) % 4 == 0,
+                  "pieces per slot");
+    static_assert(BK == 16 || BK == 32, "k-tile depth");
+    static_assert(NSLOT >= 3 && (NSLOT - 2) * LD_PER_SLOT <= 63 && NSLOT - 2 <= 3, "ring depth");
+    constexpr int GROUP_M = 8;
+    __shared__ __attribute__((aligned(1024))) PlaneSlot<BM, BN, BK> ring[NSLOT];
+
+    const int ntiles = num_m * num_n;
+    const int per_xcd = (ntiles + 7) / 8;
+    const int tile = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+    if (tile >= ntiles) return;
+    const int group = tile / (GROUP_M * num_n);
+    const int first_m = group * GROUP_M;
+    const int gsize = min(num_m - first_m, GROUP_M);
+    const int pid_m = first_m + (tile % (GROUP_M * num_n)) % gsize;
+    const int pid_n = (tile % (GROUP_M * num_n)) / gsize;
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wave / WGN, wn = wave % WGN;
+    const int HD = a.H * a.D;
+    const int m0 = pid_m * BM;
+    const int n0 = pid_n * BN;
+    const int p = n0 / HD;
+    const int col0 = n0 - p * HD;
+    const size_t MK = (size_t)a.M * K;
+    const uint16_t* __restrict__ Eh = Ep;
+    const uint16_t* __restrict__ El = Ep + MK;
+    const uint16_t* __restrict__ Wh = Wp + (size_t)p * 2 * HD * K + (size_t)col0 * K;
+    const uint16_t* __restrict__ Wl = Wh + (size_t)HD * K;
+
+    // The slot's 16-byte pieces form one list, plane by plane (E hi, E lo,
+    // W hi, W lo), dealt to the waves in blocks of 64 (one dma16 each), so
+    // every thread issues LPT loads whatever the split between the planes.
+    auto issue = [&](PlaneSlot<BM, BN, BK>& slot, int kt) {
+#pragma unroll
+        for (int j = 0; j < LPT; ++j) {
+            const int blk = wave * LPT + j;                      // wave-uniform
+            const bool on_a = blk < 2 * A_BLK;
+            const int in_plane = on_a ? (blk < A_BLK ? blk : blk - A_BLK)
+                                      : (blk - 2 * A_BLK < B_BLK ? blk - 2 * A_BLK : blk - 2 * A_BLK - B_BLK);
+            const bool lo = on_a ? blk >= A_BLK : blk - 2 * A_BLK >= B_BLK;
+            const int s = in_plane * 64 + lane;
+            const int row = s / PPR;
+            const int piece = plane_pos<BK>(row, s % PPR);
+            const uint16_t* src = on_a ? (lo ? El : Eh) + (size_t)min(m0 + row, a.M - 1) * K
+                                       : (lo ? Wl : Wh) + (size_t)row * K;
+            uint16_t* dst = on_a ? (lo ? slot.al : slot.ah) : (lo ? slot.bl : slot.bh);
+            dma16(src + kt * BK + piece * 8, __builtin_amdgcn_readfirstlane(lds_addr(dst + in_plane * 64 * 8)));
+        }
+    };
+    struct Frags {
+        bf16x8 ah[MB], al[MB], bh[NB], bl[NB];
+    };
+    auto read = [&](const PlaneSlot<BM, BN, BK>& slot, int kk, Frags& f) {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+            const int row = wm * WTM + mb * 32 + (lane & 31);
+            const int piece = plane_pos<BK>(row, (kk >> 3) + (lane >> 5));
+            f.ah[mb] = *reinterpret_cast<const bf16x8*>(slot.ah + row * BK + piece * 8);
+            f.al[mb] = *reinterpret_cast<const bf16x8*>(slot.al + row * BK + piece * 8);
+        }
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            const int row = wn * WTN + nb * 32 + (lane & 31);
+            const int piece = plane_pos<BK>(row, (kk >> 3) + (lane >> 5));
+            f.bh[nb] = *reinterpret_cast<const bf16x8*>(slot.bh + row * BK + piece * 8);
+            f.bl[nb] = *reinterpret_cast<const bf16x8*>(slot.bl + row * BK + piece * 8);
+        }
+    };
+    f32x16 acc[MB][NB];
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+    // Three passes over the blocks, one per product term, so consecutive
+    // MFMAs write different accumulators: three back-to-back products into
+    // one accumulator each wait for the previous result, which left the
+    // matrix pipe idle for most of every k step.
+    auto mma = [&](const Frags& f) {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+                acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.al[mb], f.bh[nb], acc[mb][nb], 0, 0, 0);
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+                acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.ah[mb], f.bl[nb], acc[mb][nb], 0, 0, 0);
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+                acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.ah[mb], f.bh[nb], acc[mb][nb], 0, 0, 0);
+    };
+
+    const int nk = K / BK;
+    // before the wait for k-tile j, k-tiles 0..min(j + NSLOT - 3, nk - 1) have
+    // been issued (0..NSLOT-2 for j = 0): wait until only the later ones are
+    // outstanding, then a barrier makes every thread's loads of j visible
+    auto sync_tile = [&](int j) {
+        const int issued = min(j == 0 ? NSLOT - 2 : j + NSLOT - 3, nk - 1);
+        const int later = issued - j;
+        if (later >= 3)
+            __builtin_amdgcn_s_waitcnt(vmcnt_wait(3 * LD_PER_SLOT));
+        else if (later == 2)
+            __builtin_amdgcn_s_waitcnt(vmcnt_wait(2 * LD_PER_SLOT));
+        else if (later == 1)
+            __builtin_amdgcn_s_waitcnt(vmcnt_wait(LD_PER_SLOT));
+        else
+            __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));
+        __builtin_amdgcn_s_barrier();
+    };
+    for (int t = 0; t < NSLOT - 1 && t < nk; ++t) issue(ring[t], t);
+    sync_tile(0);
+    Frags cur;
+    read(ring[0], 0, cur);
+    int slot = 0;
+    if constexpr (BK == 32) {
+        Frags nxt;
+        for (int s = 0; s + 1 < nk; ++s) {   // last k-tile peeled: no join before its MFMAs
+            read(ring[slot], 16, nxt);
+            mma(cur);
+            const int next_slot = slot + 1 == NSLOT ? 0 : slot + 1;
+            sync_tile(s + 1);
+            const int t = s - 1 + NSLOT;
+            const int fill = slot == 0 ? NSLOT - 1 : slot - 1;
+            if (t < nk) issue(ring[fill], t);
+            read(ring[next_slot], 0, cur);
+            mma(nxt);
+            slot = next_slot;
+        }
+        read(ring[slot], 16, nxt);
+        mma(cur);
+        mma(nxt);
+    } else {
+        // one 16-deep step per k-tile: k-tile s+1 is read right after its
+        // barrier and its reads overlap the products of k-tile s; at that
+        // barrier every wave has consumed k-tile s-1, whose slot is refilled.
+        // Two k-tiles per pass with two fragment buffers that alternate, so
+        // no fragment register is written while products still read it.
+        Frags nxt;
+        auto step = [&](int s, const Frags& have, Frags& next) {
+            const int next_slot = slot + 1 == NSLOT ? 0 : slot + 1;
+            sync_tile(s + 1);
+            const int t = s - 1 + NSLOT;
+            const int fill = slot == 0 ? NSLOT - 1 : slot - 1;
+            if (t < nk) issue(ring[fill], t);
+            read(ring[next_slot], 0, next);
+            mma(have);
+            slot = next_slot;
+        };
+        // one exit from the loop: the accumulators keep their registers
+        int s = 0;
+        while (s + 2 < nk) {
+            step(s, cur, nxt);
+            step(s + 1, nxt, cur);
+            s += 2;
+        }
+        if (nk - s == 2) {
+            step(s, cur, nxt);
+            mma(nxt);
+        } else {
+            mma(cur);
+        }
+    }
+    if constexpr (LIFT)
+        epilogue_lift<BM, BN, WGM, WGN>(a, acc, m0, n0);
+    else
+        epilogue<BM, BN, WGM, WGN, float>(a, acc, m0, p, col0);
 }
 
 // fp32 populate for gfx950 on v_mfma_f32_32x32x2_f32: 64x64 output tiles,
@@ -1262,6 +1575,113 @@ hipError_t launch_lift(const LiftLaunch& a, hipStream_t st) {
     hipLaunchKernelGGL((populate_f32_dma_kernel<3, 32, true>), dim3(grid), dim3(256), 0, st, g, num_m,
                        num_n);
     return hipGetLastError();
+}
+
+namespace {
+
+// Planes workspace: E (or x) hi and lo planes, [M][K] each, then from the
+// next 256-byte boundary n_mat weight plane pairs [N][K].
+size_t planes_w_offset(long long M, int K) { return ((size_t)(2 * M * K * 2) + 255) / 256 * 256; }
+
+size_t planes_bytes(long long M, int K, int n_mat, int N) {
+    return planes_w_offset(M, K) + (size_t)n_mat * 2 * N * K * 2;
+}
+
+bool planes_shape_ok(int K, int N) { return K % 64 == 0 && N % 128 == 0; }
+
+#ifndef CKE_PLANES_MIN_BIG_TILES
+#define CKE_PLANES_MIN_BIG_TILES 128
+#endif
+
+
+// split prologue (E rows, then every weight transposed) and the product
+hipError_t launch_planes(GemmArgs g, int K, int N_per_mat, int n_mat, int n_total, bool lift,
+                         void* ws, hipStream_t st) {
+    uint16_t* Ep = static_cast<uint16_t*>(ws);
+    uint16_t* Wp = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + planes_w_offset(g.M, K));
+    // 192 x 256 tiles stream fewer operand bytes per product, but only pay
+    // while they still give most compute units a tile
+    const long long tiles_big = (long long)((g.M + 191) / 192) * (n_total / 256);
+    const bool big = N_per_mat % 256 == 0 && tiles_big >= CKE_PLANES_MIN_BIG_TILES;
+    const size_t n8 = (size_t)g.M * K / 8;
+    const size_t blocks = (n8 + 255) / 256;
+    const dim3 sgrid((unsigned)(blocks < 4096 ? blocks : 4096));
+    const dim3 tgrid(N_per_mat / 64, K / 64, n_mat);
+    const float* E = static_cast<const float*>(g.E);
+    hipLaunchKernelGGL(split_rows_kernel, sgrid, dim3(256), 0, st, E, n8, Ep, Ep + (size_t)g.M * K);
+    hipLaunchKernelGGL(split_transpose_kernel, tgrid, dim3(256), 0, st, g.wt, K, N_per_mat, Wp);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int bm = big ? 192 : 128, bn = big ? 256 : 128;
+    const int num_m = (g.M + bm - 1) / bm;
+    const int num_n = n_total / bn;
+    const int ntiles = num_m * num_n;
+    const int grid = ((ntiles + 7) / 8) * 8;
+    if (big) {
+        if (lift)
+            hipLaunchKernelGGL((populate_planes_x3_kernel<192, 256, 16, 4, true>), dim3(grid),
+                               dim3(256), 0, st, g, Ep, Wp, K, num_m, num_n);
+        else
+            hipLaunchKernelGGL((populate_planes_x3_kernel<192, 256, 16, 4, false>), dim3(grid),
+                               dim3(256), 0, st, g, Ep, Wp, K, num_m, num_n);
+    } else {
+        if (lift)
+            hipLaunchKernelGGL((populate_planes_x3_kernel<128, 128, 32, 4, true>), dim3(grid), dim3(256), 0, st,
+                               g, Ep, Wp, K, num_m, num_n);
+        else
+            hipLaunchKernelGGL((populate_planes_x3_kernel<128, 128, 32, 4, false>), dim3(grid), dim3(256), 0, st,
+                               g, Ep, Wp, K, num_m, num_n);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+size_t populate_planes_bytes(const PopulateLaunch& a) {
+    if (a.bf16 || a.fp8 || !planes_shape_ok(a.dm, a.H * a.D)) return 0;
+    return planes_bytes((long long)a.B * a.T, a.dm, 2 * a.L, a.H * a.D);
+}
+
+size_t lift_planes_bytes(const LiftLaunch& a) {
+    if (!planes_shape_ok(a.k_in, a.n)) return 0;
+    return planes_bytes(a.rows, a.k_in, 1, a.n);
+}
+
+hipError_t launch_populate_planes(const PopulateLaunch& a, void* ws, hipStream_t st) {
+    GemmArgs g;
+    g.pos = nullptr;
+    g.pos_rows = 0;
+    g.E = a.E;
+    g.wt = a.wt;
+    g.Kc = a.Kc;
+    g.Vc = a.Vc;
+    g.M = a.B * a.T;
+    g.dm = a.dm;
+    g.T = a.T;
+    g.L = a.L;
+    g.B = a.B;
+    g.H = a.H;
+    g.D = a.D;
+    const int HD = a.H * a.D;
+    return launch_planes(g, a.dm, HD, 2 * a.L, 2 * a.L * HD, false, ws, st);
+}
+
+hipError_t launch_lift_planes(const LiftLaunch& a, void* ws, hipStream_t st) {
+    GemmArgs g;
+    std::memset(&g, 0, sizeof(g));
+    g.E = a.x;
+    g.wt.w[0] = a.w;
+    g.Kc = a.out;
+    g.M = a.rows;
+    g.dm = a.k_in;
+    g.T = a.rows;
+    g.L = 1;
+    g.B = 1;
+    g.H = a.n / 64;
+    g.D = 64;
+    g.pos = a.pos;
+    g.pos_rows = a.pos_rows;
+    return launch_planes(g, a.k_in, a.n, 1, a.n, true, ws, st);
 }
 
 hipError_t launch_populate(const PopulateLaunch& a, hipStream_t st) {

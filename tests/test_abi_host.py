@@ -351,3 +351,41 @@ def test_binding_lift_checks_shapes():
         pc.cke_memory_lift_gelu(x, w, torch.zeros(30, 128), torch.zeros(15, 64))
     with pytest.raises(ValueError, match="device tensor"):
         pc.cke_memory_lift_gelu(x, w, torch.zeros(30, 128))
+
+
+def test_populate_and_lift_workspace_sizes():
+    """The split-planes workspace: E's hi and lo planes, then (256-byte
+    aligned) a hi and a lo plane of every weight; none for bf16 inputs or
+    widths the planes kernel does not take."""
+    g = base_geom()
+    e_planes = 2 * 1500 * 512 * 2
+    w_planes = 12 * 2 * 512 * 512 * 2
+    assert pc.cke_xattn_populate_workspace_bytes(g) == (e_planes + 255) // 256 * 256 + w_planes
+    assert pc.cke_xattn_populate_workspace_bytes(g, pc.CKE_BF16, pc.CKE_BF16) == 0
+    assert pc.cke_xattn_populate_workspace_bytes(base_geom(cache_dtype=pc.CKE_BF16)) == 0
+    assert pc.cke_xattn_populate_workspace_bytes(base_geom(d_model=96, n_heads=3, head_dim=32)) == 0
+    assert pc.cke_xattn_populate_workspace_bytes(base_geom(mem_len=0)) == 0
+    assert pc.cke_memory_lift_workspace_bytes(1500, 4096, 2048) == \
+        2 * 1500 * 4096 * 2 + 2 * 4096 * 2048 * 2
+    assert pc.cke_memory_lift_workspace_bytes(64, 4096, 64) == 0      # n not a multiple of 128
+    assert pc.cke_memory_lift_workspace_bytes(0, 4096, 2048) == 0
+
+
+def test_populate_ws_rejects_a_missing_or_short_workspace_before_launch():
+    g = base_geom(n_layers=2)
+    h = pc.cke_xattn_cache_create(g, FAKE, FAKE, FAKE)
+    try:
+        arr = ctypes.c_void_p * 2
+        ok = arr(FAKE, FAKE)
+        need = pc.cke_xattn_populate_workspace_bytes(g)
+        L = pc.lib()
+        assert L.cke_xattn_populate_ws(h, FAKE, 0, ok, ok, 0, None, need, None) == pc.CKE_EINVAL
+        assert L.cke_xattn_populate_ws(h, FAKE, 0, ok, ok, 0, FAKE, need - 1, None) == pc.CKE_EINVAL
+        assert "needs" in pc.cke_last_error()
+        assert L.cke_xattn_populate_ws(h, FAKE, 0, ok, ok, 0, FAKE + 16, need, None) == pc.CKE_EINVAL
+        assert not pc.cke_xattn_is_ready(h)
+    finally:
+        pc.cke_xattn_cache_destroy(h)
+    Lb = pc.lib()
+    assert Lb.cke_memory_lift_gelu_ws(FAKE, 30, 64, FAKE, 128, None, 0, FAKE, None, 0, None) == \
+        pc.CKE_EINVAL

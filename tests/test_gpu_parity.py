@@ -190,6 +190,53 @@ def test_random_geometry_populate_then_decode(kw):
         assert err <= tol, (layer, err)
 
 
+# ------------------------------------------ populate from split bf16 planes
+PLANES_CASES = [
+    ("base", {}),
+    (None, dict(n_layers=2, n_streams=3, mem_len=77, d_model=256, n_heads=4, head_dim=64)),
+    (None, dict(n_layers=3, n_streams=2, mem_len=130, d_model=384, n_heads=3, head_dim=128)),
+    (None, dict(n_layers=1, n_streams=5, mem_len=1, d_model=128, n_heads=4, head_dim=32)),
+    (None, dict(n_layers=2, n_streams=1, mem_len=300, d_model=640, n_heads=10, head_dim=64)),
+]
+
+
+@pytest.mark.parametrize("name,kw", PLANES_CASES, ids=lambda x: str(x))
+def test_populate_from_split_planes_matches_oracle(name, kw):
+    """The workspace populate (operands split once into bf16 planes, then
+    three bf16 products per k step) within 1e-4 of the oracle on every
+    element, and bit-identical to the populate that splits every tile as it
+    loads it (the same products in the same order); the workspace starts as
+    NaN, so nothing may be read from it before it is written."""
+    g = geometry(name, **kw)
+    cache, wt, (E, WK, WV) = make_cache(g)
+    ref_k, ref_v = cache.k.clone(), cache.v.clone()
+    ws = cache.populate_workspace()
+    assert ws is not None and ws.numel() * 4 == pc.cke_xattn_populate_workspace_bytes(cache.geom)
+    ws.fill_(float("nan"))
+    cache.k.fill_(float("nan"))
+    cache.v.fill_(float("nan"))
+    cache.populate(E, WK, WV, ws=ws)
+    torch.cuda.synchronize()
+    Kc, Vc = oracle_caches(g, wt)
+    assert max_abs(to_np(cache.k), Kc) <= TOL["f32"]
+    assert max_abs(to_np(cache.v), Vc) <= TOL["f32"]
+    assert torch.equal(cache.k, ref_k) and torch.equal(cache.v, ref_v)
+    assert cache.ready
+
+
+def test_populate_workspace_is_refused_when_too_small():
+    g = geometry("base")
+    cache, wt, (E, WK, WV) = make_cache(g)
+    need = pc.cke_xattn_populate_workspace_bytes(cache.geom)
+    small = torch.empty((need - 256) // 4, device=DEV)
+    cache.k.fill_(0.0)
+    with pytest.raises(pc.CkeError) as e:
+        cache.populate(E, WK, WV, ws=small)
+    assert e.value.code == pc.CKE_EINVAL
+    torch.cuda.synchronize()
+    assert float(cache.k.abs().max()) == 0.0      # nothing was launched
+
+
 # -------------------------------------------------------------- cross decode
 DEC_CASES = [
     ("tiny", {}),
@@ -612,13 +659,26 @@ LIFT_CASES = [
 ]
 
 
+LIFT_CASES += [
+    dict(rows=200, k_in=256, n=256, pos_rows=15),   # the split-planes path: k_in % 64, n % 128
+    dict(rows=130, k_in=1024, n=384, pos_rows=0),
+]
+
+
+@pytest.mark.parametrize("ws", [False, True], ids=["tile-split", "planes"])
 @pytest.mark.parametrize("c", LIFT_CASES, ids=lambda c: "r%d-k%d-n%d-p%d" % tuple(c.values()))
-def test_memory_lift_matches_oracle(c):
+def test_memory_lift_matches_oracle(c, ws):
     x = synth.normal([90, 0, c["rows"]], (c["rows"], c["k_in"]))
     W = synth.normal([90, 1, c["rows"]], (c["k_in"], c["n"]), 0.02)
     pos = synth.normal([90, 2, c["rows"]], (c["pos_rows"], c["n"]), 0.02) if c["pos_rows"] else None
     out = torch.full((c["rows"], c["n"]), float("nan"), device=DEV)
-    pc.cke_memory_lift_gelu(t32(x), t32(W), out, None if pos is None else t32(pos))
+    wsb = None
+    if ws:
+        need = pc.cke_memory_lift_workspace_bytes(c["rows"], c["k_in"], c["n"])
+        if need == 0:
+            assert c["k_in"] % 64 or c["n"] % 128
+        wsb = torch.full((max(need, 256) // 4,), float("nan"), device=DEV)
+    pc.cke_memory_lift_gelu(t32(x), t32(W), out, None if pos is None else t32(pos), ws=wsb)
     torch.cuda.synchronize()
     want = oracle.lift_gelu(x, W, pos)
     assert max_abs(to_np(out), want) <= TOL["f32"]
@@ -904,11 +964,14 @@ def test_qformer_memory_lift_full_size():
     g = synth.get("qformer")
     wt = synth.workload_tensors(g, ("X_lift", "W_lift", "pos"))
     rows = g.n_streams * g.mem_len
-    out = torch.full((rows, g.d_model), float("nan"), device=DEV)
-    pc.cke_memory_lift_gelu(t32(wt["X_lift"]), t32(wt["W_lift"]), out, t32(wt["pos"]))
-    torch.cuda.synchronize()
     want = oracle.lift_gelu(wt["X_lift"], wt["W_lift"], wt["pos"])
-    assert max_abs(to_np(out), want) <= TOL["f32"]
+    need = pc.cke_memory_lift_workspace_bytes(rows, g.lift_in, g.d_model)
+    assert need > 0
+    for ws in (None, torch.full((need // 4,), float("nan"), device=DEV)):
+        out = torch.full((rows, g.d_model), float("nan"), device=DEV)
+        pc.cke_memory_lift_gelu(t32(wt["X_lift"]), t32(wt["W_lift"]), out, t32(wt["pos"]), ws=ws)
+        torch.cuda.synchronize()
+        assert max_abs(to_np(out), want) <= TOL["f32"], ws is None
 
 
 def test_qformer_populate_and_decode_full_size():
@@ -923,13 +986,18 @@ def test_qformer_populate_and_decode_full_size():
     wt = synth.workload_tensors(g)
     cache = pc.XattnCache(g.n_layers, g.n_streams, g.mem_len, g.d_model, g.n_heads, g.head_dim,
                           max_q=g.n_q)
-    _nan_fill(cache.k)
-    _nan_fill(cache.v)
-    cache.populate(t32(E), [t32(w) for w in wt["WK"]], [t32(w) for w in wt["WV"]])
-    torch.cuda.synchronize()
     Kc, Vc = oracle.populate(E, wt["WK"], wt["WV"], g.n_heads, g.head_dim)
-    assert max_abs(to_np(cache.k), Kc) <= TOL["f32"]
-    assert max_abs(to_np(cache.v), Vc) <= TOL["f32"]
+    ws = cache.populate_workspace()
+    assert ws is not None
+    for w in (None, ws):      # per-tile split, then split planes in the workspace
+        _nan_fill(cache.k)
+        _nan_fill(cache.v)
+        if w is not None:
+            w.fill_(float("nan"))
+        cache.populate(t32(E), [t32(x) for x in wt["WK"]], [t32(x) for x in wt["WV"]], ws=w)
+        torch.cuda.synchronize()
+        assert max_abs(to_np(cache.k), Kc) <= TOL["f32"]
+        assert max_abs(to_np(cache.v), Vc) <= TOL["f32"]
     K32, V32 = Kc.astype(np.float32), Vc.astype(np.float32)
     cache.k.copy_(t32(K32))
     cache.v.copy_(t32(V32))
