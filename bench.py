@@ -517,6 +517,35 @@ def measure_decoder_step(torch, pc, w, stream, tokens=4):
     return res
 
 
+def measure_launch_floor(torch, stream, launches=256):
+    """Time per launch of a chain of dependent one-element kernels (torch's
+    in-place add on a single float) replayed as one HIP graph: the floor
+    that every call of a window pays whatever its work, against which the
+    latency-bound per-call times are read."""
+    x = torch.zeros(1, device="cuda")
+    with torch.cuda.stream(stream):
+        for _ in range(8):
+            x.add_(1.0)
+    stream.synchronize()
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr, stream=stream):
+        for _ in range(launches):
+            x.add_(1.0)
+    torch.cuda.synchronize()
+    best = float("inf")
+    for _ in range(3):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        with torch.cuda.stream(stream):
+            gr.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        best = min(best, e0.elapsed_time(e1) * 1e-3 / launches)
+    return {"launches": launches, "us_per_launch": best * 1e6,
+            "kernel": "one-element in-place add (torch), dependent chain in one HIP graph"}
+
+
 def measure_cold_decode(torch, pc, w, stream, calls=24):
     """Cross-decode time with the 256 MB MALL cold: each call follows a fill of
     a 512 MB buffer (which evicts the cache). One HIP graph holds `calls` of
@@ -875,6 +904,11 @@ def measure(name, args, torch, pc, stream, extras):
         cold = measure_cold_decode(torch, pc, w, stream)
         if cold:
             blk["xattn_decode_mall_cold"] = cold
+        floor = measure_launch_floor(torch, stream)
+        launches = w.calls("selfattn") + w.calls("xattn_decode") * (2 if w.cache.n_splits > 1 else 1)
+        floor["launches_per_step"] = launches + 1
+        floor["floor_tokens_per_s"] = w.tokens_per_window / ((launches + 1) * floor["us_per_launch"] * 1e-6)
+        blk["launch_floor"] = floor
     del w
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
