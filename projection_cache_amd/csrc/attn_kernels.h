@@ -43,12 +43,10 @@ namespace {
 // Why a second launch: merging inside this kernel needs the partials of
 // other workgroups, which run on other XCDs with their own L2. A
 // release/acquire pair per workgroup is a whole-L2 writeback + invalidate on
-// gfx950. Fence-free variants (device-scope stores acknowledged before a
-// device-scope ticket add, the last arrival reading the partials with
-// device-scope loads; or tagged 64-bit partial words) pay a contended atomic
-// and device-scope round trips on their tail (Whisper Base: 8.2 against
-// 6.9 us per call). All measured slower than a second small kernel, whose
-// inputs are coherent at the kernel boundary.
+// gfx950, and a fence-free variant (tagged 64-bit partial words with
+// device-scope atomic loads and stores, last arrival by ticket) pays several
+// device-scope round trips on its tail; both measured slower than a second
+// small kernel, whose inputs are coherent at the kernel boundary.
 template <int D, typename TE, int NQ, int NW, int NP, bool STREAM>
 __global__ __launch_bounds__(NW * 64) void xattn_partial_kernel(
     const float* __restrict__ q, const TE* __restrict__ Kl, const TE* __restrict__ Vl,
