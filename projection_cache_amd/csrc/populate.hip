@@ -62,21 +62,29 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, const f32x16 (&acc)[
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = wave / WGN, wn = wave % WGN;
     const int l = p < a.L ? p : p - a.L;
-    TOUT* C = static_cast<TOUT*>(p < a.L ? a.Kc : a.Vc);
+    const size_t TD = (size_t)a.T * a.D;
+    TOUT* C = static_cast<TOUT*>(p < a.L ? a.Kc : a.Vc) + (size_t)l * a.B * a.H * TD;
+    // address = row part ((b*H)*T + t)*D + column part h*T*D + d: the column
+    // part is fixed per block column, the row part per accumulator register,
+    // so the divisions run once per row and once per column, not per element
+    size_t coff[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+        const int col = col0 + wn * WTN + nb * 32 + (lane & 31);
+        const int h = col / a.D;
+        coff[nb] = (size_t)h * TD + (col - h * a.D);
+    }
+    const int rbase = m0 + wm * WTM;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-            const int col = col0 + wn * WTN + nb * 32 + (lane & 31);
-            const int h = col / a.D, d = col - (col / a.D) * a.D;
+        for (int r = 0; r < 16; ++r) {
+            const int row = rbase + mb * 32 + acc_row(lane, r);
+            if (row < a.M) {
+                const int b = row / a.T;
+                TOUT* Cr = C + (size_t)b * a.H * TD + (size_t)(row - b * a.T) * a.D;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int row = m0 + wm * WTM + mb * 32 + acc_row(lane, r);
-                if (row < a.M) {
-                    const int b = row / a.T, t = row - (row / a.T) * a.T;
-                    const size_t idx = ((((size_t)l * a.B + b) * a.H + h) * a.T + t) * a.D + d;
-                    store_out<TOUT>(C, idx, acc[mb][nb][r]);
-                }
+                for (int nb = 0; nb < NB; ++nb) store_out<TOUT>(Cr, coff[nb], acc[mb][nb][r]);
             }
         }
 }
@@ -95,18 +103,20 @@ __device__ __forceinline__ void epilogue_lift(const GemmArgs& a, const f32x16 (&
     const int N = a.H * a.D;
     float* C = static_cast<float*>(a.Kc);
     auto gelu = [](float v) { return 0.5f * v * (1.f + erff(v * 0.70710678118654752f)); };
+    const int col = n0 + wn * WTN + (lane & 31);
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-            const int col = n0 + wn * WTN + nb * 32 + (lane & 31);
+        for (int r = 0; r < 16; ++r) {
+            const int row = m0 + wm * WTM + mb * 32 + acc_row(lane, r);
+            if (row < a.M) {
+                float* Cr = C + (size_t)row * N + col;
+                const float* P = a.pos ? a.pos + (size_t)(row % a.pos_rows) * N + col : nullptr;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int row = m0 + wm * WTM + mb * 32 + acc_row(lane, r);
-                if (row < a.M) {
+                for (int nb = 0; nb < NB; ++nb) {
                     float v = gelu(acc[mb][nb][r]);
-                    if (a.pos) v += a.pos[(size_t)(row % a.pos_rows) * N + col];
-                    C[(size_t)row * N + col] = v;
+                    if (P) v += P[nb * 32];
+                    Cr[nb * 32] = v;
                 }
             }
         }
