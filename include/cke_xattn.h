@@ -64,12 +64,15 @@ enum {
  * the bytes of a bf16 cache. */
 enum { CKE_F32 = 0, CKE_BF16 = 1, CKE_FP8 = 2 };
 
+/* Largest number of decoder layers one cache (and one populate) serves. */
+enum { CKE_MAX_LAYERS = 128 };
+
 /* Geometry of one projection cache. Fail-closed: mem_len must be positive and
  * n_heads*head_dim must equal d_model (C-Kernel-Engine page, "View 3": both
  * are hard errors, not defaults). head_dim must be 32, 64 or 128 and d_model
  * a multiple of 32. */
 typedef struct cke_xattn_geom {
-    int32_t n_layers;    /* L, >= 1 */
+    int32_t n_layers;    /* L, 1 .. CKE_MAX_LAYERS */
     int32_t n_streams;   /* B: independent encoder memories, >= 1 */
     int32_t mem_len;     /* T: encoder memory rows per stream, >= 1 */
     int32_t d_model;     /* encoder width = n_heads * head_dim */
@@ -157,6 +160,49 @@ size_t cke_xattn_populate_workspace_bytes(const cke_xattn_geom* g, int e_dtype,
 int cke_xattn_populate_ws(cke_xattn_cache* c, const void* E, int e_dtype,
                           const void* const* WK, const void* const* WV,
                           int w_dtype, void* ws, size_t ws_bytes, void* stream);
+
+/* Weight planes prepared ahead of time. The projection weights are the same
+ * for every encoder window (C-Kernel-Engine, "Whisper: Trace One Encoder
+ * Tensor into Every Decoder Layer", "The concept": one E per window feeds
+ * fixed per-layer WK_l, WV_l), so their split into bf16 planes can run once,
+ * after the weights are loaded, instead of inside every populate.
+ *
+ * cke_weight_planes splits n_mat fp32 device matrices W[i], each [k][n]
+ * row-major, into planes [n_mat][hi, lo][n][k] bf16 (each matrix transposed;
+ * hi = bf16(x), lo = bf16(x - hi), both nearest-even), the same planes
+ * cke_xattn_populate_ws writes into its workspace.
+ *   W             HOST array of n_mat device pointers, each 16-byte aligned
+ *   n_mat         1 .. 2 * CKE_MAX_LAYERS
+ *   k, n          k a multiple of 64, n of 128
+ *   planes, bytes device, 256-byte aligned, at least
+ *                 cke_weight_planes_bytes(n_mat, k, n) bytes; owned by the
+ *                 caller, valid until the caller overwrites or frees them
+ * cke_weight_planes_bytes returns 0 for unsupported sizes; the call returns
+ * CKE_EINVAL for them and for NULL, misaligned or too small arguments. */
+size_t cke_weight_planes_bytes(int n_mat, int k, int n);
+int cke_weight_planes(const float* const* W, int n_mat, int k, int n, void* planes,
+                      size_t bytes, void* stream);
+
+/* Bytes of the per-call planes of rows x k fp32 values (hi and lo, each
+ * [rows][k] bf16, rounded up to 256): the workspace of the two calls below.
+ * 0 when k is not a multiple of 64 or rows < 1. */
+size_t cke_row_planes_bytes(int rows, int k);
+
+/* cke_xattn_populate_ws with the weights already split: the same
+ * projection (same page and section as cke_xattn_populate), bit-identical to
+ * cke_xattn_populate_ws on the same fp32 E and weights. Per call only E is
+ * split, into ws.
+ *   E         device fp32 [B][T][d_model], 16-byte aligned
+ *   w_planes  cke_weight_planes of the 2L matrices WK_0 .. WK_{L-1},
+ *             WV_0 .. WV_{L-1} in that order, k = d_model, n = H*D; w_bytes
+ *             at least cke_weight_planes_bytes(2L, d_model, H*D)
+ *   ws        device, 256-byte aligned, ws_bytes at least
+ *             cke_row_planes_bytes(B*T, d_model); dead after the call
+ * Only fp32 caches with d_model a multiple of 64 and H*D of 128. Sets the
+ * ready flag once the work is enqueued. CKE_EINVAL for any other geometry
+ * and for NULL, misaligned or too small arguments. */
+int cke_xattn_populate_planes(cke_xattn_cache* c, const float* E, const void* w_planes,
+                              size_t w_bytes, void* ws, size_t ws_bytes, void* stream);
 
 /* Cross-attention decode at one layer:
  *   out[b][i][h][:] = sum_t softmax_t(scale * q[b][i][h].K_l[b][h][t]) V_l[b][h][t]
@@ -327,6 +373,20 @@ size_t cke_memory_lift_workspace_bytes(int rows, int k_in, int n);
 int cke_memory_lift_gelu_ws(const float* x, int rows, int k_in, const float* w, int n,
                             const float* pos, int pos_rows, float* out, void* ws,
                             size_t ws_bytes, void* stream);
+
+/* cke_memory_lift_gelu_ws with the lift weight already split by
+ * cke_weight_planes (n_mat = 1, k = k_in, n): bit-identical to
+ * cke_memory_lift_gelu_ws on the same x and w (same page and section as
+ * cke_memory_lift_gelu). Per call only x is split, into ws.
+ *   w_planes, w_bytes  at least cke_weight_planes_bytes(1, k_in, n) bytes
+ *   ws, ws_bytes       device, 256-byte aligned, at least
+ *                      cke_row_planes_bytes(rows, k_in); dead after the call
+ * k_in a multiple of 64, n of 128. Errors as cke_memory_lift_gelu, plus
+ * CKE_EINVAL for unsupported sizes and NULL, misaligned or too small
+ * planes or workspace. */
+int cke_memory_lift_gelu_planes(const float* x, int rows, int k_in, const void* w_planes,
+                                size_t w_bytes, int n, const float* pos, int pos_rows,
+                                float* out, void* ws, size_t ws_bytes, void* stream);
 
 /* Message for the last non-OK status returned on this thread. */
 const char* cke_last_error(void);

@@ -111,6 +111,16 @@ _lib.cke_decoder_layer_step_noalloc.argtypes = [_P, ctypes.POINTER(cke_decoder_l
                                                 ctypes.POINTER(cke_kv_layer), _I, _P, _I, _F, _P]
 _lib.cke_memory_lift_gelu.restype = _I
 _lib.cke_memory_lift_gelu.argtypes = [_P, _I, _I, _P, _I, _P, _I, _P, _P]
+_lib.cke_weight_planes_bytes.restype = _SZ
+_lib.cke_weight_planes_bytes.argtypes = [_I, _I, _I]
+_lib.cke_weight_planes.restype = _I
+_lib.cke_weight_planes.argtypes = [ctypes.POINTER(_P), _I, _I, _I, _P, _SZ, _P]
+_lib.cke_row_planes_bytes.restype = _SZ
+_lib.cke_row_planes_bytes.argtypes = [_I, _I]
+_lib.cke_xattn_populate_planes.restype = _I
+_lib.cke_xattn_populate_planes.argtypes = [_P, _P, _P, _SZ, _P, _SZ, _P]
+_lib.cke_memory_lift_gelu_planes.restype = _I
+_lib.cke_memory_lift_gelu_planes.argtypes = [_P, _I, _I, _P, _SZ, _I, _P, _I, _P, _P, _SZ, _P]
 
 EXPORTED = ["cke_xattn_region_bytes", "cke_xattn_layer_offset_bytes",
             "cke_xattn_workspace_bytes", "cke_xattn_num_splits", "cke_xattn_cache_create",
@@ -121,7 +131,8 @@ EXPORTED = ["cke_xattn_region_bytes", "cke_xattn_layer_offset_bytes",
             "cke_selfattn_prefill_append", "cke_xattn_decode_weights",
             "cke_decoder_step_workspace_bytes", "cke_decoder_layer_step",
             "cke_decoder_step_scratch_bytes", "cke_decoder_layer_step_noalloc",
-            "cke_memory_lift_gelu",
+            "cke_memory_lift_gelu", "cke_weight_planes_bytes", "cke_weight_planes",
+            "cke_row_planes_bytes", "cke_xattn_populate_planes", "cke_memory_lift_gelu_planes",
             "cke_last_error", "cke_version"]
 
 
@@ -263,6 +274,81 @@ def cke_xattn_populate_workspace_bytes(g: cke_xattn_geom, e_dtype=CKE_F32, w_dty
 
 def cke_memory_lift_workspace_bytes(rows: int, k_in: int, n: int) -> int:
     return int(_lib.cke_memory_lift_workspace_bytes(int(rows), int(k_in), int(n)))
+
+
+def cke_weight_planes_bytes(n_mat: int, k: int, n: int) -> int:
+    return int(_lib.cke_weight_planes_bytes(int(n_mat), int(k), int(n)))
+
+
+def cke_row_planes_bytes(rows: int, k: int) -> int:
+    return int(_lib.cke_row_planes_bytes(int(rows), int(k)))
+
+
+def _planes(name, t):
+    """(address, bytes) of a planes or workspace tensor (device, any dtype)."""
+    if not isinstance(t, torch.Tensor):
+        raise ValueError("%s must be a device tensor" % name)
+    return _dev(name, t), t.numel() * t.element_size()
+
+
+def cke_weight_planes(W, planes, stream=None) -> None:
+    """Split fp32 weights W (a sequence of n_mat device tensors [k][n]) into
+    bf16 hi/lo planes in `planes` (a device tensor of at least
+    cke_weight_planes_bytes(n_mat, k, n) bytes)."""
+    if len(W) < 1:
+        raise ValueError("W must hold at least one weight")
+    k, n = W[0].shape
+    ptrs = _devs(*[("W[%d]" % i, w, (k, n), _F32) for i, w in enumerate(W)])
+    p_ptr, p_bytes = _planes("planes", planes)
+    arr = (_P * len(W))(*ptrs)
+    _check(_lib.cke_weight_planes(arr, len(W), int(k), int(n), p_ptr, p_bytes, _stream(stream)))
+
+
+def weight_planes(W, stream=None):
+    """A new device tensor holding the planes of the fp32 weights W."""
+    k, n = W[0].shape
+    nbytes = cke_weight_planes_bytes(len(W), k, n)
+    if nbytes == 0:
+        raise CkeError(CKE_EINVAL, "weights of shape %s x %d take no planes" % ((k, n), len(W)))
+    planes = torch.empty(nbytes // 2, dtype=torch.int16, device=W[0].device)
+    cke_weight_planes(W, planes, stream)
+    return planes
+
+
+def cke_xattn_populate_planes(cache, E, w_planes, ws, stream=None) -> None:
+    """Populate every layer from fp32 E [B][T][d_model] and the prepared
+    planes of WK_0..WK_{L-1}, WV_0..WV_{L-1} (cke_weight_planes); E's planes
+    go to `ws` (at least cke_row_planes_bytes(B*T, d_model) bytes)."""
+    g = _geom(cache)
+    e_ptr = _dev("E", E, (g.n_streams, g.mem_len, g.d_model), _F32)
+    w_ptr, w_bytes = _planes("w_planes", w_planes)
+    ws_ptr, ws_bytes = _planes("ws", ws)
+    _check(_lib.cke_xattn_populate_planes(_handle(cache), e_ptr, w_ptr, w_bytes, ws_ptr, ws_bytes,
+                                          _stream(stream)))
+
+
+def cke_memory_lift_gelu_planes(x, w_planes, n, out, ws, pos=None, stream=None) -> None:
+    """cke_memory_lift_gelu with the lift weight [k_in][n] prepared by
+    cke_weight_planes; x's planes go to `ws` (at least
+    cke_row_planes_bytes(rows, k_in) bytes)."""
+    if not isinstance(x, torch.Tensor) or x.dim() != 2:
+        raise ValueError("x must be a 2-d tensor [rows][k_in]")
+    rows, k_in = x.shape
+    if out.numel() != rows * n:
+        raise ValueError("out must hold rows x n = %d elements (got %d)" % (rows * n, out.numel()))
+    specs = [("x", x, (rows, k_in), _F32), ("out", out, None, _F32)]
+    pos_rows = 0
+    if pos is not None:
+        if pos.dim() != 2:
+            raise ValueError("pos must be a 2-d tensor [pos_rows][n]")
+        pos_rows = pos.shape[0]
+        specs.append(("pos", pos, (pos_rows, n), _F32))
+    ptrs = _devs(*specs)
+    w_ptr, w_bytes = _planes("w_planes", w_planes)
+    ws_ptr, ws_bytes = _planes("ws", ws)
+    _check(_lib.cke_memory_lift_gelu_planes(ptrs[0], int(rows), int(k_in), w_ptr, w_bytes, int(n),
+                                            ptrs[2] if pos is not None else None, int(pos_rows),
+                                            ptrs[1], ws_ptr, ws_bytes, _stream(stream)))
 
 
 def _ws(ws):
@@ -490,6 +576,21 @@ class XattnCache:
 
     def populate(self, E, WK, WV, stream=None, ws=None):
         cke_xattn_populate(self, E, WK, WV, stream, ws=ws)
+
+    def weight_planes(self, WK, WV, stream=None):
+        """The prepared planes of this geometry's fp32 weights (one device
+        tensor; call once per set of weights)."""
+        return weight_planes(list(WK) + list(WV), stream)
+
+    def populate_planes(self, E, w_planes, ws, stream=None):
+        cke_xattn_populate_planes(self, E, w_planes, ws, stream)
+
+    def row_planes_workspace(self, device="cuda"):
+        """A device workspace for populate_planes (E's planes)."""
+        n = cke_row_planes_bytes(self.geom.n_streams * self.geom.mem_len, self.geom.d_model)
+        if n == 0:
+            raise CkeError(CKE_EINVAL, "this geometry takes no planes")
+        return torch.empty((n + 3) // 4, dtype=torch.float32, device=device)
 
     def populate_workspace(self, device="cuda"):
         """A device workspace for populate(..., ws=) of fp32 inputs, or None

@@ -92,6 +92,7 @@ size_t region_elems(const cke_xattn_geom* g) {
 #ifndef CKE_MAX_SPLITS
 #define CKE_MAX_SPLITS 64
 #endif
+static_assert(CKE_MAX_LAYERS == cke::kMaxLayers, "layer cap of the header and the kernels");
 static_assert(CKE_MAX_SPLITS >= 1 && CKE_MAX_SPLITS <= cke::kMaxSplits, "split cap");
 
 // Split of the T memory rows of one (stream, head) across workgroups. Fixed
@@ -206,6 +207,21 @@ int cke_xattn_is_ready(const cke_xattn_cache* c) { return c ? c->ready : 0; }
 
 namespace {
 
+// Geometry part of a populate launch descriptor (no weights).
+void populate_geom(const cke_xattn_cache* c, const void* E, cke::PopulateLaunch* a) {
+    const cke_xattn_geom& g = c->g;
+    std::memset(a, 0, sizeof(*a));
+    a->E = E;
+    a->Kc = c->k;
+    a->Vc = c->v;
+    a->L = g.n_layers;
+    a->B = g.n_streams;
+    a->T = g.mem_len;
+    a->dm = g.d_model;
+    a->H = g.n_heads;
+    a->D = g.head_dim;
+}
+
 // Checks shared by the populate calls; fills the launch descriptor.
 int populate_args(const cke_xattn_cache* c, const void* E, int e_dtype, const void* const* WK,
                   const void* const* WV, int w_dtype, cke::PopulateLaunch* a) {
@@ -222,7 +238,7 @@ int populate_args(const cke_xattn_cache* c, const void* E, int e_dtype, const vo
     if (fp8 && (g.n_heads * g.head_dim) % 256 != 0)
         return fail(CKE_EINVAL, "an fp8 cache needs n_heads * head_dim to be a multiple of 256");
     if (!aligned16(E)) return fail(CKE_EINVAL, "E must be 16-byte aligned");
-    std::memset(a, 0, sizeof(*a));
+    populate_geom(c, E, a);
     for (int l = 0; l < g.n_layers; ++l) {
         if (!WK[l] || !WV[l]) return fail(CKE_EINVAL, "weight pointer of layer %d is NULL", l);
         if (!aligned16(WK[l]) || !aligned16(WV[l]))
@@ -230,15 +246,6 @@ int populate_args(const cke_xattn_cache* c, const void* E, int e_dtype, const vo
         a->wt.w[l] = WK[l];
         a->wt.w[g.n_layers + l] = WV[l];
     }
-    a->E = E;
-    a->Kc = c->k;
-    a->Vc = c->v;
-    a->L = g.n_layers;
-    a->B = g.n_streams;
-    a->T = g.mem_len;
-    a->dm = g.d_model;
-    a->H = g.n_heads;
-    a->D = g.head_dim;
     a->bf16 = bf16 || fp8;
     a->fp8 = fp8;
     return CKE_OK;
@@ -292,6 +299,59 @@ int cke_xattn_populate_ws(cke_xattn_cache* c, const void* E, int e_dtype, const 
                           const void* const* WV, int w_dtype, void* ws, size_t ws_bytes,
                           void* stream) {
     return populate_impl(c, E, e_dtype, WK, WV, w_dtype, ws, ws_bytes, true, stream);
+}
+
+size_t cke_weight_planes_bytes(int n_mat, int k, int n) { return cke::weight_planes_bytes(n_mat, k, n); }
+
+size_t cke_row_planes_bytes(int rows, int k) { return cke::row_planes_bytes(rows, k); }
+
+int cke_weight_planes(const float* const* W, int n_mat, int k, int n, void* planes, size_t bytes,
+                      void* stream) {
+    const size_t need = cke::weight_planes_bytes(n_mat, k, n);
+    if (!need)
+        return fail(CKE_EINVAL, "weight planes need 1..%d matrices, k a multiple of 64 and n of 128 "
+                    "(got %d, %d, %d)", 2 * cke::kMaxLayers, n_mat, k, n);
+    if (!W) return fail(CKE_EINVAL, "weight table is NULL");
+    if (!planes || (reinterpret_cast<uintptr_t>(planes) & (kAlign - 1)) != 0)
+        return fail(CKE_EINVAL, "planes must be non-NULL and 256-byte aligned");
+    if (bytes < need) return fail(CKE_EINVAL, "planes hold %zu bytes; %zu needed", bytes, need);
+    cke::WeightTable wt;
+    std::memset(&wt, 0, sizeof(wt));
+    for (int i = 0; i < n_mat; ++i) {
+        if (!W[i] || !aligned16(W[i]))
+            return fail(CKE_EINVAL, "weight %d must be non-NULL and 16-byte aligned", i);
+        wt.w[i] = W[i];
+    }
+    hipError_t e = cke::launch_weight_planes(wt, n_mat, k, n, planes, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(CKE_EDEVICE, "weight split launch failed: %s", hipGetErrorString(e));
+    return CKE_OK;
+}
+
+int cke_xattn_populate_planes(cke_xattn_cache* c, const float* E, const void* w_planes,
+                              size_t w_bytes, void* ws, size_t ws_bytes, void* stream) {
+    if (!c) return fail(CKE_EINVAL, "cache handle is NULL");
+    const cke_xattn_geom& g = c->g;
+    if (g.cache_dtype != CKE_F32) return fail(CKE_EINVAL, "prepared weight planes serve fp32 caches only");
+    const int HD = g.n_heads * g.head_dim;
+    const size_t w_need = cke::weight_planes_bytes(2 * g.n_layers, g.d_model, HD);
+    const size_t e_need = cke::row_planes_bytes((long long)g.n_streams * g.mem_len, g.d_model);
+    if (!w_need || !e_need)
+        return fail(CKE_EINVAL, "prepared weight planes need d_model a multiple of 64 and n_heads * "
+                    "head_dim of 128 (got %d, %d)", g.d_model, HD);
+    if (!E || !w_planes || !ws) return fail(CKE_EINVAL, "E, w_planes and ws must be non-NULL");
+    if (!aligned16(E)) return fail(CKE_EINVAL, "E must be 16-byte aligned");
+    if ((reinterpret_cast<uintptr_t>(w_planes) & (kAlign - 1)) != 0 ||
+        (reinterpret_cast<uintptr_t>(ws) & (kAlign - 1)) != 0)
+        return fail(CKE_EINVAL, "w_planes and ws must be 256-byte aligned");
+    if (w_bytes < w_need) return fail(CKE_EINVAL, "w_planes hold %zu bytes; %zu needed", w_bytes, w_need);
+    if (ws_bytes < e_need) return fail(CKE_EINVAL, "workspace holds %zu bytes; %zu needed", ws_bytes, e_need);
+    cke::PopulateLaunch a;
+    populate_geom(c, E, &a);
+    c->ready = 0;
+    hipError_t e = cke::launch_populate_from_planes(a, w_planes, ws, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(CKE_EDEVICE, "populate launch failed: %s", hipGetErrorString(e));
+    c->ready = 1;
+    return CKE_OK;
 }
 
 }  // extern "C"
@@ -726,6 +786,30 @@ size_t cke_memory_lift_workspace_bytes(int rows, int k_in, int n) {
     a.k_in = k_in;
     a.n = n;
     return cke::lift_planes_bytes(a);
+}
+
+int cke_memory_lift_gelu_planes(const float* x, int rows, int k_in, const void* w_planes,
+                                size_t w_bytes, int n, const float* pos, int pos_rows, float* out,
+                                void* ws, size_t ws_bytes, void* stream) {
+    const size_t w_need = cke::weight_planes_bytes(1, k_in, n);
+    const size_t e_need = cke::row_planes_bytes(rows, k_in);
+    if (rows >= 1 && (!w_need || !e_need))
+        return fail(CKE_EINVAL, "prepared weight planes need k_in a multiple of 64 and n of 128 "
+                    "(got %d, %d)", k_in, n);
+    cke::LiftLaunch a;
+    // lift_args checks the weight argument for NULL and alignment only
+    const int rc = lift_args(x, rows, k_in, static_cast<const float*>(w_planes), n, pos, pos_rows, out, &a);
+    if (rc != CKE_OK) return rc;
+    if (!ws) return fail(CKE_EINVAL, "ws must be non-NULL");
+    if ((reinterpret_cast<uintptr_t>(w_planes) & (kAlign - 1)) != 0 ||
+        (reinterpret_cast<uintptr_t>(ws) & (kAlign - 1)) != 0)
+        return fail(CKE_EINVAL, "w_planes and ws must be 256-byte aligned");
+    if (w_bytes < w_need) return fail(CKE_EINVAL, "w_planes hold %zu bytes; %zu needed", w_bytes, w_need);
+    if (ws_bytes < e_need) return fail(CKE_EINVAL, "workspace holds %zu bytes; %zu needed", ws_bytes, e_need);
+    a.w = nullptr;
+    hipError_t e = cke::launch_lift_from_planes(a, w_planes, ws, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(CKE_EDEVICE, "memory lift launch failed: %s", hipGetErrorString(e));
+    return CKE_OK;
 }
 
 int cke_memory_lift_gelu_ws(const float* x, int rows, int k_in, const float* w, int n,

@@ -132,4 +132,16 @@ size_t lift_planes_bytes(const LiftLaunch& a);
 hipError_t launch_populate_planes(const PopulateLaunch& a, void* ws, hipStream_t st);
 hipError_t launch_lift_planes(const LiftLaunch& a, void* ws, hipStream_t st);
 
+// The same products with the weights split ahead of time: weight planes are
+// [n_mat][hi, lo][N][K] bf16 (each fp32 [K][N] weight transposed), the rows
+// of E or x are split per call into [hi, lo][M][K] at e_ws. 0 bytes means the
+// shape does not use planes.
+size_t weight_planes_bytes(int n_mat, int K, int N);
+size_t row_planes_bytes(long long M, int K);
+hipError_t launch_weight_planes(const WeightTable& wt, int n_mat, int K, int N, void* planes,
+                                hipStream_t st);
+hipError_t launch_populate_from_planes(const PopulateLaunch& a, const void* w_planes, void* e_ws,
+                                       hipStream_t st);
+hipError_t launch_lift_from_planes(const LiftLaunch& a, const void* w_planes, void* e_ws, hipStream_t st);
+
 }  // namespace cke

@@ -1604,24 +1604,22 @@ bool planes_shape_ok(int K, int N) { return K % 64 == 0 && N % 128 == 0; }
 #endif
 
 
-// split prologue (E rows, then every weight transposed) and the product
-hipError_t launch_planes(GemmArgs g, int K, int N_per_mat, int n_mat, int n_total, bool lift,
-                         void* ws, hipStream_t st) {
-    uint16_t* Ep = static_cast<uint16_t*>(ws);
-    uint16_t* Wp = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + planes_w_offset(g.M, K));
+// the rows of E (or x) split into hi and lo planes at Ep: [2][M][K]
+hipError_t launch_split_rows(const float* E, long long M, int K, uint16_t* Ep, hipStream_t st) {
+    const size_t n8 = (size_t)M * K / 8;
+    const size_t blocks = (n8 + 255) / 256;
+    const dim3 sgrid((unsigned)(blocks < 4096 ? blocks : 4096));
+    hipLaunchKernelGGL(split_rows_kernel, sgrid, dim3(256), 0, st, E, n8, Ep, Ep + (size_t)M * K);
+    return hipGetLastError();
+}
+
+// the product over split planes: E planes at Ep, weight planes at Wp
+hipError_t launch_planes_product(GemmArgs g, int K, int N_per_mat, int n_total, bool lift,
+                                 const uint16_t* Ep, const uint16_t* Wp, hipStream_t st) {
     // 192 x 256 tiles stream fewer operand bytes per product, but only pay
     // while they still give most compute units a tile
     const long long tiles_big = (long long)((g.M + 191) / 192) * (n_total / 256);
     const bool big = N_per_mat % 256 == 0 && tiles_big >= CKE_PLANES_MIN_BIG_TILES;
-    const size_t n8 = (size_t)g.M * K / 8;
-    const size_t blocks = (n8 + 255) / 256;
-    const dim3 sgrid((unsigned)(blocks < 4096 ? blocks : 4096));
-    const dim3 tgrid(N_per_mat / 64, K / 64, n_mat);
-    const float* E = static_cast<const float*>(g.E);
-    hipLaunchKernelGGL(split_rows_kernel, sgrid, dim3(256), 0, st, E, n8, Ep, Ep + (size_t)g.M * K);
-    hipLaunchKernelGGL(split_transpose_kernel, tgrid, dim3(256), 0, st, g.wt, K, N_per_mat, Wp);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
     const int bm = big ? 192 : 128, bn = big ? 256 : 128;
     const int num_m = (g.M + bm - 1) / bm;
     const int num_n = n_total / bn;
@@ -1645,6 +1643,20 @@ hipError_t launch_planes(GemmArgs g, int K, int N_per_mat, int n_mat, int n_tota
     return hipGetLastError();
 }
 
+// split prologue (E rows, then every weight transposed) and the product
+hipError_t launch_planes(GemmArgs g, int K, int N_per_mat, int n_mat, int n_total, bool lift,
+                         void* ws, hipStream_t st) {
+    uint16_t* Ep = static_cast<uint16_t*>(ws);
+    uint16_t* Wp = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + planes_w_offset(g.M, K));
+    hipError_t e = launch_split_rows(static_cast<const float*>(g.E), g.M, K, Ep, st);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(split_transpose_kernel, dim3(N_per_mat / 64, K / 64, n_mat), dim3(256), 0, st,
+                       g.wt, K, N_per_mat, Wp);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_planes_product(g, K, N_per_mat, n_total, lift, Ep, Wp, st);
+}
+
 }  // namespace
 
 size_t populate_planes_bytes(const PopulateLaunch& a) {
@@ -1657,7 +1669,9 @@ size_t lift_planes_bytes(const LiftLaunch& a) {
     return planes_bytes(a.rows, a.k_in, 1, a.n);
 }
 
-hipError_t launch_populate_planes(const PopulateLaunch& a, void* ws, hipStream_t st) {
+namespace {
+
+GemmArgs populate_gemm_args(const PopulateLaunch& a) {
     GemmArgs g;
     g.pos = nullptr;
     g.pos_rows = 0;
@@ -1672,11 +1686,10 @@ hipError_t launch_populate_planes(const PopulateLaunch& a, void* ws, hipStream_t
     g.B = a.B;
     g.H = a.H;
     g.D = a.D;
-    const int HD = a.H * a.D;
-    return launch_planes(g, a.dm, HD, 2 * a.L, 2 * a.L * HD, false, ws, st);
+    return g;
 }
 
-hipError_t launch_lift_planes(const LiftLaunch& a, void* ws, hipStream_t st) {
+GemmArgs lift_gemm_args(const LiftLaunch& a) {
     GemmArgs g;
     std::memset(&g, 0, sizeof(g));
     g.E = a.x;
@@ -1691,7 +1704,54 @@ hipError_t launch_lift_planes(const LiftLaunch& a, void* ws, hipStream_t st) {
     g.D = 64;
     g.pos = a.pos;
     g.pos_rows = a.pos_rows;
-    return launch_planes(g, a.k_in, a.n, 1, a.n, true, ws, st);
+    return g;
+}
+
+}  // namespace
+
+hipError_t launch_populate_planes(const PopulateLaunch& a, void* ws, hipStream_t st) {
+    const int HD = a.H * a.D;
+    return launch_planes(populate_gemm_args(a), a.dm, HD, 2 * a.L, 2 * a.L * HD, false, ws, st);
+}
+
+hipError_t launch_lift_planes(const LiftLaunch& a, void* ws, hipStream_t st) {
+    return launch_planes(lift_gemm_args(a), a.k_in, a.n, 1, a.n, true, ws, st);
+}
+
+size_t weight_planes_bytes(int n_mat, int K, int N) {
+    if (n_mat < 1 || n_mat > 2 * kMaxLayers || K < 1 || N < 1 || !planes_shape_ok(K, N)) return 0;
+    return (size_t)n_mat * 2 * N * K * 2;
+}
+
+size_t row_planes_bytes(long long M, int K) {
+    if (M < 1 || K < 1 || K % 64 != 0) return 0;
+    return planes_w_offset(M, K);
+}
+
+hipError_t launch_weight_planes(const WeightTable& wt, int n_mat, int K, int N, void* planes,
+                                hipStream_t st) {
+    hipLaunchKernelGGL(split_transpose_kernel, dim3(N / 64, K / 64, n_mat), dim3(256), 0, st, wt, K, N,
+                       static_cast<uint16_t*>(planes));
+    return hipGetLastError();
+}
+
+hipError_t launch_populate_from_planes(const PopulateLaunch& a, const void* w_planes, void* e_ws,
+                                       hipStream_t st) {
+    const GemmArgs g = populate_gemm_args(a);
+    uint16_t* Ep = static_cast<uint16_t*>(e_ws);
+    hipError_t e = launch_split_rows(static_cast<const float*>(a.E), g.M, a.dm, Ep, st);
+    if (e != hipSuccess) return e;
+    const int HD = a.H * a.D;
+    return launch_planes_product(g, a.dm, HD, 2 * a.L * HD, false, Ep,
+                                 static_cast<const uint16_t*>(w_planes), st);
+}
+
+hipError_t launch_lift_from_planes(const LiftLaunch& a, const void* w_planes, void* e_ws, hipStream_t st) {
+    const GemmArgs g = lift_gemm_args(a);
+    uint16_t* Ep = static_cast<uint16_t*>(e_ws);
+    hipError_t e = launch_split_rows(a.x, g.M, a.k_in, Ep, st);
+    if (e != hipSuccess) return e;
+    return launch_planes_product(g, a.k_in, a.n, a.n, true, Ep, static_cast<const uint16_t*>(w_planes), st);
 }
 
 hipError_t launch_populate(const PopulateLaunch& a, hipStream_t st) {

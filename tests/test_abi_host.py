@@ -389,3 +389,85 @@ def test_populate_ws_rejects_a_missing_or_short_workspace_before_launch():
     Lb = pc.lib()
     assert Lb.cke_memory_lift_gelu_ws(FAKE, 30, 64, FAKE, 128, None, 0, FAKE, None, 0, None) == \
         pc.CKE_EINVAL
+
+
+def test_prepared_weight_plane_sizes():
+    """Prepared weight planes: [n_mat][hi, lo][n][k] bf16; per-call row
+    planes [hi, lo][rows][k] bf16, rounded up to 256 bytes; 0 where the
+    planes kernel does not take the shape."""
+    assert pc.cke_weight_planes_bytes(12, 512, 512) == 12 * 2 * 512 * 512 * 2
+    assert pc.cke_weight_planes_bytes(1, 4096, 2048) == 2 * 4096 * 2048 * 2
+    assert pc.cke_weight_planes_bytes(2 * 128, 64, 128) == 256 * 2 * 64 * 128 * 2
+    for bad in ((0, 512, 512), (257, 64, 128), (1, 32, 128), (1, 512, 64), (1, 0, 128),
+                (1, 512, 0)):
+        assert pc.cke_weight_planes_bytes(*bad) == 0, bad
+    assert pc.cke_row_planes_bytes(1500, 512) == 2 * 1500 * 512 * 2
+    assert pc.cke_row_planes_bytes(15, 64) == (2 * 15 * 64 * 2 + 255) // 256 * 256
+    assert pc.cke_row_planes_bytes(0, 512) == 0
+    assert pc.cke_row_planes_bytes(15, 96) == 0
+    # the populate workspace is exactly the row planes followed by the weight planes
+    g = base_geom()
+    assert pc.cke_xattn_populate_workspace_bytes(g) == (
+        pc.cke_row_planes_bytes(1500, 512) + pc.cke_weight_planes_bytes(12, 512, 512))
+    assert pc.cke_memory_lift_workspace_bytes(1500, 4096, 2048) == (
+        pc.cke_row_planes_bytes(1500, 4096) + pc.cke_weight_planes_bytes(1, 4096, 2048))
+
+
+def test_prepared_planes_calls_reject_bad_arguments_before_launch():
+    L = pc.lib()
+    arr = ctypes.c_void_p * 2
+    need = pc.cke_weight_planes_bytes(2, 512, 512)
+    ok = arr(FAKE, FAKE)
+    for args in ((ok, 2, 512, 96, FAKE, need), (ok, 0, 512, 512, FAKE, need),
+                 (None, 2, 512, 512, FAKE, need), (ok, 2, 512, 512, None, need),
+                 (ok, 2, 512, 512, FAKE + 16, need), (ok, 2, 512, 512, FAKE, need - 1),
+                 (arr(FAKE, None), 2, 512, 512, FAKE, need), (arr(FAKE, FAKE + 4), 2, 512, 512, FAKE, need)):
+        assert L.cke_weight_planes(*args, None) == pc.CKE_EINVAL, args
+    g = base_geom(n_layers=2)
+    h = pc.cke_xattn_cache_create(g, FAKE, FAKE, FAKE)
+    try:
+        w_need = pc.cke_weight_planes_bytes(4, 512, 512)
+        e_need = pc.cke_row_planes_bytes(1500, 512)
+        for args in ((None, FAKE, FAKE, w_need, FAKE, e_need), (h, None, FAKE, w_need, FAKE, e_need),
+                     (h, FAKE, None, w_need, FAKE, e_need), (h, FAKE, FAKE, w_need, None, e_need),
+                     (h, FAKE + 4, FAKE, w_need, FAKE, e_need), (h, FAKE, FAKE + 16, w_need, FAKE, e_need),
+                     (h, FAKE, FAKE, w_need, FAKE + 16, e_need), (h, FAKE, FAKE, w_need - 1, FAKE, e_need),
+                     (h, FAKE, FAKE, w_need, FAKE, e_need - 1)):
+            assert L.cke_xattn_populate_planes(*args, None) == pc.CKE_EINVAL, args
+        assert pc.cke_xattn_is_ready(h) == 0
+    finally:
+        pc.cke_xattn_cache_destroy(h)
+    for geom in (base_geom(cache_dtype=pc.CKE_BF16), base_geom(d_model=96, n_heads=3, head_dim=32)):
+        h = pc.cke_xattn_cache_create(geom, FAKE, FAKE, FAKE)
+        try:
+            assert L.cke_xattn_populate_planes(h, FAKE, FAKE, 1 << 30, FAKE, 1 << 30,
+                                               None) == pc.CKE_EINVAL
+        finally:
+            pc.cke_xattn_cache_destroy(h)
+    w_need = pc.cke_weight_planes_bytes(1, 4096, 2048)
+    e_need = pc.cke_row_planes_bytes(1500, 4096)
+    for args in ((FAKE, 1500, 4096, FAKE, w_need, 2048, None, 0, FAKE, FAKE, e_need - 1),
+                 (FAKE, 1500, 4096, FAKE, w_need - 1, 2048, None, 0, FAKE, FAKE, e_need),
+                 (FAKE, 1500, 4096, FAKE + 16, w_need, 2048, None, 0, FAKE, FAKE, e_need),
+                 (FAKE, 1500, 4096, FAKE, w_need, 2048, None, 0, FAKE, None, e_need),
+                 (FAKE, 1500, 4096, FAKE, w_need, 2048, FAKE, 0, FAKE, FAKE, e_need),
+                 (FAKE, 1500, 4096, FAKE, w_need, 2000, None, 0, FAKE, FAKE, e_need),
+                 (FAKE, 1500, 4000, FAKE, w_need, 2048, None, 0, FAKE, FAKE, e_need),
+                 (None, 1500, 4096, FAKE, w_need, 2048, None, 0, FAKE, FAKE, e_need)):
+        assert L.cke_memory_lift_gelu_planes(*args, None) == pc.CKE_EINVAL, args
+
+
+def test_binding_prepared_planes_check_shapes_before_launch():
+    import torch
+    x = torch.zeros(4, 64)
+    with pytest.raises(ValueError):
+        pc.cke_weight_planes([x], torch.zeros(16))
+    with pytest.raises(ValueError):
+        pc.cke_memory_lift_gelu_planes(torch.zeros(4), torch.zeros(16), 128, torch.zeros(512),
+                                       torch.zeros(16))
+    with pytest.raises(ValueError):
+        pc.cke_memory_lift_gelu_planes(x, torch.zeros(16), 128, torch.zeros(4 * 127),
+                                       torch.zeros(16))
+    with pytest.raises(ValueError):
+        pc.cke_memory_lift_gelu_planes(x, torch.zeros(16), 128, torch.zeros(4 * 128),
+                                       torch.zeros(16))

@@ -224,6 +224,60 @@ def test_populate_from_split_planes_matches_oracle(name, kw):
     assert cache.ready
 
 
+@pytest.mark.parametrize("name,kw", PLANES_CASES, ids=lambda x: str(x))
+def test_populate_from_prepared_weight_planes(name, kw):
+    """Weight planes prepared once (cke_weight_planes) and reused by two
+    populates of different encoder memories: each is bit-identical to the
+    workspace populate that splits the weights itself (the oracle pins that
+    one). Planes, workspace and caches start as NaN."""
+    g = geometry(name, **kw)
+    cache, wt, (E, WK, WV) = make_cache(g)
+    nan = float("nan")
+    ws = cache.populate_workspace()
+    E2 = (E * -0.5 + 0.25).contiguous()
+    refs = []
+    for e_in in (E, E2):
+        cache.populate(e_in, WK, WV, ws=ws)
+        refs.append((cache.k.clone(), cache.v.clone()))
+    HD = g.n_heads * g.head_dim
+    nbytes = pc.cke_weight_planes_bytes(2 * g.n_layers, g.d_model, HD)
+    assert nbytes == 2 * g.n_layers * 2 * HD * g.d_model * 2
+    planes = torch.full((nbytes // 4,), -1, dtype=torch.int32, device=DEV)   # NaN bit patterns
+    pc.cke_weight_planes(list(WK) + list(WV), planes)
+    rws = torch.full((pc.cke_row_planes_bytes(g.n_streams * g.mem_len, g.d_model) // 4,), nan,
+                     device=DEV)
+    for e_in, (rk, rv) in zip((E, E2), refs):
+        cache.k.fill_(nan)
+        cache.v.fill_(nan)
+        cache.populate_planes(e_in, planes, rws)
+        torch.cuda.synchronize()
+        assert torch.equal(cache.k, rk) and torch.equal(cache.v, rv)
+        assert cache.ready
+    # the planes of a subset of the weights, made by the same call, are the
+    # matching slice of the whole
+    part = torch.full((pc.cke_weight_planes_bytes(1, g.d_model, HD) // 4,), -1, dtype=torch.int32,
+                      device=DEV)
+    pc.cke_weight_planes([WV[-1]], part)
+    torch.cuda.synchronize()
+    assert torch.equal(part, planes[-part.numel():])
+
+
+def test_populate_from_prepared_planes_refuses_short_buffers():
+    g = geometry("base")
+    cache, wt, (E, WK, WV) = make_cache(g)
+    planes = cache.weight_planes(WK, WV)
+    rws = cache.row_planes_workspace()
+    cache.k.fill_(0.0)
+    torch.cuda.synchronize()
+    for p_, w_ in ((planes[:-128], rws), (planes, rws[:-64])):
+        with pytest.raises(pc.CkeError) as e:
+            cache.populate_planes(E, p_, w_)
+        assert e.value.code == pc.CKE_EINVAL
+    torch.cuda.synchronize()
+    assert float(cache.k.abs().max()) == 0.0      # nothing was launched
+    assert cache.ready                            # refused before the flag was touched
+
+
 def test_populate_workspace_is_refused_when_too_small():
     g = geometry("base")
     cache, wt, (E, WK, WV) = make_cache(g)
@@ -682,6 +736,27 @@ def test_memory_lift_matches_oracle(c, ws):
     torch.cuda.synchronize()
     want = oracle.lift_gelu(x, W, pos)
     assert max_abs(to_np(out), want) <= TOL["f32"]
+
+
+@pytest.mark.parametrize("c", [c for c in LIFT_CASES if c["k_in"] % 64 == 0 and c["n"] % 128 == 0],
+                         ids=lambda c: "r%d-k%d-n%d-p%d" % tuple(c.values()))
+def test_memory_lift_from_prepared_weight_planes(c):
+    """The lift from a weight split once by cke_weight_planes is
+    bit-identical to the workspace lift that splits it per call."""
+    x = synth.normal([90, 0, c["rows"]], (c["rows"], c["k_in"]))
+    W = synth.normal([90, 1, c["rows"]], (c["k_in"], c["n"]), 0.02)
+    pos = synth.normal([90, 2, c["rows"]], (c["pos_rows"], c["n"]), 0.02) if c["pos_rows"] else None
+    pos_t = None if pos is None else t32(pos)
+    need = pc.cke_memory_lift_workspace_bytes(c["rows"], c["k_in"], c["n"])
+    ref = torch.empty((c["rows"], c["n"]), device=DEV)
+    pc.cke_memory_lift_gelu(t32(x), t32(W), ref, pos_t, ws=torch.empty(need // 4, device=DEV))
+    planes = pc.weight_planes([t32(W)])
+    rws = torch.full((pc.cke_row_planes_bytes(c["rows"], c["k_in"]) // 4,), float("nan"), device=DEV)
+    out = torch.full((c["rows"], c["n"]), float("nan"), device=DEV)
+    pc.cke_memory_lift_gelu_planes(t32(x), planes, c["n"], out, rws, pos=pos_t)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
+    assert max_abs(to_np(out), oracle.lift_gelu(x, W, pos)) <= TOL["f32"]
 
 
 def fp8_bracket(exact, absdot, dm):
