@@ -144,7 +144,8 @@ class Workload:
             self.e_ws = self.cache.row_planes_workspace()
         if self.lift_ws is not None:
             self.lift_planes = pc.weight_planes([self.lift["W_lift"]])
-            n = pc.cke_row_planes_bytes(g.n_streams * g.mem_len, g.lift_in)
+            n = pc.cke_memory_lift_planes_workspace_bytes(g.n_streams * g.mem_len, g.lift_in,
+                                                         g.d_model)
             self.lift_rws = torch.empty((n + 3) // 4, device=dev)
         # per-call inputs [steps][L][...]
         steps, L = g.steps, g.n_layers

@@ -184,8 +184,8 @@ int cke_weight_planes(const float* const* W, int n_mat, int k, int n, void* plan
                       size_t bytes, void* stream);
 
 /* Bytes of the per-call planes of rows x k fp32 values (hi and lo, each
- * [rows][k] bf16, rounded up to 256): the workspace of the two calls below.
- * 0 when k is not a multiple of 64 or rows < 1. */
+ * [rows][k] bf16, rounded up to 256): the workspace of
+ * cke_xattn_populate_planes. 0 when k is not a multiple of 64 or rows < 1. */
 size_t cke_row_planes_bytes(int rows, int k);
 
 /* cke_xattn_populate_ws with the weights already split: the same
@@ -362,7 +362,10 @@ int cke_memory_lift_gelu(const float* x, int rows, int k_in, const float* w, int
 /* cke_memory_lift_gelu with caller workspace: x and w are split once into
  * bf16 hi/lo planes in ws (w transposed) and the product runs as three bf16
  * products over them, as cke_xattn_populate_ws does (same page and section
- * as cke_memory_lift_gelu; same result within the same bound).
+ * as cke_memory_lift_gelu; same result within the same bound). A lift with
+ * too few 192 x 256 output tiles to occupy the compute units is also split
+ * over k_in into 2 or 4 slices whose fp32 partial sums (in ws) are added in
+ * slice order before the GELU; the result stays deterministic.
  *   ws, ws_bytes  device, 256-byte aligned, at least
  *                 cke_memory_lift_workspace_bytes(rows, k_in, n) bytes
  * Applies when k_in is a multiple of 64 and n of 128; otherwise the
@@ -377,13 +380,16 @@ int cke_memory_lift_gelu_ws(const float* x, int rows, int k_in, const float* w, 
 /* cke_memory_lift_gelu_ws with the lift weight already split by
  * cke_weight_planes (n_mat = 1, k = k_in, n): bit-identical to
  * cke_memory_lift_gelu_ws on the same x and w (same page and section as
- * cke_memory_lift_gelu). Per call only x is split, into ws.
+ * cke_memory_lift_gelu). Per call only x is split, into ws (followed by the
+ * partial sums of a lift split over k_in).
  *   w_planes, w_bytes  at least cke_weight_planes_bytes(1, k_in, n) bytes
  *   ws, ws_bytes       device, 256-byte aligned, at least
- *                      cke_row_planes_bytes(rows, k_in); dead after the call
- * k_in a multiple of 64, n of 128. Errors as cke_memory_lift_gelu, plus
- * CKE_EINVAL for unsupported sizes and NULL, misaligned or too small
- * planes or workspace. */
+ *                      cke_memory_lift_planes_workspace_bytes(rows, k_in, n);
+ *                      dead after the call
+ * k_in a multiple of 64, n of 128 (the size function returns 0 otherwise).
+ * Errors as cke_memory_lift_gelu, plus CKE_EINVAL for unsupported sizes and
+ * NULL, misaligned or too small planes or workspace. */
+size_t cke_memory_lift_planes_workspace_bytes(int rows, int k_in, int n);
 int cke_memory_lift_gelu_planes(const float* x, int rows, int k_in, const void* w_planes,
                                 size_t w_bytes, int n, const float* pos, int pos_rows,
                                 float* out, void* ws, size_t ws_bytes, void* stream);

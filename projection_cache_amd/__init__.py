@@ -119,6 +119,8 @@ _lib.cke_row_planes_bytes.restype = _SZ
 _lib.cke_row_planes_bytes.argtypes = [_I, _I]
 _lib.cke_xattn_populate_planes.restype = _I
 _lib.cke_xattn_populate_planes.argtypes = [_P, _P, _P, _SZ, _P, _SZ, _P]
+_lib.cke_memory_lift_planes_workspace_bytes.restype = _SZ
+_lib.cke_memory_lift_planes_workspace_bytes.argtypes = [_I, _I, _I]
 _lib.cke_memory_lift_gelu_planes.restype = _I
 _lib.cke_memory_lift_gelu_planes.argtypes = [_P, _I, _I, _P, _SZ, _I, _P, _I, _P, _P, _SZ, _P]
 
@@ -133,6 +135,7 @@ EXPORTED = ["cke_xattn_region_bytes", "cke_xattn_layer_offset_bytes",
             "cke_decoder_step_scratch_bytes", "cke_decoder_layer_step_noalloc",
             "cke_memory_lift_gelu", "cke_weight_planes_bytes", "cke_weight_planes",
             "cke_row_planes_bytes", "cke_xattn_populate_planes", "cke_memory_lift_gelu_planes",
+            "cke_memory_lift_planes_workspace_bytes",
             "cke_last_error", "cke_version"]
 
 
@@ -284,6 +287,10 @@ def cke_row_planes_bytes(rows: int, k: int) -> int:
     return int(_lib.cke_row_planes_bytes(int(rows), int(k)))
 
 
+def cke_memory_lift_planes_workspace_bytes(rows: int, k_in: int, n: int) -> int:
+    return int(_lib.cke_memory_lift_planes_workspace_bytes(int(rows), int(k_in), int(n)))
+
+
 def _planes(name, t):
     """(address, bytes) of a planes or workspace tensor (device, any dtype)."""
     if not isinstance(t, torch.Tensor):
@@ -329,8 +336,9 @@ def cke_xattn_populate_planes(cache, E, w_planes, ws, stream=None) -> None:
 
 def cke_memory_lift_gelu_planes(x, w_planes, n, out, ws, pos=None, stream=None) -> None:
     """cke_memory_lift_gelu with the lift weight [k_in][n] prepared by
-    cke_weight_planes; x's planes go to `ws` (at least
-    cke_row_planes_bytes(rows, k_in) bytes)."""
+    cke_weight_planes; x's planes (and the partial sums of a lift split over
+    k_in) go to `ws` (at least cke_memory_lift_planes_workspace_bytes(rows,
+    k_in, n) bytes)."""
     if not isinstance(x, torch.Tensor) or x.dim() != 2:
         raise ValueError("x must be a 2-d tensor [rows][k_in]")
     rows, k_in = x.shape

@@ -788,11 +788,22 @@ size_t cke_memory_lift_workspace_bytes(int rows, int k_in, int n) {
     return cke::lift_planes_bytes(a);
 }
 
+size_t cke_memory_lift_planes_workspace_bytes(int rows, int k_in, int n) {
+    if (rows < 1 || k_in < 1 || n < 1) return 0;
+    if ((long long)rows * k_in > (1ll << 31) - 1 || (long long)rows * n > (1ll << 31) - 1) return 0;
+    cke::LiftLaunch a;
+    std::memset(&a, 0, sizeof(a));
+    a.rows = rows;
+    a.k_in = k_in;
+    a.n = n;
+    return cke::lift_rows_bytes(a);
+}
+
 int cke_memory_lift_gelu_planes(const float* x, int rows, int k_in, const void* w_planes,
                                 size_t w_bytes, int n, const float* pos, int pos_rows, float* out,
                                 void* ws, size_t ws_bytes, void* stream) {
     const size_t w_need = cke::weight_planes_bytes(1, k_in, n);
-    const size_t e_need = cke::row_planes_bytes(rows, k_in);
+    const size_t e_need = cke_memory_lift_planes_workspace_bytes(rows, k_in, n);
     if (rows >= 1 && (!w_need || !e_need))
         return fail(CKE_EINVAL, "prepared weight planes need k_in a multiple of 64 and n of 128 "
                     "(got %d, %d)", k_in, n);

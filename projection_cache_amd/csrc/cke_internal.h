@@ -137,6 +137,9 @@ hipError_t launch_lift_planes(const LiftLaunch& a, void* ws, hipStream_t st);
 // of E or x are split per call into [hi, lo][M][K] at e_ws. 0 bytes means the
 // shape does not use planes.
 size_t weight_planes_bytes(int n_mat, int K, int N);
+// workspace of launch_lift_from_planes: x's planes, then (a memory lift split
+// over k) its partial sums
+size_t lift_rows_bytes(const LiftLaunch& a);
 size_t row_planes_bytes(long long M, int K);
 hipError_t launch_weight_planes(const WeightTable& wt, int n_mat, int K, int N, void* planes,
                                 hipStream_t st);

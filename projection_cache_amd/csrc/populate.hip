@@ -122,6 +122,30 @@ __device__ __forceinline__ void epilogue_lift(const GemmArgs& a, const f32x16 (&
         }
 }
 
+// Raw accumulators of one k slice, token-major P[m][n] (N columns), in the
+// layout of epilogue_lift.
+template <int BM, int BN, int WGM, int WGN>
+__device__ __forceinline__ void epilogue_partial(float* P, int M, int N,
+                                                 const f32x16 (&acc)[BM / WGM / 32][BN / WGN / 32],
+                                                 int m0, int n0)
+{
+    constexpr int WTM = BM / WGM, WTN = BN / WGN, MB = WTM / 32, NB = WTN / 32;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = wave / WGN, wn = wave % WGN;
+    const int col = n0 + wn * WTN + (lane & 31);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int row = m0 + wm * WTM + mb * 32 + acc_row(lane, r);
+            if (row < M) {
+                float* Pr = P + (size_t)row * N + col;
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) Pr[nb * 32] = acc[mb][nb][r];
+            }
+        }
+}
+
 // fp32 operands on v_mfma_f32_32x32x2_f32. LDS holds both tiles k-major:
 // As[k][m] (transposed on store) and Bs[k][n], so a half-wave reads 32
 // consecutive floats per operand.
@@ -1094,7 +1118,8 @@ __device__ __forceinline__ int plane_pos(int row, int piece) {
 template <int BM, int BN, int BK, int NSLOT, bool LIFT>
 __global__ __launch_bounds__(256) void populate_planes_x3_kernel(GemmArgs a, const uint16_t* __restrict__ Ep,
                                                                  const uint16_t* __restrict__ Wp, int K,
-                                                                 int num_m, int num_n)
+                                                                 int num_m, int num_n, int splits,
+                                                                 float* __restrict__ part)
 {
     constexpr int WGM = 2, WGN = 2;
     constexpr int WTM = BM / WGM, WTN = BN / WGN, MB = WTM / 32, NB = WTN / 32;
@@ -1109,10 +1134,16 @@ __global__ __launch_bounds__(256) void populate_planes_x3_kernel(GemmArgs a, con
     constexpr int GROUP_M = 8;
     __shared__ __attribute__((aligned(1024))) PlaneSlot<BM, BN, BK> ring[NSLOT];
 
+    // work item = (k slice, tile), slice-major, dealt to the XCDs in
+    // contiguous ranges so that one XCD's tiles share panels at the same k
     const int ntiles = num_m * num_n;
-    const int per_xcd = (ntiles + 7) / 8;
-    const int tile = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
-    if (tile >= ntiles) return;
+    const int per_xcd = (ntiles * splits + 7) / 8;
+    const int item = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+    if (item >= ntiles * splits) return;
+    const int slice = item / ntiles;
+    const int tile = item - slice * ntiles;
+    const int k_len = K / splits;                  // a multiple of BK, checked at launch
+    const int k_first = slice * k_len;
     const int group = tile / (GROUP_M * num_n);
     const int first_m = group * GROUP_M;
     const int gsize = min(num_m - first_m, GROUP_M);
@@ -1150,7 +1181,8 @@ __global__ __launch_bounds__(256) void populate_planes_x3_kernel(GemmArgs a, con
             const uint16_t* src = on_a ? (lo ? El : Eh) + (size_t)min(m0 + row, a.M - 1) * K
                                        : (lo ? Wl : Wh) + (size_t)row * K;
             uint16_t* dst = on_a ? (lo ? slot.al : slot.ah) : (lo ? slot.bl : slot.bh);
-            dma16(src + kt * BK + piece * 8, __builtin_amdgcn_readfirstlane(lds_addr(dst + in_plane * 64 * 8)));
+            dma16(src + k_first + kt * BK + piece * 8,
+                  __builtin_amdgcn_readfirstlane(lds_addr(dst + in_plane * 64 * 8)));
         }
     };
     struct Frags {
@@ -1201,7 +1233,7 @@ __global__ __launch_bounds__(256) void populate_planes_x3_kernel(GemmArgs a, con
                 acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.ah[mb], f.bh[nb], acc[mb][nb], 0, 0, 0);
     };
 
-    const int nk = K / BK;
+    const int nk = k_len / BK;
     // before the wait for k-tile j, k-tiles 0..min(j + NSLOT - 3, nk - 1) have
     // been issued (0..NSLOT-2 for j = 0): wait until only the later ones are
     // outstanding, then a barrier makes every thread's loads of j visible
@@ -1271,10 +1303,50 @@ __global__ __launch_bounds__(256) void populate_planes_x3_kernel(GemmArgs a, con
             mma(cur);
         }
     }
-    if constexpr (LIFT)
-        epilogue_lift<BM, BN, WGM, WGN>(a, acc, m0, n0);
-    else
+    if constexpr (LIFT) {
+        if (part)   // one k slice: raw sums, reduced by lift_reduce_kernel
+            epilogue_partial<BM, BN, WGM, WGN>(part + (size_t)slice * a.M * (a.H * a.D), a.M, a.H * a.D,
+                                               acc, m0, n0);
+        else
+            epilogue_lift<BM, BN, WGM, WGN>(a, acc, m0, n0);
+    } else {
         epilogue<BM, BN, WGM, WGN, float>(a, acc, m0, p, col0);
+    }
+}
+
+// out[m][n] = gelu(sum over s of part[s][m][n], s ascending) + pos[m % pos_rows][n]:
+// the k slices of a split lift, four consecutive columns per thread.
+__global__ __launch_bounds__(256) void lift_reduce_kernel(const float* __restrict__ part, int splits,
+                                                          int M, int N, const float* __restrict__ pos,
+                                                          int pos_rows, float* __restrict__ out)
+{
+    const size_t MN = (size_t)M * N;
+    const size_t n4 = MN / 4;
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (size_t)gridDim.x * 256) {
+        float4 v = reinterpret_cast<const float4*>(part)[i];
+        for (int sl = 1; sl < splits; ++sl) {
+            const float4 w = reinterpret_cast<const float4*>(part + (size_t)sl * MN)[i];
+            v.x += w.x;
+            v.y += w.y;
+            v.z += w.z;
+            v.w += w.w;
+        }
+        auto gelu = [](float x) { return 0.5f * x * (1.f + erff(x * 0.70710678118654752f)); };
+        v.x = gelu(v.x);
+        v.y = gelu(v.y);
+        v.z = gelu(v.z);
+        v.w = gelu(v.w);
+        if (pos) {
+            const size_t e = i * 4;
+            const int m = (int)(e / N), n = (int)(e - (size_t)m * N);
+            const float4 q = *reinterpret_cast<const float4*>(pos + (size_t)(m % pos_rows) * N + n);
+            v.x += q.x;
+            v.y += q.y;
+            v.z += q.z;
+            v.w += q.w;
+        }
+        reinterpret_cast<float4*>(out)[i] = v;
+    }
 }
 
 // fp32 populate for gfx950 on v_mfma_f32_32x32x2_f32: 64x64 output tiles,
@@ -1613,33 +1685,60 @@ hipError_t launch_split_rows(const float* E, long long M, int K, uint16_t* Ep, h
     return hipGetLastError();
 }
 
-// the product over split planes: E planes at Ep, weight planes at Wp
+// A memory lift too small to give most compute units a 192 x 256 tile is
+// split over k into 4 or 2 slices of at least 256 each, so that tiles x
+// slices stays within one workgroup per compute unit; lift_reduce_kernel
+// then adds the slices in order and applies the GELU and the positions.
+int lift_splits(long long M, int K, int N) {
+    if (N % 256 != 0) return 1;
+    const long long tiles = ((M + 191) / 192) * (N / 256);
+    if (tiles >= CKE_PLANES_MIN_BIG_TILES) return 1;
+    if (tiles * 4 <= 256 && K % 256 == 0 && K / 4 >= 256) return 4;
+    if (tiles * 2 <= 256 && K % 128 == 0 && K / 2 >= 256) return 2;
+    return 1;
+}
+
+size_t lift_partial_bytes(long long M, int K, int N) {
+    const int S = lift_splits(M, K, N);
+    return S > 1 ? ((size_t)S * M * N * 4 + 255) / 256 * 256 : 0;
+}
+
+// the product over split planes: E planes at Ep, weight planes at Wp; a
+// split lift's slices go to `part` (lift_partial_bytes)
 hipError_t launch_planes_product(GemmArgs g, int K, int N_per_mat, int n_total, bool lift,
-                                 const uint16_t* Ep, const uint16_t* Wp, hipStream_t st) {
+                                 const uint16_t* Ep, const uint16_t* Wp, float* part, hipStream_t st) {
+    const int S = lift ? lift_splits(g.M, K, n_total) : 1;
     // 192 x 256 tiles stream fewer operand bytes per product, but only pay
     // while they still give most compute units a tile
     const long long tiles_big = (long long)((g.M + 191) / 192) * (n_total / 256);
-    const bool big = N_per_mat % 256 == 0 && tiles_big >= CKE_PLANES_MIN_BIG_TILES;
+    const bool big = S > 1 || (N_per_mat % 256 == 0 && tiles_big >= CKE_PLANES_MIN_BIG_TILES);
     const int bm = big ? 192 : 128, bn = big ? 256 : 128;
     const int num_m = (g.M + bm - 1) / bm;
     const int num_n = n_total / bn;
     const int ntiles = num_m * num_n;
-    const int grid = ((ntiles + 7) / 8) * 8;
+    const int grid = ((ntiles * S + 7) / 8) * 8;
+    float* p = S > 1 ? part : nullptr;
     if (big) {
         if (lift)
             hipLaunchKernelGGL((populate_planes_x3_kernel<192, 256, 16, 4, true>), dim3(grid),
-                               dim3(256), 0, st, g, Ep, Wp, K, num_m, num_n);
+                               dim3(256), 0, st, g, Ep, Wp, K, num_m, num_n, S, p);
         else
             hipLaunchKernelGGL((populate_planes_x3_kernel<192, 256, 16, 4, false>), dim3(grid),
-                               dim3(256), 0, st, g, Ep, Wp, K, num_m, num_n);
+                               dim3(256), 0, st, g, Ep, Wp, K, num_m, num_n, 1, nullptr);
     } else {
         if (lift)
             hipLaunchKernelGGL((populate_planes_x3_kernel<128, 128, 32, 4, true>), dim3(grid), dim3(256), 0, st,
-                               g, Ep, Wp, K, num_m, num_n);
+                               g, Ep, Wp, K, num_m, num_n, 1, nullptr);
         else
             hipLaunchKernelGGL((populate_planes_x3_kernel<128, 128, 32, 4, false>), dim3(grid), dim3(256), 0, st,
-                               g, Ep, Wp, K, num_m, num_n);
+                               g, Ep, Wp, K, num_m, num_n, 1, nullptr);
     }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || S == 1) return e;
+    const size_t n4 = (size_t)g.M * n_total / 4;
+    const size_t blocks = (n4 + 255) / 256;
+    hipLaunchKernelGGL(lift_reduce_kernel, dim3((unsigned)(blocks < 2048 ? blocks : 2048)), dim3(256), 0, st,
+                       part, S, g.M, n_total, g.pos, g.pos_rows, static_cast<float*>(g.Kc));
     return hipGetLastError();
 }
 
@@ -1654,7 +1753,8 @@ hipError_t launch_planes(GemmArgs g, int K, int N_per_mat, int n_mat, int n_tota
                        g.wt, K, N_per_mat, Wp);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    return launch_planes_product(g, K, N_per_mat, n_total, lift, Ep, Wp, st);
+    float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + planes_bytes(g.M, K, n_mat, N_per_mat));
+    return launch_planes_product(g, K, N_per_mat, n_total, lift, Ep, Wp, part, st);
 }
 
 }  // namespace
@@ -1666,7 +1766,12 @@ size_t populate_planes_bytes(const PopulateLaunch& a) {
 
 size_t lift_planes_bytes(const LiftLaunch& a) {
     if (!planes_shape_ok(a.k_in, a.n)) return 0;
-    return planes_bytes(a.rows, a.k_in, 1, a.n);
+    return planes_bytes(a.rows, a.k_in, 1, a.n) + lift_partial_bytes(a.rows, a.k_in, a.n);
+}
+
+size_t lift_rows_bytes(const LiftLaunch& a) {
+    if (a.rows < 1 || !planes_shape_ok(a.k_in, a.n)) return 0;
+    return planes_w_offset(a.rows, a.k_in) + lift_partial_bytes(a.rows, a.k_in, a.n);
 }
 
 namespace {
@@ -1743,7 +1848,7 @@ hipError_t launch_populate_from_planes(const PopulateLaunch& a, const void* w_pl
     if (e != hipSuccess) return e;
     const int HD = a.H * a.D;
     return launch_planes_product(g, a.dm, HD, 2 * a.L * HD, false, Ep,
-                                 static_cast<const uint16_t*>(w_planes), st);
+                                 static_cast<const uint16_t*>(w_planes), nullptr, st);
 }
 
 hipError_t launch_lift_from_planes(const LiftLaunch& a, const void* w_planes, void* e_ws, hipStream_t st) {
@@ -1751,7 +1856,9 @@ hipError_t launch_lift_from_planes(const LiftLaunch& a, const void* w_planes, vo
     uint16_t* Ep = static_cast<uint16_t*>(e_ws);
     hipError_t e = launch_split_rows(a.x, g.M, a.k_in, Ep, st);
     if (e != hipSuccess) return e;
-    return launch_planes_product(g, a.k_in, a.n, a.n, true, Ep, static_cast<const uint16_t*>(w_planes), st);
+    float* part = reinterpret_cast<float*>(static_cast<char*>(e_ws) + planes_w_offset(g.M, a.k_in));
+    return launch_planes_product(g, a.k_in, a.n, a.n, true, Ep, static_cast<const uint16_t*>(w_planes),
+                                 part, st);
 }
 
 hipError_t launch_populate(const PopulateLaunch& a, hipStream_t st) {

@@ -365,8 +365,9 @@ def test_populate_and_lift_workspace_sizes():
     assert pc.cke_xattn_populate_workspace_bytes(base_geom(cache_dtype=pc.CKE_BF16)) == 0
     assert pc.cke_xattn_populate_workspace_bytes(base_geom(d_model=96, n_heads=3, head_dim=32)) == 0
     assert pc.cke_xattn_populate_workspace_bytes(base_geom(mem_len=0)) == 0
+    # the Q-Former lift makes 64 tiles of 192 x 256: split over k in 4 slices of partial sums
     assert pc.cke_memory_lift_workspace_bytes(1500, 4096, 2048) == \
-        2 * 1500 * 4096 * 2 + 2 * 4096 * 2048 * 2
+        2 * 1500 * 4096 * 2 + 2 * 4096 * 2048 * 2 + 4 * 1500 * 2048 * 4
     assert pc.cke_memory_lift_workspace_bytes(64, 4096, 64) == 0      # n not a multiple of 128
     assert pc.cke_memory_lift_workspace_bytes(0, 4096, 2048) == 0
 
@@ -409,8 +410,20 @@ def test_prepared_weight_plane_sizes():
     g = base_geom()
     assert pc.cke_xattn_populate_workspace_bytes(g) == (
         pc.cke_row_planes_bytes(1500, 512) + pc.cke_weight_planes_bytes(12, 512, 512))
+    slices = 4 * 1500 * 2048 * 4
     assert pc.cke_memory_lift_workspace_bytes(1500, 4096, 2048) == (
-        pc.cke_row_planes_bytes(1500, 4096) + pc.cke_weight_planes_bytes(1, 4096, 2048))
+        pc.cke_row_planes_bytes(1500, 4096) + pc.cke_weight_planes_bytes(1, 4096, 2048) + slices)
+    assert pc.cke_memory_lift_planes_workspace_bytes(1500, 4096, 2048) == (
+        pc.cke_row_planes_bytes(1500, 4096) + slices)
+    # split in two: 80 tiles of 192 x 256 in 4 slices would need 320 > 256 workgroups
+    assert pc.cke_memory_lift_planes_workspace_bytes(1500, 1024, 2560) == (
+        pc.cke_row_planes_bytes(1500, 1024) + 2 * 1500 * 2560 * 4)
+    # no split: enough tiles (256), a short k, or widths that take 128 x 128 tiles
+    assert pc.cke_memory_lift_planes_workspace_bytes(3000, 1024, 4096) == pc.cke_row_planes_bytes(3000, 1024)
+    assert pc.cke_memory_lift_planes_workspace_bytes(200, 256, 256) == pc.cke_row_planes_bytes(200, 256)
+    assert pc.cke_memory_lift_planes_workspace_bytes(130, 1024, 384) == pc.cke_row_planes_bytes(130, 1024)
+    assert pc.cke_memory_lift_planes_workspace_bytes(130, 1024, 64) == 0
+    assert pc.cke_memory_lift_planes_workspace_bytes(0, 1024, 256) == 0
 
 
 def test_prepared_planes_calls_reject_bad_arguments_before_launch():
@@ -445,7 +458,7 @@ def test_prepared_planes_calls_reject_bad_arguments_before_launch():
         finally:
             pc.cke_xattn_cache_destroy(h)
     w_need = pc.cke_weight_planes_bytes(1, 4096, 2048)
-    e_need = pc.cke_row_planes_bytes(1500, 4096)
+    e_need = pc.cke_memory_lift_planes_workspace_bytes(1500, 4096, 2048)
     for args in ((FAKE, 1500, 4096, FAKE, w_need, 2048, None, 0, FAKE, FAKE, e_need - 1),
                  (FAKE, 1500, 4096, FAKE, w_need - 1, 2048, None, 0, FAKE, FAKE, e_need),
                  (FAKE, 1500, 4096, FAKE + 16, w_need, 2048, None, 0, FAKE, FAKE, e_need),

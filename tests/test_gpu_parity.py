@@ -716,6 +716,9 @@ LIFT_CASES = [
 LIFT_CASES += [
     dict(rows=200, k_in=256, n=256, pos_rows=15),   # the split-planes path: k_in % 64, n % 128
     dict(rows=130, k_in=1024, n=384, pos_rows=0),
+    dict(rows=200, k_in=1024, n=256, pos_rows=15),  # too few 192 x 256 tiles: 4 k slices
+    dict(rows=45, k_in=2048, n=512, pos_rows=0),    # 4 k slices over a ragged row tile
+    dict(rows=1500, k_in=1024, n=2560, pos_rows=15),  # 80 tiles: 2 k slices
 ]
 
 
@@ -751,12 +754,16 @@ def test_memory_lift_from_prepared_weight_planes(c):
     ref = torch.empty((c["rows"], c["n"]), device=DEV)
     pc.cke_memory_lift_gelu(t32(x), t32(W), ref, pos_t, ws=torch.empty(need // 4, device=DEV))
     planes = pc.weight_planes([t32(W)])
-    rws = torch.full((pc.cke_row_planes_bytes(c["rows"], c["k_in"]) // 4,), float("nan"), device=DEV)
+    rws = torch.full((pc.cke_memory_lift_planes_workspace_bytes(c["rows"], c["k_in"], c["n"]) // 4,), float("nan"), device=DEV)
     out = torch.full((c["rows"], c["n"]), float("nan"), device=DEV)
     pc.cke_memory_lift_gelu_planes(t32(x), planes, c["n"], out, rws, pos=pos_t)
     torch.cuda.synchronize()
     assert torch.equal(out, ref)
     assert max_abs(to_np(out), oracle.lift_gelu(x, W, pos)) <= TOL["f32"]
+    again = torch.full_like(out, float("nan"))      # k slices are added in a fixed order
+    pc.cke_memory_lift_gelu_planes(t32(x), planes, c["n"], again, rws, pos=pos_t)
+    torch.cuda.synchronize()
+    assert torch.equal(again, out)
 
 
 def fp8_bracket(exact, absdot, dm):
