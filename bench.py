@@ -798,7 +798,12 @@ def main():
                           "xattn_calls_per_window": w.calls("xattn_decode")}))
         return
 
+    # wall-clock seconds of each phase: the GPU measurements and the host-only
+    # oracle baselines, so that a sampled GPU-busy figure can be read against them
+    phases = {}
+    t_start = time.perf_counter()
     head = measure(args.config, args, torch, pc, stream, extras=True)
+    phases[args.config + "_gpu"] = time.perf_counter() - t_start
     _progress("%s measured" % args.config)
     result = {
         "metric": METRIC,
@@ -824,18 +829,26 @@ def main():
     if also:
         result["also"] = {}
         for name in also:
+            t0 = time.perf_counter()
             blk = measure(name, args, torch, pc, stream, extras=False)
+            phases[name + "_gpu"] = time.perf_counter() - t0
             _progress("%s measured" % name)
             if not args.no_cpu_baseline:
+                t0 = time.perf_counter()
                 blk["cpu_baseline"] = cpu_baseline(name, args.cpu_seconds)
+                phases[name + "_cpu_baseline"] = time.perf_counter() - t0
                 _progress("%s oracle baseline timed" % name)
             result["also"][name] = blk
     if not args.no_cpu_baseline:
+        t0 = time.perf_counter()
         result["cpu_baseline"] = cpu_baseline(args.config, args.cpu_seconds)
-        _progress("%s oracle baseline timed" % args.config)
         if args.config in ("tiny", "base", "beam"):
             result["cpu_baseline_1thread"] = cpu_baseline(args.config, args.cpu_seconds,
                                                           threads=1)
+        phases[args.config + "_cpu_baseline"] = time.perf_counter() - t0
+        _progress("%s oracle baseline timed" % args.config)
+    phases["total"] = time.perf_counter() - t_start
+    result["phases_s"] = phases
     print(json.dumps(result))
 
 

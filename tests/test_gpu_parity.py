@@ -1296,3 +1296,64 @@ def test_graph_replays_of_decoder_layer_steps_match_eager(dtype):
         graph.replay()
         for a, b in zip(snapshot(), want):
             assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), rep
+
+
+def test_graph_replays_of_prepared_planes_lift_and_populate():
+    """The fp32 path bench.py times for a projector memory, captured once into
+    a HIP graph: the lift from prepared weight planes (split over k into four
+    slices here), the populate from prepared planes, one cross decode per
+    layer. Three replays, with eager resets and synchronisations in between,
+    reproduce the eager run bit for bit; the eager memory is checked against
+    the oracle's lift."""
+    B, T, dm, H, D, L, k_in = 8, 25, 256, 4, 64, 2, 1024
+    rows = B * T
+    assert pc.cke_memory_lift_planes_workspace_bytes(rows, k_in, dm) > pc.cke_row_planes_bytes(rows, k_in)
+    r = np.random.default_rng(77)
+    xn = (r.standard_normal((rows, k_in)) * 0.5).astype(np.float32)
+    wn = (r.standard_normal((k_in, dm)) * 0.03).astype(np.float32)
+    pn = (r.standard_normal((T, dm)) * 0.02).astype(np.float32)
+    x, Wl, pos = t32(xn), t32(wn), t32(pn)
+    WK = [t32(r.standard_normal((dm, dm)) * 0.06) for _ in range(L)]
+    WV = [t32(r.standard_normal((dm, dm)) * 0.06) for _ in range(L)]
+    cache = pc.XattnCache(L, B, T, dm, H, D, max_q=2, dtype=torch.float32)
+    E = torch.empty(B, T, dm, device=DEV)
+    lp = pc.weight_planes([Wl])
+    wp = cache.weight_planes(WK, WV)
+    lws = torch.empty(pc.cke_memory_lift_planes_workspace_bytes(rows, k_in, dm) // 4, device=DEV)
+    ews = cache.row_planes_workspace()
+    q = [t32(r.standard_normal((B, 2, H, D)) * 0.5) for _ in range(L)]
+    outs = [torch.empty(B, 2, H, D, device=DEV) for _ in range(L)]
+
+    def window():
+        pc.cke_memory_lift_gelu_planes(x, lp, dm, E.view(rows, dm), lws, pos=pos)
+        cache.populate_planes(E, wp, ews)
+        for l in range(L):
+            pc.cke_xattn_decode(q[l], cache, l, 0.125, outs[l])
+
+    def reset():
+        for t in [E, cache.k, cache.v, lws, ews] + outs:
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+
+    def snapshot():
+        torch.cuda.synchronize()
+        return [t.clone() for t in [E, cache.k, cache.v] + outs]
+
+    reset()
+    window()
+    want = snapshot()
+    assert max_abs(to_np(E).reshape(rows, dm), oracle.lift_gelu(xn, wn, pn)) <= TOL["f32"]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    reset()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s):
+        window()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        reset()
+        graph.replay()
+        got = snapshot()
+        for a, b in zip(got, want):
+            assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), rep
+        torch.cuda.synchronize()
