@@ -72,6 +72,10 @@ def parse():
                          "reported under 'also' (their windows and rooflines, no extras); "
                          "'none' for none")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the headline workload's other entry points (attention weights, decoder "
+                         "step, prefill, MALL-cold decode, launch floor): a kernel trace of such a run "
+                         "holds only the timed windows and the per-kind graphs")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="approximate CPU time budget of the oracle baseline sample")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -802,7 +806,7 @@ def main():
     # oracle baselines, so that a sampled GPU-busy figure can be read against them
     phases = {}
     t_start = time.perf_counter()
-    head = measure(args.config, args, torch, pc, stream, extras=True)
+    head = measure(args.config, args, torch, pc, stream, extras=not args.no_extras)
     phases[args.config + "_gpu"] = time.perf_counter() - t_start
     _progress("%s measured" % args.config)
     result = {
