@@ -1042,7 +1042,9 @@ def test_large_self_attention_every_position():
 
 def test_qformer_memory_lift_full_size():
     """The Q-Former workload's lift at full size (1500 x 4096 -> 2048, 15
-    position rows): every element against the oracle."""
+    position rows): every element against the oracle, per-tile split, split
+    planes in the workspace, and (the path bench.py times) the weight split
+    once into planes, with the product split over k in four slices."""
     g = synth.get("qformer")
     wt = synth.workload_tensors(g, ("X_lift", "W_lift", "pos"))
     rows = g.n_streams * g.mem_len
@@ -1054,6 +1056,15 @@ def test_qformer_memory_lift_full_size():
         pc.cke_memory_lift_gelu(t32(wt["X_lift"]), t32(wt["W_lift"]), out, t32(wt["pos"]), ws=ws)
         torch.cuda.synchronize()
         assert max_abs(to_np(out), want) <= TOL["f32"], ws is None
+    assert pc.cke_memory_lift_planes_workspace_bytes(rows, g.lift_in, g.d_model) > \
+        pc.cke_row_planes_bytes(rows, g.lift_in)                     # split over k
+    planes = pc.weight_planes([t32(wt["W_lift"])])
+    rws = torch.full((pc.cke_memory_lift_planes_workspace_bytes(rows, g.lift_in, g.d_model) // 4,),
+                     float("nan"), device=DEV)
+    out = torch.full((rows, g.d_model), float("nan"), device=DEV)
+    pc.cke_memory_lift_gelu_planes(t32(wt["X_lift"]), planes, g.d_model, out, rws, pos=t32(wt["pos"]))
+    torch.cuda.synchronize()
+    assert max_abs(to_np(out), want) <= TOL["f32"]
 
 
 def test_qformer_populate_and_decode_full_size():
@@ -1071,15 +1082,21 @@ def test_qformer_populate_and_decode_full_size():
     Kc, Vc = oracle.populate(E, wt["WK"], wt["WV"], g.n_heads, g.head_dim)
     ws = cache.populate_workspace()
     assert ws is not None
-    for w in (None, ws):      # per-tile split, then split planes in the workspace
+    WK, WV = [t32(x) for x in wt["WK"]], [t32(x) for x in wt["WV"]]
+    for mode in ("tile", "ws", "planes"):   # per-tile split, planes in the workspace, prepared planes
         _nan_fill(cache.k)
         _nan_fill(cache.v)
-        if w is not None:
-            w.fill_(float("nan"))
-        cache.populate(t32(E), [t32(x) for x in wt["WK"]], [t32(x) for x in wt["WV"]], ws=w)
+        if mode == "planes":
+            rws = cache.row_planes_workspace()
+            rws.fill_(float("nan"))
+            cache.populate_planes(t32(E), cache.weight_planes(WK, WV), rws)
+        else:
+            if mode == "ws":
+                ws.fill_(float("nan"))
+            cache.populate(t32(E), WK, WV, ws=ws if mode == "ws" else None)
         torch.cuda.synchronize()
-        assert max_abs(to_np(cache.k), Kc) <= TOL["f32"]
-        assert max_abs(to_np(cache.v), Vc) <= TOL["f32"]
+        assert max_abs(to_np(cache.k), Kc) <= TOL["f32"], mode
+        assert max_abs(to_np(cache.v), Vc) <= TOL["f32"], mode
     K32, V32 = Kc.astype(np.float32), Vc.astype(np.float32)
     cache.k.copy_(t32(K32))
     cache.v.copy_(t32(V32))
