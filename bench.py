@@ -67,7 +67,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--config", default="base", choices=sorted(synth.CONFIGS))
     ap.add_argument("--mode", default="graph", choices=["graph", "eager"])
-    ap.add_argument("--also", default="large",
+    ap.add_argument("--also", default="large,beam,qformer",
                     help="comma-separated workloads measured after the headline one and "
                          "reported under 'also' (their windows and rooflines, no extras); "
                          "'none' for none")
