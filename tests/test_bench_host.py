@@ -38,3 +38,44 @@ def test_graph_modes_refuse_to_run_under_counter_collection():
     assert bench.counter_collection_active({"ROCPROF_COUNTERS": "pmc: FETCH_SIZE"})
     assert not bench.counter_collection_active({"ROCPROF_COUNTER_COLLECTION": "0"})
     assert not bench.counter_collection_active({})
+
+
+class _W:
+    """Stand-in for bench.Workload with just what populate_report reads."""
+    def __init__(self, name, bf16, planes):
+        self.g = bench.synth.get(name)
+        self.bf16 = bf16
+        self.w_planes = object() if planes else None
+        self.pop_ws = object() if planes else None
+
+
+def test_populate_report_scores_the_issued_instruction_rate():
+    """fp32 products run as three bf16 MFMA products: `frac` is their issued
+    rate (3x the algorithmic FLOP) against the bf16 peak, with the algorithmic
+    rate against the fp32 peak beside it; bf16 populates use the bf16 peak."""
+    r = bench.populate_report(_W("base", False, True), 200.0, "f32")
+    assert abs(r["issued_tflops"] - 600.0) < 1e-9
+    assert abs(r["frac"] - 600.0 / bench.MFMA_PEAK_TFLOPS["bf16"]) < 1e-12
+    assert abs(r["algorithmic_frac_vs_f32_peak"] - 200.0 / bench.MFMA_PEAK_TFLOPS["f32"]) < 1e-12
+    assert "once when loaded" in r["mfma"] and r["target_met"] is False
+    r = bench.populate_report(_W("large", True, False), 1300.0, "bf16")
+    assert abs(r["frac"] - 1300.0 / bench.MFMA_PEAK_TFLOPS["bf16"]) < 1e-12
+    assert r["target_met"] is True
+    q = bench.populate_report(_W("qformer", False, True), 250.0, "f32")
+    assert "memory lift" in q["includes"]
+
+
+def test_phases_and_extras_flags_are_parsed():
+    old = sys.argv
+    try:
+        sys.argv = ["bench.py", "--no-extras", "--also", "none"]
+        a = bench.parse()
+    finally:
+        sys.argv = old
+    assert a.no_extras and a.also == "none"
+    sys.argv = ["bench.py"]
+    try:
+        d = bench.parse()
+    finally:
+        sys.argv = old
+    assert d.also == "large,beam,qformer" and not d.no_extras and d.gpus == 1
