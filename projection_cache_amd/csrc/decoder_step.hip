@@ -52,7 +52,14 @@ __global__ __launch_bounds__(kGemvWaves * 64) void gemv_kernel(const float* __re
     __shared__ float red[kGemvWaves][kGemvRowsMax * kGemvCols];
 
     const GemvOut o = blockIdx.y == 0 ? o0 : (blockIdx.y == 1 ? o1 : o2);
-    const int n0 = blockIdx.x * kGemvCols;
+    // Workgroup i runs on XCD i % 8. With the column blocks a multiple of 8,
+    // XCD x takes the contiguous x-th eighth of the columns, so for eight
+    // heads the columns of head h come out of XCD h, where the attention
+    // calls that read them place head h (the self-attention workgroup of
+    // head h and the cross-attention splits of head h run there).
+    const int nblk = gridDim.x;
+    const int blk = nblk % 8 == 0 ? (blockIdx.x % 8) * (nblk / 8) + blockIdx.x / 8 : blockIdx.x;
+    const int n0 = blk * kGemvCols;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int i = lane & 15, g = lane >> 4;
