@@ -745,7 +745,7 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // of a row XOR-swizzled by (m % (D/8)) and the two 8-byte halves of a piece
 // swapped when bit 3 of m is set, so that the 8-byte writes of 32 consecutive
 // rows and the 16-byte reads of consecutive pieces spread over the banks.
-template <int BM, int BN, int WGM, int WGN>
+template <int BM, int BN, int WGM, int WGN, int DC = 0>
 __device__ __forceinline__ void epilogue_t_lds(
     const GemmArgs& a,
     const f32x16 (&acc)[StreamTile<BM, BN, WGM, WGN>::NB][StreamTile<BM, BN, WGM, WGN>::MB], int m0, int p,
@@ -753,7 +753,10 @@ __device__ __forceinline__ void epilogue_t_lds(
 {
     using T = StreamTile<BM, BN, WGM, WGN>;
     constexpr int NT = T::NT;
-    const int lgD = __builtin_ctz(a.D);
+    // DC: head_dim known at compile time (0: read it from the arguments); with
+    // it every staging offset below folds to a per-lane base plus a constant
+    const int Dv = DC ? DC : a.D;
+    const int lgD = DC ? __builtin_ctz(DC) : __builtin_ctz(a.D);
     const int lgP = lgD - 3;              // log2 of 16-byte pieces per row
     const int PD = 1 << lgP;
 #pragma unroll
@@ -761,7 +764,7 @@ __device__ __forceinline__ void epilogue_t_lds(
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
             const int n = wn * T::WTN + nb * 32 + 8 * g + 4 * (lane >> 5);
-            const int j = n >> lgD, d = n & (a.D - 1);
+            const int j = n >> lgD, d = n & (Dv - 1);
             const int q = d >> 3, half = (d >> 2) & 1;
 #pragma unroll
             for (int mb = 0; mb < T::MB; ++mb) {
@@ -778,7 +781,7 @@ __device__ __forceinline__ void epilogue_t_lds(
     __syncthreads();
     const int l = p < a.L ? p : p - a.L;
     uint16_t* C = static_cast<uint16_t*>(p < a.L ? a.Kc : a.Vc);
-    const size_t TD = (size_t)a.T * a.D;
+    const size_t TD = (size_t)a.T * Dv;
     const int h0 = col0 >> lgD;
     const int b0 = m0 / a.T, t0 = m0 - b0 * a.T;
     const int tid = threadIdx.x;
@@ -798,7 +801,7 @@ __device__ __forceinline__ void epilogue_t_lds(
         }
         const int soff = (m << lgD) + ((q ^ (m & (PD - 1))) << 3);
         const bool swap = (m >> 3) & 1;
-        uint16_t* dst = C + ((size_t)(l * a.B + b) * a.H + h0) * TD + (size_t)t * a.D + q * 8;
+        uint16_t* dst = C + ((size_t)(l * a.B + b) * a.H + h0) * TD + (size_t)t * Dv + q * 8;
         for (int j = 0; j < heads; ++j) {
             uint4 v = *reinterpret_cast<const uint4*>(stage + soff + ((j * BM) << lgD));
             if (swap) { const uint32_t x = v.x, y = v.y; v.x = v.z; v.y = v.w; v.z = x; v.w = y; }
@@ -814,7 +817,7 @@ __device__ __forceinline__ void epilogue_t_lds(
 // by m % (D/16) and the four words of a piece rotated by XOR with
 // (m >> 2) % 4, so that the 4-byte writes of 32 consecutive rows spread over
 // the banks. `stage` is at least BM*BN bytes, free as for epilogue_t_lds.
-template <int BM, int BN, int WGM, int WGN>
+template <int BM, int BN, int WGM, int WGN, int DC = 0>
 __device__ __forceinline__ void epilogue_t_lds_fp8(
     const GemmArgs& a,
     const f32x16 (&acc)[StreamTile<BM, BN, WGM, WGN>::NB][StreamTile<BM, BN, WGM, WGN>::MB], int m0, int p,
@@ -822,7 +825,8 @@ __device__ __forceinline__ void epilogue_t_lds_fp8(
 {
     using T = StreamTile<BM, BN, WGM, WGN>;
     constexpr int NT = T::NT;
-    const int lgD = __builtin_ctz(a.D);
+    const int Dv = DC ? DC : a.D;         // DC as in epilogue_t_lds
+    const int lgD = DC ? __builtin_ctz(DC) : __builtin_ctz(a.D);
     const int lgP = lgD - 4;              // log2 of 16-byte pieces per row
     const int PD = 1 << lgP;
 #pragma unroll
@@ -830,7 +834,7 @@ __device__ __forceinline__ void epilogue_t_lds_fp8(
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
             const int n = wn * T::WTN + nb * 32 + 8 * g + 4 * (lane >> 5);
-            const int j = n >> lgD, d = n & (a.D - 1);
+            const int j = n >> lgD, d = n & (Dv - 1);
             const int q = d >> 4, wd = (d >> 2) & 3;
 #pragma unroll
             for (int mb = 0; mb < T::MB; ++mb) {
@@ -845,7 +849,7 @@ __device__ __forceinline__ void epilogue_t_lds_fp8(
     __syncthreads();
     const int l = p < a.L ? p : p - a.L;
     uint8_t* C = static_cast<uint8_t*>(p < a.L ? a.Kc : a.Vc);
-    const size_t TD = (size_t)a.T * a.D;
+    const size_t TD = (size_t)a.T * Dv;
     const int h0 = col0 >> lgD;
     const int b0 = m0 / a.T, t0 = m0 - b0 * a.T;
     const int tid = threadIdx.x;
@@ -863,7 +867,7 @@ __device__ __forceinline__ void epilogue_t_lds_fp8(
         }
         const int soff = (m << lgD) + ((q ^ (m & (PD - 1))) << 4);
         const int rot = (m >> 2) & 3;   // word k of the piece sits at k ^ rot
-        uint8_t* dst = C + ((size_t)(l * a.B + b) * a.H + h0) * TD + (size_t)t * a.D + q * 16;
+        uint8_t* dst = C + ((size_t)(l * a.B + b) * a.H + h0) * TD + (size_t)t * Dv + q * 16;
         for (int j = 0; j < heads; ++j) {
             uint4 v = *reinterpret_cast<const uint4*>(stage + soff + ((j * BM) << lgD));
             if (rot & 1) { uint32_t x = v.x; v.x = v.y; v.y = x; x = v.z; v.z = v.w; v.w = x; }
@@ -902,7 +906,7 @@ __device__ __forceinline__ void epilogue_t_lds_fp8(
 //    the barrier then makes every thread's loads visible;
 //  * the finished tile is staged through the ring (epilogue_t_lds, or
 //    epilogue_t_lds_fp8 for an fp8 cache) and written as whole rows.
-template <int BM, int BN, int NSLOT, bool FP8>
+template <int BM, int BN, int NSLOT, bool FP8, int DC = 0>
 __global__ __launch_bounds__(256) void populate_bf16_w4_kernel(GemmArgs a, int num_m, int num_n)
 {
     static_assert(BM == 256, "the LDS epilogue indexes 256 rows per head block");
@@ -993,10 +997,10 @@ __global__ __launch_bounds__(256) void populate_bf16_w4_kernel(GemmArgs a, int n
     static_assert(NSLOT * sizeof(StreamSlot<BM, BN>) >= BM * BN * 2, "ring too small to stage the tile");
     __syncthreads();
     if constexpr (FP8)
-        epilogue_t_lds_fp8<BM, BN, WGM, WGN>(a, acc, m0, p, col0, wm, wn, lane,
+        epilogue_t_lds_fp8<BM, BN, WGM, WGN, DC>(a, acc, m0, p, col0, wm, wn, lane,
                                              reinterpret_cast<uint8_t*>(&ring[0]));
     else
-        epilogue_t_lds<BM, BN, WGM, WGN>(a, acc, m0, p, col0, wm, wn, lane,
+        epilogue_t_lds<BM, BN, WGM, WGN, DC>(a, acc, m0, p, col0, wm, wn, lane,
                                          reinterpret_cast<uint16_t*>(&ring[0]));
 }
 
@@ -1574,8 +1578,12 @@ hipError_t launch_bf16_w4(const GemmArgs& g, hipStream_t st) {
     const int num_n = 2 * g.L * HD / BN;
     const int ntiles = num_m * num_n;
     const int grid = ((ntiles + 7) / 8) * 8;
-    hipLaunchKernelGGL((populate_bf16_w4_kernel<BM, BN, NSLOT, FP8>), dim3(grid), dim3(256), 0, st, g,
-                       num_m, num_n);
+    if (g.D == 64)   // the common head size: staging offsets fold at compile time
+        hipLaunchKernelGGL((populate_bf16_w4_kernel<BM, BN, NSLOT, FP8, 64>), dim3(grid), dim3(256), 0, st,
+                           g, num_m, num_n);
+    else
+        hipLaunchKernelGGL((populate_bf16_w4_kernel<BM, BN, NSLOT, FP8>), dim3(grid), dim3(256), 0, st, g,
+                           num_m, num_n);
     return hipGetLastError();
 }
 
