@@ -470,10 +470,12 @@ hipError_t launch_cross_nq(const XattnLaunch& a, hipStream_t st) {
     constexpr int NP = (NQ > 2 && sizeof(TE) < 4 && kCrossNP > 2) ? 2 : kCrossNP;
     const int n_bh = a.B * a.H;
     dim3 grid(8 * a.nsplit * ((n_bh + 7) / 8));
-    // streaming loads only for 16- and 8-bit caches: an fp32 cache of over
-    // 512 MB takes normal loads (one kernel variant fewer to build)
-    if (sizeof(TE) < 4 && a.stream_rows)
-        hipLaunchKernelGGL((xattn_partial_kernel<D, TE, NQ, kCrossWaves, NP, (sizeof(TE) < 4)>), grid,
+    // non-temporal buffer loads for fp32 caches and for 16- and 8-bit caches
+    // far larger than the MALL; normal loads otherwise, and for a head slab
+    // of 2 GB or more (buffer offsets are 32-bit)
+    const bool slab_ok = (size_t)a.T * a.D * sizeof(TE) < ((size_t)1 << 31) - 16;
+    if (slab_ok && (sizeof(TE) == 4 || a.stream_rows))
+        hipLaunchKernelGGL((xattn_partial_kernel<D, TE, NQ, kCrossWaves, NP, true>), grid,
                            dim3(kCrossWaves * 64), 0, st, a.q,
                            static_cast<const TE*>(a.K), static_cast<const TE*>(a.V), a.out,
                            a.part, a.stats, a.nq, a.max_q, a.H, a.T, a.nsplit, a.chunk, n_bh,

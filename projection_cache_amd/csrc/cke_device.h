@@ -45,9 +45,7 @@ __device__ __forceinline__ float round_to_bf16(float x) { return (float)(__bf16)
 // A lane's 16-byte share of a cached row is kept packed in registers (4 fp32,
 // 8 bf16 or 16 fp8 values) and widened to fp32 only where it is used, so bf16 rows
 // cost half the registers of fp32 ones. With STREAM the load is marked
-// non-temporal: right for a cache far larger than the 256 MB MALL, whose rows
-// can never be reused from it (8% faster on the Large 123 MB slab), wrong for
-// one that stays resident between decode steps (7% slower at Whisper Base).
+// non-temporal (load_tile issues such rows as buffer loads, see there).
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 template <bool STREAM = false>
 __device__ __forceinline__ uint4 load16(const void* __restrict__ p) {
@@ -210,12 +208,38 @@ __device__ __forceinline__ void load_tile(const TE* __restrict__ K, const TE* __
                                           uint4 (&kb)[NP], uint4 (&vb)[NP])
 {
     using RM = RowMap<D, TE>;
+    if constexpr (STREAM && sizeof(TE) != 2) {
+        // fp32 and fp8 rows: buffer loads from the wave-uniform K and V bases,
+        // with 32-bit byte offsets (the caller keeps a head's slab under 2 GB),
+        // marked non-temporal. Measured on the cross-attention call,
+        // alternating on one box: Whisper Base 6.47 us against 6.74 with
+        // normal global loads (fp32 rows that stay in the MALL between decode
+        // steps; non-temporal global loads had been slower still), Large over
+        // an fp8 cache 16.23 against 16.33 us with non-temporal global loads.
+        // bf16 rows keep those global loads (the branch below): Large 24.46
+        // against 24.73 us with buffer loads.
+        constexpr int kPolicyNT = 2;
+        const __amdgpu_buffer_rsrc_t rk =
+            __builtin_amdgcn_make_buffer_rsrc((void*)K, (short)0, 0x7ffffff0, 0x00020000);
+        const __amdgpu_buffer_rsrc_t rv =
+            __builtin_amdgcn_make_buffer_rsrc((void*)V, (short)0, 0x7ffffff0, 0x00020000);
 #pragma unroll
-    for (int p = 0; p < NP; ++p) {
-        const int row = min(base + p * RM::kKPW + grp, r_safe);
-        const size_t off = (size_t)row * D + sub * RM::kVec;
-        kb[p] = load16<STREAM>(K + off);
-        vb[p] = load16<STREAM>(V + off);
+        for (int p = 0; p < NP; ++p) {
+            const int row = min(base + p * RM::kKPW + grp, r_safe);
+            const int off = (row * D + sub * RM::kVec) * (int)sizeof(TE);
+            const auto k4 = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, kPolicyNT);
+            const auto v4 = __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, kPolicyNT);
+            kb[p] = make_uint4(k4[0], k4[1], k4[2], k4[3]);
+            vb[p] = make_uint4(v4[0], v4[1], v4[2], v4[3]);
+        }
+    } else {
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+            const int row = min(base + p * RM::kKPW + grp, r_safe);
+            const size_t off = (size_t)row * D + sub * RM::kVec;
+            kb[p] = load16<STREAM>(K + off);
+            vb[p] = load16<STREAM>(V + off);
+        }
     }
 }
 
