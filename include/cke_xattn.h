@@ -97,8 +97,11 @@ size_t cke_xattn_layer_offset_bytes(const cke_xattn_geom* g, int layer);
 /* Bytes of device workspace a cache needs: split-key partial results, fp32
  * [B][max_q][H][splits][D+2], then (256-byte aligned) per-head softmax
  * statistics, fp32 [B][max_q][H][2], that only cke_xattn_decode_weights
- * writes (at least 256 bytes in all). Every call writes what it reads, so the
- * workspace needs no initialisation. Returns 0 for an invalid geometry. */
+ * writes, then (256-byte aligned, when splits > 1) one 32-bit arrival
+ * counter per (stream, head), 128 bytes apart (at least 256 bytes in all).
+ * The workspace needs no initialisation: populate zeroes the counters and
+ * every decode leaves them at zero; it belongs to one cache handle. Returns 0
+ * for an invalid geometry. */
 size_t cke_xattn_workspace_bytes(const cke_xattn_geom* g);
 
 /* Number of key splits a decode call of this geometry uses (fixed per
@@ -120,6 +123,25 @@ int cke_xattn_invalidate(cke_xattn_cache* c);
 
 /* 1 if populated and not invalidated since, 0 otherwise (or for NULL). */
 int cke_xattn_is_ready(const cke_xattn_cache* c);
+
+/* Where a split decode merges its per-split partial results (C-Kernel-Engine,
+ * "Whisper: Trace One Encoder Tensor into Every Decoder Layer", "View 2":
+ * one query against all key rows, here split over workgroups and merged with
+ * the online-softmax rescaling).
+ *   mode 1 (default): in the split kernel's own launch, by the last workgroup
+ *          of each head to finish, on handles whose creation verified that
+ *          the device keeps workgroups i and i + 8 of a launch on one XCD
+ *          (a probe, once per device); otherwise, and for merges needing
+ *          more than 32 KB of LDS, as in mode 0;
+ *   mode 0: a second, small kernel on the same stream.
+ * Both give identical bits. Process-wide; affects calls made (or captured)
+ * after it. Returns the previous mode, or CKE_EINVAL for another value. */
+int cke_xattn_set_merge_mode(int mode);
+
+/* 1 if a decode of n_q queries on c would merge in the split kernel's launch
+ * under the current mode, 0 otherwise (including NULL, unsplit geometries and
+ * n_q outside [1, max_q]). */
+int cke_xattn_merges_in_launch(const cke_xattn_cache* c, int n_q);
 
 /* Prefill: fill every layer's K and V slab from encoder memory E.
  *   E   device, [B][T][d_model], e_dtype

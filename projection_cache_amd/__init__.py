@@ -77,6 +77,10 @@ _lib.cke_xattn_invalidate.restype = _I
 _lib.cke_xattn_invalidate.argtypes = [_P]
 _lib.cke_xattn_is_ready.restype = _I
 _lib.cke_xattn_is_ready.argtypes = [_P]
+_lib.cke_xattn_set_merge_mode.restype = _I
+_lib.cke_xattn_set_merge_mode.argtypes = [_I]
+_lib.cke_xattn_merges_in_launch.restype = _I
+_lib.cke_xattn_merges_in_launch.argtypes = [_P, _I]
 _lib.cke_xattn_populate.restype = _I
 _lib.cke_xattn_populate.argtypes = [_P, _P, _I, ctypes.POINTER(_P), ctypes.POINTER(_P), _I, _P]
 _lib.cke_xattn_populate_workspace_bytes.restype = _SZ
@@ -135,7 +139,8 @@ EXPORTED = ["cke_xattn_region_bytes", "cke_xattn_layer_offset_bytes",
             "cke_decoder_step_scratch_bytes", "cke_decoder_layer_step_noalloc",
             "cke_memory_lift_gelu", "cke_weight_planes_bytes", "cke_weight_planes",
             "cke_row_planes_bytes", "cke_xattn_populate_planes", "cke_memory_lift_gelu_planes",
-            "cke_memory_lift_planes_workspace_bytes",
+            "cke_memory_lift_planes_workspace_bytes", "cke_xattn_set_merge_mode",
+            "cke_xattn_merges_in_launch",
             "cke_last_error", "cke_version"]
 
 
@@ -255,6 +260,19 @@ def cke_xattn_invalidate(handle) -> None:
 
 def cke_xattn_is_ready(handle) -> bool:
     return bool(_lib.cke_xattn_is_ready(handle))
+
+
+def cke_xattn_set_merge_mode(mode: int) -> int:
+    """1: split decodes merge in their own launch where the device allows;
+    0: always in a second kernel. Returns the previous mode."""
+    rc = _lib.cke_xattn_set_merge_mode(int(mode))
+    if rc < 0:
+        raise CkeError(rc, cke_last_error())
+    return rc
+
+
+def cke_xattn_merges_in_launch(cache, n_q: int) -> bool:
+    return bool(_lib.cke_xattn_merges_in_launch(_handle(cache), int(n_q)))
 
 
 def _handle(cache):

@@ -33,30 +33,143 @@ namespace cke {
 namespace {
 
 // ----------------------------------------------------------------- cross
+// Combines the nsplit partials of each (query, dim) of head (b, h):
+//   M = max_s M_s,  L = sum_s L_s 2^(M_s - M),  out = sum_s A_s 2^(M_s - M) / L
+// GL = merge_lanes(nsplit) adjacent lanes share one output o = (query, dim);
+// lane g of them takes splits s = g, g+GL, ... (at most kMergePer). It loads
+// (M_s, L_s, A_s[d]) of all its splits at once -- clamped, branch-free
+// addresses, so the loads cost one memory round trip -- takes their max
+// first, so that the exponentials are independent of each other (no chain of
+// running-max updates), and sums L_s and A_s scaled by them in ascending s.
+// The GL lanes then combine in xor-butterfly rounds (lane distance 1, 2, 4),
+// with no LDS and no barrier; lane g = 0 writes. The same arithmetic in the
+// same order whichever kernel runs it, so both merges give identical bits.
+// L2 = true when the partials were written during this same launch by other
+// workgroups of this XCD: they are then read with the L1 bypassed (buffer
+// loads with sc0), from the XCD's L2. Every lane of a wave runs the loop the
+// same number of times (the shuffles need them all).
+template <int D, bool L2>
+__device__ __forceinline__ void merge_head(const float* __restrict__ part, float* __restrict__ out,
+                                           float* __restrict__ stats, int nq, int max_q, int H,
+                                           int nsplit, int b, int h, int tid, int nthreads)
+{
+    const int GL = merge_lanes(nsplit);
+    const int total = nq * D * GL;
+    const int lane = tid & 63;
+    constexpr int kPolicySC0 = 1;
+    const __amdgpu_buffer_rsrc_t rp =
+        __builtin_amdgcn_make_buffer_rsrc((void*)part, (short)0, 0x7ffffff0, 0x00020000);
+    for (int base = tid - lane; base < total; base += nthreads) {
+        const bool live = base + lane < total;
+        const int idx = min(base + lane, total - 1);
+        const int o = idx / GL, g = idx % GL;
+        const int i = o / D, d = o % D;
+        const size_t p0 = (((size_t)b * max_q + i) * H + h) * (size_t)nsplit * (D + 2);
+        float pm[kMergePer], pl[kMergePer], pa[kMergePer];
+#pragma unroll
+        for (int j = 0; j < kMergePer; ++j) {
+            const int s = min(g + j * GL, nsplit - 1);
+            const size_t w = p0 + (size_t)s * (D + 2);
+            if constexpr (L2) {
+                const int off = (int)(w * sizeof(float));   // the caller keeps partials under 2 GB
+                pm[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rp, off, 0, kPolicySC0));
+                pl[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rp, off + 4, 0, kPolicySC0));
+                pa[j] = __uint_as_float(
+                    __builtin_amdgcn_raw_buffer_load_b32(rp, off + (2 + d) * 4, 0, kPolicySC0));
+            } else {
+                pm[j] = part[w];
+                pl[j] = part[w + 1];
+                pa[j] = part[w + 2 + d];
+            }
+        }
+        // every lane has split g < GL <= nsplit, and every split has at least
+        // one row, so m is finite
+        float m = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < kMergePer; ++j)
+            if (g + j * GL < nsplit) m = fmaxf(m, pm[j]);
+        float l = 0.f, a = 0.f;
+#pragma unroll
+        for (int j = 0; j < kMergePer; ++j) {
+            const float e = (g + j * GL < nsplit) ? fast_exp2(pm[j] - m) : 0.f;
+            l = fmaf(pl[j], e, l);
+            a = fmaf(pa[j], e, a);
+        }
+        for (int k = 1; k < GL; k <<= 1) {
+            const float m2 = __shfl_xor(m, k), l2 = __shfl_xor(l, k), a2 = __shfl_xor(a, k);
+            const float mn = fmaxf(m, m2);
+            const float e1 = fast_exp2(m - mn), e2 = fast_exp2(m2 - mn);
+            l = fmaf(l, e1, l2 * e2);
+            a = fmaf(a, e1, a2 * e2);
+            m = mn;
+        }
+        if (live && g == 0) {
+            out[(((size_t)b * nq + i) * H + h) * D + d] = a / l;
+            if (stats && d == 0) {
+                float* st2 = stats + (((size_t)b * max_q + i) * H + h) * 2;
+                st2[0] = m;
+                st2[1] = l;
+            }
+        }
+    }
+}
+
+// The second launch of a split decode: merges every head from the partials
+// the first kernel left in memory. Z workgroups per head each take a
+// contiguous share of its (output, lane) pairs; one-dimensional grid of
+// 8 * Z * ceil(B*H / 8) workgroups placed like the split kernel's, so that
+// every workgroup of head hb runs on XCD hb % 8, where that head's partials
+// were written.
+template <int D>
+__global__ __launch_bounds__(256) void xattn_merge_kernel(
+    const float* __restrict__ part, float* __restrict__ out, float* __restrict__ stats, int nq,
+    int max_q, int H, int nsplit, int n_bh, int Z)
+{
+    const int xcd = blockIdx.x % 8, k_on_xcd = blockIdx.x / 8;
+    const int head_slot = k_on_xcd / Z;
+    const int z = k_on_xcd - head_slot * Z;
+    const int hb = xcd + 8 * head_slot;
+    if (hb >= n_bh) return;
+    merge_head<D, false>(part, out, stats, nq, max_q, H, nsplit, hb / H, hb % H,
+                         z * blockDim.x + threadIdx.x, Z * blockDim.x);
+}
+
 // Grid: 8 * nsplit * ceil(B*H / 8) workgroups in one dimension. Workgroup i
 // runs on XCD i % 8 (the dispatcher deals workgroups to the eight XCDs in
-// turn), and every split of head hb = b*H + h is placed on XCD hb % 8, the
-// XCD on which xattn_merge_kernel (grid (H, B)) merges that head: the
-// partials it reads were written through its own L2 (Whisper Base: 6.73
-// against 7.05 us per call with the splits spread over all XCDs). Split s of
-// head hb covers memory rows [s*chunk, min(T, (s+1)*chunk)) for all nq
+// turn), and every split of head hb = b*H + h is placed on XCD hb % 8. Split
+// s of head hb covers memory rows [s*chunk, min(T, (s+1)*chunk)) for all nq
 // queries of stream b, so the queries of one stream share every K/V read.
 // With nsplit == 1 it writes `out` directly; otherwise it writes its partial
-// (max, sum, acc[D]) per query to `part` and xattn_merge_kernel, launched
-// next on the same stream, combines them.
+// (max, sum, acc[D]) per query to `part`, and the partials are merged:
 //
-// Why a second launch: merging inside this kernel needs the partials of
-// other workgroups, which run on other XCDs with their own L2. A
+//   * tickets != nullptr: by the last workgroup of the head to finish, in
+//     this launch. All splits of a head share one XCD, hence one L2, which is
+//     where they meet: each workgroup waits until L2 has acknowledged its
+//     partial stores (s_waitcnt vmcnt(0)), then takes a ticket with an atomic
+//     add that executes in that L2 (no device-scope bit); the workgroup that
+//     draws ticket nsplit-1 resets the counter to 0 for the next call and
+//     merges, reading the partials past its L1 (sc0) from the same L2. No
+//     workgroup waits for another, and nothing crosses XCDs. This relies on
+//     the dispatcher's placement (workgroups i and i + 8 share an XCD), which
+//     the host verifies once per device before it passes tickets.
+//   * tickets == nullptr: by xattn_merge_kernel, launched next on the same
+//     stream; its workgroup hb runs on XCD hb % 8 as well, so the partials
+//     it reads were written through its own L2 (Whisper Base: 6.73 against
+//     7.05 us per call with the splits spread over all XCDs).
+//
+// Both merges run merge_head, so they give identical bits. Device-scope
+// variants of the in-launch merge were slower than the second launch: a
 // release/acquire pair per workgroup is a whole-L2 writeback + invalidate on
-// gfx950, and a fence-free variant (tagged 64-bit partial words with
-// device-scope atomic loads and stores, last arrival by ticket) pays several
-// device-scope round trips on its tail; both measured slower than a second
-// small kernel, whose inputs are coherent at the kernel boundary.
+// gfx950 (54 us per Whisper Base call), and tagged 64-bit partial words with
+// device-scope atomics and a device-scope ticket paid memory round trips on
+// the ticket (32 adds serialised where the counter lives) and on the merge's
+// loads (8.2 against 6.9 us).
 template <int D, typename TE, int NQ, int NW, int NP, bool STREAM>
 __global__ __launch_bounds__(NW * 64) void xattn_partial_kernel(
     const float* __restrict__ q, const TE* __restrict__ Kl, const TE* __restrict__ Vl,
     float* __restrict__ out, float* __restrict__ part, float* __restrict__ stats,
-    int nq, int max_q, int H, int T, int nsplit, int chunk, int n_bh, float sl2)
+    unsigned* __restrict__ tickets, int nq, int max_q, int H, int T, int nsplit, int chunk,
+    int n_bh, float sl2)
 {
     using RM = RowMap<D, TE>;
     constexpr int VEC = RM::kVec, LPK = RM::kLPK, KPW = RM::kKPW;
@@ -113,81 +226,22 @@ __global__ __launch_bounds__(NW * 64) void xattn_partial_kernel(
         float* p = part + ((((size_t)b * max_q + i) * H + h) * nsplit + split) * (D + 2);
         p[k] = k == 0 ? sM[i] : (k == 1 ? sL[i] : sA[i * D + k - 2]);
     }
-}
-
-// Grid: (H, B). Combines the nsplit partials of each (stream, query, head)
-// of one head:
-//   M = max_s M_s,  L = sum_s L_s 2^(M_s - M),  out = sum_s A_s 2^(M_s - M) / L
-// Thread (o, g), o = (query, dim), g < G = ceil(nsplit / kMergeBatch), takes
-// splits s = g, g+G, ... (at most kMergeBatch of them). It loads (M_s, L_s,
-// A_s[d]) of all its splits at once -- clamped, branch-free addresses, so
-// every load is in flight together and the merge costs one memory round
-// trip -- and folds them in ascending s with the running-max update. Groups
-// are then combined through LDS in ascending g (deterministic). Dynamic LDS:
-// 3 floats per (o, g).
-constexpr int kMergeBatch = 16;
-
-template <int D>
-__global__ __launch_bounds__(1024) void xattn_merge_kernel(
-    const float* __restrict__ part, float* __restrict__ out, float* __restrict__ stats, int nq,
-    int max_q, int H, int nsplit)
-{
-    extern __shared__ float smem[];
-    const int h = blockIdx.x, b = blockIdx.y;
-    const int n_out = nq * D;
-    const int G = (nsplit + kMergeBatch - 1) / kMergeBatch;
-    float* sm = smem;
-    float* sl = smem + n_out * G;
-    float* sa = smem + 2 * n_out * G;
-    for (int idx = threadIdx.x; idx < n_out * G; idx += blockDim.x) {
-        const int o = idx % n_out, g = idx / n_out;
-        const int i = o / D, d = o % D;
-        const float* p0 = part + (((size_t)b * max_q + i) * H + h) * (size_t)nsplit * (D + 2);
-        float pm[kMergeBatch], pl[kMergeBatch], pa[kMergeBatch];
-#pragma unroll
-        for (int j = 0; j < kMergeBatch; ++j) {
-            const int s = min(g + j * G, nsplit - 1);
-            const float* p = p0 + (size_t)s * (D + 2);
-            pm[j] = p[0];
-            pl[j] = p[1];
-            pa[j] = p[2 + d];
-        }
-        float m = -INFINITY, l = 0.f, a = 0.f;
-#pragma unroll
-        for (int j = 0; j < kMergeBatch; ++j) {
-            if (g + j * G < nsplit) {
-                const float mn = fmaxf(m, pm[j]);
-                const float f_old = fast_exp2(m - mn);   // m = -inf on the first split: 0
-                const float f_new = fast_exp2(pm[j] - mn);
-                l = fmaf(l, f_old, pl[j] * f_new);
-                a = fmaf(a, f_old, pa[j] * f_new);
-                m = mn;
-            }
-        }
-        sm[idx] = m;
-        sl[idx] = l;
-        sa[idx] = a;
+    if (!tickets) return;
+    // this thread's partial stores acknowledged by L2 (the clobber keeps the
+    // compiler from moving any store below the wait)
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    __shared__ int s_last;
+    if (threadIdx.x == 0) {
+        unsigned* t = tickets + (size_t)hb * (kTicketBytes / sizeof(unsigned));
+        const unsigned n = __hip_atomic_fetch_add(t, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        const int last = n == (unsigned)nsplit - 1u;
+        if (last) __hip_atomic_store(t, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        s_last = last;
     }
     __syncthreads();
-    for (int o = threadIdx.x; o < n_out; o += blockDim.x) {
-        float m = -INFINITY, l = 0.f, a = 0.f;
-        for (int g = 0; g < G; ++g) {
-            const float mg = sm[g * n_out + o];
-            const float mn = fmaxf(m, mg);
-            const float f_old = fast_exp2(m - mn);
-            const float f_new = fast_exp2(mg - mn);
-            l = fmaf(l, f_old, sl[g * n_out + o] * f_new);
-            a = fmaf(a, f_old, sa[g * n_out + o] * f_new);
-            m = mn;
-        }
-        const int i = o / D, d = o % D;
-        out[(((size_t)b * nq + i) * H + h) * D + d] = a / l;
-        if (stats && d == 0) {
-            float* st2 = stats + (((size_t)b * max_q + i) * H + h) * 2;
-            st2[0] = m;
-            st2[1] = l;
-        }
-    }
+    if (!s_last) return;
+    merge_head<D, true>(part, out, stats, nq, max_q, H, nsplit, b, h, threadIdx.x, NW * 64);
 }
 
 // Short memories (e.g. 15-frame blocks): one wave per (stream, head), NW of
@@ -428,9 +482,6 @@ __global__ __launch_bounds__(NW * 64) void selfattn_prefill_kernel(
 
 // ------------------------------------------------------------- launchers
 
-#ifndef CKE_CROSS_WAVES
-#define CKE_CROSS_WAVES 4
-#endif
 #ifndef CKE_CROSS_NP
 #define CKE_CROSS_NP 4
 #endif
@@ -440,7 +491,6 @@ __global__ __launch_bounds__(NW * 64) void selfattn_prefill_kernel(
 #ifndef CKE_SELF_NP
 #define CKE_SELF_NP 4
 #endif
-constexpr int kCrossWaves = CKE_CROSS_WAVES;  // waves per cross-decode workgroup
 constexpr int kCrossNP = CKE_CROSS_NP;        // row passes per load tile
 constexpr int kSelfWaves = CKE_SELF_WAVES;
 constexpr int kSelfNP = CKE_SELF_NP;
@@ -470,6 +520,8 @@ hipError_t launch_cross_nq(const XattnLaunch& a, hipStream_t st) {
     constexpr int NP = (NQ > 2 && sizeof(TE) < 4 && kCrossNP > 2) ? 2 : kCrossNP;
     const int n_bh = a.B * a.H;
     dim3 grid(8 * a.nsplit * ((n_bh + 7) / 8));
+    unsigned* tickets =
+        (a.tickets && merge_in_launch_fits(a.nq, D, a.nsplit, n_bh, a.max_q)) ? a.tickets : nullptr;
     // non-temporal buffer loads for fp32 caches and for 16- and 8-bit caches
     // far larger than the MALL; normal loads otherwise, and for a head slab
     // of 2 GB or more (buffer offsets are 32-bit)
@@ -478,22 +530,21 @@ hipError_t launch_cross_nq(const XattnLaunch& a, hipStream_t st) {
         hipLaunchKernelGGL((xattn_partial_kernel<D, TE, NQ, kCrossWaves, NP, true>), grid,
                            dim3(kCrossWaves * 64), 0, st, a.q,
                            static_cast<const TE*>(a.K), static_cast<const TE*>(a.V), a.out,
-                           a.part, a.stats, a.nq, a.max_q, a.H, a.T, a.nsplit, a.chunk, n_bh,
-                           a.scale * kLog2e);
+                           a.part, a.stats, tickets, a.nq, a.max_q, a.H, a.T, a.nsplit, a.chunk,
+                           n_bh, a.scale * kLog2e);
     else
         hipLaunchKernelGGL((xattn_partial_kernel<D, TE, NQ, kCrossWaves, NP, false>), grid,
                            dim3(kCrossWaves * 64), 0, st, a.q,
                            static_cast<const TE*>(a.K), static_cast<const TE*>(a.V), a.out,
-                           a.part, a.stats, a.nq, a.max_q, a.H, a.T, a.nsplit, a.chunk, n_bh,
-                           a.scale * kLog2e);
+                           a.part, a.stats, tickets, a.nq, a.max_q, a.H, a.T, a.nsplit, a.chunk,
+                           n_bh, a.scale * kLog2e);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess || a.nsplit == 1) return e;
-    const int G = (a.nsplit + kMergeBatch - 1) / kMergeBatch;
-    const int pairs = a.nq * D * G;
-    const int threads = pairs >= 1024 ? 1024 : ((pairs + 63) / 64) * 64;
-    const size_t lds = (size_t)3 * pairs * sizeof(float);
-    hipLaunchKernelGGL((xattn_merge_kernel<D>), dim3(a.H, a.B), dim3(threads), lds, st, a.part,
-                       a.out, a.stats, a.nq, a.max_q, a.H, a.nsplit);
+    if (e != hipSuccess || a.nsplit == 1 || tickets) return e;
+    const int lanes = a.nq * D * merge_lanes(a.nsplit);
+    const int threads = lanes >= 256 ? 256 : ((lanes + 63) / 64) * 64;
+    const int Z = (lanes + threads - 1) / threads;
+    hipLaunchKernelGGL((xattn_merge_kernel<D>), dim3(8 * Z * ((n_bh + 7) / 8)), dim3(threads), 0, st,
+                       a.part, a.out, a.stats, a.nq, a.max_q, a.H, a.nsplit, n_bh, Z);
     return hipGetLastError();
 }
 

@@ -27,6 +27,7 @@ struct cke_xattn_cache {
     int ready;
     int nsplit;
     int chunk;
+    int merge_in_launch;   // split decode merges in its own launch (device placement verified)
 };
 
 namespace {
@@ -122,7 +123,9 @@ constexpr size_t kAlign = 256;
 
 // Workspace: fp32 split partials [B][max_q][H][nsplit][D+2], then (256-byte
 // aligned) fp32 per-head statistics [B][max_q][H][2] that a decode call
-// writes only when attention weights are requested.
+// writes only when attention weights are requested, then (256-byte aligned,
+// split geometries only) one arrival counter per head, 128 bytes apart,
+// which populate zeroes and every decode leaves at zero.
 size_t partial_words(const cke_xattn_geom* g, int nsplit) {
     return (size_t)g->n_streams * g->max_q * g->n_heads * (size_t)nsplit * (g->head_dim + 2);
 }
@@ -131,6 +134,46 @@ size_t stats_offset_bytes(const cke_xattn_geom* g, int nsplit) {
 }
 size_t stats_bytes(const cke_xattn_geom* g) {
     return (size_t)g->n_streams * g->max_q * g->n_heads * 2 * sizeof(float);
+}
+size_t tickets_offset_bytes(const cke_xattn_geom* g, int nsplit) {
+    return (stats_offset_bytes(g, nsplit) + stats_bytes(g) + kAlign - 1) / kAlign * kAlign;
+}
+size_t tickets_bytes(const cke_xattn_geom* g, int nsplit) {
+    return nsplit > 1 ? (size_t)g->n_streams * g->n_heads * cke::kTicketBytes : 0;
+}
+unsigned* tickets_of(const cke_xattn_cache* c) {
+    return reinterpret_cast<unsigned*>(static_cast<char*>(c->ws) + tickets_offset_bytes(&c->g, c->nsplit));
+}
+
+// In-launch merge of split decodes: process-wide switch (1 = where the
+// device allows, 0 = always the second kernel) and the per-device result of
+// the placement probe (0 = not yet probed, 1 = fails, 2 = holds).
+std::atomic<int> g_merge_mode{1};
+constexpr int kProbeDevices = 64;
+std::atomic<int> g_placement[kProbeDevices];
+std::mutex g_placement_mu;
+
+bool xcd_placement_ok() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kProbeDevices) {
+        (void)hipGetLastError();
+        return false;
+    }
+    int st = g_placement[dev].load(std::memory_order_acquire);
+    if (st) return st == 2;
+    std::lock_guard<std::mutex> lock(g_placement_mu);
+    st = g_placement[dev].load(std::memory_order_relaxed);
+    if (!st) {
+        st = cke::probe_xcd_placement() ? 2 : 1;
+        g_placement[dev].store(st, std::memory_order_release);
+    }
+    return st == 2;
+}
+
+// Zero the arrival counters (after a populate, before the first decode).
+hipError_t reset_tickets(const cke_xattn_cache* c, hipStream_t st) {
+    if (!c->merge_in_launch) return hipSuccess;
+    return cke::launch_zero_words(tickets_of(c), tickets_bytes(&c->g, c->nsplit) / sizeof(unsigned), st);
 }
 
 }  // namespace
@@ -166,7 +209,7 @@ size_t cke_xattn_workspace_bytes(const cke_xattn_geom* g) {
     if (check_geom(g) != CKE_OK) return 0;
     int s, c;
     split_plan(g, &s, &c);
-    const size_t b = stats_offset_bytes(g, s) + stats_bytes(g);
+    const size_t b = tickets_offset_bytes(g, s) + tickets_bytes(g, s);
     return b < kAlign ? kAlign : b;
 }
 
@@ -189,6 +232,9 @@ int cke_xattn_cache_create(const cke_xattn_geom* g, void* k_dev, void* v_dev, vo
     c->ws = ws_dev;
     c->ready = 0;
     split_plan(g, &c->nsplit, &c->chunk);
+    // split geometries: verify (once per device) that the dispatcher keeps
+    // workgroups i and i + 8 on one XCD, which the in-launch merge relies on
+    c->merge_in_launch = c->nsplit > 1 && xcd_placement_ok();
     *out = c;
     return CKE_OK;
 }
@@ -202,6 +248,18 @@ int cke_xattn_invalidate(cke_xattn_cache* c) {
 }
 
 int cke_xattn_is_ready(const cke_xattn_cache* c) { return c ? c->ready : 0; }
+
+int cke_xattn_set_merge_mode(int mode) {
+    if (mode != 0 && mode != 1) return fail(CKE_EINVAL, "merge mode must be 0 or 1 (got %d)", mode);
+    return g_merge_mode.exchange(mode);
+}
+
+int cke_xattn_merges_in_launch(const cke_xattn_cache* c, int n_q) {
+    if (!c || !c->merge_in_launch || !g_merge_mode.load(std::memory_order_relaxed)) return 0;
+    if (n_q < 1 || n_q > c->g.max_q) return 0;
+    return cke::merge_in_launch_fits(n_q, c->g.head_dim, c->nsplit,
+                                     (long long)c->g.n_streams * c->g.n_heads, c->g.max_q) ? 1 : 0;
+}
 
 }  // extern "C"
 
@@ -267,6 +325,7 @@ int populate_impl(cke_xattn_cache* c, const void* E, int e_dtype, const void* co
     c->ready = 0;
     hipError_t e = need ? cke::launch_populate_planes(a, ws, static_cast<hipStream_t>(stream))
                         : cke::launch_populate(a, static_cast<hipStream_t>(stream));
+    if (e == hipSuccess) e = reset_tickets(c, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(CKE_EDEVICE, "populate launch failed: %s", hipGetErrorString(e));
     c->ready = 1;
     return CKE_OK;
@@ -349,6 +408,7 @@ int cke_xattn_populate_planes(cke_xattn_cache* c, const float* E, const void* w_
     populate_geom(c, E, &a);
     c->ready = 0;
     hipError_t e = cke::launch_populate_from_planes(a, w_planes, ws, static_cast<hipStream_t>(stream));
+    if (e == hipSuccess) e = reset_tickets(c, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(CKE_EDEVICE, "populate launch failed: %s", hipGetErrorString(e));
     c->ready = 1;
     return CKE_OK;
@@ -445,6 +505,7 @@ int cross_decode(const float* q, int n_q, const cke_xattn_cache* c, int layer, f
     // 256 MB MALL is never re-read from it, so its rows are streamed
     a.stream_rows = 2 * region_elems(&g) * elem_bytes(g.cache_dtype) > kStreamCacheBytes;
     a.stats = stats;
+    a.tickets = c->merge_in_launch && g_merge_mode.load(std::memory_order_relaxed) ? tickets_of(c) : nullptr;
     hipError_t e = cke::launch_xattn_decode(a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(CKE_EDEVICE, "decode launch failed: %s", hipGetErrorString(e));
     return CKE_OK;

@@ -21,7 +21,30 @@ struct XattnLaunch {
     int dtype;           // CKE_F32, CKE_BF16 or CKE_FP8
     bool stream_rows;    // whole cross cache far larger than the MALL: non-temporal row loads
     float* stats;        // nullptr, or fp32 [B][max_q][H][2]: each head's final (max, sum), base 2
+    unsigned* tickets;   // nullptr (merge by a second kernel), or B*H zeroed counters of
+                         // kTicketBytes each: the split kernel merges in the same launch
 };
+
+// One arrival counter per head, each in a 128-byte line of its own.
+constexpr size_t kTicketBytes = 128;
+#ifndef CKE_CROSS_WAVES
+#define CKE_CROSS_WAVES 4
+#endif
+constexpr int kCrossWaves = CKE_CROSS_WAVES;  // waves per cross-decode workgroup
+
+// Merge of split partials: merge_lanes(nsplit) lanes (1, 2, 4 or 8) share one
+// output, each folding at most kMergePer splits (nsplit <= 64).
+constexpr int kMergePer = 8;
+inline __host__ __device__ int merge_lanes(int nsplit) {
+    return nsplit <= 8 ? 1 : (nsplit <= 16 ? 2 : (nsplit <= 32 ? 4 : 8));
+}
+// Whether a split decode may merge in its own launch: one pass of the split
+// kernel's threads covers every (output, lane) pair, and the partials stay
+// under 2 GB (32-bit buffer offsets). Otherwise a second kernel merges.
+inline bool merge_in_launch_fits(int nq, int D, int nsplit, long long n_bh, int max_q) {
+    return nsplit > 1 && nq * D * merge_lanes(nsplit) <= kCrossWaves * 64 &&
+           (size_t)n_bh * max_q * nsplit * (D + 2) * sizeof(float) < ((size_t)1 << 31) - 16;
+}
 
 struct SelfLaunch {
     const float* q;
@@ -76,6 +99,7 @@ constexpr int kShortMemRows = 64;
 
 // Largest number of key splits a decode call may use.
 constexpr int kMaxSplits = 64;
+static_assert(kMaxSplits <= 8 * kMergePer, "a merge covers at most 8 lanes of kMergePer splits");
 
 struct PopulateLaunch {
     const void* E;       // [B*T][d_model]
@@ -107,6 +131,12 @@ hipError_t launch_gemv(const GemvLaunch& a, hipStream_t st);
 int cross_keys_per_pass(int D, int elem_bytes);
 
 hipError_t launch_xattn_decode(const XattnLaunch& a, hipStream_t st);
+// Zero n 32-bit words (a kernel, so that it can sit inside a captured graph).
+hipError_t launch_zero_words(unsigned* p, size_t n, hipStream_t st);
+// Whether workgroups i and i + 8 of a launch always run on the same XCD on
+// the current device (a probe launch on a private stream, synchronised).
+// false on any HIP error.
+bool probe_xcd_placement();
 
 hipError_t launch_selfattn_append(const SelfLaunch& a, hipStream_t st);
 hipError_t launch_selfattn_prefill(const PrefillLaunch& a, hipStream_t st);

@@ -84,13 +84,47 @@ def test_workspace_and_split_plan():
         s = pc.cke_xattn_num_splits(g)
         assert 1 <= s <= 64
         ws = pc.cke_xattn_workspace_bytes(g)
+        al = lambda x: (x + 255) // 256 * 256
         need = g.n_streams * g.max_q * g.n_heads * s * (g.head_dim + 2) * 4
         stats = g.n_streams * g.max_q * g.n_heads * 2 * 4
-        assert ws >= (need + 255) // 256 * 256 + stats
+        # partials, statistics, then one 128-byte arrival counter per head when split
+        tickets = g.n_streams * g.n_heads * 128 if s > 1 else 0
+        assert ws == max(256, al(al(need) + stats) + tickets)
     # Whisper Base splits its 1500 rows across workgroups, Q-Former does not
     assert pc.cke_xattn_num_splits(base_geom()) > 1
     assert pc.cke_xattn_num_splits(base_geom(n_layers=2, n_streams=100, mem_len=15, d_model=2048,
                                              n_heads=32, max_q=3)) == 1
+
+
+def test_merge_mode_switch_and_query():
+    """cke_xattn_set_merge_mode takes 0 or 1 and returns the previous mode;
+    cke_xattn_merges_in_launch is 0 for NULL, unsplit geometries, query
+    counts outside [1, max_q] and in mode 0."""
+    prev = pc.cke_xattn_set_merge_mode(0)
+    try:
+        assert prev in (0, 1)
+        assert pc.cke_xattn_set_merge_mode(1) == 0
+        assert pc.lib().cke_xattn_set_merge_mode(2) == pc.CKE_EINVAL
+        assert "merge mode" in pc.cke_last_error()
+        assert pc.lib().cke_xattn_set_merge_mode(-1) == pc.CKE_EINVAL
+        assert pc.cke_xattn_set_merge_mode(1) == 1
+        assert pc.lib().cke_xattn_merges_in_launch(None, 1) == 0
+        unsplit = base_geom(n_layers=2, n_streams=100, mem_len=15, d_model=2048, n_heads=32, max_q=3)
+        h = pc.cke_xattn_cache_create(unsplit, FAKE, FAKE, FAKE)
+        try:
+            assert pc.lib().cke_xattn_merges_in_launch(h, 1) == 0
+        finally:
+            pc.cke_xattn_cache_destroy(h)
+        h = pc.cke_xattn_cache_create(base_geom(max_q=2), FAKE, FAKE, FAKE)
+        try:
+            for n_q in (0, 3, -1):
+                assert pc.lib().cke_xattn_merges_in_launch(h, n_q) == 0
+            pc.cke_xattn_set_merge_mode(0)
+            assert pc.lib().cke_xattn_merges_in_launch(h, 1) == 0
+        finally:
+            pc.cke_xattn_cache_destroy(h)
+    finally:
+        pc.cke_xattn_set_merge_mode(prev)
 
 
 def test_ready_flag_state_machine_without_gpu():

@@ -403,6 +403,105 @@ def test_cross_decode_is_deterministic_and_nq_zero_is_noop():
     assert bool(torch.all(out == 7.0))
 
 
+# Split geometries for the in-launch merge, with whether it applies (one pass
+# of the split kernel's 256 threads must cover n_q * D * lanes, lanes = 1, 2,
+# 4 or 8 for up to 8, 16, 32 or 64 splits): Whisper Base; B*H not a multiple
+# of 8 (12 and 15 heads); 2, 13, 16 and 63 splits (odd split counts leave
+# some lanes fewer splits); D = 32, 64 and 128; fp32, bf16 and fp8 rows;
+# several queries. Beam's 5 queries and Base with 8 take the second kernel.
+MERGE_CASES = [
+    ("base", {}, True),
+    ("beam", {}, False),
+    (None, dict(n_layers=2, n_streams=3, n_q=1, mem_len=777, d_model=256, n_heads=4, head_dim=64,
+                dtype="bf16"), True),
+    (None, dict(n_layers=1, n_streams=5, n_q=2, mem_len=300, d_model=96, n_heads=3, head_dim=32),
+     True),
+    (None, dict(n_layers=1, n_streams=8, n_q=1, mem_len=1000, d_model=256, n_heads=2, head_dim=128,
+                dtype="fp8"), True),
+    (None, dict(n_layers=1, n_streams=1, n_q=1, mem_len=20000, d_model=64, n_heads=2, head_dim=32),
+     True),
+    (None, dict(n_layers=1, n_streams=4, n_q=4, mem_len=500, d_model=128, n_heads=4, head_dim=32),
+     True),
+    (None, dict(n_layers=1, n_streams=32, n_q=1, mem_len=300, d_model=256, n_heads=4, head_dim=64),
+     True),
+    (None, dict(n_layers=1, n_streams=1, n_q=8, mem_len=1500, d_model=512, n_heads=8, head_dim=64),
+     False),
+]
+
+
+def _ticket_words(cache):
+    """The per-head arrival counters of a split cache's workspace (the layout
+    cke_xattn_workspace_bytes documents): one 32-bit word every 128 bytes."""
+    g = cache.geom
+    ns = pc.cke_xattn_num_splits(g)
+    al = lambda x: (x + 255) // 256 * 256
+    stats_off = al(g.n_streams * g.max_q * g.n_heads * ns * (g.head_dim + 2) * 4)
+    off = al(stats_off + g.n_streams * g.max_q * g.n_heads * 2 * 4)
+    n = g.n_streams * g.n_heads
+    words = cache.ws.view(torch.int32)[off // 4: off // 4 + 32 * n]
+    return words.view(n, 32)[:, 0]
+
+
+@pytest.mark.parametrize("name,kw,fused", MERGE_CASES, ids=lambda x: str(x))
+def test_in_launch_merge_matches_the_merge_kernel_bit_for_bit(name, kw, fused):
+    """The last-arriving workgroup of each head merges in the split kernel's
+    own launch (mode 1) with the same bits as the second merge kernel (mode
+    0), over consecutive calls (every call leaves the arrival counters at
+    zero), with and without attention weights; and it is what runs by default
+    on this device wherever it applies."""
+    g = geometry(name, **kw)
+    cache, wt, _ = make_cache(g)
+    assert pc.cke_xattn_num_splits(cache.geom) > 1
+    prev = pc.cke_xattn_set_merge_mode(1)
+    try:
+        assert pc.cke_xattn_merges_in_launch(cache, g.n_q) == fused, "placement probe failed?"
+        runs = []
+        for mode in (1, 0, 1):
+            assert pc.cke_xattn_set_merge_mode(mode) in (0, 1)
+            assert pc.cke_xattn_merges_in_launch(cache, g.n_q) == (fused and bool(mode))
+            res = []
+            for step in range(3):
+                for layer in range(g.n_layers):
+                    q = t32(synth.decode_call_inputs(g, step, layer)["q_cross"])
+                    res.append(cache.decode(q, layer, g.scale).clone())
+            q = t32(synth.decode_call_inputs(g, 3, 0)["q_cross"])
+            out, w = cache.decode_weights(q, 0, g.scale, [0, g.n_heads - 1])
+            res += [out.clone(), w.clone()]
+            torch.cuda.synchronize()
+            assert int(_ticket_words(cache).abs().sum()) == 0, mode
+            runs.append(res)
+        for a, b in zip(runs[0], runs[1]):
+            assert torch.equal(a, b)
+        for a, b in zip(runs[0], runs[2]):
+            assert torch.equal(a, b)
+        if g.dtype != "fp8":   # fp8: parity on the oracle's own fp8 values, test_fp8_cross_decode_*
+            Kc, Vc = oracle_caches(g, wt)
+            q = synth.decode_call_inputs(g, 0, 0)["q_cross"]
+            want = oracle.cross_decode(q, Kc[0], Vc[0], g.scale)
+            assert max_abs(to_np(runs[0][0]), want) <= TOL[g.dtype]
+    finally:
+        pc.cke_xattn_set_merge_mode(prev)
+
+
+def test_populate_clears_the_arrival_counters():
+    """Counters left non-zero (here: overwritten) are zeroed by the next
+    populate, so the first decode after it merges every head."""
+    g = geometry("base")
+    cache, wt, (E, WK, WV) = make_cache(g)
+    Kc, Vc = oracle_caches(g, wt)
+    q = synth.decode_call_inputs(g, 0, 1)["q_cross"]
+    good = cache.decode(t32(q), 1, g.scale).clone()
+    words = _ticket_words(cache)
+    words.fill_(5)
+    cache.populate(E, WK, WV)
+    out = torch.full_like(good, float("nan"))
+    cache.decode(t32(q), 1, g.scale, out=out)
+    torch.cuda.synchronize()
+    assert int(_ticket_words(cache).abs().sum()) == 0
+    assert torch.equal(out, good)
+    assert max_abs(to_np(out), oracle.cross_decode(q, Kc[1], Vc[1], g.scale)) <= 1e-4
+
+
 def test_ready_flag_on_gpu():
     """C-Kernel-Engine 'View 3': new encoder memory invalidates the cache and
     decode refuses (-2) until populate has run again."""
