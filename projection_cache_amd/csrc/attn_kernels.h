@@ -41,8 +41,8 @@ namespace {
 // addresses, so the loads cost one memory round trip -- takes their max
 // first, so that the exponentials are independent of each other (no chain of
 // running-max updates), and sums L_s and A_s scaled by them in ascending s.
-// The GL lanes then combine in xor-butterfly rounds (lane distance 1, 2, 4),
-// with no LDS and no barrier; lane g = 0 writes. The same arithmetic in the
+// The GL lanes then combine in rounds of lane permutes (DPP), with no LDS and
+// no barrier; lane g = 0 writes. The same arithmetic in the
 // same order whichever kernel runs it, so both merges give identical bits.
 // L2 = true when the partials were written during this same launch by other
 // workgroups of this XCD: they are then read with the L1 bypassed (buffer
@@ -95,14 +95,19 @@ __device__ __forceinline__ void merge_head(const float* __restrict__ part, float
             l = fmaf(pl[j], e, l);
             a = fmaf(pa[j], e, a);
         }
-        for (int k = 1; k < GL; k <<= 1) {
-            const float m2 = __shfl_xor(m, k), l2 = __shfl_xor(l, k), a2 = __shfl_xor(a, k);
+        // combine with the partner lane's (m, l, a): DPP quad permutes for
+        // lane distances 1 and 2, the half-row mirror (lane i with 7 - i) to
+        // join the two quads of an 8-lane group
+        auto join = [&](float m2, float l2, float a2) {
             const float mn = fmaxf(m, m2);
             const float e1 = fast_exp2(m - mn), e2 = fast_exp2(m2 - mn);
             l = fmaf(l, e1, l2 * e2);
             a = fmaf(a, e1, a2 * e2);
             m = mn;
-        }
+        };
+        if (GL >= 2) join(dpp<0xB1>(m), dpp<0xB1>(l), dpp<0xB1>(a));
+        if (GL >= 4) join(dpp<0x4E>(m), dpp<0x4E>(l), dpp<0x4E>(a));
+        if (GL >= 8) join(dpp<0x141>(m), dpp<0x141>(l), dpp<0x141>(a));
         if (live && g == 0) {
             out[(((size_t)b * nq + i) * H + h) * D + d] = a / l;
             if (stats && d == 0) {
