@@ -348,6 +348,30 @@ DECODE_SOURCES = ("attn_kernels.h", "attn_decode.hip", "attn_f32.hip", "attn_bf1
                   "attn_fp8.hip", "cke_device.h")
 
 
+def graph_kernel_nodes(graph):
+    """Kernel launches in a captured window graph (hipGraphGetNodes on its raw
+    handle, kernel nodes only), or None where the runtime does not expose it."""
+    import ctypes
+    try:
+        raw = graph.raw_cuda_graph()
+        hip = ctypes.CDLL("libamdhip64.so")
+        n = ctypes.c_size_t(0)
+        if hip.hipGraphGetNodes(ctypes.c_void_p(raw), None, ctypes.byref(n)) != 0:
+            return None
+        nodes = (ctypes.c_void_p * n.value)()
+        if hip.hipGraphGetNodes(ctypes.c_void_p(raw), nodes, ctypes.byref(n)) != 0:
+            return None
+        kinds = ctypes.c_int(-1)
+        count = 0
+        for i in range(n.value):
+            if hip.hipGraphNodeGetType(ctypes.c_void_p(nodes[i]), ctypes.byref(kinds)) != 0:
+                return None
+            count += kinds.value == 0   # hipGraphNodeTypeKernel
+        return count
+    except (AttributeError, OSError, RuntimeError):
+        return None
+
+
 def measured_traffic(config):
     """HBM bytes per cross-attention decode call (split + merge kernels) from the
     committed rocprofv3 counter summary, scaled by its copy calibration; None if
@@ -877,8 +901,10 @@ def measure(name, args, torch, pc, stream, extras):
         torch.cuda.synchronize()
         return graph
 
+    window_launches = None
     if args.mode == "graph":
         graph = capture(("populate", "selfattn", "xattn_decode"))
+        window_launches = graph_kernel_nodes(graph)
 
         def run():
             with torch.cuda.stream(stream):
@@ -929,6 +955,9 @@ def measure(name, args, torch, pc, stream, extras):
 
     cross_b = w.cross_bytes_per_call()
     cross_gbs = cross_b / avg["xattn_decode"] / 1e9
+    fused_merge = pc.cke_xattn_merges_in_launch(w.cache, max(g.n_q, 1))
+    merge_text = ("" if w.cache.n_splits == 1 else
+                  ", split partials merged in the same launch" if fused_merge else " + xattn_merge_kernel")
     traffic = measured_traffic(name)
     kernels = {
         "xattn_decode": {"avg_us": avg["xattn_decode"] * 1e6, "calls_per_step": len(dur["xattn_decode"]),
@@ -960,8 +989,7 @@ def measure(name, args, torch, pc, stream, extras):
                    "tokens_per_step": w.tokens_per_window, "decode_steps": g.steps,
                    "layers": g.n_layers, "mode": args.mode},
         "roofline": {"bound": "hbm",
-                     "kernel": "cke_xattn_decode (xattn_partial_kernel%s)"
-                               % (" + xattn_merge_kernel" if w.cache.n_splits > 1 else ""),
+                     "kernel": "cke_xattn_decode (xattn_partial_kernel%s)" % merge_text,
                      "achieved": cross_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": cross_gbs / HBM_PEAK_GBS,
                      "traffic": traffic["bytes"] if traffic else None,
@@ -994,9 +1022,13 @@ def measure(name, args, torch, pc, stream, extras):
         if cold:
             blk["xattn_decode_mall_cold"] = cold
         floor = measure_launch_floor(torch, stream)
-        launches = w.calls("selfattn") + w.calls("xattn_decode") * (2 if w.cache.n_splits > 1 else 1)
-        floor["launches_per_step"] = launches + 1
-        floor["floor_tokens_per_s"] = w.tokens_per_window / ((launches + 1) * floor["us_per_launch"] * 1e-6)
+        launches = window_launches
+        if launches is None:   # estimate: one populate launch, the decode calls' kernels
+            per_cross = 2 if (w.cache.n_splits > 1 and not fused_merge) else 1
+            launches = 1 + w.calls("selfattn") + w.calls("xattn_decode") * per_cross
+        floor["launches_per_step"] = launches
+        floor["launches_counted"] = window_launches is not None
+        floor["floor_tokens_per_s"] = w.tokens_per_window / (launches * floor["us_per_launch"] * 1e-6)
         blk["launch_floor"] = floor
     del w
     torch.cuda.synchronize()

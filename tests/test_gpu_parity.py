@@ -408,7 +408,9 @@ def test_cross_decode_is_deterministic_and_nq_zero_is_noop():
 # 4 or 8 for up to 8, 16, 32 or 64 splits): Whisper Base; B*H not a multiple
 # of 8 (12 and 15 heads); 2, 13, 16 and 63 splits (odd split counts leave
 # some lanes fewer splits); D = 32, 64 and 128; fp32, bf16 and fp8 rows;
-# several queries. Beam's 5 queries and Base with 8 take the second kernel.
+# several queries. Beam's 5 queries, Base with 8, a 63-split head with 2
+# queries and 3 queries of 128 dims take the second kernel (several
+# workgroups per head).
 MERGE_CASES = [
     ("base", {}, True),
     ("beam", {}, False),
@@ -426,6 +428,10 @@ MERGE_CASES = [
      True),
     (None, dict(n_layers=1, n_streams=1, n_q=8, mem_len=1500, d_model=512, n_heads=8, head_dim=64),
      False),
+    (None, dict(n_layers=1, n_streams=1, n_q=2, mem_len=20000, d_model=128, n_heads=2,
+                head_dim=64), False),
+    (None, dict(n_layers=1, n_streams=8, n_q=3, mem_len=900, d_model=256, n_heads=2, head_dim=128,
+                dtype="bf16"), False),
 ]
 
 
