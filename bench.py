@@ -392,12 +392,16 @@ def measured_traffic(config):
         return None
     cal = t["calibration"]
     read = write = 0.0
+    found = False
     for k, v in per.items():
-        if "xattn_partial_kernel" in k or "xattn_merge_kernel" in k:
+        if any(n in k for n in ("xattn_partial_kernel", "xattn_merge_kernel", "xattn_short_kernel")):
             if "FETCH_SIZE" not in v or "WRITE_SIZE" not in v:
                 return None
+            found = True
             read += v["FETCH_SIZE"] * 1024 / cal["read_factor"]
             write += v["WRITE_SIZE"] * 1024 / cal["write_factor"]
+    if not found:
+        return None
     return {"bytes": read + write, "read": read, "write": write}
 
 
@@ -890,11 +894,12 @@ def measure(name, args, torch, pc, stream, extras):
     g = w.g
     torch.cuda.synchronize()
 
-    def capture(kinds, reps=1):
+    def capture(kinds, reps=1, keep=False):
         with torch.cuda.stream(stream):
             w.window(stream, kinds)    # warm the kernels once outside capture
         stream.synchronize()
-        graph = torch.cuda.CUDAGraph()
+        # keep_graph: the captured graph stays inspectable (for counting its launches)
+        graph = torch.cuda.CUDAGraph(keep_graph=True) if keep else torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph, stream=stream):
             for _ in range(reps):
                 w.window(torch.cuda.current_stream(), kinds)
@@ -904,7 +909,12 @@ def measure(name, args, torch, pc, stream, extras):
     window_launches = None
     if args.mode == "graph":
         graph = capture(("populate", "selfattn", "xattn_decode"))
-        window_launches = graph_kernel_nodes(graph)
+        try:   # a second capture of the same window, kept to count its kernel launches
+            counted = capture(("populate", "selfattn", "xattn_decode"), keep=True)
+            window_launches = graph_kernel_nodes(counted)
+            del counted
+        except (TypeError, RuntimeError):
+            window_launches = None
 
         def run():
             with torch.cuda.stream(stream):
@@ -956,6 +966,8 @@ def measure(name, args, torch, pc, stream, extras):
     cross_b = w.cross_bytes_per_call()
     cross_gbs = cross_b / avg["xattn_decode"] / 1e9
     fused_merge = pc.cke_xattn_merges_in_launch(w.cache, max(g.n_q, 1))
+    # memories of at most 64 rows take the one-wave-per-head kernel
+    cross_kernel = "xattn_short_kernel" if g.mem_len <= 64 else "xattn_partial_kernel"
     merge_text = ("" if w.cache.n_splits == 1 else
                   ", split partials merged in the same launch" if fused_merge else " + xattn_merge_kernel")
     traffic = measured_traffic(name)
@@ -989,7 +1001,7 @@ def measure(name, args, torch, pc, stream, extras):
                    "tokens_per_step": w.tokens_per_window, "decode_steps": g.steps,
                    "layers": g.n_layers, "mode": args.mode},
         "roofline": {"bound": "hbm",
-                     "kernel": "cke_xattn_decode (xattn_partial_kernel%s)" % merge_text,
+                     "kernel": "cke_xattn_decode (%s%s)" % (cross_kernel, merge_text),
                      "achieved": cross_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": cross_gbs / HBM_PEAK_GBS,
                      "traffic": traffic["bytes"] if traffic else None,

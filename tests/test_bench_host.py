@@ -79,3 +79,22 @@ def test_phases_and_extras_flags_are_parsed():
     finally:
         sys.argv = old
     assert d.also == "large,beam,qformer" and not d.no_extras and d.gpus == 1
+
+
+def test_counter_traffic_of_the_decode_call_is_near_its_algorithmic_bytes():
+    """The committed HBM counters (profiles/hbm_traffic.json), where they still
+    describe the decode kernels' sources, put each workload's cross-attention
+    call within a few percent above its algorithmic bytes: K and V of one layer
+    slab once, queries and outputs, plus the split partials where a second
+    kernel merges them (Beam); the one-wave-per-head kernel of the Q-Former's
+    15-row memories is counted too. Configurations without counters give None,
+    never 0."""
+    algorithmic = {"base": 6148096, "beam": 6164480, "large": 123043840, "large_fp8": 61603840,
+                   "qformer": 29491200}
+    for name, want in algorithmic.items():
+        t = bench.measured_traffic(name)
+        if t is None:        # sources changed since the counters were taken
+            continue
+        assert 0.99 * want <= t["bytes"] <= 1.2 * want, (name, t["bytes"], want)
+        assert t["bytes"] == t["read"] + t["write"]
+    assert bench.measured_traffic("no such workload") is None
