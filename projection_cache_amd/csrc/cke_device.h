@@ -260,9 +260,14 @@ __device__ __forceinline__ void compute_tile(int base, int r1, int cur_row, bool
     using RM = RowMap<D, TE>;
     constexpr int VEC = RM::kVec, LPK = RM::kLPK, KPW = RM::kKPW;
     const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
+    // every one of the NQ queries is computed, also those past nq (their
+    // query vector is zero and their state unused): one straight-line block,
+    // so the compiler interleaves the queries' independent reduction and
+    // softmax chains instead of running them one after another
+    (void)nq;
 #pragma unroll
     for (int i = 0; i < NQ; ++i) {
-        if (i < nq) {
+        {
             float s[NP];
             float mt = -INFINITY;
 #pragma unroll
@@ -426,9 +431,10 @@ __device__ __forceinline__ void wave_merge_groups(WaveState<NQ, RowMap<D, TE>::k
 {
     using RM = RowMap<D, TE>;
     constexpr int VEC = RM::kVec, LPK = RM::kLPK;
+    (void)nq;   // all NQ, as in compute_tile: straight-line code
 #pragma unroll
     for (int i = 0; i < NQ; ++i) {
-        if (i < nq) {
+        {
             const float M = xor_max<LPK, 64>(st.m[i]);
             const float f = M == -INFINITY ? 0.f : fast_exp2(st.m[i] - M);
             st.m[i] = M;
@@ -454,7 +460,7 @@ __device__ __forceinline__ void wg_merge(
     wave_merge_groups<D, TE, NQ>(st, nq);
 #pragma unroll
     for (int i = 0; i < NQ; ++i) {
-        if (i < nq) {
+        {
             if (lane < LPK) {
 #pragma unroll
                 for (int j = 0; j < VEC; ++j) wa[(w * NQ + i) * D + lane * VEC + j] = st.acc[i][j];
