@@ -358,9 +358,12 @@ __device__ __forceinline__ void compute_tile_causal(int base, const int (&lim)[N
 {
     using RM = RowMap<D, TE>;
     constexpr int VEC = RM::kVec, LPK = RM::kLPK, KPW = RM::kKPW;
+    // all NQ queries in straight-line code, as in compute_tile (the caller
+    // gives queries past nq a copy of the last query and its limit)
+    (void)nq;
 #pragma unroll
     for (int i = 0; i < NQ; ++i) {
-        if (i < nq) {
+        {
             float s[NP];
             float mt = -INFINITY;
 #pragma unroll
