@@ -97,9 +97,27 @@ static_assert(CKE_MAX_LAYERS == cke::kMaxLayers, "layer cap of the header and th
 static_assert(CKE_MAX_SPLITS >= 1 && CKE_MAX_SPLITS <= cke::kMaxSplits, "split cap");
 
 // Split of the T memory rows of one (stream, head) across workgroups. Fixed
-// per geometry so that decode results are reproducible run to run. Aims for
-// about CKE_TARGET_WGS workgroups (one per compute unit) but never fewer rows
-// per workgroup than one pass of its waves.
+// per geometry so that decode results are reproducible run to run.
+//  * Fewer (stream, head) pairs than CKE_TARGET_WGS (one workgroup per
+//    compute unit): split each head into about CKE_TARGET_WGS / (B*H) pieces,
+//    but never fewer rows per workgroup than one pass of its waves. The call
+//    is latency-bound; every compute unit gets a share.
+//  * At least that many pairs: the unsplit grid already covers every compute
+//    unit, but B*H workgroups over 256 units leave some units one workgroup
+//    more than others (Large: 320 heads, 64 units with two), and each unit
+//    streams at a capped rate, so the busiest units set the call's time.
+//    Split into s pieces (2 <= s <= 8, at least 256 rows each, at most 4
+//    workgroups per compute unit, so that every workgroup is resident at
+//    once) when that evens out the workgroups per unit: s minimises
+//    ceil(B*H*s / 256) * 256 / (B*H*s), ties to the smaller s. Large (bf16
+//    cache): 3 splits, 24.1 against 26.3 us per call on one box (4 splits
+//    24.1, 5 24.3, 8 24.5); over its fp8 cache 16.2 against 16.7 us (2
+//    splits 16.3; 4 splits 18.3: five workgroups per unit do not all fit).
+double unit_imbalance(long long wgs) {
+    const long long units = CKE_TARGET_WGS;
+    return (double)((wgs + units - 1) / units) * units / (double)wgs;
+}
+
 void split_plan(const cke_xattn_geom* g, int* nsplit, int* chunk) {
     if (g->mem_len <= cke::kShortMemRows) {  // one wave per head, no split
         *nsplit = 1;
@@ -109,10 +127,23 @@ void split_plan(const cke_xattn_geom* g, int* nsplit, int* chunk) {
     const int kpp = cke::cross_keys_per_pass(g->head_dim, elem_bytes(g->cache_dtype));
     const long long bh = (long long)g->n_streams * g->n_heads;
     const int max_by_rows = (g->mem_len + kpp - 1) / kpp;
-    long long want = (CKE_TARGET_WGS + bh - 1) / bh;
-    if (want > CKE_MAX_SPLITS) want = CKE_MAX_SPLITS;
-    int s = (int)(want < max_by_rows ? want : max_by_rows);
-    if (s < 1) s = 1;
+    int s = 1;
+    if (bh < CKE_TARGET_WGS) {
+        long long want = (CKE_TARGET_WGS + bh - 1) / bh;
+        if (want > CKE_MAX_SPLITS) want = CKE_MAX_SPLITS;
+        s = (int)(want < max_by_rows ? want : max_by_rows);
+        if (s < 1) s = 1;
+    } else {
+        double best = unit_imbalance(bh);
+        for (int t = 2; t <= 8 && t <= max_by_rows && bh * t <= 4LL * CKE_TARGET_WGS &&
+                        g->mem_len >= 256LL * t; ++t) {
+            const double im = unit_imbalance(bh * t);
+            if (im < best - 1e-9) {
+                best = im;
+                s = t;
+            }
+        }
+    }
     int c = (g->mem_len + s - 1) / s;
     c = ((c + kpp - 1) / kpp) * kpp;
     *chunk = c;
