@@ -342,10 +342,11 @@ def roofline_regime(bytes_per_call):
     return "bandwidth"
 
 
-# the sources of the decode kernels: counters taken before any of them
-# changed no longer describe the kernel that runs
+# the sources of the decode kernels and of their launch plan (split counts,
+# the in-launch merge): counters taken before any of them changed no longer
+# describe the kernels that run
 DECODE_SOURCES = ("attn_kernels.h", "attn_decode.hip", "attn_f32.hip", "attn_bf16.hip",
-                  "attn_fp8.hip", "cke_device.h")
+                  "attn_fp8.hip", "cke_device.h", "cke_internal.h", "cke_api.hip")
 
 
 def graph_kernel_nodes(graph):
