@@ -158,9 +158,11 @@ __global__ __launch_bounds__(256) void xattn_merge_kernel(
 //     the dispatcher's placement (workgroups i and i + 8 share an XCD), which
 //     the host verifies once per device before it passes tickets.
 //   * tickets == nullptr: by xattn_merge_kernel, launched next on the same
-//     stream; its workgroup hb runs on XCD hb % 8 as well, so the partials
-//     it reads were written through its own L2 (Whisper Base: 6.73 against
-//     7.05 us per call with the splits spread over all XCDs).
+//     stream, whose workgroups of head hb share an XCD as well (Whisper Base:
+//     6.73 against 7.05 us per call with the splits spread over all XCDs).
+//     Which XCD a class i % 8 runs on changes from one dispatch to the next,
+//     so that is not always the XCD that wrote the partials; they cross a
+//     kernel boundary and are read correctly either way.
 //
 // Both merges run merge_head, so they give identical bits. Device-scope
 // variants of the in-launch merge were slower than the second launch: a

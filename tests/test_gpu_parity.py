@@ -1098,7 +1098,8 @@ def test_full_size_decode_every_head(name):
     the last layer, with the cache holding seeded slabs of the projected
     spread (stored exactly in the cache type), against the oracle on the same
     slabs. A cache this large (K and V of 32 layers, far above the 256 MB
-    MALL) is read with streaming loads: this is that path's parity case."""
+    MALL) is read with streaming loads, and its 320 heads are split in 3 and
+    merged in the same launch: this is those paths' full-size parity case."""
     g = synth.get(name)
     cache = pc.XattnCache(g.n_layers, g.n_streams, g.mem_len, g.d_model, g.n_heads, g.head_dim,
                           max_q=g.n_q, dtype=CACHE_DT[g.dtype])
@@ -1123,6 +1124,8 @@ def test_full_size_decode_every_head(name):
             assert np.isfinite(got).all()
             want = oracle.cross_decode(q, kv[0], kv[1], g.scale)
             assert max_abs(got, want) <= TOL["f32"], (l, step)
+    # the full-size heads are split and merged in launch
+    assert pc.cke_xattn_merges_in_launch(cache, g.n_q)
 
 
 def test_large_self_attention_every_position():
