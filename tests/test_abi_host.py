@@ -96,6 +96,30 @@ def test_workspace_and_split_plan():
                                              n_heads=32, max_q=3)) == 1
 
 
+def test_split_plan_evens_out_workgroups_per_compute_unit():
+    """With at least 256 (stream, head) pairs the unsplit grid covers the 256
+    compute units; the plan then splits a head into s pieces (2..8, >= 256
+    rows each, <= 4 workgroups per unit) only where that evens out the
+    workgroups per unit, s minimising ceil(B*H*s/256)*256/(B*H*s)."""
+    def splits(n_streams, n_heads, mem_len=1500, dt=pc.CKE_BF16):
+        return pc.cke_xattn_num_splits(base_geom(n_layers=1, n_streams=n_streams, n_heads=n_heads,
+                                                 d_model=64 * n_heads, mem_len=mem_len,
+                                                 cache_dtype=dt))
+    assert splits(16, 20) == 3                # Large: 320 pairs -> 960 workgroups (3.75 per unit)
+    assert splits(16, 20, dt=pc.CKE_FP8) == 3
+    assert splits(32, 16) == 1                # 512 pairs: two per unit already
+    assert splits(16, 16) == 1                # 256: one per unit
+    assert splits(15, 20) == 3                # 300 pairs: 1.17 -> 900 workgroups (3.52 per unit)
+    assert splits(64, 20) == 1                # 1280 pairs: five per unit; no room to split
+    assert splits(16, 20, mem_len=600) == 2   # at least 256 rows per split
+    assert splits(16, 20, mem_len=300) == 1
+    # fewer pairs than units: about one workgroup per unit, as before (chunks
+    # rounded up to whole passes of the waves: 64 bf16 rows, 16 fp32 rows)
+    assert splits(1, 8, dt=pc.CKE_F32) == 32     # Whisper Base
+    assert splits(1, 8) == 24
+    assert splits(2, 8, dt=pc.CKE_F32) == 16
+
+
 def test_merge_mode_switch_and_query():
     """cke_xattn_set_merge_mode takes 0 or 1 and returns the previous mode;
     cke_xattn_merges_in_launch is 0 for NULL, unsplit geometries, query
