@@ -492,13 +492,17 @@ __global__ __launch_bounds__(NW * 64) void selfattn_prefill_kernel(
 #ifndef CKE_CROSS_NP
 #define CKE_CROSS_NP 4
 #endif
+#ifndef CKE_CROSS_NP_F32
+#define CKE_CROSS_NP_F32 3
+#endif
 #ifndef CKE_SELF_WAVES
 #define CKE_SELF_WAVES 8
 #endif
 #ifndef CKE_SELF_NP
 #define CKE_SELF_NP 4
 #endif
-constexpr int kCrossNP = CKE_CROSS_NP;        // row passes per load tile
+constexpr int kCrossNP = CKE_CROSS_NP;        // row passes per load tile (16- and 8-bit rows)
+constexpr int kCrossNPf32 = CKE_CROSS_NP_F32; // row passes per load tile (fp32 rows)
 constexpr int kSelfWaves = CKE_SELF_WAVES;
 constexpr int kSelfNP = CKE_SELF_NP;
 
@@ -520,11 +524,14 @@ hipError_t launch_cross_nq(const XattnLaunch& a, hipStream_t st) {
                            n_bh, a.scale * kLog2e);
         return hipGetLastError();
     }
-    // With more than two queries, bf16 and fp8 rows (8 or 16 values per lane)
-    // keep their tiles short: long ones cost registers (fp8 spills from four
-    // queries on). fp32 rows (4 values per lane) keep full tiles at any query
-    // count, 167 registers at most (Beam's 5 queries: 11.3 against 11.75 us).
-    constexpr int NP = (NQ > 2 && sizeof(TE) < 4 && kCrossNP > 2) ? 2 : kCrossNP;
+    // Row passes per load tile. fp32 rows (4 values per lane): 3 at any query
+    // count (Whisper Base 5.26 against 5.34 us per call with 4, Beam 8.64
+    // against 8.83; 2 and 6 slower; before the in-launch merge, 4 passes had
+    // taken Beam from 11.75 to 11.3 us against 2). bf16 and fp8 rows (8 or 16
+    // values per lane): 4 (Large 24.2 against 24.5 us with 3, over fp8 16.17
+    // against 16.35), but 2 with more than two queries: long tiles cost
+    // registers (fp8 spills from four queries on).
+    constexpr int NP = sizeof(TE) == 4 ? kCrossNPf32 : ((NQ > 2 && kCrossNP > 2) ? 2 : kCrossNP);
     const int n_bh = a.B * a.H;
     dim3 grid(8 * a.nsplit * ((n_bh + 7) / 8));
     unsigned* tickets =
