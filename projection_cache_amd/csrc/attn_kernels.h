@@ -499,7 +499,7 @@ __global__ __launch_bounds__(NW * 64) void selfattn_prefill_kernel(
 #define CKE_SELF_WAVES 8
 #endif
 #ifndef CKE_SELF_NP
-#define CKE_SELF_NP 4
+#define CKE_SELF_NP 2
 #endif
 constexpr int kCrossNP = CKE_CROSS_NP;        // row passes per load tile (16- and 8-bit rows)
 constexpr int kCrossNPf32 = CKE_CROSS_NP_F32; // row passes per load tile (fp32 rows)
