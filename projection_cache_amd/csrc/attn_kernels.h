@@ -487,6 +487,84 @@ __global__ __launch_bounds__(NW * 64) void selfattn_prefill_kernel(
     }
 }
 
+// Grid: (Hkv * Z, S), Z = ceil(n_new / QB) * G groups per kv head. One
+// workgroup per group of up to QB consecutive tokens of one query head (group
+// j of kv head hk: head h = hk*G + j % G, tokens QB*(j / G) ..), its NW waves
+// taking contiguous shares of the rows the group reads, 0 .. pos+i for token
+// i, merged through LDS. Rows below pos come from the cache, the new rows
+// from k_new / v_new rounded as they are stored; the group's own new rows are
+// written to the cache by its first head's workgroup (j % G == 0), which no
+// workgroup of this launch reads. So no workgroup depends on another, and the
+// rows of a kv head spread over Z workgroups instead of one. Rows past
+// pos+n_new-1 are neither read nor written.
+template <int D, typename TE, int NW, int NP, int QB>
+__global__ __launch_bounds__(NW * 64) void selfattn_prefill_groups_kernel(
+    const float* __restrict__ q, const float* __restrict__ k_new,
+    const float* __restrict__ v_new, TE* __restrict__ Kc, TE* __restrict__ Vc,
+    float* __restrict__ out, int Hkv, int Hq, int max_pos, int pos, int n_new, int Z, float sl2)
+{
+    using RM = RowMap<D, TE>;
+    constexpr int VEC = RM::kVec, LPK = RM::kLPK, KPW = RM::kKPW;
+    __shared__ float wm[NW * QB], wl[NW * QB], wa[NW * QB * D];
+    __shared__ float sM[QB], sL[QB], sA[QB * D];
+    const int s = blockIdx.y;
+    const int hk = blockIdx.x / Z, j = blockIdx.x - hk * Z;
+    const int G = Hq / Hkv;
+    const size_t skv = (size_t)s * Hkv + hk;
+    TE* K = Kc + skv * (size_t)max_pos * D;
+    TE* V = Vc + skv * (size_t)max_pos * D;
+    // token i of this sequence and kv head: k_new[(s * n_new + i) * Hkv + hk]
+    const float* kn = k_new + ((size_t)s * n_new * Hkv + hk) * D;
+    const float* vn = v_new + ((size_t)s * n_new * Hkv + hk) * D;
+    const size_t new_stride = (size_t)Hkv * D;
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+    const int sub = lane % LPK;
+    const int h = hk * G + j % G, i0 = QB * (j / G);
+    const int nq = min(QB, n_new - i0);
+
+    if (j % G == 0) {   // this token block's new rows, once per kv head
+        for (int x = threadIdx.x; x < nq * D; x += NW * 64) {
+            const int i = i0 + x / D, d = x % D;
+            const size_t src = (size_t)i * new_stride + d;
+            const size_t dst = (size_t)(pos + i) * D + d;
+            if constexpr (sizeof(TE) == 2) {
+                K[dst] = to_bf16_bits(kn[src]);
+                V[dst] = to_bf16_bits(vn[src]);
+            } else {
+                K[dst] = kn[src];
+                V[dst] = vn[src];
+            }
+        }
+    }
+
+    float qr[QB][VEC];
+    int lim[QB];
+#pragma unroll
+    for (int k = 0; k < QB; ++k) {
+        const int i = min(i0 + k, n_new - 1);
+        lim[k] = pos + i + 1;
+        const size_t qo = (((size_t)s * n_new + i) * Hq + h) * D;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) qr[k][e] = q[qo + sub * VEC + e];
+    }
+    const int R = pos + i0 + nq;   // rows the group reads: 0 .. R-1
+    const int per_wave = ((R + NW * KPW - 1) / (NW * KPW)) * KPW;
+    const int r0 = min(R, w * per_wave);
+    const int r1 = min(R, r0 + per_wave);
+    int lim_w[QB];
+#pragma unroll
+    for (int k = 0; k < QB; ++k) lim_w[k] = min(lim[k], r1);
+    WaveState<QB, VEC> st;
+    st.init();
+    wave_attend_causal_span<D, TE, QB, NP>(K, V, kn, vn, new_stride, pos, r0, r1, lim_w, qr, nq, sl2, st);
+    wg_merge<D, TE, QB, NW>(st, nq, wm, wl, wa, sM, sL, sA);
+    for (int x = threadIdx.x; x < nq * D; x += NW * 64) {
+        const int k = x / D, d = x % D;
+        out[(((size_t)s * n_new + i0 + k) * Hq + h) * D + d] = sA[k * D + d] / sL[k];
+    }
+}
+
 // ------------------------------------------------------------- launchers
 
 #ifndef CKE_CROSS_NP
@@ -617,6 +695,7 @@ hipError_t launch_self_t(const SelfLaunch& a, hipStream_t st) {
 
 constexpr int kPrefillQB = 8;   // tokens of one head sharing a wave's row reads
 constexpr int kPrefillNP = 2;
+constexpr long long kPrefillWaves = 2048;   // waves a grouped prefill launch aims to keep within
 
 template <int D, typename TE, int NW, int QB>
 hipError_t launch_prefill_nw(const PrefillLaunch& a, hipStream_t st) {
@@ -627,10 +706,20 @@ hipError_t launch_prefill_nw(const PrefillLaunch& a, hipStream_t st) {
     return hipGetLastError();
 }
 
-// A kv head with at most 8 queries gives each query a wave of its own
-// (short, latency-bound calls such as a few prefix rows); with more, each
-// wave takes kPrefillQB tokens of one head and reads their rows once. Up to
-// 8 waves per workgroup.
+template <int D, typename TE, int NW>
+hipError_t launch_prefill_groups(const PrefillLaunch& a, int Z, hipStream_t st) {
+    hipLaunchKernelGGL((selfattn_prefill_groups_kernel<D, TE, NW, kPrefillNP, kPrefillQB>),
+                       dim3(a.Hkv * Z, a.S), dim3(NW * 64), 0, st, a.q, a.k_new, a.v_new,
+                       static_cast<TE*>(a.K), static_cast<TE*>(a.V), a.out, a.Hkv, a.Hq, a.max_pos, a.pos,
+                       a.n_new, Z, a.scale * kLog2e);
+    return hipGetLastError();
+}
+
+// A kv head with at most 8 queries gives each query a wave of its own, in
+// one workgroup per kv head (short, latency-bound calls such as a few prefix
+// rows). With more, selfattn_prefill_groups_kernel: one workgroup per
+// kPrefillQB tokens of one head (reading their rows once), up to 8 waves
+// sharing those rows.
 template <int D, typename TE>
 hipError_t launch_prefill_d(const PrefillLaunch& a, hipStream_t st) {
     const long long G = a.Hq / a.Hkv;
@@ -641,11 +730,22 @@ hipError_t launch_prefill_d(const PrefillLaunch& a, hipStream_t st) {
         if (queries <= 4) return launch_prefill_nw<D, TE, 4, 1>(a, st);
         return launch_prefill_nw<D, TE, 8, 1>(a, st);
     }
-    const long long groups = (long long)((a.n_new + kPrefillQB - 1) / kPrefillQB) * G;
-    if (groups <= 1) return launch_prefill_nw<D, TE, 1, kPrefillQB>(a, st);
-    if (groups <= 2) return launch_prefill_nw<D, TE, 2, kPrefillQB>(a, st);
-    if (groups <= 4) return launch_prefill_nw<D, TE, 4, kPrefillQB>(a, st);
-    return launch_prefill_nw<D, TE, 8, kPrefillQB>(a, st);
+    // one workgroup per group of kPrefillQB tokens of one head, with waves
+    // enough for a load tile each over the rows its last token reads, but no
+    // more than keep the launch within about kPrefillWaves waves (8 per
+    // compute unit) so that every workgroup is resident at once: Whisper
+    // Base's 64-row chunk (64 groups) takes 8 waves per group, 8.75 against
+    // 29.2 us with one workgroup per kv head; Large's (2,560 groups) one.
+    const int Z = ((a.n_new + kPrefillQB - 1) / kPrefillQB) * (int)G;
+    constexpr int rows_per_tile = RowMap<D, TE>::kKPW * kPrefillNP;
+    const long long tiles = ((long long)a.pos + a.n_new + rows_per_tile - 1) / rows_per_tile;
+    const long long wgs = (long long)a.Hkv * Z * a.S;
+    const long long fit = kPrefillWaves / wgs;
+    const long long nw = tiles < fit ? tiles : fit;
+    if (nw <= 1) return launch_prefill_groups<D, TE, 1>(a, Z, st);
+    if (nw < 4) return launch_prefill_groups<D, TE, 2>(a, Z, st);
+    if (nw < 8) return launch_prefill_groups<D, TE, 4>(a, Z, st);
+    return launch_prefill_groups<D, TE, 8>(a, Z, st);
 }
 
 template <typename TE>

@@ -427,6 +427,58 @@ __device__ __forceinline__ void wave_attend_causal(
     }
 }
 
+// One wave attends a causal group of queries over rows [r0, r1) of a
+// self-attention cache during prefill: rows below `pos` come from the cache
+// K/V, rows from `pos` on from the fp32 new rows (row pos + i at kn, vn +
+// i * new_stride), rounded to the storage type exactly as they are stored, so
+// the wave never reads a cache row that this launch writes. Query i sees rows
+// below lim[i]; the caller clamps lim to r1. Each part is read in tiles of NP
+// passes; the cache part with register double buffering as in wave_attend.
+template <int D, typename TE, int NQ, int NP>
+__device__ __forceinline__ void wave_attend_causal_span(
+    const TE* __restrict__ K, const TE* __restrict__ V, const float* __restrict__ kn,
+    const float* __restrict__ vn, size_t new_stride, int pos, int r0, int r1, const int (&lim)[NQ],
+    const float (&q)[NQ][RowMap<D, TE>::kVec], int nq, float sl2,
+    WaveState<NQ, RowMap<D, TE>::kVec>& st)
+{
+    using RM = RowMap<D, TE>;
+    constexpr int VEC = RM::kVec, LPK = RM::kLPK, KPW = RM::kKPW;
+    constexpr int TILE = NP * KPW;
+    const int lane = threadIdx.x & 63;
+    const int grp = lane / LPK;
+    const int sub = lane % LPK;
+    if (r0 >= r1) return;
+    // cache rows [r0, c1): rows at or past c1 in the last tile are masked
+    const int c1 = min(r1, pos);
+    if (r0 < c1) {
+        int lim_c[NQ];
+#pragma unroll
+        for (int i = 0; i < NQ; ++i) lim_c[i] = min(lim[i], c1);
+        const int r_safe = c1 - 1;
+        uint4 ka[NP], va[NP], kb2[NP], vb2[NP];
+        load_tile<D, TE, NP>(K, V, r0, r_safe, grp, sub, ka, va);
+        for (int base = r0; base < c1; base += 2 * TILE) {
+            const bool more = base + TILE < c1;
+            if (more) load_tile<D, TE, NP>(K, V, base + TILE, r_safe, grp, sub, kb2, vb2);
+            compute_tile_causal<D, TE, NQ, NP>(base, lim_c, grp, q, nq, sl2, ka, va, st);
+            if (!more) break;
+            if (base + 2 * TILE < c1) load_tile<D, TE, NP>(K, V, base + 2 * TILE, r_safe, grp, sub, ka, va);
+            compute_tile_causal<D, TE, NQ, NP>(base + TILE, lim_c, grp, q, nq, sl2, kb2, vb2, st);
+        }
+    }
+    // new rows [max(r0, pos), r1), from the fp32 inputs
+    for (int base = max(r0, pos); base < r1; base += TILE) {
+        uint4 kb[NP], vb[NP];
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+            const size_t i = (size_t)(min(base + p * KPW + grp, r1 - 1) - pos);
+            kb[p] = pack_cur<TE>(load_cur<TE>(kn + i * new_stride + sub * VEC));
+            vb[p] = pack_cur<TE>(load_cur<TE>(vn + i * new_stride + sub * VEC));
+        }
+        compute_tile_causal<D, TE, NQ, NP>(base, lim, grp, q, nq, sl2, kb, vb, st);
+    }
+}
+
 // Merge the row groups of one wave: afterwards every lane holds the wave's
 // (max, sum) per query and the wave's unnormalised output for its own dims.
 template <int D, typename TE, int NQ>
