@@ -593,7 +593,9 @@ def measure_decoder_step(torch, pc, w, stream, tokens=4):
     by = 6 * dm * dm * welem + slab + self_rows + 12 * S * dm * 4
     res = {"seqs": S, "layers": L, "tokens": tokens, "avg_us_per_layer": t_f * 1e6,
            "tokens_per_s": S / (t_f * L), "bytes_per_layer": by, "GB_s": by / t_f / 1e9,
-           "launches_per_layer": 6 if w.cache.n_splits == 1 else 7}
+           # a split cross call adds a merge launch unless it merges in its own
+           "launches_per_layer": 6 if (w.cache.n_splits == 1 or
+                                       pc.cke_xattn_merges_in_launch(w.cache, max(g.n_q, 1))) else 7}
     if not w.bf16:
         H, D = g.n_heads, g.head_dim
         q, k, v, so, x1, qc, co = (torch.empty(S, dm, device="cuda") for _ in range(7))
