@@ -123,8 +123,8 @@ __device__ __forceinline__ void merge_head(const float* __restrict__ part, float
 // the first kernel left in memory. Z workgroups per head each take a
 // contiguous share of its (output, lane) pairs; one-dimensional grid of
 // 8 * Z * ceil(B*H / 8) workgroups placed like the split kernel's, so that
-// every workgroup of head hb runs on XCD hb % 8, where that head's partials
-// were written.
+// the workgroups of head hb share an XCD (the one that wrote that head's
+// partials when the two dispatches start their rounds of XCDs alike).
 template <int D>
 __global__ __launch_bounds__(256) void xattn_merge_kernel(
     const float* __restrict__ part, float* __restrict__ out, float* __restrict__ stats, int nq,
@@ -139,11 +139,13 @@ __global__ __launch_bounds__(256) void xattn_merge_kernel(
                          z * blockDim.x + threadIdx.x, Z * blockDim.x);
 }
 
-// Grid: 8 * nsplit * ceil(B*H / 8) workgroups in one dimension. Workgroup i
-// runs on XCD i % 8 (the dispatcher deals workgroups to the eight XCDs in
-// turn), and every split of head hb = b*H + h is placed on XCD hb % 8. Split
-// s of head hb covers memory rows [s*chunk, min(T, (s+1)*chunk)) for all nq
-// queries of stream b, so the queries of one stream share every K/V read.
+// Grid: 8 * nsplit * ceil(B*H / 8) workgroups in one dimension. Workgroups i
+// and i + 8 run on the same XCD (the dispatcher deals workgroups to the eight
+// XCDs in turn; which XCD it starts a dispatch on varies), and every split of
+// head hb = b*H + h is placed in class hb % 8, so all splits of a head share
+// an XCD. Split s of head hb covers memory rows [s*chunk, min(T, (s+1)*chunk))
+// for all nq queries of stream b, so the queries of one stream share every
+// K/V read.
 // With nsplit == 1 it writes `out` directly; otherwise it writes its partial
 // (max, sum, acc[D]) per query to `part`, and the partials are merged:
 //
@@ -160,9 +162,9 @@ __global__ __launch_bounds__(256) void xattn_merge_kernel(
 //   * tickets == nullptr: by xattn_merge_kernel, launched next on the same
 //     stream, whose workgroups of head hb share an XCD as well (Whisper Base:
 //     6.73 against 7.05 us per call with the splits spread over all XCDs).
-//     Which XCD a class i % 8 runs on changes from one dispatch to the next,
-//     so that is not always the XCD that wrote the partials; they cross a
-//     kernel boundary and are read correctly either way.
+//     That is not always the XCD that wrote the partials, since each dispatch
+//     starts its round of XCDs elsewhere; they cross a kernel boundary and
+//     are read correctly either way.
 //
 // Both merges run merge_head, so they give identical bits. Device-scope
 // variants of the in-launch merge were slower than the second launch: a

@@ -52,11 +52,13 @@ __global__ __launch_bounds__(kGemvWaves * 64) void gemv_kernel(const float* __re
     __shared__ float red[kGemvWaves][kGemvRowsMax * kGemvCols];
 
     const GemvOut o = blockIdx.y == 0 ? o0 : (blockIdx.y == 1 ? o1 : o2);
-    // Workgroup i runs on XCD i % 8. With the column blocks a multiple of 8,
-    // XCD x takes the contiguous x-th eighth of the columns, so for eight
-    // heads the columns of head h come out of XCD h, where the attention
-    // calls that read them place head h (the self-attention workgroup of
-    // head h and the cross-attention splits of head h run there).
+    // Workgroups i and i + 8 run on one XCD. With the column blocks a
+    // multiple of 8, class x (workgroups x, x + 8, ...) takes the contiguous
+    // x-th eighth of the columns, so for eight heads the columns of head h
+    // come out of one XCD, the class the attention calls that read them give
+    // head h (its self-attention workgroup and its cross-attention splits);
+    // it is the same XCD when the dispatches start their rounds of XCDs
+    // alike, which varies.
     const int nblk = gridDim.x;
     const int blk = nblk % 8 == 0 ? (blockIdx.x % 8) * (nblk / 8) + blockIdx.x / 8 : blockIdx.x;
     const int n0 = blk * kGemvCols;
