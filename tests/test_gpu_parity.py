@@ -316,6 +316,12 @@ DEC_CASES = [
     # Whisper Base geometry with the largest query count (8) on the split path
     (None, dict(n_layers=1, n_streams=1, n_q=8, mem_len=1500, d_model=512, n_heads=8,
                 head_dim=64)),
+    # more (stream, head) pairs than compute units (264, 320): split in 3 only to even out the
+    # workgroups per unit, merged in launch (fp32 with 2 queries; bf16 like Large)
+    (None, dict(n_layers=1, n_streams=33, n_q=2, mem_len=800, d_model=256, n_heads=8,
+                head_dim=32)),
+    (None, dict(n_layers=1, n_streams=40, mem_len=800, d_model=256, n_heads=8, head_dim=32,
+                dtype="bf16")),
 ]
 
 
