@@ -110,7 +110,11 @@ int cke_xattn_num_splits(const cke_xattn_geom* g);
 
 /* Create a handle over caller-allocated device regions k_dev, v_dev (each
  * cke_xattn_region_bytes) and ws_dev (cke_xattn_workspace_bytes, 256-byte
- * aligned). The handle starts NOT ready. */
+ * aligned). The handle starts NOT ready. The first creation of a handle with
+ * a split geometry (cke_xattn_num_splits > 1) on a device runs a short
+ * placement probe there (one kernel on a private stream, waited for; see
+ * cke_xattn_set_merge_mode), so do it outside stream capture; later
+ * creations reuse its result. */
 int cke_xattn_cache_create(const cke_xattn_geom* g, void* k_dev, void* v_dev,
                            void* ws_dev, cke_xattn_cache** out);
 
