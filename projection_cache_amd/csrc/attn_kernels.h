@@ -183,7 +183,6 @@ __global__ __launch_bounds__(NW * 64) void xattn_partial_kernel(
     using RM = RowMap<D, TE>;
     constexpr int VEC = RM::kVec, LPK = RM::kLPK, KPW = RM::kKPW;
     __shared__ float wm[NW * NQ], wl[NW * NQ], wa[NW * NQ * D];
-    __shared__ float sM[NQ], sL[NQ], sA[NQ * D];
 
     const int xcd = blockIdx.x % 8, k_on_xcd = blockIdx.x / 8;
     const int head_slot = k_on_xcd / nsplit;
@@ -215,27 +214,32 @@ __global__ __launch_bounds__(NW * 64) void xattn_partial_kernel(
     WaveState<NQ, VEC> st;
     st.init();
     wave_attend<D, TE, NQ, NP, STREAM>(K, V, r0, r1, qr, nq, sl2, st);
-    wg_merge<D, TE, NQ, NW>(st, nq, wm, wl, wa, sM, sL, sA);
+    wg_share<D, TE, NQ, NW>(st, nq, wm, wl, wa);
 
-    if (nsplit == 1) {
-        for (int idx = threadIdx.x; idx < nq * D; idx += NW * 64) {
-            const int i = idx / D, d = idx % D;
-            out[(((size_t)b * nq + i) * H + h) * D + d] = sA[i * D + d] / sL[i];
+    // one thread per (query, dim) writes the output (one split) or the
+    // partial, layout [B][max_q][H][nsplit][D+2]: M, L, acc[0..D); the
+    // thread of dim 0 adds M and L
+    for (int idx = threadIdx.x; idx < nq * D; idx += NW * 64) {
+        const int i = idx / D, d = idx % D;
+        float M, L, A;
+        wg_combine<D, NQ, NW>(wm, wl, wa, i, d, M, L, A);
+        if (nsplit == 1) {
+            out[(((size_t)b * nq + i) * H + h) * D + d] = A / L;
+            if (stats && d == 0) {
+                float* st2 = stats + (((size_t)b * max_q + i) * H + h) * 2;
+                st2[0] = M;
+                st2[1] = L;
+            }
+        } else {
+            float* p = part + ((((size_t)b * max_q + i) * H + h) * nsplit + split) * (D + 2);
+            p[2 + d] = A;
+            if (d == 0) {
+                p[0] = M;
+                p[1] = L;
+            }
         }
-        if (stats && threadIdx.x < nq) {
-            float* st2 = stats + (((size_t)b * max_q + threadIdx.x) * H + h) * 2;
-            st2[0] = sM[threadIdx.x];
-            st2[1] = sL[threadIdx.x];
-        }
-        return;
     }
-    // partial layout [B][max_q][H][nsplit][D+2]: M, L, acc[0..D)
-    for (int idx = threadIdx.x; idx < nq * (D + 2); idx += NW * 64) {
-        const int i = idx / (D + 2), k = idx % (D + 2);
-        float* p = part + ((((size_t)b * max_q + i) * H + h) * nsplit + split) * (D + 2);
-        p[k] = k == 0 ? sM[i] : (k == 1 ? sL[i] : sA[i * D + k - 2]);
-    }
-    if (!tickets) return;
+    if (nsplit == 1 || !tickets) return;
     // this thread's partial stores acknowledged by L2 (the clobber keeps the
     // compiler from moving any store below the wait)
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -314,7 +318,6 @@ __global__ __launch_bounds__(NW * 64) void selfattn_append_kernel(
     using RM = RowMap<D, TE>;
     constexpr int VEC = RM::kVec, LPK = RM::kLPK, KPW = RM::kKPW;
     __shared__ float wm[NW], wl[NW], wa[NW * D];
-    __shared__ float sM[1], sL[1], sA[D];
 
     const int h = blockIdx.x, s = blockIdx.y;
     const size_t bh = (size_t)s * H + h;
@@ -360,12 +363,17 @@ __global__ __launch_bounds__(NW * 64) void selfattn_append_kernel(
             for (int j = 0; j < VEC; ++j) out[bh * D + sub * VEC + j] = st.acc[0][j] / st.l[0];
         }
     } else {
-        wg_merge<D, TE, 1, NW>(st, 1, wm, wl, wa, sM, sL, sA);
-        for (int d = threadIdx.x; d < D; d += NW * 64) out[bh * D + d] = sA[d] / sL[0];
+        wg_share<D, TE, 1, NW>(st, 1, wm, wl, wa);
+        for (int d = threadIdx.x; d < D; d += NW * 64) {
+            float M, L, A;
+            wg_combine<D, 1, NW>(wm, wl, wa, 0, d, M, L, A);
+            out[bh * D + d] = A / L;
+        }
     }
     // Scatter the new row last. No wave reads it from memory (its owner folds
     // it in from k_new / v_new), and stored earlier its loads and stores would
-    // come before, and delay, the cache-row loads.
+    // come before, and delay, the cache-row loads; stored from the owner's
+    // registers before the merge, the barrier would wait for the stores.
     for (int d = threadIdx.x; d < D; d += NW * 64) {
         if constexpr (sizeof(TE) == 2) {
             K[(size_t)pos * D + d] = to_bf16_bits(kn[d]);
@@ -508,7 +516,6 @@ __global__ __launch_bounds__(NW * 64) void selfattn_prefill_groups_kernel(
     using RM = RowMap<D, TE>;
     constexpr int VEC = RM::kVec, LPK = RM::kLPK, KPW = RM::kKPW;
     __shared__ float wm[NW * QB], wl[NW * QB], wa[NW * QB * D];
-    __shared__ float sM[QB], sL[QB], sA[QB * D];
     const int s = blockIdx.y;
     const int hk = blockIdx.x / Z, j = blockIdx.x - hk * Z;
     const int G = Hq / Hkv;
@@ -560,10 +567,12 @@ __global__ __launch_bounds__(NW * 64) void selfattn_prefill_groups_kernel(
     WaveState<QB, VEC> st;
     st.init();
     wave_attend_causal_span<D, TE, QB, NP>(K, V, kn, vn, new_stride, pos, r0, r1, lim_w, qr, nq, sl2, st);
-    wg_merge<D, TE, QB, NW>(st, nq, wm, wl, wa, sM, sL, sA);
+    wg_share<D, TE, QB, NW>(st, nq, wm, wl, wa);
     for (int x = threadIdx.x; x < nq * D; x += NW * 64) {
         const int k = x / D, d = x % D;
-        out[(((size_t)s * n_new + i0 + k) * Hq + h) * D + d] = sA[k * D + d] / sL[k];
+        float M, L, A;
+        wg_combine<D, QB, NW>(wm, wl, wa, k, d, M, L, A);
+        out[(((size_t)s * n_new + i0 + k) * Hq + h) * D + d] = A / L;
     }
 }
 

@@ -181,7 +181,7 @@ struct RowMap {
 // Running softmax state of one lane group (the LPK lanes sharing a row slot)
 // for up to NQ queries: m is the group's running max in the base-2 domain
 // (scores pre-multiplied by scale*log2 e), l and acc the sums relative to it.
-// wg_merge() combines the groups of a wave and then the waves.
+// wg_share() and wg_combine() combine the groups of a wave and then the waves.
 template <int NQ, int VEC>
 struct WaveState {
     float m[NQ];
@@ -246,7 +246,7 @@ __device__ __forceinline__ void load_tile(const TE* __restrict__ K, const TE* __
 // Fold one loaded tile into the lane group's running softmax state. Each
 // group of LPK lanes (one row slot) keeps its own running max, so a tile
 // needs no communication across groups; groups are merged once, in
-// wg_merge. Lanes of a group hold identical scores and max. Rows past r1 get
+// wave_merge_groups. Lanes of a group hold identical scores and max. Rows past r1 get
 // score -inf and a zero V share (their loaded bytes may be anything); the
 // row equal to cur_row uses the values ck/cv instead of the loaded ones.
 template <int D, typename TE, int NQ, int NP>
@@ -500,13 +500,17 @@ __device__ __forceinline__ void wave_merge_groups(WaveState<NQ, RowMap<D, TE>::k
     }
 }
 
-// Merge the NW waves of a workgroup. Afterwards, for i < nq and d < D,
-// sM[i], sL[i], sA[i*D + d] hold the workgroup's (max, sum, unnormalised
-// output). LDS scratch: wm, wl [NW*NQ], wa [NW*NQ*D]. Ends with a barrier.
+// Merge the NW waves of a workgroup, in two parts. wg_share merges the row
+// groups of each wave, leaves every wave's (max, sum, unnormalised output) in
+// LDS (wm, wl [NW*NQ], wa [NW*NQ*D]) and ends with a barrier. wg_combine then
+// forms, for one query i and dim d,
+//   M = max_w m_w,  L = sum_w l_w 2^(m_w - M),  A = sum_w a_w[d] 2^(m_w - M)
+// over the waves in ascending order. Each thread that writes (i, d) forms M
+// and L itself, so the results leave with no second barrier, and any two
+// threads form the same M and L bit for bit.
 template <int D, typename TE, int NQ, int NW>
-__device__ __forceinline__ void wg_merge(
-    WaveState<NQ, RowMap<D, TE>::kVec>& st, int nq, float* wm, float* wl,
-    float* wa, float* sM, float* sL, float* sA)
+__device__ __forceinline__ void wg_share(WaveState<NQ, RowMap<D, TE>::kVec>& st, int nq,
+                                         float* wm, float* wl, float* wa)
 {
     using RM = RowMap<D, TE>;
     constexpr int VEC = RM::kVec, LPK = RM::kLPK;
@@ -515,34 +519,33 @@ __device__ __forceinline__ void wg_merge(
     wave_merge_groups<D, TE, NQ>(st, nq);
 #pragma unroll
     for (int i = 0; i < NQ; ++i) {
-        {
-            if (lane < LPK) {
+        if (lane < LPK) {
 #pragma unroll
-                for (int j = 0; j < VEC; ++j) wa[(w * NQ + i) * D + lane * VEC + j] = st.acc[i][j];
-            }
-            if (lane == 0) {
-                wm[w * NQ + i] = st.m[i];
-                wl[w * NQ + i] = st.l[i];
-            }
+            for (int j = 0; j < VEC; ++j) wa[(w * NQ + i) * D + lane * VEC + j] = st.acc[i][j];
+        }
+        if (lane == 0) {
+            wm[w * NQ + i] = st.m[i];
+            wl[w * NQ + i] = st.l[i];
         }
     }
     __syncthreads();
-    for (int idx = threadIdx.x; idx < nq * D; idx += NW * 64) {
-        const int i = idx / D, d = idx % D;
-        float M = -INFINITY;
+}
+
+template <int D, int NQ, int NW>
+__device__ __forceinline__ void wg_combine(const float* wm, const float* wl, const float* wa, int i,
+                                           int d, float& M, float& L, float& A)
+{
+    M = -INFINITY;
 #pragma unroll
-        for (int v = 0; v < NW; ++v) M = fmaxf(M, wm[v * NQ + i]);
-        float L = 0.f, A = 0.f;
+    for (int v = 0; v < NW; ++v) M = fmaxf(M, wm[v * NQ + i]);
+    L = 0.f;
+    A = 0.f;
 #pragma unroll
-        for (int v = 0; v < NW; ++v) {
-            const float f = fast_exp2(wm[v * NQ + i] - M);
-            L = fmaf(wl[v * NQ + i], f, L);
-            A = fmaf(wa[(v * NQ + i) * D + d], f, A);
-        }
-        sA[i * D + d] = A;
-        if (d == 0) { sM[i] = M; sL[i] = L; }
+    for (int v = 0; v < NW; ++v) {
+        const float f = fast_exp2(wm[v * NQ + i] - M);
+        L = fmaf(wl[v * NQ + i], f, L);
+        A = fmaf(wa[(v * NQ + i) * D + d], f, A);
     }
-    __syncthreads();
 }
 
 }  // namespace cke
