@@ -592,6 +592,7 @@ __global__ __launch_bounds__(NW * 64) void selfattn_prefill_groups_kernel(
 #endif
 constexpr int kCrossNP = CKE_CROSS_NP;        // row passes per load tile (16- and 8-bit rows)
 constexpr int kCrossNPf32 = CKE_CROSS_NP_F32; // row passes per load tile (fp32 rows)
+constexpr int kCrossNP16 = kCrossNP16Rows;    // bf16 rows, one query
 constexpr int kSelfWaves = CKE_SELF_WAVES;
 constexpr int kSelfNP = CKE_SELF_NP;
 
@@ -617,10 +618,16 @@ hipError_t launch_cross_nq(const XattnLaunch& a, hipStream_t st) {
     // count (Whisper Base 5.26 against 5.34 us per call with 4, Beam 8.64
     // against 8.83; 2 and 6 slower; before the in-launch merge, 4 passes had
     // taken Beam from 11.75 to 11.3 us against 2). bf16 and fp8 rows (8 or 16
-    // values per lane): 4 (Large 24.2 against 24.5 us with 3, over fp8 16.17
-    // against 16.35), but 2 with more than two queries: long tiles cost
-    // registers (fp8 spills from four queries on).
-    constexpr int NP = sizeof(TE) == 4 ? kCrossNPf32 : ((NQ > 2 && kCrossNP > 2) ? 2 : kCrossNP);
+    // values per lane): 4 (over fp8 16.17 against 16.35 us with 3), but 2
+    // with more than two queries: long tiles cost registers (fp8 spills from
+    // four queries on). bf16 rows and one query: 3, whose 80 VGPRs let a
+    // compute unit hold 6 of these workgroups (4 at the 97 VGPRs of 4 passes),
+    // so the 4-way split of Large's 320 heads, 5 per unit, is resident at
+    // once: 22.97 against 23.98 us per call (4 passes, 3 splits).
+    constexpr int NP = sizeof(TE) == 4
+                           ? kCrossNPf32
+                           : ((sizeof(TE) == 2 && NQ == 1) ? kCrossNP16
+                                                           : ((NQ > 2 && kCrossNP > 2) ? 2 : kCrossNP));
     const int n_bh = a.B * a.H;
     dim3 grid(8 * a.nsplit * ((n_bh + 7) / 8));
     unsigned* tickets =

@@ -106,13 +106,15 @@ static_assert(CKE_MAX_SPLITS >= 1 && CKE_MAX_SPLITS <= cke::kMaxSplits, "split c
 //    unit, but B*H workgroups over 256 units leave some units one workgroup
 //    more than others (Large: 320 heads, 64 units with two), and each unit
 //    streams at a capped rate, so the busiest units set the call's time.
-//    Split into s pieces (2 <= s <= 8, at least 256 rows each, at most 4
-//    workgroups per compute unit, so that every workgroup is resident at
-//    once) when that evens out the workgroups per unit: s minimises
-//    ceil(B*H*s / 256) * 256 / (B*H*s), ties to the smaller s. Large (bf16
-//    cache): 3 splits, 24.1 against 26.3 us per call on one box (4 splits
-//    24.1, 5 24.3, 8 24.5); over its fp8 cache 16.2 against 16.7 us (2
-//    splits 16.3; 4 splits 18.3: five workgroups per unit do not all fit).
+//    Split into s pieces (2 <= s <= 8, at least 256 rows each, at most
+//    cross_units_cap workgroups per compute unit, so that every workgroup is
+//    resident at once) when that evens out the workgroups per unit: s
+//    minimises ceil(B*H*s / 256) * 256 / (B*H*s), ties to the smaller s.
+//    Large (bf16 cache): 4 splits, 5 workgroups on every unit, 22.97 against
+//    26.3 us per call unsplit (3 splits, the best while a unit held only 4 of
+//    these workgroups: 24.0); over its fp8 cache 3 splits, 16.2 against 16.7
+//    us (2 splits 16.3; 4 splits 18.3: five workgroups per unit do not all
+//    fit).
 double unit_imbalance(long long wgs) {
     const long long units = CKE_TARGET_WGS;
     return (double)((wgs + units - 1) / units) * units / (double)wgs;
@@ -135,7 +137,7 @@ void split_plan(const cke_xattn_geom* g, int* nsplit, int* chunk) {
         if (s < 1) s = 1;
     } else {
         double best = unit_imbalance(bh);
-        for (int t = 2; t <= 8 && t <= max_by_rows && bh * t <= 4LL * CKE_TARGET_WGS &&
+        for (int t = 2; t <= 8 && t <= max_by_rows && bh * t <= (long long)cke::cross_units_cap(elem_bytes(g->cache_dtype), g->max_q) * CKE_TARGET_WGS &&
                         g->mem_len >= 256LL * t; ++t) {
             const double im = unit_imbalance(bh * t);
             if (im < best - 1e-9) {

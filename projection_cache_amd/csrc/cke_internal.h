@@ -31,6 +31,21 @@ constexpr size_t kTicketBytes = 128;
 #define CKE_CROSS_WAVES 4
 #endif
 constexpr int kCrossWaves = CKE_CROSS_WAVES;  // waves per cross-decode workgroup
+#ifndef CKE_CROSS_NP_BF16
+#define CKE_CROSS_NP_BF16 3
+#endif
+constexpr int kCrossNP16Rows = CKE_CROSS_NP_BF16;  // row passes per load tile: bf16 rows, one query
+
+// Most split-kernel workgroups the split plan puts on one compute unit when
+// there are at least as many (stream, head) pairs as units: as many as a unit
+// holds at once, so no workgroup waits for another to finish. Register-limited
+// as compiled (4 waves per workgroup, 512 VGPRs per SIMD lane): bf16 rows with
+// one query take 80 VGPRs (3-pass tiles), so 6 fit; fp8 rows take 115, so 4.
+// Other cases keep 4 (fp32 and multi-query geometries with that many pairs
+// were not measured).
+inline int cross_units_cap(int elem_bytes, int max_q) {
+    return (elem_bytes == 2 && max_q == 1 && kCrossNP16Rows <= 3) ? 6 : 4;
+}
 
 // Merge of split partials: merge_lanes(nsplit) lanes (1, 2, 4 or 8) share one
 // output, each folding at most kMergePer splits (nsplit <= 64).

@@ -99,17 +99,21 @@ def test_workspace_and_split_plan():
 def test_split_plan_evens_out_workgroups_per_compute_unit():
     """With at least 256 (stream, head) pairs the unsplit grid covers the 256
     compute units; the plan then splits a head into s pieces (2..8, >= 256
-    rows each, <= 4 workgroups per unit) only where that evens out the
-    workgroups per unit, s minimising ceil(B*H*s/256)*256/(B*H*s)."""
-    def splits(n_streams, n_heads, mem_len=1500, dt=pc.CKE_BF16):
+    rows each, at most 6 workgroups per unit for single-query bf16 caches and
+    4 otherwise) only where that evens out the workgroups per unit, s
+    minimising ceil(B*H*s/256)*256/(B*H*s)."""
+    def splits(n_streams, n_heads, mem_len=1500, dt=pc.CKE_BF16, max_q=1):
         return pc.cke_xattn_num_splits(base_geom(n_layers=1, n_streams=n_streams, n_heads=n_heads,
                                                  d_model=64 * n_heads, mem_len=mem_len,
-                                                 cache_dtype=dt))
-    assert splits(16, 20) == 3                # Large: 320 pairs -> 960 workgroups (3.75 per unit)
-    assert splits(16, 20, dt=pc.CKE_FP8) == 3
+                                                 cache_dtype=dt, max_q=max_q))
+    assert splits(16, 20) == 4                # Large: 320 pairs -> 1280 workgroups (5 per unit)
+    assert splits(16, 20, dt=pc.CKE_FP8) == 3  # at most 4 per unit: 960 (3.75 per unit)
+    assert splits(16, 20, dt=pc.CKE_F32) == 3
+    assert splits(16, 20, max_q=2) == 3
     assert splits(32, 16) == 1                # 512 pairs: two per unit already
     assert splits(16, 16) == 1                # 256: one per unit
-    assert splits(15, 20) == 3                # 300 pairs: 1.17 -> 900 workgroups (3.52 per unit)
+    assert splits(15, 20) == 5                # 300 pairs: 1.17 -> 1500 workgroups (5.86 per unit)
+    assert splits(15, 20, dt=pc.CKE_FP8) == 3  # 900 workgroups (3.52 per unit)
     assert splits(64, 20) == 1                # 1280 pairs: five per unit; no room to split
     assert splits(16, 20, mem_len=600) == 2   # at least 256 rows per split
     assert splits(16, 20, mem_len=300) == 1

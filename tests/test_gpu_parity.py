@@ -317,7 +317,8 @@ DEC_CASES = [
     (None, dict(n_layers=1, n_streams=1, n_q=8, mem_len=1500, d_model=512, n_heads=8,
                 head_dim=64)),
     # more (stream, head) pairs than compute units (264, 320): split in 3 only to even out the
-    # workgroups per unit, merged in launch (fp32 with 2 queries; bf16 like Large)
+    # workgroups per unit, merged in launch (fp32 with 2 queries; bf16 like Large, whose 800
+    # rows allow at most 3 splits of 256)
     (None, dict(n_layers=1, n_streams=33, n_q=2, mem_len=800, d_model=256, n_heads=8,
                 head_dim=32)),
     (None, dict(n_layers=1, n_streams=40, mem_len=800, d_model=256, n_heads=8, head_dim=32,
@@ -1104,8 +1105,9 @@ def test_full_size_decode_every_head(name):
     the last layer, with the cache holding seeded slabs of the projected
     spread (stored exactly in the cache type), against the oracle on the same
     slabs. A cache this large (K and V of 32 layers, far above the 256 MB
-    MALL) is read with streaming loads, and its 320 heads are split in 3 and
-    merged in the same launch: this is those paths' full-size parity case."""
+    MALL) is read with streaming loads, and its 320 heads are split (in 4
+    over the bf16 cache, 3 over fp8) and merged in the same launch: this is
+    those paths' full-size parity case."""
     g = synth.get(name)
     cache = pc.XattnCache(g.n_layers, g.n_streams, g.mem_len, g.d_model, g.n_heads, g.head_dim,
                           max_q=g.n_q, dtype=CACHE_DT[g.dtype])
@@ -1131,6 +1133,7 @@ def test_full_size_decode_every_head(name):
             want = oracle.cross_decode(q, kv[0], kv[1], g.scale)
             assert max_abs(got, want) <= TOL["f32"], (l, step)
     # the full-size heads are split and merged in launch
+    assert pc.cke_xattn_num_splits(cache.geom) == (4 if g.dtype == "bf16" else 3)
     assert pc.cke_xattn_merges_in_launch(cache, g.n_q)
 
 
