@@ -350,10 +350,13 @@ __global__ __launch_bounds__(NW * 64) void selfattn_append_kernel(
     WaveState<1, VEC> st;
     st.init();
     wave_attend<D, TE, 1, NP>(K, V, r0, min(r1, pos), qr, 1, sl2, st);
+    uint4 ck = make_uint4(0u, 0u, 0u, 0u), cv = ck;
     if (has_cur) {
         keep_below(ckr);
         keep_below(cvr);
-        fold_row<D, TE, 1>(pos, pack_cur<TE>(ckr), pack_cur<TE>(cvr), lane / LPK, qr, 1, sl2, st);
+        ck = pack_cur<TE>(ckr);
+        cv = pack_cur<TE>(cvr);
+        fold_row<D, TE, 1>(pos, ck, cv, lane / LPK, qr, 1, sl2, st);
     }
     if constexpr (NW == 1) {
         // one wave holds every row: no cross-wave merge, no barrier
@@ -370,18 +373,13 @@ __global__ __launch_bounds__(NW * 64) void selfattn_append_kernel(
             out[bh * D + d] = A / L;
         }
     }
-    // Scatter the new row last. No wave reads it from memory (its owner folds
-    // it in from k_new / v_new), and stored earlier its loads and stores would
-    // come before, and delay, the cache-row loads; stored from the owner's
-    // registers before the merge, the barrier would wait for the stores.
-    for (int d = threadIdx.x; d < D; d += NW * 64) {
-        if constexpr (sizeof(TE) == 2) {
-            K[(size_t)pos * D + d] = to_bf16_bits(kn[d]);
-            V[(size_t)pos * D + d] = to_bf16_bits(vn[d]);
-        } else {
-            K[(size_t)pos * D + d] = kn[d];
-            V[(size_t)pos * D + d] = vn[d];
-        }
+    // Scatter the new row last, from its owner's registers (the values it
+    // folded in). No wave reads it from memory. Stored before the cache-row
+    // loads it would delay them, and stored before the merge the barrier
+    // would wait for the stores.
+    if (has_cur && lane < LPK) {
+        *reinterpret_cast<uint4*>(K + (size_t)pos * D + sub * VEC) = ck;
+        *reinterpret_cast<uint4*>(V + (size_t)pos * D + sub * VEC) = cv;
     }
 }
 
