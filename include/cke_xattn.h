@@ -108,6 +108,16 @@ size_t cke_xattn_workspace_bytes(const cke_xattn_geom* g);
  * geometry, so results are run-to-run deterministic). 0 if invalid. */
 int cke_xattn_num_splits(const cke_xattn_geom* g);
 
+/* Number of leading (stream, head) pairs, b*H + h < this value, that a decode
+ * call of this geometry runs unsplit, one workgroup each; the others use
+ * cke_xattn_num_splits splits. Nonzero only when B*H = 256k + R with R a
+ * multiple of 8 that divides 256: the first 256k pairs whole and the last R
+ * split 256/R ways, so each of the 256 compute units streams k whole pairs
+ * and one split piece, and the split pairs, finished early, merge while whole
+ * pairs still stream. A plan choice only: results agree with any other split
+ * to rounding. 0 if invalid. */
+int cke_xattn_whole_pairs(const cke_xattn_geom* g);
+
 /* Create a handle over caller-allocated device regions k_dev, v_dev (each
  * cke_xattn_region_bytes) and ws_dev (cke_xattn_workspace_bytes, 256-byte
  * aligned). The handle starts NOT ready. The first creation of a handle with

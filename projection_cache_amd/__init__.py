@@ -68,6 +68,8 @@ _lib.cke_xattn_workspace_bytes.restype = _SZ
 _lib.cke_xattn_workspace_bytes.argtypes = [ctypes.POINTER(cke_xattn_geom)]
 _lib.cke_xattn_num_splits.restype = _I
 _lib.cke_xattn_num_splits.argtypes = [ctypes.POINTER(cke_xattn_geom)]
+_lib.cke_xattn_whole_pairs.restype = _I
+_lib.cke_xattn_whole_pairs.argtypes = [ctypes.POINTER(cke_xattn_geom)]
 _lib.cke_xattn_cache_create.restype = _I
 _lib.cke_xattn_cache_create.argtypes = [ctypes.POINTER(cke_xattn_geom), _P, _P, _P,
                                         ctypes.POINTER(_P)]
@@ -129,7 +131,8 @@ _lib.cke_memory_lift_gelu_planes.restype = _I
 _lib.cke_memory_lift_gelu_planes.argtypes = [_P, _I, _I, _P, _SZ, _I, _P, _I, _P, _P, _SZ, _P]
 
 EXPORTED = ["cke_xattn_region_bytes", "cke_xattn_layer_offset_bytes",
-            "cke_xattn_workspace_bytes", "cke_xattn_num_splits", "cke_xattn_cache_create",
+            "cke_xattn_workspace_bytes", "cke_xattn_num_splits", "cke_xattn_whole_pairs",
+            "cke_xattn_cache_create",
             "cke_xattn_cache_destroy", "cke_xattn_invalidate", "cke_xattn_is_ready",
             "cke_xattn_populate", "cke_xattn_populate_workspace_bytes", "cke_xattn_populate_ws",
             "cke_memory_lift_workspace_bytes", "cke_memory_lift_gelu_ws",
@@ -241,6 +244,10 @@ def cke_xattn_workspace_bytes(g: cke_xattn_geom) -> int:
 
 def cke_xattn_num_splits(g: cke_xattn_geom) -> int:
     return int(_lib.cke_xattn_num_splits(ctypes.byref(g)))
+
+
+def cke_xattn_whole_pairs(g: cke_xattn_geom) -> int:
+    return int(_lib.cke_xattn_whole_pairs(ctypes.byref(g)))
 
 
 def cke_xattn_cache_create(g: cke_xattn_geom, k_dev, v_dev, ws_dev) -> int:

@@ -128,12 +128,12 @@ __device__ __forceinline__ void merge_head(const float* __restrict__ part, float
 template <int D>
 __global__ __launch_bounds__(256) void xattn_merge_kernel(
     const float* __restrict__ part, float* __restrict__ out, float* __restrict__ stats, int nq,
-    int max_q, int H, int nsplit, int n_bh, int Z)
+    int max_q, int H, int nsplit, int n_bh, int Z, int n_whole)
 {
     const int xcd = blockIdx.x % 8, k_on_xcd = blockIdx.x / 8;
     const int head_slot = k_on_xcd / Z;
     const int z = k_on_xcd - head_slot * Z;
-    const int hb = xcd + 8 * head_slot;
+    const int hb = n_whole + xcd + 8 * head_slot;
     if (hb >= n_bh) return;
     merge_head<D, false>(part, out, stats, nq, max_q, H, nsplit, hb / H, hb % H,
                          z * blockDim.x + threadIdx.x, Z * blockDim.x);
@@ -178,16 +178,21 @@ __global__ __launch_bounds__(NW * 64) void xattn_partial_kernel(
     const float* __restrict__ q, const TE* __restrict__ Kl, const TE* __restrict__ Vl,
     float* __restrict__ out, float* __restrict__ part, float* __restrict__ stats,
     unsigned* __restrict__ tickets, int nq, int max_q, int H, int T, int nsplit, int chunk,
-    int n_bh, float sl2)
+    int n_bh, int n_whole, float sl2)
 {
     using RM = RowMap<D, TE>;
     constexpr int VEC = RM::kVec, LPK = RM::kLPK, KPW = RM::kKPW;
     __shared__ float wm[NW * NQ], wl[NW * NQ], wa[NW * NQ * D];
 
-    const int xcd = blockIdx.x % 8, k_on_xcd = blockIdx.x / 8;
-    const int head_slot = k_on_xcd / nsplit;
-    const int split = k_on_xcd - head_slot * nsplit;
-    const int hb = xcd + 8 * head_slot;
+    // workgroups 0 .. n_whole-1: pairs 0 .. n_whole-1 whole; then the split
+    // pairs, placed by class as above (n_whole is a multiple of 8)
+    const int j = (int)blockIdx.x - n_whole;
+    const bool whole = j < 0;
+    const int xcd = j & 7, k_on_xcd = j >> 3;
+    const int head_slot = whole ? 0 : k_on_xcd / nsplit;
+    const int split = whole ? 0 : k_on_xcd - head_slot * nsplit;
+    const int hb = whole ? (int)blockIdx.x : n_whole + xcd + 8 * head_slot;
+    const int ns = whole ? 1 : nsplit;   // splits of this pair
     if (hb >= n_bh) return;   // B*H not a multiple of 8: this XCD has one head fewer
     const int h = hb % H, b = hb / H;
     const size_t bh = (size_t)hb;
@@ -206,7 +211,7 @@ __global__ __launch_bounds__(NW * 64) void xattn_partial_kernel(
     }
 
     const int c0 = split * chunk;
-    const int c1 = min(T, c0 + chunk);
+    const int c1 = whole ? T : min(T, c0 + chunk);
     const int per_wave = ((c1 - c0 + NW * KPW - 1) / (NW * KPW)) * KPW;
     const int r0 = min(c1, c0 + w * per_wave);
     const int r1 = min(c1, r0 + per_wave);
@@ -223,7 +228,7 @@ __global__ __launch_bounds__(NW * 64) void xattn_partial_kernel(
         const int i = idx / D, d = idx % D;
         float M, L, A;
         wg_combine<D, NQ, NW>(wm, wl, wa, i, d, M, L, A);
-        if (nsplit == 1) {
+        if (ns == 1) {
             out[(((size_t)b * nq + i) * H + h) * D + d] = A / L;
             if (stats && d == 0) {
                 float* st2 = stats + (((size_t)b * max_q + i) * H + h) * 2;
@@ -239,7 +244,7 @@ __global__ __launch_bounds__(NW * 64) void xattn_partial_kernel(
             }
         }
     }
-    if (nsplit == 1 || !tickets) return;
+    if (ns == 1 || !tickets) return;
     // this thread's partial stores acknowledged by L2 (the clobber keeps the
     // compiler from moving any store below the wait)
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -627,7 +632,7 @@ hipError_t launch_cross_nq(const XattnLaunch& a, hipStream_t st) {
                            : ((sizeof(TE) == 2 && NQ == 1) ? kCrossNP16
                                                            : ((NQ > 2 && kCrossNP > 2) ? 2 : kCrossNP));
     const int n_bh = a.B * a.H;
-    dim3 grid(8 * a.nsplit * ((n_bh + 7) / 8));
+    dim3 grid(a.n_whole + 8 * a.nsplit * ((n_bh - a.n_whole + 7) / 8));
     unsigned* tickets =
         (a.tickets && merge_in_launch_fits(a.nq, D, a.nsplit, n_bh, a.max_q)) ? a.tickets : nullptr;
     // non-temporal buffer loads for fp32 caches and for 16- and 8-bit caches
@@ -639,20 +644,20 @@ hipError_t launch_cross_nq(const XattnLaunch& a, hipStream_t st) {
                            dim3(kCrossWaves * 64), 0, st, a.q,
                            static_cast<const TE*>(a.K), static_cast<const TE*>(a.V), a.out,
                            a.part, a.stats, tickets, a.nq, a.max_q, a.H, a.T, a.nsplit, a.chunk,
-                           n_bh, a.scale * kLog2e);
+                           n_bh, a.n_whole, a.scale * kLog2e);
     else
         hipLaunchKernelGGL((xattn_partial_kernel<D, TE, NQ, kCrossWaves, NP, false>), grid,
                            dim3(kCrossWaves * 64), 0, st, a.q,
                            static_cast<const TE*>(a.K), static_cast<const TE*>(a.V), a.out,
                            a.part, a.stats, tickets, a.nq, a.max_q, a.H, a.T, a.nsplit, a.chunk,
-                           n_bh, a.scale * kLog2e);
+                           n_bh, a.n_whole, a.scale * kLog2e);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.nsplit == 1 || tickets) return e;
     const int lanes = a.nq * D * merge_lanes(a.nsplit);
     const int threads = lanes >= 256 ? 256 : ((lanes + 63) / 64) * 64;
     const int Z = (lanes + threads - 1) / threads;
-    hipLaunchKernelGGL((xattn_merge_kernel<D>), dim3(8 * Z * ((n_bh + 7) / 8)), dim3(threads), 0, st,
-                       a.part, a.out, a.stats, a.nq, a.max_q, a.H, a.nsplit, n_bh, Z);
+    hipLaunchKernelGGL((xattn_merge_kernel<D>), dim3(8 * Z * ((n_bh - a.n_whole + 7) / 8)), dim3(threads), 0,
+                       st, a.part, a.out, a.stats, a.nq, a.max_q, a.H, a.nsplit, n_bh, Z, a.n_whole);
     return hipGetLastError();
 }
 

@@ -27,6 +27,7 @@ struct cke_xattn_cache {
     int ready;
     int nsplit;
     int chunk;
+    int n_whole;           // pairs 0 .. n_whole-1 decoded unsplit (split_plan)
     int merge_in_launch;   // split decode merges in its own launch (device placement verified)
 };
 
@@ -115,12 +116,21 @@ static_assert(CKE_MAX_SPLITS >= 1 && CKE_MAX_SPLITS <= cke::kMaxSplits, "split c
 //    these workgroups: 24.0); over its fp8 cache 3 splits, 16.2 against 16.7
 //    us (2 splits 16.3; 4 splits 18.3: five workgroups per unit do not all
 //    fit).
+//  * Where B*H = 256k + R with R dividing 256, whole pairs plus one split
+//    group instead (cke_xattn_whole_pairs): Large's 320 pairs as 256 whole
+//    and 64 split in 4, one whole pair and one piece per unit. A uniform
+//    split ends with every head's merge after the last rows are streamed;
+//    here the split pairs finish early and merge while the whole pairs still
+//    stream, and whole pairs need no merge: Large 21.96 against 23.04 us per
+//    call (4 uniform splits), over fp8 15.48 against 15.95 (3 splits).
 double unit_imbalance(long long wgs) {
     const long long units = CKE_TARGET_WGS;
     return (double)((wgs + units - 1) / units) * units / (double)wgs;
 }
 
-void split_plan(const cke_xattn_geom* g, int* nsplit, int* chunk) {
+void split_plan(const cke_xattn_geom* g, int* nsplit, int* chunk, int* n_whole = nullptr) {
+    int whole = 0;
+    if (n_whole) *n_whole = 0;
     if (g->mem_len <= cke::kShortMemRows) {  // one wave per head, no split
         *nsplit = 1;
         *chunk = g->mem_len;
@@ -145,11 +155,25 @@ void split_plan(const cke_xattn_geom* g, int* nsplit, int* chunk) {
                 s = t;
             }
         }
+        // B*H = 256k + R with R dividing 256 (and a multiple of 8): the
+        // first 256k pairs whole (k per unit) and the last R split 256/R ways
+        // (one piece per unit), so every unit streams the same rows and the
+        // split pairs, done early, merge while whole pairs still stream.
+        const long long R = bh % CKE_TARGET_WGS;
+        if (R > 0 && R % 8 == 0 && CKE_TARGET_WGS % R == 0) {
+            const long long t = CKE_TARGET_WGS / R;
+            if (t >= 2 && t <= 8 && t <= max_by_rows && g->mem_len >= 256LL * t &&
+                bh / CKE_TARGET_WGS + 1 <= cke::cross_units_cap(elem_bytes(g->cache_dtype), g->max_q)) {
+                s = (int)t;
+                whole = (int)(bh - R);
+            }
+        }
     }
     int c = (g->mem_len + s - 1) / s;
     c = ((c + kpp - 1) / kpp) * kpp;
     *chunk = c;
     *nsplit = (g->mem_len + c - 1) / c;
+    if (n_whole) *n_whole = *nsplit > 1 ? whole : 0;
 }
 
 constexpr size_t kAlign = 256;
@@ -238,6 +262,13 @@ int cke_xattn_num_splits(const cke_xattn_geom* g) {
     return s;
 }
 
+int cke_xattn_whole_pairs(const cke_xattn_geom* g) {
+    if (check_geom(g) != CKE_OK) return 0;
+    int s, c, w;
+    split_plan(g, &s, &c, &w);
+    return w;
+}
+
 size_t cke_xattn_workspace_bytes(const cke_xattn_geom* g) {
     if (check_geom(g) != CKE_OK) return 0;
     int s, c;
@@ -264,7 +295,7 @@ int cke_xattn_cache_create(const cke_xattn_geom* g, void* k_dev, void* v_dev, vo
     c->v = v_dev;
     c->ws = ws_dev;
     c->ready = 0;
-    split_plan(g, &c->nsplit, &c->chunk);
+    split_plan(g, &c->nsplit, &c->chunk, &c->n_whole);
     // split geometries: verify (once per device) that the dispatcher keeps
     // workgroups i and i + 8 on one XCD, which the in-launch merge relies on
     c->merge_in_launch = c->nsplit > 1 && xcd_placement_ok();
@@ -532,6 +563,7 @@ int cross_decode(const float* q, int n_q, const cke_xattn_cache* c, int layer, f
     a.max_q = g.max_q;
     a.nsplit = c->nsplit;
     a.chunk = c->chunk;
+    a.n_whole = c->n_whole;
     a.scale = scale;
     a.dtype = g.cache_dtype;
     // K and V of every layer together: a cache this much larger than the

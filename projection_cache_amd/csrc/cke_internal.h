@@ -17,6 +17,8 @@ struct XattnLaunch {
     float* out;
     float* part;         // workspace: split partials [B][max_q][H][nsplit][D+2]
     int B, H, T, D, nq, max_q, nsplit, chunk;
+    int n_whole;         // (stream, head) pairs 0 .. n_whole-1 run unsplit, one workgroup each
+                         // (a multiple of 8); the rest are split nsplit ways
     float scale;
     int dtype;           // CKE_F32, CKE_BF16 or CKE_FP8
     bool stream_rows;    // whole cross cache far larger than the MALL: non-temporal row loads

@@ -101,15 +101,19 @@ def test_split_plan_evens_out_workgroups_per_compute_unit():
     compute units; the plan then splits a head into s pieces (2..8, >= 256
     rows each, at most 6 workgroups per unit for single-query bf16 caches and
     4 otherwise) only where that evens out the workgroups per unit, s
-    minimising ceil(B*H*s/256)*256/(B*H*s)."""
+    minimising ceil(B*H*s/256)*256/(B*H*s); where B*H = 256k + R with R a
+    multiple of 8 dividing 256, it runs the first 256k pairs whole and splits
+    the last R pairs 256/R ways instead."""
     def splits(n_streams, n_heads, mem_len=1500, dt=pc.CKE_BF16, max_q=1):
         return pc.cke_xattn_num_splits(base_geom(n_layers=1, n_streams=n_streams, n_heads=n_heads,
                                                  d_model=64 * n_heads, mem_len=mem_len,
                                                  cache_dtype=dt, max_q=max_q))
-    assert splits(16, 20) == 4                # Large: 320 pairs -> 1280 workgroups (5 per unit)
-    assert splits(16, 20, dt=pc.CKE_FP8) == 3  # at most 4 per unit: 960 (3.75 per unit)
-    assert splits(16, 20, dt=pc.CKE_F32) == 3
-    assert splits(16, 20, max_q=2) == 3
+    assert splits(16, 20) == 4                # Large: 320 = 256 + 64 pairs (whole pairs below)
+    assert splits(16, 20, dt=pc.CKE_FP8) == 4
+    assert splits(16, 20, mem_len=1000) == 3  # < 256 rows per piece of 4: uniform, 960 workgroups
+    assert splits(16, 20, mem_len=1000, dt=pc.CKE_FP8) == 3
+    assert splits(16, 20, dt=pc.CKE_F32) == 4
+    assert splits(16, 20, max_q=2) == 4
     assert splits(32, 16) == 1                # 512 pairs: two per unit already
     assert splits(16, 16) == 1                # 256: one per unit
     assert splits(15, 20) == 5                # 300 pairs: 1.17 -> 1500 workgroups (5.86 per unit)
@@ -117,6 +121,20 @@ def test_split_plan_evens_out_workgroups_per_compute_unit():
     assert splits(64, 20) == 1                # 1280 pairs: five per unit; no room to split
     assert splits(16, 20, mem_len=600) == 2   # at least 256 rows per split
     assert splits(16, 20, mem_len=300) == 1
+    # whole pairs: B*H = 256k + R, R a multiple of 8 dividing 256, split 256/R ways
+    def whole(n_streams, n_heads, mem_len=1500, dt=pc.CKE_BF16):
+        return pc.cke_xattn_whole_pairs(base_geom(n_layers=1, n_streams=n_streams, n_heads=n_heads,
+                                                  d_model=64 * n_heads, mem_len=mem_len,
+                                                  cache_dtype=dt))
+    assert whole(16, 20) == 256 and whole(16, 20, dt=pc.CKE_FP8) == 256
+    assert whole(40, 8, mem_len=1024, dt=pc.CKE_F32) == 256
+    assert splits(40, 8, mem_len=1024, dt=pc.CKE_F32) == 4
+    assert whole(16, 20, mem_len=1000) == 0   # pieces of 4 would be < 256 rows
+    assert whole(15, 20) == 0                 # 300 = 256 + 44: 44 does not divide 256
+    assert whole(36, 8) == 0                  # 288 = 256 + 32: 8 pieces per pair, T / 8 < 256
+    assert whole(36, 8, mem_len=2048) == 256 and splits(36, 8, mem_len=2048) == 8
+    assert whole(32, 16) == 0 and whole(1, 8) == 0
+    assert pc.lib().cke_xattn_whole_pairs(None) == 0
     # fewer pairs than units: about one workgroup per unit, as before (chunks
     # rounded up to whole passes of the waves: 64 bf16 rows, 16 fp32 rows)
     assert splits(1, 8, dt=pc.CKE_F32) == 32     # Whisper Base

@@ -323,6 +323,11 @@ DEC_CASES = [
                 head_dim=32)),
     (None, dict(n_layers=1, n_streams=40, mem_len=800, d_model=256, n_heads=8, head_dim=32,
                 dtype="bf16")),
+    # 320 pairs = 256 whole (one workgroup each) + 64 split in 4: the whole-pairs plan (fp32,
+    # and bf16 with 2 queries)
+    (None, dict(n_layers=1, n_streams=40, mem_len=1024, d_model=256, n_heads=8, head_dim=32)),
+    (None, dict(n_layers=1, n_streams=40, n_q=2, mem_len=1100, d_model=256, n_heads=8, head_dim=32,
+                dtype="bf16")),
 ]
 
 
@@ -439,6 +444,9 @@ MERGE_CASES = [
                 head_dim=64), False),
     (None, dict(n_layers=1, n_streams=8, n_q=3, mem_len=900, d_model=256, n_heads=2, head_dim=128,
                 dtype="bf16"), False),
+    # 256 whole pairs + 64 split in 4 (only the split pairs merge)
+    (None, dict(n_layers=1, n_streams=40, mem_len=1024, d_model=256, n_heads=8, head_dim=32),
+     True),
 ]
 
 
@@ -1105,9 +1113,9 @@ def test_full_size_decode_every_head(name):
     the last layer, with the cache holding seeded slabs of the projected
     spread (stored exactly in the cache type), against the oracle on the same
     slabs. A cache this large (K and V of 32 layers, far above the 256 MB
-    MALL) is read with streaming loads, and its 320 heads are split (in 4
-    over the bf16 cache, 3 over fp8) and merged in the same launch: this is
-    those paths' full-size parity case."""
+    MALL) is read with streaming loads, and of its 320 heads 256 run whole
+    and 64 are split in 4 and merged in the same launch: this is those paths'
+    full-size parity case."""
     g = synth.get(name)
     cache = pc.XattnCache(g.n_layers, g.n_streams, g.mem_len, g.d_model, g.n_heads, g.head_dim,
                           max_q=g.n_q, dtype=CACHE_DT[g.dtype])
@@ -1133,7 +1141,8 @@ def test_full_size_decode_every_head(name):
             want = oracle.cross_decode(q, kv[0], kv[1], g.scale)
             assert max_abs(got, want) <= TOL["f32"], (l, step)
     # the full-size heads are split and merged in launch
-    assert pc.cke_xattn_num_splits(cache.geom) == (4 if g.dtype == "bf16" else 3)
+    assert pc.cke_xattn_num_splits(cache.geom) == 4
+    assert pc.cke_xattn_whole_pairs(cache.geom) == 256
     assert pc.cke_xattn_merges_in_launch(cache, g.n_q)
 
 
