@@ -356,6 +356,9 @@ WEIGHT_CASES = [
     (None, dict(n_layers=1, n_streams=2, n_q=2, mem_len=300, d_model=256, n_heads=2,
                 head_dim=128, dtype="bf16"), [1]),
     (None, dict(n_layers=1, n_streams=3, mem_len=77, d_model=96, n_heads=3, head_dim=32), [0, 1, 2]),
+    # streams 0-31 whole, streams 32-39 split in 4 (the whole-pairs plan)
+    (None, dict(n_layers=1, n_streams=40, mem_len=1024, d_model=256, n_heads=8, head_dim=32),
+     [0, 5, 7]),
 ]
 
 
