@@ -111,11 +111,11 @@ int cke_xattn_num_splits(const cke_xattn_geom* g);
 /* Number of leading (stream, head) pairs, b*H + h < this value, that a decode
  * call of this geometry runs unsplit, one workgroup each; the others use
  * cke_xattn_num_splits splits. Nonzero only when B*H = 256k + R with R a
- * multiple of 8 that divides 256: the first 256k pairs whole and the last R
- * split 256/R ways, so each of the 256 compute units streams k whole pairs
- * and one split piece, and the split pairs, finished early, merge while whole
- * pairs still stream. A plan choice only: results agree with any other split
- * to rounding. 0 if invalid. */
+ * multiple of 8 such that the last R pairs split into u*256/R pieces (u = 1,
+ * or 2 for single-query bf16 caches; 2 to 8 pieces of at least 128 rows)
+ * give each of the 256 compute units k whole pairs and u pieces; the split
+ * pairs, finished early, merge while whole pairs still stream. A plan choice
+ * only: results agree with any other split to rounding. 0 if invalid. */
 int cke_xattn_whole_pairs(const cke_xattn_geom* g);
 
 /* Create a handle over caller-allocated device regions k_dev, v_dev (each

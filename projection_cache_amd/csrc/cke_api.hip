@@ -116,13 +116,14 @@ static_assert(CKE_MAX_SPLITS >= 1 && CKE_MAX_SPLITS <= cke::kMaxSplits, "split c
 //    these workgroups: 24.0); over its fp8 cache 3 splits, 16.2 against 16.7
 //    us (2 splits 16.3; 4 splits 18.3: five workgroups per unit do not all
 //    fit).
-//  * Where B*H = 256k + R with R dividing 256, whole pairs plus one split
-//    group instead (cke_xattn_whole_pairs): Large's 320 pairs as 256 whole
-//    and 64 split in 4, one whole pair and one piece per unit. A uniform
-//    split ends with every head's merge after the last rows are streamed;
-//    here the split pairs finish early and merge while the whole pairs still
-//    stream, and whole pairs need no merge: Large 21.96 against 23.04 us per
-//    call (4 uniform splits), over fp8 15.48 against 15.95 (3 splits).
+//  * Where B*H = 256k + R with R a multiple of 8 that divides 256 (or 512),
+//    whole pairs plus one split group instead (cke_xattn_whole_pairs):
+//    Large's 320 pairs as 256 whole and 64 split in 8 (two pieces per unit;
+//    over fp8 in 4, one per unit). A uniform split ends with every head's
+//    merge after the last rows are streamed; here the split pairs finish
+//    early and merge while the whole pairs still stream, and whole pairs need
+//    no merge: Large 21.96 against 23.04 us per call (4 uniform splits), over
+//    fp8 15.48 against 15.95 (3 splits).
 double unit_imbalance(long long wgs) {
     const long long units = CKE_TARGET_WGS;
     return (double)((wgs + units - 1) / units) * units / (double)wgs;
@@ -155,15 +156,20 @@ void split_plan(const cke_xattn_geom* g, int* nsplit, int* chunk, int* n_whole =
                 s = t;
             }
         }
-        // B*H = 256k + R with R dividing 256 (and a multiple of 8): the
-        // first 256k pairs whole (k per unit) and the last R split 256/R ways
-        // (one piece per unit), so every unit streams the same rows and the
-        // split pairs, done early, merge while whole pairs still stream.
+        // B*H = 256k + R, R a multiple of 8: the first 256k pairs whole (k
+        // per unit) and the last R split into u*256/R pieces (u per unit), so
+        // every unit streams the same rows and the split pairs, done early,
+        // merge while whole pairs still stream. u = 2 for single-query bf16
+        // rows where it fits (Large 21.82 against 21.93 us per call with
+        // u = 1), else 1 (over fp8 u = 2 took 15.80 against 15.49 us).
         const long long R = bh % CKE_TARGET_WGS;
-        if (R > 0 && R % 8 == 0 && CKE_TARGET_WGS % R == 0) {
-            const long long t = CKE_TARGET_WGS / R;
-            if (t >= 2 && t <= 8 && t <= max_by_rows && g->mem_len >= 256LL * t &&
-                bh / CKE_TARGET_WGS + 1 <= cke::cross_units_cap(elem_bytes(g->cache_dtype), g->max_q)) {
+        const int cap = cke::cross_units_cap(elem_bytes(g->cache_dtype), g->max_q);
+        const int u_max = (elem_bytes(g->cache_dtype) == 2 && g->max_q == 1) ? 2 : 1;
+        for (int u = u_max; u >= 1 && R > 0 && R % 8 == 0 && whole == 0; --u) {
+            if ((u * CKE_TARGET_WGS) % R != 0) continue;
+            const long long t = u * CKE_TARGET_WGS / R;
+            if (t >= 2 && t <= 8 && t <= max_by_rows && g->mem_len >= 128LL * t &&
+                bh / CKE_TARGET_WGS + u <= cap) {
                 s = (int)t;
                 whole = (int)(bh - R);
             }

@@ -108,10 +108,11 @@ def test_split_plan_evens_out_workgroups_per_compute_unit():
         return pc.cke_xattn_num_splits(base_geom(n_layers=1, n_streams=n_streams, n_heads=n_heads,
                                                  d_model=64 * n_heads, mem_len=mem_len,
                                                  cache_dtype=dt, max_q=max_q))
-    assert splits(16, 20) == 4                # Large: 320 = 256 + 64 pairs (whole pairs below)
-    assert splits(16, 20, dt=pc.CKE_FP8) == 4
-    assert splits(16, 20, mem_len=1000) == 3  # < 256 rows per piece of 4: uniform, 960 workgroups
-    assert splits(16, 20, mem_len=1000, dt=pc.CKE_FP8) == 3
+    assert splits(16, 20) == 8                # Large: 320 = 256 + 64 pairs, 2 pieces per unit
+    assert splits(16, 20, dt=pc.CKE_FP8) == 4  # one piece per unit
+    assert splits(16, 20, mem_len=1000) == 4  # pieces of 8 would be < 128 rows: 4, one per unit
+    assert splits(16, 20, mem_len=520) == 4   # 130 rows per piece of 4: one per unit
+    assert splits(16, 20, mem_len=500) == 1   # < 128 rows per piece, and < 256 per uniform split
     assert splits(16, 20, dt=pc.CKE_F32) == 4
     assert splits(16, 20, max_q=2) == 4
     assert splits(32, 16) == 1                # 512 pairs: two per unit already
@@ -119,9 +120,9 @@ def test_split_plan_evens_out_workgroups_per_compute_unit():
     assert splits(15, 20) == 5                # 300 pairs: 1.17 -> 1500 workgroups (5.86 per unit)
     assert splits(15, 20, dt=pc.CKE_FP8) == 3  # 900 workgroups (3.52 per unit)
     assert splits(64, 20) == 1                # 1280 pairs: five per unit; no room to split
-    assert splits(16, 20, mem_len=600) == 2   # at least 256 rows per split
+    assert splits(15, 20, mem_len=600) == 2   # uniform: at least 256 rows per split
     assert splits(16, 20, mem_len=300) == 1
-    # whole pairs: B*H = 256k + R, R a multiple of 8 dividing 256, split 256/R ways
+    # whole pairs: B*H = 256k + R, R a multiple of 8, split u*256/R ways (u = 2 for one-query bf16)
     def whole(n_streams, n_heads, mem_len=1500, dt=pc.CKE_BF16):
         return pc.cke_xattn_whole_pairs(base_geom(n_layers=1, n_streams=n_streams, n_heads=n_heads,
                                                   d_model=64 * n_heads, mem_len=mem_len,
@@ -129,10 +130,10 @@ def test_split_plan_evens_out_workgroups_per_compute_unit():
     assert whole(16, 20) == 256 and whole(16, 20, dt=pc.CKE_FP8) == 256
     assert whole(40, 8, mem_len=1024, dt=pc.CKE_F32) == 256
     assert splits(40, 8, mem_len=1024, dt=pc.CKE_F32) == 4
-    assert whole(16, 20, mem_len=1000) == 0   # pieces of 4 would be < 256 rows
-    assert whole(15, 20) == 0                 # 300 = 256 + 44: 44 does not divide 256
-    assert whole(36, 8) == 0                  # 288 = 256 + 32: 8 pieces per pair, T / 8 < 256
-    assert whole(36, 8, mem_len=2048) == 256 and splits(36, 8, mem_len=2048) == 8
+    assert whole(16, 20, mem_len=400) == 0    # pieces of 4 would be < 128 rows
+    assert whole(15, 20) == 0                 # 300 = 256 + 44: 44 divides neither 256 nor 512
+    assert whole(36, 8) == 256 and splits(36, 8) == 8    # 288 = 256 + 32: 16 pieces too many, 8
+    assert whole(36, 8, mem_len=1000) == 0    # 8 pieces of 125 rows
     assert whole(32, 16) == 0 and whole(1, 8) == 0
     assert pc.lib().cke_xattn_whole_pairs(None) == 0
     # fewer pairs than units: about one workgroup per unit, as before (chunks

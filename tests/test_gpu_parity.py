@@ -316,12 +316,15 @@ DEC_CASES = [
     # Whisper Base geometry with the largest query count (8) on the split path
     (None, dict(n_layers=1, n_streams=1, n_q=8, mem_len=1500, d_model=512, n_heads=8,
                 head_dim=64)),
-    # more (stream, head) pairs than compute units (264, 320): split in 3 only to even out the
-    # workgroups per unit, merged in launch (fp32 with 2 queries; bf16 like Large, whose 800
-    # rows allow at most 3 splits of 256)
+    # more (stream, head) pairs than compute units (264, 300): split in 3 only to even out the
+    # workgroups per unit, merged in launch (fp32 with 2 queries; bf16, 300 pairs, not a
+    # multiple of 8)
     (None, dict(n_layers=1, n_streams=33, n_q=2, mem_len=800, d_model=256, n_heads=8,
                 head_dim=32)),
-    (None, dict(n_layers=1, n_streams=40, mem_len=800, d_model=256, n_heads=8, head_dim=32,
+    (None, dict(n_layers=1, n_streams=75, mem_len=800, d_model=128, n_heads=4, head_dim=32,
+                dtype="bf16")),
+    # 320 pairs = 256 whole + 64 in 8 pieces, two per unit (bf16, one query)
+    (None, dict(n_layers=1, n_streams=40, mem_len=1536, d_model=256, n_heads=8, head_dim=32,
                 dtype="bf16")),
     # 320 pairs = 256 whole (one workgroup each) + 64 split in 4: the whole-pairs plan (fp32,
     # and bf16 with 2 queries)
@@ -1117,8 +1120,8 @@ def test_full_size_decode_every_head(name):
     spread (stored exactly in the cache type), against the oracle on the same
     slabs. A cache this large (K and V of 32 layers, far above the 256 MB
     MALL) is read with streaming loads, and of its 320 heads 256 run whole
-    and 64 are split in 4 and merged in the same launch: this is those paths'
-    full-size parity case."""
+    and 64 are split (in 8 over the bf16 cache, 4 over fp8) and merged in the
+    same launch: this is those paths' full-size parity case."""
     g = synth.get(name)
     cache = pc.XattnCache(g.n_layers, g.n_streams, g.mem_len, g.d_model, g.n_heads, g.head_dim,
                           max_q=g.n_q, dtype=CACHE_DT[g.dtype])
@@ -1144,7 +1147,7 @@ def test_full_size_decode_every_head(name):
             want = oracle.cross_decode(q, kv[0], kv[1], g.scale)
             assert max_abs(got, want) <= TOL["f32"], (l, step)
     # the full-size heads are split and merged in launch
-    assert pc.cke_xattn_num_splits(cache.geom) == 4
+    assert pc.cke_xattn_num_splits(cache.geom) == (8 if g.dtype == "bf16" else 4)
     assert pc.cke_xattn_whole_pairs(cache.geom) == 256
     assert pc.cke_xattn_merges_in_launch(cache, g.n_q)
 
